@@ -1,0 +1,124 @@
+"""LoLA hot path on AMD MI355X: hybrid linear attention + sliding window + SRE-scored sparse cache.
+
+The computation lives in liblola.so (HIP kernels for gfx950 behind the C ABI of include/lola.h).
+This module is its thin Python face: it owns device memory through torch tensors and marshals
+pointers; the functions carry the ABI's names.  It never computes any part of the method itself.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import torch
+
+from . import _binding as _b
+from ._binding import (LOLA_BF16, LOLA_EDEVICE, LOLA_EINVAL, LOLA_EUNSUPPORTED, LOLA_F32, LOLA_OK,
+                       LOLA_PHI_ELU1, LOLA_PHI_SOFTMAX_PM, LolaError)
+
+__all__ = ["LolaState", "LolaPhi", "lola_state_init", "lola_workspace_bytes", "lola_prefill",
+           "lola_decode_step", "LolaError", "LOLA_OK", "LOLA_EINVAL", "LOLA_EUNSUPPORTED",
+           "LOLA_EDEVICE", "library_path", "PHI_KINDS"]
+
+PHI_KINDS = {"elu1": LOLA_PHI_ELU1, "softmax_pm": LOLA_PHI_SOFTMAX_PM}
+_DTYPES = {torch.float32: LOLA_F32, torch.bfloat16: LOLA_BF16}
+
+
+def library_path() -> str:
+    return _b.LIB_PATH
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+class LolaPhi:
+    """Feature map phi (kind "elu1" or "softmax_pm") with its fp32 weight W [d_k][D or D/2]."""
+
+    def __init__(self, kind: str, W: torch.Tensor, D: int = 128):
+        if W.dtype != torch.float32 or not W.is_contiguous():
+            raise ValueError("W must be a contiguous float32 tensor")
+        self.kind = kind
+        self.W = W
+        self.c = _b.LolaPhi(PHI_KINDS[kind], W.shape[0], D, 0, W.data_ptr())
+
+
+class LolaState:
+    """Per-layer state of B sequences x n_heads heads, allocated on `device` (see lola_state)."""
+
+    def __init__(self, B: int, n_heads: int, d_k: int, d_v: int, D: int, eta: int, lam: int,
+                 dtype: torch.dtype, device="cuda"):
+        kw = dict(device=device)
+        self.dtype = dtype
+        self.H = torch.zeros(B, n_heads, d_v, D, dtype=torch.float32, **kw)
+        self.s = torch.zeros(B, n_heads, D, dtype=torch.float32, **kw)
+        self.win_k = torch.zeros(B, n_heads, max(eta, 1), d_k, dtype=dtype, **kw)
+        self.win_v = torch.zeros(B, n_heads, max(eta, 1), d_v, dtype=dtype, **kw)
+        self.cache_k = torch.zeros(B, n_heads, max(lam, 1), d_k, dtype=dtype, **kw)
+        self.cache_v = torch.zeros(B, n_heads, max(lam, 1), d_v, dtype=dtype, **kw)
+        self.cache_pos = torch.full((B, n_heads, max(lam, 1)), -1, dtype=torch.int32, **kw)
+        self.c = _b.LolaState(B, n_heads, d_k, d_v, D, eta, lam, _DTYPES[dtype], 0,
+                              self.H.data_ptr(), self.s.data_ptr(), self.win_k.data_ptr(),
+                              self.win_v.data_ptr(), self.cache_k.data_ptr(), self.cache_v.data_ptr(),
+                              self.cache_pos.data_ptr())
+
+    @property
+    def t(self) -> int:
+        return int(self.c.t)
+
+    @property
+    def shape(self) -> Tuple[int, int, int, int, int, int, int]:
+        c = self.c
+        return c.B, c.n_heads, c.d_k, c.d_v, c.D, c.eta, c.lambda_
+
+    def snapshot(self) -> dict:
+        """Device copies of every state array plus t (for restore / checkpoint)."""
+        return {k: getattr(self, k).clone() for k in
+                ("H", "s", "win_k", "win_v", "cache_k", "cache_v", "cache_pos")} | {"t": self.t}
+
+    def restore(self, snap: dict) -> None:
+        for k in ("H", "s", "win_k", "win_v", "cache_k", "cache_v", "cache_pos"):
+            getattr(self, k).copy_(snap[k])
+        self.c.t = snap["t"]
+
+
+def lola_workspace_bytes(state: LolaState, n_max: int, C: int) -> int:
+    return int(_b.load().lola_workspace_bytes(ctypes.byref(state.c), n_max, C))
+
+
+def lola_state_init(state: LolaState, stream=None) -> None:
+    _b.check("lola_state_init", _b.load().lola_state_init(ctypes.byref(state.c), _stream(stream)))
+
+
+def lola_prefill(state: LolaState, phi: LolaPhi, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                 C: int, y: Optional[torch.Tensor] = None, fold_at: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None, stream=None):
+    """Chunked prefill of q, k, v [B][h][n][d]; returns (y, fold_at).  Asynchronous on `stream`."""
+    n = q.shape[2]
+    if y is None:
+        y = torch.empty(q.shape[0], q.shape[1], n, v.shape[3], dtype=v.dtype, device=v.device)
+    need = lola_workspace_bytes(state, n, C)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    code = _b.load().lola_prefill(ctypes.byref(state.c), ctypes.byref(phi.c), _ptr(q), _ptr(k), _ptr(v),
+                                  n, C, _ptr(y), _ptr(fold_at), _ptr(workspace), workspace.numel(),
+                                  _stream(stream))
+    _b.check("lola_prefill", code)
+    return y, fold_at
+
+
+def lola_decode_step(state: LolaState, phi: LolaPhi, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                     y: Optional[torch.Tensor] = None, folded_pos: Optional[torch.Tensor] = None,
+                     stream=None):
+    """One decode token, q, k, v [B][h][d]; returns (y, folded_pos).  Asynchronous on `stream`."""
+    if y is None:
+        y = torch.empty(v.shape, dtype=v.dtype, device=v.device)
+    code = _b.load().lola_decode_step(ctypes.byref(state.c), ctypes.byref(phi.c), _ptr(q), _ptr(k),
+                                      _ptr(v), _ptr(y), _ptr(folded_pos), _stream(stream))
+    _b.check("lola_decode_step", code)
+    return y, folded_pos

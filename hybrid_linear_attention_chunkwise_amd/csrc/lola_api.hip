@@ -1,0 +1,209 @@
+// C ABI of the LoLA library: validation, workspace sizing and launch sequencing.  See include/lola.h.
+#include <limits.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "../../include/lola.h"
+#include "lola_internal.hpp"
+
+namespace {
+
+using lola::WsLayout;
+
+constexpr int kMaxLambda = 1024;
+constexpr int kMaxChunk = 256;
+constexpr size_t kLdsLimit = 160 * 1024;
+
+inline int64_t rup(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Shape checks shared by every entry point.  Returns LOLA_OK, LOLA_EINVAL or LOLA_EUNSUPPORTED.
+lola_status check_shape(const lola_state* st) {
+    if (!st) return LOLA_EINVAL;
+    if (st->B <= 0 || st->n_heads <= 0 || st->d_k <= 0 || st->d_v <= 0 || st->D <= 0) return LOLA_EINVAL;
+    if (st->eta < 0 || st->lambda < 0) return LOLA_EINVAL;
+    if (st->dtype != LOLA_F32 && st->dtype != LOLA_BF16) return LOLA_EINVAL;
+    if (st->t < 0) return LOLA_EINVAL;
+    if (st->d_k != st->d_v || (st->d_k != 64 && st->d_k != 128)) return LOLA_EUNSUPPORTED;
+    if (st->D != 128) return LOLA_EUNSUPPORTED;
+    if (st->lambda > kMaxLambda) return LOLA_EUNSUPPORTED;
+    if ((int64_t)st->B * st->n_heads > INT_MAX / 2) return LOLA_EUNSUPPORTED;
+    return LOLA_OK;
+}
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+lola_status check_state_ptrs(const lola_state* st) {
+    if (!st->H || !st->s || !aligned16(st->H) || !aligned16(st->s)) return LOLA_EINVAL;
+    if (st->eta > 0 && (!st->win_k || !st->win_v || !aligned16(st->win_k) || !aligned16(st->win_v)))
+        return LOLA_EINVAL;
+    if (st->lambda > 0 && (!st->cache_k || !st->cache_v || !st->cache_pos || !aligned16(st->cache_k) ||
+                           !aligned16(st->cache_v) || !aligned16(st->cache_pos)))
+        return LOLA_EINVAL;
+    return LOLA_OK;
+}
+
+lola_status check_phi(const lola_state* st, const lola_phi* phi) {
+    if (!phi || !phi->W || !aligned16(phi->W)) return LOLA_EINVAL;
+    if (phi->kind != LOLA_PHI_ELU1 && phi->kind != LOLA_PHI_SOFTMAX_PM) return LOLA_EINVAL;
+    if (phi->d_k != st->d_k || phi->D != st->D) return LOLA_EINVAL;
+    return LOLA_OK;
+}
+
+WsLayout make_layout(const lola_state* st, int64_t n, int32_t C) {
+    const int64_t esz = st->dtype == LOLA_BF16 ? 2 : 4;
+    const int64_t D = st->D, dv = st->d_v, lam = st->lambda;
+    WsLayout L;
+    memset(&L, 0, sizeof(L));
+    L.nchunks = (int32_t)((n + C - 1) / C);
+    L.cand_rows = (int32_t)rup(lam + C, 16);
+    L.c_pad16 = (int32_t)rup(C, 16);
+    L.c_pad32 = (int32_t)rup(C, 32);
+    int64_t p = 0;
+    L.cand_phi = p;  p = rup(p + L.cand_rows * D * esz, 256);
+    L.cand_v = p;    p = rup(p + L.cand_rows * dv * esz, 256);
+    L.slot_pos = p;  p = rup(p + (lam + 1) * 4, 256);
+    L.slot_src = p;  p = rup(p + (lam + 1) * 4, 256);
+    L.chunk0 = p;
+    int64_t q = 0;
+    L.c_snap_h = q;    q = rup(q + dv * D * esz, 256);
+    L.c_snap_s = q;    q = rup(q + D * 4, 256);
+    L.c_cache_pos = q; q = rup(q + (lam + 1) * 4, 256);
+    L.c_cache_src = q; q = rup(q + (lam + 1) * 4, 256);
+    L.c_fold_n = q;    q = rup(q + 4, 256);
+    L.c_fold_pos = q;  q = rup(q + L.c_pad16 * 4, 256);
+    L.c_fold_phi = q;  q = rup(q + L.c_pad16 * D * esz, 256);
+    L.c_fold_vt = q;   q = rup(q + dv * L.c_pad32 * esz, 256);
+    L.per_chunk = q;
+    L.per_bh = rup(L.chunk0 + (int64_t)L.nchunks * L.per_chunk, 256);
+    return L;
+}
+
+lola_status check_prefill_config(const lola_state* st, int64_t n, int32_t C) {
+    if (n < 0 || C < 1) return LOLA_EINVAL;
+    if (st->lambda > 0 && st->eta < C - 1) return LOLA_EINVAL;   // causality of chunk-level promotion
+    if (C > kMaxChunk) return LOLA_EUNSUPPORTED;
+    if (st->t + n + st->eta >= (int64_t)INT_MAX) return LOLA_EUNSUPPORTED;
+    if (n > INT_MAX / 2) return LOLA_EUNSUPPORTED;
+    const int esz = st->dtype == LOLA_BF16 ? 2 : 4;
+    if (lola::chain_lds_bytes(st->d_k, 1, esz, st->lambda, C) > kLdsLimit ||
+        lola::chain_lds_bytes(st->d_k, 0, esz, st->lambda, C) > kLdsLimit)
+        return LOLA_EUNSUPPORTED;
+    return LOLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lola_status_string(lola_status status) {
+    switch (status) {
+        case LOLA_OK: return "LOLA_OK";
+        case LOLA_EINVAL: return "LOLA_EINVAL: invalid argument";
+        case LOLA_EUNSUPPORTED: return "LOLA_EUNSUPPORTED: shape outside the supported set";
+        case LOLA_EDEVICE: return "LOLA_EDEVICE: HIP launch or runtime failure";
+        default: return "unknown lola_status";
+    }
+}
+
+size_t lola_workspace_bytes(const lola_state* st, int64_t n_max, int32_t C) {
+    if (check_shape(st) != LOLA_OK || n_max < 0 || C < 1 || C > kMaxChunk) return 0;
+    if (n_max == 0) return 256;
+    const WsLayout L = make_layout(st, n_max, C);
+    return (size_t)L.per_bh * (size_t)st->B * (size_t)st->n_heads;
+}
+
+lola_status lola_state_init(lola_state* st, void* stream) {
+    lola_status rc = check_shape(st);
+    if (rc != LOLA_OK) return rc;
+    rc = check_state_ptrs(st);
+    if (rc != LOLA_OK) return rc;
+    lola::InitArgs a;
+    a.BH = st->B * st->n_heads;
+    a.D = st->D;
+    a.d_v = st->d_v;
+    a.lam = st->lambda;
+    a.H = st->H;
+    a.s = st->s;
+    a.cache_pos = st->cache_pos;
+    if (lola::launch_init(a, (hipStream_t)stream) != hipSuccess) return LOLA_EDEVICE;
+    st->t = 0;
+    return LOLA_OK;
+}
+
+lola_status lola_prefill(lola_state* st, const lola_phi* phi, const void* q, const void* k, const void* v,
+                         int64_t n, int32_t C, void* y, int32_t* fold_at, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    lola_status rc = check_shape(st);
+    if (rc != LOLA_OK) return rc;
+    rc = check_state_ptrs(st);
+    if (rc != LOLA_OK) return rc;
+    rc = check_phi(st, phi);
+    if (rc != LOLA_OK) return rc;
+    rc = check_prefill_config(st, n, C);
+    if (rc != LOLA_OK) return rc;
+    if (n == 0) return LOLA_OK;
+    if (!q || !k || !v || !y || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y)) return LOLA_EINVAL;
+    if (fold_at && !aligned16(fold_at)) return LOLA_EINVAL;
+    const WsLayout L = make_layout(st, n, C);
+    const size_t need = (size_t)L.per_bh * (size_t)st->B * (size_t)st->n_heads;
+    if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes < need) return LOLA_EINVAL;
+
+    lola::PrefillArgs a;
+    a.BH = st->B * st->n_heads;
+    a.n = (int)n;
+    a.C = C;
+    a.eta = st->eta;
+    a.lam = st->lambda;
+    a.nchunks = L.nchunks;
+    a.nqt = (C + 63) / 64;
+    a.t0 = st->t;
+    a.q = q; a.k = k; a.v = v; a.y = y;
+    a.W = phi->W;
+    a.H = st->H; a.s = st->s;
+    a.win_k = st->win_k; a.win_v = st->win_v;
+    a.cache_k = st->cache_k; a.cache_v = st->cache_v; a.cache_pos = st->cache_pos;
+    a.fold_at = fold_at;
+    a.ws = reinterpret_cast<char*>(workspace);
+    a.L = L;
+    if ((int64_t)a.BH * a.nchunks * a.nqt > (int64_t)INT_MAX) return LOLA_EUNSUPPORTED;
+    const hipError_t e = lola::launch_prefill(a, st->dtype, st->d_k, phi->kind, (hipStream_t)stream);
+    if (e != hipSuccess) return LOLA_EDEVICE;
+    if (getenv("LOLA_DEBUG_SYNC") && hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return LOLA_EDEVICE;
+    st->t += n;
+    return LOLA_OK;
+}
+
+lola_status lola_decode_step(lola_state* st, const lola_phi* phi, const void* q, const void* k, const void* v,
+                             void* y, int32_t* folded_pos, void* stream) {
+    lola_status rc = check_shape(st);
+    if (rc != LOLA_OK) return rc;
+    rc = check_state_ptrs(st);
+    if (rc != LOLA_OK) return rc;
+    rc = check_phi(st, phi);
+    if (rc != LOLA_OK) return rc;
+    if (!q || !k || !v || !y || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y)) return LOLA_EINVAL;
+    if (folded_pos && !aligned16(folded_pos)) return LOLA_EINVAL;
+    if (st->t + 1 + st->eta >= (int64_t)INT_MAX) return LOLA_EUNSUPPORTED;
+    const int esz = st->dtype == LOLA_BF16 ? 2 : 4;
+    const size_t lds = lola::decode_lds_bytes(st->d_k, phi->kind, esz, st->lambda) + 4 * (size_t)(st->eta + 16);
+    if (lds > kLdsLimit) return LOLA_EUNSUPPORTED;
+
+    lola::DecodeArgs a;
+    a.BH = st->B * st->n_heads;
+    a.eta = st->eta;
+    a.lam = st->lambda;
+    a.t = st->t;
+    a.q = q; a.k = k; a.v = v; a.y = y;
+    a.W = phi->W;
+    a.H = st->H; a.s = st->s;
+    a.win_k = st->win_k; a.win_v = st->win_v;
+    a.cache_k = st->cache_k; a.cache_v = st->cache_v; a.cache_pos = st->cache_pos;
+    a.folded_pos = folded_pos;
+    const hipError_t e = lola::launch_decode(a, st->dtype, st->d_k, phi->kind, (hipStream_t)stream);
+    if (e != hipSuccess) return LOLA_EDEVICE;
+    if (getenv("LOLA_DEBUG_SYNC") && hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return LOLA_EDEVICE;
+    st->t += 1;
+    return LOLA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+// Internal launch interface between the C ABI layer (lola_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lola {
+
+// Per-(sequence, head) scratch used by one prefill call.  Offsets are in bytes from the start of the
+// (b, h) block; every region starts on a 256-byte boundary.
+struct WsLayout {
+    int64_t per_bh;        // bytes per (b, h)
+    int64_t cand_phi;      // [cand_rows][D]   T : phi of cache slots (rows 0..lam-1) and leaving tokens
+    int64_t cand_v;        // [cand_rows][d_v] T : values of the same rows
+    int64_t slot_pos;      // [lam] int32      : final cache table after the call (position, -1 empty)
+    int64_t slot_src;      // [lam] int32      : where each final member's K/V come from (see Src below)
+    int64_t chunk0;        // first per-chunk record
+    int64_t per_chunk;     // bytes per chunk record
+    // offsets inside a chunk record
+    int64_t c_snap_h;      // [d_v][D] T      : H at the chunk start (H transposed)
+    int64_t c_snap_s;      // [D] fp32        : s at the chunk start
+    int64_t c_cache_pos;   // [lam] int32     : cache after this chunk's allocation (positions)
+    int64_t c_cache_src;   // [lam] int32     : their sources
+    int64_t c_fold_n;      // int32           : number of tokens folded by this chunk
+    int64_t c_fold_pos;    // [c_pad16] int32 : their positions
+    int64_t c_fold_phi;    // [c_pad16][D] T  : their features, row-major
+    int64_t c_fold_vt;     // [d_v][c_pad32] T: their values, transposed
+    int32_t cand_rows;     // round_up(lam + C, 16)
+    int32_t c_pad16;
+    int32_t c_pad32;
+    int32_t nchunks;
+};
+
+// A source index names where a token's K/V live during a prefill call:
+//   0 <= src < n              : input row src of the call
+//   n <= src < n + lam        : initial cache slot (src - n) of the state
+//   n + lam <= src            : initial window ring slot (src - n - lam) of the state
+// The commit kernel runs last, so the state's initial window and cache stay readable until then.
+
+struct PrefillArgs {
+    int BH, n, C, eta, lam, nchunks, nqt;
+    int64_t t0;
+    const void* q;
+    const void* k;
+    const void* v;
+    void* y;
+    const float* W;
+    float* H;             // [BH][d_v][D]
+    float* s;             // [BH][D]
+    void* win_k;
+    void* win_v;
+    void* cache_k;
+    void* cache_v;
+    int32_t* cache_pos;
+    int32_t* fold_at;     // nullable
+    char* ws;
+    WsLayout L;
+};
+
+struct DecodeArgs {
+    int BH, eta, lam;
+    int64_t t;
+    const void* q;
+    const void* k;
+    const void* v;
+    void* y;
+    const float* W;
+    float* H;
+    float* s;
+    void* win_k;
+    void* win_v;
+    void* cache_k;
+    void* cache_v;
+    int32_t* cache_pos;
+    int32_t* folded_pos;  // nullable
+};
+
+struct InitArgs {
+    int BH, D, d_v, lam;
+    float* H;
+    float* s;
+    int32_t* cache_pos;
+};
+
+// Launchers (return hipSuccess or the launch error).  dtype: 0 = fp32, 1 = bf16.
+hipError_t launch_init(const InitArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, int dtype, int d, int phi_kind, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int d, int phi_kind, hipStream_t stream);
+
+// LDS bytes the chain kernel needs for (lam, C) at element size esz; used for validation.
+size_t chain_lds_bytes(int d, int phi_kind, int esz, int lam, int C);
+size_t decode_lds_bytes(int d, int phi_kind, int esz, int lam);
+
+}  // namespace lola

@@ -1,0 +1,327 @@
+// Prefill read-out: one workgroup per (sequence/head, chunk, 64-query tile); four waves of 16 queries.
+//
+// Eq. (14) of the LoLA notes (2.5) with the chunk schedule the chain kernel recorded:
+//   linear part  L(t) = H_c^T phi(q_t) + sum_{i in S_c, tau_i <= t} (phi(q_t).phi(k_i)) v_i
+//   exact part   E(t) = sum_{i in window(t) U cache_c, i not linear} exp(q_t.k_i / sqrt(d_k)) v_i
+//   y_t = (L + E) / (L_den + E_den), one shared denominator.
+// H_c is the chunk-start snapshot; S_c the tokens folded by chunk c (tau_i = max(i + eta, chunk start));
+// cache_c the cache after chunk c's allocation.  A cache key that is still inside query t's window is
+// read through the window, so no key is counted twice.
+//
+// Contractions run on MFMA in the transposed orientation (values x queries): the score tile K Q^T
+// comes out with the key index along the accumulator rows, which is the layout the P V^T product
+// needs for its B operand, so probabilities never leave registers.  Key and value blocks of 32 are
+// staged once per workgroup in LDS (values transposed) and shared by the four waves.
+#include "lola_common.hpp"
+#include "lola_internal.hpp"
+
+namespace lola {
+
+namespace {
+
+template <typename T>
+__device__ __forceinline__ void store4o(T* dst, float a, float b, float c, float d);
+template <>
+__device__ __forceinline__ void store4o<float>(float* dst, float a, float b, float c, float d) {
+    *reinterpret_cast<float4*>(dst) = make_float4(a, b, c, d);
+}
+template <>
+__device__ __forceinline__ void store4o<bf16>(bf16* dst, float a, float b, float c, float d) {
+    bf16x4 v;
+    v[0] = (bf16)a; v[1] = (bf16)b; v[2] = (bf16)c; v[3] = (bf16)d;
+    *reinterpret_cast<bf16x4*>(dst) = v;
+}
+
+template <typename T>
+__device__ __forceinline__ Frag8<T> frag_from_rows(const float (&lo)[4], const float (&hi)[4]) {
+    return frag_from_acc<T>(f4{lo[0], lo[1], lo[2], lo[3]}, f4{hi[0], hi[1], hi[2], hi[3]});
+}
+
+template <typename T, int DK, int PHI>
+__global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
+    constexpr int D = kFeat, DV = DK, JT = DV / 16;
+    constexpr int DW = (PHI == kPhiSoftmaxPM) ? D / 2 : D;
+    constexpr int WT_LD = DK + 4, KB = 32, K_LD = DK + 4, VT_LD = KB + 4;
+    __shared__ __align__(16) T wt[DW * WT_LD];
+    __shared__ __align__(16) T sK[KB * K_LD];
+    __shared__ __align__(16) T sVT[DV * VT_LD];
+    __shared__ float sS[D];
+    __shared__ int sKeyPos[KB];
+    __shared__ int sKeyBand[KB];
+    __shared__ int sFoldPos[256];
+
+    const int nqt = A.nqt, nch = A.nchunks;
+    const int bid = blockIdx.x;
+    const int qt = bid % nqt;
+    const int ch = (bid / nqt) % nch;
+    const int bh = bid / (nqt * nch);
+    const int n = A.n, C = A.C, eta = A.eta, lam = A.lam;
+    const int64_t t0 = A.t0;
+    const int64_t a = t0 + (int64_t)ch * C;
+    const int64_t b = min(a + (int64_t)C, t0 + (int64_t)n);
+    const int64_t q0 = a + 64 * qt;
+    if (q0 >= b) return;   // whole workgroup: ragged last chunk
+
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c = l & 15;
+    const char* rec = A.ws + (int64_t)bh * A.L.per_bh + A.L.chunk0 + (int64_t)ch * A.L.per_chunk;
+    const T* snapH = reinterpret_cast<const T*>(rec + A.L.c_snap_h);
+    const float* snapS = reinterpret_cast<const float*>(rec + A.L.c_snap_s);
+    const int* cachePos = reinterpret_cast<const int*>(rec + A.L.c_cache_pos);
+    const int* cacheSrc = reinterpret_cast<const int*>(rec + A.L.c_cache_src);
+    const int nf = *reinterpret_cast<const int*>(rec + A.L.c_fold_n);
+    const int* foldPos = reinterpret_cast<const int*>(rec + A.L.c_fold_pos);
+    const T* foldPhi = reinterpret_cast<const T*>(rec + A.L.c_fold_phi);
+    const T* foldVT = reinterpret_cast<const T*>(rec + A.L.c_fold_vt);
+    const int cp32 = A.L.c_pad32;
+
+    const T* qin = reinterpret_cast<const T*>(A.q) + (int64_t)bh * n * DK;
+    const T* kin = reinterpret_cast<const T*>(A.k) + (int64_t)bh * n * DK;
+    const T* vin = reinterpret_cast<const T*>(A.v) + (int64_t)bh * n * DV;
+    const T* ringK = eta > 0 ? reinterpret_cast<const T*>(A.win_k) + (int64_t)bh * eta * DK : nullptr;
+    const T* ringV = eta > 0 ? reinterpret_cast<const T*>(A.win_v) + (int64_t)bh * eta * DV : nullptr;
+    const T* cK = lam > 0 ? reinterpret_cast<const T*>(A.cache_k) + (int64_t)bh * lam * DK : nullptr;
+    const T* cV = lam > 0 ? reinterpret_cast<const T*>(A.cache_v) + (int64_t)bh * lam * DV : nullptr;
+    T* yout = reinterpret_cast<T*>(A.y) + (int64_t)bh * n * DV;
+
+    stage_wt<T>(wt, WT_LD, A.W, DK, DW);
+    for (int d = tid; d < D; d += 256) sS[d] = snapS[d];
+    for (int i = tid; i < nf; i += 256) sFoldPos[i] = foldPos[i];
+    __syncthreads();
+
+    const int64_t tq = q0 + 16 * w + c;          // this lane's query (column c of the wave's tile)
+    const bool qvalid = tq < b;
+    const bool wave_active = q0 + 16 * w < b;
+
+    // queries as B operand (column c = query), and their features
+    Frag8<T> qf[DK / 32];
+#pragma unroll
+    for (int ss = 0; ss < DK / 32; ++ss) qf[ss] = qvalid ? load_frag(qin + (tq - t0) * DK, ss, g) : frag_zero<T>();
+    float ph[D / 16][4];
+    phi_tile<T, DK, PHI>(wt, WT_LD, qf, ph);
+    Frag8<T> pf[D / 32];
+#pragma unroll
+    for (int ss = 0; ss < D / 32; ++ss) pf[ss] = frag_from_rows<T>(ph[2 * ss], ph[2 * ss + 1]);
+
+    // linear part: H_c^T phi(Q)^T and phi(Q) s_c
+    f4 L[JT];
+#pragma unroll
+    for (int J = 0; J < JT; ++J) L[J] = zero4();
+#pragma unroll
+    for (int ss = 0; ss < D / 32; ++ss)
+#pragma unroll
+        for (int J = 0; J < JT; ++J) mma32(L[J], load_frag(snapH + (16 * J + c) * D, ss, g), pf[ss]);
+    float lden = 0.f;
+#pragma unroll
+    for (int ft = 0; ft < D / 16; ++ft)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) lden += ph[ft][r] * sS[16 * ft + 4 * g + r];
+    lden = sum_groups(lden);
+
+    // tokens folded by this chunk become linear at tau = max(exit time, chunk start)
+    float lden_f = 0.f;
+    for (int fb = 0; fb * 32 < nf; ++fb) {
+        f4 sp[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const int i = 32 * fb + 16 * h2 + c;
+            sp[h2] = zero4();
+#pragma unroll
+            for (int ss = 0; ss < D / 32; ++ss) {
+                const Frag8<T> af = i < nf ? load_frag(foldPhi + (int64_t)i * D, ss, g) : frag_zero<T>();
+                mma32(sp[h2], af, pf[ss]);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int ii = 32 * fb + 16 * h2 + 4 * g + r;
+                bool ok = false;
+                if (ii < nf) {
+                    const int64_t tau = max((int64_t)sFoldPos[ii] + eta, a);
+                    ok = tau <= tq;
+                }
+                sp[h2][r] = ok ? sp[h2][r] : 0.f;
+                lden_f += sp[h2][r];
+            }
+        }
+        const Frag8<T> bw = frag_from_acc<T>(sp[0], sp[1]);
+#pragma unroll
+        for (int J = 0; J < JT; ++J) mma32(L[J], load_frag(foldVT + (int64_t)(16 * J + c) * cp32, fb, g), bw);
+    }
+    lden += sum_groups(lden_f);
+
+    // exact part: the window band of this query tile, then the chunk's cache list
+    const int64_t blo = max((int64_t)0, q0 - eta + 1);
+    const int64_t bhi = min(q0 + 63, b - 1);
+    const int nb = (eta > 0 && bhi >= blo) ? (int)(bhi - blo + 1) : 0;
+    const int NK = nb + lam;
+    const float scale = 1.0f / sqrtf((float)DK);
+    float m_run = -INFINITY, l_part = 0.f;
+    f4 O[JT];
+#pragma unroll
+    for (int J = 0; J < JT; ++J) O[J] = zero4();
+
+    for (int kb = 0; kb * KB < NK; ++kb) {
+        {   // stage 32 keys: thread -> (key j, eighth p) of the row
+            const int j = tid >> 3, p = tid & 7;
+            const int kk = kb * KB + j;
+            const T* rk = nullptr;
+            const T* rv = nullptr;
+            int pos = -1, band = 0;
+            if (kk < nb) {
+                const int64_t ps = blo + kk;
+                pos = (int)ps;
+                band = 1;
+                if (ps >= t0) { rk = kin + (ps - t0) * DK; rv = vin + (ps - t0) * DV; }
+                else { rk = ringK + (ps % eta) * DK; rv = ringV + (ps % eta) * DV; }
+            } else if (kk < NK) {
+                const int jj = kk - nb;
+                pos = cachePos[jj];
+                if (pos >= 0) {
+                    const int src = cacheSrc[jj];
+                    if (src < n) { rk = kin + (int64_t)src * DK; rv = vin + (int64_t)src * DV; }
+                    else if (src < n + lam) { rk = cK + (int64_t)(src - n) * DK; rv = cV + (int64_t)(src - n) * DV; }
+                    else { rk = ringK + (int64_t)(src - n - lam) * DK; rv = ringV + (int64_t)(src - n - lam) * DV; }
+                }
+            }
+            constexpr int KE = DK / 8, VE = DV / 8;
+#pragma unroll
+            for (int e = 0; e < KE; ++e) sK[j * K_LD + p * KE + e] = rk ? rk[p * KE + e] : from_f<T>(0.f);
+#pragma unroll
+            for (int e = 0; e < VE; ++e) sVT[(p * VE + e) * VT_LD + j] = rv ? rv[p * VE + e] : from_f<T>(0.f);
+            if (p == 0) { sKeyPos[j] = rk ? pos : -1; sKeyBand[j] = band; }
+        }
+        __syncthreads();
+        if (wave_active) {
+            f4 st[2];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                st[kt] = zero4();
+#pragma unroll
+                for (int ss = 0; ss < DK / 32; ++ss) mma32(st[kt], load_frag(sK + (16 * kt + c) * K_LD, ss, g), qf[ss]);
+            }
+            float bmax = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = 16 * kt + 4 * g + r;
+                    const int pos = sKeyPos[j];
+                    bool ok;
+                    if (sKeyBand[j]) ok = pos >= 0 && (int64_t)pos <= tq && (int64_t)pos >= tq - eta + 1;
+                    else ok = pos >= 0 && (int64_t)pos <= tq - eta;
+                    const float sc = ok ? st[kt][r] * scale : -INFINITY;
+                    st[kt][r] = sc;
+                    bmax = fmaxf(bmax, sc);
+                }
+            bmax = max_groups(bmax);
+            const float m_new = fmaxf(m_run, bmax);
+            const bool any = m_new != -INFINITY;
+            const float alpha = (any && m_run != -INFINITY) ? fast_exp(m_run - m_new) : (any ? 0.f : 1.f);
+#pragma unroll
+            for (int J = 0; J < JT; ++J)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) O[J][r] *= alpha;
+            l_part *= alpha;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float p = (st[kt][r] != -INFINITY) ? fast_exp(st[kt][r] - m_new) : 0.f;
+                    st[kt][r] = p;
+                    l_part += p;
+                }
+            m_run = m_new;
+            const Frag8<T> bp = frag_from_acc<T>(st[0], st[1]);
+#pragma unroll
+            for (int J = 0; J < JT; ++J) mma32(O[J], load_frag(sVT + (16 * J + c) * VT_LD, 0, g), bp);
+        }
+        __syncthreads();
+    }
+
+    // joint normalisation with a common scale exp(-cmax), cmax = max(m, log L_den)
+    const float lsum = sum_groups(l_part);
+    if (qvalid) {
+        float cm;
+        if (lden > 0.f) cm = (m_run != -INFINITY) ? fmaxf(m_run, logf(lden)) : logf(lden);
+        else cm = m_run;
+        const float sl = lden > 0.f ? fast_exp(-cm) : 0.f;
+        const float se = m_run != -INFINITY ? fast_exp(m_run - cm) : 0.f;
+        const float inv = 1.f / (lden * sl + lsum * se);
+        T* yrow = yout + (tq - t0) * DV;
+#pragma unroll
+        for (int J = 0; J < JT; ++J)
+            store4o<T>(yrow + 16 * J + 4 * g, (L[J][0] * sl + O[J][0] * se) * inv, (L[J][1] * sl + O[J][1] * se) * inv,
+                       (L[J][2] * sl + O[J][2] * se) * inv, (L[J][3] * sl + O[J][3] * se) * inv);
+    }
+}
+
+// Commit: move the final cache members' K/V into the state's slots, then write the last eta input
+// tokens into the window ring.  One workgroup per (sequence, head); runs after the read-out.
+template <typename T, int DK>
+__global__ __launch_bounds__(256) void commit_kernel(PrefillArgs A) {
+    constexpr int DV = DK;
+    const int bh = blockIdx.x, tid = threadIdx.x;
+    const int n = A.n, eta = A.eta, lam = A.lam;
+    const int64_t t0 = A.t0;
+    const char* wsb = A.ws + (int64_t)bh * A.L.per_bh;
+    const int* fp = reinterpret_cast<const int*>(wsb + A.L.slot_pos);
+    const int* fs = reinterpret_cast<const int*>(wsb + A.L.slot_src);
+    const T* kin = reinterpret_cast<const T*>(A.k) + (int64_t)bh * n * DK;
+    const T* vin = reinterpret_cast<const T*>(A.v) + (int64_t)bh * n * DV;
+    if (lam > 0) {
+        T* cK = reinterpret_cast<T*>(A.cache_k) + (int64_t)bh * lam * DK;
+        T* cV = reinterpret_cast<T*>(A.cache_v) + (int64_t)bh * lam * DV;
+        const T* ringK = eta > 0 ? reinterpret_cast<const T*>(A.win_k) + (int64_t)bh * eta * DK : nullptr;
+        const T* ringV = eta > 0 ? reinterpret_cast<const T*>(A.win_v) + (int64_t)bh * eta * DV : nullptr;
+        int32_t* cpos = A.cache_pos + (int64_t)bh * lam;
+        for (int i = tid; i < lam * DK; i += 256) {
+            const int j = i / DK, e = i - j * DK;
+            const int src = fs[j];
+            if (src < 0 || src == n + j) continue;           // empty, or a member that kept its slot
+            if (src < n) { cK[i] = kin[(int64_t)src * DK + e]; cV[(int64_t)j * DV + e] = vin[(int64_t)src * DV + e]; }
+            else { const int r = src - n - lam; cK[i] = ringK[(int64_t)r * DK + e]; cV[(int64_t)j * DV + e] = ringV[(int64_t)r * DV + e]; }
+        }
+        for (int j = tid; j < lam; j += 256) cpos[j] = fp[j];
+    }
+    __syncthreads();
+    if (eta > 0) {
+        T* ringK = reinterpret_cast<T*>(A.win_k) + (int64_t)bh * eta * DK;
+        T* ringV = reinterpret_cast<T*>(A.win_v) + (int64_t)bh * eta * DV;
+        const int64_t plo = max(t0, t0 + n - eta);
+        const int cnt = (int)(t0 + n - plo);
+        for (int i = tid; i < cnt * DK; i += 256) {
+            const int x = i / DK, e = i - x * DK;
+            const int64_t pos = plo + x;
+            const int slot = (int)(pos % eta);
+            ringK[(int64_t)slot * DK + e] = kin[(pos - t0) * DK + e];
+            ringV[(int64_t)slot * DV + e] = vin[(pos - t0) * DV + e];
+        }
+    }
+}
+
+}  // namespace
+
+template <typename T, int DK, int PHI>
+hipError_t launch_chain_t(const PrefillArgs& a, hipStream_t stream);
+
+template <typename T, int DK, int PHI>
+hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
+    hipError_t e = launch_chain_t<T, DK, PHI>(a, stream);
+    if (e != hipSuccess) return e;
+    const int64_t blocks = (int64_t)a.BH * a.nchunks * a.nqt;
+    hipLaunchKernelGGL((readout_kernel<T, DK, PHI>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((commit_kernel<T, DK>), dim3(a.BH), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, int dtype, int d, int phi_kind, hipStream_t stream) {
+    if (dtype == 0) {
+        if (d == 64) return phi_kind ? launch_prefill_t<float, 64, 1>(a, stream) : launch_prefill_t<float, 64, 0>(a, stream);
+        return phi_kind ? launch_prefill_t<float, 128, 1>(a, stream) : launch_prefill_t<float, 128, 0>(a, stream);
+    }
+    if (d == 64) return phi_kind ? launch_prefill_t<bf16, 64, 1>(a, stream) : launch_prefill_t<bf16, 64, 0>(a, stream);
+    return phi_kind ? launch_prefill_t<bf16, 128, 1>(a, stream) : launch_prefill_t<bf16, 128, 0>(a, stream);
+}
+
+}  // namespace lola

@@ -1,0 +1,129 @@
+/*
+ * lola.h — C ABI of the LoLA hot path on AMD MI355X (gfx950): causal linear attention with a
+ * fixed-size memory (H, s), a sliding window of exact KV, and a bounded sparse cache of exact KV
+ * whose members are chosen by self-recall error (SRE).
+ *
+ * Source of the method: "LoLA: Low-Rank Linear Attention With Sparse Caching" reading notes
+ * (cc.laoqi.cc, paper 2505.23666 v3), part 2 ("Method"):
+ *   2.2 Eqs. (3)-(5)   H += phi(k) v^T, s += phi(k); linear read-out H^T phi(q) / phi(q)^T s
+ *   2.3 Eq. (10)       SRE(k, v | H, s) = || H^T phi(k) / (phi(k)^T s) - v ||_2
+ *   2.4 Eqs. (11)-(13) candidates = cache + the token leaving the window; keep the lambda largest
+ *                      SRE (scored against the state before the update); fold the rest into H, s
+ *   2.5 Eq. (14)       y = [H^T phi(q) + sum_cache a v + sum_window a v] / [phi(q)^T s + sum a + sum a],
+ *                      a = exp(q^T k / sqrt(d_k))
+ *   2.6 Eq. (15)       chunked prefill: allocation once per chunk of C tokens against the chunk-start
+ *                      state; candidates = cache + the window tokens that leave during the chunk
+ *
+ * Semantics fixed where the notes leave a step open:
+ *   - the window of query t is positions max(0, t-eta+1) .. t; token i leaves it at time i + eta;
+ *   - a folded token that was leaving the window becomes visible in (H, s) at its exit time; a folded
+ *     former cache member becomes visible at the chunk start; each step scores, folds, then reads out;
+ *   - lambda == 0 or eta >= C - 1 (a chunk may only promote tokens all its queries have seen);
+ *   - if phi(k)^T s == 0 the recall is zero, so SRE = ||v||;
+ *   - exactly lambda are kept; equal SRE keeps the older position.
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers owned by the caller.  The library never allocates,
+ *     frees or synchronises; all work is enqueued on `stream` (a hipStream_t; NULL = default stream)
+ *     and the call returns before it completes.
+ *   - Arguments are validated on the host before anything is enqueued.  A failed validation returns
+ *     LOLA_EINVAL or LOLA_EUNSUPPORTED and leaves the state (device arrays and `t`) untouched.
+ *     A launch failure returns LOLA_EDEVICE (the state may then be partially updated).
+ *   - No global state: distinct states may be driven from different threads and streams.
+ *   - Supported shapes (v1): d_k == d_v in {64, 128}, D == 128, 0 <= lambda <= 1024, 1 <= C <= 256,
+ *     eta >= 0, positions below 2^31.
+ *   - Device arrays must be 16-byte aligned.
+ */
+#ifndef LOLA_H
+#define LOLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t lola_status;
+#define LOLA_OK 0
+#define LOLA_EINVAL (-1)        /* bad argument: null pointer, bad size, misalignment, small workspace */
+#define LOLA_EUNSUPPORTED (-2)  /* well-formed but outside the shapes the kernels are built for */
+#define LOLA_EDEVICE (-3)       /* a HIP launch or runtime call failed */
+
+/* Storage type of q, k, v, y and of the window / cache K, V.  H and s are always fp32. */
+#define LOLA_F32 0
+#define LOLA_BF16 1
+
+/* Feature map phi: R^{d_k} -> R^D (section 2.2).  W is shared by queries, keys, heads and batches.
+ *   LOLA_PHI_ELU1:       phi(x) = elu(xW) + 1,                     W: [d_k][D]   fp32 row-major
+ *   LOLA_PHI_SOFTMAX_PM: phi(x) = [softmax(xW); softmax(-xW)],     W: [d_k][D/2] fp32 row-major */
+#define LOLA_PHI_ELU1 0
+#define LOLA_PHI_SOFTMAX_PM 1
+
+typedef struct lola_phi {
+    int32_t kind;      /* LOLA_PHI_* */
+    int32_t d_k;       /* must equal the state's d_k */
+    int32_t D;         /* feature dimension; must equal the state's D */
+    int32_t reserved;
+    const float *W;    /* device, fp32, row-major, see above */
+} lola_phi;
+
+/* The persistent per-layer state of B sequences x n_heads heads (section 2.4's three memories).
+ * The struct itself lives in host memory; the arrays it points to are device memory.
+ *   H         [B][n_heads][d_v][D]  fp32   H transposed: entry (i, j) of H (feature i, value j) is at
+ *                                          offset j*D + i within a head
+ *   s         [B][n_heads][D]       fp32
+ *   win_k     [B][n_heads][eta][d_k]       dtype; ring: position p lives in slot p mod eta
+ *   win_v     [B][n_heads][eta][d_v]       dtype
+ *   cache_k   [B][n_heads][lambda][d_k]    dtype; slot order is arbitrary
+ *   cache_v   [B][n_heads][lambda][d_v]    dtype
+ *   cache_pos [B][n_heads][lambda]  int32  absolute position held by each slot, -1 = empty
+ *   t                                      tokens consumed by every sequence (host value, advanced
+ *                                          by lola_prefill and lola_decode_step)
+ * Pointers for zero-sized arrays (eta == 0 or lambda == 0) may be NULL. */
+typedef struct lola_state {
+    int32_t B, n_heads, d_k, d_v, D, eta, lambda, dtype;
+    int64_t t;
+    float *H;
+    float *s;
+    void *win_k, *win_v;
+    void *cache_k, *cache_v;
+    int32_t *cache_pos;
+} lola_state;
+
+/* Bytes of device scratch lola_prefill needs for calls of up to n_max tokens with chunk C, for the
+ * state's shape.  Returns 0 if the shape is invalid or unsupported. */
+size_t lola_workspace_bytes(const lola_state *st, int64_t n_max, int32_t C);
+
+/* Empties the state: H = 0, s = 0, every cache slot empty (cache_pos = -1), t = 0.
+ * Window and cache K/V contents are left as they are (they are dead until written). */
+lola_status lola_state_init(lola_state *st, void *stream);
+
+/* Chunked prefill (section 2.6, Eq. (15)) of n new tokens for every sequence and head.
+ *   q, k: [B][n_heads][n][d_k], v: [B][n_heads][n][d_v], y (output): [B][n_heads][n][d_v], all in
+ *   the state's dtype, contiguous.  Chunk boundaries are t, t+C, t+2C, ... (relative to the call's
+ *   starting t).  fold_at (nullable) [B][n_heads][n] int32 receives, for each input token, the
+ *   call-local chunk index at which it was folded into (H, s), or -1.
+ *   workspace: device scratch of at least lola_workspace_bytes(st, n, C) bytes, 256-byte aligned;
+ *   it may be reused once the enqueued work has finished.  On return st->t has advanced by n.
+ *   n == 0 is a no-op. */
+lola_status lola_prefill(lola_state *st, const lola_phi *phi, const void *q, const void *k,
+                         const void *v, int64_t n, int32_t C, void *y, int32_t *fold_at,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* One decode token for every sequence and head (section 2.4 single-token update, then Eq. (14)):
+ * the token leaving the window (if any) joins the candidates, one candidate is folded when the cache
+ * overflows, and y is read out.  q, k: [B][n_heads][d_k], v, y: [B][n_heads][d_v] in the state's
+ * dtype.  folded_pos (nullable) [B][n_heads] int32 receives the position folded by this step or -1.
+ * On return st->t has advanced by 1. */
+lola_status lola_decode_step(lola_state *st, const lola_phi *phi, const void *q, const void *k,
+                             const void *v, void *y, int32_t *folded_pos, void *stream);
+
+/* Static, human-readable text for a status code. */
+const char *lola_status_string(lola_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOLA_H */

@@ -1,0 +1,168 @@
+"""Helpers shared by the GPU parity tests: run the library through its C ABI, run the fp64 oracle on
+sampled (sequence, head) pairs in a process pool, and compare.
+
+Tolerances (written here, used by every parity test):
+  * fp32 storage: outputs within 1e-4 max row-relative error; fold schedule bit-exact except at
+    near-ties, i.e. chunks where the oracle's boundary gap (SRE_(lam) - SRE_(lam+1)) / SRE_(lam) is
+    at most 1e-6; from such a chunk on the oracle follows the GPU schedule (replay) and the
+    remaining outputs are graded against that replay.
+  * bf16 storage: outputs within 2e-2 max row-relative error against the oracle replaying the GPU
+    schedule, whose validity is checked in fp64 with relative tolerance 2e-2.
+Row-relative error of a row t is ||y_t - yhat_t||_2 / ||yhat_t||_2; the maximum over rows is reported.
+"""
+from __future__ import annotations
+
+import concurrent.futures
+import multiprocessing
+import os
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+FP32_TOL = 1e-4
+BF16_TOL = 2e-2
+TIE_BAND = 1e-6
+
+
+def n_workers() -> int:
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    return max(1, min(16, cores))
+
+
+def row_rel_err(y: np.ndarray, ref: np.ndarray) -> float:
+    y = np.asarray(y, dtype=np.float64).reshape(-1, ref.shape[-1])
+    ref = np.asarray(ref, dtype=np.float64).reshape(-1, ref.shape[-1])
+    num = np.linalg.norm(y - ref, axis=1)
+    den = np.maximum(np.linalg.norm(ref, axis=1), 1e-300)
+    return float((num / den).max()) if len(num) else 0.0
+
+
+# --------------------------------------------------------------------------------------------------
+# oracle jobs (run in worker processes; they import only numpy and the oracle)
+# --------------------------------------------------------------------------------------------------
+
+def _oracle_job(job: dict) -> dict:
+    import numpy as _np
+    from oracle import lola_oracle as O
+    phi = O.make_phi(job["phi"], job["W"])
+    d_k, d_v = job["q"].shape[1], job["v"].shape[1]
+    st = O.new_state(d_k, d_v, job["D"], job["eta"], job["lam"])
+    out = {}
+    y_o, sched_o = O.prefill(st, phi, job["q"], job["k"], job["v"], job["C"])
+    out["y_oracle"] = y_o
+    out["fold_at_oracle"] = sched_o.fold_at
+    out["gap"] = sched_o.gap
+    out["cache_oracle"] = sorted(st.cache)
+    out["H_oracle"] = st.H
+    out["s_oracle"] = st.s
+    gpu_fold = job.get("fold_at_gpu")
+    if gpu_fold is not None and not _np.array_equal(gpu_fold, sched_o.fold_at):
+        st2 = O.new_state(d_k, d_v, job["D"], job["eta"], job["lam"])
+        y_r, sched_r = O.replay(st2, phi, job["q"], job["k"], job["v"], job["C"], gpu_fold, tol=job["tol"])
+        out["y_replay"] = y_r
+        out["replay_problems"] = sched_r.problems
+        out["replay_worst"] = sched_r.worst_inversion
+        out["cache_replay"] = sorted(st2.cache)
+        out["H_replay"] = st2.H
+        out["s_replay"] = st2.s
+        # first chunk where the two schedules differ, and the oracle's gap there
+        C = job["C"]
+        diff = _np.nonzero(gpu_fold != sched_o.fold_at)[0]
+        chunks = set()
+        for i in diff:
+            for f in (gpu_fold[i], sched_o.fold_at[i]):
+                if f >= 0:
+                    chunks.add(int(f))
+        out["first_diff_chunk"] = min(chunks) if chunks else None
+    return out
+
+
+def _ctx():
+    return multiprocessing.get_context("spawn")
+
+
+def run_oracle_heads(jobs: Sequence[dict]) -> List[dict]:
+    if len(jobs) == 1:
+        return [_oracle_job(jobs[0])]
+    with concurrent.futures.ProcessPoolExecutor(max_workers=min(n_workers(), len(jobs)),
+                                                mp_context=_ctx()) as ex:
+        return list(ex.map(_oracle_job, jobs))
+
+
+def grade_prefill(res: dict, y_gpu: np.ndarray, fold_gpu: np.ndarray, dtype: str,
+                  cache_gpu: Optional[List[int]] = None) -> dict:
+    """Checks one (sequence, head) against the oracle result; returns a report, raises on failure."""
+    rep: Dict[str, object] = {}
+    same = np.array_equal(fold_gpu, res["fold_at_oracle"])
+    rep["schedule_identical"] = bool(same)
+    if same:
+        ref, cache_ref = res["y_oracle"], res["cache_oracle"]
+    else:
+        ref, cache_ref = res["y_replay"], res["cache_replay"]
+        assert not res["replay_problems"], f"invalid GPU schedule: {res['replay_problems'][:3]}"
+        if dtype == "f32":
+            c = res["first_diff_chunk"]
+            gap = res["gap"][c] if c is not None else None
+            assert gap is not None and gap <= TIE_BAND, (
+                f"fp32 schedule differs at chunk {c} with oracle gap {gap} > {TIE_BAND}")
+            rep["near_tie_chunk"] = c
+            rep["near_tie_gap"] = gap
+        rep["membership_agreement"] = float(np.mean(fold_gpu == res["fold_at_oracle"]))
+    err = row_rel_err(y_gpu, ref)
+    rep["max_row_rel_err"] = err
+    tol = FP32_TOL if dtype == "f32" else BF16_TOL
+    assert err <= tol, f"output error {err:.3e} > {tol}"
+    if cache_gpu is not None:
+        assert sorted(cache_gpu) == list(cache_ref), "final cache membership differs"
+    return rep
+
+
+def gpu_run_prefill(q, k, v, W, phi_kind: str, eta: int, lam: int, C: int, dtype: str, D: int = 128,
+                    chunks: Optional[Sequence[int]] = None, state=None):
+    """Runs lola_prefill on cuda:0 for numpy q, k, v [B][h][n][d]; returns host arrays.
+
+    ``chunks`` splits the call into several consecutive prefill calls of the given lengths."""
+    import torch
+    import hybrid_linear_attention_chunkwise_amd as lola
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    dev = torch.device("cuda:0")
+    B, h, n, d_k = q.shape
+    d_v = v.shape[-1]
+    if state is None:
+        state = lola.LolaState(B, h, d_k, d_v, D, eta, lam, tdt, device=dev)
+        lola.lola_state_init(state)
+    phi = lola.LolaPhi(phi_kind, torch.from_numpy(np.ascontiguousarray(W, dtype=np.float32)).to(dev), D)
+    qt = torch.from_numpy(q).to(dev).to(tdt)
+    kt = torch.from_numpy(k).to(dev).to(tdt)
+    vt = torch.from_numpy(v).to(dev).to(tdt)
+    ys, folds = [], []
+    bounds = [n] if chunks is None else list(chunks)
+    start = 0
+    for ln in bounds:
+        sl = slice(start, start + ln)
+        fold = torch.full((B, h, ln), -7, dtype=torch.int32, device=dev)
+        y, _ = lola.lola_prefill(state, phi, qt[:, :, sl].contiguous(), kt[:, :, sl].contiguous(),
+                                 vt[:, :, sl].contiguous(), C, fold_at=fold)
+        ys.append(y)
+        folds.append(fold)
+        start += ln
+    torch.cuda.synchronize()
+    y = torch.cat(ys, dim=2).float().cpu().numpy()
+    fold = torch.cat(folds, dim=2).cpu().numpy()
+    return y, fold, state, phi
+
+
+def state_to_host(state) -> dict:
+    import torch
+    torch.cuda.synchronize()
+    return {"H": state.H.cpu().numpy(), "s": state.s.cpu().numpy(),
+            "win_k": state.win_k.float().cpu().numpy(), "win_v": state.win_v.float().cpu().numpy(),
+            "cache_k": state.cache_k.float().cpu().numpy(), "cache_v": state.cache_v.float().cpu().numpy(),
+            "cache_pos": state.cache_pos.cpu().numpy(), "t": state.t}
+
+
+def cache_members(cache_pos_row: np.ndarray) -> List[int]:
+    return sorted(int(p) for p in cache_pos_row if p >= 0)

@@ -1,0 +1,76 @@
+"""The C-ABI library loads and exports every entry point include/lola.h declares; host-side
+validation answers without touching a GPU (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from hybrid_linear_attention_chunkwise_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lola.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lola_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("liblola.so is not built (run __graft_entry__.build())")
+    return B.load()
+
+
+def test_header_declares_the_abi():
+    assert _declared() == sorted(B.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in (B.LOLA_OK, B.LOLA_EINVAL, B.LOLA_EUNSUPPORTED, B.LOLA_EDEVICE):
+        assert B.status_string(code).startswith("LOLA_")
+    assert "unknown" in B.status_string(42)
+
+
+def _state(**kw):
+    base = dict(B=2, n_heads=3, d_k=128, d_v=128, D=128, eta=256, lambda_=256, dtype=B.LOLA_BF16, t=0)
+    base.update(kw)
+    st = B.LolaState()
+    for k, v in base.items():
+        setattr(st, k, v)
+    return st
+
+
+def test_workspace_bytes_and_shape_checks(lib):
+    st = _state()
+    n1 = lib.lola_workspace_bytes(ctypes.byref(st), 4096, 64)
+    n2 = lib.lola_workspace_bytes(ctypes.byref(st), 8192, 64)
+    assert n1 > 0 and n2 > n1 and n1 % 256 == 0
+    assert lib.lola_workspace_bytes(ctypes.byref(_state(d_k=96, d_v=96)), 64, 16) == 0
+    assert lib.lola_workspace_bytes(ctypes.byref(_state(D=64)), 64, 16) == 0
+    assert lib.lola_workspace_bytes(ctypes.byref(_state()), 64, 0) == 0
+    assert lib.lola_workspace_bytes(ctypes.byref(_state(B=0)), 64, 16) == 0
+
+
+def test_prefill_validation_without_gpu(lib):
+    phi = B.LolaPhi(B.LOLA_PHI_SOFTMAX_PM, 128, 128, 0, None)
+    st = _state()     # null device pointers
+    rc = lib.lola_prefill(ctypes.byref(st), ctypes.byref(phi), None, None, None, 16, 16, None, None,
+                          None, 0, None)
+    assert rc == B.LOLA_EINVAL
+    st = _state(d_k=96, d_v=96)
+    rc = lib.lola_prefill(ctypes.byref(st), ctypes.byref(phi), None, None, None, 16, 16, None, None,
+                          None, 0, None)
+    assert rc == B.LOLA_EUNSUPPORTED
+    rc = lib.lola_decode_step(ctypes.byref(_state()), ctypes.byref(phi), None, None, None, None, None, None)
+    assert rc == B.LOLA_EINVAL
+    rc = lib.lola_state_init(None, None)
+    assert rc == B.LOLA_EINVAL

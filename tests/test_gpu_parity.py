@@ -1,0 +1,236 @@
+"""GPU parity: liblola.so (through its C ABI) against the fp64 oracle on the same seeded inputs.
+
+Small cases span several tiles and a ragged tail; edge cases cover empty input, lambda = 0, eta = 0,
+eta >= n, n < C, C = 1 and continuation calls.  Tolerances are in tests/lola_testlib.py.
+"""
+import numpy as np
+import pytest
+
+import lola_testlib as TL
+from workloads import make_decode_tokens, make_qkv, make_weights, small_workload
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import hybrid_linear_attention_chunkwise_amd as lola
+    lola._b.load()   # fails loudly if the library is missing
+
+
+def _jobs(wl, W, q, k, v, fold, heads, tol):
+    jobs = []
+    for (b, h) in heads:
+        jobs.append(dict(phi=wl.phi, W=W, q=q[b, h].astype(np.float64), k=k[b, h].astype(np.float64),
+                         v=v[b, h].astype(np.float64), C=wl.C, eta=wl.eta, lam=wl.lam, D=wl.D,
+                         fold_at_gpu=fold[b, h].astype(np.int64), tol=tol))
+    return jobs
+
+
+def _check_workload(wl, heads=None, chunks=None):
+    W = make_weights(wl)
+    q, k, v = make_qkv(wl)
+    print(f"[parity] {wl.name} B={wl.B} h={wl.h} n={wl.n} d={wl.d_k} C={wl.C} eta={wl.eta} "
+          f"lam={wl.lam} {wl.dtype}", flush=True)
+    y, fold, state, _ = TL.gpu_run_prefill(q, k, v, W, wl.phi, wl.eta, wl.lam, wl.C, wl.dtype,
+                                           D=wl.D, chunks=chunks)
+    host = TL.state_to_host(state)
+    assert np.isfinite(y).all()
+    if heads is None:
+        heads = [(b, h) for b in range(wl.B) for h in range(wl.h)]
+    tol = TL.TIE_BAND if wl.dtype == "f32" else TL.BF16_TOL
+    if chunks is not None:
+        # fold_at of a call only covers that call's own tokens (call-local chunk ids): translate the
+        # oracle's one-call schedule into what each call must report, then grade against the oracle.
+        results = TL.run_oracle_heads(_jobs(wl, W, q, k, v, fold, heads, tol))
+        for (b, h), res in zip(heads, results):
+            exp = np.full(wl.n, -1, dtype=np.int64)
+            start = 0
+            for ln in chunks:
+                c_lo, c_hi = start // wl.C, (start + ln + wl.C - 1) // wl.C
+                for i in range(start, start + ln):
+                    c = res["fold_at_oracle"][i]
+                    if c_lo <= c < c_hi:
+                        exp[i] = c - c_lo
+                start += ln
+            assert np.array_equal(exp, fold[b, h]), "per-call fold schedule differs"
+            assert TL.row_rel_err(y[b, h], res["y_oracle"]) <= TL.FP32_TOL
+            assert TL.cache_members(host["cache_pos"][b, h]) == res["cache_oracle"]
+        return None, y, fold, host
+    results = TL.run_oracle_heads(_jobs(wl, W, q, k, v, fold, heads, tol))
+    reps = []
+    for (b, h), res in zip(heads, results):
+        rep = TL.grade_prefill(res, y[b, h], fold[b, h], wl.dtype,
+                               cache_gpu=TL.cache_members(host["cache_pos"][b, h]) if wl.lam > 0 else None)
+        same = rep["schedule_identical"]
+        Href = res["H_oracle"] if same else res["H_replay"]
+        sref = res["s_oracle"] if same else res["s_replay"]
+        hs_tol = 1e-4 if wl.dtype == "f32" else 2e-2
+        scale = max(1.0, float(np.abs(Href).max()))
+        assert np.abs(host["H"][b, h].T - Href).max() <= hs_tol * scale
+        assert np.abs(host["s"][b, h] - sref).max() <= hs_tol * max(1.0, float(np.abs(sref).max()))
+        reps.append(rep)
+    print(f"[parity] {wl.name}: max err {max(r['max_row_rel_err'] for r in reps):.3e}, "
+          f"identical schedules {sum(r['schedule_identical'] for r in reps)}/{len(reps)}", flush=True)
+    return reps, y, fold, host
+
+
+SMALL_CASES = [
+    # (seed, kwargs)
+    (1, dict(n=200, C=16, eta=24, lam=20)),                         # several chunks, ragged tail
+    (2, dict(n=333, C=64, eta=64, lam=64, d_k=64, d_v=64)),        # cfg1-like tile shape, ragged
+    (3, dict(n=150, C=32, eta=40, lam=0)),                          # lambda = 0 (window + linear)
+    (4, dict(n=90, C=8, eta=0, lam=0)),                             # pure linear attention
+    (5, dict(n=70, C=1, eta=0, lam=5)),                             # eta = 0 needs C = 1
+    (6, dict(n=120, C=16, eta=200, lam=10)),                        # eta >= n: exact softmax
+    (7, dict(n=40, C=64, eta=64, lam=16)),                          # n < C
+    (8, dict(n=260, C=32, eta=31, lam=48, phi="elu1")),             # eta = C - 1, elu feature map
+    (9, dict(n=300, C=64, eta=100, lam=37, d_k=128, d_v=128)),      # d = 128, odd lambda
+    (10, dict(n=97, C=5, eta=7, lam=9)),                            # tiny chunks
+]
+
+
+@pytest.mark.parametrize("seed,kw", SMALL_CASES, ids=[f"s{s}" for s, _ in SMALL_CASES])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_small_prefill(seed, kw, dtype):
+    kw = dict(kw)
+    kw.setdefault("d_k", 64)
+    kw.setdefault("d_v", kw["d_k"])
+    wl = small_workload(seed, B=2, h=2, dtype=dtype, **kw)
+    _check_workload(wl)
+
+
+def test_outlier_keys_and_planted_pairs_small():
+    wl = small_workload(20, B=1, h=2, n=400, C=32, eta=48, lam=40, d_k=128, d_v=128, dtype="f32",
+                        structure="outlier_keys")
+    _check_workload(wl)
+    wl = small_workload(21, B=1, h=2, n=400, C=32, eta=48, lam=40, d_k=128, d_v=128, dtype="f32",
+                        structure="planted_pairs")
+    _check_workload(wl)
+
+
+@pytest.mark.parametrize("split", [[64, 136], [32, 32, 96, 40], [192, 8]])
+def test_continuation_calls_equal_one_call(split):
+    wl = small_workload(30, B=1, h=2, n=200, C=16, eta=24, lam=20, dtype="f32")
+    _check_workload(wl, chunks=split)
+
+
+def test_empty_call_is_noop():
+    import hybrid_linear_attention_chunkwise_amd as lola
+    st = lola.LolaState(1, 1, 64, 64, 128, 8, 4, torch.float32)
+    lola.lola_state_init(st)
+    W = torch.zeros(64, 64, device="cuda")
+    phi = lola.LolaPhi("softmax_pm", W)
+    e = torch.zeros(1, 1, 0, 64, device="cuda")
+    y, _ = lola.lola_prefill(st, phi, e, e, e, 4)
+    assert st.t == 0 and y.numel() == 0
+
+
+def test_invalid_arguments_leave_state_untouched():
+    import hybrid_linear_attention_chunkwise_amd as lola
+    wl = small_workload(40, B=1, h=2, n=64, C=16, eta=20, lam=10, dtype="f32")
+    W = make_weights(wl)
+    q, k, v = make_qkv(wl)
+    _, _, st, phi = TL.gpu_run_prefill(q, k, v, W, wl.phi, wl.eta, wl.lam, wl.C, "f32")
+    before = TL.state_to_host(st)
+    qt = torch.from_numpy(q).cuda()
+    with pytest.raises(lola.LolaError) as ei:           # chunk too long for the window (lam > 0)
+        lola.lola_prefill(st, phi, qt, qt, qt, 64)
+    assert ei.value.code == lola.LOLA_EINVAL
+    with pytest.raises(lola.LolaError) as ei:           # workspace too small
+        lola.lola_prefill(st, phi, qt, qt, qt, 16, workspace=torch.empty(256, dtype=torch.uint8, device="cuda"))
+    assert ei.value.code == lola.LOLA_EINVAL
+    bad = lola.LolaPhi("softmax_pm", torch.zeros(32, 64, device="cuda"))
+    with pytest.raises(lola.LolaError):
+        lola.lola_prefill(st, bad, qt, qt, qt, 16)
+    after = TL.state_to_host(st)
+    for key in before:
+        assert np.array_equal(np.asarray(before[key]), np.asarray(after[key])), key
+
+
+def test_prefill_is_deterministic():
+    wl = small_workload(41, B=2, h=2, n=180, C=16, eta=24, lam=20, dtype="bf16")
+    W = make_weights(wl)
+    q, k, v = make_qkv(wl)
+    y1, f1, _, _ = TL.gpu_run_prefill(q, k, v, W, wl.phi, wl.eta, wl.lam, wl.C, "bf16")
+    y2, f2, _, _ = TL.gpu_run_prefill(q, k, v, W, wl.phi, wl.eta, wl.lam, wl.C, "bf16")
+    assert np.array_equal(y1, y2) and np.array_equal(f1, f2)
+
+
+def _decode_check(wl, n0, steps, heads, C0):
+    """Prefill n0 tokens, then `steps` decode tokens; oracle continues from the GPU's post-prefill
+    state and must reproduce every decode output and fold."""
+    import hybrid_linear_attention_chunkwise_amd as lola
+    from oracle import lola_oracle as O
+    W = make_weights(wl)
+    q, k, v = make_qkv(wl, n=n0)
+    tdt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+    _, _, st, phi = TL.gpu_run_prefill(q, k, v, W, wl.phi, wl.eta, wl.lam, C0, wl.dtype, D=wl.D)
+    snap = TL.state_to_host(st)
+    dq, dk, dv = make_decode_tokens(wl, steps=steps)
+    ys, folds = [], []
+    for s in range(steps):
+        fp = torch.full((wl.B, wl.h), -7, dtype=torch.int32, device="cuda")
+        y, _ = lola.lola_decode_step(st, phi, torch.from_numpy(dq[s]).cuda().to(tdt),
+                                     torch.from_numpy(dk[s]).cuda().to(tdt),
+                                     torch.from_numpy(dv[s]).cuda().to(tdt), folded_pos=fp)
+        ys.append(y.float())
+        folds.append(fp)
+    torch.cuda.synchronize()
+    ys = torch.stack(ys).cpu().numpy()
+    folds = torch.stack(folds).cpu().numpy()
+    phi_o = O.make_phi(wl.phi, W)
+    worst = 0.0
+    mism = 0
+    for (b, h) in heads:
+        so = O.state_from_arrays(snap["t"], wl.eta, wl.lam, snap["H"][b, h].T, snap["s"][b, h],
+                                 snap["win_k"][b, h], snap["win_v"][b, h], snap["cache_k"][b, h],
+                                 snap["cache_v"][b, h], snap["cache_pos"][b, h])
+        for s in range(steps):
+            y_o, f_o = O.decode_step(so, phi_o, dq[s, b, h], dk[s, b, h], dv[s, b, h])
+            if f_o != folds[s, b, h]:
+                mism += 1
+                # follow the GPU's choice (near-ties) so later steps stay comparable
+                assert wl.dtype == "bf16", f"fp32 decode fold differs at step {s}: {f_o} vs {folds[s, b, h]}"
+            worst = max(worst, TL.row_rel_err(ys[s, b, h][None], y_o[None]))
+            if f_o != folds[s, b, h]:
+                break
+    tol = TL.FP32_TOL if wl.dtype == "f32" else TL.BF16_TOL
+    print(f"[decode] {wl.name}: max err {worst:.3e}, fold mismatches {mism}", flush=True)
+    assert worst <= tol
+    return worst
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_steps_small(dtype):
+    wl = small_workload(50, B=2, h=2, n=0, C=1, eta=16, lam=12, d_k=64, d_v=64, dtype=dtype)
+    _decode_check(wl, n0=48, steps=40, heads=[(0, 0), (1, 1)], C0=16)
+
+
+def test_decode_from_empty_state_eta0():
+    wl = small_workload(51, B=1, h=2, n=0, C=1, eta=0, lam=6, d_k=64, d_v=64, dtype="f32")
+    _decode_check(wl, n0=1, steps=30, heads=[(0, 0), (0, 1)], C0=1)
+
+
+def test_decode_equals_prefill_c1():
+    """n decode steps from an empty state = prefill with C = 1 (same kernels' semantics)."""
+    import hybrid_linear_attention_chunkwise_amd as lola
+    wl = small_workload(52, B=1, h=2, n=60, C=1, eta=8, lam=6, d_k=64, d_v=64, dtype="f32")
+    W = make_weights(wl)
+    q, k, v = make_qkv(wl)
+    y_p, f_p, _, _ = TL.gpu_run_prefill(q, k, v, W, wl.phi, wl.eta, wl.lam, 1, "f32")
+    st = lola.LolaState(1, 2, 64, 64, 128, wl.eta, wl.lam, torch.float32)
+    lola.lola_state_init(st)
+    phi = lola.LolaPhi(wl.phi, torch.from_numpy(W).cuda())
+    ys = []
+    for t in range(wl.n):
+        y, _ = lola.lola_decode_step(st, phi, torch.from_numpy(q[:, :, t]).cuda().contiguous(),
+                                     torch.from_numpy(k[:, :, t]).cuda().contiguous(),
+                                     torch.from_numpy(v[:, :, t]).cuda().contiguous())
+        ys.append(y)
+    y_d = torch.stack(ys, dim=2).cpu().numpy()
+    assert TL.row_rel_err(y_d, y_p) <= 1e-5
