@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Throughput of the LoLA hot path on one MI355X; prints one JSON line.
+
+Headline step: one chunked prefill of the n = 4096, 32-head, d = 128 bf16 workload (softmax-pair
+feature map, C = 64, eta = lambda = 256, 2% outlier keys) from a freshly initialised state.
+Also measured: 256 decode steps of 64 sequences x 32 heads after an 8192-token prior context, and the
+fp64 CPU oracle on a bounded sample of the headline workload.
+
+Inputs are seeded synthetic data resident in device memory before timing starts.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "prefill tokens/s and decode tokens/s per GPU; % of MFMA / HBM roofline"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ("lola_common.hpp", "lola_chain.hip", "lola_readout.hip", "lola_decode.hip")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "hybrid_linear_attention_chunkwise_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def prefill_flops(wl) -> dict:
+    """Algorithmic FLOPs per launch of each prefill kernel (per token and head, times B*h*n)."""
+    dw = wl.D if wl.phi == "elu1" else wl.D // 2
+    phi = 2 * wl.d_k * dw
+    chain = 2 * wl.D * (wl.d_v + 1) * (wl.C + wl.lam) / wl.C + 2 * wl.D * (wl.d_v + 1) + phi
+    readout = (phi + 2 * (wl.d_k + wl.d_v) * (wl.eta + wl.lam) + 2 * wl.D * (wl.d_v + 1)
+               + (wl.D + wl.d_v + 1) * (wl.C + 1))
+    units = wl.B * wl.h * wl.n
+    return {"chain": chain * units, "readout": readout * units, "per_token_head": chain + readout}
+
+
+def decode_bytes_per_seq_head(wl) -> int:
+    """Minimum HBM bytes one decode step moves per (sequence, head) under the natural layout."""
+    esz = 2 if wl.dtype == "bf16" else 4
+    H = 2 * wl.D * wl.d_v * 4
+    s = 2 * wl.D * 4
+    window = wl.eta * (wl.d_k + wl.d_v) * esz
+    cache = wl.lam * (wl.d_k + wl.d_v) * esz
+    writes = (wl.d_k + wl.d_v) * esz * 2
+    io = (2 * wl.d_k + wl.d_v) * esz + wl.d_v * esz
+    return H + s + window + cache + writes + io
+
+
+def load_traffic(kernel: str, src_hash: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it matches the source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_hash") != src_hash:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def bench_prefill(args, lola, torch, wl):
+    from workloads import make_qkv, make_weights
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    W = make_weights(wl)
+    q, k, v = make_qkv(wl)
+    qt = torch.from_numpy(q).to(dev).to(tdt)
+    kt = torch.from_numpy(k).to(dev).to(tdt)
+    vt = torch.from_numpy(v).to(dev).to(tdt)
+    st = lola.LolaState(wl.B, wl.h, wl.d_k, wl.d_v, wl.D, wl.eta, wl.lam, tdt, device=dev)
+    phi = lola.LolaPhi(wl.phi, torch.from_numpy(W).to(dev), wl.D)
+    y = torch.empty_like(vt)
+    ws = torch.empty(lola.lola_workspace_bytes(st, wl.n, wl.C), dtype=torch.uint8, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in ev:
+        e.record()
+
+    def step(events=None):
+        lola.lola_state_init(st)
+        lola.lola_prefill(st, phi, qt, kt, vt, wl.C, y=y, workspace=ws, events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    kern = {"chain": 0.0, "readout": 0.0, "commit": 0.0}
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(ev)
+        # per-kernel durations from the boundary events of this step (same stream as the kernels)
+        ev[3].synchronize()
+        kern["chain"] += ev[0].elapsed_time(ev[1])
+        kern["readout"] += ev[1].elapsed_time(ev[2])
+        kern["commit"] += ev[2].elapsed_time(ev[3])
+    torch.cuda.synchronize()
+    t_evented = time.perf_counter() - t0
+    # the timed region proper: K back-to-back steps, no host waits inside
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern = {k_: v_ / args.steps for k_, v_ in kern.items()}   # ms per launch
+    log(f"prefill: {elapsed / args.steps * 1e3:.3f} ms/step (evented pass {t_evented / args.steps * 1e3:.3f}); "
+        f"kernels ms: {kern}")
+    return elapsed, kern
+
+
+def bench_decode(args, lola, torch, wl):
+    from workloads import make_decode_tokens_device, make_qkv_device, make_weights
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    W = make_weights(wl)
+    st = lola.LolaState(wl.B, wl.h, wl.d_k, wl.d_v, wl.D, wl.eta, wl.lam, tdt, device=dev)
+    phi = lola.LolaPhi(wl.phi, torch.from_numpy(W).to(dev), wl.D)
+    lola.lola_state_init(st)
+    # prior context, untimed, in two prefill calls
+    part = wl.n // 2
+    ws = torch.empty(lola.lola_workspace_bytes(st, part, wl.C), dtype=torch.uint8, device=dev)
+    qp, kp, vp = make_qkv_device(wl, dev, tdt)
+    for s0 in (0, part):
+        lola.lola_prefill(st, phi, qp[:, :, s0:s0 + part].contiguous(), kp[:, :, s0:s0 + part].contiguous(),
+                          vp[:, :, s0:s0 + part].contiguous(), wl.C, workspace=ws)
+    del qp, kp, vp, ws
+    torch.cuda.synchronize()
+    snap = st.snapshot()
+    dq, dk, dv = make_decode_tokens_device(wl, dev, tdt)
+    y = torch.empty(wl.B, wl.h, wl.d_v, dtype=tdt, device=dev)
+    steps = wl.decode_steps
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    best = None
+    kern_ms = None
+    for run in range(args.decode_runs + 1):      # first run is warm-up
+        st.restore(snap)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(steps):
+            evs[s].record()
+            lola.lola_decode_step(st, phi, dq[s], dk[s], dv[s], y=y)
+        evs[steps].record()
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        if run > 0 and (best is None or el < best):
+            best = el
+            kern_ms = sum(evs[s].elapsed_time(evs[s + 1]) for s in range(steps)) / steps
+    log(f"decode: {best / steps * 1e3:.3f} ms/step wall, kernel {kern_ms:.3f} ms/step")
+    return best, kern_ms
+
+
+def _oracle_head(job):
+    import numpy as np
+    from oracle import lola_oracle as O
+    phi = O.make_phi(job["phi"], job["W"])
+    st = O.new_state(job["q"].shape[1], job["v"].shape[1], job["D"], job["eta"], job["lam"])
+    O.prefill(st, phi, job["q"].astype(np.float64), job["k"].astype(np.float64),
+              job["v"].astype(np.float64), job["C"])
+    return True
+
+
+def cpu_baseline(wl, heads: int):
+    """The fp64 oracle, as it stands, on `heads` full heads of the headline workload."""
+    import concurrent.futures
+    import multiprocessing
+    from workloads import make_qkv, make_weights
+    W = make_weights(wl)
+    q, k, v = make_qkv(wl)
+    heads = min(heads, wl.B * wl.h)
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    workers = max(1, min(16, cores, heads))
+    jobs = [dict(phi=wl.phi, W=W, q=q[0, h], k=k[0, h], v=v[0, h], C=wl.C, eta=wl.eta, lam=wl.lam, D=wl.D)
+            for h in range(heads)]
+    ctx = multiprocessing.get_context("spawn")
+    with concurrent.futures.ProcessPoolExecutor(max_workers=workers, mp_context=ctx) as ex:
+        list(ex.map(_oracle_head, jobs[:1]))          # start the workers before timing
+        t0 = time.perf_counter()
+        list(ex.map(_oracle_head, jobs))
+        wall = time.perf_counter() - t0
+    layer_tokens = wl.n * heads / (wl.B * wl.h)        # tokens of the whole layer this sample equals
+    return {"value": layer_tokens / wall, "unit": "prefill tokens/s", "cores": workers, "kind": "oracle",
+            "sample": f"{heads} of {wl.B * wl.h} (sequence, head) pairs of the headline workload, full "
+                      f"n = {wl.n} each, fp64 numpy, {workers} worker processes; value = "
+                      f"{wl.n} * {heads}/{wl.B * wl.h} layer tokens / {wall:.2f} s wall"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-runs", type=int, default=2)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: every (sequence, head) is independent, so a multi-GPU "
+              "run is N copies of this one; run it with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import hybrid_linear_attention_chunkwise_amd as lola
+    from workloads import CONFIGS
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    lola._b.load()
+    wl = CONFIGS[2]
+    src_hash = kernel_source_hash()
+    elapsed, kern = bench_prefill(args, lola, torch, wl)
+    ms_per_step = elapsed / args.steps * 1e3
+    tokens = wl.B * wl.n
+    value = tokens * args.steps / elapsed
+    fl = prefill_flops(wl)
+    dominant = max(("chain", "readout"), key=lambda k_: kern[k_])
+    ach = fl[dominant] / (kern[dominant] * 1e-3) / 1e12
+    traffic = load_traffic(dominant, src_hash)
+    roofline = {"bound": "mfma", "kernel": f"lola_{dominant}", "achieved": round(ach, 3),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 5),
+                "traffic": traffic, "kernel_ms": round(kern[dominant], 4),
+                "algorithmic_flop_per_launch": fl[dominant]}
+    out = {"metric": METRIC, "value": round(value, 1), "unit": "prefill tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded N(0,1) q/k/v, 2% keys x4)",
+           "config": {"workload": wl.name, "B": wl.B, "heads": wl.h, "n": wl.n, "d_k": wl.d_k,
+                      "d_v": wl.d_v, "D": wl.D, "phi": wl.phi, "C": wl.C, "eta": wl.eta, "lambda": wl.lam},
+           "roofline": roofline,
+           "kernels_ms": {k_: round(v_, 4) for k_, v_ in kern.items()},
+           "kernel_source_hash": src_hash}
+    all_fl = fl["chain"] + fl["readout"]
+    out["prefill_mfma_frac_whole_step"] = round(all_fl / (elapsed / args.steps) / 1e12 / PEAK_BF16_TFLOPS, 5)
+    if not args.no_decode:
+        dwl = CONFIGS[4]
+        best, kern_ms = bench_decode(args, lola, torch, dwl)
+        per_step = best / dwl.decode_steps
+        byts = decode_bytes_per_seq_head(dwl) * dwl.B * dwl.h
+        ach_d = byts / (kern_ms * 1e-3) / 1e9
+        out["decode"] = {"value": round(dwl.B * dwl.decode_steps / best, 1), "unit": "decode tokens/s",
+                         "workload": dwl.name, "ms_per_step": round(per_step * 1e3, 4),
+                         "roofline": {"bound": "hbm", "kernel": "lola_decode", "achieved": round(ach_d, 1),
+                                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach_d / PEAK_HBM_GBS, 4),
+                                      "traffic": load_traffic("decode", src_hash),
+                                      "kernel_ms": round(kern_ms, 4), "algorithmic_bytes_per_launch": byts}}
+    if not args.no_cpu_baseline:
+        log("cpu baseline: running the oracle ...")
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_heads)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -97,17 +97,25 @@ def lola_state_init(state: LolaState, stream=None) -> None:
 
 def lola_prefill(state: LolaState, phi: LolaPhi, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                  C: int, y: Optional[torch.Tensor] = None, fold_at: Optional[torch.Tensor] = None,
-                 workspace: Optional[torch.Tensor] = None, stream=None):
-    """Chunked prefill of q, k, v [B][h][n][d]; returns (y, fold_at).  Asynchronous on `stream`."""
+                 workspace: Optional[torch.Tensor] = None, stream=None, events=None):
+    """Chunked prefill of q, k, v [B][h][n][d]; returns (y, fold_at).  Asynchronous on `stream`.
+
+    ``events``: optional 4 torch.cuda.Event (created with enable_timing=True) recorded at the kernel
+    boundaries (before the chain kernel, chain|read-out, read-out|commit, after commit)."""
     n = q.shape[2]
     if y is None:
         y = torch.empty(q.shape[0], q.shape[1], n, v.shape[3], dtype=v.dtype, device=v.device)
     need = lola_workspace_bytes(state, n, C)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    code = _b.load().lola_prefill(ctypes.byref(state.c), ctypes.byref(phi.c), _ptr(q), _ptr(k), _ptr(v),
-                                  n, C, _ptr(y), _ptr(fold_at), _ptr(workspace), workspace.numel(),
-                                  _stream(stream))
+    lib = _b.load()
+    args = (ctypes.byref(state.c), ctypes.byref(phi.c), _ptr(q), _ptr(k), _ptr(v), n, C, _ptr(y),
+            _ptr(fold_at), _ptr(workspace), workspace.numel(), _stream(stream))
+    if events is None:
+        code = lib.lola_prefill(*args)
+    else:
+        handles = (ctypes.c_void_p * 4)(*[None if e is None else e.cuda_event for e in events])
+        code = lib.lola_prefill_profiled(*args, handles)
     _b.check("lola_prefill", code)
     return y, fold_at
 

@@ -21,8 +21,8 @@ LOLA_BF16 = 1
 LOLA_PHI_ELU1 = 0
 LOLA_PHI_SOFTMAX_PM = 1
 
-EXPORTED = ("lola_workspace_bytes", "lola_state_init", "lola_prefill", "lola_decode_step",
-            "lola_status_string")
+EXPORTED = ("lola_workspace_bytes", "lola_state_init", "lola_prefill", "lola_prefill_profiled",
+            "lola_decode_step", "lola_status_string")
 
 
 class LolaPhi(ctypes.Structure):
@@ -65,6 +65,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lola_state_init.restype = i32
     lib.lola_prefill.argtypes = [sp, pp, vp, vp, vp, i64, i32, vp, vp, vp, sz, vp]
     lib.lola_prefill.restype = i32
+    lib.lola_prefill_profiled.argtypes = [sp, pp, vp, vp, vp, i64, i32, vp, vp, vp, sz, vp,
+                                          ctypes.POINTER(vp)]
+    lib.lola_prefill_profiled.restype = i32
     lib.lola_decode_step.argtypes = [sp, pp, vp, vp, vp, vp, vp, vp]
     lib.lola_decode_step.restype = i32
     lib.lola_status_string.argtypes = [i32]

@@ -130,9 +130,10 @@ lola_status lola_state_init(lola_state* st, void* stream) {
     return LOLA_OK;
 }
 
-lola_status lola_prefill(lola_state* st, const lola_phi* phi, const void* q, const void* k, const void* v,
-                         int64_t n, int32_t C, void* y, int32_t* fold_at, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+static lola_status prefill_impl(lola_state* st, const lola_phi* phi, const void* q, const void* k,
+                                const void* v, int64_t n, int32_t C, void* y, int32_t* fold_at,
+                                void* workspace, size_t workspace_bytes, void* stream,
+                                void* const* events) {
     lola_status rc = check_shape(st);
     if (rc != LOLA_OK) return rc;
     rc = check_state_ptrs(st);
@@ -166,11 +167,25 @@ lola_status lola_prefill(lola_state* st, const lola_phi* phi, const void* q, con
     a.ws = reinterpret_cast<char*>(workspace);
     a.L = L;
     if ((int64_t)a.BH * a.nchunks * a.nqt > (int64_t)INT_MAX) return LOLA_EUNSUPPORTED;
-    const hipError_t e = lola::launch_prefill(a, st->dtype, st->d_k, phi->kind, (hipStream_t)stream);
+    const hipError_t e = lola::launch_prefill(a, st->dtype, st->d_k, phi->kind, (hipStream_t)stream,
+                                              reinterpret_cast<hipEvent_t const*>(events));
     if (e != hipSuccess) return LOLA_EDEVICE;
     if (getenv("LOLA_DEBUG_SYNC") && hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return LOLA_EDEVICE;
     st->t += n;
     return LOLA_OK;
+}
+
+lola_status lola_prefill(lola_state* st, const lola_phi* phi, const void* q, const void* k, const void* v,
+                         int64_t n, int32_t C, void* y, int32_t* fold_at, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    return prefill_impl(st, phi, q, k, v, n, C, y, fold_at, workspace, workspace_bytes, stream, nullptr);
+}
+
+lola_status lola_prefill_profiled(lola_state* st, const lola_phi* phi, const void* q, const void* k,
+                                  const void* v, int64_t n, int32_t C, void* y, int32_t* fold_at,
+                                  void* workspace, size_t workspace_bytes, void* stream,
+                                  void* const events[4]) {
+    return prefill_impl(st, phi, q, k, v, n, C, y, fold_at, workspace, workspace_bytes, stream, events);
 }
 
 lola_status lola_decode_step(lola_state* st, const lola_phi* phi, const void* q, const void* k, const void* v,

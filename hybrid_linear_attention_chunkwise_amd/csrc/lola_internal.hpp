@@ -84,7 +84,8 @@ struct InitArgs {
 
 // Launchers (return hipSuccess or the launch error).  dtype: 0 = fp32, 1 = bf16.
 hipError_t launch_init(const InitArgs& a, hipStream_t stream);
-hipError_t launch_prefill(const PrefillArgs& a, int dtype, int d, int phi_kind, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, int dtype, int d, int phi_kind, hipStream_t stream,
+                          hipEvent_t const* events = nullptr);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int d, int phi_kind, hipStream_t stream);
 
 // LDS bytes the chain kernel needs for (lam, C) at element size esz; used for validation.

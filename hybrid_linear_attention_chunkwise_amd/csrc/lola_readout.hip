@@ -303,25 +303,37 @@ __global__ __launch_bounds__(256) void commit_kernel(PrefillArgs A) {
 template <typename T, int DK, int PHI>
 hipError_t launch_chain_t(const PrefillArgs& a, hipStream_t stream);
 
+static hipError_t record(hipEvent_t const* ev, int i, hipStream_t stream) {
+    if (!ev || !ev[i]) return hipSuccess;
+    return hipEventRecord(ev[i], stream);
+}
+
 template <typename T, int DK, int PHI>
-hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
-    hipError_t e = launch_chain_t<T, DK, PHI>(a, stream);
+hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream, hipEvent_t const* ev) {
+    hipError_t e = record(ev, 0, stream);
     if (e != hipSuccess) return e;
+    e = launch_chain_t<T, DK, PHI>(a, stream);
+    if (e != hipSuccess) return e;
+    if ((e = record(ev, 1, stream)) != hipSuccess) return e;
     const int64_t blocks = (int64_t)a.BH * a.nchunks * a.nqt;
     hipLaunchKernelGGL((readout_kernel<T, DK, PHI>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if ((e = record(ev, 2, stream)) != hipSuccess) return e;
     hipLaunchKernelGGL((commit_kernel<T, DK>), dim3(a.BH), dim3(256), 0, stream, a);
-    return hipGetLastError();
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return record(ev, 3, stream);
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, int dtype, int d, int phi_kind, hipStream_t stream) {
+hipError_t launch_prefill(const PrefillArgs& a, int dtype, int d, int phi_kind, hipStream_t stream,
+                          hipEvent_t const* ev) {
     if (dtype == 0) {
-        if (d == 64) return phi_kind ? launch_prefill_t<float, 64, 1>(a, stream) : launch_prefill_t<float, 64, 0>(a, stream);
-        return phi_kind ? launch_prefill_t<float, 128, 1>(a, stream) : launch_prefill_t<float, 128, 0>(a, stream);
+        if (d == 64) return phi_kind ? launch_prefill_t<float, 64, 1>(a, stream, ev) : launch_prefill_t<float, 64, 0>(a, stream, ev);
+        return phi_kind ? launch_prefill_t<float, 128, 1>(a, stream, ev) : launch_prefill_t<float, 128, 0>(a, stream, ev);
     }
-    if (d == 64) return phi_kind ? launch_prefill_t<bf16, 64, 1>(a, stream) : launch_prefill_t<bf16, 64, 0>(a, stream);
-    return phi_kind ? launch_prefill_t<bf16, 128, 1>(a, stream) : launch_prefill_t<bf16, 128, 0>(a, stream);
+    if (d == 64) return phi_kind ? launch_prefill_t<bf16, 64, 1>(a, stream, ev) : launch_prefill_t<bf16, 64, 0>(a, stream, ev);
+    return phi_kind ? launch_prefill_t<bf16, 128, 1>(a, stream, ev) : launch_prefill_t<bf16, 128, 0>(a, stream, ev);
 }
 
 }  // namespace lola

@@ -111,6 +111,16 @@ lola_status lola_prefill(lola_state *st, const lola_phi *phi, const void *q, con
                          const void *v, int64_t n, int32_t C, void *y, int32_t *fold_at,
                          void *workspace, size_t workspace_bytes, void *stream);
 
+/* lola_prefill plus kernel-boundary timing: records events[0] before the allocation-chain kernel,
+ * events[1] between the chain and the read-out kernel, events[2] between the read-out and the commit
+ * kernel and events[3] after the commit kernel, all on `stream`.  events[i] are hipEvent_t handles
+ * created by the caller (any may be NULL).  Arguments, validation and results are those of
+ * lola_prefill; nothing is recorded when n == 0 or validation fails. */
+lola_status lola_prefill_profiled(lola_state *st, const lola_phi *phi, const void *q, const void *k,
+                                  const void *v, int64_t n, int32_t C, void *y, int32_t *fold_at,
+                                  void *workspace, size_t workspace_bytes, void *stream,
+                                  void *const events[4]);
+
 /* One decode token for every sequence and head (section 2.4 single-token update, then Eq. (14)):
  * the token leaving the window (if any) joins the candidates, one candidate is folded when the cache
  * overflows, and y is read out.  q, k: [B][n_heads][d_k], v, y: [B][n_heads][d_v] in the state's

@@ -1,0 +1,121 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration the benchmark times.
+
+The library processes every (sequence, head) of a workload in one call; the fp64 oracle recomputes a
+sample of them in full (a head's state depends on its whole history), in a process pool.  fp32 runs
+reuse the same bf16-representable inputs.
+"""
+import numpy as np
+import pytest
+
+import lola_testlib as TL
+from workloads import CONFIGS, make_decode_tokens_device, make_qkv, make_qkv_device, make_weights
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import hybrid_linear_attention_chunkwise_amd as lola
+    lola._b.load()
+
+
+def _run_config(cfg_id, dtype, heads):
+    wl = CONFIGS[cfg_id]
+    W = make_weights(wl)
+    q, k, v = make_qkv(wl)
+    print(f"[config {cfg_id}] {wl.name} as {dtype}: GPU prefill of B={wl.B} h={wl.h} n={wl.n}", flush=True)
+    y, fold, state, _ = TL.gpu_run_prefill(q, k, v, W, wl.phi, wl.eta, wl.lam, wl.C, dtype, D=wl.D)
+    host = TL.state_to_host(state)
+    assert np.isfinite(y).all()
+    tol = TL.TIE_BAND if dtype == "f32" else TL.BF16_TOL
+    jobs = [dict(phi=wl.phi, W=W, q=q[b, h].astype(np.float64), k=k[b, h].astype(np.float64),
+                 v=v[b, h].astype(np.float64), C=wl.C, eta=wl.eta, lam=wl.lam, D=wl.D,
+                 fold_at_gpu=fold[b, h].astype(np.int64), tol=tol) for (b, h) in heads]
+    print(f"[config {cfg_id}] oracle on {len(heads)} sampled heads ...", flush=True)
+    results = TL.run_oracle_heads(jobs)
+    reps = []
+    for (b, h), res in zip(heads, results):
+        rep = TL.grade_prefill(res, y[b, h], fold[b, h], dtype,
+                               cache_gpu=TL.cache_members(host["cache_pos"][b, h]))
+        reps.append(rep)
+        print(f"[config {cfg_id}] head ({b},{h}): {rep}", flush=True)
+    return reps
+
+
+def test_config1_full_fp32():
+    reps = _run_config(1, "f32", [(0, 0)])
+    assert reps[0]["schedule_identical"]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_config2_sampled(dtype):
+    _run_config(2, dtype, [(0, 0), (0, 7), (0, 18), (0, 31)])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_config3_sampled(dtype):
+    _run_config(3, dtype, [(0, 0), (1, 9), (3, 31)])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_config5_sampled(dtype):
+    _run_config(5, dtype, [(0, 5)])
+
+
+def test_config4_decode_sampled():
+    """64 sequences x 32 heads, 8192-token prior context (prefill), then 256 decode steps."""
+    import hybrid_linear_attention_chunkwise_amd as lola
+    from oracle import lola_oracle as O
+    wl = CONFIGS[4]
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16
+    W = make_weights(wl)
+    st = lola.LolaState(wl.B, wl.h, wl.d_k, wl.d_v, wl.D, wl.eta, wl.lam, tdt, device=dev)
+    phi = lola.LolaPhi(wl.phi, torch.from_numpy(W).to(dev), wl.D)
+    lola.lola_state_init(st)
+    qp, kp, vp = make_qkv_device(wl, dev, tdt)
+    heads = [(0, 0), (17, 5), (63, 31)]
+    fold = torch.full((wl.B, wl.h, wl.n), -7, dtype=torch.int32, device=dev)
+    y, _ = lola.lola_prefill(st, phi, qp, kp, vp, wl.C, fold_at=fold)
+    y_pref = torch.stack([y[b, h] for (b, h) in heads]).float().cpu().numpy()
+    fold_h = {bh: fold[bh].cpu().numpy().astype(np.int64) for bh in heads}
+    del y, fold
+    hq = {bh: (qp[bh].float().cpu().numpy().astype(np.float64), kp[bh].float().cpu().numpy().astype(np.float64),
+               vp[bh].float().cpu().numpy().astype(np.float64)) for bh in heads}
+    del qp, kp, vp
+    snap = TL.state_to_host(st)
+    dq, dk, dv = make_decode_tokens_device(wl, dev, tdt)
+    ys, folds = [], []
+    for s in range(wl.decode_steps):
+        fp = torch.full((wl.B, wl.h), -7, dtype=torch.int32, device=dev)
+        y, _ = lola.lola_decode_step(st, phi, dq[s], dk[s], dv[s], folded_pos=fp)
+        ys.append(y.float())
+        folds.append(fp)
+    torch.cuda.synchronize()
+    ys = torch.stack(ys).cpu().numpy()
+    folds = torch.stack(folds).cpu().numpy()
+    dqh, dkh, dvh = dq.float().cpu().numpy(), dk.float().cpu().numpy(), dv.float().cpu().numpy()
+    # (1) the prior-context prefill of the sampled heads: oracle replaying the GPU schedule (bf16)
+    jobs = [dict(phi=wl.phi, W=W, q=hq[bh][0], k=hq[bh][1], v=hq[bh][2], C=wl.C, eta=wl.eta, lam=wl.lam,
+                 D=wl.D, fold_at_gpu=fold_h[bh], tol=TL.BF16_TOL) for bh in heads[:2]]
+    phi_o = O.make_phi(wl.phi, W)
+    for i, (bh, res) in enumerate(zip(heads[:2], TL.run_oracle_heads(jobs))):
+        rep = TL.grade_prefill(res, y_pref[i], fold_h[bh], "bf16")
+        print(f"[config 4] prior-context prefill head {bh}: {rep}", flush=True)
+    # (2) decode: the oracle continues from the GPU's post-prefill state
+    worst, mism = 0.0, 0
+    for (b, h) in heads:
+        so = O.state_from_arrays(snap["t"], wl.eta, wl.lam, snap["H"][b, h].T, snap["s"][b, h],
+                                 snap["win_k"][b, h], snap["win_v"][b, h], snap["cache_k"][b, h],
+                                 snap["cache_v"][b, h], snap["cache_pos"][b, h])
+        for s in range(wl.decode_steps):
+            y_o, f_o = O.decode_step(so, phi_o, dqh[s, b, h], dkh[s, b, h], dvh[s, b, h])
+            worst = max(worst, TL.row_rel_err(ys[s, b, h][None], y_o[None]))
+            if f_o != folds[s, b, h]:
+                mism += 1
+                break       # a bf16 near-tie: the two states part ways from here
+    print(f"[config 4] decode: max err {worst:.3e}, heads that diverged at a near-tie: {mism}", flush=True)
+    assert worst <= TL.BF16_TOL

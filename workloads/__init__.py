@@ -16,7 +16,7 @@ from typing import Dict, Optional
 import numpy as np
 
 __all__ = ["Workload", "CONFIGS", "round_to_bf16", "make_weights", "make_qkv", "make_inputs",
-           "make_decode_tokens", "small_workload"]
+           "make_decode_tokens", "small_workload", "make_qkv_device", "make_decode_tokens_device"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -161,3 +161,38 @@ def small_workload(seed: int, *, B=1, h=2, n=200, d_k=64, d_v=64, phi="softmax_p
     """A small workload for parity tests (several tiles and a ragged tail)."""
     return Workload(f"small_s{seed}", B=B, h=h, n=n, d_k=d_k, d_v=d_v, phi=phi, D=D, C=C, eta=eta,
                     lam=lam, dtype=dtype, structure=structure, seed=1000 + seed)
+
+
+def _torch_gen(wl: Workload, stream: int, device):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(np.random.SeedSequence([wl.seed, stream, 7]).generate_state(1)[0]))
+    return g
+
+
+def make_qkv_device(wl: Workload, device, dtype, n: Optional[int] = None, B: Optional[int] = None,
+                    h: Optional[int] = None):
+    """Device-side seeded N(0, 1) q, k, v [B][h][n][d] in `dtype` (for workloads too large to draw on
+    the host, such as the 8192-token prior context of the decode workload).  Consumers that need
+    host copies (the oracle) copy these tensors back."""
+    import torch
+    n = wl.n if n is None else n
+    B = wl.B if B is None else B
+    h = wl.h if h is None else h
+    out = []
+    for stream, d in ((11, wl.d_k), (12, wl.d_k), (13, wl.d_v)):
+        g = _torch_gen(wl, stream, device)
+        out.append(torch.randn((B, h, n, d), generator=g, device=device, dtype=torch.float32).to(dtype))
+    return tuple(out)
+
+
+def make_decode_tokens_device(wl: Workload, device, dtype, steps: Optional[int] = None):
+    """Device-side seeded decode tokens q, k, v [steps][B][h][d] in `dtype`."""
+    import torch
+    steps = wl.decode_steps if steps is None else steps
+    out = []
+    for stream, d in ((16, wl.d_k), (17, wl.d_k), (18, wl.d_v)):
+        g = _torch_gen(wl, stream, device)
+        out.append(torch.randn((steps, wl.B, wl.h, d), generator=g, device=device,
+                               dtype=torch.float32).to(dtype))
+    return tuple(out)
