@@ -25,7 +25,7 @@ METRIC = "prefill tokens/s and decode tokens/s per GPU; % of MFMA / HBM roofline
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ("lola_common.hpp", "lola_chain.hip", "lola_readout.hip", "lola_decode.hip")
+KERNEL_SOURCES = ("lola_common.hpp", "lola_phi.hip", "lola_chain.hip", "lola_readout.hip", "lola_decode.hip")
 
 
 def log(msg: str) -> None:
@@ -88,7 +88,7 @@ def bench_prefill(args, lola, torch, wl):
     phi = lola.LolaPhi(wl.phi, torch.from_numpy(W).to(dev), wl.D)
     y = torch.empty_like(vt)
     ws = torch.empty(lola.lola_workspace_bytes(st, wl.n, wl.C), dtype=torch.uint8, device=dev)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
     for e in ev:
         e.record()
 
@@ -99,15 +99,14 @@ def bench_prefill(args, lola, torch, wl):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    kern = {"chain": 0.0, "readout": 0.0, "commit": 0.0}
+    kern = {"phi": 0.0, "chain": 0.0, "readout": 0.0, "commit": 0.0}
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step(ev)
         # per-kernel durations from the boundary events of this step (same stream as the kernels)
-        ev[3].synchronize()
-        kern["chain"] += ev[0].elapsed_time(ev[1])
-        kern["readout"] += ev[1].elapsed_time(ev[2])
-        kern["commit"] += ev[2].elapsed_time(ev[3])
+        ev[4].synchronize()
+        for i, name in enumerate(("phi", "chain", "readout", "commit")):
+            kern[name] += ev[i].elapsed_time(ev[i + 1])
     torch.cuda.synchronize()
     t_evented = time.perf_counter() - t0
     # the timed region proper: K back-to-back steps, no host waits inside

@@ -100,8 +100,8 @@ def lola_prefill(state: LolaState, phi: LolaPhi, q: torch.Tensor, k: torch.Tenso
                  workspace: Optional[torch.Tensor] = None, stream=None, events=None):
     """Chunked prefill of q, k, v [B][h][n][d]; returns (y, fold_at).  Asynchronous on `stream`.
 
-    ``events``: optional 4 torch.cuda.Event (created with enable_timing=True) recorded at the kernel
-    boundaries (before the chain kernel, chain|read-out, read-out|commit, after commit)."""
+    ``events``: optional 5 torch.cuda.Event (created with enable_timing=True) recorded at the kernel
+    boundaries: before the feature kernel, then after the feature, chain, read-out and commit kernels."""
     n = q.shape[2]
     if y is None:
         y = torch.empty(q.shape[0], q.shape[1], n, v.shape[3], dtype=v.dtype, device=v.device)
@@ -114,7 +114,7 @@ def lola_prefill(state: LolaState, phi: LolaPhi, q: torch.Tensor, k: torch.Tenso
     if events is None:
         code = lib.lola_prefill(*args)
     else:
-        handles = (ctypes.c_void_p * 4)(*[None if e is None else e.cuda_event for e in events])
+        handles = (ctypes.c_void_p * 5)(*[None if e is None else e.cuda_event for e in events])
         code = lib.lola_prefill_profiled(*args, handles)
     _b.check("lola_prefill", code)
     return y, fold_at

@@ -11,7 +11,7 @@ namespace {
 using lola::WsLayout;
 
 constexpr int kMaxLambda = 1024;
-constexpr int kMaxChunk = 256;
+constexpr int kMaxChunk = 128;
 constexpr size_t kLdsLimit = 160 * 1024;
 
 inline int64_t rup(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -55,12 +55,10 @@ WsLayout make_layout(const lola_state* st, int64_t n, int32_t C) {
     WsLayout L;
     memset(&L, 0, sizeof(L));
     L.nchunks = (int32_t)((n + C - 1) / C);
-    L.cand_rows = (int32_t)rup(lam + C, 16);
     L.c_pad16 = (int32_t)rup(C, 16);
-    L.c_pad32 = (int32_t)rup(C, 32);
+    L.c_pad64 = (int32_t)rup(C, 64);
     int64_t p = 0;
-    L.cand_phi = p;  p = rup(p + L.cand_rows * D * esz, 256);
-    L.cand_v = p;    p = rup(p + L.cand_rows * dv * esz, 256);
+    L.phi_store = p; p = rup(p + (n + lam + st->eta) * D * esz, 256);
     L.slot_pos = p;  p = rup(p + (lam + 1) * 4, 256);
     L.slot_src = p;  p = rup(p + (lam + 1) * 4, 256);
     L.chunk0 = p;
@@ -71,8 +69,8 @@ WsLayout make_layout(const lola_state* st, int64_t n, int32_t C) {
     L.c_cache_src = q; q = rup(q + (lam + 1) * 4, 256);
     L.c_fold_n = q;    q = rup(q + 4, 256);
     L.c_fold_pos = q;  q = rup(q + L.c_pad16 * 4, 256);
-    L.c_fold_phi = q;  q = rup(q + L.c_pad16 * D * esz, 256);
-    L.c_fold_vt = q;   q = rup(q + dv * L.c_pad32 * esz, 256);
+    L.c_fold_src = q;  q = rup(q + L.c_pad16 * 4, 256);
+    L.c_fold_vt = q;   q = rup(q + dv * L.c_pad64 * esz, 256);
     L.per_chunk = q;
     L.per_bh = rup(L.chunk0 + (int64_t)L.nchunks * L.per_chunk, 256);
     return L;
@@ -184,7 +182,7 @@ lola_status lola_prefill(lola_state* st, const lola_phi* phi, const void* q, con
 lola_status lola_prefill_profiled(lola_state* st, const lola_phi* phi, const void* q, const void* k,
                                   const void* v, int64_t n, int32_t C, void* y, int32_t* fold_at,
                                   void* workspace, size_t workspace_bytes, void* stream,
-                                  void* const events[4]) {
+                                  void* const events[5]) {
     return prefill_impl(st, phi, q, k, v, n, C, y, fold_at, workspace, workspace_bytes, stream, events);
 }
 

@@ -245,6 +245,27 @@ __device__ __forceinline__ int block_exclusive_scan(int* arr, int n, int* tmp) {
     return total;
 }
 
+// ---------------------------------------------------------------------------------------------
+// Exclusive prefix counts of a predicate over rows 0..N-1 without LDS scans or barriers: every wave
+// ballots all 64-row chunks (cheap) and writes the prefix of the chunks it owns (chunk k belongs to
+// wave k % nwaves).  pred(row) must read data that is already visible to the whole block.  Returns
+// the total count (the same in every lane).
+// ---------------------------------------------------------------------------------------------
+template <typename Pred>
+__device__ __forceinline__ int ballot_prefix(int N, int nwaves, Pred pred, int* out) {
+    const int l = lane_id(), w = threadIdx.x >> 6;
+    const unsigned long long lt = l ? (~0ull >> (64 - l)) : 0ull;
+    int base = 0;
+    for (int k = 0; k * 64 < N; ++k) {
+        const int r = k * 64 + l;
+        const bool p = r < N && pred(r);
+        const unsigned long long m = __ballot(p);
+        if (k % nwaves == w && r < N) out[r] = base + __popcll(m & lt);
+        base += __popcll(m);
+    }
+    return base;
+}
+
 // Row pointer helpers for element types stored as raw bytes.
 template <typename T>
 __device__ __forceinline__ const T* row_ptr(const void* base, int64_t row, int ld) {

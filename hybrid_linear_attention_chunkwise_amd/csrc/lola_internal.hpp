@@ -10,24 +10,22 @@ namespace lola {
 // (b, h) block; every region starts on a 256-byte boundary.
 struct WsLayout {
     int64_t per_bh;        // bytes per (b, h)
-    int64_t cand_phi;      // [cand_rows][D]   T : phi of cache slots (rows 0..lam-1) and leaving tokens
-    int64_t cand_v;        // [cand_rows][d_v] T : values of the same rows
+    int64_t phi_store;     // [n + lam + eta][D] T : phi(k) of every token the call scores, by source index
     int64_t slot_pos;      // [lam] int32      : final cache table after the call (position, -1 empty)
     int64_t slot_src;      // [lam] int32      : where each final member's K/V come from (see Src below)
     int64_t chunk0;        // first per-chunk record
     int64_t per_chunk;     // bytes per chunk record
     // offsets inside a chunk record
-    int64_t c_snap_h;      // [d_v][D] T      : H at the chunk start (H transposed)
+    int64_t c_snap_h;      // [d_v/16][D/32][64][8] T: H at the chunk start, in MFMA fragment order
     int64_t c_snap_s;      // [D] fp32        : s at the chunk start
     int64_t c_cache_pos;   // [lam] int32     : cache after this chunk's allocation (positions)
     int64_t c_cache_src;   // [lam] int32     : their sources
     int64_t c_fold_n;      // int32           : number of tokens folded by this chunk
     int64_t c_fold_pos;    // [c_pad16] int32 : their positions
-    int64_t c_fold_phi;    // [c_pad16][D] T  : their features, row-major
-    int64_t c_fold_vt;     // [d_v][c_pad32] T: their values, transposed
-    int32_t cand_rows;     // round_up(lam + C, 16)
+    int64_t c_fold_src;    // [c_pad16] int32 : their sources (features live in phi_store[src])
+    int64_t c_fold_vt;     // [d_v][c_pad64] T: their values, transposed
     int32_t c_pad16;
-    int32_t c_pad32;
+    int32_t c_pad64;
     int32_t nchunks;
 };
 
@@ -83,6 +81,8 @@ struct InitArgs {
 };
 
 // Launchers (return hipSuccess or the launch error).  dtype: 0 = fp32, 1 = bf16.
+template <typename T, int DK, int PHI>
+hipError_t launch_phi_t(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_init(const InitArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int d, int phi_kind, hipStream_t stream,
                           hipEvent_t const* events = nullptr);

@@ -48,7 +48,8 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
     __shared__ float sS[D];
     __shared__ int sKeyPos[KB];
     __shared__ int sKeyBand[KB];
-    __shared__ int sFoldPos[256];
+    __shared__ int sFoldPos[128];
+    __shared__ int sFoldSrc[128];
 
     const int nqt = A.nqt, nch = A.nchunks;
     const int bid = blockIdx.x;
@@ -70,9 +71,10 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
     const int* cacheSrc = reinterpret_cast<const int*>(rec + A.L.c_cache_src);
     const int nf = *reinterpret_cast<const int*>(rec + A.L.c_fold_n);
     const int* foldPos = reinterpret_cast<const int*>(rec + A.L.c_fold_pos);
-    const T* foldPhi = reinterpret_cast<const T*>(rec + A.L.c_fold_phi);
+    const int* foldSrc = reinterpret_cast<const int*>(rec + A.L.c_fold_src);
+    const T* phiStore = reinterpret_cast<const T*>(A.ws + (int64_t)bh * A.L.per_bh + A.L.phi_store);
     const T* foldVT = reinterpret_cast<const T*>(rec + A.L.c_fold_vt);
-    const int cp32 = A.L.c_pad32;
+    const int cp32 = A.L.c_pad64;
 
     const T* qin = reinterpret_cast<const T*>(A.q) + (int64_t)bh * n * DK;
     const T* kin = reinterpret_cast<const T*>(A.k) + (int64_t)bh * n * DK;
@@ -85,7 +87,7 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
 
     stage_wt<T>(wt, WT_LD, A.W, DK, DW);
     for (int d = tid; d < D; d += 256) sS[d] = snapS[d];
-    for (int i = tid; i < nf; i += 256) sFoldPos[i] = foldPos[i];
+    for (int i = tid; i < nf; i += 256) { sFoldPos[i] = foldPos[i]; sFoldSrc[i] = foldSrc[i]; }
     __syncthreads();
 
     const int64_t tq = q0 + 16 * w + c;          // this lane's query (column c of the wave's tile)
@@ -109,7 +111,8 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
 #pragma unroll
     for (int ss = 0; ss < D / 32; ++ss)
 #pragma unroll
-        for (int J = 0; J < JT; ++J) mma32(L[J], load_frag(snapH + (16 * J + c) * D, ss, g), pf[ss]);
+        for (int J = 0; J < JT; ++J)
+            mma32(L[J], *reinterpret_cast<const Frag8<T>*>(snapH + ((int64_t)(J * (D / 32) + ss) * 64 + l) * 8), pf[ss]);
     float lden = 0.f;
 #pragma unroll
     for (int ft = 0; ft < D / 16; ++ft)
@@ -127,7 +130,7 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
             sp[h2] = zero4();
 #pragma unroll
             for (int ss = 0; ss < D / 32; ++ss) {
-                const Frag8<T> af = i < nf ? load_frag(foldPhi + (int64_t)i * D, ss, g) : frag_zero<T>();
+                const Frag8<T> af = i < nf ? load_frag(phiStore + (int64_t)sFoldSrc[i] * D, ss, g) : frag_zero<T>();
                 mma32(sp[h2], af, pf[ss]);
             }
 #pragma unroll
@@ -312,18 +315,20 @@ template <typename T, int DK, int PHI>
 hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream, hipEvent_t const* ev) {
     hipError_t e = record(ev, 0, stream);
     if (e != hipSuccess) return e;
+    if ((e = launch_phi_t<T, DK, PHI>(a, stream)) != hipSuccess) return e;
+    if ((e = record(ev, 1, stream)) != hipSuccess) return e;
     e = launch_chain_t<T, DK, PHI>(a, stream);
     if (e != hipSuccess) return e;
-    if ((e = record(ev, 1, stream)) != hipSuccess) return e;
+    if ((e = record(ev, 2, stream)) != hipSuccess) return e;
     const int64_t blocks = (int64_t)a.BH * a.nchunks * a.nqt;
     hipLaunchKernelGGL((readout_kernel<T, DK, PHI>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if ((e = record(ev, 2, stream)) != hipSuccess) return e;
+    if ((e = record(ev, 3, stream)) != hipSuccess) return e;
     hipLaunchKernelGGL((commit_kernel<T, DK>), dim3(a.BH), dim3(256), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return record(ev, 3, stream);
+    return record(ev, 4, stream);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int d, int phi_kind, hipStream_t stream,

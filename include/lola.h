@@ -30,7 +30,7 @@
  *     LOLA_EINVAL or LOLA_EUNSUPPORTED and leaves the state (device arrays and `t`) untouched.
  *     A launch failure returns LOLA_EDEVICE (the state may then be partially updated).
  *   - No global state: distinct states may be driven from different threads and streams.
- *   - Supported shapes (v1): d_k == d_v in {64, 128}, D == 128, 0 <= lambda <= 1024, 1 <= C <= 256,
+ *   - Supported shapes (v1): d_k == d_v in {64, 128}, D == 128, 0 <= lambda <= 1024, 1 <= C <= 128,
  *     eta >= 0, positions below 2^31.
  *   - Device arrays must be 16-byte aligned.
  */
@@ -111,15 +111,15 @@ lola_status lola_prefill(lola_state *st, const lola_phi *phi, const void *q, con
                          const void *v, int64_t n, int32_t C, void *y, int32_t *fold_at,
                          void *workspace, size_t workspace_bytes, void *stream);
 
-/* lola_prefill plus kernel-boundary timing: records events[0] before the allocation-chain kernel,
- * events[1] between the chain and the read-out kernel, events[2] between the read-out and the commit
- * kernel and events[3] after the commit kernel, all on `stream`.  events[i] are hipEvent_t handles
+/* lola_prefill plus kernel-boundary timing.  A prefill enqueues four kernels: features, allocation
+ * chain, read-out and commit.  events[0] is recorded before the feature kernel, events[i] after the
+ * i-th kernel (events[4] after the commit kernel), all on `stream`.  events[i] are hipEvent_t handles
  * created by the caller (any may be NULL).  Arguments, validation and results are those of
  * lola_prefill; nothing is recorded when n == 0 or validation fails. */
 lola_status lola_prefill_profiled(lola_state *st, const lola_phi *phi, const void *q, const void *k,
                                   const void *v, int64_t n, int32_t C, void *y, int32_t *fold_at,
                                   void *workspace, size_t workspace_bytes, void *stream,
-                                  void *const events[4]);
+                                  void *const events[5]);
 
 /* One decode token for every sequence and head (section 2.4 single-token update, then Eq. (14)):
  * the token leaving the window (if any) joins the candidates, one candidate is folded when the cache
