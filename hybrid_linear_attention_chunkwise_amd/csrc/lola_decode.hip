@@ -2,11 +2,13 @@
 // the token leaving the window joins the cache as a candidate, SRE against the state before the
 // update, fold the lowest) followed by Eq. (14) of 2.5.
 //
-// Memory-bound: every step streams H (read + write), the window ring and the cache.  H is staged once
-// in LDS (fp32) and serves the SRE numerators (MFMA, candidates as columns), the fold (rank-1 update)
-// and the linear read-out; candidate features come from the cached keys through the same phi tile as
-// the prefill path.  Logits of the cache members are produced in the candidate pass, so cache keys
-// are read once.
+// Memory-bound: every step streams H (read + write), the window ring and the cache.  The workgroup
+// has one wave per 16 value rows of H^T; each wave keeps its rows in fp32 registers for the whole
+// step (fold and linear read-out happen there) and publishes a bf16 copy in LDS, in MFMA fragment
+// order, which all waves read as the A operand of the SRE numerators H^T Phi_E^T.  Candidates (the
+// cache slots and the leaving token) are processed in 16-column tiles: keys give both the exact logits
+// and the features (one MFMA tile through W^T), values give the squared errors.  Window keys give the
+// remaining logits; one pass over window and cache values then forms the exact numerator.
 #include "lola_common.hpp"
 #include "lola_internal.hpp"
 
@@ -16,30 +18,42 @@ namespace {
 
 __host__ __device__ inline size_t al16d(size_t x) { return (x + 15) & ~size_t(15); }
 
+template <typename T, int DK, int PHI>
+struct DecCfg {
+    static constexpr int D = kFeat, DV = DK;
+    static constexpr int DW = (PHI == kPhiSoftmaxPM) ? D / 2 : D;
+    static constexpr int NW = DV / 16;          // waves: one per 16 value rows of H^T
+    static constexpr int NT = 64 * NW;
+    static constexpr int WT_LD = DK + 4;
+    static constexpr int EPV = 16 / (int)sizeof(T);
+};
+
 struct DecLds {
-    size_t ht, wt, s, q, ek, ev, phiq, phif, pre, cpos, sre, logit, wlogit, red, o, total;
+    size_t hb, wt, s, q, phiq, phif, vf, ek, ev, cpos, sre, logit, wlog, red, o, lsum, total;
 };
 
 template <typename T, int DK, int PHI>
 __host__ __device__ inline DecLds dec_lds(int lam, int eta) {
-    constexpr int D = kFeat, DV = DK, DW = (PHI == kPhiSoftmaxPM) ? D / 2 : D;
+    using Cfg = DecCfg<T, DK, PHI>;
+    constexpr int D = Cfg::D, DV = Cfg::DV;
     DecLds o;
     size_t p = 0;
-    o.ht = p;     p = al16d(p + sizeof(float) * DV * (D + 4));
-    o.wt = p;     p = al16d(p + sizeof(T) * DW * (DK + 4));
+    o.hb = p;     p = al16d(p + sizeof(T) * DV * D);                 // H^T in fragment order
+    o.wt = p;     p = al16d(p + sizeof(T) * Cfg::DW * Cfg::WT_LD);
     o.s = p;      p = al16d(p + sizeof(float) * D);
     o.q = p;      p = al16d(p + sizeof(float) * DK);
-    o.ek = p;     p = al16d(p + sizeof(T) * DK);
-    o.ev = p;     p = al16d(p + sizeof(T) * DV);
     o.phiq = p;   p = al16d(p + sizeof(float) * D);
     o.phif = p;   p = al16d(p + sizeof(float) * D);
-    o.pre = p;    p = al16d(p + sizeof(float) * 2 * DW);
+    o.vf = p;     p = al16d(p + sizeof(float) * DV);
+    o.ek = p;     p = al16d(p + sizeof(T) * DK);
+    o.ev = p;     p = al16d(p + sizeof(T) * DV);
     o.cpos = p;   p = al16d(p + sizeof(int) * (lam + 1));
     o.sre = p;    p = al16d(p + sizeof(float) * (lam + 16));
     o.logit = p;  p = al16d(p + sizeof(float) * (lam + 16));
-    o.wlogit = p; p = al16d(p + sizeof(float) * (eta + 16));
-    o.red = p;    p = al16d(p + sizeof(unsigned long long) * 16);
-    o.o = p;      p = al16d(p + sizeof(float) * 4 * DV);
+    o.wlog = p;   p = al16d(p + sizeof(float) * (eta + 16));
+    o.red = p;    p = al16d(p + sizeof(unsigned long long) * 32);
+    o.o = p;      p = al16d(p + sizeof(float) * Cfg::NW * DV);
+    o.lsum = p;   p = al16d(p + sizeof(float) * DV);
     o.total = p;
     return o;
 }
@@ -48,29 +62,45 @@ __device__ __forceinline__ unsigned long long keep_key_d(float sre, int pos) {
     return ((unsigned long long)__float_as_uint(sre) << 32) | (unsigned long long)(0xFFFFFFFFu - (unsigned)pos);
 }
 
+template <typename T>
+__device__ __forceinline__ void load4f(const T* p, float (&o)[4]);
+template <>
+__device__ __forceinline__ void load4f<float>(const float* p, float (&o)[4]) {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+}
+template <>
+__device__ __forceinline__ void load4f<bf16>(const bf16* p, float (&o)[4]) {
+    const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+    o[0] = (float)v[0]; o[1] = (float)v[1]; o[2] = (float)v[2]; o[3] = (float)v[3];
+}
+
 template <typename T, int DK, int PHI>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs A) {
-    constexpr int D = kFeat, DV = DK, JT = DV / 16;
-    constexpr int DW = (PHI == kPhiSoftmaxPM) ? D / 2 : D;
-    constexpr int HT_LD = D + 4, WT_LD = DK + 4;
+__global__ __launch_bounds__(4 * DK) void decode_kernel(DecodeArgs A) {
+    using Cfg = DecCfg<T, DK, PHI>;
+    constexpr int D = Cfg::D, DV = Cfg::DV, DW = Cfg::DW, NW = Cfg::NW, NT = Cfg::NT, WT_LD = Cfg::WT_LD,
+                  EPV = Cfg::EPV, JT = DV / 16, IT = D / 16;
     extern __shared__ __align__(16) char smem[];
     const int lam = A.lam, eta = A.eta;
     const DecLds lo = dec_lds<T, DK, PHI>(lam, eta);
-    float* sHT = reinterpret_cast<float*>(smem + lo.ht);
+    T* sHb = reinterpret_cast<T*>(smem + lo.hb);
     T* wt = reinterpret_cast<T*>(smem + lo.wt);
     float* sS = reinterpret_cast<float*>(smem + lo.s);
     float* sQ = reinterpret_cast<float*>(smem + lo.q);
-    T* sEk = reinterpret_cast<T*>(smem + lo.ek);
-    T* sEv = reinterpret_cast<T*>(smem + lo.ev);
     float* sPhiQ = reinterpret_cast<float*>(smem + lo.phiq);
     float* sPhiF = reinterpret_cast<float*>(smem + lo.phif);
-    float* sPre = reinterpret_cast<float*>(smem + lo.pre);
+    float* sVf = reinterpret_cast<float*>(smem + lo.vf);
+    T* sEk = reinterpret_cast<T*>(smem + lo.ek);
+    T* sEv = reinterpret_cast<T*>(smem + lo.ev);
     int* sCpos = reinterpret_cast<int*>(smem + lo.cpos);
     float* sSre = reinterpret_cast<float*>(smem + lo.sre);
     float* sLogit = reinterpret_cast<float*>(smem + lo.logit);
-    float* sWLogit = reinterpret_cast<float*>(smem + lo.wlogit);
+    float* sWlog = reinterpret_cast<float*>(smem + lo.wlog);
     unsigned long long* sRed = reinterpret_cast<unsigned long long*>(smem + lo.red);
     float* sO = reinterpret_cast<float*>(smem + lo.o);
+    float* sL = reinterpret_cast<float*>(smem + lo.lsum);
+    int* sRedI = reinterpret_cast<int*>(sRed + 8);
+    float* sRedF = reinterpret_cast<float*>(sRed + 16);
 
     const int bh = blockIdx.x;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c = l & 15;
@@ -94,35 +124,60 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs A) {
     const T* ekg = eta == 0 ? kg : (has_e ? ringK + (t % eta) * DK : nullptr);
     const T* evg = eta == 0 ? vg : (has_e ? ringV + (t % eta) * DV : nullptr);
 
-    // ---- stage state and inputs ----
-    for (int i = tid; i < DV * D / 4; i += 256) {
-        const int d = (4 * i) / D, f = 4 * i - d * D;
-        const float4 h = *reinterpret_cast<const float4*>(Hg + 4 * i);
-        *reinterpret_cast<float4*>(sHT + d * HT_LD + f) = h;
+    // ---- stage: H^T rows of this wave (fp32 registers) and their bf16 copy in fragment order ----
+    f4 acc[IT];
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+        const float4 h = *reinterpret_cast<const float4*>(Hg + (16 * w + c) * D + 16 * i + 4 * g);
+        acc[i] = f4{h.x, h.y, h.z, h.w};
     }
     stage_wt<T>(wt, WT_LD, A.W, DK, DW);
-    for (int d = tid; d < D; d += 256) sS[d] = sg[d];
-    for (int d = tid; d < DK; d += 256) {
+    for (int d = tid; d < D; d += NT) sS[d] = sg[d];
+    for (int d = tid; d < DK; d += NT) {
         sQ[d] = to_f(qg[d]);
         sEk[d] = has_e ? ekg[d] : from_f<T>(0.f);
     }
-    for (int d = tid; d < DV; d += 256) sEv[d] = has_e ? evg[d] : from_f<T>(0.f);
-    for (int j = tid; j < lam; j += 256) sCpos[j] = cpos[j];
-    if (tid == 0) { sRed[0] = 0; sRed[1] = ~0ull; sRed[2] = ~0ull; }
+    for (int d = tid; d < DV; d += NT) sEv[d] = has_e ? evg[d] : from_f<T>(0.f);
+    for (int j = tid; j < lam; j += NT) sCpos[j] = cpos[j];
+    if (tid == 0) sRed[1] = ~0ull;
+#pragma unroll
+    for (int ss = 0; ss < D / 32; ++ss)
+        *reinterpret_cast<Frag8<T>*>(sHb + ((w * (D / 32) + ss) * 64 + l) * 8) =
+            frag_from_acc<T>(acc[2 * ss], acc[2 * ss + 1]);
     __syncthreads();
-    for (int j = tid; j < lam; j += 256) {
-        if (sCpos[j] >= 0) atomicAdd(reinterpret_cast<unsigned long long*>(&sRed[0]), 1ull);
-        else atomicMin(&sRed[2], (unsigned long long)j);
+    // occupied slots and the first empty one, by wave ballots (every wave gets the same answer)
+    int nG = 0, first_empty = -1;
+    for (int k = 0; k * 64 < lam; ++k) {
+        const int j = k * 64 + l;
+        const unsigned long long occ = __ballot(j < lam && sCpos[j] >= 0);
+        const unsigned long long emp = __ballot(j < lam && sCpos[j] < 0);
+        nG += __popcll(occ);
+        if (first_empty < 0 && emp) first_empty = k * 64 + __ffsll((long long)emp) - 1;
+    }
+    // features of the query: wave 0, one tile with the query in column 0
+    if (w == 0) {
+        Frag8<T> xf[DK / 32];
+#pragma unroll
+        for (int ss = 0; ss < DK / 32; ++ss) xf[ss] = c == 0 ? load_frag(qg, ss, g) : frag_zero<T>();
+        float ph[D / 16][4];
+        phi_tile<T, DK, PHI>(wt, WT_LD, xf, ph);
+        if (c == 0)
+#pragma unroll
+            for (int ft = 0; ft < D / 16; ++ft)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sPhiQ[16 * ft + 4 * g + r] = ph[ft][r];
     }
     __syncthreads();
-    const int nG = (int)sRed[0];
-    const int first_empty = sRed[2] == ~0ull ? -1 : (int)sRed[2];
     const bool scoring = has_e && lam > 0 && nG >= lam;
 
-    // ---- candidate pass: cache slots (rows 0..lam-1) and the leaving token (row lam) ----
-    // logits for every candidate; SRE only when the cache overflows.
+    // ---- candidate tiles: cache slots (rows 0..lam-1) and the leaving token (row lam) ----
     const int nrow = lam + 1;
-    for (int tile = w; tile * 16 < nrow; tile += 4) {
+    float sv[D / 32][8];
+#pragma unroll
+    for (int ss = 0; ss < D / 32; ++ss)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sv[ss][e] = sS[32 * ss + 16 * (e >> 2) + 4 * g + (e & 3)];
+    for (int tile = w; tile * 16 < nrow; tile += NW) {
         const int row = tile * 16 + c;
         bool valid;
         const T* rk;
@@ -130,47 +185,54 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs A) {
         if (row < lam) { valid = sCpos[row] >= 0; rk = cK + (int64_t)row * DK; rv = cV + (int64_t)row * DV; }
         else { valid = (row == lam) && has_e; rk = sEk; rv = sEv; }
         Frag8<T> kf[DK / 32];
+#pragma unroll
+        for (int ss = 0; ss < DK / 32; ++ss) kf[ss] = valid ? load_frag(rk, ss, g) : frag_zero<T>();
+        float vv[JT][4];
+        if (scoring) {
+#pragma unroll
+            for (int J = 0; J < JT; ++J) {
+                if (valid) load4f<T>(rv + 16 * J + 4 * g, vv[J]);
+                else { vv[J][0] = vv[J][1] = vv[J][2] = vv[J][3] = 0.f; }
+            }
+        }
         float lg = 0.f;
 #pragma unroll
-        for (int ss = 0; ss < DK / 32; ++ss) {
-            kf[ss] = valid ? load_frag(rk, ss, g) : frag_zero<T>();
+        for (int ss = 0; ss < DK / 32; ++ss)
 #pragma unroll
             for (int e = 0; e < 8; ++e) lg += frag_get(kf[ss], e) * sQ[32 * ss + 16 * (e >> 2) + 4 * g + (e & 3)];
-        }
         lg = sum_groups(lg) * scale;
+        if (g == 0 && row <= lam) sLogit[row] = lg;
         if (scoring) {
             float ph[D / 16][4];
             phi_tile<T, DK, PHI>(wt, WT_LD, kf, ph);
             float den = 0.f;
 #pragma unroll
-            for (int ft = 0; ft < D / 16; ++ft)
+            for (int ss = 0; ss < D / 32; ++ss)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) den += ph[ft][r] * sS[16 * ft + 4 * g + r];
+                for (int e = 0; e < 8; ++e) den += ph[2 * ss + (e >> 2)][e & 3] * sv[ss][e];
             den = sum_groups(den);
-            f4 num[JT];
-#pragma unroll
-            for (int J = 0; J < JT; ++J) num[J] = zero4();
-#pragma unroll
-            for (int ss = 0; ss < D / 32; ++ss) {
-                const Frag8<T> bf = frag_from_acc<T>(f4{ph[2 * ss][0], ph[2 * ss][1], ph[2 * ss][2], ph[2 * ss][3]},
-                                                     f4{ph[2 * ss + 1][0], ph[2 * ss + 1][1], ph[2 * ss + 1][2], ph[2 * ss + 1][3]});
-#pragma unroll
-                for (int J = 0; J < JT; ++J) mma32(num[J], load_frag_cvt<T>(sHT + (16 * J + c) * HT_LD, ss, g), bf);
-            }
-            const float inv = den != 0.f ? 1.f / den : 0.f;
+            const float inv = den != 0.f ? 1.f / den : 0.f;     // empty state: recall 0
             float sq = 0.f;
 #pragma unroll
-            for (int J = 0; J < JT; ++J)
+            for (int J = 0; J < JT; ++J) {
+                f4 num = zero4();
+#pragma unroll
+                for (int ss = 0; ss < D / 32; ++ss) {
+                    const Frag8<T> a = *reinterpret_cast<const Frag8<T>*>(sHb + ((J * (D / 32) + ss) * 64 + l) * 8);
+                    const Frag8<T> b = frag_from_acc<T>(f4{ph[2 * ss][0], ph[2 * ss][1], ph[2 * ss][2], ph[2 * ss][3]},
+                                                        f4{ph[2 * ss + 1][0], ph[2 * ss + 1][1], ph[2 * ss + 1][2],
+                                                           ph[2 * ss + 1][3]});
+                    mma32(num, a, b);
+                }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float vv = valid ? to_f(rv[16 * J + 4 * g + r]) : 0.f;
-                    const float x = num[J][r] * inv - vv;
+                    const float x = num[r] * inv - vv[J][r];
                     sq += x * x;
                 }
+            }
             sq = sum_groups(sq);
             if (g == 0 && row <= lam) sSre[row] = sqrtf(sq);
         }
-        if (g == 0 && row <= lam) sLogit[row] = lg;
     }
     __syncthreads();
 
@@ -179,22 +241,29 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs A) {
     int e_slot = -1;         // slot that receives the leaving token
     if (scoring) {
         unsigned long long best = ~0ull;
-        for (int r = tid; r < nrow; r += 256) {
+        for (int r = tid; r < nrow; r += NT) {
             const bool valid = r < lam ? sCpos[r] >= 0 : has_e;
             if (!valid) continue;
             const int pos = r < lam ? sCpos[r] : (int)e_pos;
             const unsigned long long k = keep_key_d(sSre[r], pos);
             best = k < best ? k : best;
         }
-        atomicMin(&sRed[1], best);
+        for (int o = 32; o > 0; o >>= 1) {
+            const unsigned long long y = __shfl_xor(best, o);
+            best = y < best ? y : best;
+        }
+        if (l == 0) atomicMin(&sRed[1], best);
         __syncthreads();
         const unsigned long long kmin = sRed[1];
-        // the position in the low word identifies the row
         const int fpos = (int)(0xFFFFFFFFu - (unsigned)(kmin & 0xFFFFFFFFull));
         if (fpos == (int)e_pos) f_row = lam;
         else {
-            for (int r = 0; r < lam; ++r)
-                if (sCpos[r] == fpos) { f_row = r; break; }
+            if (tid == 0) sRedI[2] = -1;
+            __syncthreads();
+            for (int r = tid; r < lam; r += NT)
+                if (sCpos[r] == fpos) sRedI[2] = r;
+            __syncthreads();
+            f_row = sRedI[2];
         }
         if (f_row < lam) e_slot = f_row;
     } else if (has_e) {
@@ -202,59 +271,36 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs A) {
         else e_slot = first_empty;
     }
 
-    // ---- features of the query and of the folded token (VALU; W^T in LDS) ----
-    {
-        const T* kf = nullptr;
-        if (f_row >= 0) kf = f_row < lam ? cK + (int64_t)f_row * DK : sEk;
-        for (int i = tid; i < 2 * DW; i += 256) {
-            const int which = i / DW, j = i - which * DW;
-            float z = 0.f;
-            if (which == 0) {
-                for (int d = 0; d < DK; ++d) z += sQ[d] * to_f(wt[j * WT_LD + d]);
-            } else if (kf) {
-                for (int d = 0; d < DK; ++d) z += to_f(kf[d]) * to_f(wt[j * WT_LD + d]);
-            }
-            sPre[i] = z;
-        }
-    }
-    __syncthreads();
-    if (w < 2) {
-        // wave 0: query, wave 1: folded token
-        float* outp = w == 0 ? sPhiQ : sPhiF;
-        const float* pre = sPre + w * DW;
-        if (PHI == kPhiSoftmaxPM) {
-            float mx = -INFINITY, mn = INFINITY;
-            for (int j = l; j < DW; j += 64) { mx = fmaxf(mx, pre[j]); mn = fminf(mn, pre[j]); }
-            for (int o = 32; o > 0; o >>= 1) { mx = fmaxf(mx, __shfl_xor(mx, o)); mn = fminf(mn, __shfl_xor(mn, o)); }
-            float sp = 0.f, sm = 0.f;
-            for (int j = l; j < DW; j += 64) { sp += fast_exp(pre[j] - mx); sm += fast_exp(mn - pre[j]); }
-            for (int o = 32; o > 0; o >>= 1) { sp += __shfl_xor(sp, o); sm += __shfl_xor(sm, o); }
-            for (int j = l; j < DW; j += 64) {
-                outp[j] = fast_exp(pre[j] - mx) / sp;
-                outp[DW + j] = fast_exp(mn - pre[j]) / sm;
-            }
-        } else {
-            for (int j = l; j < DW; j += 64) { const float z = pre[j]; outp[j] = z > 0.f ? z + 1.f : fast_exp(z); }
-        }
-    }
-    __syncthreads();
-
-    // ---- fold (rank-1 update of H and s) ----
+    // ---- fold: features of the folded token (wave 0, one MFMA tile), then the rank-1 update ----
     if (f_row >= 0) {
-        const T* vf = f_row < lam ? cV + (int64_t)f_row * DV : sEv;
-        for (int i = tid; i < DV * D; i += 256) {
-            const int d = i / D, f = i - d * D;
-            sHT[d * HT_LD + f] += to_f(vf[d]) * sPhiF[f];
+        const T* kf_row = f_row < lam ? cK + (int64_t)f_row * DK : sEk;
+        const T* vf_row = f_row < lam ? cV + (int64_t)f_row * DV : sEv;
+        if (w == 0) {
+            Frag8<T> xf[DK / 32];
+#pragma unroll
+            for (int ss = 0; ss < DK / 32; ++ss) xf[ss] = c == 0 ? load_frag(kf_row, ss, g) : frag_zero<T>();
+            float ph[D / 16][4];
+            phi_tile<T, DK, PHI>(wt, WT_LD, xf, ph);
+            if (c == 0)
+#pragma unroll
+                for (int ft = 0; ft < D / 16; ++ft)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sPhiF[16 * ft + 4 * g + r] = ph[ft][r];
         }
-        for (int f = tid; f < D; f += 256) sS[f] += sPhiF[f];
+        for (int d = tid; d < DV; d += NT) sVf[d] = to_f(vf_row[d]);
+        __syncthreads();
+        const float vd = sVf[16 * w + c];
+#pragma unroll
+        for (int i = 0; i < IT; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i][r] += vd * sPhiF[16 * i + 4 * g + r];
+        for (int f = tid; f < D; f += NT) sS[f] += sPhiF[f];
     }
-    __syncthreads();
 
-    // ---- read-out ----
-    // window logits: positions max(0, t-eta+1) .. t-1 from the ring, t from the input
+    // ---- window logits: positions max(0, t-eta+1) .. t-1 from the ring, t from the input ----
     const int64_t wlo = max((int64_t)0, t - eta + 1);
     const int nw = eta > 0 ? (int)(t - wlo + 1) : 0;
-    for (int tile = w; tile * 16 < nw; tile += 4) {
+    for (int tile = w; tile * 16 < nw; tile += NW) {
         const int i = tile * 16 + c;
         const bool valid = i < nw;
         const int64_t p = wlo + i;
@@ -267,9 +313,20 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs A) {
             for (int e = 0; e < 8; ++e) lg += frag_get(kf, e) * sQ[32 * ss + 16 * (e >> 2) + 4 * g + (e & 3)];
         }
         lg = sum_groups(lg) * scale;
-        if (g == 0 && valid) sWLogit[i] = lg;
+        if (g == 0 && valid) sWlog[i] = lg;
+    }
+    // linear part (registers): L[d] for this wave's rows, and phi(q).s
+    float Lrow;
+    {
+        float part_ = 0.f;
+#pragma unroll
+        for (int i = 0; i < IT; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) part_ += acc[i][r] * sPhiQ[16 * i + 4 * g + r];
+        Lrow = sum_groups(part_);
     }
     __syncthreads();
+
     // exact set: window + cache after the allocation (occupied slots except a folded one, plus the
     // leaving token unless it was folded)
     auto cache_row_exact = [&](int r) -> bool {
@@ -277,52 +334,80 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs A) {
         return has_e && f_row != lam && lam > 0;
     };
     float mloc = -INFINITY;
-    for (int i = tid; i < nw; i += 256) mloc = fmaxf(mloc, sWLogit[i]);
-    for (int r = tid; r < nrow; r += 256)
+    for (int i = tid; i < nw; i += NT) mloc = fmaxf(mloc, sWlog[i]);
+    for (int r = tid; r < nrow; r += NT)
         if (cache_row_exact(r)) mloc = fmaxf(mloc, sLogit[r]);
     for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o));
-    float* sRedF = reinterpret_cast<float*>(sRed + 4);
     if (l == 0) sRedF[w] = mloc;
     __syncthreads();
-    const float m = fmaxf(fmaxf(sRedF[0], sRedF[1]), fmaxf(sRedF[2], sRedF[3]));
-    // weighted values: wave w takes keys w, w+4, ...; lane handles value columns l, l+64
-    float o0 = 0.f, o1 = 0.f, lsum = 0.f;
+    float m = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) m = fmaxf(m, sRedF[ww]);
+
+    // ---- weighted values: lane group (w, g) takes keys kk = 4*NW*j + 4*w + g; 16 lanes per row,
+    //      EPV values per lane ----
+    constexpr int LPR = DV / EPV;                 // lanes per value row
+    constexpr int RPW = 64 / LPR;                 // rows per wave instruction
+    const int sub = l / LPR, col = (l % LPR) * EPV;
+    float o[EPV];
+#pragma unroll
+    for (int x = 0; x < EPV; ++x) o[x] = 0.f;
+    float lsum = 0.f;
     const int nkeys = nw + nrow;
-    for (int i = w; i < nkeys; i += 4) {
-        float lg;
-        const T* rv;
-        if (i < nw) {
-            const int64_t p = wlo + i;
-            lg = sWLogit[i];
-            rv = p == t ? vg : ringV + (p % eta) * DV;
-        } else {
-            const int r = i - nw;
-            if (!cache_row_exact(r)) continue;
-            lg = sLogit[r];
-            rv = r < lam ? cV + (int64_t)r * DV : sEv;
+    for (int kk0 = w * RPW; kk0 < nkeys; kk0 += NW * RPW * 4) {
+        uint4 raw[4];
+        float pw[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int kk = kk0 + u * NW * RPW + sub;
+            float lg = -INFINITY;
+            const T* rv = nullptr;
+            if (kk < nw) {
+                const int64_t p = wlo + kk;
+                lg = sWlog[kk];
+                rv = p == t ? vg : ringV + (p % eta) * DV;
+            } else if (kk < nkeys) {
+                const int r = kk - nw;
+                if (cache_row_exact(r)) {
+                    lg = sLogit[r];
+                    rv = r < lam ? cV + (int64_t)r * DV : sEv;
+                }
+            }
+            pw[u] = rv ? fast_exp(lg - m) : 0.f;
+            raw[u] = rv ? *reinterpret_cast<const uint4*>(rv + col) : make_uint4(0, 0, 0, 0);
         }
-        const float p = fast_exp(lg - m);
-        lsum += p;
-        o0 += p * to_f(rv[l]);
-        if (DV > 64) o1 += p * to_f(rv[l + 64]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const T* e = reinterpret_cast<const T*>(&raw[u]);
+#pragma unroll
+            for (int x = 0; x < EPV; ++x) o[x] += pw[u] * to_f(e[x]);
+            if ((l % LPR) == 0) lsum += pw[u];
+        }
     }
-    sO[w * DV + l] = o0;
-    if (DV > 64) sO[w * DV + l + 64] = o1;
-    if (l == 0) sRedF[4 + w] = lsum;
+    // reduce the RPW row groups of the wave, then the waves through LDS
+#pragma unroll
+    for (int x = 0; x < EPV; ++x)
+        for (int sh = LPR; sh < 64; sh <<= 1) o[x] += __shfl_xor(o[x], sh);
+    for (int sh = 1; sh < 64; sh <<= 1) lsum += __shfl_xor(lsum, sh);
+    if (sub == 0)
+#pragma unroll
+        for (int x = 0; x < EPV; ++x) sO[w * DV + col + x] = o[x];
+    if (l == 0) sRedF[8 + w] = lsum;
+    if (g == 0) sL[16 * w + c] = Lrow;
     __syncthreads();
-    // linear part and output
+
+    // ---- output ----
     {
-        const float lsum_all = sRedF[4] + sRedF[5] + sRedF[6] + sRedF[7];
-        // L[d] = sum_f H^T[d][f] phi_q[f]; threads pair up on one row d
-        const int d = tid >> 1, half = tid & 1;
-        float Ld = 0.f;
-        if (d < DV)
-            for (int f = half * (D / 2); f < (half + 1) * (D / 2); ++f) Ld += sHT[d * HT_LD + f] * sPhiQ[f];
-        Ld += __shfl_xor(Ld, 1);
         float lden = 0.f;
         for (int f = 0; f < D; ++f) lden += sPhiQ[f] * sS[f];
-        if (d < DV && half == 0) {
-            const float Od = sO[d] + sO[DV + d] + sO[2 * DV + d] + sO[3 * DV + d];
+        float lsum_all = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) lsum_all += sRedF[8 + ww];
+        for (int d = tid; d < DV; d += NT) {
+            float Od = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) Od += sO[ww * DV + d];
+            const float Ld = sL[d];
             const bool any = m != -INFINITY;
             float cm;
             if (lden > 0.f) cm = any ? fmaxf(m, logf(lden)) : logf(lden);
@@ -333,23 +418,22 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs A) {
             reinterpret_cast<T*>(A.y)[(int64_t)bh * DV + d] = from_f<T>(yv);
         }
     }
-    __syncthreads();
 
     // ---- state write-back ----
-    for (int i = tid; i < DV * D / 4; i += 256) {
-        const int d = (4 * i) / D, f = 4 * i - d * D;
-        *reinterpret_cast<float4*>(Hg + 4 * i) = *reinterpret_cast<const float4*>(sHT + d * HT_LD + f);
-    }
-    for (int f = tid; f < D; f += 256) sg[f] = sS[f];
+#pragma unroll
+    for (int i = 0; i < IT; ++i)
+        *reinterpret_cast<float4*>(Hg + (16 * w + c) * D + 16 * i + 4 * g) =
+            make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+    for (int f = tid; f < D; f += NT) sg[f] = sS[f];
     if (e_slot >= 0) {
-        for (int d = tid; d < DK; d += 256) cK[(int64_t)e_slot * DK + d] = sEk[d];
-        for (int d = tid; d < DV; d += 256) cV[(int64_t)e_slot * DV + d] = sEv[d];
+        for (int d = tid; d < DK; d += NT) cK[(int64_t)e_slot * DK + d] = sEk[d];
+        for (int d = tid; d < DV; d += NT) cV[(int64_t)e_slot * DV + d] = sEv[d];
         if (tid == 0) cpos[e_slot] = (int)e_pos;
     }
     if (eta > 0) {
         const int slot = (int)(t % eta);
-        for (int d = tid; d < DK; d += 256) ringK[(int64_t)slot * DK + d] = kg[d];
-        for (int d = tid; d < DV; d += 256) ringV[(int64_t)slot * DV + d] = vg[d];
+        for (int d = tid; d < DK; d += NT) ringK[(int64_t)slot * DK + d] = kg[d];
+        for (int d = tid; d < DV; d += NT) ringV[(int64_t)slot * DV + d] = vg[d];
     }
     if (A.folded_pos && tid == 0) {
         int fp = -1;
@@ -377,7 +461,7 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(a.BH), dim3(256), lds, stream, a);
+    hipLaunchKernelGGL(kern, dim3(a.BH), dim3(DecCfg<T, DK, PHI>::NT), lds, stream, a);
     return hipGetLastError();
 }
 
