@@ -48,9 +48,11 @@ struct ChainCfg {
     static constexpr int BUF = NB * (PHI_LD + V_LD);         // elements per batch buffer
     static constexpr int FB = sizeof(T) == 2 ? 64 : 32;      // tokens per fold batch
     static constexpr int ST_LD = FB + EPV;                   // 16-byte aligned rows
-    static constexpr int FLPT = FB * CPR / NT;               // pieces per thread per fold batch
+    static constexpr int TPW = 4 / (int)sizeof(T);           // tokens packed per 32-bit LDS word
+    static constexpr int FIPT = FB / TPW * CPR / NT;         // fold staging items per thread
+    static constexpr int FLPT = FIPT * TPW;                  // pieces per thread per fold batch
     static constexpr int NBIN = 256;                         // selection histogram
-    static_assert(NB * CPR % NT == 0 && FB * CPR % NT == 0, "batches must split evenly");
+    static_assert(NB * CPR % NT == 0 && (FB / (4 / (int)sizeof(T))) * CPR % NT == 0, "batches must split evenly");
     static_assert((D + DV) * ST_LD <= 2 * BUF, "fold staging must fit in the batch buffers");
 };
 
@@ -129,7 +131,7 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
     constexpr int D = Cfg::D, DV = Cfg::DV, NW = Cfg::NW, NT = Cfg::NT, IT = Cfg::IT, EPV = Cfg::EPV,
                   NB = Cfg::NB, TPB = Cfg::TPB, CPR = Cfg::CPR, CPHI = Cfg::CPHI, LPT = Cfg::LPT,
                   PHI_LD = Cfg::PHI_LD, V_LD = Cfg::V_LD, BUF = Cfg::BUF, FB = Cfg::FB, ST_LD = Cfg::ST_LD,
-                  FLPT = Cfg::FLPT, NBIN = Cfg::NBIN;
+                  FLPT = Cfg::FLPT, NBIN = Cfg::NBIN, TPW = Cfg::TPW, FIPT = Cfg::FIPT;
     extern __shared__ __align__(16) char smem[];
     const int lam = A.lam, eta = A.eta, n = A.n, C = A.C;
     const ChainLds lo = chain_lds<T, DK, PHI>(lam, C);
@@ -413,19 +415,24 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
             if (flag[r] == 2) foldRow[a1[r]] = r;
         __syncthreads();
         uint4 stg[FLPT];
+        // fold staging item: TPW consecutive tokens (m0 .. m0+TPW-1) x one 16-byte piece pc, so that
+        // the transposed LDS writes below are whole 32-bit words at consecutive addresses
         auto load_fold = [&](int fb) {
 #pragma unroll
-            for (int u = 0; u < FLPT; ++u) {
+            for (int u = 0; u < FIPT; ++u) {
                 const int q = tid + NT * u;
-                const int m = q / CPR, pc = q % CPR;
-                const int k = fb * FB + m;
-                uint4 val = make_uint4(0, 0, 0, 0);
-                if (k < nS) {
-                    const int s_ = cSrc[foldRow[k]];
-                    const T* p_ = pc < CPHI ? src.phi_row(s_) + pc * EPV : src.v_row(s_) + (pc - CPHI) * EPV;
-                    val = *reinterpret_cast<const uint4*>(p_);
+                const int m0 = (q % (FB / TPW)) * TPW, pc = q / (FB / TPW);
+#pragma unroll
+                for (int z = 0; z < TPW; ++z) {
+                    const int k = fb * FB + m0 + z;
+                    uint4 val = make_uint4(0, 0, 0, 0);
+                    if (k < nS) {
+                        const int s_ = cSrc[foldRow[k]];
+                        const T* p_ = pc < CPHI ? src.phi_row(s_) + pc * EPV : src.v_row(s_) + (pc - CPHI) * EPV;
+                        val = *reinterpret_cast<const uint4*>(p_);
+                    }
+                    stg[u * TPW + z] = val;
                 }
-                stg[u] = val;
             }
         };
         if (nS > 0) load_fold(0);
@@ -476,17 +483,16 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
             for (int fb = 0; fb * FB < nS; ++fb) {
                 if (fb > 0) load_fold(fb);
 #pragma unroll
-                for (int u = 0; u < FLPT; ++u) {
+                for (int u = 0; u < FIPT; ++u) {
                     const int q = tid + NT * u;
-                    const int m = q / CPR, pc = q % CPR;
-                    const T* e = reinterpret_cast<const T*>(&stg[u]);
-                    if (pc < CPHI) {
+                    const int m0 = (q % (FB / TPW)) * TPW, pc = q / (FB / TPW);
+                    T* dst0 = pc < CPHI ? stPhi + (pc * EPV) * ST_LD + m0 : stV + ((pc - CPHI) * EPV) * ST_LD + m0;
 #pragma unroll
-                        for (int x = 0; x < EPV; ++x) stPhi[(pc * EPV + x) * ST_LD + m] = e[x];
-                    } else {
-                        const int e0 = (pc - CPHI) * EPV;
+                    for (int x = 0; x < EPV; ++x) {
+                        T word[TPW];
 #pragma unroll
-                        for (int x = 0; x < EPV; ++x) stV[(e0 + x) * ST_LD + m] = e[x];
+                        for (int z = 0; z < TPW; ++z) word[z] = reinterpret_cast<const T*>(&stg[u * TPW + z])[x];
+                        *reinterpret_cast<uint32_t*>(dst0 + x * ST_LD) = *reinterpret_cast<const uint32_t*>(word);
                     }
                 }
                 __syncthreads();

@@ -203,12 +203,28 @@ __device__ __forceinline__ void phi_tile(const T* wt, int wt_ld, const Frag8<T> 
     }
 }
 
-// Stage W^T (T) in LDS: wt[j * wt_ld + d] = W[d][j], W fp32 [DK][DW] row-major.
-template <typename T>
-__device__ __forceinline__ void stage_wt(T* wt, int wt_ld, const float* __restrict__ W, int DK, int DW) {
-    for (int i = threadIdx.x; i < DK * DW; i += blockDim.x) {
-        const int d = i / DW, j = i - d * DW;
-        wt[j * wt_ld + d] = from_f<T>(W[i]);
+// Stage W^T (T) in LDS: wt[j * wt_ld + d] = W[d][j], W fp32 [DK][DW] row-major.  All of a thread's
+// 16-byte loads are issued before any store, so the copy costs one memory latency.
+template <typename T, int DK, int DW, int NT>
+__device__ __forceinline__ void stage_wt(T* wt, int wt_ld, const float* __restrict__ W) {
+    constexpr int N4 = DK * DW / 4;
+    constexpr int PER = (N4 + NT - 1) / NT;
+    float4 v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int i4 = threadIdx.x + NT * u;
+        if (i4 < N4) v[u] = reinterpret_cast<const float4*>(W)[i4];
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int i4 = threadIdx.x + NT * u;
+        if (i4 < N4) {
+            const int i = 4 * i4, d = i / DW, j = i - d * DW;
+            wt[(j + 0) * wt_ld + d] = from_f<T>(v[u].x);
+            wt[(j + 1) * wt_ld + d] = from_f<T>(v[u].y);
+            wt[(j + 2) * wt_ld + d] = from_f<T>(v[u].z);
+            wt[(j + 3) * wt_ld + d] = from_f<T>(v[u].w);
+        }
     }
 }
 

@@ -131,7 +131,7 @@ __global__ __launch_bounds__(4 * DK) void decode_kernel(DecodeArgs A) {
         const float4 h = *reinterpret_cast<const float4*>(Hg + (16 * w + c) * D + 16 * i + 4 * g);
         acc[i] = f4{h.x, h.y, h.z, h.w};
     }
-    stage_wt<T>(wt, WT_LD, A.W, DK, DW);
+    stage_wt<T, DK, DW, NT>(wt, WT_LD, A.W);
     for (int d = tid; d < D; d += NT) sS[d] = sg[d];
     for (int d = tid; d < DK; d += NT) {
         sQ[d] = to_f(qg[d]);

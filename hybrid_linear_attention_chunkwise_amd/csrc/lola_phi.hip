@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void phi_kernel(PrefillArgs A) {
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c = l & 15;
     const int n = A.n, lam = A.lam, eta = A.eta;
     const int rows = n + lam + eta;
-    stage_wt<T>(wt, WT_LD, A.W, DK, DW);
+    stage_wt<T, DK, DW, 256>(wt, WT_LD, A.W);
     __syncthreads();
     const int r = blockIdx.x * 64 + w * 16 + c;
     const T* rk = nullptr;

@@ -10,8 +10,9 @@
 //
 // Contractions run on MFMA in the transposed orientation (values x queries): the score tile K Q^T
 // comes out with the key index along the accumulator rows, which is the layout the P V^T product
-// needs for its B operand, so probabilities never leave registers.  Key and value blocks of 32 are
-// staged once per workgroup in LDS (values transposed) and shared by the four waves.
+// needs for its B operand, so probabilities never leave registers.  Key and value blocks of 64 are
+// staged once per workgroup in LDS (values transposed) and shared by the four waves; the next
+// block's 16-byte loads are in flight while the current block is used.
 #include "lola_common.hpp"
 #include "lola_internal.hpp"
 
@@ -41,7 +42,14 @@ template <typename T, int DK, int PHI>
 __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
     constexpr int D = kFeat, DV = DK, JT = DV / 16;
     constexpr int DW = (PHI == kPhiSoftmaxPM) ? D / 2 : D;
-    constexpr int WT_LD = DK + 4, KB = 32, K_LD = DK + 4, VT_LD = KB + 4;
+    constexpr int EPV = 16 / (int)sizeof(T);
+    constexpr int WT_LD = DK + 4, KB = 64, K_LD = DK + EPV, VT_LD = KB + EPV;
+    constexpr int CPK = DK / EPV;                   // 16-byte pieces per key row
+    constexpr int KPT = KB * CPK / 256;             // key pieces per thread per block
+    constexpr int TPW = 4 / (int)sizeof(T);         // keys packed per 32-bit LDS word
+    constexpr int NCG = 256 * TPW / KB;             // value column groups
+    constexpr int VD = DV / NCG;                    // value columns per thread
+    constexpr int VPT = VD / EPV;                   // value pieces per key and thread
     __shared__ __align__(16) T wt[DW * WT_LD];
     __shared__ __align__(16) T sK[KB * K_LD];
     __shared__ __align__(16) T sVT[DV * VT_LD];
@@ -74,7 +82,7 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
     const int* foldSrc = reinterpret_cast<const int*>(rec + A.L.c_fold_src);
     const T* phiStore = reinterpret_cast<const T*>(A.ws + (int64_t)bh * A.L.per_bh + A.L.phi_store);
     const T* foldVT = reinterpret_cast<const T*>(rec + A.L.c_fold_vt);
-    const int cp32 = A.L.c_pad64;
+    const int cpv = A.L.c_pad64;
 
     const T* qin = reinterpret_cast<const T*>(A.q) + (int64_t)bh * n * DK;
     const T* kin = reinterpret_cast<const T*>(A.k) + (int64_t)bh * n * DK;
@@ -85,7 +93,62 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
     const T* cV = lam > 0 ? reinterpret_cast<const T*>(A.cache_v) + (int64_t)bh * lam * DV : nullptr;
     T* yout = reinterpret_cast<T*>(A.y) + (int64_t)bh * n * DV;
 
-    stage_wt<T>(wt, WT_LD, A.W, DK, DW);
+    // exact keys of this query tile: its window band, then the chunk's cache list
+    const int64_t blo = max((int64_t)0, q0 - eta + 1);
+    const int64_t bhi = min(q0 + 63, b - 1);
+    const int nb = (eta > 0 && bhi >= blo) ? (int)(bhi - blo + 1) : 0;
+    const int NK = nb + lam;
+    const int nblk = (NK + KB - 1) / KB;
+    // key kk -> (position, band?, K row, V row); position -1 = no key
+    auto key_rows = [&](int kk, int& pos, int& band, const T*& rk, const T*& rv) {
+        pos = -1; band = 0; rk = nullptr; rv = nullptr;
+        if (kk < nb) {
+            const int64_t ps = blo + kk;
+            pos = (int)ps;
+            band = 1;
+            if (ps >= t0) { rk = kin + (ps - t0) * DK; rv = vin + (ps - t0) * DV; }
+            else { rk = ringK + (ps % eta) * DK; rv = ringV + (ps % eta) * DV; }
+        } else if (kk < NK) {
+            const int jj = kk - nb;
+            const int p = cachePos[jj];
+            if (p >= 0) {
+                pos = p;
+                const int src = cacheSrc[jj];
+                if (src < n) { rk = kin + (int64_t)src * DK; rv = vin + (int64_t)src * DV; }
+                else if (src < n + lam) { rk = cK + (int64_t)(src - n) * DK; rv = cV + (int64_t)(src - n) * DV; }
+                else { rk = ringK + (int64_t)(src - n - lam) * DK; rv = ringV + (int64_t)(src - n - lam) * DV; }
+            }
+        }
+    };
+    uint4 kst[KPT], vst[TPW][VPT];
+    int vpos[TPW], vband[TPW];
+    auto prefetch = [&](int kb) {
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) {
+            const int q = tid + 256 * u;
+            const int j = q / CPK, p = q % CPK;
+            int pos, band;
+            const T* rk;
+            const T* rv;
+            key_rows(kb * KB + j, pos, band, rk, rv);
+            kst[u] = rk ? *reinterpret_cast<const uint4*>(rk + p * EPV) : make_uint4(0, 0, 0, 0);
+        }
+        {   // values: thread -> (TPW consecutive keys, one column group)
+            const int j0 = (tid % (KB / TPW)) * TPW, cg = tid / (KB / TPW);
+#pragma unroll
+            for (int z = 0; z < TPW; ++z) {
+                const T* rk;
+                const T* rv;
+                key_rows(kb * KB + j0 + z, vpos[z], vband[z], rk, rv);
+#pragma unroll
+                for (int u = 0; u < VPT; ++u)
+                    vst[z][u] = rv ? *reinterpret_cast<const uint4*>(rv + cg * VD + u * EPV) : make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+    if (nblk > 0) prefetch(0);
+
+    stage_wt<T, DK, DW, 256>(wt, WT_LD, A.W);
     for (int d = tid; d < D; d += 256) sS[d] = snapS[d];
     for (int i = tid; i < nf; i += 256) { sFoldPos[i] = foldPos[i]; sFoldSrc[i] = foldSrc[i]; }
     __syncthreads();
@@ -104,7 +167,7 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
 #pragma unroll
     for (int ss = 0; ss < D / 32; ++ss) pf[ss] = frag_from_rows<T>(ph[2 * ss], ph[2 * ss + 1]);
 
-    // linear part: H_c^T phi(Q)^T and phi(Q) s_c
+    // linear part: H_c^T phi(Q)^T (snapshot stored in fragment order) and phi(Q) s_c
     f4 L[JT];
 #pragma unroll
     for (int J = 0; J < JT; ++J) L[J] = zero4();
@@ -128,9 +191,10 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
         for (int h2 = 0; h2 < 2; ++h2) {
             const int i = 32 * fb + 16 * h2 + c;
             sp[h2] = zero4();
+            const T* prow = i < nf ? phiStore + (int64_t)sFoldSrc[i] * D : nullptr;
 #pragma unroll
             for (int ss = 0; ss < D / 32; ++ss) {
-                const Frag8<T> af = i < nf ? load_frag(phiStore + (int64_t)sFoldSrc[i] * D, ss, g) : frag_zero<T>();
+                const Frag8<T> af = prow ? load_frag(prow, ss, g) : frag_zero<T>();
                 mma32(sp[h2], af, pf[ss]);
             }
 #pragma unroll
@@ -147,63 +211,54 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
         }
         const Frag8<T> bw = frag_from_acc<T>(sp[0], sp[1]);
 #pragma unroll
-        for (int J = 0; J < JT; ++J) mma32(L[J], load_frag(foldVT + (int64_t)(16 * J + c) * cp32, fb, g), bw);
+        for (int J = 0; J < JT; ++J) mma32(L[J], load_frag(foldVT + (int64_t)(16 * J + c) * cpv, fb, g), bw);
     }
     lden += sum_groups(lden_f);
 
-    // exact part: the window band of this query tile, then the chunk's cache list
-    const int64_t blo = max((int64_t)0, q0 - eta + 1);
-    const int64_t bhi = min(q0 + 63, b - 1);
-    const int nb = (eta > 0 && bhi >= blo) ? (int)(bhi - blo + 1) : 0;
-    const int NK = nb + lam;
+    // exact part: blocks of KB keys staged in LDS (keys row-major, values transposed), the next
+    // block's loads in flight while this one is used
     const float scale = 1.0f / sqrtf((float)DK);
     float m_run = -INFINITY, l_part = 0.f;
     f4 O[JT];
 #pragma unroll
     for (int J = 0; J < JT; ++J) O[J] = zero4();
 
-    for (int kb = 0; kb * KB < NK; ++kb) {
-        {   // stage 32 keys: thread -> (key j, eighth p) of the row
-            const int j = tid >> 3, p = tid & 7;
-            const int kk = kb * KB + j;
-            const T* rk = nullptr;
-            const T* rv = nullptr;
-            int pos = -1, band = 0;
-            if (kk < nb) {
-                const int64_t ps = blo + kk;
-                pos = (int)ps;
-                band = 1;
-                if (ps >= t0) { rk = kin + (ps - t0) * DK; rv = vin + (ps - t0) * DV; }
-                else { rk = ringK + (ps % eta) * DK; rv = ringV + (ps % eta) * DV; }
-            } else if (kk < NK) {
-                const int jj = kk - nb;
-                pos = cachePos[jj];
-                if (pos >= 0) {
-                    const int src = cacheSrc[jj];
-                    if (src < n) { rk = kin + (int64_t)src * DK; rv = vin + (int64_t)src * DV; }
-                    else if (src < n + lam) { rk = cK + (int64_t)(src - n) * DK; rv = cV + (int64_t)(src - n) * DV; }
-                    else { rk = ringK + (int64_t)(src - n - lam) * DK; rv = ringV + (int64_t)(src - n - lam) * DV; }
+    for (int kb = 0; kb < nblk; ++kb) {
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) {
+            const int q = tid + 256 * u;
+            const int j = q / CPK, p = q % CPK;
+            *reinterpret_cast<uint4*>(sK + j * K_LD + p * EPV) = kst[u];
+        }
+        {   // transposed value block: whole 32-bit words, consecutive threads -> consecutive words
+            const int j0 = (tid % (KB / TPW)) * TPW, cg = tid / (KB / TPW);
+#pragma unroll
+            for (int u = 0; u < VPT; ++u)
+#pragma unroll
+                for (int x = 0; x < EPV; ++x) {
+                    T word[TPW];
+#pragma unroll
+                    for (int z = 0; z < TPW; ++z) word[z] = reinterpret_cast<const T*>(&vst[z][u])[x];
+                    *reinterpret_cast<uint32_t*>(sVT + (cg * VD + u * EPV + x) * VT_LD + j0) =
+                        *reinterpret_cast<const uint32_t*>(word);
                 }
-            }
-            constexpr int KE = DK / 8, VE = DV / 8;
+            if (cg == 0)
 #pragma unroll
-            for (int e = 0; e < KE; ++e) sK[j * K_LD + p * KE + e] = rk ? rk[p * KE + e] : from_f<T>(0.f);
-#pragma unroll
-            for (int e = 0; e < VE; ++e) sVT[(p * VE + e) * VT_LD + j] = rv ? rv[p * VE + e] : from_f<T>(0.f);
-            if (p == 0) { sKeyPos[j] = rk ? pos : -1; sKeyBand[j] = band; }
+                for (int z = 0; z < TPW; ++z) { sKeyPos[j0 + z] = vpos[z]; sKeyBand[j0 + z] = vband[z]; }
         }
         __syncthreads();
+        if (kb + 1 < nblk) prefetch(kb + 1);
         if (wave_active) {
-            f4 st[2];
+            f4 st[KB / 16];
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
+            for (int kt = 0; kt < KB / 16; ++kt) {
                 st[kt] = zero4();
 #pragma unroll
                 for (int ss = 0; ss < DK / 32; ++ss) mma32(st[kt], load_frag(sK + (16 * kt + c) * K_LD, ss, g), qf[ss]);
             }
             float bmax = -INFINITY;
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int kt = 0; kt < KB / 16; ++kt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int j = 16 * kt + 4 * g + r;
@@ -225,7 +280,7 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
                 for (int r = 0; r < 4; ++r) O[J][r] *= alpha;
             l_part *= alpha;
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int kt = 0; kt < KB / 16; ++kt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float p = (st[kt][r] != -INFINITY) ? fast_exp(st[kt][r] - m_new) : 0.f;
@@ -233,9 +288,12 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
                     l_part += p;
                 }
             m_run = m_new;
-            const Frag8<T> bp = frag_from_acc<T>(st[0], st[1]);
 #pragma unroll
-            for (int J = 0; J < JT; ++J) mma32(O[J], load_frag(sVT + (16 * J + c) * VT_LD, 0, g), bp);
+            for (int k2 = 0; k2 < KB / 32; ++k2) {
+                const Frag8<T> bp = frag_from_acc<T>(st[2 * k2], st[2 * k2 + 1]);
+#pragma unroll
+                for (int J = 0; J < JT; ++J) mma32(O[J], load_frag(sVT + (16 * J + c) * VT_LD, k2, g), bp);
+            }
         }
         __syncthreads();
     }
@@ -258,10 +316,11 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
 }
 
 // Commit: move the final cache members' K/V into the state's slots, then write the last eta input
-// tokens into the window ring.  One workgroup per (sequence, head); runs after the read-out.
+// tokens into the window ring.  One workgroup per (sequence, head); runs after the read-out.  Rows
+// move as 16-byte pieces, several loads in flight per thread.
 template <typename T, int DK>
 __global__ __launch_bounds__(256) void commit_kernel(PrefillArgs A) {
-    constexpr int DV = DK;
+    constexpr int DV = DK, EPV = 16 / (int)sizeof(T), CPR = DK / EPV, UN = 4;
     const int bh = blockIdx.x, tid = threadIdx.x;
     const int n = A.n, eta = A.eta, lam = A.lam;
     const int64_t t0 = A.t0;
@@ -276,12 +335,27 @@ __global__ __launch_bounds__(256) void commit_kernel(PrefillArgs A) {
         const T* ringK = eta > 0 ? reinterpret_cast<const T*>(A.win_k) + (int64_t)bh * eta * DK : nullptr;
         const T* ringV = eta > 0 ? reinterpret_cast<const T*>(A.win_v) + (int64_t)bh * eta * DV : nullptr;
         int32_t* cpos = A.cache_pos + (int64_t)bh * lam;
-        for (int i = tid; i < lam * DK; i += 256) {
-            const int j = i / DK, e = i - j * DK;
-            const int src = fs[j];
-            if (src < 0 || src == n + j) continue;           // empty, or a member that kept its slot
-            if (src < n) { cK[i] = kin[(int64_t)src * DK + e]; cV[(int64_t)j * DV + e] = vin[(int64_t)src * DV + e]; }
-            else { const int r = src - n - lam; cK[i] = ringK[(int64_t)r * DK + e]; cV[(int64_t)j * DV + e] = ringV[(int64_t)r * DV + e]; }
+        const int items = lam * 2 * CPR;                 // (slot, K or V, piece)
+        for (int i0 = tid; i0 < items; i0 += 256 * UN) {
+            uint4 val[UN];
+            T* dst[UN];
+#pragma unroll
+            for (int u = 0; u < UN; ++u) {
+                const int it = i0 + 256 * u;
+                dst[u] = nullptr;
+                if (it >= items) continue;
+                const int j = it / (2 * CPR), rem = it % (2 * CPR), isv = rem / CPR, p = rem % CPR;
+                const int src = fs[j];
+                if (src < 0 || src == n + j) continue;    // empty, or a member that kept its slot
+                const T* row;
+                if (src < n) row = (isv ? vin : kin) + (int64_t)src * DK;
+                else row = (isv ? ringV : ringK) + (int64_t)(src - n - lam) * DK;
+                val[u] = *reinterpret_cast<const uint4*>(row + p * EPV);
+                dst[u] = (isv ? cV : cK) + (int64_t)j * DK + p * EPV;
+            }
+#pragma unroll
+            for (int u = 0; u < UN; ++u)
+                if (dst[u]) *reinterpret_cast<uint4*>(dst[u]) = val[u];
         }
         for (int j = tid; j < lam; j += 256) cpos[j] = fp[j];
     }
@@ -291,12 +365,24 @@ __global__ __launch_bounds__(256) void commit_kernel(PrefillArgs A) {
         T* ringV = reinterpret_cast<T*>(A.win_v) + (int64_t)bh * eta * DV;
         const int64_t plo = max(t0, t0 + n - eta);
         const int cnt = (int)(t0 + n - plo);
-        for (int i = tid; i < cnt * DK; i += 256) {
-            const int x = i / DK, e = i - x * DK;
-            const int64_t pos = plo + x;
-            const int slot = (int)(pos % eta);
-            ringK[(int64_t)slot * DK + e] = kin[(pos - t0) * DK + e];
-            ringV[(int64_t)slot * DV + e] = vin[(pos - t0) * DV + e];
+        const int items = cnt * 2 * CPR;
+        for (int i0 = tid; i0 < items; i0 += 256 * UN) {
+            uint4 val[UN];
+            T* dst[UN];
+#pragma unroll
+            for (int u = 0; u < UN; ++u) {
+                const int it = i0 + 256 * u;
+                dst[u] = nullptr;
+                if (it >= items) continue;
+                const int x = it / (2 * CPR), rem = it % (2 * CPR), isv = rem / CPR, p = rem % CPR;
+                const int64_t pos = plo + x;
+                const int slot = (int)(pos % eta);
+                val[u] = *reinterpret_cast<const uint4*>((isv ? vin : kin) + (pos - t0) * DK + p * EPV);
+                dst[u] = (isv ? ringV : ringK) + (int64_t)slot * DK + p * EPV;
+            }
+#pragma unroll
+            for (int u = 0; u < UN; ++u)
+                if (dst[u]) *reinterpret_cast<uint4*>(dst[u]) = val[u];
         }
     }
 }
