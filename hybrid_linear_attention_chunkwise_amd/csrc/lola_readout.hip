@@ -161,60 +161,6 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
     Frag8<T> qf[DK / 32];
 #pragma unroll
     for (int ss = 0; ss < DK / 32; ++ss) qf[ss] = qvalid ? load_frag(qin + (tq - t0) * DK, ss, g) : frag_zero<T>();
-    float ph[D / 16][4];
-    phi_tile<T, DK, PHI>(wt, WT_LD, qf, ph);
-    Frag8<T> pf[D / 32];
-#pragma unroll
-    for (int ss = 0; ss < D / 32; ++ss) pf[ss] = frag_from_rows<T>(ph[2 * ss], ph[2 * ss + 1]);
-
-    // linear part: H_c^T phi(Q)^T (snapshot stored in fragment order) and phi(Q) s_c
-    f4 L[JT];
-#pragma unroll
-    for (int J = 0; J < JT; ++J) L[J] = zero4();
-#pragma unroll
-    for (int ss = 0; ss < D / 32; ++ss)
-#pragma unroll
-        for (int J = 0; J < JT; ++J)
-            mma32(L[J], *reinterpret_cast<const Frag8<T>*>(snapH + ((int64_t)(J * (D / 32) + ss) * 64 + l) * 8), pf[ss]);
-    float lden = 0.f;
-#pragma unroll
-    for (int ft = 0; ft < D / 16; ++ft)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) lden += ph[ft][r] * sS[16 * ft + 4 * g + r];
-    lden = sum_groups(lden);
-
-    // tokens folded by this chunk become linear at tau = max(exit time, chunk start)
-    float lden_f = 0.f;
-    for (int fb = 0; fb * 32 < nf; ++fb) {
-        f4 sp[2];
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-            const int i = 32 * fb + 16 * h2 + c;
-            sp[h2] = zero4();
-            const T* prow = i < nf ? phiStore + (int64_t)sFoldSrc[i] * D : nullptr;
-#pragma unroll
-            for (int ss = 0; ss < D / 32; ++ss) {
-                const Frag8<T> af = prow ? load_frag(prow, ss, g) : frag_zero<T>();
-                mma32(sp[h2], af, pf[ss]);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int ii = 32 * fb + 16 * h2 + 4 * g + r;
-                bool ok = false;
-                if (ii < nf) {
-                    const int64_t tau = max((int64_t)sFoldPos[ii] + eta, a);
-                    ok = tau <= tq;
-                }
-                sp[h2][r] = ok ? sp[h2][r] : 0.f;
-                lden_f += sp[h2][r];
-            }
-        }
-        const Frag8<T> bw = frag_from_acc<T>(sp[0], sp[1]);
-#pragma unroll
-        for (int J = 0; J < JT; ++J) mma32(L[J], load_frag(foldVT + (int64_t)(16 * J + c) * cpv, fb, g), bw);
-    }
-    lden += sum_groups(lden_f);
-
     // exact part: blocks of KB keys staged in LDS (keys row-major, values transposed), the next
     // block's loads in flight while this one is used
     const float scale = 1.0f / sqrtf((float)DK);
@@ -297,6 +243,61 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
         }
         __syncthreads();
     }
+
+    // linear part, after the exact loop so its registers are not live during it
+    float ph[D / 16][4];
+    phi_tile<T, DK, PHI>(wt, WT_LD, qf, ph);
+    Frag8<T> pf[D / 32];
+#pragma unroll
+    for (int ss = 0; ss < D / 32; ++ss) pf[ss] = frag_from_rows<T>(ph[2 * ss], ph[2 * ss + 1]);
+
+    // linear part: H_c^T phi(Q)^T (snapshot stored in fragment order) and phi(Q) s_c
+    f4 L[JT];
+#pragma unroll
+    for (int J = 0; J < JT; ++J) L[J] = zero4();
+#pragma unroll
+    for (int ss = 0; ss < D / 32; ++ss)
+#pragma unroll
+        for (int J = 0; J < JT; ++J)
+            mma32(L[J], *reinterpret_cast<const Frag8<T>*>(snapH + ((int64_t)(J * (D / 32) + ss) * 64 + l) * 8), pf[ss]);
+    float lden = 0.f;
+#pragma unroll
+    for (int ft = 0; ft < D / 16; ++ft)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) lden += ph[ft][r] * sS[16 * ft + 4 * g + r];
+    lden = sum_groups(lden);
+
+    // tokens folded by this chunk become linear at tau = max(exit time, chunk start)
+    float lden_f = 0.f;
+    for (int fb = 0; fb * 32 < nf; ++fb) {
+        f4 sp[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const int i = 32 * fb + 16 * h2 + c;
+            sp[h2] = zero4();
+            const T* prow = i < nf ? phiStore + (int64_t)sFoldSrc[i] * D : nullptr;
+#pragma unroll
+            for (int ss = 0; ss < D / 32; ++ss) {
+                const Frag8<T> af = prow ? load_frag(prow, ss, g) : frag_zero<T>();
+                mma32(sp[h2], af, pf[ss]);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int ii = 32 * fb + 16 * h2 + 4 * g + r;
+                bool ok = false;
+                if (ii < nf) {
+                    const int64_t tau = max((int64_t)sFoldPos[ii] + eta, a);
+                    ok = tau <= tq;
+                }
+                sp[h2][r] = ok ? sp[h2][r] : 0.f;
+                lden_f += sp[h2][r];
+            }
+        }
+        const Frag8<T> bw = frag_from_acc<T>(sp[0], sp[1]);
+#pragma unroll
+        for (int J = 0; J < JT; ++J) mma32(L[J], load_frag(foldVT + (int64_t)(16 * J + c) * cpv, fb, g), bw);
+    }
+    lden += sum_groups(lden_f);
 
     // joint normalisation with a common scale exp(-cmax), cmax = max(m, log L_den)
     const float lsum = sum_groups(l_part);
