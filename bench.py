@@ -64,15 +64,21 @@ def decode_bytes_per_seq_head(wl) -> int:
 
 
 def load_traffic(kernel: str, src_hash: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it matches the source."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it matches the source.
+
+    The summary's table has one row per kernel: name, workload, grid, launches, FETCH_SIZE KiB,
+    WRITE_SIZE KiB, calibrated bytes per launch, kernel source hash.  A row taken from other kernel
+    sources than these is stale and ignored.
+    """
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        d = json.load(f)
-    if d.get("kernel_source_hash") != src_hash:
-        return None
-    return d.get("hbm_bytes_per_launch")
+        for line in f:
+            cols = [c.strip() for c in line.strip().strip("|").split("|")]
+            if len(cols) == 8 and cols[0] == kernel and cols[7] == src_hash:
+                return int(cols[6])
+    return None
 
 
 def bench_prefill(args, lola, torch, wl):
@@ -210,6 +216,9 @@ def main() -> int:
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: every (sequence, head) is independent, so a multi-GPU "
@@ -224,8 +233,22 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     lola._b.load()
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n * 4}))
+        return 0
     wl = CONFIGS[2]
     src_hash = kernel_source_hash()
+    if args.no_prefill:        # profiling mode: the decode workload only
+        dwl = CONFIGS[4]
+        best, kern_ms = bench_decode(args, lola, torch, dwl)
+        print(json.dumps({"decode_ms_per_step": best / dwl.decode_steps * 1e3, "decode_kernel_ms": kern_ms}))
+        return 0
     elapsed, kern = bench_prefill(args, lola, torch, wl)
     ms_per_step = elapsed / args.steps * 1e3
     tokens = wl.B * wl.n
