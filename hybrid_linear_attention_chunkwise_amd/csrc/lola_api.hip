@@ -61,6 +61,8 @@ WsLayout make_layout(const lola_state* st, int64_t n, int32_t C) {
     L.phi_store = p; p = rup(p + (n + lam + st->eta) * D * esz, 256);
     L.slot_pos = p;  p = rup(p + (lam + 1) * 4, 256);
     L.slot_src = p;  p = rup(p + (lam + 1) * 4, 256);
+    L.mir_phi = p;   p = rup(p + rup(lam, 16) * D * esz, 256);
+    L.mir_v = p;     p = rup(p + rup(lam, 16) * dv * esz, 256);
     L.chunk0 = p;
     int64_t q = 0;
     L.c_snap_h = q;    q = rup(q + dv * D * esz, 256);

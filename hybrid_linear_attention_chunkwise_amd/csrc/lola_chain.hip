@@ -11,17 +11,19 @@
 //   6. fold: H += Phi_S^T V_S, s += sum Phi_S.
 //
 // H lives in registers for the whole call as MFMA accumulators: one wave per 16 value columns of H
-// (D x d_v, feature rows, value columns), all feature rows.  The SRE numerators are computed
-// transposed, H^T Phi_E^T, with those accumulators used directly as the MFMA A operand (see
-// lola_common.hpp), so each candidate is one accumulator column and its squared error over the
-// wave's value rows needs one cross-lane sum.  The wave partials are summed in a fixed order, so
-// results are deterministic.  Selection keeps the lambda largest keys with a 256-bin histogram of SRE
-// and an exact rank only inside the boundary bin; prefix counts use wave ballots, not LDS scans.
+// (D x d_v, feature rows, value columns), all feature rows.  At each chunk start every wave converts
+// its accumulators into operand fragments of H^T (see lola_common.hpp) and writes them twice: to the
+// chunk's snapshot for the read-out kernel and to LDS.  Scoring then runs candidate-major: wave w
+// takes candidate tiles w, w + NW, ..., reads H^T from LDS as the A operand and the candidates'
+// features straight from memory as the B operand, so each candidate's whole recall H^T phi(k), and
+// with it the SRE, is formed inside one wave.  Selection keeps the lambda largest keys with a
+// 256-bin histogram of SRE and an exact rank only inside the boundary bin; prefix counts use wave
+// ballots, not LDS scans.  The fold stages the folded rows transposed in LDS and accumulates
+// H += Phi_S^T V_S into the same registers.
 //
 // Every token's features are computed once and stored by source index (the same index that locates
 // its K/V), so a token that enters the cache is never copied: a slot is just (position, source).
-// Candidate rows reach LDS in double-buffered 32 KB batches of 16-byte loads; the first batch of the
-// next chunk is fetched while the current chunk folds.
+// The first scoring tile of the next chunk is fetched while the current chunk folds.
 #include "lola_common.hpp"
 #include "lola_internal.hpp"
 
@@ -38,30 +40,46 @@ struct ChainCfg {
     static constexpr int IT = D / 16;                        // accumulator tiles along D
     static constexpr int EPV = 16 / (int)sizeof(T);          // elements per 16-byte piece
     static constexpr int ROWB = (D + DV) * (int)sizeof(T);   // bytes of one candidate row (phi | v)
-    static constexpr int NB = ROWB <= 512 ? 64 : 32;         // candidate rows per batch
-    static constexpr int TPB = NB / 16;                      // tiles per batch
     static constexpr int CPR = ROWB / 16;                    // 16-byte pieces per row
     static constexpr int CPHI = D / EPV;                     // pieces holding phi
-    static constexpr int LPT = NB * CPR / NT;                // pieces per thread per batch
-    static constexpr int PHI_LD = D + EPV;                   // LDS row strides (keep 16-byte alignment)
-    static constexpr int V_LD = DV + EPV;
-    static constexpr int BUF = NB * (PHI_LD + V_LD);         // elements per batch buffer
     static constexpr int FB = sizeof(T) == 2 ? 64 : 32;      // tokens per fold batch
     static constexpr int ST_LD = FB + EPV;                   // 16-byte aligned rows
+    static constexpr int STAGE = (D + DV) * ST_LD;           // fold staging elements: [D + DV][ST_LD]
+    static constexpr int HFR = NW * (D / 32) * 64 * 8;       // H^T copy, MFMA fragment order
     static constexpr int TPW = 4 / (int)sizeof(T);           // tokens packed per 32-bit LDS word
     static constexpr int FIPT = FB / TPW * CPR / NT;         // fold staging items per thread
     static constexpr int FLPT = FIPT * TPW;                  // pieces per thread per fold batch
     static constexpr int NBIN = 256;                         // selection histogram
-    static_assert(NB * CPR % NT == 0 && (FB / (4 / (int)sizeof(T))) * CPR % NT == 0, "batches must split evenly");
-    static_assert((D + DV) * ST_LD <= 2 * BUF, "fold staging must fit in the batch buffers");
+    static_assert((FB / (4 / (int)sizeof(T))) * CPR % NT == 0, "fold batches must split evenly");
 };
 
-// Rows of the per-candidate arrays: lam + C rounded up to 64 (a whole number of batches).
-__host__ __device__ inline int cand_rows(int lam, int C) { return ((lam + C + 63) / 64) * 64; }
+// Four consecutive elements of a value row (one accumulator column's rows 4g .. 4g + 3).
+template <typename T> struct Quad;
+template <> struct Quad<float> { f4 v; };
+template <> struct Quad<bf16> { bf16x4 v; };
+__device__ __forceinline__ Quad<float> load_quad(const float* p) { return {*reinterpret_cast<const f4*>(p)}; }
+__device__ __forceinline__ Quad<bf16> load_quad(const bf16* p) { return {*reinterpret_cast<const bf16x4*>(p)}; }
+__device__ __forceinline__ void store_quad(float* p, const Quad<float>& q) { *reinterpret_cast<f4*>(p) = q.v; }
+__device__ __forceinline__ void store_quad(bf16* p, const Quad<bf16>& q) { *reinterpret_cast<bf16x4*>(p) = q.v; }
+
+// One lane's share of a 16-candidate scoring tile: the features of candidate c = lane % 16 as the B
+// operand (all of D), and the value entries that meet the lane's accumulator rows (one Quad per
+// 16-row tile of H^T).
+template <typename T, int D, int NW>
+struct CandTile {
+    Frag8<T> f[D / 32];
+    Quad<T> v[NW];
+};
+
+// Candidate table: cache slots in rows 0 .. lam-1, the leaving tokens from row lam16 = lam rounded up
+// to 16, so a 16-row scoring tile never mixes the two.  Rows of the per-candidate arrays: lam16 + C
+// rounded up to 64 (whole ballot groups and tiles).
+__host__ __device__ inline int x_base(int lam) { return (lam + 15) & ~15; }
+__host__ __device__ inline int cand_rows(int lam, int C) { return ((x_base(lam) + C + 63) / 64) * 64; }
 
 struct ChainLds {
-    size_t buf, s, slot_pos, slot_src, c_src, c_pos, key, aux, flag, a1, a2, a3, free_list, fold_row,
-        part, den, hist, tmp, total;
+    size_t stage, hcopy, s, slot_pos, slot_src, c_src, c_pos, key, aux, flag, a1, a2, a3, fold_row,
+        ent_row, slot_of_x, hist, tmp, total;
 };
 
 __host__ __device__ inline size_t al16(size_t x) { return (x + 15) & ~size_t(15); }
@@ -72,7 +90,8 @@ __host__ __device__ inline ChainLds chain_lds(int lam, int C) {
     const int nr = cand_rows(lam, C);
     ChainLds o;
     size_t p = 0;
-    o.buf = p;       p = al16(p + sizeof(T) * 2 * Cfg::BUF);
+    o.stage = p;     p = al16(p + sizeof(T) * Cfg::STAGE);
+    o.hcopy = p;     p = al16(p + sizeof(T) * Cfg::HFR);
     o.s = p;         p = al16(p + sizeof(float) * Cfg::D);
     o.slot_pos = p;  p = al16(p + sizeof(int) * (lam + 1));
     o.slot_src = p;  p = al16(p + sizeof(int) * (lam + 1));
@@ -84,10 +103,9 @@ __host__ __device__ inline ChainLds chain_lds(int lam, int C) {
     o.a1 = p;        p = al16(p + sizeof(int) * nr);
     o.a2 = p;        p = al16(p + sizeof(int) * (lam + 1));
     o.a3 = p;        p = al16(p + sizeof(int) * (C + 1));
-    o.free_list = p; p = al16(p + sizeof(int) * (lam + 1));
     o.fold_row = p;  p = al16(p + sizeof(int) * (C + 1));
-    o.part = p;      p = al16(p + sizeof(float) * Cfg::NW * nr);
-    o.den = p;       p = al16(p + sizeof(float) * nr);
+    o.ent_row = p;   p = al16(p + sizeof(int) * (C + 1));
+    o.slot_of_x = p; p = al16(p + sizeof(int) * (C + 1));
     o.hist = p;      p = al16(p + sizeof(int) * (Cfg::NBIN + 4));
     o.tmp = p;       p = al16(p + sizeof(int) * 32);
     o.total = p;
@@ -129,13 +147,13 @@ template <typename T, int DK, int PHI>
 __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
     using Cfg = ChainCfg<T, DK, PHI>;
     constexpr int D = Cfg::D, DV = Cfg::DV, NW = Cfg::NW, NT = Cfg::NT, IT = Cfg::IT, EPV = Cfg::EPV,
-                  NB = Cfg::NB, TPB = Cfg::TPB, CPR = Cfg::CPR, CPHI = Cfg::CPHI, LPT = Cfg::LPT,
-                  PHI_LD = Cfg::PHI_LD, V_LD = Cfg::V_LD, BUF = Cfg::BUF, FB = Cfg::FB, ST_LD = Cfg::ST_LD,
-                  FLPT = Cfg::FLPT, NBIN = Cfg::NBIN, TPW = Cfg::TPW, FIPT = Cfg::FIPT;
+                  CPHI = Cfg::CPHI, FB = Cfg::FB, ST_LD = Cfg::ST_LD, FLPT = Cfg::FLPT, NBIN = Cfg::NBIN,
+                  TPW = Cfg::TPW, FIPT = Cfg::FIPT;
     extern __shared__ __align__(16) char smem[];
     const int lam = A.lam, eta = A.eta, n = A.n, C = A.C;
     const ChainLds lo = chain_lds<T, DK, PHI>(lam, C);
-    T* bufs = reinterpret_cast<T*>(smem + lo.buf);
+    T* stage = reinterpret_cast<T*>(smem + lo.stage);
+    T* hcopy = reinterpret_cast<T*>(smem + lo.hcopy);
     float* sS = reinterpret_cast<float*>(smem + lo.s);
     int* slotPos = reinterpret_cast<int*>(smem + lo.slot_pos);
     int* slotSrc = reinterpret_cast<int*>(smem + lo.slot_src);
@@ -147,10 +165,9 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
     int* a1 = reinterpret_cast<int*>(smem + lo.a1);
     int* a2 = reinterpret_cast<int*>(smem + lo.a2);
     int* a3 = reinterpret_cast<int*>(smem + lo.a3);
-    int* freeList = reinterpret_cast<int*>(smem + lo.free_list);
     int* foldRow = reinterpret_cast<int*>(smem + lo.fold_row);
-    float* part = reinterpret_cast<float*>(smem + lo.part);
-    float* sDen = reinterpret_cast<float*>(smem + lo.den);
+    int* entRow = reinterpret_cast<int*>(smem + lo.ent_row);
+    int* slotOfX = reinterpret_cast<int*>(smem + lo.slot_of_x);
     int* hist = reinterpret_cast<int*>(smem + lo.hist);
     int* tmp = reinterpret_cast<int*>(smem + lo.tmp);
 
@@ -158,6 +175,8 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c = l & 15;
     const int64_t t0 = A.t0;
     const int nrp = cand_rows(lam, C);
+    const int xb = x_base(lam);                           // first leaving-token row of the table
+    const int ct = xb >> 4;                               // scoring tiles that hold cache slots
 
     char* wsb = A.ws + (int64_t)bh * A.L.per_bh;
     Sources<T, DK> src;
@@ -165,6 +184,8 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
     src.cV = lam > 0 ? reinterpret_cast<const T*>(A.cache_v) + (int64_t)bh * lam * DV : nullptr;
     src.ringV = eta > 0 ? reinterpret_cast<const T*>(A.win_v) + (int64_t)bh * eta * DV : nullptr;
     src.phi = reinterpret_cast<const T*>(wsb + A.L.phi_store);
+    T* mirPhi = reinterpret_cast<T*>(wsb + A.L.mir_phi);
+    const int mirVoff = (int)((A.L.mir_v - A.L.mir_phi) / (int64_t)sizeof(T));   // mir_v - mir_phi
     src.n = n;
     src.lam = lam;
     const int32_t* cPosState = lam > 0 ? A.cache_pos + (int64_t)bh * lam : nullptr;
@@ -176,15 +197,15 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
         xlo = a - eta > 0 ? a - eta : 0;
         return b - eta > xlo ? (int)(b - eta - xlo) : 0;
     };
-    // candidate table of chunk ch: cache slots (rows 0..lam-1) then leaving tokens (rows lam..)
+    // candidate table of chunk ch: cache slots (rows 0..lam-1) then leaving tokens (rows xb..)
     auto build_table = [&](int ch) {
         int64_t xlo;
         const int nX = chunk_x(ch, xlo);
         for (int r = tid; r < nrp; r += NT) {
             int s_ = -1, p_ = -1, f = 0;
             if (r < lam) { s_ = slotSrc[r]; p_ = slotPos[r]; f = p_ >= 0; }
-            else if (r < lam + nX) {
-                const int64_t pos = xlo + (r - lam);
+            else if (r >= xb && r < xb + nX) {
+                const int64_t pos = xlo + (r - xb);
                 p_ = (int)pos;
                 s_ = pos >= t0 ? (int)(pos - t0) : n + lam + (int)(pos % eta);
                 f = 1;
@@ -194,32 +215,82 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
             flag[r] = f;
         }
     };
-    uint4 stage[LPT];
-    auto load_batch = [&](int bt, int NR) {
+    // Scoring tile j: candidates in table rows 16j .. 16j + 15, one per lane column c.  Cache tiles
+    // (j < ct) come from the slot mirror, where features and values already sit in operand and
+    // accumulator order (one 16-byte or 8-byte piece per lane and register, contiguous across the
+    // wave).  Leaving-token tiles come from their rows; a lane without a candidate reads input row 0
+    // instead, so the loads need no branch (its column of the products is never used).
+    auto load_tile = [&](CandTile<T, D, NW>& t, int j) {
+        if (j < ct) {
+            const T* b = mirPhi + ((int64_t)j * (D / 32) * 64 + l) * 8;
 #pragma unroll
-        for (int u = 0; u < LPT; ++u) {
-            const int q = tid + NT * u;
-            const int row = bt * NB + q / CPR, pc = q % CPR;
-            uint4 val = make_uint4(0, 0, 0, 0);
-            if (row < NR && flag[row]) {
-                const int s_ = cSrc[row];
-                const T* p_ = pc < CPHI ? src.phi_row(s_) + pc * EPV : src.v_row(s_) + (pc - CPHI) * EPV;
-                val = *reinterpret_cast<const uint4*>(p_);
+            for (int ss = 0; ss < D / 32; ++ss) t.f[ss] = *reinterpret_cast<const Frag8<T>*>(b + ss * 64 * 8);
+            const T* bv = mirPhi + mirVoff + ((int64_t)j * NW * 64 + l) * 4;
+#pragma unroll
+            for (int wv = 0; wv < NW; ++wv) t.v[wv] = load_quad(bv + wv * 64 * 4);
+        } else {
+            const int row = 16 * j + c;                       // < nrp: tiles never pass the table
+            const int f = flag[row], s0 = cSrc[row];
+            const int s_ = f != 0 ? s0 : 0;
+            const T* pr = src.phi_row(s_);
+#pragma unroll
+            for (int ss = 0; ss < D / 32; ++ss) t.f[ss] = load_frag(pr, ss, g);
+            const T* vr = src.v_row(s_) + 4 * g;
+#pragma unroll
+            for (int wv = 0; wv < NW; ++wv) t.v[wv] = load_quad(vr + 16 * wv);
+        }
+    };
+    // Lane (g, c) of a tile's registers holds exactly the pieces of candidate c that belong at lane
+    // (g, slot % 16) of the slot's mirror tile: this writes them there.
+    auto tile_to_slot = [&](const CandTile<T, D, NW>& t, int slot) {
+        T* b = mirPhi + ((int64_t)(slot >> 4) * (D / 32) * 64 + g * 16 + (slot & 15)) * 8;
+#pragma unroll
+        for (int ss = 0; ss < D / 32; ++ss) *reinterpret_cast<Frag8<T>*>(b + ss * 64 * 8) = t.f[ss];
+        T* bv = mirPhi + mirVoff + ((int64_t)(slot >> 4) * NW * 64 + g * 16 + (slot & 15)) * 4;
+#pragma unroll
+        for (int wv = 0; wv < NW; ++wv) store_quad(bv + wv * 64 * 4, t.v[wv]);
+    };
+    // Copy rows into the slot mirror from their sources: info(e, slot, source) names item e; a
+    // negative source skips it.  A row is QPR four-element pieces (features, then values); each
+    // thread loads MU pieces before it stores any, so a round costs one memory latency.
+    constexpr int QPR = D / 4 + DV / 4;
+    constexpr int MU = 4;
+    auto rows_to_mirror = [&](int nrows, auto&& info) {
+        for (int q0 = 0; q0 < nrows * QPR; q0 += NT * MU) {
+            Quad<T> qv[MU];
+            int doff[MU];                                     // element offset from mir_phi, -1: none
+#pragma unroll
+            for (int u = 0; u < MU; ++u) {
+                const int q = q0 + tid + NT * u;
+                doff[u] = -1;
+                if (q < nrows * QPR) {
+                    const int e = q / QPR, it = q - e * QPR;
+                    int slot, s_;
+                    info(e, slot, s_);
+                    if (s_ >= 0) {
+                        const int tile = slot >> 4, cc = slot & 15;
+                        if (it < D / 4) {                     // feature piece (ss, h, gg)
+                            const int ss = it >> 3, h = (it >> 2) & 1, gg = it & 3;
+                            qv[u] = load_quad(src.phi_row(s_) + 32 * ss + 16 * h + 4 * gg);
+                            doff[u] = ((tile * (D / 32) + ss) * 64 + gg * 16 + cc) * 8 + 4 * h;
+                        } else {                              // value piece (wv, gg)
+                            const int iv = it - D / 4, wv = iv >> 2, gg = iv & 3;
+                            qv[u] = load_quad(src.v_row(s_) + 16 * wv + 4 * gg);
+                            doff[u] = mirVoff + ((tile * NW + wv) * 64 + gg * 16 + cc) * 4;
+                        }
+                    }
+                }
             }
-            stage[u] = val;
-        }
-    };
-    auto store_batch = [&](int bi) {
-        T* bphi = bufs + bi * BUF;
-        T* bv = bphi + NB * PHI_LD;
 #pragma unroll
-        for (int u = 0; u < LPT; ++u) {
-            const int q = tid + NT * u;
-            const int r = q / CPR, pc = q % CPR;
-            T* dst = pc < CPHI ? bphi + r * PHI_LD + pc * EPV : bv + r * V_LD + (pc - CPHI) * EPV;
-            *reinterpret_cast<uint4*>(dst) = stage[u];
+            for (int u = 0; u < MU; ++u)
+                if (doff[u] >= 0) store_quad(mirPhi + doff[u], qv[u]);
         }
     };
+    // bf16 keeps the next tile in flight while a tile is computed; fp32 operands are twice the
+    // registers, so there a tile is fetched when its turn comes.
+    constexpr bool PREF = sizeof(T) == 2;
+    constexpr int AG = NW >= 8 ? NW / 2 : NW;                 // A fragments per LDS group
+    CandTile<T, D, NW> cur, nxt;
 
     // ---------------- set-up ----------------
     for (int d = tid; d < D; d += NT) sS[d] = A.s[(int64_t)bh * D + d];
@@ -241,20 +312,24 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
     }
     __syncthreads();
     int nG = ballot_prefix(lam, NW, [&](int j) { return slotPos[j] >= 0; }, a2);
+    rows_to_mirror(lam, [&](int e, int& slot, int& s_) { slot = e; s_ = slotSrc[e]; });
     build_table(0);
     __syncthreads();
     bool prefetched = false;
     {
         int64_t xlo0;
         const int nX0 = chunk_x(0, xlo0);
-        if (lam > 0 && nG + nX0 > lam) { load_batch(0, lam + nX0); prefetched = true; }
+        if (lam > 0 && nG + nX0 > lam) {
+            if (w < (xb + nX0 + 15) / 16) load_tile(cur, w);
+            prefetched = true;
+        }
     }
 
     // ---------------- chunk loop ----------------
     for (int ch = 0; ch < A.nchunks; ++ch) {
         int64_t xlo;
         const int nX = chunk_x(ch, xlo);
-        const int NR = lam + nX;
+        const int NR = xb + nX;
         char* rec = wsb + A.L.chunk0 + (int64_t)ch * A.L.per_chunk;
 
         // (1) snapshot of the chunk-start state, in the fragment order the read-out kernel loads
@@ -264,6 +339,7 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
             for (int ss = 0; ss < D / 32; ++ss) {
                 const Frag8<T> f = frag_from_acc<T>(acc[2 * ss], acc[2 * ss + 1]);
                 *reinterpret_cast<Frag8<T>*>(snapH + ((int64_t)(w * (D / 32) + ss) * 64 + l) * 8) = f;
+                *reinterpret_cast<Frag8<T>*>(hcopy + ((w * (D / 32) + ss) * 64 + l) * 8) = f;
             }
             float* snapS = reinterpret_cast<float*>(rec + A.L.c_snap_s);
             for (int d = tid; d < D; d += NT) snapS[d] = sS[d];
@@ -271,87 +347,70 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
 
         // (3) decide which candidates are folded
         const bool scoring = lam > 0 && nG + nX > lam;
+        const int ntile = (NR + 15) >> 4;
         if (scoring) {
-            float sv[D / 32][8];
-#pragma unroll
-            for (int ss = 0; ss < D / 32; ++ss)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) sv[ss][e] = sS[32 * ss + 16 * (e >> 2) + 4 * g + (e & 3)];
-            Frag8<T> hb[D / 32];
-#pragma unroll
-            for (int ss = 0; ss < D / 32; ++ss) hb[ss] = frag_from_acc<T>(acc[2 * ss], acc[2 * ss + 1]);
+            // SRE of every candidate against the chunk-start state.  Each wave takes whole 16-candidate
+            // tiles (tile j goes to wave j % NW) and computes their full recall H^T phi(k) from the
+            // LDS copy of H^T, so a candidate's error needs no exchange between waves.  The next
+            // tile's loads are in flight while the current one is computed.
+            __syncthreads();                                  // every wave's part of the H^T copy
 
-            const int nbatch = (NR + NB - 1) / NB;
-            if (!prefetched) load_batch(0, NR);
-            store_batch(0);
-            __syncthreads();
-            for (int bt = 0; bt < nbatch; ++bt) {
-                if (bt + 1 < nbatch) load_batch(bt + 1, NR);
-                const T* bphi = bufs + (bt & 1) * BUF;
-                const T* bv = bphi + NB * PHI_LD;
-                // pass 1: numerators^T (rows = this wave's value columns, columns = 16 candidates);
-                // the denominator phi.s of tile t is computed by wave t % NW only
-                f4 num[TPB];
+            unsigned mn = 0x7F800000u, mx = 0u;
+            if (!prefetched && w < ntile) load_tile(cur, w);
+            for (int j = w; j < ntile; j += NW) {
+                const bool has_next = j + NW < ntile;
+                if (PREF && has_next) load_tile(nxt, j + NW);
+                f4 rec[NW];
 #pragma unroll
-                for (int tile = 0; tile < TPB; ++tile) {
-                    num[tile] = zero4();
-                    const bool mine = (tile % NW) == w;
-                    float den = 0.f;
+                for (int wv = 0; wv < NW; ++wv) rec[wv] = zero4();
+                float den = 0.f;
 #pragma unroll
-                    for (int ss = 0; ss < D / 32; ++ss) {
-                        const Frag8<T> bf = load_frag(bphi + (tile * 16 + c) * PHI_LD, ss, g);
-                        mma32(num[tile], hb[ss], bf);
-                        if (mine)
+                for (int ss = 0; ss < D / 32; ++ss) {
+                    const f4 slo = *reinterpret_cast<const f4*>(sS + 32 * ss + 4 * g);
+                    const f4 shi = *reinterpret_cast<const f4*>(sS + 32 * ss + 16 + 4 * g);
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) den += frag_get(bf, e) * sv[ss][e];
-                    }
-                    if (mine) {
-                        den = sum_groups(den);
-                        if (g == 0) sDen[bt * NB + tile * 16 + c] = den;
+                    for (int e = 0; e < 4; ++e)
+                        den += frag_get(cur.f[ss], e) * slo[e] + frag_get(cur.f[ss], 4 + e) * shi[e];
+#pragma unroll
+                    for (int w0 = 0; w0 < NW; w0 += AG) {
+                        Frag8<T> a[AG];
+#pragma unroll
+                        for (int u = 0; u < AG; ++u)
+                            a[u] = *reinterpret_cast<const Frag8<T>*>(hcopy + (((w0 + u) * (D / 32) + ss) * 64 + l) * 8);
+#pragma unroll
+                        for (int u = 0; u < AG; ++u) mma32(rec[w0 + u], a[u], cur.f[ss]);
+                        __builtin_amdgcn_sched_barrier(0);        // bound the A fragments in flight
                     }
                 }
-                __syncthreads();
-                // pass 2: squared error over the wave's value rows
+                den = sum_groups(den);
+                const float inv = den != 0.f ? __builtin_amdgcn_rcpf(den) : 0.f;   // empty state: recall 0
+                float sq = 0.f;
 #pragma unroll
-                for (int tile = 0; tile < TPB; ++tile) {
-                    const int rr = bt * NB + tile * 16 + c;
-                    const float den = sDen[rr];
-                    const float inv = den != 0.f ? 1.f / den : 0.f;     // empty state: recall 0
-                    const T* vr = bv + (tile * 16 + c) * V_LD + 16 * w + 4 * g;
-                    float sq = 0.f;
+                for (int wv = 0; wv < NW; ++wv)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const float x = num[tile][r] * inv - to_f(vr[r]);
+                        const float x = rec[wv][r] * inv - to_f(cur.v[wv].v[r]);
                         sq += x * x;
                     }
-                    sq = sum_groups(sq);
-                    if (g == 0 && rr < NR) part[w * nrp + rr] = sq;
+                sq = sum_groups(sq);
+                const int row = 16 * j + c;
+                if (row < NR) {
+                    const bool ok = flag[row] != 0;
+                    const float sre = sqrtf(sq);
+                    if (g == 0) key[row] = ok ? keep_key(sre, cPos[row]) : 0ull;
+                    if (ok) { mn = min(mn, __float_as_uint(sre)); mx = max(mx, __float_as_uint(sre)); }
                 }
-                if (bt + 1 < nbatch) store_batch((bt + 1) & 1);
-                __syncthreads();
-            }
-            // keys, and the SRE range for the histogram
-            {
-                unsigned mn = 0x7F800000u, mx = 0u;
-                for (int r = tid; r < NR; r += NT) {
-                    unsigned long long k = 0ull;
-                    if (flag[r]) {
-                        float s2 = 0.f;
-#pragma unroll
-                        for (int ww = 0; ww < NW; ++ww) s2 += part[ww * nrp + r];
-                        const float sre = sqrtf(s2);
-                        k = keep_key(sre, cPos[r]);
-                        mn = min(mn, __float_as_uint(sre));
-                        mx = max(mx, __float_as_uint(sre));
-                    }
-                    key[r] = k;
+                if (has_next) {
+                    if (PREF) cur = nxt;
+                    else load_tile(cur, j + NW);
                 }
-                mn = wave_min_u32(mn);
-                mx = wave_max_u32(mx);
-                if (l == 0) { tmp[8 + w] = (int)mn; tmp[16 + w] = (int)mx; }
-                for (int i = tid; i < NBIN; i += NT) hist[i] = 0;
-                if (tid == 0) tmp[4] = 0;
             }
+            // the SRE range for the histogram
+            mn = wave_min_u32(mn);
+            mx = wave_max_u32(mx);
+            if (l == 0) { tmp[8 + w] = (int)mn; tmp[16 + w] = (int)mx; }
+            for (int i = tid; i < NBIN; i += NT) hist[i] = 0;
+            if (tid == 0) tmp[4] = 0;
             __syncthreads();
             unsigned umn = 0x7F800000u, umx = 0u;
 #pragma unroll
@@ -408,11 +467,27 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
             __syncthreads();
         }
 
-        // (4) fold order first, so the fold's loads overlap the rest of the bookkeeping
+        // (4) prefix counts: fold order over the table, freed cache slots, entrants (kept leaving tokens)
         const int nS = ballot_prefix(NR, NW, [&](int r) { return flag[r] == 2; }, a1);
+        ballot_prefix(lam, NW, [&](int j) { return slotPos[j] < 0 || flag[j] == 2; }, a2);
+        const int nE = ballot_prefix(nX, NW, [&](int x) { return flag[xb + x] == 1; }, a3);
         __syncthreads();
-        for (int r = tid; r < NR; r += NT)
-            if (flag[r] == 2) foldRow[a1[r]] = r;
+        // (5) the fold list (recorded for the read-out kernel) and the entrant list
+        {
+            int* recFoldPos = reinterpret_cast<int*>(rec + A.L.c_fold_pos);
+            int* recFoldSrc = reinterpret_cast<int*>(rec + A.L.c_fold_src);
+            for (int r = tid; r < NR; r += NT) {
+                if (flag[r] != 2) continue;
+                const int k = a1[r], pos = cPos[r];
+                foldRow[k] = r;
+                recFoldPos[k] = pos;
+                recFoldSrc[k] = cSrc[r];
+                if (foldAt && pos >= t0) foldAt[pos - t0] = ch;
+            }
+            if (tid == 0) *reinterpret_cast<int*>(rec + A.L.c_fold_n) = nS;
+            for (int x = tid; x < nX; x += NT)
+                if (flag[xb + x] == 1) entRow[a3[x]] = x;
+        }
         __syncthreads();
         uint4 stg[FLPT];
         // fold staging item: TPW consecutive tokens (m0 .. m0+TPW-1) x one 16-byte piece pc, so that
@@ -436,34 +511,39 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
             }
         };
         if (nS > 0) load_fold(0);
-        ballot_prefix(lam, NW, [&](int j) { return slotPos[j] < 0 || flag[j] == 2; }, a2);
-        ballot_prefix(nX, NW, [&](int x) { return flag[lam + x] == 1; }, a3);
-        __syncthreads();
-        for (int j = tid; j < lam; j += NT)
-            if ((slotPos[j] < 0) || flag[j] == 2) freeList[a2[j]] = j;
-        {
-            int* recFoldPos = reinterpret_cast<int*>(rec + A.L.c_fold_pos);
-            int* recFoldSrc = reinterpret_cast<int*>(rec + A.L.c_fold_src);
-            for (int k = tid; k < nS; k += NT) {
-                const int r = foldRow[k];
-                const int pos = cPos[r];
-                recFoldPos[k] = pos;
-                recFoldSrc[k] = cSrc[r];
-                if (foldAt && pos >= t0) foldAt[pos - t0] = ch;
+        // (6) the k-th freed slot (in slot order) goes to the k-th entrant; the other freed slots empty
+        for (int j = tid; j < lam; j += NT) {
+            if (slotPos[j] >= 0 && flag[j] != 2) continue;
+            const int k = a2[j];
+            if (k < nE) {
+                const int x = entRow[k];
+                slotPos[j] = cPos[xb + x];
+                slotSrc[j] = cSrc[xb + x];
+                slotOfX[x] = j;
+            } else {
+                slotPos[j] = -1;
+                slotSrc[j] = -1;
             }
-            if (tid == 0) *reinterpret_cast<int*>(rec + A.L.c_fold_n) = nS;
         }
         __syncthreads();
-        for (int j = tid; j < lam; j += NT)
-            if (flag[j] == 2) { slotPos[j] = -1; slotSrc[j] = -1; }
-        __syncthreads();
-        for (int x = tid; x < nX; x += NT) {
-            if (flag[lam + x] != 1) continue;
-            const int j = freeList[a3[x]];
-            slotPos[j] = cPos[lam + x];
-            slotSrc[j] = cSrc[lam + x];
+        // (7) the entrants' features and values into their slots' mirror rows.  After scoring, the
+        // leaving-token tiles are the last tile of their waves and still sit in registers (when there
+        // are no more of them than waves); otherwise they are copied from their sources.
+        if (lam > 0 && nE > 0) {
+            if (scoring && ntile - ct <= NW) {
+                const int jl = w < ntile ? w + NW * ((ntile - 1 - w) / NW) : -1;
+                if (jl >= ct) {
+                    const int x = 16 * (jl - ct) + c;
+                    if (x < nX && flag[xb + x] == 1) tile_to_slot(cur, slotOfX[x]);
+                }
+            } else {
+                rows_to_mirror(nE, [&](int e, int& slot, int& s_) {
+                    const int x = entRow[e];
+                    slot = slotOfX[x];
+                    s_ = cSrc[xb + x];
+                });
+            }
         }
-        __syncthreads();
         {
             int* rp = reinterpret_cast<int*>(rec + A.L.c_cache_pos);
             int* rs = reinterpret_cast<int*>(rec + A.L.c_cache_src);
@@ -478,8 +558,8 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
         {
             T* recVT = reinterpret_cast<T*>(rec + A.L.c_fold_vt);
             const int cpv = A.L.c_pad64;
-            T* stPhi = bufs;                      // [D][ST_LD]   (reuses the batch buffers)
-            T* stV = bufs + D * ST_LD;            // [DV][ST_LD]
+            T* stPhi = stage;                     // [D][ST_LD]
+            T* stV = stage + D * ST_LD;           // [DV][ST_LD]
             for (int fb = 0; fb * FB < nS; ++fb) {
                 if (fb > 0) load_fold(fb);
 #pragma unroll
@@ -498,13 +578,18 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
                 __syncthreads();
                 if (more && (fb + 1) * FB >= nS) build_table(ch + 1);
 #pragma unroll
-                for (int kk = 0; kk < FB / 32; ++kk)
+                for (int kk = 0; kk < FB / 32; ++kk) {
+                    const Frag8<T> bf = load_frag(stV + (16 * w + c) * ST_LD, kk, g);
 #pragma unroll
-                    for (int i = 0; i < IT; ++i) {
-                        const Frag8<T> af = load_frag(stPhi + (16 * i + c) * ST_LD, kk, g);
-                        const Frag8<T> bf = load_frag(stV + (16 * w + c) * ST_LD, kk, g);
-                        mma32(acc[i], af, bf);
+                    for (int i0 = 0; i0 < IT; i0 += 4) {
+                        Frag8<T> af[4];
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) af[u] = load_frag(stPhi + (16 * (i0 + u) + c) * ST_LD, kk, g);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) mma32(acc[i0 + u], af[u], bf);
+                        __builtin_amdgcn_sched_barrier(0);        // bound the A fragments in flight
                     }
+                }
                 {   // s: NT / D threads per feature row
                     constexpr int TPR = NT / D;
                     const int d = tid / TPR, pr = tid % TPR;
@@ -533,7 +618,10 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
         if (more) {
             int64_t xn;
             const int nXn = chunk_x(ch + 1, xn);
-            if (lam > 0 && nG + nXn > lam) { load_batch(0, lam + nXn); prefetched = true; }
+            if (lam > 0 && nG + nXn > lam) {
+                if (w < (xb + nXn + 15) / 16) load_tile(cur, w);
+                prefetched = true;
+            }
         }
     }
 
