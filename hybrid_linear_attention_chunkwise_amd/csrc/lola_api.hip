@@ -9,9 +9,9 @@
 namespace {
 
 using lola::WsLayout;
+using lola::kMaxLambda;
+using lola::kMaxChunk;
 
-constexpr int kMaxLambda = 1024;
-constexpr int kMaxChunk = 128;
 constexpr size_t kLdsLimit = 160 * 1024;
 
 inline int64_t rup(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -85,8 +85,7 @@ lola_status check_prefill_config(const lola_state* st, int64_t n, int32_t C) {
     if (st->t + n + st->eta >= (int64_t)INT_MAX) return LOLA_EUNSUPPORTED;
     if (n > INT_MAX / 2) return LOLA_EUNSUPPORTED;
     const int esz = st->dtype == LOLA_BF16 ? 2 : 4;
-    if (lola::chain_lds_bytes(st->d_k, 1, esz, st->lambda, C) > kLdsLimit ||
-        lola::chain_lds_bytes(st->d_k, 0, esz, st->lambda, C) > kLdsLimit)
+    if (lola::chain_lds_bytes(st->d_k, 1, esz) > kLdsLimit || lola::chain_lds_bytes(st->d_k, 0, esz) > kLdsLimit)
         return LOLA_EUNSUPPORTED;
     return LOLA_OK;
 }

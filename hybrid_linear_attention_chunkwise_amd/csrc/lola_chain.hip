@@ -74,24 +74,26 @@ struct CandTile {
 // Candidate table: cache slots in rows 0 .. lam-1, the leaving tokens from row lam16 = lam rounded up
 // to 16, so a 16-row scoring tile never mixes the two.  Rows of the per-candidate arrays: lam16 + C
 // rounded up to 64 (whole ballot groups and tiles).
-__host__ __device__ inline int x_base(int lam) { return (lam + 15) & ~15; }
-__host__ __device__ inline int cand_rows(int lam, int C) { return ((x_base(lam) + C + 63) / 64) * 64; }
+__host__ __device__ constexpr int x_base(int lam) { return (lam + 15) & ~15; }
+__host__ __device__ constexpr int cand_rows(int lam, int C) { return ((x_base(lam) + C + 63) / 64) * 64; }
 
 struct ChainLds {
-    size_t stage, hcopy, s, slot_pos, slot_src, c_src, c_pos, key, aux, flag, a1, a2, a3, fold_row,
-        ent_row, slot_of_x, hist, tmp, total;
+    size_t s, slot_pos, slot_src, c_src, c_pos, key, aux, flag, a1, a2, a3, fold_row, ent_row, slot_of_x,
+        hist, tmp, hcopy, stage, total;
 };
 
-__host__ __device__ inline size_t al16(size_t x) { return (x + 15) & ~size_t(15); }
+__host__ __device__ constexpr size_t al16(size_t x) { return (x + 15) & ~size_t(15); }
 
+// LDS layout, sized for the largest supported cache and chunk so that every offset is a compile-time
+// constant (the LDS instructions then carry them as immediates instead of one register per array).
+// The small per-row arrays come first, inside the 64 KB immediate range.
 template <typename T, int DK, int PHI>
-__host__ __device__ inline ChainLds chain_lds(int lam, int C) {
+__host__ __device__ constexpr ChainLds chain_lds() {
     using Cfg = ChainCfg<T, DK, PHI>;
-    const int nr = cand_rows(lam, C);
-    ChainLds o;
+    constexpr int lam = kMaxLambda, C = kMaxChunk;
+    constexpr int nr = cand_rows(lam, C);
+    ChainLds o{};
     size_t p = 0;
-    o.stage = p;     p = al16(p + sizeof(T) * Cfg::STAGE);
-    o.hcopy = p;     p = al16(p + sizeof(T) * Cfg::HFR);
     o.s = p;         p = al16(p + sizeof(float) * Cfg::D);
     o.slot_pos = p;  p = al16(p + sizeof(int) * (lam + 1));
     o.slot_src = p;  p = al16(p + sizeof(int) * (lam + 1));
@@ -108,6 +110,8 @@ __host__ __device__ inline ChainLds chain_lds(int lam, int C) {
     o.slot_of_x = p; p = al16(p + sizeof(int) * (C + 1));
     o.hist = p;      p = al16(p + sizeof(int) * (Cfg::NBIN + 4));
     o.tmp = p;       p = al16(p + sizeof(int) * 32);
+    o.hcopy = p;     p = al16(p + sizeof(T) * Cfg::HFR);
+    o.stage = p;     p = al16(p + sizeof(T) * Cfg::STAGE);
     o.total = p;
     return o;
 }
@@ -151,7 +155,7 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
                   TPW = Cfg::TPW, FIPT = Cfg::FIPT;
     extern __shared__ __align__(16) char smem[];
     const int lam = A.lam, eta = A.eta, n = A.n, C = A.C;
-    const ChainLds lo = chain_lds<T, DK, PHI>(lam, C);
+    constexpr ChainLds lo = chain_lds<T, DK, PHI>();
     T* stage = reinterpret_cast<T*>(smem + lo.stage);
     T* hcopy = reinterpret_cast<T*>(smem + lo.hcopy);
     float* sS = reinterpret_cast<float*>(smem + lo.s);
@@ -289,7 +293,6 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
     // bf16 keeps the next tile in flight while a tile is computed; fp32 operands are twice the
     // registers, so there a tile is fetched when its turn comes.
     constexpr bool PREF = sizeof(T) == 2;
-    constexpr int AG = NW >= 8 ? NW / 2 : NW;                 // A fragments per LDS group
     CandTile<T, D, NW> cur, nxt;
 
     // ---------------- set-up ----------------
@@ -360,9 +363,9 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
             for (int j = w; j < ntile; j += NW) {
                 const bool has_next = j + NW < ntile;
                 if (PREF && has_next) load_tile(nxt, j + NW);
-                f4 rec[NW];
-#pragma unroll
-                for (int wv = 0; wv < NW; ++wv) rec[wv] = zero4();
+                // the recall in two halves of the value rows (the B fragments stay in registers, each A
+                // fragment is still read once), which halves the accumulators held at a time
+                constexpr int HW = NW >= 8 ? NW / 2 : NW;
                 float den = 0.f;
 #pragma unroll
                 for (int ss = 0; ss < D / 32; ++ss) {
@@ -371,27 +374,33 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         den += frag_get(cur.f[ss], e) * slo[e] + frag_get(cur.f[ss], 4 + e) * shi[e];
-#pragma unroll
-                    for (int w0 = 0; w0 < NW; w0 += AG) {
-                        Frag8<T> a[AG];
-#pragma unroll
-                        for (int u = 0; u < AG; ++u)
-                            a[u] = *reinterpret_cast<const Frag8<T>*>(hcopy + (((w0 + u) * (D / 32) + ss) * 64 + l) * 8);
-#pragma unroll
-                        for (int u = 0; u < AG; ++u) mma32(rec[w0 + u], a[u], cur.f[ss]);
-                        __builtin_amdgcn_sched_barrier(0);        // bound the A fragments in flight
-                    }
                 }
                 den = sum_groups(den);
                 const float inv = den != 0.f ? __builtin_amdgcn_rcpf(den) : 0.f;   // empty state: recall 0
                 float sq = 0.f;
 #pragma unroll
-                for (int wv = 0; wv < NW; ++wv)
+                for (int w0 = 0; w0 < NW; w0 += HW) {
+                    f4 rec[HW];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float x = rec[wv][r] * inv - to_f(cur.v[wv].v[r]);
-                        sq += x * x;
+                    for (int u = 0; u < HW; ++u) rec[u] = zero4();
+#pragma unroll
+                    for (int ss = 0; ss < D / 32; ++ss) {
+                        Frag8<T> a[HW];
+#pragma unroll
+                        for (int u = 0; u < HW; ++u)
+                            a[u] = *reinterpret_cast<const Frag8<T>*>(hcopy + (((w0 + u) * (D / 32) + ss) * 64 + l) * 8);
+#pragma unroll
+                        for (int u = 0; u < HW; ++u) mma32(rec[u], a[u], cur.f[ss]);
+                        __builtin_amdgcn_sched_barrier(0);        // bound the A fragments in flight
                     }
+#pragma unroll
+                    for (int u = 0; u < HW; ++u)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float x = rec[u][r] * inv - to_f(cur.v[w0 + u].v[r]);
+                            sq += x * x;
+                        }
+                }
                 sq = sum_groups(sq);
                 const int row = 16 * j + c;
                 if (row < NR) {
@@ -643,7 +652,7 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
 
 template <typename T, int DK, int PHI>
 hipError_t launch_chain_t(const PrefillArgs& a, hipStream_t stream) {
-    const size_t lds = chain_lds<T, DK, PHI>(a.lam, a.C).total;
+    constexpr size_t lds = chain_lds<T, DK, PHI>().total;
     auto kern = chain_kernel<T, DK, PHI>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -652,13 +661,13 @@ hipError_t launch_chain_t(const PrefillArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-size_t chain_lds_bytes(int d, int phi_kind, int esz, int lam, int C) {
+size_t chain_lds_bytes(int d, int phi_kind, int esz) {
     if (esz == 4) {
-        if (d == 64) return phi_kind ? chain_lds<float, 64, 1>(lam, C).total : chain_lds<float, 64, 0>(lam, C).total;
-        return phi_kind ? chain_lds<float, 128, 1>(lam, C).total : chain_lds<float, 128, 0>(lam, C).total;
+        if (d == 64) return phi_kind ? chain_lds<float, 64, 1>().total : chain_lds<float, 64, 0>().total;
+        return phi_kind ? chain_lds<float, 128, 1>().total : chain_lds<float, 128, 0>().total;
     }
-    if (d == 64) return phi_kind ? chain_lds<bf16, 64, 1>(lam, C).total : chain_lds<bf16, 64, 0>(lam, C).total;
-    return phi_kind ? chain_lds<bf16, 128, 1>(lam, C).total : chain_lds<bf16, 128, 0>(lam, C).total;
+    if (d == 64) return phi_kind ? chain_lds<bf16, 64, 1>().total : chain_lds<bf16, 64, 0>().total;
+    return phi_kind ? chain_lds<bf16, 128, 1>().total : chain_lds<bf16, 128, 0>().total;
 }
 
 template hipError_t launch_chain_t<float, 64, 0>(const PrefillArgs&, hipStream_t);

@@ -6,6 +6,9 @@
 
 namespace lola {
 
+constexpr int kMaxLambda = 1024;     // largest cache the kernels support
+constexpr int kMaxChunk = 128;       // largest prefill chunk
+
 // Per-(sequence, head) scratch used by one prefill call.  Offsets are in bytes from the start of the
 // (b, h) block; every region starts on a 256-byte boundary.
 struct WsLayout {
@@ -90,8 +93,8 @@ hipError_t launch_prefill(const PrefillArgs& a, int dtype, int d, int phi_kind, 
                           hipEvent_t const* events = nullptr);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int d, int phi_kind, hipStream_t stream);
 
-// LDS bytes the chain kernel needs for (lam, C) at element size esz; used for validation.
-size_t chain_lds_bytes(int d, int phi_kind, int esz, int lam, int C);
+// LDS bytes the chain kernel uses (sized for kMaxLambda / kMaxChunk) at element size esz.
+size_t chain_lds_bytes(int d, int phi_kind, int esz);
 size_t decode_lds_bytes(int d, int phi_kind, int esz, int lam);
 
 }  // namespace lola
