@@ -296,14 +296,23 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
     CandTile<T, D, NW> cur, nxt;
 
     // ---------------- set-up ----------------
+    // The call's chunks may be walked in several launches (chunk ranges [c_begin, c_end)); H, s and
+    // the slot table carry over through the state and the workspace, the slot mirror stays in place.
+    const bool first = A.c_begin == 0;
     for (int d = tid; d < D; d += NT) sS[d] = A.s[(int64_t)bh * D + d];
-    for (int j = tid; j < lam; j += NT) {
-        const int p = cPosState[j];
-        slotPos[j] = p;
-        slotSrc[j] = p >= 0 ? n + j : -1;
+    if (first) {
+        for (int j = tid; j < lam; j += NT) {
+            const int p = cPosState[j];
+            slotPos[j] = p;
+            slotSrc[j] = p >= 0 ? n + j : -1;
+        }
+        if (foldAt)
+            for (int i = tid; i < n; i += NT) foldAt[i] = -1;
+    } else {
+        const int* fp = reinterpret_cast<const int*>(wsb + A.L.slot_pos);
+        const int* fs = reinterpret_cast<const int*>(wsb + A.L.slot_src);
+        for (int j = tid; j < lam; j += NT) { slotPos[j] = fp[j]; slotSrc[j] = fs[j]; }
     }
-    if (foldAt)
-        for (int i = tid; i < n; i += NT) foldAt[i] = -1;
     f4 acc[IT];
     {
         const float* Hb = A.H + (int64_t)bh * DV * D;
@@ -315,13 +324,13 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
     }
     __syncthreads();
     int nG = ballot_prefix(lam, NW, [&](int j) { return slotPos[j] >= 0; }, a2);
-    rows_to_mirror(lam, [&](int e, int& slot, int& s_) { slot = e; s_ = slotSrc[e]; });
-    build_table(0);
+    if (first) rows_to_mirror(lam, [&](int e, int& slot, int& s_) { slot = e; s_ = slotSrc[e]; });
+    build_table(A.c_begin);
     __syncthreads();
     bool prefetched = false;
     {
         int64_t xlo0;
-        const int nX0 = chunk_x(0, xlo0);
+        const int nX0 = chunk_x(A.c_begin, xlo0);
         if (lam > 0 && nG + nX0 > lam) {
             if (w < (xb + nX0 + 15) / 16) load_tile(cur, w);
             prefetched = true;
@@ -329,7 +338,7 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
     }
 
     // ---------------- chunk loop ----------------
-    for (int ch = 0; ch < A.nchunks; ++ch) {
+    for (int ch = A.c_begin; ch < A.c_end; ++ch) {
         int64_t xlo;
         const int nX = chunk_x(ch, xlo);
         const int NR = xb + nX;
@@ -559,7 +568,7 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
             for (int j = tid; j < lam; j += NT) { rp[j] = slotPos[j]; rs[j] = slotSrc[j]; }
         }
         nG = scoring ? lam : (lam == 0 ? 0 : nG + nX);
-        const bool more = ch + 1 < A.nchunks;
+        const bool more = ch + 1 < A.c_end;
 
         // (6) fold in batches of FB tokens: H += Phi_S^T V_S (MFMA), s += column sums.  Once the last
         // batch is staged, the next chunk's candidate table is built so its first batch can be

@@ -42,6 +42,7 @@ struct WsLayout {
 
 struct PrefillArgs {
     int BH, n, C, eta, lam, nchunks, nqt;
+    int c_begin, c_end;   // chunk range of one chain / read-out launch
     int64_t t0;
     const void* q;
     const void* k;

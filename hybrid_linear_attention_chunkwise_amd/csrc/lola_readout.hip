@@ -16,6 +16,8 @@
 #include "lola_common.hpp"
 #include "lola_internal.hpp"
 
+#include <mutex>
+
 namespace lola {
 
 namespace {
@@ -59,11 +61,11 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
     __shared__ int sFoldPos[128];
     __shared__ int sFoldSrc[128];
 
-    const int nqt = A.nqt, nch = A.nchunks;
+    const int nqt = A.nqt, nseg = A.c_end - A.c_begin;
     const int bid = blockIdx.x;
     const int qt = bid % nqt;
-    const int ch = (bid / nqt) % nch;
-    const int bh = bid / (nqt * nch);
+    const int ch = A.c_begin + (bid / nqt) % nseg;
+    const int bh = bid / (nqt * nseg);
     const int n = A.n, C = A.C, eta = A.eta, lam = A.lam;
     const int64_t t0 = A.t0;
     const int64_t a = t0 + (int64_t)ch * C;
@@ -393,29 +395,121 @@ __global__ __launch_bounds__(256) void commit_kernel(PrefillArgs A) {
 template <typename T, int DK, int PHI>
 hipError_t launch_chain_t(const PrefillArgs& a, hipStream_t stream);
 
+// A second stream per device for the read-out, with the events that order it against the caller's
+// stream.  Created on first use with default priority and kept for the life of the process; the
+// mutex serialises enqueueing (the events are reused by every call).
+constexpr int kMaxSegments = 8;
+constexpr int kOverlapMinChunks = 8;
+struct SideStream {
+    hipStream_t stream = nullptr;
+    hipEvent_t seg[kMaxSegments] = {};
+    hipEvent_t join = nullptr;
+    std::mutex mu;
+};
+
+static SideStream* side_stream() {
+    static std::mutex init_mu;
+    static SideStream* per_dev[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> guard(init_mu);
+    if (per_dev[dev]) return per_dev[dev];
+    SideStream* s = new SideStream();
+    bool ok = hipStreamCreateWithFlags(&s->stream, hipStreamNonBlocking) == hipSuccess;
+    for (int i = 0; ok && i < kMaxSegments; ++i)
+        ok = hipEventCreateWithFlags(&s->seg[i], hipEventDisableTiming) == hipSuccess;
+    ok = ok && hipEventCreateWithFlags(&s->join, hipEventDisableTiming) == hipSuccess;
+    if (!ok) {
+        (void)hipGetLastError();
+        delete s;                       // handles created so far are left to the process end
+        return nullptr;
+    }
+    per_dev[dev] = s;
+    return s;
+}
+
 static hipError_t record(hipEvent_t const* ev, int i, hipStream_t stream) {
     if (!ev || !ev[i]) return hipSuccess;
     return hipEventRecord(ev[i], stream);
 }
 
 template <typename T, int DK, int PHI>
-hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream, hipEvent_t const* ev) {
-    hipError_t e = record(ev, 0, stream);
-    if (e != hipSuccess) return e;
-    if ((e = launch_phi_t<T, DK, PHI>(a, stream)) != hipSuccess) return e;
-    if ((e = record(ev, 1, stream)) != hipSuccess) return e;
-    e = launch_chain_t<T, DK, PHI>(a, stream);
-    if (e != hipSuccess) return e;
-    if ((e = record(ev, 2, stream)) != hipSuccess) return e;
-    const int64_t blocks = (int64_t)a.BH * a.nchunks * a.nqt;
+static hipError_t launch_readout(PrefillArgs a, int c0, int c1, hipStream_t stream) {
+    a.c_begin = c0;
+    a.c_end = c1;
+    const int64_t blocks = (int64_t)a.BH * (c1 - c0) * a.nqt;
     hipLaunchKernelGGL((readout_kernel<T, DK, PHI>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if ((e = record(ev, 3, stream)) != hipSuccess) return e;
+    return hipGetLastError();
+}
+
+template <typename T, int DK, int PHI>
+static hipError_t launch_chain_range(PrefillArgs a, int c0, int c1, hipStream_t stream) {
+    a.c_begin = c0;
+    a.c_end = c1;
+    return launch_chain_t<T, DK, PHI>(a, stream);
+}
+
+// Chunk ranges for the overlapped schedule: sizes shrink toward the end (each about 0.6 of the one
+// before), so the read-out of the last range, the only one not hidden behind the chain, is short.
+static int split_chunks(int nchunks, int* bounds, int max_seg) {
+    int sizes[16];
+    int k = 0, sum = 0, sz = nchunks / 16 > 2 ? nchunks / 16 : 2;
+    while (k < max_seg && sum < nchunks) {               // from the last range backwards
+        const int take = sz < nchunks - sum ? sz : nchunks - sum;
+        sizes[k++] = take;
+        sum += take;
+        sz = (sz * 5 + 2) / 3;
+    }
+    if (sum < nchunks) sizes[k - 1] += nchunks - sum;   // out of ranges: the first one takes the rest
+    if (k >= 2 && sizes[k - 1] < sizes[k - 2]) {         // a short remainder joins its neighbour
+        sizes[k - 2] += sizes[k - 1];
+        --k;
+    }
+    bounds[0] = 0;
+    for (int i = 0; i < k; ++i) bounds[i + 1] = bounds[i] + sizes[k - 1 - i];
+    return k;
+}
+
+template <typename T, int DK, int PHI>
+hipError_t launch_prefill_t(const PrefillArgs& a0, hipStream_t stream, hipEvent_t const* ev) {
+    PrefillArgs a = a0;
+    hipError_t e;
+    SideStream* side = (ev == nullptr && a.nchunks >= kOverlapMinChunks) ? side_stream() : nullptr;
+    if (side == nullptr) {
+        // one chain launch, then the read-out: used when timing the kernels one by one
+        if ((e = record(ev, 0, stream)) != hipSuccess) return e;
+        a.c_begin = 0;
+        a.c_end = a.nchunks;
+        if ((e = launch_phi_t<T, DK, PHI>(a, stream)) != hipSuccess) return e;
+        if ((e = record(ev, 1, stream)) != hipSuccess) return e;
+        if ((e = launch_chain_range<T, DK, PHI>(a, 0, a.nchunks, stream)) != hipSuccess) return e;
+        if ((e = record(ev, 2, stream)) != hipSuccess) return e;
+        if ((e = launch_readout<T, DK, PHI>(a, 0, a.nchunks, stream)) != hipSuccess) return e;
+        if ((e = record(ev, 3, stream)) != hipSuccess) return e;
+        hipLaunchKernelGGL((commit_kernel<T, DK>), dim3(a.BH), dim3(256), 0, stream, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        return record(ev, 4, stream);
+    }
+    // Overlapped: the chain walks the chunk ranges on the caller's stream; the read-out of a range
+    // runs on the side stream as soon as the chain has finished it, beside the next range's chain.
+    // The side stream forks from and joins back into the caller's stream, so the call stays ordered
+    // (and capturable) as one unit.
+    std::lock_guard<std::mutex> guard(side->mu);
+    int bounds[kMaxSegments + 1];
+    const int nseg = split_chunks(a.nchunks, bounds, kMaxSegments);
+    if ((e = launch_phi_t<T, DK, PHI>(a, stream)) != hipSuccess) return e;
+    for (int i = 0; i < nseg; ++i) {
+        if ((e = launch_chain_range<T, DK, PHI>(a, bounds[i], bounds[i + 1], stream)) != hipSuccess) return e;
+        if ((e = hipEventRecord(side->seg[i], stream)) != hipSuccess) return e;
+        if ((e = hipStreamWaitEvent(side->stream, side->seg[i], 0)) != hipSuccess) return e;
+        if ((e = launch_readout<T, DK, PHI>(a, bounds[i], bounds[i + 1], side->stream)) != hipSuccess) return e;
+    }
+    if ((e = hipEventRecord(side->join, side->stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(stream, side->join, 0)) != hipSuccess) return e;
+    a.c_begin = 0;
+    a.c_end = a.nchunks;
     hipLaunchKernelGGL((commit_kernel<T, DK>), dim3(a.BH), dim3(256), 0, stream, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return record(ev, 4, stream);
+    return hipGetLastError();
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int d, int phi_kind, hipStream_t stream,
