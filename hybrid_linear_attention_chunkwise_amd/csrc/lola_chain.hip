@@ -195,6 +195,13 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
     const int32_t* cPosState = lam > 0 ? A.cache_pos + (int64_t)bh * lam : nullptr;
     int32_t* foldAt = A.fold_at ? A.fold_at + (int64_t)bh * n : nullptr;
 
+    // ring slot (position mod eta) of a position in [t0 - eta, t0), from one 64-bit remainder:
+    // pos = t0 - eta + off with 0 <= off < eta, so pos mod eta = (t0 mod eta + off) mod eta
+    const int ring0 = eta > 0 ? (int)(t0 % eta) : 0;
+    auto ring_slot = [&](int64_t pos) {
+        const int sl = ring0 + (int)(pos - (t0 - eta));
+        return sl >= eta ? sl - eta : sl;
+    };
     auto chunk_x = [&](int ch, int64_t& xlo) {           // leaving tokens of chunk ch: [xlo, xlo + nX)
         const int64_t a = t0 + (int64_t)ch * C;
         const int64_t b = min(a + (int64_t)C, t0 + (int64_t)n);
@@ -211,7 +218,7 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
             else if (r >= xb && r < xb + nX) {
                 const int64_t pos = xlo + (r - xb);
                 p_ = (int)pos;
-                s_ = pos >= t0 ? (int)(pos - t0) : n + lam + (int)(pos % eta);
+                s_ = pos >= t0 ? (int)(pos - t0) : n + lam + ring_slot(pos);
                 f = 1;
             }
             cSrc[r] = s_;
@@ -414,7 +421,7 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
                 const int row = 16 * j + c;
                 if (row < NR) {
                     const bool ok = flag[row] != 0;
-                    const float sre = sqrtf(sq);
+                    const float sre = __builtin_amdgcn_sqrtf(sq);
                     if (g == 0) key[row] = ok ? keep_key(sre, cPos[row]) : 0ull;
                     if (ok) { mn = min(mn, __float_as_uint(sre)); mx = max(mx, __float_as_uint(sre)); }
                 }

@@ -36,8 +36,11 @@ template <typename T> __device__ __forceinline__ T from_f(float x);
 template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16)x; }
 
-// exp via the hardware base-2 exponential.
-__device__ __forceinline__ float fast_exp(float x) { return exp2f(x * 1.4426950408889634f); }
+// exp via the hardware base-2 exponential (one v_exp_f32; results below the normal range flush to 0,
+// which only ever meets weights that are negligible next to the largest one).
+__device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+// Hardware reciprocal (about 1 ulp), for normalisers.
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
 // ---------------------------------------------------------------------------------------------
 // Fragments
@@ -187,7 +190,7 @@ __device__ __forceinline__ void phi_tile(const T* wt, int wt_ld, const Frag8<T> 
             }
         sp = sum_groups(sp);
         sm = sum_groups(sm);
-        const float ip = 1.f / sp, im = 1.f / sm;
+        const float ip = fast_rcp(sp), im = fast_rcp(sm);
 #pragma unroll
         for (int ft = 0; ft < DW / 16; ++ft)
 #pragma unroll

@@ -211,7 +211,7 @@ __global__ __launch_bounds__(4 * DK) void decode_kernel(DecodeArgs A) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) den += ph[2 * ss + (e >> 2)][e & 3] * sv[ss][e];
             den = sum_groups(den);
-            const float inv = den != 0.f ? 1.f / den : 0.f;     // empty state: recall 0
+            const float inv = den != 0.f ? fast_rcp(den) : 0.f;     // empty state: recall 0
             float sq = 0.f;
 #pragma unroll
             for (int J = 0; J < JT; ++J) {
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(4 * DK) void decode_kernel(DecodeArgs A) {
                 }
             }
             sq = sum_groups(sq);
-            if (g == 0 && row <= lam) sSre[row] = sqrtf(sq);
+            if (g == 0 && row <= lam) sSre[row] = __builtin_amdgcn_sqrtf(sq);
         }
     }
     __syncthreads();
@@ -300,11 +300,14 @@ __global__ __launch_bounds__(4 * DK) void decode_kernel(DecodeArgs A) {
     // ---- window logits: positions max(0, t-eta+1) .. t-1 from the ring, t from the input ----
     const int64_t wlo = max((int64_t)0, t - eta + 1);
     const int nw = eta > 0 ? (int)(t - wlo + 1) : 0;
+    // ring slot of window position wlo + i (i < nw <= eta), from one 64-bit remainder
+    const int wslot0 = eta > 0 ? (int)(wlo % eta) : 0;
+    auto wslot = [&](int i) { const int sl = wslot0 + i; return sl >= eta ? sl - eta : sl; };
     for (int tile = w; tile * 16 < nw; tile += NW) {
         const int i = tile * 16 + c;
         const bool valid = i < nw;
         const int64_t p = wlo + i;
-        const T* rk = valid ? (p == t ? kg : ringK + (p % eta) * DK) : nullptr;
+        const T* rk = valid ? (p == t ? kg : ringK + wslot(i) * DK) : nullptr;
         float lg = 0.f;
 #pragma unroll
         for (int ss = 0; ss < DK / 32; ++ss) {
@@ -365,7 +368,7 @@ __global__ __launch_bounds__(4 * DK) void decode_kernel(DecodeArgs A) {
             if (kk < nw) {
                 const int64_t p = wlo + kk;
                 lg = sWlog[kk];
-                rv = p == t ? vg : ringV + (p % eta) * DV;
+                rv = p == t ? vg : ringV + wslot(kk) * DV;
             } else if (kk < nkeys) {
                 const int r = kk - nw;
                 if (cache_row_exact(r)) {

@@ -100,6 +100,7 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
     const int64_t bhi = min(q0 + 63, b - 1);
     const int nb = (eta > 0 && bhi >= blo) ? (int)(bhi - blo + 1) : 0;
     const int NK = nb + lam;
+    const int blo_slot = eta > 0 ? (int)(blo % eta) : 0;    // ring slot of the first band key
     const int nblk = (NK + KB - 1) / KB;
     // key kk -> (position, band?, K row, V row); position -1 = no key
     auto key_rows = [&](int kk, int& pos, int& band, const T*& rk, const T*& rv) {
@@ -109,7 +110,11 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
             pos = (int)ps;
             band = 1;
             if (ps >= t0) { rk = kin + (ps - t0) * DK; rv = vin + (ps - t0) * DV; }
-            else { rk = ringK + (ps % eta) * DK; rv = ringV + (ps % eta) * DV; }
+            else {
+                const int sl = (int)((blo_slot + kk) % eta);
+                rk = ringK + sl * DK;
+                rv = ringV + sl * DV;
+            }
         } else if (kk < NK) {
             const int jj = kk - nb;
             const int p = cachePos[jj];
@@ -368,6 +373,7 @@ __global__ __launch_bounds__(256) void commit_kernel(PrefillArgs A) {
         T* ringV = reinterpret_cast<T*>(A.win_v) + (int64_t)bh * eta * DV;
         const int64_t plo = max(t0, t0 + n - eta);
         const int cnt = (int)(t0 + n - plo);
+        const int slot0 = (int)(plo % eta);           // ring slot of plo; later ones follow (x < eta)
         const int items = cnt * 2 * CPR;
         for (int i0 = tid; i0 < items; i0 += 256 * UN) {
             uint4 val[UN];
@@ -379,7 +385,7 @@ __global__ __launch_bounds__(256) void commit_kernel(PrefillArgs A) {
                 if (it >= items) continue;
                 const int x = it / (2 * CPR), rem = it % (2 * CPR), isv = rem / CPR, p = rem % CPR;
                 const int64_t pos = plo + x;
-                const int slot = (int)(pos % eta);
+                const int slot = slot0 + x >= eta ? slot0 + x - eta : slot0 + x;
                 val[u] = *reinterpret_cast<const uint4*>((isv ? vin : kin) + (pos - t0) * DK + p * EPV);
                 dst[u] = (isv ? ringV : ringK) + (int64_t)slot * DK + p * EPV;
             }
