@@ -25,7 +25,8 @@ METRIC = "prefill tokens/s and decode tokens/s per GPU; % of MFMA / HBM roofline
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ("lola_common.hpp", "lola_phi.hip", "lola_chain.hip", "lola_readout.hip", "lola_decode.hip")
+KERNEL_SOURCES = ("lola_common.hpp", "lola_phi.hip", "lola_chain.hip", "lola_readout.hip", "lola_decode.hip",
+                  "lola_decode_fast.hip")
 
 
 def log(msg: str) -> None:

@@ -213,7 +213,12 @@ lola_status lola_decode_step(lola_state* st, const lola_phi* phi, const void* q,
     a.win_k = st->win_k; a.win_v = st->win_v;
     a.cache_k = st->cache_k; a.cache_v = st->cache_v; a.cache_pos = st->cache_pos;
     a.folded_pos = folded_pos;
-    const hipError_t e = lola::launch_decode(a, st->dtype, st->d_k, phi->kind, (hipStream_t)stream);
+    // bf16 states whose cache and window fit the register-resident kernel take it
+    const bool fast = st->dtype == LOLA_BF16 && lola::decode_fast_fits(st->d_k, st->lambda, st->eta) &&
+                      lola::decode_fast_lds_bytes(st->d_k, phi->kind) <= kLdsLimit &&
+                      !getenv("LOLA_DECODE_GENERAL");
+    const hipError_t e = fast ? lola::launch_decode_fast(a, st->d_k, phi->kind, (hipStream_t)stream)
+                              : lola::launch_decode(a, st->dtype, st->d_k, phi->kind, (hipStream_t)stream);
     if (e != hipSuccess) return LOLA_EDEVICE;
     if (getenv("LOLA_DEBUG_SYNC") && hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return LOLA_EDEVICE;
     st->t += 1;

@@ -122,21 +122,69 @@ __device__ __forceinline__ void mma32(f4& acc, const Frag8<bf16>& a, const Frag8
 // ---------------------------------------------------------------------------------------------
 // Cross-lane reductions inside a wave.
 // ---------------------------------------------------------------------------------------------
-// Over the four lane groups (lanes c, c+16, c+32, c+48): a column of an accumulator tile.
+// Over the four lane groups (lanes c, c+16, c+32, c+48): a column of an accumulator tile.  The gfx950
+// lane-swap instructions pair each lane with lane ^ 16 (then ^ 32) in VALU registers, without the LDS
+// crossbar; the two halves returned are the lane's own value and its partner's.
+__device__ __forceinline__ void pair16(float x, float& a, float& b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void pair32(float x, float& a, float& b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
 __device__ __forceinline__ float sum_groups(float x) {
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    return x;
+    float a, b;
+    pair16(x, a, b);
+    pair32(a + b, a, b);
+    return a + b;
 }
 __device__ __forceinline__ float max_groups(float x) {
-    x = fmaxf(x, __shfl_xor(x, 16));
-    x = fmaxf(x, __shfl_xor(x, 32));
-    return x;
+    float a, b;
+    pair16(x, a, b);
+    pair32(fmaxf(a, b), a, b);
+    return fmaxf(a, b);
 }
 __device__ __forceinline__ float min_groups(float x) {
-    x = fminf(x, __shfl_xor(x, 16));
-    x = fminf(x, __shfl_xor(x, 32));
+    float a, b;
+    pair16(x, a, b);
+    pair32(fminf(a, b), a, b);
+    return fminf(a, b);
+}
+// Inclusive sum over the 16 lanes of a lane group with DPP row shifts (VALU only, no LDS): lane 15
+// of each group (c == 15) ends with the group's total.
+template <int CTRL>
+__device__ __forceinline__ float dpp_shr(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float sum_cols_last(float x) {
+    x += dpp_shr<0x111>(x);   // row_shr:1
+    x += dpp_shr<0x112>(x);   // row_shr:2
+    x += dpp_shr<0x114>(x);   // row_shr:4
+    x += dpp_shr<0x118>(x);   // row_shr:8
     return x;
+}
+// Whole-wave sum / max, every lane gets the result: quad and row rotations by DPP, then the lane
+// swaps across the four rows (VALU only).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float wave_sum(float x) {
+    x += dpp_mov<0xB1>(x);    // quad_perm [1,0,3,2]
+    x += dpp_mov<0x4E>(x);    // quad_perm [2,3,0,1]
+    x += dpp_mov<0x124>(x);   // row_ror:4
+    x += dpp_mov<0x128>(x);   // row_ror:8
+    return sum_groups(x);
+}
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmaxf(x, dpp_mov<0xB1>(x));
+    x = fmaxf(x, dpp_mov<0x4E>(x));
+    x = fmaxf(x, dpp_mov<0x124>(x));
+    x = fmaxf(x, dpp_mov<0x128>(x));
+    return max_groups(x);
 }
 // Over the 16 columns of one lane group: a row of an accumulator tile.
 __device__ __forceinline__ float sum_cols(float x) {

@@ -93,6 +93,10 @@ hipError_t launch_init(const InitArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int d, int phi_kind, hipStream_t stream,
                           hipEvent_t const* events = nullptr);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int d, int phi_kind, hipStream_t stream);
+// Register-resident decode for bf16 storage, when the cache and window fit its tiles.
+bool decode_fast_fits(int d, int lam, int eta);
+size_t decode_fast_lds_bytes(int d, int phi_kind);
+hipError_t launch_decode_fast(const DecodeArgs& a, int d, int phi_kind, hipStream_t stream);
 
 // LDS bytes the chain kernel uses (sized for kMaxLambda / kMaxChunk) at element size esz.
 size_t chain_lds_bytes(int d, int phi_kind, int esz);
