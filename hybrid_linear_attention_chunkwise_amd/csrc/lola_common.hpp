@@ -79,6 +79,23 @@ __device__ __forceinline__ Frag8<bf16> load_frag(const bf16* row, int ss, int g)
     f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     return f;
 }
+// The contiguous variant of the order: lane group g feeds row[32ss + 8g .. +7], one 16-byte load.
+// Usable wherever both operands of a product are loaded from memory in that same order (the MFMA
+// sums over its eight k values per group in any order).
+__device__ __forceinline__ Frag8<bf16> load_frag_contig(const bf16* row, int ss, int g) {
+    Frag8<bf16> f;
+    f.v = *reinterpret_cast<const bf16x8*>(row + 32 * ss + 8 * g);
+    return f;
+}
+__device__ __forceinline__ Frag8<float> load_frag_contig(const float* row, int ss, int g) {
+    const float4 lo = *reinterpret_cast<const float4*>(row + 32 * ss + 8 * g);
+    const float4 hi = *reinterpret_cast<const float4*>(row + 32 * ss + 8 * g + 4);
+    Frag8<float> f;
+    f.v[0] = lo.x; f.v[1] = lo.y; f.v[2] = lo.z; f.v[3] = lo.w;
+    f.v[4] = hi.x; f.v[5] = hi.y; f.v[6] = hi.z; f.v[7] = hi.w;
+    return f;
+}
+
 // fp32 source converted to the operand type (used for fp32 state feeding bf16 MFMA).
 template <typename T> __device__ __forceinline__ Frag8<T> load_frag_cvt(const float* row, int ss, int g);
 template <> __device__ __forceinline__ Frag8<float> load_frag_cvt<float>(const float* row, int ss, int g) {
@@ -197,11 +214,12 @@ __device__ __forceinline__ float sum_cols(float x) {
 
 // ---------------------------------------------------------------------------------------------
 // Feature map phi on a 16-row tile (section 2.2; the two fixed forms of the library).
-//   x frags: xf[ss] holds row c = lane % 16 of the 16 inputs, reduction over d_k.
+//   x frags: xf[ss] holds row c = lane % 16 of the 16 inputs, reduction over d_k (in the standard
+//   order, or the contiguous one when CONTIG; W^T is then read in the same order).
 //   wt: W transposed in LDS, [DW][wt_ld] (row j = column j of W).
 //   out[ft][r] = phi(x_c)[16*ft + 4*g + r], ft = 0..7 (D = 128).
 // ---------------------------------------------------------------------------------------------
-template <typename T, int DK, int PHI>
+template <typename T, int DK, int PHI, bool CONTIG = false>
 __device__ __forceinline__ void phi_tile(const T* wt, int wt_ld, const Frag8<T> (&xf)[DK / 32],
                                          float (&out)[kFeat / 16][4]) {
     constexpr int DW = (PHI == kPhiSoftmaxPM) ? kFeat / 2 : kFeat;
@@ -212,7 +230,8 @@ __device__ __forceinline__ void phi_tile(const T* wt, int wt_ld, const Frag8<T> 
         pre[ft] = zero4();
 #pragma unroll
         for (int ss = 0; ss < DK / 32; ++ss) {
-            const Frag8<T> a = load_frag(wt + (16 * ft + c) * wt_ld, ss, g);
+            const Frag8<T> a = CONTIG ? load_frag_contig(wt + (16 * ft + c) * wt_ld, ss, g)
+                                      : load_frag(wt + (16 * ft + c) * wt_ld, ss, g);
             mma32(pre[ft], a, xf[ss]);
         }
     }

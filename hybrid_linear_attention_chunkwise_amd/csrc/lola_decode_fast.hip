@@ -10,7 +10,8 @@
 // window values are fetched once the window keys have been used, while the allocation runs.
 //
 // Logits come from MFMA with the query as row 0 of the A operand; features through W^T as in the
-// other kernels; the SRE numerators H^T phi(k) from the bf16 H^T copy in LDS.
+// other kernels; the SRE numerators H^T phi(k) from the bf16 H^T copy in LDS.  Keys, the query and
+// W^T use the contiguous fragment order (one 16-byte load per lane and super-step).
 #include "lola_common.hpp"
 #include "lola_internal.hpp"
 
@@ -24,7 +25,7 @@ template <int DK, int PHI>
 struct FastCfg {
     static constexpr int D = kFeat, DV = DK;
     static constexpr int DW = (PHI == kPhiSoftmaxPM) ? D / 2 : D;
-    static constexpr int NW = DV / 16, NT = 64 * NW, WT_LD = DK + 4, JT = DV / 16;
+    static constexpr int NW = DV / 16, NT = 64 * NW, WT_LD = DK + 8, JT = DV / 16;   // 16-byte rows
     static constexpr int MT = 3;                              // candidate tiles per wave
     static constexpr int MW = 2;                              // window-key tiles per wave
     static constexpr int LPR = DV / 8;                        // lanes per value row (8 bf16 each)
@@ -136,22 +137,59 @@ __global__ __launch_bounds__(4 * DK) void decode_fast_kernel(DecodeArgs A) {
     auto ctile = [&](int ww, int u) { return u < MT - 1 ? ww + NW * u : NW * u + (NW - 1 - ww); };
 
     // ---------------- every load of the step ----------------
+    // First H^T and the small operands, whose LDS copies are the only stores that wait on memory;
+    // then the key and candidate tiles, which stay in flight through the barrier and are consumed
+    // in the order they were issued.
+    constexpr int WPT = DK * DW / 4 / NT;                     // float4 pieces of W per thread
+    static_assert(DK * DW / 4 % NT == 0 && 2 * NT >= Cfg::MAXC && NT >= D, "thread coverage");
     f4 acc[IT];
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
         const float4 h = *reinterpret_cast<const float4*>(Hg + (16 * w + c) * D + 16 * i + 4 * g);
         acc[i] = f4{h.x, h.y, h.z, h.w};
     }
+    // every workgroup reads all of W at the same moment: start each one at a different piece so the
+    // requests spread over the cache channels instead of queueing on the same lines
+    float4 wreg[WPT];
+    const int wrot = (bh * 97) & (NT * WPT - 1);
+#pragma unroll
+    for (int u = 0; u < WPT; ++u) wreg[u] = reinterpret_cast<const float4*>(A.W)[(tid + NT * u + wrot) & (NT * WPT - 1)];
+    const float s_in = tid < D ? sg[tid] : 0.f;
+    const int cp_in = tid < lam ? cpos[tid] : -1;
+    const int cp_in2 = tid + NT < lam ? cpos[tid + NT] : -1;
+    T ek_in = from_f<T>(0.f), ev_in = from_f<T>(0.f);
+    if (has_e && tid < DK) ek_in = ekg[tid];
+    if (has_e && tid < DV) ev_in = evg[tid];
+    static_assert((NT * WPT & (NT * WPT - 1)) == 0, "W pieces: a power of two");
+#pragma unroll
+    for (int u = 0; u < WPT; ++u) {
+        const int i = 4 * ((tid + NT * u + wrot) & (NT * WPT - 1)), d = i / DW, j = i - d * DW;
+        wt[(j + 0) * WT_LD + d] = from_f<T>(wreg[u].x);
+        wt[(j + 1) * WT_LD + d] = from_f<T>(wreg[u].y);
+        wt[(j + 2) * WT_LD + d] = from_f<T>(wreg[u].z);
+        wt[(j + 3) * WT_LD + d] = from_f<T>(wreg[u].w);
+    }
+    if (tid < D) sS[tid] = s_in;
+    if (tid < lam) sCpos[tid] = cp_in;
+    if (tid + NT < lam) sCpos[tid + NT] = cp_in2;
+    if (tid < DK) sEk[tid] = ek_in;
+    if (tid < DV) sEv[tid] = ev_in;
+    if (tid == 0) sRed[1] = ~0ull;
+#pragma unroll
+    for (int ss = 0; ss < D / 32; ++ss)
+        *reinterpret_cast<Frag8<T>*>(sHb + ((w * (D / 32) + ss) * 64 + l) * 8) =
+            frag_from_acc<T>(acc[2 * ss], acc[2 * ss + 1]);
+    __builtin_amdgcn_sched_barrier(0);                        // the tile loads stay below
     // the query, as row 0 of an A operand (and column 0 of a B operand: the same registers)
     Frag8<T> qa[DK / 32];
 #pragma unroll
-    for (int ss = 0; ss < DK / 32; ++ss) qa[ss] = c == 0 ? load_frag(qg, ss, g) : frag_zero<T>();
+    for (int ss = 0; ss < DK / 32; ++ss) qa[ss] = c == 0 ? load_frag_contig(qg, ss, g) : frag_zero<T>();
     Frag8<T> wk[MW][DK / 32];
 #pragma unroll
     for (int u = 0; u < MW; ++u) {
         const T* rk = wrow(16 * (w + NW * u) + c, ringK, kg, DK);
 #pragma unroll
-        for (int ss = 0; ss < DK / 32; ++ss) wk[u][ss] = load_frag(rk, ss, g);
+        for (int ss = 0; ss < DK / 32; ++ss) wk[u][ss] = load_frag_contig(rk, ss, g);
     }
     Frag8<T> ck[MT][DK / 32];
     bf16x4 cv[MT][JT];
@@ -163,21 +201,10 @@ __global__ __launch_bounds__(4 * DK) void decode_fast_kernel(DecodeArgs A) {
         if (r < lam) { rk = cK + (int64_t)r * DK; rv = cV + (int64_t)r * DV; }
         else if (r == lam) { rk = ekg; rv = evg; }
 #pragma unroll
-        for (int ss = 0; ss < DK / 32; ++ss) ck[u][ss] = load_frag(rk, ss, g);
+        for (int ss = 0; ss < DK / 32; ++ss) ck[u][ss] = load_frag_contig(rk, ss, g);
 #pragma unroll
         for (int J = 0; J < JT; ++J) cv[u][J] = *reinterpret_cast<const bf16x4*>(rv + 16 * J + 4 * g);
     }
-    // small operands last: their LDS stores wait for every load issued before them
-    stage_wt<T, DK, DW, NT>(wt, WT_LD, A.W);
-    for (int d = tid; d < D; d += NT) sS[d] = sg[d];
-    for (int j = tid; j < lam; j += NT) sCpos[j] = cpos[j];
-    for (int d = tid; d < DK; d += NT) sEk[d] = has_e ? ekg[d] : from_f<T>(0.f);
-    for (int d = tid; d < DV; d += NT) sEv[d] = has_e ? evg[d] : from_f<T>(0.f);
-    if (tid == 0) sRed[1] = ~0ull;
-#pragma unroll
-    for (int ss = 0; ss < D / 32; ++ss)
-        *reinterpret_cast<Frag8<T>*>(sHb + ((w * (D / 32) + ss) * 64 + l) * 8) =
-            frag_from_acc<T>(acc[2 * ss], acc[2 * ss + 1]);
     __syncthreads();
 
     // ---------------- logits (query in row 0; lane (0, c) holds column c) ----------------
@@ -214,7 +241,7 @@ __global__ __launch_bounds__(4 * DK) void decode_fast_kernel(DecodeArgs A) {
     // features of the query: wave 0 (no last-group candidate tile)
     if (w == 0) {
         float ph[D / 16][4];
-        phi_tile<T, DK, PHI>(wt, WT_LD, qa, ph);
+        phi_tile<T, DK, PHI, true>(wt, WT_LD, qa, ph);
         if (c == 0)
 #pragma unroll
             for (int ft = 0; ft < D / 16; ++ft)
@@ -229,7 +256,7 @@ __global__ __launch_bounds__(4 * DK) void decode_fast_kernel(DecodeArgs A) {
             const int j = ctile(w, u);
             if (j >= ntc) continue;
             float ph[D / 16][4];
-            phi_tile<T, DK, PHI>(wt, WT_LD, ck[u], ph);
+            phi_tile<T, DK, PHI, true>(wt, WT_LD, ck[u], ph);
             float den = 0.f;
 #pragma unroll
             for (int ft = 0; ft < D / 16; ++ft) {
@@ -317,7 +344,7 @@ __global__ __launch_bounds__(4 * DK) void decode_fast_kernel(DecodeArgs A) {
             for (int u = 0; u < MT; ++u) {
                 if (u != uf) continue;
                 float ph[D / 16][4];
-                phi_tile<T, DK, PHI>(wt, WT_LD, ck[u], ph);
+                phi_tile<T, DK, PHI, true>(wt, WT_LD, ck[u], ph);
                 if (c == cf) {
 #pragma unroll
                     for (int ft = 0; ft < D / 16; ++ft)

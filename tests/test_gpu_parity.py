@@ -234,3 +234,47 @@ def test_decode_equals_prefill_c1():
         ys.append(y)
     y_d = torch.stack(ys, dim=2).cpu().numpy()
     assert TL.row_rel_err(y_d, y_p) <= 1e-5
+
+
+@pytest.mark.parametrize("path", ["register", "general"])
+def test_decode_bf16_d128_both_kernels(path, monkeypatch):
+    """bf16 decode at d = 128 through the register-resident kernel and through the general one
+    (forced by LOLA_DECODE_GENERAL), each against the oracle."""
+    if path == "general":
+        monkeypatch.setenv("LOLA_DECODE_GENERAL", "1")
+    else:
+        monkeypatch.delenv("LOLA_DECODE_GENERAL", raising=False)
+    wl = small_workload(53, B=2, h=2, n=0, C=1, eta=24, lam=20, d_k=128, d_v=128, dtype="bf16")
+    _decode_check(wl, n0=72, steps=40, heads=[(0, 1), (1, 0)], C0=16)
+
+
+def test_decode_bf16_cache_beyond_register_path():
+    """A cache too large for the register-resident decode kernel (lambda + 1 > 384) takes the
+    general kernel automatically."""
+    wl = small_workload(54, B=1, h=2, n=0, C=1, eta=32, lam=400, d_k=128, d_v=128, dtype="bf16")
+    _decode_check(wl, n0=480, steps=24, heads=[(0, 0), (0, 1)], C0=32)
+
+
+def test_overlapped_prefill_equals_sequential():
+    """The overlapped schedule (read-out of finished chunk ranges on a side stream) gives the same
+    bits as one chain launch followed by the read-out (the profiled entry point)."""
+    import hybrid_linear_attention_chunkwise_amd as lola
+    wl = small_workload(55, B=2, h=3, n=700, C=16, eta=24, lam=20, dtype="bf16")
+    W = make_weights(wl)
+    q, k, v = make_qkv(wl)
+    dev = torch.device("cuda:0")
+    phi = lola.LolaPhi(wl.phi, torch.from_numpy(W).to(dev))
+    qt, kt, vt = (torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (q, k, v))
+    outs = []
+    for profiled in (False, True):
+        st = lola.LolaState(wl.B, wl.h, wl.d_k, wl.d_v, wl.D, wl.eta, wl.lam, torch.bfloat16, device=dev)
+        lola.lola_state_init(st)
+        fold = torch.full((wl.B, wl.h, wl.n), -7, dtype=torch.int32, device=dev)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if profiled else None
+        y, _ = lola.lola_prefill(st, phi, qt, kt, vt, wl.C, fold_at=fold, events=ev)
+        torch.cuda.synchronize()
+        outs.append((y.float().cpu().numpy(), fold.cpu().numpy(), TL.state_to_host(st)))
+    (y0, f0, s0), (y1, f1, s1) = outs
+    assert np.array_equal(y0, y1) and np.array_equal(f0, f1)
+    for key in s0:
+        assert np.array_equal(np.asarray(s0[key]), np.asarray(s1[key])), key
