@@ -323,77 +323,98 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
     }
 }
 
-// Commit: move the final cache members' K/V into the state's slots, then write the last eta input
-// tokens into the window ring.  One workgroup per (sequence, head); runs after the read-out.  Rows
-// move as 16-byte pieces, several loads in flight per thread.
+// Commit, in two launches so that every workgroup can work on any slice of a (sequence, head):
+//  1. the final cache members' K/V into the state's slots (a member may come from the initial window
+//     ring, so this completes before the ring is overwritten), and the slots' positions;
+//  2. the last eta input tokens into the window ring.
+// Rows move as 16-byte pieces; each thread has UN loads in flight.  Grid: (B*h, kCommitSlices).
+constexpr int kCommitSlices = 8;
+
 template <typename T, int DK>
-__global__ __launch_bounds__(256) void commit_kernel(PrefillArgs A) {
+__global__ __launch_bounds__(256) void commit_cache_kernel(PrefillArgs A) {
     constexpr int DV = DK, EPV = 16 / (int)sizeof(T), CPR = DK / EPV, UN = 4;
-    const int bh = blockIdx.x, tid = threadIdx.x;
+    const int bh = blockIdx.x, tid = threadIdx.x + 256 * blockIdx.y;
+    constexpr int NTH = 256 * kCommitSlices;
     const int n = A.n, eta = A.eta, lam = A.lam;
-    const int64_t t0 = A.t0;
+    if (lam == 0) return;
     const char* wsb = A.ws + (int64_t)bh * A.L.per_bh;
     const int* fp = reinterpret_cast<const int*>(wsb + A.L.slot_pos);
     const int* fs = reinterpret_cast<const int*>(wsb + A.L.slot_src);
     const T* kin = reinterpret_cast<const T*>(A.k) + (int64_t)bh * n * DK;
     const T* vin = reinterpret_cast<const T*>(A.v) + (int64_t)bh * n * DV;
-    if (lam > 0) {
-        T* cK = reinterpret_cast<T*>(A.cache_k) + (int64_t)bh * lam * DK;
-        T* cV = reinterpret_cast<T*>(A.cache_v) + (int64_t)bh * lam * DV;
-        const T* ringK = eta > 0 ? reinterpret_cast<const T*>(A.win_k) + (int64_t)bh * eta * DK : nullptr;
-        const T* ringV = eta > 0 ? reinterpret_cast<const T*>(A.win_v) + (int64_t)bh * eta * DV : nullptr;
-        int32_t* cpos = A.cache_pos + (int64_t)bh * lam;
-        const int items = lam * 2 * CPR;                 // (slot, K or V, piece)
-        for (int i0 = tid; i0 < items; i0 += 256 * UN) {
-            uint4 val[UN];
-            T* dst[UN];
+    T* cK = reinterpret_cast<T*>(A.cache_k) + (int64_t)bh * lam * DK;
+    T* cV = reinterpret_cast<T*>(A.cache_v) + (int64_t)bh * lam * DV;
+    const T* ringK = eta > 0 ? reinterpret_cast<const T*>(A.win_k) + (int64_t)bh * eta * DK : nullptr;
+    const T* ringV = eta > 0 ? reinterpret_cast<const T*>(A.win_v) + (int64_t)bh * eta * DV : nullptr;
+    int32_t* cpos = A.cache_pos + (int64_t)bh * lam;
+    const int items = lam * 2 * CPR;                     // (slot, K or V, piece)
+    for (int i0 = tid; i0 < items; i0 += NTH * UN) {
+        uint4 val[UN];
+        T* dst[UN];
 #pragma unroll
-            for (int u = 0; u < UN; ++u) {
-                const int it = i0 + 256 * u;
-                dst[u] = nullptr;
-                if (it >= items) continue;
-                const int j = it / (2 * CPR), rem = it % (2 * CPR), isv = rem / CPR, p = rem % CPR;
-                const int src = fs[j];
-                if (src < 0 || src == n + j) continue;    // empty, or a member that kept its slot
-                const T* row;
-                if (src < n) row = (isv ? vin : kin) + (int64_t)src * DK;
-                else row = (isv ? ringV : ringK) + (int64_t)(src - n - lam) * DK;
-                val[u] = *reinterpret_cast<const uint4*>(row + p * EPV);
-                dst[u] = (isv ? cV : cK) + (int64_t)j * DK + p * EPV;
-            }
-#pragma unroll
-            for (int u = 0; u < UN; ++u)
-                if (dst[u]) *reinterpret_cast<uint4*>(dst[u]) = val[u];
+        for (int u = 0; u < UN; ++u) {
+            const int it = i0 + NTH * u;
+            dst[u] = nullptr;
+            if (it >= items) continue;
+            const int j = it / (2 * CPR), rem = it % (2 * CPR), isv = rem / CPR, p = rem % CPR;
+            const int src = fs[j];
+            if (src < 0 || src == n + j) continue;        // empty, or a member that kept its slot
+            const T* row;
+            if (src < n) row = (isv ? vin : kin) + (int64_t)src * DK;
+            else row = (isv ? ringV : ringK) + (int64_t)(src - n - lam) * DK;
+            val[u] = *reinterpret_cast<const uint4*>(row + p * EPV);
+            dst[u] = (isv ? cV : cK) + (int64_t)j * DK + p * EPV;
         }
-        for (int j = tid; j < lam; j += 256) cpos[j] = fp[j];
+#pragma unroll
+        for (int u = 0; u < UN; ++u)
+            if (dst[u]) *reinterpret_cast<uint4*>(dst[u]) = val[u];
     }
-    __syncthreads();
-    if (eta > 0) {
-        T* ringK = reinterpret_cast<T*>(A.win_k) + (int64_t)bh * eta * DK;
-        T* ringV = reinterpret_cast<T*>(A.win_v) + (int64_t)bh * eta * DV;
-        const int64_t plo = max(t0, t0 + n - eta);
-        const int cnt = (int)(t0 + n - plo);
-        const int slot0 = (int)(plo % eta);           // ring slot of plo; later ones follow (x < eta)
-        const int items = cnt * 2 * CPR;
-        for (int i0 = tid; i0 < items; i0 += 256 * UN) {
-            uint4 val[UN];
-            T* dst[UN];
+    for (int j = tid; j < lam; j += NTH) cpos[j] = fp[j];
+}
+
+template <typename T, int DK>
+__global__ __launch_bounds__(256) void commit_ring_kernel(PrefillArgs A) {
+    constexpr int DV = DK, EPV = 16 / (int)sizeof(T), CPR = DK / EPV, UN = 4;
+    const int bh = blockIdx.x, tid = threadIdx.x + 256 * blockIdx.y;
+    constexpr int NTH = 256 * kCommitSlices;
+    const int n = A.n, eta = A.eta;
+    if (eta == 0) return;
+    const int64_t t0 = A.t0;
+    const T* kin = reinterpret_cast<const T*>(A.k) + (int64_t)bh * n * DK;
+    const T* vin = reinterpret_cast<const T*>(A.v) + (int64_t)bh * n * DV;
+    T* ringK = reinterpret_cast<T*>(A.win_k) + (int64_t)bh * eta * DK;
+    T* ringV = reinterpret_cast<T*>(A.win_v) + (int64_t)bh * eta * DV;
+    const int64_t plo = max(t0, t0 + n - eta);
+    const int cnt = (int)(t0 + n - plo);
+    const int slot0 = (int)(plo % eta);                 // ring slot of plo; later ones follow (x < eta)
+    const int items = cnt * 2 * CPR;
+    for (int i0 = tid; i0 < items; i0 += NTH * UN) {
+        uint4 val[UN];
+        T* dst[UN];
 #pragma unroll
-            for (int u = 0; u < UN; ++u) {
-                const int it = i0 + 256 * u;
-                dst[u] = nullptr;
-                if (it >= items) continue;
-                const int x = it / (2 * CPR), rem = it % (2 * CPR), isv = rem / CPR, p = rem % CPR;
-                const int64_t pos = plo + x;
-                const int slot = slot0 + x >= eta ? slot0 + x - eta : slot0 + x;
-                val[u] = *reinterpret_cast<const uint4*>((isv ? vin : kin) + (pos - t0) * DK + p * EPV);
-                dst[u] = (isv ? ringV : ringK) + (int64_t)slot * DK + p * EPV;
-            }
-#pragma unroll
-            for (int u = 0; u < UN; ++u)
-                if (dst[u]) *reinterpret_cast<uint4*>(dst[u]) = val[u];
+        for (int u = 0; u < UN; ++u) {
+            const int it = i0 + NTH * u;
+            dst[u] = nullptr;
+            if (it >= items) continue;
+            const int x = it / (2 * CPR), rem = it % (2 * CPR), isv = rem / CPR, p = rem % CPR;
+            const int64_t pos = plo + x;
+            const int slot = slot0 + x >= eta ? slot0 + x - eta : slot0 + x;
+            val[u] = *reinterpret_cast<const uint4*>((isv ? vin : kin) + (pos - t0) * DK + p * EPV);
+            dst[u] = (isv ? ringV : ringK) + (int64_t)slot * DK + p * EPV;
         }
+#pragma unroll
+        for (int u = 0; u < UN; ++u)
+            if (dst[u]) *reinterpret_cast<uint4*>(dst[u]) = val[u];
     }
+}
+
+template <typename T, int DK>
+static hipError_t launch_commit(const PrefillArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL((commit_cache_kernel<T, DK>), dim3(a.BH, kCommitSlices), dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((commit_ring_kernel<T, DK>), dim3(a.BH, kCommitSlices), dim3(256), 0, stream, a);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -492,8 +513,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a0, hipStream_t stream, hipEvent_
         if ((e = record(ev, 2, stream)) != hipSuccess) return e;
         if ((e = launch_readout<T, DK, PHI>(a, 0, a.nchunks, stream)) != hipSuccess) return e;
         if ((e = record(ev, 3, stream)) != hipSuccess) return e;
-        hipLaunchKernelGGL((commit_kernel<T, DK>), dim3(a.BH), dim3(256), 0, stream, a);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = launch_commit<T, DK>(a, stream)) != hipSuccess) return e;
         return record(ev, 4, stream);
     }
     // Overlapped: the chain walks the chunk ranges on the caller's stream; the read-out of a range
@@ -514,8 +534,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a0, hipStream_t stream, hipEvent_
     if ((e = hipStreamWaitEvent(stream, side->join, 0)) != hipSuccess) return e;
     a.c_begin = 0;
     a.c_end = a.nchunks;
-    hipLaunchKernelGGL((commit_kernel<T, DK>), dim3(a.BH), dim3(256), 0, stream, a);
-    return hipGetLastError();
+    return launch_commit<T, DK>(a, stream);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int d, int phi_kind, hipStream_t stream,
