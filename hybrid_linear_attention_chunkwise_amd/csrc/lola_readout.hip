@@ -323,97 +323,84 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
     }
 }
 
-// Commit, in two launches so that every workgroup can work on any slice of a (sequence, head):
+// Commit, one workgroup per (sequence, head), in two phases split by a barrier:
 //  1. the final cache members' K/V into the state's slots (a member may come from the initial window
 //     ring, so this completes before the ring is overwritten), and the slots' positions;
 //  2. the last eta input tokens into the window ring.
-// Rows move as 16-byte pieces; each thread has UN loads in flight.  Grid: (B*h, kCommitSlices).
-constexpr int kCommitSlices = 8;
+// Rows move as 16-byte pieces; each thread has UN loads in flight.
+constexpr int kCommitThreads = 1024;
 
 template <typename T, int DK>
-__global__ __launch_bounds__(256) void commit_cache_kernel(PrefillArgs A) {
-    constexpr int DV = DK, EPV = 16 / (int)sizeof(T), CPR = DK / EPV, UN = 4;
-    const int bh = blockIdx.x, tid = threadIdx.x + 256 * blockIdx.y;
-    constexpr int NTH = 256 * kCommitSlices;
+__global__ __launch_bounds__(kCommitThreads) void commit_kernel(PrefillArgs A) {
+    constexpr int DV = DK, EPV = 16 / (int)sizeof(T), CPR = DK / EPV, UN = 4, NTH = kCommitThreads;
+    const int bh = blockIdx.x, tid = threadIdx.x;
     const int n = A.n, eta = A.eta, lam = A.lam;
-    if (lam == 0) return;
-    const char* wsb = A.ws + (int64_t)bh * A.L.per_bh;
-    const int* fp = reinterpret_cast<const int*>(wsb + A.L.slot_pos);
-    const int* fs = reinterpret_cast<const int*>(wsb + A.L.slot_src);
-    const T* kin = reinterpret_cast<const T*>(A.k) + (int64_t)bh * n * DK;
-    const T* vin = reinterpret_cast<const T*>(A.v) + (int64_t)bh * n * DV;
-    T* cK = reinterpret_cast<T*>(A.cache_k) + (int64_t)bh * lam * DK;
-    T* cV = reinterpret_cast<T*>(A.cache_v) + (int64_t)bh * lam * DV;
-    const T* ringK = eta > 0 ? reinterpret_cast<const T*>(A.win_k) + (int64_t)bh * eta * DK : nullptr;
-    const T* ringV = eta > 0 ? reinterpret_cast<const T*>(A.win_v) + (int64_t)bh * eta * DV : nullptr;
-    int32_t* cpos = A.cache_pos + (int64_t)bh * lam;
-    const int items = lam * 2 * CPR;                     // (slot, K or V, piece)
-    for (int i0 = tid; i0 < items; i0 += NTH * UN) {
-        uint4 val[UN];
-        T* dst[UN];
-#pragma unroll
-        for (int u = 0; u < UN; ++u) {
-            const int it = i0 + NTH * u;
-            dst[u] = nullptr;
-            if (it >= items) continue;
-            const int j = it / (2 * CPR), rem = it % (2 * CPR), isv = rem / CPR, p = rem % CPR;
-            const int src = fs[j];
-            if (src < 0 || src == n + j) continue;        // empty, or a member that kept its slot
-            const T* row;
-            if (src < n) row = (isv ? vin : kin) + (int64_t)src * DK;
-            else row = (isv ? ringV : ringK) + (int64_t)(src - n - lam) * DK;
-            val[u] = *reinterpret_cast<const uint4*>(row + p * EPV);
-            dst[u] = (isv ? cV : cK) + (int64_t)j * DK + p * EPV;
-        }
-#pragma unroll
-        for (int u = 0; u < UN; ++u)
-            if (dst[u]) *reinterpret_cast<uint4*>(dst[u]) = val[u];
-    }
-    for (int j = tid; j < lam; j += NTH) cpos[j] = fp[j];
-}
-
-template <typename T, int DK>
-__global__ __launch_bounds__(256) void commit_ring_kernel(PrefillArgs A) {
-    constexpr int DV = DK, EPV = 16 / (int)sizeof(T), CPR = DK / EPV, UN = 4;
-    const int bh = blockIdx.x, tid = threadIdx.x + 256 * blockIdx.y;
-    constexpr int NTH = 256 * kCommitSlices;
-    const int n = A.n, eta = A.eta;
-    if (eta == 0) return;
     const int64_t t0 = A.t0;
     const T* kin = reinterpret_cast<const T*>(A.k) + (int64_t)bh * n * DK;
     const T* vin = reinterpret_cast<const T*>(A.v) + (int64_t)bh * n * DV;
-    T* ringK = reinterpret_cast<T*>(A.win_k) + (int64_t)bh * eta * DK;
-    T* ringV = reinterpret_cast<T*>(A.win_v) + (int64_t)bh * eta * DV;
-    const int64_t plo = max(t0, t0 + n - eta);
-    const int cnt = (int)(t0 + n - plo);
-    const int slot0 = (int)(plo % eta);                 // ring slot of plo; later ones follow (x < eta)
-    const int items = cnt * 2 * CPR;
-    for (int i0 = tid; i0 < items; i0 += NTH * UN) {
-        uint4 val[UN];
-        T* dst[UN];
+    T* ringK = eta > 0 ? reinterpret_cast<T*>(A.win_k) + (int64_t)bh * eta * DK : nullptr;
+    T* ringV = eta > 0 ? reinterpret_cast<T*>(A.win_v) + (int64_t)bh * eta * DV : nullptr;
+    if (lam > 0) {
+        const char* wsb = A.ws + (int64_t)bh * A.L.per_bh;
+        const int* fp = reinterpret_cast<const int*>(wsb + A.L.slot_pos);
+        const int* fs = reinterpret_cast<const int*>(wsb + A.L.slot_src);
+        T* cK = reinterpret_cast<T*>(A.cache_k) + (int64_t)bh * lam * DK;
+        T* cV = reinterpret_cast<T*>(A.cache_v) + (int64_t)bh * lam * DV;
+        int32_t* cpos = A.cache_pos + (int64_t)bh * lam;
+        const int items = lam * 2 * CPR;                 // (slot, K or V, piece)
+        for (int i0 = tid; i0 < items; i0 += NTH * UN) {
+            uint4 val[UN];
+            T* dst[UN];
 #pragma unroll
-        for (int u = 0; u < UN; ++u) {
-            const int it = i0 + NTH * u;
-            dst[u] = nullptr;
-            if (it >= items) continue;
-            const int x = it / (2 * CPR), rem = it % (2 * CPR), isv = rem / CPR, p = rem % CPR;
-            const int64_t pos = plo + x;
-            const int slot = slot0 + x >= eta ? slot0 + x - eta : slot0 + x;
-            val[u] = *reinterpret_cast<const uint4*>((isv ? vin : kin) + (pos - t0) * DK + p * EPV);
-            dst[u] = (isv ? ringV : ringK) + (int64_t)slot * DK + p * EPV;
+            for (int u = 0; u < UN; ++u) {
+                const int it = i0 + NTH * u;
+                dst[u] = nullptr;
+                if (it >= items) continue;
+                const int j = it / (2 * CPR), rem = it % (2 * CPR), isv = rem / CPR, pc = rem % CPR;
+                const int src = fs[j];
+                if (src < 0 || src == n + j) continue;    // empty, or a member that kept its slot
+                const T* row;
+                if (src < n) row = (isv ? vin : kin) + (int64_t)src * DK;
+                else row = (isv ? ringV : ringK) + (int64_t)(src - n - lam) * DK;
+                val[u] = *reinterpret_cast<const uint4*>(row + pc * EPV);
+                dst[u] = (isv ? cV : cK) + (int64_t)j * DK + pc * EPV;
+            }
+#pragma unroll
+            for (int u = 0; u < UN; ++u)
+                if (dst[u]) *reinterpret_cast<uint4*>(dst[u]) = val[u];
         }
+        for (int j = tid; j < lam; j += NTH) cpos[j] = fp[j];
+    }
+    __syncthreads();                                     // every read of the old ring is done
+    if (eta > 0) {
+        const int64_t plo = max(t0, t0 + n - eta);
+        const int cnt = (int)(t0 + n - plo);
+        const int slot0 = (int)(plo % eta);             // ring slot of plo; later ones follow (x < eta)
+        const int items = cnt * 2 * CPR;
+        for (int i0 = tid; i0 < items; i0 += NTH * UN) {
+            uint4 val[UN];
+            T* dst[UN];
 #pragma unroll
-        for (int u = 0; u < UN; ++u)
-            if (dst[u]) *reinterpret_cast<uint4*>(dst[u]) = val[u];
+            for (int u = 0; u < UN; ++u) {
+                const int it = i0 + NTH * u;
+                dst[u] = nullptr;
+                if (it >= items) continue;
+                const int x = it / (2 * CPR), rem = it % (2 * CPR), isv = rem / CPR, pc = rem % CPR;
+                const int64_t pos = plo + x;
+                const int slot = slot0 + x >= eta ? slot0 + x - eta : slot0 + x;
+                val[u] = *reinterpret_cast<const uint4*>((isv ? vin : kin) + (pos - t0) * DK + pc * EPV);
+                dst[u] = (isv ? ringV : ringK) + (int64_t)slot * DK + pc * EPV;
+            }
+#pragma unroll
+            for (int u = 0; u < UN; ++u)
+                if (dst[u]) *reinterpret_cast<uint4*>(dst[u]) = val[u];
+        }
     }
 }
 
 template <typename T, int DK>
 static hipError_t launch_commit(const PrefillArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((commit_cache_kernel<T, DK>), dim3(a.BH, kCommitSlices), dim3(256), 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((commit_ring_kernel<T, DK>), dim3(a.BH, kCommitSlices), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((commit_kernel<T, DK>), dim3(a.BH), dim3(kCommitThreads), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -476,16 +463,21 @@ static hipError_t launch_chain_range(PrefillArgs a, int c0, int c1, hipStream_t 
     return launch_chain_t<T, DK, PHI>(a, stream);
 }
 
-// Chunk ranges for the overlapped schedule: sizes shrink toward the end (each about 0.6 of the one
-// before), so the read-out of the last range, the only one not hidden behind the chain, is short.
-static int split_chunks(int nchunks, int* bounds, int max_seg) {
-    int sizes[16];
-    int k = 0, sum = 0, sz = nchunks / 16 > 2 ? nchunks / 16 : 2;
+// Chunk ranges for the overlapped schedule.  Only the read-out of the last range is not hidden behind
+// the chain, and a read-out workgroup takes about as long however many run beside it, so the last
+// range holds as many chunks as one wave of workgroups covers (ncu / per_chunk, at least 2).  Going
+// backwards each range doubles: the read-out of a range (on the compute units the chain leaves free)
+// then still finishes before the chain finishes the next one, and there are few launches.
+static int split_chunks(int nchunks, int per_chunk, int ncu, int* bounds, int max_seg) {
+    int sizes[kMaxSegments];
+    int k = 0, sum = 0;
+    int sz = per_chunk > 0 ? (ncu + per_chunk - 1) / per_chunk : 2;
+    sz = sz < 2 ? 2 : sz;
     while (k < max_seg && sum < nchunks) {               // from the last range backwards
         const int take = sz < nchunks - sum ? sz : nchunks - sum;
         sizes[k++] = take;
         sum += take;
-        sz = (sz * 5 + 2) / 3;
+        sz *= 2;
     }
     if (sum < nchunks) sizes[k - 1] += nchunks - sum;   // out of ranges: the first one takes the rest
     if (k >= 2 && sizes[k - 1] < sizes[k - 2]) {         // a short remainder joins its neighbour
@@ -495,6 +487,19 @@ static int split_chunks(int nchunks, int* bounds, int max_seg) {
     bounds[0] = 0;
     for (int i = 0; i < k; ++i) bounds[i + 1] = bounds[i] + sizes[k - 1 - i];
     return k;
+}
+
+static int device_cus() {
+    static int ncu = 0;
+    if (ncu == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            ncu = v;
+        else
+            ncu = 256;
+    }
+    return ncu;
 }
 
 template <typename T, int DK, int PHI>
@@ -522,7 +527,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a0, hipStream_t stream, hipEvent_
     // (and capturable) as one unit.
     std::lock_guard<std::mutex> guard(side->mu);
     int bounds[kMaxSegments + 1];
-    const int nseg = split_chunks(a.nchunks, bounds, kMaxSegments);
+    const int nseg = split_chunks(a.nchunks, a.BH * a.nqt, device_cus(), bounds, kMaxSegments);
     if ((e = launch_phi_t<T, DK, PHI>(a, stream)) != hipSuccess) return e;
     for (int i = 0; i < nseg; ++i) {
         if ((e = launch_chain_range<T, DK, PHI>(a, bounds[i], bounds[i + 1], stream)) != hipSuccess) return e;
@@ -530,11 +535,16 @@ hipError_t launch_prefill_t(const PrefillArgs& a0, hipStream_t stream, hipEvent_
         if ((e = hipStreamWaitEvent(side->stream, side->seg[i], 0)) != hipSuccess) return e;
         if ((e = launch_readout<T, DK, PHI>(a, bounds[i], bounds[i + 1], side->stream)) != hipSuccess) return e;
     }
-    if ((e = hipEventRecord(side->join, side->stream)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(stream, side->join, 0)) != hipSuccess) return e;
+    // The commit overwrites the state's cache and window rows.  A call that starts from an empty
+    // state (t = 0: no cache member, no window token) never reads those rows in the read-out, so its
+    // commit runs on the caller's stream beside the last read-out; otherwise it follows the last
+    // read-out on the side stream.  Then the caller's stream joins.
     a.c_begin = 0;
     a.c_end = a.nchunks;
-    return launch_commit<T, DK>(a, stream);
+    const bool fresh = a.t0 == 0;
+    if ((e = launch_commit<T, DK>(a, fresh ? stream : side->stream)) != hipSuccess) return e;
+    if ((e = hipEventRecord(side->join, side->stream)) != hipSuccess) return e;
+    return hipStreamWaitEvent(stream, side->join, 0);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int d, int phi_kind, hipStream_t stream,
