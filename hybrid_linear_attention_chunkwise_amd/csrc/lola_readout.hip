@@ -17,6 +17,7 @@
 #include "lola_internal.hpp"
 
 #include <mutex>
+#include <type_traits>
 
 namespace lola {
 
@@ -60,6 +61,8 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
     __shared__ int sKeyBand[KB];
     __shared__ int sFoldPos[128];
     __shared__ int sFoldSrc[128];
+    __shared__ int sCachePos[kMaxLambda];
+    __shared__ int sCacheSrc[kMaxLambda];
 
     const int nqt = A.nqt, nseg = A.c_end - A.c_begin;
     const int bid = blockIdx.x;
@@ -102,8 +105,9 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
     const int NK = nb + lam;
     const int blo_slot = eta > 0 ? (int)(blo % eta) : 0;    // ring slot of the first band key
     const int nblk = (NK + KB - 1) / KB;
-    // key kk -> (position, band?, K row, V row); position -1 = no key
-    auto key_rows = [&](int kk, int& pos, int& band, const T*& rk, const T*& rv) {
+    // key kk -> (position, band?, K row, V row); position -1 = no key.  The chunk's cache list is read
+    // from memory for the first block and from its LDS copy after that (one memory latency per block).
+    auto key_rows = [&](int kk, int& pos, int& band, const T*& rk, const T*& rv, auto fromLds) {
         pos = -1; band = 0; rk = nullptr; rv = nullptr;
         if (kk < nb) {
             const int64_t ps = blo + kk;
@@ -117,10 +121,10 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
             }
         } else if (kk < NK) {
             const int jj = kk - nb;
-            const int p = cachePos[jj];
+            const int p = decltype(fromLds)::value ? sCachePos[jj] : cachePos[jj];
             if (p >= 0) {
                 pos = p;
-                const int src = cacheSrc[jj];
+                const int src = decltype(fromLds)::value ? sCacheSrc[jj] : cacheSrc[jj];
                 if (src < n) { rk = kin + (int64_t)src * DK; rv = vin + (int64_t)src * DV; }
                 else if (src < n + lam) { rk = cK + (int64_t)(src - n) * DK; rv = cV + (int64_t)(src - n) * DV; }
                 else { rk = ringK + (int64_t)(src - n - lam) * DK; rv = ringV + (int64_t)(src - n - lam) * DV; }
@@ -129,7 +133,7 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
     };
     uint4 kst[KPT], vst[TPW][VPT];
     int vpos[TPW], vband[TPW];
-    auto prefetch = [&](int kb) {
+    auto prefetch = [&](int kb, auto fromLds) {
 #pragma unroll
         for (int u = 0; u < KPT; ++u) {
             const int q = tid + 256 * u;
@@ -137,7 +141,7 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
             int pos, band;
             const T* rk;
             const T* rv;
-            key_rows(kb * KB + j, pos, band, rk, rv);
+            key_rows(kb * KB + j, pos, band, rk, rv, fromLds);
             kst[u] = rk ? *reinterpret_cast<const uint4*>(rk + p * EPV) : make_uint4(0, 0, 0, 0);
         }
         {   // values: thread -> (TPW consecutive keys, one column group)
@@ -146,18 +150,19 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
             for (int z = 0; z < TPW; ++z) {
                 const T* rk;
                 const T* rv;
-                key_rows(kb * KB + j0 + z, vpos[z], vband[z], rk, rv);
+                key_rows(kb * KB + j0 + z, vpos[z], vband[z], rk, rv, fromLds);
 #pragma unroll
                 for (int u = 0; u < VPT; ++u)
                     vst[z][u] = rv ? *reinterpret_cast<const uint4*>(rv + cg * VD + u * EPV) : make_uint4(0, 0, 0, 0);
             }
         }
     };
-    if (nblk > 0) prefetch(0);
+    if (nblk > 0) prefetch(0, std::false_type{});
 
     stage_wt<T, DK, DW, 256>(wt, WT_LD, A.W);
     for (int d = tid; d < D; d += 256) sS[d] = snapS[d];
     for (int i = tid; i < nf; i += 256) { sFoldPos[i] = foldPos[i]; sFoldSrc[i] = foldSrc[i]; }
+    for (int j = tid; j < lam; j += 256) { sCachePos[j] = cachePos[j]; sCacheSrc[j] = cacheSrc[j]; }
     __syncthreads();
 
     const int64_t tq = q0 + 16 * w + c;          // this lane's query (column c of the wave's tile)
@@ -200,7 +205,7 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
                 for (int z = 0; z < TPW; ++z) { sKeyPos[j0 + z] = vpos[z]; sKeyBand[j0 + z] = vband[z]; }
         }
         __syncthreads();
-        if (kb + 1 < nblk) prefetch(kb + 1);
+        if (kb + 1 < nblk) prefetch(kb + 1, std::true_type{});
         if (wave_active) {
             f4 st[KB / 16];
 #pragma unroll
