@@ -492,10 +492,29 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
             __syncthreads();
         }
 
-        // (4) prefix counts: fold order over the table, freed cache slots, entrants (kept leaving tokens)
-        const int nS = ballot_prefix(NR, NW, [&](int r) { return flag[r] == 2; }, a1);
-        ballot_prefix(lam, NW, [&](int j) { return slotPos[j] < 0 || flag[j] == 2; }, a2);
-        const int nE = ballot_prefix(nX, NW, [&](int x) { return flag[xb + x] == 1; }, a3);
+        // (4) prefix counts, all three in one pass over the table (one LDS read of each row): fold order
+        // over the table (a1), freed cache slots (a2), entrants, the kept leaving tokens (a3).  Every
+        // wave ballots every 64-row group and writes the prefixes of the groups it owns.
+        int nS = 0, nE = 0;
+        {
+            const unsigned long long lt = l ? (~0ull >> (64 - l)) : 0ull;
+            int nFree = 0;
+#pragma unroll 2
+            for (int k = 0; k * 64 < NR; ++k) {
+                const int r = k * 64 + l;
+                const int f = r < NR ? flag[r] : 0;
+                const bool p2 = r < lam && (slotPos[r] < 0 || f == 2);
+                const unsigned long long m1 = __ballot(f == 2), m2 = __ballot(p2), m3 = __ballot(r >= xb && f == 1);
+                if (k % NW == w && r < NR) {
+                    a1[r] = nS + __popcll(m1 & lt);
+                    if (r < lam) a2[r] = nFree + __popcll(m2 & lt);
+                    if (r >= xb) a3[r - xb] = nE + __popcll(m3 & lt);
+                }
+                nS += __popcll(m1);
+                nFree += __popcll(m2);
+                nE += __popcll(m3);
+            }
+        }
         __syncthreads();
         // (5) the fold list (recorded for the read-out kernel) and the entrant list
         {
