@@ -78,7 +78,7 @@ __host__ __device__ constexpr int x_base(int lam) { return (lam + 15) & ~15; }
 __host__ __device__ constexpr int cand_rows(int lam, int C) { return ((x_base(lam) + C + 63) / 64) * 64; }
 
 struct ChainLds {
-    size_t s, slot_pos, slot_src, c_src, c_pos, key, aux, flag, a1, a2, a3, fold_row, ent_row, slot_of_x,
+    size_t s, slot_pos, slot_src, c_src, c_pos, key, aux, flag, a1, a2, a3, fold_src, ent_row, ent_pos, ent_src, slot_of_x,
         hist, tmp, hcopy, stage, total;
 };
 
@@ -105,8 +105,10 @@ __host__ __device__ constexpr ChainLds chain_lds() {
     o.a1 = p;        p = al16(p + sizeof(int) * nr);
     o.a2 = p;        p = al16(p + sizeof(int) * (lam + 1));
     o.a3 = p;        p = al16(p + sizeof(int) * (C + 1));
-    o.fold_row = p;  p = al16(p + sizeof(int) * (C + 1));
+    o.fold_src = p;  p = al16(p + sizeof(int) * (C + 1));
     o.ent_row = p;   p = al16(p + sizeof(int) * (C + 1));
+    o.ent_pos = p;   p = al16(p + sizeof(int) * (C + 1));
+    o.ent_src = p;   p = al16(p + sizeof(int) * (C + 1));
     o.slot_of_x = p; p = al16(p + sizeof(int) * (C + 1));
     o.hist = p;      p = al16(p + sizeof(int) * (Cfg::NBIN + 4));
     o.tmp = p;       p = al16(p + sizeof(int) * 32);
@@ -122,14 +124,6 @@ __device__ __forceinline__ unsigned long long keep_key(float sre, int pos) {
     return ((unsigned long long)__float_as_uint(sre) << 32) | (unsigned long long)(0xFFFFFFFFu - (unsigned)pos);
 }
 
-__device__ __forceinline__ unsigned wave_min_u32(unsigned x) {
-    for (int o = 32; o > 0; o >>= 1) x = min(x, (unsigned)__shfl_xor((int)x, o));
-    return x;
-}
-__device__ __forceinline__ unsigned wave_max_u32(unsigned x) {
-    for (int o = 32; o > 0; o >>= 1) x = max(x, (unsigned)__shfl_xor((int)x, o));
-    return x;
-}
 
 // Where a token's V and features live during the call (see the source index in lola_internal.hpp).
 template <typename T, int DK>
@@ -169,8 +163,10 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
     int* a1 = reinterpret_cast<int*>(smem + lo.a1);
     int* a2 = reinterpret_cast<int*>(smem + lo.a2);
     int* a3 = reinterpret_cast<int*>(smem + lo.a3);
-    int* foldRow = reinterpret_cast<int*>(smem + lo.fold_row);
-    int* entRow = reinterpret_cast<int*>(smem + lo.ent_row);
+    int* foldSrcL = reinterpret_cast<int*>(smem + lo.fold_src);   // source of the k-th folded token
+    int* entRow = reinterpret_cast<int*>(smem + lo.ent_row);      // k-th entrant: leaving-token index,
+    int* entPos = reinterpret_cast<int*>(smem + lo.ent_pos);      // position
+    int* entSrc = reinterpret_cast<int*>(smem + lo.ent_src);      // and source
     int* slotOfX = reinterpret_cast<int*>(smem + lo.slot_of_x);
     int* hist = reinterpret_cast<int*>(smem + lo.hist);
     int* tmp = reinterpret_cast<int*>(smem + lo.tmp);
@@ -431,8 +427,9 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
                 }
             }
             // the SRE range for the histogram
-            mn = wave_min_u32(mn);
-            mx = wave_max_u32(mx);
+            // (non-negative floats order like their bit patterns)
+            mn = __float_as_uint(wave_min(__uint_as_float(mn)));
+            mx = __float_as_uint(wave_max(__uint_as_float(mx)));
             if (l == 0) { tmp[8 + w] = (int)mn; tmp[16 + w] = (int)mx; }
             for (int i = tid; i < NBIN; i += NT) hist[i] = 0;
             if (tid == 0) tmp[4] = 0;
@@ -454,9 +451,7 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
                 int v4[4], s4 = 0;
 #pragma unroll
                 for (int u = 0; u < 4; ++u) { v4[u] = hist[4 * l + u]; s4 += v4[u]; }
-                int x = s4;
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) { const int y = __shfl_up(x, o); if (l >= o) x += y; }
+                const int x = wave_inclusive_sum(s4);
                 int run = x - s4, bstar = -1, need = 0;
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
@@ -466,8 +461,8 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
                 // every wave finds the same (bin, need); spread it from the owning lane
                 const unsigned long long own = __ballot(bstar >= 0);
                 const int srcl = __ffsll((long long)own) - 1;
-                bstar = __shfl(bstar, srcl);
-                need = __shfl(need, srcl);
+                bstar = __builtin_amdgcn_readlane(bstar, srcl);
+                need = __builtin_amdgcn_readlane(need, srcl);
                 int* blist = aux;                                 // members of the boundary bin
                 for (int r = tid; r < NR; r += NT) {
                     if (!flag[r]) continue;
@@ -522,15 +517,20 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
             int* recFoldSrc = reinterpret_cast<int*>(rec + A.L.c_fold_src);
             for (int r = tid; r < NR; r += NT) {
                 if (flag[r] != 2) continue;
-                const int k = a1[r], pos = cPos[r];
-                foldRow[k] = r;
+                const int k = a1[r], pos = cPos[r], sr = cSrc[r];
+                foldSrcL[k] = sr;
                 recFoldPos[k] = pos;
-                recFoldSrc[k] = cSrc[r];
+                recFoldSrc[k] = sr;
                 if (foldAt && pos >= t0) foldAt[pos - t0] = ch;
             }
             if (tid == 0) *reinterpret_cast<int*>(rec + A.L.c_fold_n) = nS;
             for (int x = tid; x < nX; x += NT)
-                if (flag[xb + x] == 1) entRow[a3[x]] = x;
+                if (flag[xb + x] == 1) {
+                    const int k = a3[x];
+                    entRow[k] = x;
+                    entPos[k] = cPos[xb + x];
+                    entSrc[k] = cSrc[xb + x];
+                }
         }
         __syncthreads();
         uint4 stg[FLPT];
@@ -546,7 +546,7 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
                     const int k = fb * FB + m0 + z;
                     uint4 val = make_uint4(0, 0, 0, 0);
                     if (k < nS) {
-                        const int s_ = cSrc[foldRow[k]];
+                        const int s_ = foldSrcL[k];
                         const T* p_ = pc < CPHI ? src.phi_row(s_) + pc * EPV : src.v_row(s_) + (pc - CPHI) * EPV;
                         val = *reinterpret_cast<const uint4*>(p_);
                     }
@@ -560,10 +560,9 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
             if (slotPos[j] >= 0 && flag[j] != 2) continue;
             const int k = a2[j];
             if (k < nE) {
-                const int x = entRow[k];
-                slotPos[j] = cPos[xb + x];
-                slotSrc[j] = cSrc[xb + x];
-                slotOfX[x] = j;
+                slotPos[j] = entPos[k];
+                slotSrc[j] = entSrc[k];
+                slotOfX[entRow[k]] = j;
             } else {
                 slotPos[j] = -1;
                 slotSrc[j] = -1;
@@ -582,9 +581,8 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
                 }
             } else {
                 rows_to_mirror(nE, [&](int e, int& slot, int& s_) {
-                    const int x = entRow[e];
-                    slot = slotOfX[x];
-                    s_ = cSrc[xb + x];
+                    slot = slotOfX[entRow[e]];
+                    s_ = entSrc[e];
                 });
             }
         }

@@ -203,6 +203,29 @@ __device__ __forceinline__ float wave_max(float x) {
     x = fmaxf(x, dpp_mov<0x128>(x));
     return max_groups(x);
 }
+__device__ __forceinline__ float wave_min(float x) {
+    x = fminf(x, dpp_mov<0xB1>(x));
+    x = fminf(x, dpp_mov<0x4E>(x));
+    x = fminf(x, dpp_mov<0x124>(x));
+    x = fminf(x, dpp_mov<0x128>(x));
+    return min_groups(x);
+}
+// Inclusive prefix sum over the whole wave: row_shr steps inside each 16-lane row, then the totals
+// of the earlier rows (VALU and scalar reads only, no LDS).
+template <int CTRL>
+__device__ __forceinline__ int dpp_shr_i(int x) {
+    return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, true);
+}
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+    x += dpp_shr_i<0x111>(x);
+    x += dpp_shr_i<0x112>(x);
+    x += dpp_shr_i<0x114>(x);
+    x += dpp_shr_i<0x118>(x);
+    const int row = lane_id() >> 4;
+    const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
+              r2 = __builtin_amdgcn_readlane(x, 47);
+    return x + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
 // Over the 16 columns of one lane group: a row of an accumulator tile.
 __device__ __forceinline__ float sum_cols(float x) {
     x += __shfl_xor(x, 1);
