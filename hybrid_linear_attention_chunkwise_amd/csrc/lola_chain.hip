@@ -227,14 +227,28 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
     // accumulator order (one 16-byte or 8-byte piece per lane and register, contiguous across the
     // wave).  Leaving-token tiles come from their rows; a lane without a candidate reads input row 0
     // instead, so the loads need no branch (its column of the products is never used).
+    // Mirror values: a lane's quads of VP consecutive row tiles sit together (one 16-byte piece), so
+    // a tile's values take NW / VP loads.
+    constexpr int VP = sizeof(T) == 2 ? 2 : 1;
+    auto mir_v_off = [&](int tile, int wv, int lane) {
+        return mirVoff + (((tile * (NW / VP) + wv / VP) * 64 + lane) * VP + wv % VP) * 4;
+    };
     auto load_tile = [&](CandTile<T, D, NW>& t, int j) {
         if (j < ct) {
             const T* b = mirPhi + ((int64_t)j * (D / 32) * 64 + l) * 8;
 #pragma unroll
             for (int ss = 0; ss < D / 32; ++ss) t.f[ss] = *reinterpret_cast<const Frag8<T>*>(b + ss * 64 * 8);
-            const T* bv = mirPhi + mirVoff + ((int64_t)j * NW * 64 + l) * 4;
+            const T* bv = mirPhi + mir_v_off(j, 0, l);
 #pragma unroll
-            for (int wv = 0; wv < NW; ++wv) t.v[wv] = load_quad(bv + wv * 64 * 4);
+            for (int wp = 0; wp < NW / VP; ++wp) {
+                if constexpr (VP == 2) {
+                    const uint4 x = *reinterpret_cast<const uint4*>(bv + wp * 64 * 8);
+                    __builtin_memcpy(&t.v[2 * wp], &x, 8);
+                    __builtin_memcpy(&t.v[2 * wp + 1], reinterpret_cast<const char*>(&x) + 8, 8);
+                } else {
+                    t.v[wp] = load_quad(bv + wp * 64 * 4);
+                }
+            }
         } else {
             const int row = 16 * j + c;                       // < nrp: tiles never pass the table
             const int f = flag[row], s0 = cSrc[row];
@@ -253,9 +267,18 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
         T* b = mirPhi + ((int64_t)(slot >> 4) * (D / 32) * 64 + g * 16 + (slot & 15)) * 8;
 #pragma unroll
         for (int ss = 0; ss < D / 32; ++ss) *reinterpret_cast<Frag8<T>*>(b + ss * 64 * 8) = t.f[ss];
-        T* bv = mirPhi + mirVoff + ((int64_t)(slot >> 4) * NW * 64 + g * 16 + (slot & 15)) * 4;
+        T* bv = mirPhi + mir_v_off(slot >> 4, 0, g * 16 + (slot & 15));
 #pragma unroll
-        for (int wv = 0; wv < NW; ++wv) store_quad(bv + wv * 64 * 4, t.v[wv]);
+        for (int wp = 0; wp < NW / VP; ++wp) {
+            if constexpr (VP == 2) {
+                uint4 x;
+                __builtin_memcpy(&x, &t.v[2 * wp], 8);
+                __builtin_memcpy(reinterpret_cast<char*>(&x) + 8, &t.v[2 * wp + 1], 8);
+                *reinterpret_cast<uint4*>(bv + wp * 64 * 8) = x;
+            } else {
+                store_quad(bv + wp * 64 * 4, t.v[wp]);
+            }
+        }
     };
     // Copy rows into the slot mirror from their sources: info(e, slot, source) names item e; a
     // negative source skips it.  A row is QPR four-element pieces (features, then values); each
@@ -283,7 +306,7 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
                         } else {                              // value piece (wv, gg)
                             const int iv = it - D / 4, wv = iv >> 2, gg = iv & 3;
                             qv[u] = load_quad(src.v_row(s_) + 16 * wv + 4 * gg);
-                            doff[u] = mirVoff + ((tile * NW + wv) * 64 + gg * 16 + cc) * 4;
+                            doff[u] = mir_v_off(tile, wv, gg * 16 + cc);
                         }
                     }
                 }

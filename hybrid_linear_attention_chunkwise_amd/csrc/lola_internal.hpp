@@ -17,7 +17,7 @@ struct WsLayout {
     int64_t slot_pos;      // [lam] int32      : final cache table after the call (position, -1 empty)
     int64_t slot_src;      // [lam] int32      : where each final member's K/V come from (see Src below)
     int64_t mir_phi;       // [lam16/16][D/32][64][8] T: features of the cache slots, MFMA operand order
-    int64_t mir_v;         // [lam16/16][d_v/16][64][4] T: values of the cache slots, accumulator order
+    int64_t mir_v;         // [lam16/16][d_v/32][64][2][4] T (bf16; fp32: [d_v/16][64][4]): cache slots' values, accumulator order
     int64_t chunk0;        // first per-chunk record
     int64_t per_chunk;     // bytes per chunk record
     // offsets inside a chunk record
