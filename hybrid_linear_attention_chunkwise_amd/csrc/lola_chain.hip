@@ -353,15 +353,20 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
     if (first) rows_to_mirror(lam, [&](int e, int& slot, int& s_) { slot = e; s_ = slotSrc[e]; });
     build_table(A.c_begin);
     __syncthreads();
+    // The first two tiles of each wave (cur, nxt) are fetched before the chunk starts.
     bool prefetched = false;
-    {
-        int64_t xlo0;
-        const int nX0 = chunk_x(A.c_begin, xlo0);
-        if (lam > 0 && nG + nX0 > lam) {
-            if (w < (xb + nX0 + 15) / 16) load_tile(cur, w);
+    auto prefetch_first = [&](int ch_) {
+        int64_t xl;
+        const int nX_ = chunk_x(ch_, xl);
+        prefetched = false;
+        if (lam > 0 && nG + nX_ > lam) {
+            const int nt = (xb + nX_ + 15) / 16;
+            if (w < nt) load_tile(cur, w);
+            if (PREF && w + NW < nt) load_tile(nxt, w + NW);
             prefetched = true;
         }
-    }
+    };
+    prefetch_first(A.c_begin);
 
     // ---------------- chunk loop ----------------
     for (int ch = A.c_begin; ch < A.c_end; ++ch) {
@@ -397,7 +402,7 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
             if (!prefetched && w < ntile) load_tile(cur, w);
             for (int j = w; j < ntile; j += NW) {
                 const bool has_next = j + NW < ntile;
-                if (PREF && has_next) load_tile(nxt, j + NW);
+                if (PREF && has_next && !(prefetched && j == w)) load_tile(nxt, j + NW);
                 // the recall in two halves of the value rows (the B fragments stay in registers, each A
                 // fragment is still read once), which halves the accumulators held at a time
                 constexpr int HW = NW >= 8 ? NW / 2 : NW;
@@ -680,14 +685,7 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
             }
         }
         prefetched = false;
-        if (more) {
-            int64_t xn;
-            const int nXn = chunk_x(ch + 1, xn);
-            if (lam > 0 && nG + nXn > lam) {
-                if (w < (xb + nXn + 15) / 16) load_tile(cur, w);
-                prefetched = true;
-            }
-        }
+        if (more) prefetch_first(ch + 1);
     }
 
     // ---------------- final state ----------------
