@@ -41,7 +41,9 @@ __device__ __forceinline__ Frag8<T> frag_from_rows(const float (&lo)[4], const f
     return frag_from_acc<T>(f4{lo[0], lo[1], lo[2], lo[3]}, f4{hi[0], hi[1], hi[2], hi[3]});
 }
 
-template <typename T, int DK, int PHI>
+// NB: key blocks in flight.  1 keeps the registers low enough for two workgroups per CU (the bulk of
+// the read-out, beside the chain); 2 is for the last chunk range, whose workgroups run alone.
+template <typename T, int DK, int PHI, int NB>
 __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
     constexpr int D = kFeat, DV = DK, JT = DV / 16;
     constexpr int DW = (PHI == kPhiSoftmaxPM) ? D / 2 : D;
@@ -131,9 +133,14 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
             }
         }
     };
-    uint4 kst[KPT], vst[TPW][VPT];
-    int vpos[TPW], vband[TPW];
-    auto prefetch = [&](int kb, auto fromLds) {
+    // A key block in flight: its key pieces, value pieces, positions and band flags.  NB buffers, so
+    // the loads of the next NB blocks are in flight while a block is used.
+    struct KVBuf {
+        uint4 k[KPT];
+        uint4 v[TPW][VPT];
+        int pos[TPW], band[TPW];
+    };
+    auto prefetch = [&](KVBuf& bf, int kb, auto fromLds) {
 #pragma unroll
         for (int u = 0; u < KPT; ++u) {
             const int q = tid + 256 * u;
@@ -142,7 +149,7 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
             const T* rk;
             const T* rv;
             key_rows(kb * KB + j, pos, band, rk, rv, fromLds);
-            kst[u] = rk ? *reinterpret_cast<const uint4*>(rk + p * EPV) : make_uint4(0, 0, 0, 0);
+            bf.k[u] = rk ? *reinterpret_cast<const uint4*>(rk + p * EPV) : make_uint4(0, 0, 0, 0);
         }
         {   // values: thread -> (TPW consecutive keys, one column group)
             const int j0 = (tid % (KB / TPW)) * TPW, cg = tid / (KB / TPW);
@@ -150,14 +157,17 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
             for (int z = 0; z < TPW; ++z) {
                 const T* rk;
                 const T* rv;
-                key_rows(kb * KB + j0 + z, vpos[z], vband[z], rk, rv, fromLds);
+                key_rows(kb * KB + j0 + z, bf.pos[z], bf.band[z], rk, rv, fromLds);
 #pragma unroll
                 for (int u = 0; u < VPT; ++u)
-                    vst[z][u] = rv ? *reinterpret_cast<const uint4*>(rv + cg * VD + u * EPV) : make_uint4(0, 0, 0, 0);
+                    bf.v[z][u] = rv ? *reinterpret_cast<const uint4*>(rv + cg * VD + u * EPV) : make_uint4(0, 0, 0, 0);
             }
         }
     };
-    if (nblk > 0) prefetch(0, std::false_type{});
+    KVBuf bufs[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+        if (i < nblk) prefetch(bufs[i], i, std::false_type{});
 
     stage_wt<T, DK, DW, 256>(wt, WT_LD, A.W);
     for (int d = tid; d < D; d += 256) sS[d] = snapS[d];
@@ -173,20 +183,19 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
     Frag8<T> qf[DK / 32];
 #pragma unroll
     for (int ss = 0; ss < DK / 32; ++ss) qf[ss] = qvalid ? load_frag(qin + (tq - t0) * DK, ss, g) : frag_zero<T>();
-    // exact part: blocks of KB keys staged in LDS (keys row-major, values transposed), the next
-    // block's loads in flight while this one is used
+    // exact part: blocks of KB keys staged in LDS (keys row-major, values transposed)
     const float scale = 1.0f / sqrtf((float)DK);
     float m_run = -INFINITY, l_part = 0.f;
     f4 O[JT];
 #pragma unroll
     for (int J = 0; J < JT; ++J) O[J] = zero4();
 
-    for (int kb = 0; kb < nblk; ++kb) {
+    auto stage = [&](const KVBuf& bf) {
 #pragma unroll
         for (int u = 0; u < KPT; ++u) {
             const int q = tid + 256 * u;
             const int j = q / CPK, p = q % CPK;
-            *reinterpret_cast<uint4*>(sK + j * K_LD + p * EPV) = kst[u];
+            *reinterpret_cast<uint4*>(sK + j * K_LD + p * EPV) = bf.k[u];
         }
         {   // transposed value block: whole 32-bit words, consecutive threads -> consecutive words
             const int j0 = (tid % (KB / TPW)) * TPW, cg = tid / (KB / TPW);
@@ -196,16 +205,16 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
                 for (int x = 0; x < EPV; ++x) {
                     T word[TPW];
 #pragma unroll
-                    for (int z = 0; z < TPW; ++z) word[z] = reinterpret_cast<const T*>(&vst[z][u])[x];
+                    for (int z = 0; z < TPW; ++z) word[z] = reinterpret_cast<const T*>(&bf.v[z][u])[x];
                     *reinterpret_cast<uint32_t*>(sVT + (cg * VD + u * EPV + x) * VT_LD + j0) =
                         *reinterpret_cast<const uint32_t*>(word);
                 }
             if (cg == 0)
 #pragma unroll
-                for (int z = 0; z < TPW; ++z) { sKeyPos[j0 + z] = vpos[z]; sKeyBand[j0 + z] = vband[z]; }
+                for (int z = 0; z < TPW; ++z) { sKeyPos[j0 + z] = bf.pos[z]; sKeyBand[j0 + z] = bf.band[z]; }
         }
-        __syncthreads();
-        if (kb + 1 < nblk) prefetch(kb + 1, std::true_type{});
+    };
+    auto compute = [&]() {
         if (wave_active) {
             f4 st[KB / 16];
 #pragma unroll
@@ -253,7 +262,19 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
                 for (int J = 0; J < JT; ++J) mma32(O[J], load_frag(sVT + (16 * J + c) * VT_LD, k2, g), bp);
             }
         }
-        __syncthreads();
+    };
+    for (int kb0 = 0; kb0 < nblk; kb0 += NB) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int kb = kb0 + i;
+            if (kb < nblk) {
+                stage(bufs[i]);
+                __syncthreads();
+                if (kb + NB < nblk) prefetch(bufs[i], kb + NB, std::true_type{});
+                compute();
+                __syncthreads();
+            }
+        }
     }
 
     // linear part, after the exact loop so its registers are not live during it
@@ -279,36 +300,56 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
         for (int r = 0; r < 4; ++r) lden += ph[ft][r] * sS[16 * ft + 4 * g + r];
     lden = sum_groups(lden);
 
-    // tokens folded by this chunk become linear at tau = max(exit time, chunk start)
+    // tokens folded by this chunk become linear at tau = max(exit time, chunk start).  fold_group
+    // handles FG groups of 32 folded tokens: every load of the groups (their features and transposed
+    // values) is issued before any of it is used.  The last-range variant takes 64 tokens per round
+    // trip; the bulk variant 32, which keeps its registers within two workgroups per CU.
     float lden_f = 0.f;
-    for (int fb = 0; fb * 32 < nf; ++fb) {
-        f4 sp[2];
+    auto fold_group = [&](int fb0, auto fgc) {
+        constexpr int FG = decltype(fgc)::value;
+        Frag8<T> af[FG][2][D / 32], vf[FG][JT];
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-            const int i = 32 * fb + 16 * h2 + c;
-            sp[h2] = zero4();
-            const T* prow = i < nf ? phiStore + (int64_t)sFoldSrc[i] * D : nullptr;
+        for (int f2 = 0; f2 < FG; ++f2) {
+            const int fb = fb0 + f2;
 #pragma unroll
-            for (int ss = 0; ss < D / 32; ++ss) {
-                const Frag8<T> af = prow ? load_frag(prow, ss, g) : frag_zero<T>();
-                mma32(sp[h2], af, pf[ss]);
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int i = 32 * fb + 16 * h2 + c;
+                const T* prow = i < nf ? phiStore + (int64_t)sFoldSrc[i] * D : nullptr;
+#pragma unroll
+                for (int ss = 0; ss < D / 32; ++ss) af[f2][h2][ss] = prow ? load_frag(prow, ss, g) : frag_zero<T>();
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int ii = 32 * fb + 16 * h2 + 4 * g + r;
-                bool ok = false;
-                if (ii < nf) {
-                    const int64_t tau = max((int64_t)sFoldPos[ii] + eta, a);
-                    ok = tau <= tq;
-                }
-                sp[h2][r] = ok ? sp[h2][r] : 0.f;
-                lden_f += sp[h2][r];
-            }
+            for (int J = 0; J < JT; ++J)
+                vf[f2][J] = fb * 32 < nf ? load_frag(foldVT + (int64_t)(16 * J + c) * cpv, fb, g) : frag_zero<T>();
         }
-        const Frag8<T> bw = frag_from_acc<T>(sp[0], sp[1]);
 #pragma unroll
-        for (int J = 0; J < JT; ++J) mma32(L[J], load_frag(foldVT + (int64_t)(16 * J + c) * cpv, fb, g), bw);
-    }
+        for (int f2 = 0; f2 < FG; ++f2) {
+            const int fb = fb0 + f2;
+            f4 sp[2];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                sp[h2] = zero4();
+#pragma unroll
+                for (int ss = 0; ss < D / 32; ++ss) mma32(sp[h2], af[f2][h2][ss], pf[ss]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int ii = 32 * fb + 16 * h2 + 4 * g + r;
+                    bool ok = false;
+                    if (ii < nf) {
+                        const int64_t tau = max((int64_t)sFoldPos[ii] + eta, a);
+                        ok = tau <= tq;
+                    }
+                    sp[h2][r] = ok ? sp[h2][r] : 0.f;
+                    lden_f += sp[h2][r];
+                }
+            }
+            const Frag8<T> bw = frag_from_acc<T>(sp[0], sp[1]);
+#pragma unroll
+            for (int J = 0; J < JT; ++J) mma32(L[J], vf[f2][J], bw);
+        }
+    };
+    constexpr int FG = NB >= 2 ? 2 : 1;
+    for (int fb0 = 0; fb0 * 32 < nf; fb0 += FG) fold_group(fb0, std::integral_constant<int, FG>{});
     lden += sum_groups(lden_f);
 
     // joint normalisation with a common scale exp(-cmax), cmax = max(m, log L_den)
@@ -453,11 +494,14 @@ static hipError_t record(hipEvent_t const* ev, int i, hipStream_t stream) {
 }
 
 template <typename T, int DK, int PHI>
-static hipError_t launch_readout(PrefillArgs a, int c0, int c1, hipStream_t stream) {
+static hipError_t launch_readout(PrefillArgs a, int c0, int c1, hipStream_t stream, bool last_range = false) {
     a.c_begin = c0;
     a.c_end = c1;
     const int64_t blocks = (int64_t)a.BH * (c1 - c0) * a.nqt;
-    hipLaunchKernelGGL((readout_kernel<T, DK, PHI>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    if (last_range)
+        hipLaunchKernelGGL((readout_kernel<T, DK, PHI, 2>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((readout_kernel<T, DK, PHI, 1>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -538,7 +582,8 @@ hipError_t launch_prefill_t(const PrefillArgs& a0, hipStream_t stream, hipEvent_
         if ((e = launch_chain_range<T, DK, PHI>(a, bounds[i], bounds[i + 1], stream)) != hipSuccess) return e;
         if ((e = hipEventRecord(side->seg[i], stream)) != hipSuccess) return e;
         if ((e = hipStreamWaitEvent(side->stream, side->seg[i], 0)) != hipSuccess) return e;
-        if ((e = launch_readout<T, DK, PHI>(a, bounds[i], bounds[i + 1], side->stream)) != hipSuccess) return e;
+        if ((e = launch_readout<T, DK, PHI>(a, bounds[i], bounds[i + 1], side->stream, nseg > 1 && i == nseg - 1)) != hipSuccess)
+            return e;
     }
     // The commit overwrites the state's cache and window rows.  A call that starts from an empty
     // state (t = 0: no cache member, no window token) never reads those rows in the read-out, so its
