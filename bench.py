@@ -25,6 +25,7 @@ METRIC = "prefill tokens/s and decode tokens/s per GPU; % of MFMA / HBM roofline
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+MULTI_TOKEN_C = 16          # tokens per call in the multi-token decode measurement
 KERNEL_SOURCES = ("lola_common.hpp", "lola_phi.hip", "lola_chain.hip", "lola_readout.hip", "lola_decode.hip",
                   "lola_decode_fast.hip")
 
@@ -167,7 +168,28 @@ def bench_decode(args, lola, torch, wl):
             best = el
             kern_ms = sum(evs[s].elapsed_time(evs[s + 1]) for s in range(steps)) / steps
     log(f"decode: {best / steps * 1e3:.3f} ms/step wall, kernel {kern_ms:.3f} ms/step")
-    return best, kern_ms
+    # multi-token decode: the same tokens in calls of C_DEC tokens (allocation once per call)
+    c_dec = MULTI_TOKEN_C
+    calls = steps // c_dec
+    parts = [tuple(torch.stack([x[s] for s in range(c * c_dec, (c + 1) * c_dec)], dim=2).contiguous()
+                   for x in (dq, dk, dv)) for c in range(calls)]
+    ws_m = torch.empty(lola.lola_workspace_bytes(st, c_dec, c_dec), dtype=torch.uint8, device=dev)
+    ym = torch.empty(wl.B, wl.h, c_dec, wl.d_v, dtype=tdt, device=dev)
+    best_m = None
+    for run in range(args.decode_runs + 1):
+        st.restore(snap)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for mq, mk, mv in parts:
+            lola.lola_prefill(st, phi, mq, mk, mv, c_dec, y=ym, workspace=ws_m)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        if run > 0 and (best_m is None or el < best_m):
+            best_m = el
+    log(f"multi-token decode ({c_dec} tokens per call): {best_m / calls * 1e3:.3f} ms/call")
+    multi = {"value": round(wl.B * calls * c_dec / best_m, 1), "unit": "decode tokens/s", "tokens_per_call": c_dec,
+             "ms_per_call": round(best_m / calls * 1e3, 4)}
+    return best, kern_ms, multi
 
 
 def _oracle_head(job):
@@ -247,7 +269,7 @@ def main() -> int:
     src_hash = kernel_source_hash()
     if args.no_prefill:        # profiling mode: the decode workload only
         dwl = CONFIGS[4]
-        best, kern_ms = bench_decode(args, lola, torch, dwl)
+        best, kern_ms, _ = bench_decode(args, lola, torch, dwl)
         print(json.dumps({"decode_ms_per_step": best / dwl.decode_steps * 1e3, "decode_kernel_ms": kern_ms}))
         return 0
     elapsed, kern = bench_prefill(args, lola, torch, wl)
@@ -275,7 +297,7 @@ def main() -> int:
     out["prefill_mfma_frac_whole_step"] = round(all_fl / (elapsed / args.steps) / 1e12 / PEAK_BF16_TFLOPS, 5)
     if not args.no_decode:
         dwl = CONFIGS[4]
-        best, kern_ms = bench_decode(args, lola, torch, dwl)
+        best, kern_ms, multi = bench_decode(args, lola, torch, dwl)
         per_step = best / dwl.decode_steps
         byts = decode_bytes_per_seq_head(dwl) * dwl.B * dwl.h
         ach_d = byts / (kern_ms * 1e-3) / 1e9
@@ -284,7 +306,8 @@ def main() -> int:
                          "roofline": {"bound": "hbm", "kernel": "lola_decode", "achieved": round(ach_d, 1),
                                       "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach_d / PEAK_HBM_GBS, 4),
                                       "traffic": load_traffic("decode", src_hash),
-                                      "kernel_ms": round(kern_ms, 4), "algorithmic_bytes_per_launch": byts}}
+                                      "kernel_ms": round(kern_ms, 4), "algorithmic_bytes_per_launch": byts},
+                         "multi_token": multi}
     if not args.no_cpu_baseline:
         log("cpu baseline: running the oracle ...")
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_heads)

@@ -278,3 +278,41 @@ def test_overlapped_prefill_equals_sequential():
     assert np.array_equal(y0, y1) and np.array_equal(f0, f1)
     for key in s0:
         assert np.array_equal(np.asarray(s0[key]), np.asarray(s1[key])), key
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("c_dec", [4, 8])
+def test_multi_token_decode_calls(dtype, c_dec):
+    """Multi-token decode: a live state (full window and cache) takes short prefill calls of c_dec
+    tokens with C = c_dec, so the allocation runs once per c_dec tokens.  Each call is checked
+    against the oracle continuing from the GPU's state before that call (so a bf16 near-tie in one
+    call cannot shift the next), output by output, and in fp32 also the resulting cache."""
+    import hybrid_linear_attention_chunkwise_amd as lola
+    from oracle import lola_oracle as O
+    wl = small_workload(56, B=1, h=2, n=0, C=c_dec, eta=24, lam=20, d_k=64, d_v=64, dtype=dtype)
+    W = make_weights(wl)
+    n0, calls = 64, 6
+    q, k, v = make_qkv(wl, n=n0 + calls * c_dec)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    _, _, st, phi = TL.gpu_run_prefill(q[:, :, :n0], k[:, :, :n0], v[:, :, :n0], W, wl.phi, wl.eta,
+                                       wl.lam, 16, dtype, D=wl.D)
+    phi_o = O.make_phi(wl.phi, W)
+    tol = TL.FP32_TOL if dtype == "f32" else TL.BF16_TOL
+    worst = 0.0
+    for call in range(calls):
+        lo, hi = n0 + call * c_dec, n0 + (call + 1) * c_dec
+        snap = TL.state_to_host(st)
+        qc, kc, vc = (np.ascontiguousarray(x[:, :, lo:hi]) for x in (q, k, v))
+        y, _ = lola.lola_prefill(st, phi, *(torch.from_numpy(x).cuda().to(tdt) for x in (qc, kc, vc)), c_dec)
+        y = y.float().cpu().numpy()
+        after = TL.state_to_host(st)
+        for h in range(wl.h):
+            so = O.state_from_arrays(snap["t"], wl.eta, wl.lam, snap["H"][0, h].T, snap["s"][0, h],
+                                     snap["win_k"][0, h], snap["win_v"][0, h], snap["cache_k"][0, h],
+                                     snap["cache_v"][0, h], snap["cache_pos"][0, h])
+            y_o, _ = O.prefill(so, phi_o, qc[0, h], kc[0, h], vc[0, h], C=c_dec)
+            worst = max(worst, TL.row_rel_err(y[0, h], y_o))
+            if dtype == "f32":
+                assert TL.cache_members(after["cache_pos"][0, h]) == sorted(so.cache)
+    print(f"[multi-token decode] {dtype} c_dec={c_dec}: max err {worst:.3e}", flush=True)
+    assert worst <= tol
