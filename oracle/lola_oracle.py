@@ -16,6 +16,9 @@ Source: "LoLA: Low-Rank Linear Attention With Sparse Caching" reading notes (cc.
   * 2.6, Eq. (15) and Fig. 2: chunked prefill of length C; after a chunk the oldest window chunk and
     the cache are scored together (about C + lambda candidates) and the rest folded in one batch.
   * 2.7: per-head persistent element count.
+  * 4.4, Fig. 3 and Fig. 10 with Eq. (26): the collision map, the SRE of each KV held by the linear
+    state against each later state, zero while the KV is not in the state; its relative form subtracts
+    the SRE the KV had right after it was written (a difference, not a ratio).
 
 Readings where the notes leave a step open (each is listed in the design notes of the repository):
   R1 window: the window seen by query t is positions max(0, t-eta+1) .. t (it includes the current
@@ -31,6 +34,10 @@ Readings where the notes leave a step open (each is listed in the design notes o
   R5 empty state: if phi(k)^T s == 0 the recall is the zero vector, so SRE = ||v||_2.
   R6 ties: exactly lambda are kept; equal SRE is broken toward the older (smaller) position.
   R7 a single feature map phi (and weight W) is shared by queries and keys, heads and batches.
+  R8 collision map: the states are the chunk-end states of a chunked prefill (the figure's per-token
+     states are read at chunk granularity, where the chunked path has complete states), one row per
+     chunk; a KV enters the map at the end of the chunk that folds it, and "right after it was
+     written" is that same row.
 
 Parity status: every function here is pinned by the tests in tests/test_oracle_*.py (closed forms,
 textbook special cases, hand-derived schedules, invariants and an independent per-pair evaluation).
@@ -38,13 +45,13 @@ textbook special cases, hand-derived schedules, invariants and an independent pe
 from __future__ import annotations
 
 import dataclasses
-from typing import List, Optional
+from typing import Callable, List, Optional
 
 import numpy as np
 
 __all__ = ["phi_elu1", "phi_softmax_pm", "make_phi", "sre", "SeqState", "new_state", "prefill",
            "decode_step", "replay", "exact_attention_read", "state_elements", "Schedule",
-           "state_from_arrays"]
+           "state_from_arrays", "sre_collisions"]
 
 
 # --------------------------------------------------------------------------------------------------
@@ -187,13 +194,14 @@ def exact_attention_read(q_t, phi_q, H, s, keys, vals, d_k):
 
 
 def prefill(st: SeqState, phi, q, k, v, C: int, fold_at_in: Optional[np.ndarray] = None,
-            tol: float = 0.0):
+            tol: float = 0.0, on_chunk_end: Optional[Callable[[int, SeqState], None]] = None):
     """Chunked prefill of n tokens for one sequence and head (section 2.6), read out token by token.
 
     q, k: [n][d_k]; v: [n][d_v].  Mutates ``st``.  Returns (y [n][d_v], Schedule).
     ``fold_at_in`` replays an external schedule (call-local chunk id per input token, -1 = not
     folded): its decisions replace the top-lambda, and each is checked against the fp64 SRE order
-    with relative tolerance ``tol`` (problems are recorded in the returned Schedule)."""
+    with relative tolerance ``tol`` (problems are recorded in the returned Schedule).
+    ``on_chunk_end(c, st)`` is called once per chunk, after the chunk's folds and commit."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -273,6 +281,8 @@ def prefill(st: SeqState, phi, q, k, v, C: int, fold_at_in: Optional[np.ndarray]
         st.cache = kept
         st.t = b
         assert kept_set.isdisjoint(S)
+        if on_chunk_end is not None:
+            on_chunk_end(c, st)
     return y, sched
 
 
@@ -292,6 +302,34 @@ def replay(st: SeqState, phi, q, k, v, C: int, fold_at: np.ndarray, tol: float):
     Valid: every chunk keeps min(lambda, |E|) candidates and min_{kept} SRE >= max_{folded} SRE *
     (1 - tol), SRE in fp64 against the chunk-start state.  Mutates ``st``; returns (y, Schedule)."""
     return prefill(st, phi, q, k, v, C, fold_at_in=np.asarray(fold_at), tol=tol)
+
+
+def sre_collisions(st: SeqState, phi, q, k, v, C: int, fold_at_in: Optional[np.ndarray] = None,
+                   tol: float = 0.0, relative: bool = False):
+    """Collision map of one prefill call (section 4.4, Fig. 3; relative form Fig. 10, Eq. (26)).
+
+    Runs ``prefill`` (mutating ``st``; ``fold_at_in`` / ``tol`` as there) and returns (M, y, Schedule)
+    with M [n_chunks][n]: M[r, i] = SRE(phi(k_i), v_i | H_r, s_r) for the state (H_r, s_r) at the end
+    of chunk r, for every input token i folded in chunk r or before; 0 for a token not in that state
+    (still in the window or the cache, reading R8).  relative: each entry minus the token's entry in
+    the row of its own fold, so that row reads 0 and rows before it stay 0."""
+    states = []
+    y, sched = prefill(st, phi, q, k, v, C, fold_at_in=fold_at_in, tol=tol,
+                       on_chunk_end=lambda c, s_: states.append((s_.H.copy(), s_.s.copy())))
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    phi_k = phi(k)
+    fa = sched.fold_at
+    M = np.zeros((len(states), k.shape[0]))
+    for r, (H, s) in enumerate(states):
+        held = (fa >= 0) & (fa <= r)
+        if held.any():
+            M[r, held] = sre(phi_k[held], v[held], H, s)
+    if relative:
+        for i in np.nonzero(fa >= 0)[0]:
+            first = M[fa[i], i]
+            M[fa[i]:, i] -= first
+    return M, y, sched
 
 
 def state_elements(t: int, d_k: int, d_v: int, D: int, eta: int, lam: int) -> int:

@@ -412,3 +412,104 @@ def test_replay_flags_a_wrong_schedule():
     st = O.new_state(8, 6, 8, eta, lam)
     _, s2 = O.replay(st, phi, q, k, v, C, bad, tol=0.0)
     assert s2.problems
+
+
+# ------------------------------------------------------------------------------------------------
+# Collision map (4.4, Fig. 3; relative form Fig. 10, Eq. (26)).
+# ------------------------------------------------------------------------------------------------
+
+def _pairwise_sre(phi_k, v, members, i):
+    """SRE of token i against the state holding exactly ``members``, in kernel form: the recall is the
+    kappa-weighted mean of the members' values with kappa(i, j) = phi(k_i)^T phi(k_j), written with
+    scalar loops (no H, no s)."""
+    num = np.zeros(v.shape[1])
+    den = 0.0
+    for j in members:
+        kap = sum(float(phi_k[i, e]) * float(phi_k[j, e]) for e in range(phi_k.shape[1]))
+        num += kap * v[j]
+        den += kap
+    rec = num / den if den != 0.0 else np.zeros_like(num)
+    return float(np.sqrt(((rec - v[i]) ** 2).sum()))
+
+
+def test_collision_single_kv_recalls_itself():
+    # (c) of the method's checks: a state holding one KV recalls v exactly, so its map entry is 0.
+    phi, q, k, v = _rand_problem(30, 1)
+    st = O.new_state(8, 6, 8, 0, 0)
+    M, _, sched = O.sre_collisions(st, phi, q, k, v, C=1)
+    assert M.shape == (1, 1) and sched.fold_at.tolist() == [0]
+    assert abs(M[0, 0]) < 1e-12 * np.linalg.norm(v[0])
+
+
+@pytest.mark.parametrize("relative", [False, True])
+def test_collision_pure_linear_is_pairwise_kernel_form(relative):
+    # eta = lambda = 0, C = 1: token i is written at step i, so row r holds tokens 0..r.
+    phi, q, k, v = _rand_problem(31, 10)
+    st = O.new_state(8, 6, 8, 0, 0)
+    M, _, sched = O.sre_collisions(st, phi, q, k, v, C=1, relative=relative)
+    assert sched.fold_at.tolist() == list(range(10))
+    pk = phi(k)
+    for r in range(10):
+        for i in range(10):
+            want = _pairwise_sre(pk, v, range(r + 1), i) if i <= r else 0.0
+            if relative and i <= r:
+                want -= _pairwise_sre(pk, v, range(i + 1), i)
+            assert abs(M[r, i] - want) < 1e-10, (r, i, M[r, i], want)
+
+
+def test_collision_one_hot_features_is_bucket_mean():
+    # With one-hot features (bucket = argmax of the first D entries of k) two keys collide exactly
+    # when they share a bucket, and the recall is the mean value of the bucket's stored KV.  A window
+    # of eta and no cache: token i leaves the window at time i + eta, so chunk (i + eta) // C folds it.
+    D, eta, C, n = 4, 4, 3, 23
+    rng = np.random.default_rng(32)
+    k = rng.standard_normal((n, 8))
+    q = rng.standard_normal((n, 8))
+    v = rng.standard_normal((n, 6))
+    bucket = np.argmax(k[:, :D], axis=1)
+
+    def onehot(x):
+        x = np.atleast_2d(x)
+        return np.eye(D)[np.argmax(x[:, :D], axis=1)]
+
+    st = O.new_state(8, 6, D, eta, 0)
+    M, _, sched = O.sre_collisions(st, onehot, q, k, v, C=C)
+    fa_want = [(i + eta) // C if i + eta < n else -1 for i in range(n)]
+    assert sched.fold_at.tolist() == fa_want
+    for r in range(M.shape[0]):
+        for i in range(n):
+            if fa_want[i] < 0 or fa_want[i] > r:
+                assert M[r, i] == 0.0
+                continue
+            same = [j for j in range(n) if bucket[j] == bucket[i] and 0 <= fa_want[j] <= r]
+            want = np.linalg.norm(v[same].mean(axis=0) - v[i])
+            assert abs(M[r, i] - want) < 1e-12, (r, i)
+
+
+@pytest.mark.parametrize("relative", [False, True])
+def test_collision_with_cache_matches_rebuilt_states(relative):
+    # Window, cache and chunks together: row r must equal the SRE against the state rebuilt from the
+    # schedule alone (every token folded in chunk r or before), and a token the cache holds past its
+    # window exit keeps a zero column until its own fold.
+    eta, lam, C, n = 6, 4, 4, 40
+    phi, q, k, v = _rand_problem(33, n, scale=1.5)
+    st = O.new_state(8, 6, 8, eta, lam)
+    M, _, sched = O.sre_collisions(st, phi, q, k, v, C=C, relative=relative)
+    fa = sched.fold_at
+    pk = phi(k)
+    held_late = [i for i in range(n) if fa[i] > (i + eta) // C or (fa[i] < 0 and i + eta < n)]
+    assert held_late, "the cache never held a token past its window exit"
+    for r in range(M.shape[0]):
+        members = [j for j in range(n) if 0 <= fa[j] <= r]
+        for i in range(n):
+            if fa[i] < 0 or fa[i] > r:
+                assert M[r, i] == 0.0
+                continue
+            want = _pairwise_sre(pk, v, members, i)
+            if relative:
+                first = [j for j in range(n) if 0 <= fa[j] <= fa[i]]
+                want -= _pairwise_sre(pk, v, first, i)
+            assert abs(M[r, i] - want) < 1e-10, (r, i)
+    if relative:
+        for i in np.nonzero(fa >= 0)[0]:
+            assert M[fa[i], i] == 0.0
