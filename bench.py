@@ -27,7 +27,7 @@ PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 MULTI_TOKEN_C = 16          # tokens per call in the multi-token decode measurement
 KERNEL_SOURCES = ("lola_common.hpp", "lola_phi.hip", "lola_chain.hip", "lola_readout.hip", "lola_decode.hip",
-                  "lola_decode_fast.hip")
+                  "lola_decode_fast.hip", "lola_collide.hip")
 
 
 def log(msg: str) -> None:
@@ -128,6 +128,48 @@ def bench_prefill(args, lola, torch, wl):
     log(f"prefill: {elapsed / args.steps * 1e3:.3f} ms/step (evented pass {t_evented / args.steps * 1e3:.3f}); "
         f"kernels ms: {kern}")
     return elapsed, kern
+
+
+def bench_collisions(args, lola, torch, wl):
+    """SRE collision map of one prefill call of the workload (every token against every chunk-end
+    state): one prefill, then the map timed on its own.  Algorithmic flops: 2 D d_v per map entry whose
+    token is in the state (the recall H^T phi(k)); the normaliser and the norm are not counted."""
+    import numpy as np
+    from workloads import make_qkv, make_weights
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    W = make_weights(wl)
+    q, k, v = make_qkv(wl)
+    qt, kt, vt = (torch.from_numpy(x).to(dev).to(tdt) for x in (q, k, v))
+    st = lola.LolaState(wl.B, wl.h, wl.d_k, wl.d_v, wl.D, wl.eta, wl.lam, tdt, device=dev)
+    phi = lola.LolaPhi(wl.phi, torch.from_numpy(W).to(dev), wl.D)
+    ws = torch.empty(lola.lola_workspace_bytes(st, wl.n, wl.C), dtype=torch.uint8, device=dev)
+    fold = torch.empty(wl.B, wl.h, wl.n, dtype=torch.int32, device=dev)
+    lola.lola_state_init(st)
+    lola.lola_prefill(st, phi, qt, kt, vt, wl.C, fold_at=fold, workspace=ws)
+    R = (wl.n + wl.C - 1) // wl.C
+    out = torch.empty(wl.B, wl.h, R, wl.n, dtype=torch.float32, device=dev)
+    fa = fold.cpu().numpy().astype(np.int64)
+    entries = int(np.where(fa >= 0, R - fa, 0).sum())
+    for _ in range(args.warmup):
+        lola.lola_sre_collisions(st, vt, fold, wl.C, ws, out=out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        lola.lola_sre_collisions(st, vt, fold, wl.C, ws, out=out)
+    e1.record()
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    flop = 2.0 * wl.D * wl.d_v * entries
+    ach = flop / (ms * 1e-3) / 1e12
+    log(f"collision map: {ms:.4f} ms, {entries} entries in the state of {wl.B * wl.h * R * wl.n}, "
+        f"{ach:.1f} TFLOP/s")
+    return {"kernel": "lola_collide", "workload": wl.name, "rows": R, "kernel_ms": round(ms, 4),
+            "entries_in_state": entries, "entries_total": wl.B * wl.h * R * wl.n,
+            "roofline": {"bound": "mfma", "achieved": round(ach, 3), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 5),
+                         "algorithmic_flop_per_launch": flop}}
 
 
 def bench_decode(args, lola, torch, wl):
@@ -240,6 +282,7 @@ def main() -> int:
     ap.add_argument("--cpu-heads", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-collisions", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -308,6 +351,8 @@ def main() -> int:
                                       "traffic": load_traffic("decode", src_hash),
                                       "kernel_ms": round(kern_ms, 4), "algorithmic_bytes_per_launch": byts},
                          "multi_token": multi}
+    if not args.no_collisions:
+        out["collision_map"] = bench_collisions(args, lola, torch, wl)
     if not args.no_cpu_baseline:
         log("cpu baseline: running the oracle ...")
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_heads)

@@ -16,7 +16,7 @@ from ._binding import (LOLA_BF16, LOLA_EDEVICE, LOLA_EINVAL, LOLA_EUNSUPPORTED, 
                        LOLA_PHI_ELU1, LOLA_PHI_SOFTMAX_PM, LolaError)
 
 __all__ = ["LolaState", "LolaPhi", "lola_state_init", "lola_workspace_bytes", "lola_prefill",
-           "lola_decode_step", "LolaError", "LOLA_OK", "LOLA_EINVAL", "LOLA_EUNSUPPORTED",
+           "lola_decode_step", "lola_sre_collisions", "LolaError", "LOLA_OK", "LOLA_EINVAL", "LOLA_EUNSUPPORTED",
            "LOLA_EDEVICE", "library_path", "PHI_KINDS"]
 
 PHI_KINDS = {"elu1": LOLA_PHI_ELU1, "softmax_pm": LOLA_PHI_SOFTMAX_PM}
@@ -130,3 +130,19 @@ def lola_decode_step(state: LolaState, phi: LolaPhi, q: torch.Tensor, k: torch.T
                                       _ptr(v), _ptr(y), _ptr(folded_pos), _stream(stream))
     _b.check("lola_decode_step", code)
     return y, folded_pos
+
+
+def lola_sre_collisions(state: LolaState, v: torch.Tensor, fold_at: torch.Tensor, C: int,
+                        workspace: torch.Tensor, relative: bool = False,
+                        out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """SRE collision map [B][h][ceil(n / C)][n] fp32 of the lola_prefill call that just ran with these
+    v, fold_at, C and workspace (see include/lola.h).  Asynchronous on `stream`."""
+    n = v.shape[2]
+    R = (n + C - 1) // C
+    if out is None:
+        out = torch.empty(v.shape[0], v.shape[1], R, n, dtype=torch.float32, device=v.device)
+    code = _b.load().lola_sre_collisions(ctypes.byref(state.c), _ptr(v), _ptr(fold_at), n, C,
+                                         _ptr(workspace), workspace.numel(), int(bool(relative)),
+                                         _ptr(out), _stream(stream))
+    _b.check("lola_sre_collisions", code)
+    return out

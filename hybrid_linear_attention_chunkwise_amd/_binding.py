@@ -22,7 +22,7 @@ LOLA_PHI_ELU1 = 0
 LOLA_PHI_SOFTMAX_PM = 1
 
 EXPORTED = ("lola_workspace_bytes", "lola_state_init", "lola_prefill", "lola_prefill_profiled",
-            "lola_decode_step", "lola_status_string")
+            "lola_decode_step", "lola_sre_collisions", "lola_status_string")
 
 
 class LolaPhi(ctypes.Structure):
@@ -70,6 +70,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lola_prefill_profiled.restype = i32
     lib.lola_decode_step.argtypes = [sp, pp, vp, vp, vp, vp, vp, vp]
     lib.lola_decode_step.restype = i32
+    lib.lola_sre_collisions.argtypes = [sp, vp, vp, i64, i32, vp, sz, i32, vp, vp]
+    lib.lola_sre_collisions.restype = i32
     lib.lola_status_string.argtypes = [i32]
     lib.lola_status_string.restype = ctypes.c_char_p
     _lib = lib

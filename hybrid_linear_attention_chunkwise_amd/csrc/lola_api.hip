@@ -225,4 +225,40 @@ lola_status lola_decode_step(lola_state* st, const lola_phi* phi, const void* q,
     return LOLA_OK;
 }
 
+lola_status lola_sre_collisions(const lola_state* st, const void* v, const int32_t* fold_at, int64_t n,
+                                int32_t C, const void* workspace, size_t workspace_bytes, int32_t relative,
+                                float* out, void* stream) {
+    lola_status rc = check_shape(st);
+    if (rc != LOLA_OK) return rc;
+    if (!st->H || !st->s || !aligned16(st->H) || !aligned16(st->s)) return LOLA_EINVAL;
+    if (n < 0 || C < 1 || (relative != 0 && relative != 1)) return LOLA_EINVAL;
+    if (C > kMaxChunk || n > INT_MAX / 2) return LOLA_EUNSUPPORTED;
+    if (n == 0) return LOLA_OK;
+    if (!v || !fold_at || !out || !aligned16(v) || !aligned16(fold_at) || !aligned16(out)) return LOLA_EINVAL;
+    const WsLayout L = make_layout(st, n, C);
+    const size_t need = (size_t)L.per_bh * (size_t)st->B * (size_t)st->n_heads;
+    if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes < need) return LOLA_EINVAL;
+
+    lola::CollideArgs a;
+    a.BH = st->B * st->n_heads;
+    a.n = (int)n;
+    a.C = C;
+    a.eta = st->eta;
+    a.nchunks = L.nchunks;
+    a.tok_per_block = lola::kCollideTokensPerBlock;
+    a.nblk = (int)((n + a.tok_per_block - 1) / a.tok_per_block);
+    a.relative = relative;
+    a.v = v;
+    a.fold_at = fold_at;
+    a.H = st->H;
+    a.s = st->s;
+    a.ws = reinterpret_cast<const char*>(workspace);
+    a.L = L;
+    a.out = out;
+    if ((int64_t)a.BH * a.nchunks * a.nblk > (int64_t)INT_MAX) return LOLA_EUNSUPPORTED;
+    if (lola::launch_collide(a, st->dtype, st->d_k, (hipStream_t)stream) != hipSuccess) return LOLA_EDEVICE;
+    if (getenv("LOLA_DEBUG_SYNC") && hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return LOLA_EDEVICE;
+    return LOLA_OK;
+}
+
 }  // extern "C"

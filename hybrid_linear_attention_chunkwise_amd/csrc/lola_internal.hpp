@@ -79,6 +79,21 @@ struct DecodeArgs {
     int32_t* folded_pos;  // nullable
 };
 
+// SRE collision map of one prefill call, read from that call's workspace and the state it left.
+struct CollideArgs {
+    int BH, n, C, eta, nchunks;
+    int nblk, tok_per_block;   // token blocks per map row and tokens per block
+    int relative;
+    const void* v;             // the call's values [BH][n][d_v]
+    const int32_t* fold_at;    // the call's fold chunks [BH][n]
+    const float* H;            // state after the call (the last row)
+    const float* s;
+    const char* ws;            // the call's workspace
+    WsLayout L;                // its layout (same n and C)
+    float* out;                // [BH][nchunks][n]
+};
+constexpr int kCollideTokensPerBlock = 512;
+
 struct InitArgs {
     int BH, D, d_v, lam;
     float* H;
@@ -97,6 +112,8 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, int d, int phi_kind, hi
 bool decode_fast_fits(int d, int lam, int eta);
 size_t decode_fast_lds_bytes(int d, int phi_kind);
 hipError_t launch_decode_fast(const DecodeArgs& a, int d, int phi_kind, hipStream_t stream);
+
+hipError_t launch_collide(const CollideArgs& a, int dtype, int d, hipStream_t stream);
 
 // LDS bytes the chain kernel uses (sized for kMaxLambda / kMaxChunk) at element size esz.
 size_t chain_lds_bytes(int d, int phi_kind, int esz);

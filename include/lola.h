@@ -129,6 +129,26 @@ lola_status lola_prefill_profiled(lola_state *st, const lola_phi *phi, const voi
 lola_status lola_decode_step(lola_state *st, const lola_phi *phi, const void *q, const void *k,
                              const void *v, void *y, int32_t *folded_pos, void *stream);
 
+/* SRE collision map of the prefill call that just ran (section 4.4, Fig. 3; relative form Fig. 10 and
+ * Eq. (26)): the self-recall error (Eq. (10)) of each of the call's tokens against the linear state at
+ * the end of each of the call's chunks.
+ *   Row r (0 <= r < R = ceil(n / C)) is the state (H, s) at the end of call-local chunk r; for r < R - 1
+ *   it is read from the chunk records the call left in `workspace`, the last row is st's current H, s.
+ *   out [B][n_heads][R][n] fp32 (device): out[.., r, i] = SRE(phi(k_i), v_i | H_r, s_r) if
+ *   0 <= fold_at[i] <= r (token i is in that state), else 0 (still in the window or the cache, or never
+ *   folded).  relative = 1: each entry minus the same token's entry at row fold_at[i], so that row is
+ *   0 (Eq. (26) is a difference, not a ratio).  phi(k_i) is the feature row the call stored in the
+ *   workspace.
+ *   Contract: call it after the lola_prefill(st, ..., v, n, C, ..., fold_at, workspace, ...) it maps, in
+ *   stream order, with the same st, v, n, C, fold_at (non-NULL there) and workspace, and before anything
+ *   else writes the workspace or advances the state.  Otherwise the map is meaningless; every access
+ *   still stays inside the buffers sized by these arguments.  v, fold_at, out: 16-byte aligned.
+ *   n == 0 is a no-op.  LOLA_EINVAL for NULL or misaligned pointers, relative outside {0, 1}, or a
+ *   workspace smaller than lola_workspace_bytes(st, n, C). */
+lola_status lola_sre_collisions(const lola_state *st, const void *v, const int32_t *fold_at, int64_t n,
+                                int32_t C, const void *workspace, size_t workspace_bytes, int32_t relative,
+                                float *out, void *stream);
+
 /* Static, human-readable text for a status code. */
 const char *lola_status_string(lola_status status);
 

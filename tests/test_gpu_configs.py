@@ -119,3 +119,13 @@ def test_config4_decode_sampled():
                 break       # a bf16 near-tie: the two states part ways from here
     print(f"[config 4] decode: max err {worst:.3e}, heads that diverged at a near-tie: {mism}", flush=True)
     assert worst <= TL.BF16_TOL
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_config2_collision_map_sampled(dtype):
+    """The collision map at the headline prefill shape (32 heads, n = 4096, C = 64: 64 rows), two
+    heads recomputed in full by the oracle."""
+    import dataclasses
+    from test_gpu_parity import collision_check
+    wl = dataclasses.replace(CONFIGS[2], dtype=dtype)
+    collision_check(wl, [(0, 3), (0, 30)])

@@ -316,3 +316,94 @@ def test_multi_token_decode_calls(dtype, c_dec):
                 assert TL.cache_members(after["cache_pos"][0, h]) == sorted(so.cache)
     print(f"[multi-token decode] {dtype} c_dec={c_dec}: max err {worst:.3e}", flush=True)
     assert worst <= tol
+
+
+# ------------------------------------------------------------------------------------------------
+# SRE collision map (lola_sre_collisions) against the oracle's map under the GPU's schedule.
+# ------------------------------------------------------------------------------------------------
+
+def collision_check(wl, heads, relative_modes=(False, True)):
+    """Runs lola_prefill with a kept workspace, then the collision map in each mode, and compares
+    every entry with the oracle's map (sre_collisions replaying the GPU's fold schedule).
+
+    Zero entries (tokens not yet in a state) must match exactly.  Other entries: |gpu - oracle| <=
+    tol * (||v_i|| + max_r SRE_r(i)), tol the output tolerance of the storage type (1e-4 fp32, 2e-2
+    bf16); an SRE is a distance to v_i, so an error in the recall moves it by at most that much."""
+    import hybrid_linear_attention_chunkwise_amd as lola
+    from oracle import lola_oracle as O
+    W = make_weights(wl)
+    q, k, v = make_qkv(wl)
+    dev = torch.device("cuda:0")
+    tdt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+    print(f"[collisions] {wl.name} B={wl.B} h={wl.h} n={wl.n} d={wl.d_k} C={wl.C} eta={wl.eta} "
+          f"lam={wl.lam} {wl.dtype}", flush=True)
+    st = lola.LolaState(wl.B, wl.h, wl.d_k, wl.d_v, wl.D, wl.eta, wl.lam, tdt, device=dev)
+    lola.lola_state_init(st)
+    phi = lola.LolaPhi(wl.phi, torch.from_numpy(W).to(dev), wl.D)
+    qt, kt, vt = (torch.from_numpy(x).to(dev).to(tdt) for x in (q, k, v))
+    ws = torch.empty(max(lola.lola_workspace_bytes(st, wl.n, wl.C), 256), dtype=torch.uint8, device=dev)
+    fold = torch.full((wl.B, wl.h, wl.n), -7, dtype=torch.int32, device=dev)
+    lola.lola_prefill(st, phi, qt, kt, vt, wl.C, fold_at=fold, workspace=ws)
+    maps = {}
+    for rel in relative_modes:
+        maps[rel] = lola.lola_sre_collisions(st, vt, fold, wl.C, ws, relative=rel).cpu().numpy()
+    fold_h = fold.cpu().numpy()
+    R = (wl.n + wl.C - 1) // wl.C
+    tol = TL.FP32_TOL if wl.dtype == "f32" else TL.BF16_TOL
+    phi_o = O.make_phi(wl.phi, W)
+    worst = 0.0
+    for (b, h) in heads:
+        args = (phi_o, q[b, h].astype(np.float64), k[b, h].astype(np.float64), v[b, h].astype(np.float64), wl.C)
+        ref = {}
+        for rel in sorted(set(relative_modes) | {False}):
+            st_o = O.new_state(wl.d_k, wl.d_v, wl.D, wl.eta, wl.lam)
+            ref[rel], _, sched = O.sre_collisions(st_o, *args, fold_at_in=fold_h[b, h].astype(np.int64),
+                                                  tol=1.0, relative=rel)
+        scale = np.linalg.norm(v[b, h].astype(np.float64), axis=1) + ref[False].max(axis=0)
+        for rel in relative_modes:
+            got = maps[rel][b, h]
+            assert got.shape == (R, wl.n)
+            assert np.isfinite(got).all()
+            fa = fold_h[b, h][None, :]
+            zero = ~((fa >= 0) & (fa <= np.arange(R)[:, None]))
+            assert np.array_equal(got[zero], np.zeros(zero.sum())), "entries outside the state must be 0"
+            err = float((np.abs(got - ref[rel]) / scale[None, :]).max()) if got.size else 0.0
+            worst = max(worst, err)
+            assert err <= tol, f"head ({b},{h}) relative={rel}: error {err:.3e} > {tol}"
+    print(f"[collisions] {wl.name}: max scaled error {worst:.3e}", flush=True)
+    return worst
+
+
+COLLIDE_CASES = [
+    (60, dict(n=300, C=16, eta=24, lam=20)),                        # window + cache, ragged last chunk
+    (61, dict(n=1100, C=64, eta=64, lam=64)),                       # several token blocks, ragged block
+    (62, dict(n=90, C=8, eta=0, lam=0)),                            # pure linear: in from its own chunk
+    (63, dict(n=120, C=16, eta=200, lam=10)),                       # eta >= n: nothing folded, all 0
+    (64, dict(n=530, C=32, eta=40, lam=0, d_k=128, d_v=128)),       # d = 128, window only
+    (65, dict(n=70, C=1, eta=0, lam=5)),                            # C = 1: one row per token
+]
+
+
+@pytest.mark.parametrize("seed,kw", COLLIDE_CASES, ids=[f"s{s}" for s, _ in COLLIDE_CASES])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_sre_collisions_small(seed, kw, dtype):
+    wl = small_workload(seed, B=1, h=2, dtype=dtype, **kw)
+    collision_check(wl, [(0, 0), (0, 1)])
+
+
+def test_sre_collisions_rejects_bad_arguments():
+    import hybrid_linear_attention_chunkwise_amd as lola
+    wl = small_workload(66, B=1, h=1, n=64, C=16, eta=24, lam=20, dtype="f32")
+    dev = torch.device("cuda:0")
+    st = lola.LolaState(wl.B, wl.h, wl.d_k, wl.d_v, wl.D, wl.eta, wl.lam, torch.float32, device=dev)
+    lola.lola_state_init(st)
+    vt = torch.zeros(1, 1, 64, 64, device=dev)
+    fold = torch.full((1, 1, 64), -1, dtype=torch.int32, device=dev)
+    need = lola.lola_workspace_bytes(st, 64, 16)
+    small_ws = torch.empty(need - 256, dtype=torch.uint8, device=dev)
+    with pytest.raises(lola.LolaError) as e:
+        lola.lola_sre_collisions(st, vt, fold, 16, small_ws)
+    assert e.value.code == lola.LOLA_EINVAL
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    out = lola.lola_sre_collisions(st, vt, fold, 16, ws)   # nothing folded: all zeros
+    assert torch.count_nonzero(out).item() == 0
