@@ -255,7 +255,8 @@ lola_status lola_sre_collisions(const lola_state* st, const void* v, const int32
     a.ws = reinterpret_cast<const char*>(workspace);
     a.L = L;
     a.out = out;
-    if ((int64_t)a.BH * a.nchunks * a.nblk > (int64_t)INT_MAX) return LOLA_EUNSUPPORTED;
+    if ((int64_t)a.BH * ((a.nchunks + lola::kCollideRows - 1) / lola::kCollideRows) * a.nblk > (int64_t)INT_MAX)
+        return LOLA_EUNSUPPORTED;
     if (lola::launch_collide(a, st->dtype, st->d_k, (hipStream_t)stream) != hipSuccess) return LOLA_EDEVICE;
     if (getenv("LOLA_DEBUG_SYNC") && hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return LOLA_EDEVICE;
     return LOLA_OK;

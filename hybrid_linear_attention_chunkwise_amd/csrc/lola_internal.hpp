@@ -92,7 +92,8 @@ struct CollideArgs {
     WsLayout L;                // its layout (same n and C)
     float* out;                // [BH][nchunks][n]
 };
-constexpr int kCollideTokensPerBlock = 512;
+constexpr int kCollideTokensPerBlock = 256;
+constexpr int kCollideRows = 2;           // map rows per workgroup (their H^T side by side in LDS)
 
 struct InitArgs {
     int BH, D, d_v, lam;
