@@ -34,7 +34,7 @@ Readings where the notes leave a step open (each is listed in the design notes o
   R5 empty state: if phi(k)^T s == 0 the recall is the zero vector, so SRE = ||v||_2.
   R6 ties: exactly lambda are kept; equal SRE is broken toward the older (smaller) position.
   R7 a single feature map phi (and weight W) is shared by queries and keys, heads and batches.
-  R8 collision map: the states are the chunk-end states of a chunked prefill (the figure's per-token
+  R17 collision map: the states are the chunk-end states of a chunked prefill (the figure's per-token
      states are read at chunk granularity, where the chunked path has complete states), one row per
      chunk; a KV enters the map at the end of the chunk that folds it, and "right after it was
      written" is that same row.
@@ -311,7 +311,7 @@ def sre_collisions(st: SeqState, phi, q, k, v, C: int, fold_at_in: Optional[np.n
     Runs ``prefill`` (mutating ``st``; ``fold_at_in`` / ``tol`` as there) and returns (M, y, Schedule)
     with M [n_chunks][n]: M[r, i] = SRE(phi(k_i), v_i | H_r, s_r) for the state (H_r, s_r) at the end
     of chunk r, for every input token i folded in chunk r or before; 0 for a token not in that state
-    (still in the window or the cache, reading R8).  relative: each entry minus the token's entry in
+    (still in the window or the cache, reading R17).  relative: each entry minus the token's entry in
     the row of its own fold, so that row reads 0 and rows before it stay 0."""
     states = []
     y, sched = prefill(st, phi, q, k, v, C, fold_at_in=fold_at_in, tol=tol,
