@@ -16,6 +16,11 @@ Source: "LoLA: Low-Rank Linear Attention With Sparse Caching" reading notes (cc.
   * 2.6, Eq. (15) and Fig. 2: chunked prefill of length C; after a chunk the oldest window chunk and
     the cache are scored together (about C + lambda candidates) and the rest folded in one batch.
   * 2.7: per-head persistent element count.
+  * 4.5, Table 4 (App. F): alternative cache-scoring rules, each accumulated over the queries that
+    see the key in their window: squared and absolute difference of the exp kernel and the feature
+    kernel, their ratio (feature over exp), and the exp kernel alone.
+  * 4.8, Table 12 (App. I): read-branch masks; storage and allocation are unchanged, the query reads
+    only some of {linear state, sparse cache, window}.
   * 4.4, Fig. 3 and Fig. 10 with Eq. (26): the collision map, the SRE of each KV held by the linear
     state against each later state, zero while the KV is not in the state; its relative form subtracts
     the SRE the KV had right after it was written (a difference, not a ratio).
@@ -34,6 +39,13 @@ Readings where the notes leave a step open (each is listed in the design notes o
   R5 empty state: if phi(k)^T s == 0 the recall is the zero vector, so SRE = ||v||_2.
   R6 ties: exactly lambda are kept; equal SRE is broken toward the older (smaller) position.
   R7 a single feature map phi (and weight W) is shared by queries and keys, heads and batches.
+  R18 read masks: a hidden branch leaves both the numerator and the denominator of Eq. (14); every
+     mask includes the window, the one memory that always holds the current token.
+  R19 query-accumulated scores: key i gathers f(q_t, k_i) from every query t whose window holds it
+     (i <= t <= i + eta - 1, reading R1); an allocation at chunk start a uses what queries t < a have
+     added, so a leaving token's score may still be partial while a cache member's is complete.  The
+     kept keys are the lambda largest scores (ties: older position), like SRE.  The score is fixed
+     once the key leaves the window; the state carries it with the key.
   R17 collision map: the states are the chunk-end states of a chunked prefill (the figure's per-token
      states are read at chunk granularity, where the chunked path has complete states), one row per
      chunk; a KV enters the map at the end of the chunk that folds it, and "right after it was
@@ -51,7 +63,14 @@ import numpy as np
 
 __all__ = ["phi_elu1", "phi_softmax_pm", "make_phi", "sre", "SeqState", "new_state", "prefill",
            "decode_step", "replay", "exact_attention_read", "state_elements", "Schedule",
-           "state_from_arrays", "sre_collisions"]
+           "state_from_arrays", "sre_collisions", "READ_STATE", "READ_SPARSE", "READ_WINDOW",
+           "READ_ALL", "SCORE_RULES", "query_score"]
+
+# Read-branch masks (4.8, Table 12).
+READ_STATE, READ_SPARSE, READ_WINDOW = 1, 2, 4
+READ_ALL = READ_STATE | READ_SPARSE | READ_WINDOW
+# Cache-scoring rules (4.5, Table 4): SRE against the state, or a score accumulated over queries.
+SCORE_RULES = ("sre", "kernel_sq", "kernel_abs", "ratio", "attn")
 
 
 # --------------------------------------------------------------------------------------------------
@@ -103,6 +122,24 @@ def sre(phi_k: np.ndarray, v: np.ndarray, H: np.ndarray, s: np.ndarray) -> np.nd
     return np.sqrt(((recall - v) ** 2).sum(axis=-1))
 
 
+def query_score(rule: str, q_t, phi_q, k, phi_k, d_k: int) -> np.ndarray:
+    """One query's contribution to the query-accumulated scores of keys k [m][d_k] (reading R19).
+
+    e = exp(q^T k / sqrt(d_k)) is the exp kernel, p = phi(q)^T phi(k) the feature kernel:
+    kernel_sq (e - p)^2, kernel_abs |e - p|, ratio p / e, attn e."""
+    e = np.exp(np.atleast_2d(k) @ q_t / np.sqrt(d_k))
+    p = np.atleast_2d(phi_k) @ phi_q
+    if rule == "kernel_sq":
+        return (e - p) ** 2
+    if rule == "kernel_abs":
+        return np.abs(e - p)
+    if rule == "ratio":
+        return p / e
+    if rule == "attn":
+        return e
+    raise ValueError(f"unknown query-accumulated rule {rule!r}")
+
+
 # --------------------------------------------------------------------------------------------------
 # Per-sequence state: the three memories of section 2.4 (window, sparse cache, linear state).
 # --------------------------------------------------------------------------------------------------
@@ -118,16 +155,20 @@ class SeqState:
     V: np.ndarray                  # [capacity][d_v]
     cache: List[int]               # positions in the sparse cache G
     folded: List[int]              # positions folded into (H, s), in fold order
+    score: np.ndarray = None       # [capacity]: query-accumulated score by position (reading R19)
 
     def window(self, t: int) -> range:
         """Positions in the window of query t (reading R1)."""
         return range(max(0, t - self.eta + 1), t + 1)
 
     def ensure(self, cap: int) -> None:
+        if self.score is None:
+            self.score = np.zeros(self.K.shape[0])
         if self.K.shape[0] < cap:
             grow = cap - self.K.shape[0]
             self.K = np.concatenate([self.K, np.full((grow, self.K.shape[1]), np.nan)])
             self.V = np.concatenate([self.V, np.full((grow, self.V.shape[1]), np.nan)])
+            self.score = np.concatenate([self.score, np.zeros(grow)])
 
     def forget(self, i: int) -> None:
         self.K[i] = np.nan
@@ -135,7 +176,8 @@ class SeqState:
 
     def copy(self) -> "SeqState":
         return SeqState(self.eta, self.lam, self.H.copy(), self.s.copy(), self.t, self.K.copy(),
-                        self.V.copy(), list(self.cache), list(self.folded))
+                        self.V.copy(), list(self.cache), list(self.folded),
+                        None if self.score is None else self.score.copy())
 
 
 def new_state(d_k: int, d_v: int, D: int, eta: int, lam: int) -> SeqState:
@@ -143,10 +185,12 @@ def new_state(d_k: int, d_v: int, D: int, eta: int, lam: int) -> SeqState:
                     K=np.zeros((0, d_k)), V=np.zeros((0, d_v)), cache=[], folded=[])
 
 
-def state_from_arrays(t, eta, lam, H, s, win_k, win_v, cache_k, cache_v, cache_pos) -> SeqState:
+def state_from_arrays(t, eta, lam, H, s, win_k, win_v, cache_k, cache_v, cache_pos, win_score=None,
+                      cache_score=None) -> SeqState:
     """Build a state from a ring window (slot = pos mod eta) and a slotted cache (pos -1 = empty).
 
-    Used to continue from a state produced elsewhere (for example a post-prefill snapshot)."""
+    Used to continue from a state produced elsewhere (for example a post-prefill snapshot).
+    win_score / cache_score (optional, same slots) restore the query-accumulated scores."""
     d_k = win_k.shape[-1] if eta > 0 else cache_k.shape[-1]
     d_v = win_v.shape[-1] if eta > 0 else cache_v.shape[-1]
     st = SeqState(eta=eta, lam=lam, H=np.array(H, dtype=np.float64),
@@ -156,11 +200,15 @@ def state_from_arrays(t, eta, lam, H, s, win_k, win_v, cache_k, cache_v, cache_p
     for pos in range(max(0, t - eta), t):
         st.K[pos] = win_k[pos % eta]
         st.V[pos] = win_v[pos % eta]
+        if win_score is not None:
+            st.score[pos] = win_score[pos % eta]
     for slot, pos in enumerate(np.asarray(cache_pos).tolist()):
         if pos >= 0:
             st.K[pos] = cache_k[slot]
             st.V[pos] = cache_v[slot]
             st.cache.append(int(pos))
+            if cache_score is not None:
+                st.score[pos] = cache_score[slot]
     st.cache.sort()
     return st
 
@@ -177,13 +225,14 @@ class Schedule:
     worst_inversion: float = 0.0                  # replay: max (max_S SRE - min_G' SRE) / max_S SRE
 
 
-def exact_attention_read(q_t, phi_q, H, s, keys, vals, d_k):
+def exact_attention_read(q_t, phi_q, H, s, keys, vals, d_k, use_state: bool = True):
     """Eq. (14): one shared denominator over the linear state and the exact keys.
 
     Numerator and denominator are both multiplied by exp(-m), m the largest exact logit, which is an
-    exact identity that keeps the exponentials in range."""
-    lin_num = H.T @ phi_q
-    lin_den = float(phi_q @ s)
+    exact identity that keeps the exponentials in range.  use_state=False drops the linear terms
+    (read mask without the state, reading R18)."""
+    lin_num = H.T @ phi_q if use_state else np.zeros(H.shape[1])
+    lin_den = float(phi_q @ s) if use_state else 0.0
     if len(keys) == 0:
         return lin_num / lin_den
     logits = (keys @ q_t) / np.sqrt(d_k)
@@ -194,14 +243,17 @@ def exact_attention_read(q_t, phi_q, H, s, keys, vals, d_k):
 
 
 def prefill(st: SeqState, phi, q, k, v, C: int, fold_at_in: Optional[np.ndarray] = None,
-            tol: float = 0.0, on_chunk_end: Optional[Callable[[int, SeqState], None]] = None):
+            tol: float = 0.0, on_chunk_end: Optional[Callable[[int, SeqState], None]] = None,
+            read_mask: int = READ_ALL, score_rule: str = "sre"):
     """Chunked prefill of n tokens for one sequence and head (section 2.6), read out token by token.
 
     q, k: [n][d_k]; v: [n][d_v].  Mutates ``st``.  Returns (y [n][d_v], Schedule).
     ``fold_at_in`` replays an external schedule (call-local chunk id per input token, -1 = not
     folded): its decisions replace the top-lambda, and each is checked against the fp64 SRE order
     with relative tolerance ``tol`` (problems are recorded in the returned Schedule).
-    ``on_chunk_end(c, st)`` is called once per chunk, after the chunk's folds and commit."""
+    ``on_chunk_end(c, st)`` is called once per chunk, after the chunk's folds and commit.
+    ``read_mask`` (READ_*) selects the memories the queries read (reading R18); ``score_rule`` one of
+    SCORE_RULES ranks the candidates (SRE against the state, or reading R19's accumulated scores)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -211,6 +263,10 @@ def prefill(st: SeqState, phi, q, k, v, C: int, fold_at_in: Optional[np.ndarray]
         raise ValueError("chunk length must be >= 1")
     if lam > 0 and eta < C - 1:
         raise ValueError("reading R4: lambda > 0 needs eta >= C - 1")
+    if not read_mask & READ_WINDOW or read_mask & ~READ_ALL:
+        raise ValueError("reading R18: a read mask holds the window and nothing but the three memories")
+    if score_rule not in SCORE_RULES:
+        raise ValueError(f"unknown score rule {score_rule!r}")
     t0 = st.t
     st.ensure(t0 + n)
     st.K[t0:t0 + n] = k
@@ -225,7 +281,10 @@ def prefill(st: SeqState, phi, q, k, v, C: int, fold_at_in: Optional[np.ndarray]
         E = sorted(set(st.cache) | set(X))
         scores = None
         if len(E) > lam and lam > 0:
-            scores = dict(zip(E, sre(phi(st.K[E]), st.V[E], st.H, st.s)))
+            if score_rule == "sre":
+                scores = dict(zip(E, sre(phi(st.K[E]), st.V[E], st.H, st.s)))
+            else:   # reading R19: what queries before the chunk start have added
+                scores = {i: float(st.score[i]) for i in E}
         gap = None
         if fold_at_in is None:
             if len(E) <= lam:
@@ -269,11 +328,15 @@ def prefill(st: SeqState, phi, q, k, v, C: int, fold_at_in: Optional[np.ndarray]
                     st.H += np.outer(phi_S[i], v_S[i])
                     st.s += phi_S[i]
             win = st.window(t)
-            extra = [i for i in kept if i < win.start]
+            extra = [i for i in kept if i < win.start] if read_mask & READ_SPARSE else []
             idx = np.concatenate([np.arange(win.start, win.stop, dtype=np.int64),
                                   np.asarray(extra, dtype=np.int64)])
             phi_q = phi(q[t - t0][None, :])[0]
-            y[t - t0] = exact_attention_read(q[t - t0], phi_q, st.H, st.s, st.K[idx], st.V[idx], d_k)
+            y[t - t0] = exact_attention_read(q[t - t0], phi_q, st.H, st.s, st.K[idx], st.V[idx], d_k,
+                                             use_state=bool(read_mask & READ_STATE))
+            if score_rule != "sre" and len(win) > 0:   # query t adds to every key in its window
+                wi = np.arange(win.start, win.stop, dtype=np.int64)
+                st.score[wi] += query_score(score_rule, q[t - t0], phi_q, st.K[wi], phi(st.K[wi]), d_k)
         # 5. commit: G <- G', folded tokens lose their exact KV
         for i in S:
             st.forget(i)
@@ -286,12 +349,12 @@ def prefill(st: SeqState, phi, q, k, v, C: int, fold_at_in: Optional[np.ndarray]
     return y, sched
 
 
-def decode_step(st: SeqState, phi, q, k, v):
+def decode_step(st: SeqState, phi, q, k, v, read_mask: int = READ_ALL, score_rule: str = "sre"):
     """One decode token (section 2.4 single-token update, then Eq. (14)): prefill with C = 1.
 
     Returns (y [d_v], folded position or -1)."""
     y, sched = prefill(st, phi, np.asarray(q)[None, :], np.asarray(k)[None, :],
-                       np.asarray(v)[None, :], C=1)
+                       np.asarray(v)[None, :], C=1, read_mask=read_mask, score_rule=score_rule)
     S = sched.folded[0]
     return y[0], (S[0] if S else -1)
 

@@ -513,3 +513,129 @@ def test_collision_with_cache_matches_rebuilt_states(relative):
     if relative:
         for i in np.nonzero(fa >= 0)[0]:
             assert M[fa[i], i] == 0.0
+
+
+# ------------------------------------------------------------------------------------------------
+# Read-branch masks (4.8, Table 12) and query-accumulated scoring rules (4.5, Table 4).
+# ------------------------------------------------------------------------------------------------
+
+def _sliding_window_softmax(q, k, v, eta):
+    n, d_k = q.shape
+    y = np.zeros_like(v)
+    for t in range(n):
+        lo = max(0, t - eta + 1)
+        w = np.array([np.exp(float(np.dot(q[t], k[i])) / np.sqrt(d_k)) for i in range(lo, t + 1)])
+        y[t] = w @ v[lo:t + 1] / w.sum()
+    return y
+
+
+@pytest.mark.parametrize("lam,C", [(0, 1), (5, 4), (9, 7)])
+def test_read_window_only_is_sliding_window_softmax(lam, C):
+    """Only the window read: softmax over the last eta tokens, whatever the cache and state hold."""
+    eta, n = 6, 40
+    phi, q, k, v = _rand_problem(40, n)
+    st = O.new_state(8, 6, 8, eta, lam)
+    y, _ = O.prefill(st, phi, q, k, v, C, read_mask=O.READ_WINDOW)
+    np.testing.assert_allclose(y, _sliding_window_softmax(q, k, v, eta), rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("mask", [O.READ_WINDOW, O.READ_WINDOW | O.READ_STATE, O.READ_WINDOW | O.READ_SPARSE,
+                                  O.READ_ALL])
+@pytest.mark.parametrize("eta,lam,C", [(6, 5, 4), (10, 4, 1), (5, 8, 6)])
+def test_read_masks_per_pair_and_schedule_unchanged(mask, eta, lam, C):
+    """Eq. (14) pair by pair with the hidden branches' terms removed from numerator and denominator;
+    the allocation (fold sets, kept sets) is the unmasked one."""
+    n = 48
+    phi, q, k, v = _rand_problem(41, n, scale=1.3)
+    _, sched_full, _ = _run(phi, q, k, v, eta, lam, C)
+    st = O.new_state(8, 6, 8, eta, lam)
+    y, sched = O.prefill(st, phi, q, k, v, C, read_mask=mask)
+    assert sched.folded == sched_full.folded and sched.kept == sched_full.kept
+    fq, fk = phi(q), phi(k)
+    fold_chunk = {i: c for c, S in enumerate(sched.folded) for i in S}
+    for t in range(n):
+        c = t // C
+        kept = set(sched.kept[c])
+        num, den = np.zeros(v.shape[1]), 0.0
+        for i in range(t + 1):
+            fc = fold_chunk.get(i, n)
+            if fc <= c and max(i + eta, fc * C) <= t:
+                if not mask & O.READ_STATE:
+                    continue
+                w = fq[t] @ fk[i]
+            elif t - eta + 1 <= i:
+                w = np.exp(q[t] @ k[i] / np.sqrt(8))
+            else:
+                assert i in kept
+                if not mask & O.READ_SPARSE:
+                    continue
+                w = np.exp(q[t] @ k[i] / np.sqrt(8))
+            num += w * v[i]
+            den += w
+        np.testing.assert_allclose(y[t], num / den, rtol=1e-11, atol=1e-12)
+
+
+def test_read_mask_without_window_is_rejected():
+    phi, q, k, v = _rand_problem(42, 5)
+    with pytest.raises(ValueError):
+        O.prefill(O.new_state(8, 6, 8, 2, 2), phi, q, k, v, 1, read_mask=O.READ_STATE | O.READ_SPARSE)
+
+
+def _rule_value(rule, qt, kt, fqt, fkt):
+    """One query's contribution, written with scalar loops."""
+    dot = sum(float(a) * float(b) for a, b in zip(qt, kt))
+    e = float(np.exp(dot / np.sqrt(len(qt))))
+    p = sum(float(a) * float(b) for a, b in zip(fqt, fkt))
+    return {"kernel_sq": (e - p) ** 2, "kernel_abs": abs(e - p), "ratio": p / e, "attn": e}[rule]
+
+
+@pytest.mark.parametrize("rule", ["kernel_sq", "kernel_abs", "ratio", "attn"])
+@pytest.mark.parametrize("eta,lam,C", [(4, 3, 1), (6, 5, 4), (8, 4, 3)])
+def test_query_scores_kept_sets_are_top_lambda_by_brute_force(rule, eta, lam, C):
+    """At each chunk start a, a candidate's score is the sum of its contributions from the queries
+    t < a whose window held it (i <= t <= i + eta - 1), and the kept set is the lambda largest
+    (ties: older)."""
+    n = 36
+    phi, q, k, v = _rand_problem(43, n, scale=1.4)
+    fq, fk = phi(q), phi(k)
+    st = O.new_state(8, 6, 8, eta, lam)
+    _, sched = O.prefill(st, phi, q, k, v, C, score_rule=rule)
+    cache = []
+    for c, a in enumerate(sched.chunk_start):
+        b = min(a + C, n)
+        E = sorted(set(cache) | {i for i in range(a - eta, b - eta) if i >= 0})
+        if len(E) <= lam:
+            want = E
+        else:
+            sc = {i: sum(_rule_value(rule, q[t], k[i], fq[t], fk[i]) for t in range(i, min(i + eta, a)))
+                  for i in E}
+            want = sorted(sorted(E, key=lambda i: (-sc[i], i))[:lam])
+        assert sched.kept[c] == want, (c, sched.kept[c], want)
+        cache = want
+
+
+@pytest.mark.parametrize("rule", ["kernel_sq", "attn", "ratio"])
+def test_query_scores_c1_final_cache_is_global_top_lambda(rule):
+    """C = 1: a leaving token's score is complete and fixed, so greedy keep-the-largest leaves the
+    lambda best of all tokens that have left the window."""
+    n, eta, lam = 40, 5, 6
+    phi, q, k, v = _rand_problem(44, n, scale=1.2)
+    fq, fk = phi(q), phi(k)
+    st = O.new_state(8, 6, 8, eta, lam)
+    O.prefill(st, phi, q, k, v, 1, score_rule=rule)
+    left = list(range(n - eta))
+    sc = {i: sum(_rule_value(rule, q[t], k[i], fq[t], fk[i]) for t in range(i, i + eta)) for i in left}
+    assert sorted(st.cache) == sorted(sorted(left, key=lambda i: (-sc[i], i))[:lam])
+
+
+def test_query_scores_survive_a_call_boundary():
+    """Scores carried by the state: two calls equal one call, with any rule."""
+    phi, q, k, v = _rand_problem(45, 48, scale=1.2)
+    for rule in ("kernel_abs", "attn"):
+        st1 = O.new_state(8, 6, 8, 6, 5)
+        y1, s1 = O.prefill(st1, phi, q, k, v, 4, score_rule=rule)
+        st2 = O.new_state(8, 6, 8, 6, 5)
+        ya, _ = O.prefill(st2, phi, q[:20], k[:20], v[:20], 4, score_rule=rule)
+        yb, _ = O.prefill(st2, phi, q[20:], k[20:], v[20:], 4, score_rule=rule)
+        np.testing.assert_allclose(np.concatenate([ya, yb]), y1, rtol=1e-12, atol=1e-13)
+        assert sorted(st1.cache) == sorted(st2.cache)
