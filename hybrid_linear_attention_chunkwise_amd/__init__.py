@@ -13,11 +13,13 @@ import torch
 
 from . import _binding as _b
 from ._binding import (LOLA_BF16, LOLA_EDEVICE, LOLA_EINVAL, LOLA_EUNSUPPORTED, LOLA_F32, LOLA_OK,
-                       LOLA_PHI_ELU1, LOLA_PHI_SOFTMAX_PM, LolaError)
+                       LOLA_PHI_ELU1, LOLA_PHI_SOFTMAX_PM, LOLA_READ_ALL, LOLA_READ_SPARSE,
+                       LOLA_READ_STATE, LOLA_READ_WINDOW, SCORE_RULES, LolaError)
 
 __all__ = ["LolaState", "LolaPhi", "lola_state_init", "lola_workspace_bytes", "lola_prefill",
            "lola_decode_step", "lola_sre_collisions", "LolaError", "LOLA_OK", "LOLA_EINVAL", "LOLA_EUNSUPPORTED",
-           "LOLA_EDEVICE", "library_path", "PHI_KINDS"]
+           "LOLA_EDEVICE", "library_path", "PHI_KINDS", "LOLA_READ_STATE", "LOLA_READ_SPARSE",
+           "LOLA_READ_WINDOW", "LOLA_READ_ALL", "SCORE_RULES"]
 
 PHI_KINDS = {"elu1": LOLA_PHI_ELU1, "softmax_pm": LOLA_PHI_SOFTMAX_PM}
 _DTYPES = {torch.float32: LOLA_F32, torch.bfloat16: LOLA_BF16}
@@ -62,10 +64,13 @@ class LolaState:
         self.cache_k = torch.zeros(B, n_heads, max(lam, 1), d_k, dtype=dtype, **kw)
         self.cache_v = torch.zeros(B, n_heads, max(lam, 1), d_v, dtype=dtype, **kw)
         self.cache_pos = torch.full((B, n_heads, max(lam, 1)), -1, dtype=torch.int32, **kw)
+        self.win_score = torch.zeros(B, n_heads, max(eta, 1), dtype=torch.float32, **kw)
+        self.cache_score = torch.zeros(B, n_heads, max(lam, 1), dtype=torch.float32, **kw)
         self.c = _b.LolaState(B, n_heads, d_k, d_v, D, eta, lam, _DTYPES[dtype], 0,
                               self.H.data_ptr(), self.s.data_ptr(), self.win_k.data_ptr(),
                               self.win_v.data_ptr(), self.cache_k.data_ptr(), self.cache_v.data_ptr(),
-                              self.cache_pos.data_ptr())
+                              self.cache_pos.data_ptr(), self.win_score.data_ptr(),
+                              self.cache_score.data_ptr())
 
     @property
     def t(self) -> int:
@@ -78,11 +83,12 @@ class LolaState:
 
     def snapshot(self) -> dict:
         """Device copies of every state array plus t (for restore / checkpoint)."""
-        return {k: getattr(self, k).clone() for k in
-                ("H", "s", "win_k", "win_v", "cache_k", "cache_v", "cache_pos")} | {"t": self.t}
+        return {k: getattr(self, k).clone() for k in self._ARRAYS} | {"t": self.t}
+
+    _ARRAYS = ("H", "s", "win_k", "win_v", "cache_k", "cache_v", "cache_pos", "win_score", "cache_score")
 
     def restore(self, snap: dict) -> None:
-        for k in ("H", "s", "win_k", "win_v", "cache_k", "cache_v", "cache_pos"):
+        for k in self._ARRAYS:
             getattr(self, k).copy_(snap[k])
         self.c.t = snap["t"]
 
@@ -95,13 +101,22 @@ def lola_state_init(state: LolaState, stream=None) -> None:
     _b.check("lola_state_init", _b.load().lola_state_init(ctypes.byref(state.c), _stream(stream)))
 
 
+def _options(read_mask: int, score_rule: str):
+    """ctypes options, or None for the defaults."""
+    if read_mask == LOLA_READ_ALL and score_rule == "sre":
+        return None
+    return _b.LolaOptions(read_mask, SCORE_RULES[score_rule], (ctypes.c_int32 * 2)(0, 0))
+
+
 def lola_prefill(state: LolaState, phi: LolaPhi, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                  C: int, y: Optional[torch.Tensor] = None, fold_at: Optional[torch.Tensor] = None,
-                 workspace: Optional[torch.Tensor] = None, stream=None, events=None):
+                 workspace: Optional[torch.Tensor] = None, stream=None, events=None,
+                 read_mask: int = LOLA_READ_ALL, score_rule: str = "sre"):
     """Chunked prefill of q, k, v [B][h][n][d]; returns (y, fold_at).  Asynchronous on `stream`.
 
     ``events``: optional 5 torch.cuda.Event (created with enable_timing=True) recorded at the kernel
-    boundaries: before the feature kernel, then after the feature, chain, read-out and commit kernels."""
+    boundaries: before the feature kernel, then after the feature, chain, read-out and commit kernels.
+    ``read_mask`` / ``score_rule``: see lola_options (lola_prefill_ex); not combinable with events."""
     n = q.shape[2]
     if y is None:
         y = torch.empty(q.shape[0], q.shape[1], n, v.shape[3], dtype=v.dtype, device=v.device)
@@ -111,7 +126,12 @@ def lola_prefill(state: LolaState, phi: LolaPhi, q: torch.Tensor, k: torch.Tenso
     lib = _b.load()
     args = (ctypes.byref(state.c), ctypes.byref(phi.c), _ptr(q), _ptr(k), _ptr(v), n, C, _ptr(y),
             _ptr(fold_at), _ptr(workspace), workspace.numel(), _stream(stream))
-    if events is None:
+    opts = _options(read_mask, score_rule)
+    if opts is not None:
+        if events is not None:
+            raise ValueError("events are recorded by the default-options entry point only")
+        code = lib.lola_prefill_ex(*args[:7], ctypes.byref(opts), *args[7:])
+    elif events is None:
         code = lib.lola_prefill(*args)
     else:
         handles = (ctypes.c_void_p * 5)(*[None if e is None else e.cuda_event for e in events])
@@ -122,12 +142,19 @@ def lola_prefill(state: LolaState, phi: LolaPhi, q: torch.Tensor, k: torch.Tenso
 
 def lola_decode_step(state: LolaState, phi: LolaPhi, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                      y: Optional[torch.Tensor] = None, folded_pos: Optional[torch.Tensor] = None,
-                     stream=None):
+                     stream=None, read_mask: int = LOLA_READ_ALL, score_rule: str = "sre"):
     """One decode token, q, k, v [B][h][d]; returns (y, folded_pos).  Asynchronous on `stream`."""
     if y is None:
         y = torch.empty(v.shape, dtype=v.dtype, device=v.device)
-    code = _b.load().lola_decode_step(ctypes.byref(state.c), ctypes.byref(phi.c), _ptr(q), _ptr(k),
-                                      _ptr(v), _ptr(y), _ptr(folded_pos), _stream(stream))
+    lib = _b.load()
+    opts = _options(read_mask, score_rule)
+    if opts is None:
+        code = lib.lola_decode_step(ctypes.byref(state.c), ctypes.byref(phi.c), _ptr(q), _ptr(k),
+                                    _ptr(v), _ptr(y), _ptr(folded_pos), _stream(stream))
+    else:
+        code = lib.lola_decode_step_ex(ctypes.byref(state.c), ctypes.byref(phi.c), _ptr(q), _ptr(k),
+                                       _ptr(v), ctypes.byref(opts), _ptr(y), _ptr(folded_pos),
+                                       _stream(stream))
     _b.check("lola_decode_step", code)
     return y, folded_pos
 

@@ -21,8 +21,14 @@ LOLA_BF16 = 1
 LOLA_PHI_ELU1 = 0
 LOLA_PHI_SOFTMAX_PM = 1
 
-EXPORTED = ("lola_workspace_bytes", "lola_state_init", "lola_prefill", "lola_prefill_profiled",
-            "lola_decode_step", "lola_sre_collisions", "lola_status_string")
+EXPORTED = ("lola_workspace_bytes", "lola_state_init", "lola_prefill", "lola_prefill_ex",
+            "lola_prefill_profiled", "lola_decode_step", "lola_decode_step_ex", "lola_sre_collisions",
+            "lola_status_string")
+LOLA_READ_STATE = 1
+LOLA_READ_SPARSE = 2
+LOLA_READ_WINDOW = 4
+LOLA_READ_ALL = 7
+SCORE_RULES = {"sre": 0, "kernel_sq": 1, "kernel_abs": 2, "ratio": 3, "attn": 4}
 
 
 class LolaPhi(ctypes.Structure):
@@ -36,7 +42,13 @@ class LolaState(ctypes.Structure):
                 ("lambda_", ctypes.c_int32), ("dtype", ctypes.c_int32), ("t", ctypes.c_int64),
                 ("H", ctypes.c_void_p), ("s", ctypes.c_void_p), ("win_k", ctypes.c_void_p),
                 ("win_v", ctypes.c_void_p), ("cache_k", ctypes.c_void_p), ("cache_v", ctypes.c_void_p),
-                ("cache_pos", ctypes.c_void_p)]
+                ("cache_pos", ctypes.c_void_p), ("win_score", ctypes.c_void_p),
+                ("cache_score", ctypes.c_void_p)]
+
+
+class LolaOptions(ctypes.Structure):
+    _fields_ = [("read_mask", ctypes.c_int32), ("score_rule", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 2)]
 
 
 class LolaError(RuntimeError):
@@ -70,6 +82,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lola_prefill_profiled.restype = i32
     lib.lola_decode_step.argtypes = [sp, pp, vp, vp, vp, vp, vp, vp]
     lib.lola_decode_step.restype = i32
+    op = ctypes.POINTER(LolaOptions)
+    lib.lola_prefill_ex.argtypes = [sp, pp, vp, vp, vp, i64, i32, op, vp, vp, vp, sz, vp]
+    lib.lola_prefill_ex.restype = i32
+    lib.lola_decode_step_ex.argtypes = [sp, pp, vp, vp, vp, op, vp, vp, vp]
+    lib.lola_decode_step_ex.restype = i32
     lib.lola_sre_collisions.argtypes = [sp, vp, vp, i64, i32, vp, sz, i32, vp, vp]
     lib.lola_sre_collisions.restype = i32
     lib.lola_status_string.argtypes = [i32]

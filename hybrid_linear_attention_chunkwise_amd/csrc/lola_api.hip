@@ -42,6 +42,20 @@ lola_status check_state_ptrs(const lola_state* st) {
     return LOLA_OK;
 }
 
+// Options: mask within the three memories and holding the window; a known rule; zero reserved fields.
+// Scores need the state's score arrays.
+lola_status check_options(const lola_state* st, const lola_options* opt) {
+    if (!opt) return LOLA_OK;
+    if ((opt->read_mask & ~LOLA_READ_ALL) != 0 || !(opt->read_mask & LOLA_READ_WINDOW)) return LOLA_EINVAL;
+    if (opt->score_rule < LOLA_SCORE_SRE || opt->score_rule > LOLA_SCORE_ATTN) return LOLA_EINVAL;
+    if (opt->reserved[0] != 0 || opt->reserved[1] != 0) return LOLA_EINVAL;
+    if (opt->score_rule != LOLA_SCORE_SRE) {
+        if (st->eta > 0 && (!st->win_score || !aligned16(st->win_score))) return LOLA_EINVAL;
+        if (st->lambda > 0 && (!st->cache_score || !aligned16(st->cache_score))) return LOLA_EINVAL;
+    }
+    return LOLA_OK;
+}
+
 lola_status check_phi(const lola_state* st, const lola_phi* phi) {
     if (!phi || !phi->W || !aligned16(phi->W)) return LOLA_EINVAL;
     if (phi->kind != LOLA_PHI_ELU1 && phi->kind != LOLA_PHI_SOFTMAX_PM) return LOLA_EINVAL;
@@ -121,17 +135,20 @@ lola_status lola_state_init(lola_state* st, void* stream) {
     a.D = st->D;
     a.d_v = st->d_v;
     a.lam = st->lambda;
+    a.eta = st->eta;
     a.H = st->H;
     a.s = st->s;
     a.cache_pos = st->cache_pos;
+    a.win_score = st->eta > 0 ? st->win_score : nullptr;
+    a.cache_score = st->lambda > 0 ? st->cache_score : nullptr;
     if (lola::launch_init(a, (hipStream_t)stream) != hipSuccess) return LOLA_EDEVICE;
     st->t = 0;
     return LOLA_OK;
 }
 
 static lola_status prefill_impl(lola_state* st, const lola_phi* phi, const void* q, const void* k,
-                                const void* v, int64_t n, int32_t C, void* y, int32_t* fold_at,
-                                void* workspace, size_t workspace_bytes, void* stream,
+                                const void* v, int64_t n, int32_t C, const lola_options* opt, void* y,
+                                int32_t* fold_at, void* workspace, size_t workspace_bytes, void* stream,
                                 void* const* events) {
     lola_status rc = check_shape(st);
     if (rc != LOLA_OK) return rc;
@@ -139,6 +156,9 @@ static lola_status prefill_impl(lola_state* st, const lola_phi* phi, const void*
     if (rc != LOLA_OK) return rc;
     rc = check_phi(st, phi);
     if (rc != LOLA_OK) return rc;
+    rc = check_options(st, opt);
+    if (rc != LOLA_OK) return rc;
+    if (opt && opt->score_rule != LOLA_SCORE_SRE) return LOLA_EUNSUPPORTED;
     rc = check_prefill_config(st, n, C);
     if (rc != LOLA_OK) return rc;
     if (n == 0) return LOLA_OK;
@@ -156,6 +176,7 @@ static lola_status prefill_impl(lola_state* st, const lola_phi* phi, const void*
     a.lam = st->lambda;
     a.nchunks = L.nchunks;
     a.nqt = (C + 63) / 64;
+    a.read_mask = opt ? opt->read_mask : LOLA_READ_ALL;
     a.t0 = st->t;
     a.q = q; a.k = k; a.v = v; a.y = y;
     a.W = phi->W;
@@ -177,24 +198,33 @@ static lola_status prefill_impl(lola_state* st, const lola_phi* phi, const void*
 lola_status lola_prefill(lola_state* st, const lola_phi* phi, const void* q, const void* k, const void* v,
                          int64_t n, int32_t C, void* y, int32_t* fold_at, void* workspace,
                          size_t workspace_bytes, void* stream) {
-    return prefill_impl(st, phi, q, k, v, n, C, y, fold_at, workspace, workspace_bytes, stream, nullptr);
+    return prefill_impl(st, phi, q, k, v, n, C, nullptr, y, fold_at, workspace, workspace_bytes, stream, nullptr);
+}
+
+lola_status lola_prefill_ex(lola_state* st, const lola_phi* phi, const void* q, const void* k, const void* v,
+                            int64_t n, int32_t C, const lola_options* opt, void* y, int32_t* fold_at,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    return prefill_impl(st, phi, q, k, v, n, C, opt, y, fold_at, workspace, workspace_bytes, stream, nullptr);
 }
 
 lola_status lola_prefill_profiled(lola_state* st, const lola_phi* phi, const void* q, const void* k,
                                   const void* v, int64_t n, int32_t C, void* y, int32_t* fold_at,
                                   void* workspace, size_t workspace_bytes, void* stream,
                                   void* const events[5]) {
-    return prefill_impl(st, phi, q, k, v, n, C, y, fold_at, workspace, workspace_bytes, stream, events);
+    return prefill_impl(st, phi, q, k, v, n, C, nullptr, y, fold_at, workspace, workspace_bytes, stream, events);
 }
 
-lola_status lola_decode_step(lola_state* st, const lola_phi* phi, const void* q, const void* k, const void* v,
-                             void* y, int32_t* folded_pos, void* stream) {
+static lola_status decode_impl(lola_state* st, const lola_phi* phi, const void* q, const void* k, const void* v,
+                               const lola_options* opt, void* y, int32_t* folded_pos, void* stream) {
     lola_status rc = check_shape(st);
     if (rc != LOLA_OK) return rc;
     rc = check_state_ptrs(st);
     if (rc != LOLA_OK) return rc;
     rc = check_phi(st, phi);
     if (rc != LOLA_OK) return rc;
+    rc = check_options(st, opt);
+    if (rc != LOLA_OK) return rc;
+    if (opt && opt->score_rule != LOLA_SCORE_SRE) return LOLA_EUNSUPPORTED;
     if (!q || !k || !v || !y || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y)) return LOLA_EINVAL;
     if (folded_pos && !aligned16(folded_pos)) return LOLA_EINVAL;
     if (st->t + 1 + st->eta >= (int64_t)INT_MAX) return LOLA_EUNSUPPORTED;
@@ -206,6 +236,7 @@ lola_status lola_decode_step(lola_state* st, const lola_phi* phi, const void* q,
     a.BH = st->B * st->n_heads;
     a.eta = st->eta;
     a.lam = st->lambda;
+    a.read_mask = opt ? opt->read_mask : LOLA_READ_ALL;
     a.t = st->t;
     a.q = q; a.k = k; a.v = v; a.y = y;
     a.W = phi->W;
@@ -223,6 +254,16 @@ lola_status lola_decode_step(lola_state* st, const lola_phi* phi, const void* q,
     if (getenv("LOLA_DEBUG_SYNC") && hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return LOLA_EDEVICE;
     st->t += 1;
     return LOLA_OK;
+}
+
+lola_status lola_decode_step(lola_state* st, const lola_phi* phi, const void* q, const void* k, const void* v,
+                             void* y, int32_t* folded_pos, void* stream) {
+    return decode_impl(st, phi, q, k, v, nullptr, y, folded_pos, stream);
+}
+
+lola_status lola_decode_step_ex(lola_state* st, const lola_phi* phi, const void* q, const void* k, const void* v,
+                                const lola_options* opt, void* y, int32_t* folded_pos, void* stream) {
+    return decode_impl(st, phi, q, k, v, opt, y, folded_pos, stream);
 }
 
 lola_status lola_sre_collisions(const lola_state* st, const void* v, const int32_t* fold_at, int64_t n,

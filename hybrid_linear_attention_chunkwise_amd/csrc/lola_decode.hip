@@ -333,6 +333,7 @@ __global__ __launch_bounds__(4 * DK) void decode_kernel(DecodeArgs A) {
     // exact set: window + cache after the allocation (occupied slots except a folded one, plus the
     // leaving token unless it was folded)
     auto cache_row_exact = [&](int r) -> bool {
+        if (!(A.read_mask & kReadSparse)) return false;   // hidden cache: no exact cache keys
         if (r < lam) return sCpos[r] >= 0 && r != f_row;
         return has_e && f_row != lam && lam > 0;
     };
@@ -401,8 +402,10 @@ __global__ __launch_bounds__(4 * DK) void decode_kernel(DecodeArgs A) {
 
     // ---- output ----
     {
+        const bool rs = (A.read_mask & kReadState) != 0;   // hidden state: no linear terms
         float lden = 0.f;
-        for (int f = 0; f < D; ++f) lden += sPhiQ[f] * sS[f];
+        if (rs)
+            for (int f = 0; f < D; ++f) lden += sPhiQ[f] * sS[f];
         float lsum_all = 0.f;
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) lsum_all += sRedF[8 + ww];
@@ -410,7 +413,7 @@ __global__ __launch_bounds__(4 * DK) void decode_kernel(DecodeArgs A) {
             float Od = 0.f;
 #pragma unroll
             for (int ww = 0; ww < NW; ++ww) Od += sO[ww * DV + d];
-            const float Ld = sL[d];
+            const float Ld = rs ? sL[d] : 0.f;
             const bool any = m != -INFINITY;
             float cm;
             if (lden > 0.f) cm = any ? fmaxf(m, logf(lden)) : logf(lden);
@@ -453,6 +456,8 @@ __global__ __launch_bounds__(256) void init_kernel(InitArgs A) {
     if (i < nh) A.H[i] = 0.f;
     if (i < ns) A.s[i] = 0.f;
     if (i < nc) A.cache_pos[i] = -1;
+    if (A.cache_score && i < nc) A.cache_score[i] = 0.f;
+    if (A.win_score && i < (int64_t)A.BH * A.eta) A.win_score[i] = 0.f;
 }
 
 }  // namespace
@@ -489,7 +494,8 @@ size_t decode_lds_bytes(int d, int phi_kind, int esz, int lam) {
 
 hipError_t launch_init(const InitArgs& a, hipStream_t stream) {
     const int64_t total = (int64_t)a.BH * a.D * a.d_v;
-    const int64_t mx = total > (int64_t)a.BH * a.lam ? total : (int64_t)a.BH * a.lam;
+    int64_t mx = total > (int64_t)a.BH * a.lam ? total : (int64_t)a.BH * a.lam;
+    if (a.win_score && (int64_t)a.BH * a.eta > mx) mx = (int64_t)a.BH * a.eta;
     const unsigned blocks = (unsigned)((mx + 255) / 256);
     if (blocks == 0) return hipSuccess;
     hipLaunchKernelGGL(init_kernel, dim3(blocks), dim3(256), 0, stream, a);

@@ -371,6 +371,7 @@ __global__ __launch_bounds__(4 * DK) void decode_fast_kernel(DecodeArgs A) {
     // ---------------- exact part of Eq. (14) ----------------
     // exact keys: the window, and the cache after the allocation (the leaving token if it was kept)
     auto cand_exact = [&](int r) -> bool {
+        if (!(A.read_mask & kReadSparse)) return false;   // hidden cache: no exact cache keys
         if (r < lam) return sCpos[r] >= 0 && r != f_row;
         return r == lam && has_e && f_row != lam && lam > 0;
     };
@@ -459,14 +460,15 @@ __global__ __launch_bounds__(4 * DK) void decode_fast_kernel(DecodeArgs A) {
     // ---------------- output, joint normalisation with the common scale exp(-cm) ----------------
     if (tid < DV) {
         const int d = tid;
-        const float lden = sRedF[20];
+        const bool rs = (A.read_mask & kReadState) != 0;   // hidden state: no linear terms
+        const float lden = rs ? sRedF[20] : 0.f;
         float lsum_all = 0.f, Od = 0.f;
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) {
             lsum_all += sRedF[8 + ww];
             Od += sO[ww * DV + d] + sOc[ww * DV + d];
         }
-        const float Ld = sL[d];
+        const float Ld = rs ? sL[d] : 0.f;
         float cm;
         if (lden > 0.f) cm = any ? fmaxf(m, logf(lden)) : logf(lden);
         else cm = m;

@@ -40,8 +40,12 @@ struct WsLayout {
 //   n + lam <= src            : initial window ring slot (src - n - lam) of the state
 // The commit kernel runs last, so the state's initial window and cache stay readable until then.
 
+// Read-branch mask bits (which memories a query reads in Eq. (14)).
+constexpr int kReadState = 1, kReadSparse = 2, kReadWindow = 4, kReadAll = 7;
+
 struct PrefillArgs {
     int BH, n, C, eta, lam, nchunks, nqt;
+    int read_mask;        // kRead* bits; always holds kReadWindow
     int c_begin, c_end;   // chunk range of one chain / read-out launch
     int64_t t0;
     const void* q;
@@ -63,6 +67,7 @@ struct PrefillArgs {
 
 struct DecodeArgs {
     int BH, eta, lam;
+    int read_mask;        // kRead* bits; always holds kReadWindow
     int64_t t;
     const void* q;
     const void* k;
@@ -96,10 +101,12 @@ constexpr int kCollideTokensPerBlock = 256;
 constexpr int kCollideRows = 2;           // map rows per workgroup (their H^T side by side in LDS)
 
 struct InitArgs {
-    int BH, D, d_v, lam;
+    int BH, D, d_v, lam, eta;
     float* H;
     float* s;
     int32_t* cache_pos;
+    float* win_score;     // nullable
+    float* cache_score;   // nullable
 };
 
 // Launchers (return hipSuccess or the launch error).  dtype: 0 = fp32, 1 = bf16.

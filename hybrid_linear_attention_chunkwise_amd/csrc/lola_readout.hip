@@ -104,7 +104,7 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
     const int64_t blo = max((int64_t)0, q0 - eta + 1);
     const int64_t bhi = min(q0 + 63, b - 1);
     const int nb = (eta > 0 && bhi >= blo) ? (int)(bhi - blo + 1) : 0;
-    const int NK = nb + lam;
+    const int NK = nb + ((A.read_mask & kReadSparse) ? lam : 0);   // a hidden cache adds no keys
     const int blo_slot = eta > 0 ? (int)(blo % eta) : 0;    // ring slot of the first band key
     const int nblk = (NK + KB - 1) / KB;
     // key kk -> (position, band?, K row, V row); position -1 = no key.  The chunk's cache list is read
@@ -277,80 +277,83 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
         }
     }
 
-    // linear part, after the exact loop so its registers are not live during it
-    float ph[D / 16][4];
-    phi_tile<T, DK, PHI>(wt, WT_LD, qf, ph);
-    Frag8<T> pf[D / 32];
-#pragma unroll
-    for (int ss = 0; ss < D / 32; ++ss) pf[ss] = frag_from_rows<T>(ph[2 * ss], ph[2 * ss + 1]);
-
-    // linear part: H_c^T phi(Q)^T (snapshot stored in fragment order) and phi(Q) s_c
+    // linear part (skipped when the read mask hides the state: no terms in numerator or denominator)
     f4 L[JT];
 #pragma unroll
     for (int J = 0; J < JT; ++J) L[J] = zero4();
-#pragma unroll
-    for (int ss = 0; ss < D / 32; ++ss)
-#pragma unroll
-        for (int J = 0; J < JT; ++J)
-            mma32(L[J], *reinterpret_cast<const Frag8<T>*>(snapH + ((int64_t)(J * (D / 32) + ss) * 64 + l) * 8), pf[ss]);
     float lden = 0.f;
+    if (A.read_mask & kReadState) {
+        // linear part, after the exact loop so its registers are not live during it
+        float ph[D / 16][4];
+        phi_tile<T, DK, PHI>(wt, WT_LD, qf, ph);
+        Frag8<T> pf[D / 32];
 #pragma unroll
-    for (int ft = 0; ft < D / 16; ++ft)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) lden += ph[ft][r] * sS[16 * ft + 4 * g + r];
-    lden = sum_groups(lden);
+        for (int ss = 0; ss < D / 32; ++ss) pf[ss] = frag_from_rows<T>(ph[2 * ss], ph[2 * ss + 1]);
 
-    // tokens folded by this chunk become linear at tau = max(exit time, chunk start).  fold_group
-    // handles FG groups of 32 folded tokens: every load of the groups (their features and transposed
-    // values) is issued before any of it is used.  The last-range variant takes 64 tokens per round
-    // trip; the bulk variant 32, which keeps its registers within two workgroups per CU.
-    float lden_f = 0.f;
-    auto fold_group = [&](int fb0, auto fgc) {
-        constexpr int FG = decltype(fgc)::value;
-        Frag8<T> af[FG][2][D / 32], vf[FG][JT];
+        // linear part: H_c^T phi(Q)^T (snapshot stored in fragment order) and phi(Q) s_c
 #pragma unroll
-        for (int f2 = 0; f2 < FG; ++f2) {
-            const int fb = fb0 + f2;
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                const int i = 32 * fb + 16 * h2 + c;
-                const T* prow = i < nf ? phiStore + (int64_t)sFoldSrc[i] * D : nullptr;
-#pragma unroll
-                for (int ss = 0; ss < D / 32; ++ss) af[f2][h2][ss] = prow ? load_frag(prow, ss, g) : frag_zero<T>();
-            }
+        for (int ss = 0; ss < D / 32; ++ss)
 #pragma unroll
             for (int J = 0; J < JT; ++J)
-                vf[f2][J] = fb * 32 < nf ? load_frag(foldVT + (int64_t)(16 * J + c) * cpv, fb, g) : frag_zero<T>();
-        }
+                mma32(L[J], *reinterpret_cast<const Frag8<T>*>(snapH + ((int64_t)(J * (D / 32) + ss) * 64 + l) * 8), pf[ss]);
 #pragma unroll
-        for (int f2 = 0; f2 < FG; ++f2) {
-            const int fb = fb0 + f2;
-            f4 sp[2];
+        for (int ft = 0; ft < D / 16; ++ft)
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                sp[h2] = zero4();
+            for (int r = 0; r < 4; ++r) lden += ph[ft][r] * sS[16 * ft + 4 * g + r];
+        lden = sum_groups(lden);
+
+        // tokens folded by this chunk become linear at tau = max(exit time, chunk start).  fold_group
+        // handles FG groups of 32 folded tokens: every load of the groups (their features and transposed
+        // values) is issued before any of it is used.  The last-range variant takes 64 tokens per round
+        // trip; the bulk variant 32, which keeps its registers within two workgroups per CU.
+        float lden_f = 0.f;
+        auto fold_group = [&](int fb0, auto fgc) {
+            constexpr int FG = decltype(fgc)::value;
+            Frag8<T> af[FG][2][D / 32], vf[FG][JT];
 #pragma unroll
-                for (int ss = 0; ss < D / 32; ++ss) mma32(sp[h2], af[f2][h2][ss], pf[ss]);
+            for (int f2 = 0; f2 < FG; ++f2) {
+                const int fb = fb0 + f2;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int ii = 32 * fb + 16 * h2 + 4 * g + r;
-                    bool ok = false;
-                    if (ii < nf) {
-                        const int64_t tau = max((int64_t)sFoldPos[ii] + eta, a);
-                        ok = tau <= tq;
-                    }
-                    sp[h2][r] = ok ? sp[h2][r] : 0.f;
-                    lden_f += sp[h2][r];
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const int i = 32 * fb + 16 * h2 + c;
+                    const T* prow = i < nf ? phiStore + (int64_t)sFoldSrc[i] * D : nullptr;
+#pragma unroll
+                    for (int ss = 0; ss < D / 32; ++ss) af[f2][h2][ss] = prow ? load_frag(prow, ss, g) : frag_zero<T>();
                 }
-            }
-            const Frag8<T> bw = frag_from_acc<T>(sp[0], sp[1]);
 #pragma unroll
-            for (int J = 0; J < JT; ++J) mma32(L[J], vf[f2][J], bw);
-        }
-    };
-    constexpr int FG = NB >= 2 ? 2 : 1;
-    for (int fb0 = 0; fb0 * 32 < nf; fb0 += FG) fold_group(fb0, std::integral_constant<int, FG>{});
-    lden += sum_groups(lden_f);
+                for (int J = 0; J < JT; ++J)
+                    vf[f2][J] = fb * 32 < nf ? load_frag(foldVT + (int64_t)(16 * J + c) * cpv, fb, g) : frag_zero<T>();
+            }
+#pragma unroll
+            for (int f2 = 0; f2 < FG; ++f2) {
+                const int fb = fb0 + f2;
+                f4 sp[2];
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    sp[h2] = zero4();
+#pragma unroll
+                    for (int ss = 0; ss < D / 32; ++ss) mma32(sp[h2], af[f2][h2][ss], pf[ss]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int ii = 32 * fb + 16 * h2 + 4 * g + r;
+                        bool ok = false;
+                        if (ii < nf) {
+                            const int64_t tau = max((int64_t)sFoldPos[ii] + eta, a);
+                            ok = tau <= tq;
+                        }
+                        sp[h2][r] = ok ? sp[h2][r] : 0.f;
+                        lden_f += sp[h2][r];
+                    }
+                }
+                const Frag8<T> bw = frag_from_acc<T>(sp[0], sp[1]);
+#pragma unroll
+                for (int J = 0; J < JT; ++J) mma32(L[J], vf[f2][J], bw);
+            }
+        };
+        constexpr int FG = NB >= 2 ? 2 : 1;
+        for (int fb0 = 0; fb0 * 32 < nf; fb0 += FG) fold_group(fb0, std::integral_constant<int, FG>{});
+        lden += sum_groups(lden_f);
+    }
 
     // joint normalisation with a common scale exp(-cmax), cmax = max(m, log L_den)
     const float lsum = sum_groups(l_part);

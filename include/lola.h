@@ -89,7 +89,41 @@ typedef struct lola_state {
     void *win_k, *win_v;
     void *cache_k, *cache_v;
     int32_t *cache_pos;
+    /* Query-accumulated cache scores (section 4.5, Table 4), used only by the LOLA_SCORE_* rules other
+     * than LOLA_SCORE_SRE and otherwise ignored (may be NULL):
+     *   win_score   [B][n_heads][eta]     fp32  score gathered so far by the window token in each ring slot
+     *   cache_score [B][n_heads][lambda]  fp32  final score of the key in each cache slot
+     * A state keeps one scoring rule for its whole life; lola_state_init zeroes both. */
+    float *win_score;
+    float *cache_score;
 } lola_state;
+
+/* Read-branch masks (section 4.8, Table 12): the memories a query reads in Eq. (14).  Storage and
+ * allocation do not depend on the mask: a hidden memory keeps its keys, its terms just leave both the
+ * numerator and the denominator.  Every mask contains LOLA_READ_WINDOW, the one memory that always
+ * holds the current token. */
+#define LOLA_READ_STATE 1    /* the linear state H, s (with the chunk's newly folded tokens) */
+#define LOLA_READ_SPARSE 2   /* the sparse cache of exact KV */
+#define LOLA_READ_WINDOW 4   /* the sliding window */
+#define LOLA_READ_ALL 7
+
+/* Cache-scoring rules (section 4.5, Table 4).  LOLA_SCORE_SRE ranks the candidates by self-recall error
+ * against the chunk-start state (Eq. (10)).  The others give each key a score accumulated over the
+ * queries whose window holds it, from one query's e = exp(q.k / sqrt(d_k)) and p = phi(q).phi(k):
+ * (e - p)^2, |e - p|, p / e, or e.  An allocation at a chunk start uses what the queries before it have
+ * added; a key's score is fixed once it leaves the window.  Every rule keeps the lambda largest scores,
+ * ties to the older position. */
+#define LOLA_SCORE_SRE 0
+#define LOLA_SCORE_KERNEL_SQ 1
+#define LOLA_SCORE_KERNEL_ABS 2
+#define LOLA_SCORE_RATIO 3
+#define LOLA_SCORE_ATTN 4
+
+typedef struct lola_options {
+    int32_t read_mask;    /* LOLA_READ_* bits, containing LOLA_READ_WINDOW */
+    int32_t score_rule;   /* LOLA_SCORE_* */
+    int32_t reserved[2];  /* must be 0 */
+} lola_options;
 
 /* Bytes of device scratch lola_prefill needs for calls of up to n_max tokens with chunk C, for the
  * state's shape.  Returns 0 if the shape is invalid or unsupported. */
@@ -121,6 +155,14 @@ lola_status lola_prefill_profiled(lola_state *st, const lola_phi *phi, const voi
                                   void *workspace, size_t workspace_bytes, void *stream,
                                   void *const events[5]);
 
+/* lola_prefill with options (NULL = LOLA_READ_ALL and LOLA_SCORE_SRE, which is lola_prefill).
+ * A rule other than LOLA_SCORE_SRE needs the state's win_score and cache_score (16-byte aligned).
+ * LOLA_EINVAL for a mask without the window or with other bits, an unknown rule, non-zero reserved
+ * fields or missing score arrays. */
+lola_status lola_prefill_ex(lola_state *st, const lola_phi *phi, const void *q, const void *k, const void *v,
+                            int64_t n, int32_t C, const lola_options *opt, void *y, int32_t *fold_at,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
 /* One decode token for every sequence and head (section 2.4 single-token update, then Eq. (14)):
  * the token leaving the window (if any) joins the candidates, one candidate is folded when the cache
  * overflows, and y is read out.  q, k: [B][n_heads][d_k], v, y: [B][n_heads][d_v] in the state's
@@ -128,6 +170,13 @@ lola_status lola_prefill_profiled(lola_state *st, const lola_phi *phi, const voi
  * On return st->t has advanced by 1. */
 lola_status lola_decode_step(lola_state *st, const lola_phi *phi, const void *q, const void *k,
                              const void *v, void *y, int32_t *folded_pos, void *stream);
+
+/* lola_decode_step with options (NULL = defaults, which is lola_decode_step).  The read mask applies as
+ * in lola_prefill_ex.  A scoring rule other than LOLA_SCORE_SRE returns LOLA_EUNSUPPORTED here: such
+ * states decode through lola_prefill_ex with n = C = 1 (or several tokens per call), which is the same
+ * single-token update and needs the workspace this entry point does not take. */
+lola_status lola_decode_step_ex(lola_state *st, const lola_phi *phi, const void *q, const void *k, const void *v,
+                                const lola_options *opt, void *y, int32_t *folded_pos, void *stream);
 
 /* SRE collision map of the prefill call that just ran (section 4.4, Fig. 3; relative form Fig. 10 and
  * Eq. (26)): the self-recall error (Eq. (10)) of each of the call's tokens against the linear state at

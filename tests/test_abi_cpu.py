@@ -74,3 +74,31 @@ def test_prefill_validation_without_gpu(lib):
     assert rc == B.LOLA_EINVAL
     rc = lib.lola_state_init(None, None)
     assert rc == B.LOLA_EINVAL
+
+
+def _fake_ptrs(st):
+    """Non-null, 256-byte aligned addresses that validation accepts (nothing reads them: every call
+    below is rejected before any work is queued)."""
+    for i, name in enumerate(("H", "s", "win_k", "win_v", "cache_k", "cache_v", "cache_pos")):
+        setattr(st, name, 0x100000 + 0x1000 * i)
+    return st
+
+
+@pytest.mark.parametrize("mask,rule,reserved", [(0, 0, 0), (B.LOLA_READ_STATE | B.LOLA_READ_SPARSE, 0, 0),
+                                                 (8 | B.LOLA_READ_WINDOW, 0, 0), (B.LOLA_READ_ALL, 5, 0),
+                                                 (B.LOLA_READ_ALL, -1, 0), (B.LOLA_READ_ALL, 0, 1),
+                                                 (B.LOLA_READ_ALL, 1, 0)])
+def test_options_validation_without_gpu(lib, mask, rule, reserved):
+    """Masks without the window or with other bits, unknown rules, non-zero reserved fields, and a
+    query-accumulated rule on a state without score arrays are all rejected up front."""
+    phi = B.LolaPhi(B.LOLA_PHI_SOFTMAX_PM, 128, 128, 0, 0x200000)
+    st = _fake_ptrs(_state())
+    opt = B.LolaOptions(mask, rule, (ctypes.c_int32 * 2)(reserved, 0))
+    p = 0x300000
+    rc = lib.lola_prefill_ex(ctypes.byref(st), ctypes.byref(phi), p, p, p, 16, 16, ctypes.byref(opt), p,
+                             None, 0x400000, 1 << 40, None)
+    assert rc == B.LOLA_EINVAL
+    rc = lib.lola_decode_step_ex(ctypes.byref(st), ctypes.byref(phi), p, p, p, ctypes.byref(opt), p, None,
+                                 None)
+    assert rc == B.LOLA_EINVAL
+    assert st.t == 0

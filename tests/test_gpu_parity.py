@@ -161,9 +161,9 @@ def test_prefill_is_deterministic():
     assert np.array_equal(y1, y2) and np.array_equal(f1, f2)
 
 
-def _decode_check(wl, n0, steps, heads, C0):
+def _decode_check(wl, n0, steps, heads, C0, read_mask=7):
     """Prefill n0 tokens, then `steps` decode tokens; oracle continues from the GPU's post-prefill
-    state and must reproduce every decode output and fold."""
+    state and must reproduce every decode output and fold.  read_mask applies to the decode steps."""
     import hybrid_linear_attention_chunkwise_amd as lola
     from oracle import lola_oracle as O
     W = make_weights(wl)
@@ -177,7 +177,8 @@ def _decode_check(wl, n0, steps, heads, C0):
         fp = torch.full((wl.B, wl.h), -7, dtype=torch.int32, device="cuda")
         y, _ = lola.lola_decode_step(st, phi, torch.from_numpy(dq[s]).cuda().to(tdt),
                                      torch.from_numpy(dk[s]).cuda().to(tdt),
-                                     torch.from_numpy(dv[s]).cuda().to(tdt), folded_pos=fp)
+                                     torch.from_numpy(dv[s]).cuda().to(tdt), folded_pos=fp,
+                                     read_mask=read_mask)
         ys.append(y.float())
         folds.append(fp)
     torch.cuda.synchronize()
@@ -191,7 +192,7 @@ def _decode_check(wl, n0, steps, heads, C0):
                                  snap["win_k"][b, h], snap["win_v"][b, h], snap["cache_k"][b, h],
                                  snap["cache_v"][b, h], snap["cache_pos"][b, h])
         for s in range(steps):
-            y_o, f_o = O.decode_step(so, phi_o, dq[s, b, h], dk[s, b, h], dv[s, b, h])
+            y_o, f_o = O.decode_step(so, phi_o, dq[s, b, h], dk[s, b, h], dv[s, b, h], read_mask=read_mask)
             if f_o != folds[s, b, h]:
                 mism += 1
                 # follow the GPU's choice (near-ties) so later steps stay comparable
@@ -407,3 +408,63 @@ def test_sre_collisions_rejects_bad_arguments():
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     out = lola.lola_sre_collisions(st, vt, fold, 16, ws)   # nothing folded: all zeros
     assert torch.count_nonzero(out).item() == 0
+
+
+# ------------------------------------------------------------------------------------------------
+# Read-branch masks (lola_prefill_ex / lola_decode_step_ex): the query reads only some memories.
+# ------------------------------------------------------------------------------------------------
+
+READ_MASKS = [("window", 4), ("state_window", 5), ("sparse_window", 6)]
+
+
+@pytest.mark.parametrize("mname,mask", READ_MASKS, ids=[m for m, _ in READ_MASKS])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_read_masks_prefill(mname, mask, dtype):
+    """Masked prefill: the allocation is the unmasked one (same fold schedule, bit for bit) and the
+    outputs match the oracle's masked read-out under that schedule."""
+    import hybrid_linear_attention_chunkwise_amd as lola
+    from oracle import lola_oracle as O
+    wl = small_workload(70, B=1, h=2, n=260, C=16, eta=24, lam=20, dtype=dtype)
+    W = make_weights(wl)
+    q, k, v = make_qkv(wl)
+    dev = torch.device("cuda:0")
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    phi = lola.LolaPhi(wl.phi, torch.from_numpy(W).to(dev))
+    qt, kt, vt = (torch.from_numpy(x).to(dev).to(tdt) for x in (q, k, v))
+    res = {}
+    for m in (7, mask):
+        st = lola.LolaState(wl.B, wl.h, wl.d_k, wl.d_v, wl.D, wl.eta, wl.lam, tdt, device=dev)
+        lola.lola_state_init(st)
+        fold = torch.full((wl.B, wl.h, wl.n), -7, dtype=torch.int32, device=dev)
+        y, _ = lola.lola_prefill(st, phi, qt, kt, vt, wl.C, fold_at=fold, read_mask=m)
+        torch.cuda.synchronize()
+        res[m] = (y.float().cpu().numpy(), fold.cpu().numpy(), TL.state_to_host(st))
+    y, fold, host = res[mask]
+    assert np.array_equal(fold, res[7][1]) and np.array_equal(host["cache_pos"], res[7][2]["cache_pos"])
+    phi_o = O.make_phi(wl.phi, W)
+    worst = 0.0
+    for h in range(wl.h):
+        so = O.new_state(wl.d_k, wl.d_v, wl.D, wl.eta, wl.lam)
+        y_o, _ = O.prefill(so, phi_o, q[0, h].astype(np.float64), k[0, h].astype(np.float64),
+                           v[0, h].astype(np.float64), wl.C, fold_at_in=fold[0, h].astype(np.int64), tol=1.0,
+                           read_mask=mask)
+        worst = max(worst, TL.row_rel_err(y[0, h], y_o))
+    print(f"[read mask] prefill {mname} {dtype}: max err {worst:.3e}", flush=True)
+    assert worst <= (TL.FP32_TOL if dtype == "f32" else TL.BF16_TOL)
+
+
+@pytest.mark.parametrize("mname,mask", READ_MASKS, ids=[m for m, _ in READ_MASKS])
+@pytest.mark.parametrize("path", ["register", "general"])
+def test_read_masks_decode(mname, mask, path, monkeypatch):
+    """Masked decode through both bf16 decode kernels, against the oracle from the GPU's state."""
+    if path == "general":
+        monkeypatch.setenv("LOLA_DECODE_GENERAL", "1")
+    else:
+        monkeypatch.delenv("LOLA_DECODE_GENERAL", raising=False)
+    wl = small_workload(71, B=1, h=2, n=0, C=1, eta=24, lam=20, d_k=128, d_v=128, dtype="bf16")
+    _decode_check(wl, n0=72, steps=24, heads=[(0, 0), (0, 1)], C0=16, read_mask=mask)
+
+
+def test_read_mask_decode_f32():
+    wl = small_workload(72, B=1, h=2, n=0, C=1, eta=16, lam=12, d_k=64, d_v=64, dtype="f32")
+    _decode_check(wl, n0=48, steps=30, heads=[(0, 0), (0, 1)], C0=16, read_mask=6)
