@@ -72,7 +72,9 @@ WsLayout make_layout(const lola_state* st, int64_t n, int32_t C) {
     L.c_pad16 = (int32_t)rup(C, 16);
     L.c_pad64 = (int32_t)rup(C, 64);
     int64_t p = 0;
-    L.phi_store = p; p = rup(p + (n + lam + st->eta) * D * esz, 256);
+    L.phi_store = p; p = rup(p + (2 * n + lam + st->eta) * D * esz, 256);
+    L.score_alloc = p; p = rup(p + (n + lam + st->eta) * 4, 256);
+    L.score_full = p;  p = rup(p + (n + lam + st->eta) * 4, 256);
     L.slot_pos = p;  p = rup(p + (lam + 1) * 4, 256);
     L.slot_src = p;  p = rup(p + (lam + 1) * 4, 256);
     L.mir_phi = p;   p = rup(p + rup(lam, 16) * D * esz, 256);
@@ -158,7 +160,6 @@ static lola_status prefill_impl(lola_state* st, const lola_phi* phi, const void*
     if (rc != LOLA_OK) return rc;
     rc = check_options(st, opt);
     if (rc != LOLA_OK) return rc;
-    if (opt && opt->score_rule != LOLA_SCORE_SRE) return LOLA_EUNSUPPORTED;
     rc = check_prefill_config(st, n, C);
     if (rc != LOLA_OK) return rc;
     if (n == 0) return LOLA_OK;
@@ -177,6 +178,9 @@ static lola_status prefill_impl(lola_state* st, const lola_phi* phi, const void*
     a.nchunks = L.nchunks;
     a.nqt = (C + 63) / 64;
     a.read_mask = opt ? opt->read_mask : LOLA_READ_ALL;
+    a.score_rule = opt ? opt->score_rule : LOLA_SCORE_SRE;
+    a.win_score = st->win_score;
+    a.cache_score = st->cache_score;
     a.t0 = st->t;
     a.q = q; a.k = k; a.v = v; a.y = y;
     a.W = phi->W;

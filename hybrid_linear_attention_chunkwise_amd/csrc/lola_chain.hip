@@ -359,7 +359,7 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
         int64_t xl;
         const int nX_ = chunk_x(ch_, xl);
         prefetched = false;
-        if (lam > 0 && nG + nX_ > lam) {
+        if (lam > 0 && nG + nX_ > lam && A.score_rule == kScoreSre) {
             const int nt = (xb + nX_ + 15) / 16;
             if (w < nt) load_tile(cur, w);
             if (PREF && w + NW < nt) load_tile(nxt, w + NW);
@@ -399,62 +399,79 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
             __syncthreads();                                  // every wave's part of the H^T copy
 
             unsigned mn = 0x7F800000u, mx = 0u;
-            if (!prefetched && w < ntile) load_tile(cur, w);
-            for (int j = w; j < ntile; j += NW) {
-                const bool has_next = j + NW < ntile;
-                if (PREF && has_next && !(prefetched && j == w)) load_tile(nxt, j + NW);
-                // the recall in two halves of the value rows (the B fragments stay in registers, each A
-                // fragment is still read once), which halves the accumulators held at a time
-                constexpr int HW = NW >= 8 ? NW / 2 : NW;
-                float den = 0.f;
-#pragma unroll
-                for (int ss = 0; ss < D / 32; ++ss) {
-                    const f4 slo = *reinterpret_cast<const f4*>(sS + 32 * ss + 4 * g);
-                    const f4 shi = *reinterpret_cast<const f4*>(sS + 32 * ss + 16 + 4 * g);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        den += frag_get(cur.f[ss], e) * slo[e] + frag_get(cur.f[ss], 4 + e) * shi[e];
-                }
-                den = sum_groups(den);
-                const float inv = den != 0.f ? __builtin_amdgcn_rcpf(den) : 0.f;   // empty state: recall 0
-                float sq = 0.f;
-#pragma unroll
-                for (int w0 = 0; w0 < NW; w0 += HW) {
-                    f4 rec[HW];
-#pragma unroll
-                    for (int u = 0; u < HW; ++u) rec[u] = zero4();
+            if (A.score_rule == kScoreSre) {
+                if (!prefetched && w < ntile) load_tile(cur, w);
+                for (int j = w; j < ntile; j += NW) {
+                    const bool has_next = j + NW < ntile;
+                    if (PREF && has_next && !(prefetched && j == w)) load_tile(nxt, j + NW);
+                    // the recall in two halves of the value rows (the B fragments stay in registers, each A
+                    // fragment is still read once), which halves the accumulators held at a time
+                    constexpr int HW = NW >= 8 ? NW / 2 : NW;
+                    float den = 0.f;
 #pragma unroll
                     for (int ss = 0; ss < D / 32; ++ss) {
-                        Frag8<T> a[HW];
+                        const f4 slo = *reinterpret_cast<const f4*>(sS + 32 * ss + 4 * g);
+                        const f4 shi = *reinterpret_cast<const f4*>(sS + 32 * ss + 16 + 4 * g);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            den += frag_get(cur.f[ss], e) * slo[e] + frag_get(cur.f[ss], 4 + e) * shi[e];
+                    }
+                    den = sum_groups(den);
+                    const float inv = den != 0.f ? __builtin_amdgcn_rcpf(den) : 0.f;   // empty state: recall 0
+                    float sq = 0.f;
+#pragma unroll
+                    for (int w0 = 0; w0 < NW; w0 += HW) {
+                        f4 rec[HW];
+#pragma unroll
+                        for (int u = 0; u < HW; ++u) rec[u] = zero4();
+#pragma unroll
+                        for (int ss = 0; ss < D / 32; ++ss) {
+                            Frag8<T> a[HW];
+#pragma unroll
+                            for (int u = 0; u < HW; ++u)
+                                a[u] = *reinterpret_cast<const Frag8<T>*>(hcopy + (((w0 + u) * (D / 32) + ss) * 64 + l) * 8);
+#pragma unroll
+                            for (int u = 0; u < HW; ++u) mma32(rec[u], a[u], cur.f[ss]);
+                            __builtin_amdgcn_sched_barrier(0);        // bound the A fragments in flight
+                        }
 #pragma unroll
                         for (int u = 0; u < HW; ++u)
-                            a[u] = *reinterpret_cast<const Frag8<T>*>(hcopy + (((w0 + u) * (D / 32) + ss) * 64 + l) * 8);
 #pragma unroll
-                        for (int u = 0; u < HW; ++u) mma32(rec[u], a[u], cur.f[ss]);
-                        __builtin_amdgcn_sched_barrier(0);        // bound the A fragments in flight
+                            for (int r = 0; r < 4; ++r) {
+                                const float x = rec[u][r] * inv - to_f(cur.v[w0 + u].v[r]);
+                                sq += x * x;
+                            }
                     }
-#pragma unroll
-                    for (int u = 0; u < HW; ++u)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const float x = rec[u][r] * inv - to_f(cur.v[w0 + u].v[r]);
-                            sq += x * x;
-                        }
+                    sq = sum_groups(sq);
+                    const int row = 16 * j + c;
+                    if (row < NR) {
+                        const bool ok = flag[row] != 0;
+                        const float sre = __builtin_amdgcn_sqrtf(sq);
+                        if (g == 0) key[row] = ok ? keep_key(sre, cPos[row]) : 0ull;
+                        if (ok) { mn = min(mn, __float_as_uint(sre)); mx = max(mx, __float_as_uint(sre)); }
+                    }
+                    if (has_next) {
+                        if (PREF) cur = nxt;
+                        else load_tile(cur, j + NW);
+                    }
                 }
-                sq = sum_groups(sq);
-                const int row = 16 * j + c;
-                if (row < NR) {
-                    const bool ok = flag[row] != 0;
-                    const float sre = __builtin_amdgcn_sqrtf(sq);
-                    if (g == 0) key[row] = ok ? keep_key(sre, cPos[row]) : 0ull;
-                    if (ok) { mn = min(mn, __float_as_uint(sre)); mx = max(mx, __float_as_uint(sre)); }
-                }
-                if (has_next) {
-                    if (PREF) cur = nxt;
-                    else load_tile(cur, j + NW);
+            } else {
+                // query-accumulated rule: the scores were computed before the chain; a cache member
+                // has its complete score, a leaving token the one its own allocation sees
+                const float* scAlloc = reinterpret_cast<const float*>(wsb + A.L.score_alloc);
+                const float* scFull = reinterpret_cast<const float*>(wsb + A.L.score_full);
+                for (int r = tid; r < NR; r += NT) {
+                    unsigned long long kk = 0ull;
+                    if (flag[r] != 0) {
+                        const float sc = r < lam ? scFull[cSrc[r]] : scAlloc[cSrc[r]];
+                        kk = keep_key(sc, cPos[r]);
+                        mn = min(mn, __float_as_uint(sc));
+                        mx = max(mx, __float_as_uint(sc));
+                    }
+                    key[r] = kk;
                 }
             }
-            // the SRE range for the histogram
+            // the score range for the histogram
             // (non-negative floats order like their bit patterns)
             mn = __float_as_uint(wave_min(__uint_as_float(mn)));
             mx = __float_as_uint(wave_max(__uint_as_float(mx)));

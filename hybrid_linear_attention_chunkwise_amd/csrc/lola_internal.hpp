@@ -13,7 +13,10 @@ constexpr int kMaxChunk = 128;       // largest prefill chunk
 // (b, h) block; every region starts on a 256-byte boundary.
 struct WsLayout {
     int64_t per_bh;        // bytes per (b, h)
-    int64_t phi_store;     // [n + lam + eta][D] T : phi(k) of every token the call scores, by source index
+    int64_t phi_store;     // [n + lam + eta][D] T : phi(k) of every token the call scores, by source index,
+                           //   then [n][D] T: phi(q) of the call's queries (query-accumulated rules only)
+    int64_t score_alloc;   // [n + lam + eta] fp32: query-accumulated score a candidate has at its allocation
+    int64_t score_full;    // [n + lam + eta] fp32: the same score with every query of the call
     int64_t slot_pos;      // [lam] int32      : final cache table after the call (position, -1 empty)
     int64_t slot_src;      // [lam] int32      : where each final member's K/V come from (see Src below)
     int64_t mir_phi;       // [lam16/16][D/32][64][8] T: features of the cache slots, MFMA operand order
@@ -43,9 +46,13 @@ struct WsLayout {
 // Read-branch mask bits (which memories a query reads in Eq. (14)).
 constexpr int kReadState = 1, kReadSparse = 2, kReadWindow = 4, kReadAll = 7;
 
+// Cache-scoring rules: SRE, or a score accumulated over the queries whose window holds the key.
+constexpr int kScoreSre = 0, kScoreKernelSq = 1, kScoreKernelAbs = 2, kScoreRatio = 3, kScoreAttn = 4;
+
 struct PrefillArgs {
     int BH, n, C, eta, lam, nchunks, nqt;
     int read_mask;        // kRead* bits; always holds kReadWindow
+    int score_rule;       // kScore*
     int c_begin, c_end;   // chunk range of one chain / read-out launch
     int64_t t0;
     const void* q;
@@ -61,6 +68,8 @@ struct PrefillArgs {
     void* cache_v;
     int32_t* cache_pos;
     int32_t* fold_at;     // nullable
+    float* win_score;     // query-accumulated rules: the state's ring and cache scores
+    float* cache_score;
     char* ws;
     WsLayout L;
 };
@@ -113,6 +122,9 @@ struct InitArgs {
 template <typename T, int DK, int PHI>
 hipError_t launch_phi_t(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_init(const InitArgs& a, hipStream_t stream);
+// Query-accumulated scores of the call's keys (after the feature kernel, before the chain).
+template <typename T, int DK>
+hipError_t launch_qscore_t(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int d, int phi_kind, hipStream_t stream,
                           hipEvent_t const* events = nullptr);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int d, int phi_kind, hipStream_t stream);

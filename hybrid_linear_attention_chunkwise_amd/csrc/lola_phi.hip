@@ -2,8 +2,9 @@
 // cache members and the initial window ring (LoLA notes 2.2; the map is fixed per layer).  The
 // features do not depend on the state, so they are computed here in parallel, once, and the serial
 // allocation chain only reads them.  Output row r of phi_store uses the source index of
-// lola_internal.hpp.  One workgroup: kPhiBlocks blocks of 64 rows, four waves of one 16-row MFMA
-// tile each per block.
+// lola_internal.hpp.  Under a query-accumulated scoring rule the call's queries follow, rows
+// n + lam + eta + i = phi(q_i), for the score kernel.  One workgroup: kPhiBlocks blocks of 64 rows,
+// four waves of one 16-row MFMA tile each per block.
 #include "lola_common.hpp"
 #include "lola_internal.hpp"
 
@@ -35,7 +36,7 @@ __global__ __launch_bounds__(256) void phi_kernel(PrefillArgs A) {
     const int bh = blockIdx.y;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c = l & 15;
     const int n = A.n, lam = A.lam, eta = A.eta;
-    const int rows = n + lam + eta;
+    const int rows = n + lam + eta + (A.score_rule != kScoreSre ? n : 0);
     T* out0 = reinterpret_cast<T*>(A.ws + (int64_t)bh * A.L.per_bh + A.L.phi_store);
     // key row of phi_store row r (source index), or nullptr: no key (an empty initial cache slot)
     auto key_row = [&](int r) -> const T* {
@@ -43,7 +44,9 @@ __global__ __launch_bounds__(256) void phi_kernel(PrefillArgs A) {
         if (r < n + lam)
             return A.cache_pos[(int64_t)bh * lam + (r - n)] >= 0
                        ? reinterpret_cast<const T*>(A.cache_k) + ((int64_t)bh * lam + (r - n)) * DK : nullptr;
-        if (r < rows) return reinterpret_cast<const T*>(A.win_k) + ((int64_t)bh * eta + (r - n - lam)) * DK;
+        if (r < n + lam + eta)
+            return reinterpret_cast<const T*>(A.win_k) + ((int64_t)bh * eta + (r - n - lam)) * DK;
+        if (r < rows) return reinterpret_cast<const T*>(A.q) + ((int64_t)bh * n + (r - n - lam - eta)) * DK;
         return nullptr;
     };
     Frag8<T> xf[DK / 32], xn[DK / 32];
@@ -76,7 +79,7 @@ __global__ __launch_bounds__(256) void phi_kernel(PrefillArgs A) {
 
 template <typename T, int DK, int PHI>
 hipError_t launch_phi_t(const PrefillArgs& a, hipStream_t stream) {
-    const int rows = a.n + a.lam + a.eta;
+    const int rows = a.n + a.lam + a.eta + (a.score_rule != kScoreSre ? a.n : 0);
     dim3 grid((rows + 64 * kPhiBlocks - 1) / (64 * kPhiBlocks), a.BH);
     hipLaunchKernelGGL((phi_kernel<T, DK, PHI>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();

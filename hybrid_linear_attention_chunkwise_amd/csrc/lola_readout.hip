@@ -445,6 +445,27 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kernel(PrefillArgs A) {
                 if (dst[u]) *reinterpret_cast<uint4*>(dst[u]) = val[u];
         }
     }
+    if (A.score_rule != kScoreSre) {
+        // query-accumulated scores: each final cache member's, and each window token's so far (the
+        // window at the end of the call, old ring tokens included when the call is shorter than eta)
+        const char* wsb = A.ws + (int64_t)bh * A.L.per_bh;
+        const float* scFull = reinterpret_cast<const float*>(wsb + A.L.score_full);
+        if (lam > 0) {
+            const int* fs = reinterpret_cast<const int*>(wsb + A.L.slot_src);
+            for (int j = tid; j < lam; j += NTH) {
+                const int src = fs[j];
+                A.cache_score[(int64_t)bh * lam + j] = src >= 0 ? scFull[src] : 0.f;
+            }
+        }
+        if (eta > 0) {
+            const int64_t plo = max((int64_t)0, t0 + n - eta);
+            for (int64_t pos = plo + tid; pos < t0 + n; pos += NTH) {
+                const int slot = (int)(pos % eta);
+                const int src = pos >= t0 ? (int)(pos - t0) : n + lam + slot;
+                A.win_score[(int64_t)bh * eta + slot] = scFull[src];
+            }
+        }
+    }
 }
 
 template <typename T, int DK>
@@ -565,6 +586,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a0, hipStream_t stream, hipEvent_
         a.c_begin = 0;
         a.c_end = a.nchunks;
         if ((e = launch_phi_t<T, DK, PHI>(a, stream)) != hipSuccess) return e;
+        if (a.score_rule != kScoreSre && (e = launch_qscore_t<T, DK>(a, stream)) != hipSuccess) return e;
         if ((e = record(ev, 1, stream)) != hipSuccess) return e;
         if ((e = launch_chain_range<T, DK, PHI>(a, 0, a.nchunks, stream)) != hipSuccess) return e;
         if ((e = record(ev, 2, stream)) != hipSuccess) return e;
@@ -581,6 +603,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a0, hipStream_t stream, hipEvent_
     int bounds[kMaxSegments + 1];
     const int nseg = split_chunks(a.nchunks, a.BH * a.nqt, device_cus(), bounds, kMaxSegments);
     if ((e = launch_phi_t<T, DK, PHI>(a, stream)) != hipSuccess) return e;
+    if (a.score_rule != kScoreSre && (e = launch_qscore_t<T, DK>(a, stream)) != hipSuccess) return e;
     for (int i = 0; i < nseg; ++i) {
         if ((e = launch_chain_range<T, DK, PHI>(a, bounds[i], bounds[i + 1], stream)) != hipSuccess) return e;
         if ((e = hipEventRecord(side->seg[i], stream)) != hipSuccess) return e;

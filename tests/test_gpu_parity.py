@@ -468,3 +468,118 @@ def test_read_masks_decode(mname, mask, path, monkeypatch):
 def test_read_mask_decode_f32():
     wl = small_workload(72, B=1, h=2, n=0, C=1, eta=16, lam=12, d_k=64, d_v=64, dtype="f32")
     _decode_check(wl, n0=48, steps=30, heads=[(0, 0), (0, 1)], C0=16, read_mask=6)
+
+
+# ------------------------------------------------------------------------------------------------
+# Query-accumulated cache-scoring rules (lola_prefill_ex with lola_options.score_rule).
+# ------------------------------------------------------------------------------------------------
+
+SCORE_RULES = ["kernel_sq", "kernel_abs", "ratio", "attn"]
+# fp32 validity tolerance of a schedule under these rules: a score is a sum of up to eta terms, each
+# with an exponential good to a few ulp, summed in fp32 in another order than the oracle's fp64.
+QSCORE_FP32_TOL = 1e-4
+
+
+def _score_rule_check(wl, rule, heads, calls=None):
+    """GPU prefill (one call, or consecutive calls of the given lengths) under a scoring rule against
+    the oracle's single call: identical schedule, or (near-ties) a schedule the oracle validates with
+    the tolerance of the dtype, then outputs and the carried scores."""
+    import hybrid_linear_attention_chunkwise_amd as lola
+    from oracle import lola_oracle as O
+    W = make_weights(wl)
+    q, k, v = make_qkv(wl)
+    dev = torch.device("cuda:0")
+    tdt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+    phi = lola.LolaPhi(wl.phi, torch.from_numpy(W).to(dev))
+    st = lola.LolaState(wl.B, wl.h, wl.d_k, wl.d_v, wl.D, wl.eta, wl.lam, tdt, device=dev)
+    lola.lola_state_init(st)
+    ys, folds, call_chunks = [], [], np.full(wl.n, -1, dtype=np.int64)
+    start = 0
+    for ln in (calls or [wl.n]):
+        call_chunks[start:start + ln] = start // wl.C   # first chunk id of the call holding the token
+        sl = slice(start, start + ln)
+        qt, kt, vt = (torch.from_numpy(np.ascontiguousarray(x[:, :, sl])).to(dev).to(tdt) for x in (q, k, v))
+        fold = torch.full((wl.B, wl.h, ln), -7, dtype=torch.int32, device=dev)
+        y, _ = lola.lola_prefill(st, phi, qt, kt, vt, wl.C, fold_at=fold, score_rule=rule)
+        ys.append(y.float())
+        f = fold.clone()
+        c_lo = start // wl.C
+        f[f >= 0] += c_lo                                  # call-local chunk ids -> whole-sequence ids
+        folds.append(f)
+        start += ln
+    torch.cuda.synchronize()
+    y = torch.cat(ys, dim=2).cpu().numpy()
+    fold = torch.cat(folds, dim=2).cpu().numpy()
+    host = TL.state_to_host(st)
+    win_score = st.win_score.cpu().numpy()
+    cache_score = st.cache_score.cpu().numpy()
+    phi_o = O.make_phi(wl.phi, W)
+    out_tol = TL.FP32_TOL if wl.dtype == "f32" else TL.BF16_TOL
+    sched_tol = QSCORE_FP32_TOL if wl.dtype == "f32" else TL.BF16_TOL
+    worst, differing = 0.0, 0
+    for (b, h) in heads:
+        args = (phi_o, q[b, h].astype(np.float64), k[b, h].astype(np.float64), v[b, h].astype(np.float64), wl.C)
+        so = O.new_state(wl.d_k, wl.d_v, wl.D, wl.eta, wl.lam)
+        y_o, sched = O.prefill(so, *args, score_rule=rule)
+        if calls is not None:
+            # a call reports only its own tokens' folds, and only those it made itself
+            ends = np.cumsum(calls)
+            call_end_chunk = np.array([(ends[np.searchsorted(ends, i, side="right")] + wl.C - 1) // wl.C
+                                       for i in range(wl.n)])
+            own = (sched.fold_at >= call_chunks) & (sched.fold_at < call_end_chunk)
+            exp = np.where(own, sched.fold_at, -1)
+            assert np.array_equal(fold[b, h], exp), f"head ({b},{h}): per-call fold schedule differs"
+        elif not np.array_equal(fold[b, h], sched.fold_at):
+            differing += 1
+            so = O.new_state(wl.d_k, wl.d_v, wl.D, wl.eta, wl.lam)
+            y_o, sched = O.prefill(so, *args, fold_at_in=fold[b, h].astype(np.int64), tol=sched_tol,
+                                   score_rule=rule)
+            assert not sched.problems, f"head ({b},{h}): invalid GPU schedule {sched.problems[:3]}"
+        worst = max(worst, TL.row_rel_err(y[b, h], y_o))
+        assert TL.cache_members(host["cache_pos"][b, h]) == sorted(so.cache)
+        # carried scores: cache slots and window ring, relative to the largest score held
+        ref_c = np.array([so.score[p] if p >= 0 else 0.0 for p in host["cache_pos"][b, h][:wl.lam]])
+        t_end = wl.n
+        ring = [p for p in range(max(0, t_end - wl.eta), t_end)]
+        ref_w = np.zeros(max(wl.eta, 1))
+        for p in ring:
+            ref_w[p % wl.eta] = so.score[p]
+        scale = max(1e-30, float(np.abs(ref_c).max(initial=0.0)), float(np.abs(ref_w).max(initial=0.0)))
+        if wl.lam > 0:
+            assert np.abs(cache_score[b, h][:wl.lam] - ref_c).max() <= sched_tol * scale
+        if wl.eta > 0:
+            got_w = np.array([win_score[b, h][p % wl.eta] for p in ring])
+            assert np.abs(got_w - np.array([so.score[p] for p in ring])).max() <= sched_tol * scale
+    print(f"[score rule] {rule} {wl.dtype} calls={calls}: max err {worst:.3e}, heads with a different "
+          f"schedule {differing}/{len(heads)}", flush=True)
+    assert worst <= out_tol
+
+
+@pytest.mark.parametrize("rule", SCORE_RULES)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_score_rules_prefill(rule, dtype):
+    wl = small_workload(80, B=1, h=2, n=260, C=16, eta=24, lam=20, dtype=dtype)
+    _score_rule_check(wl, rule, [(0, 0), (0, 1)])
+
+
+@pytest.mark.parametrize("rule", ["kernel_abs", "attn"])
+def test_score_rules_d128_and_continuation(rule):
+    """d = 128, and the scores carried across call boundaries (window partial sums, cache finals)."""
+    wl = small_workload(81, B=1, h=2, n=300, C=32, eta=40, lam=24, d_k=128, d_v=128, dtype="f32")
+    _score_rule_check(wl, rule, [(0, 0), (0, 1)])
+    _score_rule_check(wl, rule, [(0, 0), (0, 1)], calls=[64, 96, 140])
+
+
+def test_score_rule_multi_token_decode():
+    """Decode under a query-accumulated rule goes through lola_prefill_ex (calls of 1, then of 4
+    tokens, C = 1) and equals the oracle's single call; lola_decode_step_ex rejects the rule."""
+    import hybrid_linear_attention_chunkwise_amd as lola
+    wl = small_workload(82, B=1, h=2, n=96, C=1, eta=12, lam=8, dtype="f32")
+    _score_rule_check(wl, "kernel_sq", [(0, 0), (0, 1)], calls=[1] * 32 + [4] * 16)
+    st = lola.LolaState(1, 1, 64, 64, 128, 12, 8, torch.float32)
+    lola.lola_state_init(st)
+    phi = lola.LolaPhi("softmax_pm", torch.zeros(64, 64).cuda())
+    x = torch.zeros(1, 1, 64, device="cuda")
+    with pytest.raises(lola.LolaError) as e:
+        lola.lola_decode_step(st, phi, x, x, x, score_rule="attn")
+    assert e.value.code == lola.LOLA_EUNSUPPORTED
