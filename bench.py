@@ -173,6 +173,42 @@ def bench_collisions(args, lola, torch, wl):
                          "algorithmic_flop_per_launch": flop}}
 
 
+def bench_options(args, lola, torch, wl):
+    """Whole-step prefill time of the workload under other lola_options: each query-accumulated
+    scoring rule (score kernel + chain ranking by the sums) and the read masks (window only; window
+    and cache).  Same step as the headline: state init + one prefill call, K back-to-back steps."""
+    from workloads import make_qkv, make_weights
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    W = make_weights(wl)
+    q, k, v = make_qkv(wl)
+    qt, kt, vt = (torch.from_numpy(x).to(dev).to(tdt) for x in (q, k, v))
+    st = lola.LolaState(wl.B, wl.h, wl.d_k, wl.d_v, wl.D, wl.eta, wl.lam, tdt, device=dev)
+    phi = lola.LolaPhi(wl.phi, torch.from_numpy(W).to(dev), wl.D)
+    y = torch.empty_like(vt)
+    ws = torch.empty(lola.lola_workspace_bytes(st, wl.n, wl.C), dtype=torch.uint8, device=dev)
+    out = {}
+    cases = [(r, lola.LOLA_READ_ALL) for r in ("kernel_sq", "kernel_abs", "ratio", "attn")]
+    cases += [("sre", lola.LOLA_READ_WINDOW), ("sre", lola.LOLA_READ_WINDOW | lola.LOLA_READ_SPARSE)]
+    for rule, mask in cases:
+        def step():
+            lola.lola_state_init(st)
+            lola.lola_prefill(st, phi, qt, kt, vt, wl.C, y=y, workspace=ws, read_mask=mask, score_rule=rule)
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / args.steps * 1e3
+        name = rule if mask == lola.LOLA_READ_ALL else ("read_window" if mask == lola.LOLA_READ_WINDOW
+                                                         else "read_window_cache")
+        out[name] = {"ms_per_step": round(ms, 4), "tokens_per_s": round(wl.B * wl.n / (ms * 1e-3), 1)}
+    log(f"options: {out}")
+    return out
+
+
 def bench_decode(args, lola, torch, wl):
     from workloads import make_decode_tokens_device, make_qkv_device, make_weights
     dev = torch.device("cuda:0")
@@ -284,6 +320,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-collisions", action="store_true")
+    ap.add_argument("--no-options", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -354,6 +391,8 @@ def main() -> int:
                          "multi_token": multi}
     if not args.no_collisions:
         out["collision_map"] = bench_collisions(args, lola, torch, wl)
+    if not args.no_options:
+        out["options"] = bench_options(args, lola, torch, wl)
     if not args.no_cpu_baseline:
         log("cpu baseline: running the oracle ...")
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_heads)

@@ -141,7 +141,9 @@ struct Sources {
     __device__ __forceinline__ const T* phi_row(int src) const { return phi + (int64_t)src * kFeat; }
 };
 
-template <typename T, int DK, int PHI>
+// QS: the candidates are ranked by query-accumulated scores computed before the chain (a separate
+// instantiation, so the SRE path is compiled exactly as it would be without the option).
+template <typename T, int DK, int PHI, bool QS>
 __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
     using Cfg = ChainCfg<T, DK, PHI>;
     constexpr int D = Cfg::D, DV = Cfg::DV, NW = Cfg::NW, NT = Cfg::NT, IT = Cfg::IT, EPV = Cfg::EPV,
@@ -359,7 +361,7 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
         int64_t xl;
         const int nX_ = chunk_x(ch_, xl);
         prefetched = false;
-        if (lam > 0 && nG + nX_ > lam && A.score_rule == kScoreSre) {
+        if (!QS && lam > 0 && nG + nX_ > lam) {
             const int nt = (xb + nX_ + 15) / 16;
             if (w < nt) load_tile(cur, w);
             if (PREF && w + NW < nt) load_tile(nxt, w + NW);
@@ -399,7 +401,7 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
             __syncthreads();                                  // every wave's part of the H^T copy
 
             unsigned mn = 0x7F800000u, mx = 0u;
-            if (A.score_rule == kScoreSre) {
+            if constexpr (!QS) {
                 if (!prefetched && w < ntile) load_tile(cur, w);
                 for (int j = w; j < ntile; j += NW) {
                     const bool has_next = j + NW < ntile;
@@ -484,9 +486,14 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
             for (int ww = 0; ww < NW; ++ww) { umn = min(umn, (unsigned)tmp[8 + ww]); umx = max(umx, (unsigned)tmp[16 + ww]); }
             const float smin = __uint_as_float(umn), smax = __uint_as_float(umx);
             const float bscale = smax > smin ? (float)NBIN / (smax - smin) : 0.f;
+            // Query-accumulated scores span decades (they hold exponentials), so their bins split the
+            // range of the bit patterns, a logarithmic scale; SRE values use linear bins.
+            constexpr bool logbins = QS;
+            const float lscale = (float)NBIN / ((float)(umx - umn) + 1.f);
             auto bin_of = [&](unsigned long long k) -> int {
-                const float x = __uint_as_float((unsigned)(k >> 32));
-                return min(NBIN - 1, (int)((x - smin) * bscale));   // monotone in the key
+                const unsigned b = (unsigned)(k >> 32);
+                if (logbins) return min(NBIN - 1, (int)((float)(b - umn) * lscale));
+                return min(NBIN - 1, (int)((__uint_as_float(b) - smin) * bscale));   // monotone in the key
             };
             for (int r = tid; r < NR; r += NT)
                 if (flag[r]) atomicAdd(&hist[bin_of(key[r])], 1);
@@ -724,7 +731,7 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
 template <typename T, int DK, int PHI>
 hipError_t launch_chain_t(const PrefillArgs& a, hipStream_t stream) {
     constexpr size_t lds = chain_lds<T, DK, PHI>().total;
-    auto kern = chain_kernel<T, DK, PHI>;
+    auto kern = a.score_rule != kScoreSre ? chain_kernel<T, DK, PHI, true> : chain_kernel<T, DK, PHI, false>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;

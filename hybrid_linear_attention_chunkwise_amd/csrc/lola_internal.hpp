@@ -15,8 +15,6 @@ struct WsLayout {
     int64_t per_bh;        // bytes per (b, h)
     int64_t phi_store;     // [n + lam + eta][D] T : phi(k) of every token the call scores, by source index,
                            //   then [n][D] T: phi(q) of the call's queries (query-accumulated rules only)
-    int64_t score_alloc;   // [n + lam + eta] fp32: query-accumulated score a candidate has at its allocation
-    int64_t score_full;    // [n + lam + eta] fp32: the same score with every query of the call
     int64_t slot_pos;      // [lam] int32      : final cache table after the call (position, -1 empty)
     int64_t slot_src;      // [lam] int32      : where each final member's K/V come from (see Src below)
     int64_t mir_phi;       // [lam16/16][D/32][64][8] T: features of the cache slots, MFMA operand order
@@ -35,6 +33,8 @@ struct WsLayout {
     int32_t c_pad16;
     int32_t c_pad64;
     int32_t nchunks;
+    int64_t score_alloc;   // [n + lam + eta] fp32: query-accumulated score a candidate has at its allocation
+    int64_t score_full;    // [n + lam + eta] fp32: the same score with every query of the call
 };
 
 // A source index names where a token's K/V live during a prefill call:
@@ -51,8 +51,6 @@ constexpr int kScoreSre = 0, kScoreKernelSq = 1, kScoreKernelAbs = 2, kScoreRati
 
 struct PrefillArgs {
     int BH, n, C, eta, lam, nchunks, nqt;
-    int read_mask;        // kRead* bits; always holds kReadWindow
-    int score_rule;       // kScore*
     int c_begin, c_end;   // chunk range of one chain / read-out launch
     int64_t t0;
     const void* q;
@@ -68,10 +66,13 @@ struct PrefillArgs {
     void* cache_v;
     int32_t* cache_pos;
     int32_t* fold_at;     // nullable
-    float* win_score;     // query-accumulated rules: the state's ring and cache scores
-    float* cache_score;
     char* ws;
     WsLayout L;
+    // options (kept after the fields above: the chain kernel's code is sensitive to their layout)
+    int read_mask;        // kRead* bits; always holds kReadWindow
+    int score_rule;       // kScore*
+    float* win_score;     // query-accumulated rules: the state's ring and cache scores
+    float* cache_score;
 };
 
 struct DecodeArgs {
