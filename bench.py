@@ -170,6 +170,7 @@ def bench_collisions(args, lola, torch, wl):
             "entries_in_state": entries, "entries_total": wl.B * wl.h * R * wl.n,
             "roofline": {"bound": "mfma", "achieved": round(ach, 3), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 5),
+                         "traffic": load_traffic("collide", kernel_source_hash()),
                          "algorithmic_flop_per_launch": flop}}
 
 
