@@ -28,7 +28,7 @@ PEAK_HBM_GBS = 8000.0
 MULTI_TOKEN_C = 16          # tokens per call in the multi-token decode measurement
 KERNEL_SOURCES = ("lola_common.hpp", "lola_phi.hip", "lola_chain.hip", "lola_readout.hip", "lola_decode.hip",
                   "lola_decode_fast.hip", "lola_collide.hip",
-                  "lola_qscore.hip")
+                  "lola_qscore.hip", "lola_hola.hip")
 
 
 def log(msg: str) -> None:

@@ -19,7 +19,7 @@ from ._binding import (LOLA_BF16, LOLA_EDEVICE, LOLA_EINVAL, LOLA_EUNSUPPORTED, 
 __all__ = ["LolaState", "LolaPhi", "lola_state_init", "lola_workspace_bytes", "lola_prefill",
            "lola_decode_step", "lola_sre_collisions", "LolaError", "LOLA_OK", "LOLA_EINVAL", "LOLA_EUNSUPPORTED",
            "LOLA_EDEVICE", "library_path", "PHI_KINDS", "LOLA_READ_STATE", "LOLA_READ_SPARSE",
-           "LOLA_READ_WINDOW", "LOLA_READ_ALL", "SCORE_RULES"]
+           "LOLA_READ_WINDOW", "LOLA_READ_ALL", "SCORE_RULES", "hola_workspace_bytes", "hola_prefill"]
 
 PHI_KINDS = {"elu1": LOLA_PHI_ELU1, "softmax_pm": LOLA_PHI_SOFTMAX_PM}
 _DTYPES = {torch.float32: LOLA_F32, torch.bfloat16: LOLA_BF16}
@@ -173,3 +173,27 @@ def lola_sre_collisions(state: LolaState, v: torch.Tensor, fold_at: torch.Tensor
                                          _ptr(out), _stream(stream))
     _b.check("lola_sre_collisions", code)
     return out
+
+
+def hola_workspace_bytes(B: int, n_heads: int, d: int, dtype: torch.dtype, n: int, C: int) -> int:
+    return int(_b.load().hola_workspace_bytes(B, n_heads, d, _DTYPES[dtype], n, C))
+
+
+def hola_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor,
+                 gamma_q: torch.Tensor, gamma_k: torch.Tensor, sink: torch.Tensor, gate: torch.Tensor,
+                 C: int, w: int, y: Optional[torch.Tensor] = None, S_out: Optional[torch.Tensor] = None,
+                 cache_pos: Optional[torch.Tensor] = None, cache_score: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """HOLA layer call (include/lola.h) on q, k, v [B][h][n][d]; returns y.  Asynchronous on `stream`."""
+    B, h, n, d = q.shape
+    if y is None:
+        y = torch.empty_like(v)
+    need = hola_workspace_bytes(B, h, d, q.dtype, n, C)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    code = _b.load().hola_prefill(B, h, d, _DTYPES[q.dtype], n, C, w, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                  _ptr(beta), _ptr(gamma_q), _ptr(gamma_k), _ptr(sink), _ptr(gate), _ptr(y),
+                                  _ptr(S_out), _ptr(cache_pos), _ptr(cache_score), _ptr(workspace),
+                                  workspace.numel(), _stream(stream))
+    _b.check("hola_prefill", code)
+    return y

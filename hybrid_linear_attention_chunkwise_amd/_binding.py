@@ -23,7 +23,7 @@ LOLA_PHI_SOFTMAX_PM = 1
 
 EXPORTED = ("lola_workspace_bytes", "lola_state_init", "lola_prefill", "lola_prefill_ex",
             "lola_prefill_profiled", "lola_decode_step", "lola_decode_step_ex", "lola_sre_collisions",
-            "lola_status_string")
+            "lola_status_string", "hola_workspace_bytes", "hola_prefill")
 LOLA_READ_STATE = 1
 LOLA_READ_SPARSE = 2
 LOLA_READ_WINDOW = 4
@@ -89,6 +89,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lola_decode_step_ex.restype = i32
     lib.lola_sre_collisions.argtypes = [sp, vp, vp, i64, i32, vp, sz, i32, vp, vp]
     lib.lola_sre_collisions.restype = i32
+    lib.hola_workspace_bytes.argtypes = [i32, i32, i32, i32, i64, i32]
+    lib.hola_workspace_bytes.restype = sz
+    lib.hola_prefill.argtypes = [i32, i32, i32, i32, i64, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                 vp, vp, vp, vp, sz, vp]
+    lib.hola_prefill.restype = i32
     lib.lola_status_string.argtypes = [i32]
     lib.lola_status_string.restype = ctypes.c_char_p
     _lib = lib

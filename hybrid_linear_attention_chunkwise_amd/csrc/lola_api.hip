@@ -108,6 +108,30 @@ lola_status check_prefill_config(const lola_state* st, int64_t n, int32_t C) {
 
 }  // namespace
 
+static lola::HolaLayout hola_layout(int64_t BH, int64_t d, int64_t esz, int64_t n, int64_t nchunks) {
+    lola::HolaLayout L;
+    int64_t p = 0;
+    const int64_t rows = BH * n;
+    L.qhat = p; p = rup(p + rows * d * 4, 256);
+    L.khat = p; p = rup(p + rows * d * 4, 256);
+    L.qtil = p; p = rup(p + rows * d * esz, 256);
+    L.ktil = p; p = rup(p + rows * d * esz, 256);
+    L.o = p;    p = rup(p + rows * d * 4, 256);
+    L.e = p;    p = rup(p + rows * d * 4, 256);
+    L.m = p;    p = rup(p + rows * 4, 256);
+    L.clist = p; p = rup(p + BH * nchunks * lola::kHolaMaxW * 4, 256);
+    L.total = p;
+    return L;
+}
+
+static lola_status hola_check(int32_t B, int32_t n_heads, int32_t d, int32_t dtype, int64_t n, int32_t C) {
+    if (B <= 0 || n_heads <= 0 || n < 0 || C < 1) return LOLA_EINVAL;
+    if (dtype != LOLA_F32 && dtype != LOLA_BF16) return LOLA_EINVAL;
+    if (d != 64 && d != 128) return LOLA_EUNSUPPORTED;
+    if (C > lola::kHolaMaxC || n > INT_MAX / 2 || (int64_t)B * n_heads > INT_MAX / 2) return LOLA_EUNSUPPORTED;
+    return LOLA_OK;
+}
+
 extern "C" {
 
 const char* lola_status_string(lola_status status) {
@@ -268,6 +292,54 @@ lola_status lola_decode_step(lola_state* st, const lola_phi* phi, const void* q,
 lola_status lola_decode_step_ex(lola_state* st, const lola_phi* phi, const void* q, const void* k, const void* v,
                                 const lola_options* opt, void* y, int32_t* folded_pos, void* stream) {
     return decode_impl(st, phi, q, k, v, opt, y, folded_pos, stream);
+}
+
+size_t hola_workspace_bytes(int32_t B, int32_t n_heads, int32_t d, int32_t dtype, int64_t n, int32_t C) {
+    if (hola_check(B, n_heads, d, dtype, n, C) != LOLA_OK) return 0;
+    if (n == 0) return 256;
+    const int64_t nchunks = (n + C - 1) / C;
+    return (size_t)hola_layout((int64_t)B * n_heads, d, dtype == LOLA_BF16 ? 2 : 4, n, nchunks).total;
+}
+
+lola_status hola_prefill(int32_t B, int32_t n_heads, int32_t d, int32_t dtype, int64_t n, int32_t C, int32_t w,
+                         const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                         const float* gamma_q, const float* gamma_k, const float* sink, const float* gate,
+                         void* y, float* S_out, int32_t* cache_pos_out, float* cache_score_out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    lola_status rc = hola_check(B, n_heads, d, dtype, n, C);
+    if (rc != LOLA_OK) return rc;
+    if (w < 0) return LOLA_EINVAL;
+    if (w > lola::kHolaMaxW) return LOLA_EUNSUPPORTED;
+    if (n == 0) return LOLA_OK;
+    if (!q || !k || !v || !y || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y)) return LOLA_EINVAL;
+    if (!alpha || !beta || !gamma_q || !gamma_k || !sink || !gate) return LOLA_EINVAL;
+    const int64_t nchunks = (n + C - 1) / C;
+    const int64_t BH = (int64_t)B * n_heads;
+    const int nqt = (C + 63) / 64;
+    if (BH * nchunks * nqt > (int64_t)INT_MAX) return LOLA_EUNSUPPORTED;
+    const lola::HolaLayout L = hola_layout(BH, d, dtype == LOLA_BF16 ? 2 : 4, n, nchunks);
+    if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes < (size_t)L.total) return LOLA_EINVAL;
+    lola::HolaArgs a;
+    a.BH = (int)BH;
+    a.heads = n_heads;
+    a.n = (int)n;
+    a.C = C;
+    a.w = w;
+    a.nchunks = (int)nchunks;
+    a.nqt = nqt;
+    a.q = q; a.k = k; a.v = v;
+    a.alpha = alpha; a.beta = beta;
+    a.gamma_q = gamma_q; a.gamma_k = gamma_k;
+    a.sink = sink; a.gate = gate;
+    a.y = y;
+    a.S_out = S_out;
+    a.cache_pos_out = w > 0 ? cache_pos_out : nullptr;
+    a.cache_score_out = w > 0 ? cache_score_out : nullptr;
+    a.ws = reinterpret_cast<char*>(workspace);
+    a.L = L;
+    if (lola::launch_hola(a, dtype, d, (hipStream_t)stream) != hipSuccess) return LOLA_EDEVICE;
+    if (getenv("LOLA_DEBUG_SYNC") && hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return LOLA_EDEVICE;
+    return LOLA_OK;
 }
 
 lola_status lola_sre_collisions(const lola_state* st, const void* v, const int32_t* fold_at, int64_t n,

@@ -110,6 +110,37 @@ struct CollideArgs {
 constexpr int kCollideTokensPerBlock = 256;
 constexpr int kCollideRows = 2;           // map rows per workgroup (their H^T side by side in LDS)
 
+// HOLA variant: a gated delta-rule state plus an exact cache chosen by write magnitude.
+constexpr int kHolaMaxW = 64;     // largest persistent cache
+constexpr int kHolaMaxC = 1024;   // largest chunk
+struct HolaLayout {               // byte offsets of whole arrays in the workspace
+    int64_t qhat, khat;           // [BH][n][d] fp32: unit-norm queries and keys of the state path
+    int64_t qtil, ktil;           // [BH][n][d] T   : RMS-normalised, gamma-scaled queries and keys
+    int64_t o, e;                 // [BH][n][d] fp32: state read-out S_t^T q_t, residual e_t
+    int64_t m;                    // [BH][n]    fp32: write magnitude beta_t ||e_t||
+    int64_t clist;                // [BH][nchunks][kHolaMaxW] int32: persistent cache at each chunk start
+    int64_t total;
+};
+struct HolaArgs {
+    int BH, heads, n, C, w, nchunks, nqt;
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* alpha;           // [BH][n]
+    const float* beta;            // [BH][n]
+    const float* gamma_q;         // [heads][d]
+    const float* gamma_k;         // [heads][d]
+    const float* sink;            // [heads]
+    const float* gate;            // [heads]
+    void* y;
+    float* S_out;                 // nullable [BH][d][d]
+    int32_t* cache_pos_out;       // nullable [BH][w]
+    float* cache_score_out;       // nullable [BH][w]
+    char* ws;
+    HolaLayout L;
+};
+hipError_t launch_hola(const HolaArgs& a, int dtype, int d, hipStream_t stream);
+
 struct InitArgs {
     int BH, D, d_v, lam, eta;
     float* H;

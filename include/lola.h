@@ -198,6 +198,37 @@ lola_status lola_sre_collisions(const lola_state *st, const void *v, const int32
                                 int32_t C, const void *workspace, size_t workspace_bytes, int32_t relative,
                                 float *out, void *stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * HOLA variant (the HOLA reading notes, cc.laoqi.cc paper 2607.02303 v1, part 2 "Method"): a gated
+ * delta-rule state (3.1 Eq. (1), 3.5) plus an exact KV cache chosen by write magnitude (3.3 Eqs. (5)-(6)),
+ * read through RMS-normalised queries and keys (3.4 Eq. (7)).  For each sequence and head, from an empty
+ * memory:
+ *   e_t = v_t - alpha_t S_{t-1}^T k^_t,   S_t = alpha_t S_{t-1} + beta_t k^_t e_t^T,   o_t = S_t^T q^_t
+ * with k^, q^ the unit-L2-norm key and query; m_t = beta_t ||e_t||_2.  The persistent cache at the start
+ * of chunk c (chunks of C tokens) holds the w positions of earlier chunks with the largest m (ties: the
+ * older).  Query t of chunk c reads by softmax over that cache, the chunk's tokens up to t, and a null
+ * sink (logit sink[h], value 0), with logits (gamma_q*q/rms(q)).(gamma_k*k/rms(k)) / sqrt(d),
+ * rms(x) = sqrt(mean(x^2) + 1e-6).  y_t = o_t + sigmoid(gate[h]) * that read-out.
+ * --------------------------------------------------------------------------------------------- */
+
+/* Bytes of device scratch hola_prefill needs (0 if the arguments are invalid or unsupported). */
+size_t hola_workspace_bytes(int32_t B, int32_t n_heads, int32_t d, int32_t dtype, int64_t n, int32_t C);
+
+/* One HOLA layer call over n tokens of B sequences x n_heads heads (all device pointers):
+ *   q, k, v, y [B][n_heads][n][d] in dtype (LOLA_F32 or LOLA_BF16), 16-byte aligned, d in {64, 128};
+ *   alpha, beta [B][n_heads][n] fp32 gates (alpha in (0, 1], beta in [0, 1]);
+ *   gamma_q, gamma_k [n_heads][d] fp32 cache-path scales; sink, gate [n_heads] fp32;
+ *   S_out (nullable) [B][n_heads][d][d] fp32 final state, row = key dimension;
+ *   cache_pos_out, cache_score_out (nullable) [B][n_heads][w]: the final persistent cache sorted by
+ *   position (-1 / 0 where fewer than w tokens exist) and its write magnitudes.
+ * 1 <= C <= 1024, 0 <= w <= 64 (LOLA_EUNSUPPORTED beyond).  workspace: hola_workspace_bytes(...) bytes,
+ * 256-byte aligned.  n == 0 is a no-op.  The state path is serial in t within a (sequence, head). */
+lola_status hola_prefill(int32_t B, int32_t n_heads, int32_t d, int32_t dtype, int64_t n, int32_t C, int32_t w,
+                         const void *q, const void *k, const void *v, const float *alpha, const float *beta,
+                         const float *gamma_q, const float *gamma_k, const float *sink, const float *gate,
+                         void *y, float *S_out, int32_t *cache_pos_out, float *cache_score_out,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static, human-readable text for a status code. */
 const char *lola_status_string(lola_status status);
 

@@ -15,7 +15,7 @@ HEADER = os.path.join(ROOT, "include", "lola.h")
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(lola_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:lola|hola)_[a-z_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")

@@ -583,3 +583,71 @@ def test_score_rule_multi_token_decode():
     with pytest.raises(lola.LolaError) as e:
         lola.lola_decode_step(st, phi, x, x, x, score_rule="attn")
     assert e.value.code == lola.LOLA_EUNSUPPORTED
+
+
+# ------------------------------------------------------------------------------------------------
+# HOLA variant (hola_prefill): gated delta rule + write-magnitude cache against oracle/hola_oracle.py.
+# ------------------------------------------------------------------------------------------------
+
+def _hola_inputs(seed, B, h, n, d, dtype):
+    """Seeded synthetic inputs; in bf16 mode the oracle gets the same bf16-rounded q, k, v."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, h, n, d)).astype(np.float32)
+    k = rng.standard_normal((B, h, n, d)).astype(np.float32)
+    v = rng.standard_normal((B, h, n, d)).astype(np.float32)
+    if dtype == "bf16":
+        q, k, v = (torch.from_numpy(x).to(torch.bfloat16).float().numpy() for x in (q, k, v))
+    alpha = rng.uniform(0.9, 1.0, (B, h, n)).astype(np.float32)
+    beta = rng.uniform(0.0, 1.0, (B, h, n)).astype(np.float32)
+    gq = rng.uniform(0.5, 1.5, (h, d)).astype(np.float32)
+    gk = rng.uniform(0.5, 1.5, (h, d)).astype(np.float32)
+    sink = rng.standard_normal(h).astype(np.float32)
+    gate = rng.standard_normal(h).astype(np.float32)
+    return q, k, v, alpha, beta, gq, gk, sink, gate
+
+
+HOLA_CASES = [
+    (90, dict(n=300, C=64, w=16, d=64)),        # several chunks, ragged tail
+    (91, dict(n=530, C=256, w=64, d=128)),      # the page's w and C, d = 128
+    (92, dict(n=100, C=1, w=8, d=64)),          # one-token chunks
+    (93, dict(n=70, C=256, w=64, d=128)),       # n < C: no persistent cache is ever read
+    (94, dict(n=200, C=32, w=0, d=64)),         # w = 0: chunk tokens and the sink only
+]
+
+
+@pytest.mark.parametrize("seed,kw", HOLA_CASES, ids=[f"s{s}" for s, _ in HOLA_CASES])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_hola_prefill(seed, kw, dtype):
+    """Outputs, final state, final cache and its magnitudes against the oracle; in bf16 the oracle
+    takes the same bf16 inputs (the GPU also rounds the normalised cache-path q, k to bf16)."""
+    import hybrid_linear_attention_chunkwise_amd as lola
+    from oracle import hola_oracle as HO
+    B, h = 1, 2
+    n, C, w, d = kw["n"], kw["C"], kw["w"], kw["d"]
+    q, k, v, alpha, beta, gq, gk, sink, gate = _hola_inputs(seed, B, h, n, d, dtype)
+    dev = torch.device("cuda:0")
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    T = lambda x, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(dt)
+    S_out = torch.empty(B, h, d, d, device=dev)
+    cpos = torch.full((B, h, max(w, 1)), -7, dtype=torch.int32, device=dev)
+    cscore = torch.empty(B, h, max(w, 1), device=dev)
+    print(f"[hola] n={n} C={C} w={w} d={d} {dtype}", flush=True)
+    y = lola.hola_prefill(T(q, tdt), T(k, tdt), T(v, tdt), T(alpha), T(beta), T(gq), T(gk), T(sink), T(gate),
+                          C, w, S_out=S_out, cache_pos=cpos, cache_score=cscore)
+    torch.cuda.synchronize()
+    y, S_out, cpos, cscore = (x.float().cpu().numpy() if x.dtype != torch.int32 else x.cpu().numpy()
+                              for x in (y, S_out, cpos, cscore))
+    tol = TL.FP32_TOL if dtype == "f32" else TL.BF16_TOL
+    worst = 0.0
+    for hh in range(h):
+        y_o, S_o, cache_o, m_o, _ = HO.hola_prefill(q[0, hh], k[0, hh], v[0, hh], alpha[0, hh], beta[0, hh],
+                                                     gq[hh], gk[hh], float(sink[hh]), float(gate[hh]), C, w)
+        got_cache = [int(p) for p in cpos[0, hh][:w] if p >= 0]
+        assert got_cache == cache_o, f"head {hh}: final cache differs"
+        if w > 0:
+            np.testing.assert_allclose(cscore[0, hh][:len(cache_o)], m_o[cache_o], rtol=1e-4 if dtype == "f32" else 2e-2)
+        worst = max(worst, TL.row_rel_err(y[0, hh], y_o))
+        scale = max(1.0, float(np.abs(S_o).max()))
+        assert np.abs(S_out[0, hh] - S_o).max() <= 1e-4 * scale
+    print(f"[hola] max output err {worst:.3e}", flush=True)
+    assert worst <= tol
