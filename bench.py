@@ -25,6 +25,7 @@ METRIC = "prefill tokens/s and decode tokens/s per GPU; % of MFMA / HBM roofline
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector
 MULTI_TOKEN_C = 16          # tokens per call in the multi-token decode measurement
 KERNEL_SOURCES = ("lola_common.hpp", "lola_phi.hip", "lola_chain.hip", "lola_readout.hip", "lola_decode.hip",
                   "lola_decode_fast.hip", "lola_collide.hip",
@@ -210,6 +211,50 @@ def bench_options(args, lola, torch, wl):
     return out
 
 
+HOLA_W, HOLA_C = 64, 256     # the HOLA page's persistent cache and chunk
+
+
+def bench_hola(args, lola, torch, wl):
+    """The HOLA variant (hola_prefill) on the headline shape (32 heads, n = 4096, d = 128, bf16) with the
+    page's w = 64 and C = 256: K back-to-back layer calls on resident seeded inputs.  The delta-rule scan
+    is serial in t per (sequence, head); its algorithmic work is 4 d^2 fp32 FLOP per token and head
+    (prediction, decayed write, read-out), priced against the fp32 vector peak."""
+    import numpy as np
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(20)
+    B, h, n, d = wl.B, wl.h, wl.n, wl.d_k
+    q, k, v = (torch.from_numpy(rng.standard_normal((B, h, n, d)).astype(np.float32)).to(dev).to(torch.bfloat16)
+               for _ in range(3))
+    alpha = torch.from_numpy(rng.uniform(0.9, 1.0, (B, h, n)).astype(np.float32)).to(dev)
+    beta = torch.from_numpy(rng.uniform(0.0, 1.0, (B, h, n)).astype(np.float32)).to(dev)
+    gq = torch.from_numpy(rng.uniform(0.5, 1.5, (h, d)).astype(np.float32)).to(dev)
+    gk = torch.from_numpy(rng.uniform(0.5, 1.5, (h, d)).astype(np.float32)).to(dev)
+    sink = torch.zeros(h, device=dev)
+    gate = torch.full((h,), -4.0, device=dev)                 # the page's gate initialisation
+    y = torch.empty_like(v)
+    ws = torch.empty(lola.hola_workspace_bytes(B, h, d, torch.bfloat16, n, HOLA_C), dtype=torch.uint8, device=dev)
+
+    def call():
+        lola.hola_prefill(q, k, v, alpha, beta, gq, gk, sink, gate, HOLA_C, HOLA_W, y=y, workspace=ws)
+    for _ in range(max(1, args.warmup)):
+        call()
+    torch.cuda.synchronize()
+    steps = max(1, args.steps // 4)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    flop = 4.0 * d * d * B * h * n
+    ach = flop / (ms * 1e-3) / 1e12
+    log(f"hola: {ms:.3f} ms/call")
+    return {"workload": f"hola_n{n}_h{h}_d{d}_w{HOLA_W}_C{HOLA_C}_bf16", "ms_per_call": round(ms, 4),
+            "tokens_per_s": round(B * n / (ms * 1e-3), 1),
+            "roofline": {"bound": "alu", "kernel": "hola_scan (whole call)", "achieved": round(ach, 3),
+                         "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(ach / PEAK_FP32_VALU_TFLOPS, 5), "algorithmic_flop_per_call": flop}}
+
+
 def bench_decode(args, lola, torch, wl):
     from workloads import make_decode_tokens_device, make_qkv_device, make_weights
     dev = torch.device("cuda:0")
@@ -322,6 +367,7 @@ def main() -> int:
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-collisions", action="store_true")
     ap.add_argument("--no-options", action="store_true")
+    ap.add_argument("--no-hola", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -394,6 +440,8 @@ def main() -> int:
         out["collision_map"] = bench_collisions(args, lola, torch, wl)
     if not args.no_options:
         out["options"] = bench_options(args, lola, torch, wl)
+    if not args.no_hola:
+        out["hola"] = bench_hola(args, lola, torch, wl)
     if not args.no_cpu_baseline:
         log("cpu baseline: running the oracle ...")
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_heads)

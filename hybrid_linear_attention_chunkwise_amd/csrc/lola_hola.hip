@@ -12,10 +12,10 @@
 // Kernels, in launch order:
 //   prep   one pass over the tokens: unit-norm q, k for the state (fp32) and the cache path's
 //          normalised q, k (storage type), 32 lanes per row;
-//   scan   the delta rule, serial in t: one workgroup per (sequence, head), thread c owns column c of S
-//          (d fp32 registers), so the prediction S^T k, the write and the read-out S^T q need no
-//          exchange between threads.  Keys, queries, values and gates are staged in LDS 32 tokens at a
-//          time and read as broadcasts;
+//   scan   the delta rule, serial in t: one workgroup per (sequence, head), four lanes of one wave per
+//          column of S (a quarter of its rows each, in registers), so the prediction S^T k and the
+//          read-out S^T q finish with two lane swaps and the write needs no exchange at all.  Keys,
+//          queries, values and gates are staged in LDS 32 tokens at a time and read as broadcasts;
 //   mag    m_t = beta_t ||e_t||, 32 lanes per row;
 //   cache  the persistent cache at every chunk start, serial in the chunks: one workgroup per (sequence,
 //          head) keeps the current cache and merges each chunk into it by exact rank (ties: older);
@@ -70,14 +70,21 @@ __global__ __launch_bounds__(256) void hola_prep_kernel(HolaArgs A) {
 }
 
 // ---------------- scan ----------------
+// 4 d threads: lane (g, c) of wave w owns rows g d/4 .. (g + 1) d/4 - 1 of column 16 w + c of S, so a
+// column's four quarters sit in lanes c, c + 16, c + 32, c + 48 of one wave and its dot products
+// (S^T k, S^T q) are completed by two lane swaps, with no LDS and no barrier per token.
 template <typename T, int D>
-__global__ __launch_bounds__(D) void hola_scan_kernel(HolaArgs A) {
+__global__ __launch_bounds__(4 * D) void hola_scan_kernel(HolaArgs A) {
     constexpr int TB = 32;                                              // tokens staged at a time
+    constexpr int RQ = D / 4;                                           // rows per thread
+    constexpr int NT = 4 * D;
     __shared__ __align__(16) float sK[TB][D];
     __shared__ __align__(16) float sQ[TB][D];
     __shared__ __align__(16) float sV[TB][D];
     __shared__ float sAl[TB], sBe[TB];
-    const int bh = blockIdx.x, c = threadIdx.x;
+    const int bh = blockIdx.x, tid = threadIdx.x;
+    const int w = tid >> 6, l = tid & 63, g = l >> 4, c = l & 15;
+    const int col = 16 * w + c, row0 = g * RQ;
     const int n = A.n;
     const float* kh = reinterpret_cast<const float*>(A.ws + A.L.khat) + (int64_t)bh * n * D;
     const float* qh = reinterpret_cast<const float*>(A.ws + A.L.qhat) + (int64_t)bh * n * D;
@@ -86,48 +93,58 @@ __global__ __launch_bounds__(D) void hola_scan_kernel(HolaArgs A) {
     const float* be = A.beta + (int64_t)bh * n;
     float* oo = reinterpret_cast<float*>(A.ws + A.L.o) + (int64_t)bh * n * D;
     float* ee = reinterpret_cast<float*>(A.ws + A.L.e) + (int64_t)bh * n * D;
-    float S[D];                                                         // column c of S: S[r] = S(r, c)
+    float S[RQ];                                                        // S[r] = S(row0 + r, col)
 #pragma unroll
-    for (int r = 0; r < D; ++r) S[r] = 0.f;
+    for (int r = 0; r < RQ; ++r) S[r] = 0.f;
     for (int t0 = 0; t0 < n; t0 += TB) {
         const int nb = min(TB, n - t0);
         __syncthreads();                                                // the previous block is used up
-        for (int i = c; i < nb * D; i += D) {
+        for (int i = tid; i < nb * D; i += NT) {
             sK[i / D][i % D] = kh[(int64_t)t0 * D + i];
             sQ[i / D][i % D] = qh[(int64_t)t0 * D + i];
             sV[i / D][i % D] = to_f(vin[(int64_t)t0 * D + i]);
         }
-        if (c < nb) { sAl[c] = al[t0 + c]; sBe[c] = be[t0 + c]; }
+        if (tid < nb) { sAl[tid] = al[t0 + tid]; sBe[tid] = be[t0 + tid]; }
         __syncthreads();
         for (int j = 0; j < nb; ++j) {
             const float a = sAl[j], b = sBe[j];
-            float u = 0.f;                                              // (S^T k)_c with the old state
+            float u4[4] = {0.f, 0.f, 0.f, 0.f};                         // (S^T k)_col with the old state
 #pragma unroll
-            for (int r4 = 0; r4 < D / 4; ++r4) {
-                const float4 k4 = *reinterpret_cast<const float4*>(&sK[j][4 * r4]);
-                u += S[4 * r4] * k4.x + S[4 * r4 + 1] * k4.y + S[4 * r4 + 2] * k4.z + S[4 * r4 + 3] * k4.w;
+            for (int r4 = 0; r4 < RQ / 4; ++r4) {
+                const float4 k4 = *reinterpret_cast<const float4*>(&sK[j][row0 + 4 * r4]);
+                u4[0] = fmaf(S[4 * r4], k4.x, u4[0]);
+                u4[1] = fmaf(S[4 * r4 + 1], k4.y, u4[1]);
+                u4[2] = fmaf(S[4 * r4 + 2], k4.z, u4[2]);
+                u4[3] = fmaf(S[4 * r4 + 3], k4.w, u4[3]);
             }
-            const float e = sV[j][c] - a * u;                           // residual of the decayed prediction
-            const float w = b * e;
-            float o = 0.f;
+            const float u = sum_groups((u4[0] + u4[1]) + (u4[2] + u4[3]));
+            const float e = sV[j][col] - a * u;                         // residual of the decayed prediction
+            const float wr = b * e;
+            float o4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int r4 = 0; r4 < D / 4; ++r4) {
-                const float4 k4 = *reinterpret_cast<const float4*>(&sK[j][4 * r4]);
-                const float4 q4 = *reinterpret_cast<const float4*>(&sQ[j][4 * r4]);
-                S[4 * r4] = fmaf(S[4 * r4], a, w * k4.x);
-                S[4 * r4 + 1] = fmaf(S[4 * r4 + 1], a, w * k4.y);
-                S[4 * r4 + 2] = fmaf(S[4 * r4 + 2], a, w * k4.z);
-                S[4 * r4 + 3] = fmaf(S[4 * r4 + 3], a, w * k4.w);
-                o += S[4 * r4] * q4.x + S[4 * r4 + 1] * q4.y + S[4 * r4 + 2] * q4.z + S[4 * r4 + 3] * q4.w;
+            for (int r4 = 0; r4 < RQ / 4; ++r4) {
+                const float4 k4 = *reinterpret_cast<const float4*>(&sK[j][row0 + 4 * r4]);
+                const float4 q4 = *reinterpret_cast<const float4*>(&sQ[j][row0 + 4 * r4]);
+                S[4 * r4] = fmaf(S[4 * r4], a, wr * k4.x);
+                S[4 * r4 + 1] = fmaf(S[4 * r4 + 1], a, wr * k4.y);
+                S[4 * r4 + 2] = fmaf(S[4 * r4 + 2], a, wr * k4.z);
+                S[4 * r4 + 3] = fmaf(S[4 * r4 + 3], a, wr * k4.w);
+                o4[0] = fmaf(S[4 * r4], q4.x, o4[0]);
+                o4[1] = fmaf(S[4 * r4 + 1], q4.y, o4[1]);
+                o4[2] = fmaf(S[4 * r4 + 2], q4.z, o4[2]);
+                o4[3] = fmaf(S[4 * r4 + 3], q4.w, o4[3]);
             }
-            oo[(int64_t)(t0 + j) * D + c] = o;
-            ee[(int64_t)(t0 + j) * D + c] = e;
+            const float o = sum_groups((o4[0] + o4[1]) + (o4[2] + o4[3]));
+            if (g == 0) {
+                oo[(int64_t)(t0 + j) * D + col] = o;
+                ee[(int64_t)(t0 + j) * D + col] = e;
+            }
         }
     }
     if (A.S_out) {
         float* so = A.S_out + (int64_t)bh * D * D;
 #pragma unroll
-        for (int r = 0; r < D; ++r) so[(int64_t)r * D + c] = S[r];
+        for (int r = 0; r < RQ; ++r) so[(int64_t)(row0 + r) * D + col] = S[r];
     }
 }
 
@@ -332,7 +349,7 @@ hipError_t launch_hola_t(const HolaArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((hola_prep_kernel<T, D>), dim3(rgrid), dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((hola_scan_kernel<T, D>), dim3(a.BH), dim3(D), 0, stream, a);
+    hipLaunchKernelGGL((hola_scan_kernel<T, D>), dim3(a.BH), dim3(4 * D), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((hola_mag_kernel<D>), dim3(rgrid), dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -129,3 +129,29 @@ def test_config2_collision_map_sampled(dtype):
     from test_gpu_parity import collision_check
     wl = dataclasses.replace(CONFIGS[2], dtype=dtype)
     collision_check(wl, [(0, 3), (0, 30)])
+
+
+def test_hola_full_size_sampled():
+    """The HOLA variant at the benchmark's shape (32 heads, n = 4096, d = 128, bf16, w = 64, C = 256),
+    two heads recomputed in full by the oracle."""
+    import hybrid_linear_attention_chunkwise_amd as lola
+    from oracle import hola_oracle as HO
+    from test_gpu_parity import _hola_inputs
+    B, h, n, d, C, w = 1, 32, 4096, 128, 256, 64
+    q, k, v, alpha, beta, gq, gk, sink, gate = _hola_inputs(95, B, h, n, d, "bf16")
+    dev = torch.device("cuda:0")
+    T = lambda x, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(dt)
+    cpos = torch.full((B, h, w), -7, dtype=torch.int32, device=dev)
+    print("[hola full] GPU", flush=True)
+    y = lola.hola_prefill(T(q, torch.bfloat16), T(k, torch.bfloat16), T(v, torch.bfloat16), T(alpha), T(beta),
+                          T(gq), T(gk), T(sink), T(gate), C, w, cache_pos=cpos)
+    y = y.float().cpu().numpy()
+    cpos = cpos.cpu().numpy()
+    for hh in (3, 30):
+        print(f"[hola full] oracle head {hh}", flush=True)
+        y_o, _, cache_o, _, _ = HO.hola_prefill(q[0, hh], k[0, hh], v[0, hh], alpha[0, hh], beta[0, hh], gq[hh],
+                                                gk[hh], float(sink[hh]), float(gate[hh]), C, w)
+        assert [int(p) for p in cpos[0, hh]] == cache_o
+        err = TL.row_rel_err(y[0, hh], y_o)
+        print(f"[hola full] head {hh}: max err {err:.3e}", flush=True)
+        assert err <= TL.BF16_TOL
