@@ -12,10 +12,10 @@
 // Kernels, in launch order:
 //   prep   one pass over the tokens: unit-norm q, k for the state (fp32) and the cache path's
 //          normalised q, k (storage type), 32 lanes per row;
-//   scan   the delta rule, serial in t: one workgroup per (sequence, head), four lanes of one wave per
-//          column of S (a quarter of its rows each, in registers), so the prediction S^T k and the
-//          read-out S^T q finish with two lane swaps and the write needs no exchange at all.  Keys,
-//          queries, values and gates are staged in LDS 32 tokens at a time and read as broadcasts;
+//   scan   the delta rule, serial in t but separable in the value dimension: one workgroup per
+//          (sequence, head, 16 columns of S), a 16-lane row per column (d/16 of its rows per lane, in
+//          registers), so S^T k and S^T q close with DPP rotations.  Keys, queries, values and gates
+//          are staged in LDS 32 tokens at a time;
 //   mag    m_t = beta_t ||e_t||, 32 lanes per row;
 //   cache  the persistent cache at every chunk start, serial in the chunks: one workgroup per (sequence,
 //          head) keeps the current cache and merges each chunk into it by exact rank (ties: older);
@@ -70,21 +70,34 @@ __global__ __launch_bounds__(256) void hola_prep_kernel(HolaArgs A) {
 }
 
 // ---------------- scan ----------------
-// 4 d threads: lane (g, c) of wave w owns rows g d/4 .. (g + 1) d/4 - 1 of column 16 w + c of S, so a
-// column's four quarters sit in lanes c, c + 16, c + 32, c + 48 of one wave and its dot products
-// (S^T k, S^T q) are completed by two lane swaps, with no LDS and no barrier per token.
+// Sum over the 16 lanes of a DPP row (every lane gets the total): rotations by 8, 4, 2, 1.
+__device__ __forceinline__ float row_sum16(float x) {
+    x += dpp_mov<0x128>(x);   // row_ror:8
+    x += dpp_mov<0x124>(x);   // row_ror:4
+    x += dpp_mov<0x122>(x);   // row_ror:2
+    x += dpp_mov<0x121>(x);   // row_ror:1
+    return x;
+}
+
+// The delta rule is serial in t but separable in the value dimension: column c of S only needs k, q,
+// alpha, beta and v_c.  One workgroup of four waves takes 16 columns of one (sequence, head); a column
+// belongs to one 16-lane row of a wave, each lane holding d/16 of its rows in registers, so S^T k and
+// S^T q close with four DPP rotations and the per-token chain stays short.  S = scl * P: the decay
+// multiplies the scalar scl, so the write costs one FMA per element (P += (beta e / scl) k); P is
+// rescaled into S before scl gets small.
 template <typename T, int D>
-__global__ __launch_bounds__(4 * D) void hola_scan_kernel(HolaArgs A) {
+__global__ __launch_bounds__(256) void hola_scan_kernel(HolaArgs A) {
     constexpr int TB = 32;                                              // tokens staged at a time
-    constexpr int RQ = D / 4;                                           // rows per thread
-    constexpr int NT = 4 * D;
+    constexpr int RP = D / 16;                                          // rows per lane
+    constexpr int NT = 256;
     __shared__ __align__(16) float sK[TB][D];
     __shared__ __align__(16) float sQ[TB][D];
-    __shared__ __align__(16) float sV[TB][D];
+    __shared__ __align__(16) float sV[TB][16];
     __shared__ float sAl[TB], sBe[TB];
-    const int bh = blockIdx.x, tid = threadIdx.x;
-    const int w = tid >> 6, l = tid & 63, g = l >> 4, c = l & 15;
-    const int col = 16 * w + c, row0 = g * RQ;
+    const int bh = blockIdx.x / (D / 16), cb = 16 * (blockIdx.x % (D / 16));   // first column of this part
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int cl = 4 * w + (l >> 4);                                    // column within the part
+    const int col = cb + cl, row0 = (l & 15) * RP;
     const int n = A.n;
     const float* kh = reinterpret_cast<const float*>(A.ws + A.L.khat) + (int64_t)bh * n * D;
     const float* qh = reinterpret_cast<const float*>(A.ws + A.L.qhat) + (int64_t)bh * n * D;
@@ -93,58 +106,64 @@ __global__ __launch_bounds__(4 * D) void hola_scan_kernel(HolaArgs A) {
     const float* be = A.beta + (int64_t)bh * n;
     float* oo = reinterpret_cast<float*>(A.ws + A.L.o) + (int64_t)bh * n * D;
     float* ee = reinterpret_cast<float*>(A.ws + A.L.e) + (int64_t)bh * n * D;
-    float S[RQ];                                                        // S[r] = S(row0 + r, col)
+    float P[RP];                                                        // P[r] = S(row0 + r, col) / scl
 #pragma unroll
-    for (int r = 0; r < RQ; ++r) S[r] = 0.f;
+    for (int r = 0; r < RP; ++r) P[r] = 0.f;
+    float scl = 1.f;
     for (int t0 = 0; t0 < n; t0 += TB) {
         const int nb = min(TB, n - t0);
         __syncthreads();                                                // the previous block is used up
         for (int i = tid; i < nb * D; i += NT) {
             sK[i / D][i % D] = kh[(int64_t)t0 * D + i];
             sQ[i / D][i % D] = qh[(int64_t)t0 * D + i];
-            sV[i / D][i % D] = to_f(vin[(int64_t)t0 * D + i]);
         }
+        for (int i = tid; i < nb * 16; i += NT) sV[i / 16][i % 16] = to_f(vin[(int64_t)(t0 + i / 16) * D + cb + i % 16]);
         if (tid < nb) { sAl[tid] = al[t0 + tid]; sBe[tid] = be[t0 + tid]; }
         __syncthreads();
+        // the next token's operands are read from LDS while the current one is computed
+        float kc[RP], qc[RP];
+#pragma unroll
+        for (int r = 0; r < RP; ++r) { kc[r] = sK[0][row0 + r]; qc[r] = sQ[0][row0 + r]; }
+        float vc = sV[0][cl], ac = sAl[0], bc = sBe[0];
         for (int j = 0; j < nb; ++j) {
-            const float a = sAl[j], b = sBe[j];
-            float u4[4] = {0.f, 0.f, 0.f, 0.f};                         // (S^T k)_col with the old state
+            const int jn = j + 1 < nb ? j + 1 : j;
+            float kn[RP], qn[RP];
 #pragma unroll
-            for (int r4 = 0; r4 < RQ / 4; ++r4) {
-                const float4 k4 = *reinterpret_cast<const float4*>(&sK[j][row0 + 4 * r4]);
-                u4[0] = fmaf(S[4 * r4], k4.x, u4[0]);
-                u4[1] = fmaf(S[4 * r4 + 1], k4.y, u4[1]);
-                u4[2] = fmaf(S[4 * r4 + 2], k4.z, u4[2]);
-                u4[3] = fmaf(S[4 * r4 + 3], k4.w, u4[3]);
-            }
-            const float u = sum_groups((u4[0] + u4[1]) + (u4[2] + u4[3]));
-            const float e = sV[j][col] - a * u;                         // residual of the decayed prediction
-            const float wr = b * e;
-            float o4[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int r = 0; r < RP; ++r) { kn[r] = sK[jn][row0 + r]; qn[r] = sQ[jn][row0 + r]; }
+            const float vn = sV[jn][cl], an = sAl[jn], bnx = sBe[jn];
+            float u2[2] = {0.f, 0.f};
 #pragma unroll
-            for (int r4 = 0; r4 < RQ / 4; ++r4) {
-                const float4 k4 = *reinterpret_cast<const float4*>(&sK[j][row0 + 4 * r4]);
-                const float4 q4 = *reinterpret_cast<const float4*>(&sQ[j][row0 + 4 * r4]);
-                S[4 * r4] = fmaf(S[4 * r4], a, wr * k4.x);
-                S[4 * r4 + 1] = fmaf(S[4 * r4 + 1], a, wr * k4.y);
-                S[4 * r4 + 2] = fmaf(S[4 * r4 + 2], a, wr * k4.z);
-                S[4 * r4 + 3] = fmaf(S[4 * r4 + 3], a, wr * k4.w);
-                o4[0] = fmaf(S[4 * r4], q4.x, o4[0]);
-                o4[1] = fmaf(S[4 * r4 + 1], q4.y, o4[1]);
-                o4[2] = fmaf(S[4 * r4 + 2], q4.z, o4[2]);
-                o4[3] = fmaf(S[4 * r4 + 3], q4.w, o4[3]);
+            for (int r = 0; r < RP; ++r) u2[r & 1] = fmaf(P[r], kc[r], u2[r & 1]);
+            const float stk = scl * row_sum16(u2[0] + u2[1]);           // (S^T k)_col
+            if (ac * scl < 1e-20f) {                                    // fold the scale into P (S unchanged)
+#pragma unroll
+                for (int r = 0; r < RP; ++r) P[r] *= scl;
+                scl = 1.f;
             }
-            const float o = sum_groups((o4[0] + o4[1]) + (o4[2] + o4[3]));
-            if (g == 0) {
+            const float sd = ac * scl;                                  // scale of the decayed state
+            const float e = vc - ac * stk;                              // residual of the decayed prediction
+            const float wr = bc * e / sd;                               // the write in P's scale
+            float o2[2] = {0.f, 0.f};
+#pragma unroll
+            for (int r = 0; r < RP; ++r) {
+                P[r] = fmaf(wr, kc[r], P[r]);
+                o2[r & 1] = fmaf(P[r], qc[r], o2[r & 1]);
+            }
+            const float o = sd * row_sum16(o2[0] + o2[1]);
+            scl = sd;
+            if ((l & 15) == 0) {
                 oo[(int64_t)(t0 + j) * D + col] = o;
                 ee[(int64_t)(t0 + j) * D + col] = e;
             }
+#pragma unroll
+            for (int r = 0; r < RP; ++r) { kc[r] = kn[r]; qc[r] = qn[r]; }
+            vc = vn; ac = an; bc = bnx;
         }
     }
     if (A.S_out) {
         float* so = A.S_out + (int64_t)bh * D * D;
 #pragma unroll
-        for (int r = 0; r < RQ; ++r) so[(int64_t)(row0 + r) * D + col] = S[r];
+        for (int r = 0; r < RP; ++r) so[(int64_t)(row0 + r) * D + col] = P[r] * scl;
     }
 }
 
@@ -213,7 +232,8 @@ __global__ __launch_bounds__(256) void hola_cache_kernel(HolaArgs A) {
         for (int i = tid; i < nc; i += 256) {
             const unsigned long long ki = sKey[i];
             int above = 0;
-            for (int j = 0; j < nc; ++j) above += sKey[j] > ki;
+#pragma unroll 16
+            for (int j = 0; j < nc; ++j) above += sKey[j] > ki;    // unrolled: the LDS reads overlap
             if (above < keep) sCur[atomicAdd(&sCount, 1)] = sCand[i];
         }
         __syncthreads();
@@ -349,7 +369,7 @@ hipError_t launch_hola_t(const HolaArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((hola_prep_kernel<T, D>), dim3(rgrid), dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((hola_scan_kernel<T, D>), dim3(a.BH), dim3(4 * D), 0, stream, a);
+    hipLaunchKernelGGL((hola_scan_kernel<T, D>), dim3(a.BH * (D / 16)), dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((hola_mag_kernel<D>), dim3(rgrid), dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
