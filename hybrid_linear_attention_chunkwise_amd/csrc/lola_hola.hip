@@ -30,6 +30,7 @@ namespace lola {
 namespace {
 
 constexpr float kHolaRmsEps = 1e-6f;
+constexpr int kHolaScanLanes = 32;   // lanes per column of S in the scan
 
 template <typename T, int PER>
 __device__ __forceinline__ void load_row_piece(const T* p, float (&x)[PER]) {
@@ -88,16 +89,29 @@ __device__ __forceinline__ float row_sum16(float x) {
 template <typename T, int D>
 __global__ __launch_bounds__(256) void hola_scan_kernel(HolaArgs A) {
     constexpr int TB = 32;                                              // tokens staged at a time
-    constexpr int RP = D / 16;                                          // rows per lane
+    constexpr int LPC = kHolaScanLanes;                                 // lanes per column: 16 or 32
+    constexpr int CPW = 256 / LPC;                                      // columns per workgroup
+    constexpr int RP = D / LPC;                                         // rows per lane
     constexpr int NT = 256;
     __shared__ __align__(16) float sK[TB][D];
     __shared__ __align__(16) float sQ[TB][D];
-    __shared__ __align__(16) float sV[TB][16];
+    __shared__ __align__(16) float sV[TB][CPW];
     __shared__ float sAl[TB], sBe[TB];
-    const int bh = blockIdx.x / (D / 16), cb = 16 * (blockIdx.x % (D / 16));   // first column of this part
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-    const int cl = 4 * w + (l >> 4);                                    // column within the part
-    const int col = cb + cl, row0 = (l & 15) * RP;
+    const int bh = blockIdx.x / (D / CPW), cb = CPW * (blockIdx.x % (D / CPW));   // first column of the part
+    const int tid = threadIdx.x;
+    const int cl = tid / LPC;                                           // column within the part
+    const int part = tid % LPC;
+    const int col = cb + cl, row0 = part * RP;
+    // a column's lanes: one 16-lane DPP row, or two rows paired by a lane swap
+    auto col_sum = [](float x) {
+        x = row_sum16(x);
+        if constexpr (LPC == 32) {
+            float a, b;
+            pair16(x, a, b);
+            x = a + b;
+        }
+        return x;
+    };
     const int n = A.n;
     const float* kh = reinterpret_cast<const float*>(A.ws + A.L.khat) + (int64_t)bh * n * D;
     const float* qh = reinterpret_cast<const float*>(A.ws + A.L.qhat) + (int64_t)bh * n * D;
@@ -117,7 +131,7 @@ __global__ __launch_bounds__(256) void hola_scan_kernel(HolaArgs A) {
             sK[i / D][i % D] = kh[(int64_t)t0 * D + i];
             sQ[i / D][i % D] = qh[(int64_t)t0 * D + i];
         }
-        for (int i = tid; i < nb * 16; i += NT) sV[i / 16][i % 16] = to_f(vin[(int64_t)(t0 + i / 16) * D + cb + i % 16]);
+        for (int i = tid; i < nb * CPW; i += NT) sV[i / CPW][i % CPW] = to_f(vin[(int64_t)(t0 + i / CPW) * D + cb + i % CPW]);
         if (tid < nb) { sAl[tid] = al[t0 + tid]; sBe[tid] = be[t0 + tid]; }
         __syncthreads();
         // the next token's operands are read from LDS while the current one is computed
@@ -134,7 +148,7 @@ __global__ __launch_bounds__(256) void hola_scan_kernel(HolaArgs A) {
             float u2[2] = {0.f, 0.f};
 #pragma unroll
             for (int r = 0; r < RP; ++r) u2[r & 1] = fmaf(P[r], kc[r], u2[r & 1]);
-            const float stk = scl * row_sum16(u2[0] + u2[1]);           // (S^T k)_col
+            const float stk = scl * col_sum(u2[0] + u2[1]);             // (S^T k)_col
             if (ac * scl < 1e-20f) {                                    // fold the scale into P (S unchanged)
 #pragma unroll
                 for (int r = 0; r < RP; ++r) P[r] *= scl;
@@ -149,9 +163,9 @@ __global__ __launch_bounds__(256) void hola_scan_kernel(HolaArgs A) {
                 P[r] = fmaf(wr, kc[r], P[r]);
                 o2[r & 1] = fmaf(P[r], qc[r], o2[r & 1]);
             }
-            const float o = sd * row_sum16(o2[0] + o2[1]);
+            const float o = sd * col_sum(o2[0] + o2[1]);
             scl = sd;
-            if ((l & 15) == 0) {
+            if (part == 0) {
                 oo[(int64_t)(t0 + j) * D + col] = o;
                 ee[(int64_t)(t0 + j) * D + col] = e;
             }
@@ -369,7 +383,7 @@ hipError_t launch_hola_t(const HolaArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((hola_prep_kernel<T, D>), dim3(rgrid), dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((hola_scan_kernel<T, D>), dim3(a.BH * (D / 16)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((hola_scan_kernel<T, D>), dim3(a.BH * (D / (256 / kHolaScanLanes))), dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((hola_mag_kernel<D>), dim3(rgrid), dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
