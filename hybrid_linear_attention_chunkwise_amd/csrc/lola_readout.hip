@@ -604,23 +604,32 @@ hipError_t launch_prefill_t(const PrefillArgs& a0, hipStream_t stream, hipEvent_
     const int nseg = split_chunks(a.nchunks, a.BH * a.nqt, device_cus(), bounds, kMaxSegments);
     if ((e = launch_phi_t<T, DK, PHI>(a, stream)) != hipSuccess) return e;
     if (a.score_rule != kScoreSre && (e = launch_qscore_t<T, DK>(a, stream)) != hipSuccess) return e;
+    // The last range's read-out follows the chain on the caller's stream, so it starts without a
+    // cross-stream hop; the earlier ranges' read-outs run on the side stream.
     for (int i = 0; i < nseg; ++i) {
         if ((e = launch_chain_range<T, DK, PHI>(a, bounds[i], bounds[i + 1], stream)) != hipSuccess) return e;
         if ((e = hipEventRecord(side->seg[i], stream)) != hipSuccess) return e;
+        if (i == nseg - 1) break;
         if ((e = hipStreamWaitEvent(side->stream, side->seg[i], 0)) != hipSuccess) return e;
-        if ((e = launch_readout<T, DK, PHI>(a, bounds[i], bounds[i + 1], side->stream, nseg > 1 && i == nseg - 1)) != hipSuccess)
-            return e;
+        if ((e = launch_readout<T, DK, PHI>(a, bounds[i], bounds[i + 1], side->stream, false)) != hipSuccess) return e;
     }
+    if ((e = launch_readout<T, DK, PHI>(a, bounds[nseg - 1], bounds[nseg], stream, nseg > 1)) != hipSuccess) return e;
     // The commit overwrites the state's cache and window rows.  A call that starts from an empty
     // state (t = 0: no cache member, no window token) never reads those rows in the read-out, so its
-    // commit runs on the caller's stream beside the last read-out; otherwise it follows the last
-    // read-out on the side stream.  Then the caller's stream joins.
+    // commit runs on the side stream as soon as the chain is done, beside the last read-out;
+    // otherwise it follows every read-out on the caller's stream.  Either way the caller's stream
+    // joins the side stream.
     a.c_begin = 0;
     a.c_end = a.nchunks;
     const bool fresh = a.t0 == 0;
-    if ((e = launch_commit<T, DK>(a, fresh ? stream : side->stream)) != hipSuccess) return e;
+    if (fresh) {
+        if ((e = hipStreamWaitEvent(side->stream, side->seg[nseg - 1], 0)) != hipSuccess) return e;
+        if ((e = launch_commit<T, DK>(a, side->stream)) != hipSuccess) return e;
+    }
     if ((e = hipEventRecord(side->join, side->stream)) != hipSuccess) return e;
-    return hipStreamWaitEvent(stream, side->join, 0);
+    if ((e = hipStreamWaitEvent(stream, side->join, 0)) != hipSuccess) return e;
+    if (!fresh) return launch_commit<T, DK>(a, stream);
+    return hipSuccess;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int d, int phi_kind, hipStream_t stream,
