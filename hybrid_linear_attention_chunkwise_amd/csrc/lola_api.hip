@@ -316,7 +316,7 @@ lola_status hola_prefill(int32_t B, int32_t n_heads, int32_t d, int32_t dtype, i
     const int64_t nchunks = (n + C - 1) / C;
     const int64_t BH = (int64_t)B * n_heads;
     const int nqt = (C + 63) / 64;
-    if (BH * nchunks * nqt > (int64_t)INT_MAX) return LOLA_EUNSUPPORTED;
+    if (BH * nchunks * nqt > (int64_t)INT_MAX || (BH * n + 7) / 8 > (int64_t)INT_MAX) return LOLA_EUNSUPPORTED;
     const lola::HolaLayout L = hola_layout(BH, d, dtype == LOLA_BF16 ? 2 : 4, n, nchunks);
     if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes < (size_t)L.total) return LOLA_EINVAL;
     lola::HolaArgs a;
