@@ -25,12 +25,13 @@
 #include "lola_common.hpp"
 #include "lola_internal.hpp"
 
+#include <type_traits>
+
 namespace lola {
 
 namespace {
 
 constexpr float kHolaRmsEps = 1e-6f;
-constexpr int kHolaScanLanes = 32;   // lanes per column of S in the scan
 
 template <typename T, int PER>
 __device__ __forceinline__ void load_row_piece(const T* p, float (&x)[PER]) {
@@ -71,44 +72,53 @@ __global__ __launch_bounds__(256) void hola_prep_kernel(HolaArgs A) {
 }
 
 // ---------------- scan ----------------
-// Sum over the 16 lanes of a DPP row (every lane gets the total): rotations by 8, 4, 2, 1.
-__device__ __forceinline__ float row_sum16(float x) {
-    x += dpp_mov<0x128>(x);   // row_ror:8
-    x += dpp_mov<0x124>(x);   // row_ror:4
-    x += dpp_mov<0x122>(x);   // row_ror:2
-    x += dpp_mov<0x121>(x);   // row_ror:1
-    return x;
-}
 
 // The delta rule is serial in t but separable in the value dimension: column c of S only needs k, q,
-// alpha, beta and v_c.  One workgroup of four waves takes 16 columns of one (sequence, head); a column
-// belongs to one 16-lane row of a wave, each lane holding d/16 of its rows in registers, so S^T k and
-// S^T q close with four DPP rotations and the per-token chain stays short.  S = scl * P: the decay
+// alpha, beta and v_c.  One workgroup of four waves takes 256 / LPC columns of one (sequence, head); a
+// column belongs to LPC lanes of one wave, each lane holding d / LPC of its rows in registers, so S^T k
+// and S^T q close with a few DPP steps and the per-token chain stays short.  S = scl * P: the decay
 // multiplies the scalar scl, so the write costs one FMA per element (P += (beta e / scl) k); P is
-// rescaled into S before scl gets small.
-template <typename T, int D>
+// rescaled into S before scl gets small.  Tokens are staged in LDS TB at a time; the next block's
+// operands are loaded into registers while the current block is scanned, and the outputs of a block
+// leave through LDS as whole rows.
+template <typename T, int D, int LPC>
 __global__ __launch_bounds__(256) void hola_scan_kernel(HolaArgs A) {
     constexpr int TB = 32;                                              // tokens staged at a time
-    constexpr int LPC = kHolaScanLanes;                                 // lanes per column: 16 or 32
-    constexpr int CPW = 256 / LPC;                                      // columns per workgroup
-    constexpr int RP = D / LPC;                                         // rows per lane
     constexpr int NT = 256;
+    constexpr int CPW = NT / LPC;                                       // columns per workgroup
+    constexpr int RP = D / LPC;                                         // rows per lane
+    constexpr int KV4 = TB * D / 4 / NT;                                // float4 of k (and of q) per thread
+    constexpr int VV = TB * CPW / NT;                                   // values per thread
+    constexpr int OV = TB * CPW / NT;                                   // outputs per thread and array
+    static_assert(LPC == 8 || LPC == 16 || LPC == 32, "lanes per column");
+    static_assert(RP % 2 == 0 && KV4 >= 1 && VV >= 1 && D % CPW == 0, "scan tiling");
     __shared__ __align__(16) float sK[TB][D];
     __shared__ __align__(16) float sQ[TB][D];
-    __shared__ __align__(16) float sV[TB][CPW];
+    __shared__ float sV[TB][CPW];
+    __shared__ float sO[TB][CPW], sE[TB][CPW];
+    __shared__ float sJunk[2][NT];                                      // the stores of the other lanes
     __shared__ float sAl[TB], sBe[TB];
     const int bh = blockIdx.x / (D / CPW), cb = CPW * (blockIdx.x % (D / CPW));   // first column of the part
     const int tid = threadIdx.x;
     const int cl = tid / LPC;                                           // column within the part
     const int part = tid % LPC;
     const int col = cb + cl, row0 = part * RP;
-    // a column's lanes: one 16-lane DPP row, or two rows paired by a lane swap
+    // a column's lanes: half a DPP row, one row, or two rows paired by a lane swap; every lane gets the sum
     auto col_sum = [](float x) {
-        x = row_sum16(x);
-        if constexpr (LPC == 32) {
-            float a, b;
-            pair16(x, a, b);
-            x = a + b;
+        if constexpr (LPC == 8) {
+            x += dpp_mov<0xB1>(x);    // quad_perm [1,0,3,2]
+            x += dpp_mov<0x4E>(x);    // quad_perm [2,3,0,1]
+            x += dpp_mov<0x141>(x);   // row_half_mirror: the other quad of the eight lanes
+        } else {
+            x += dpp_mov<0x128>(x);   // row_ror:8
+            x += dpp_mov<0x124>(x);   // row_ror:4
+            x += dpp_mov<0x122>(x);   // row_ror:2
+            x += dpp_mov<0x121>(x);   // row_ror:1
+            if constexpr (LPC == 32) {
+                float a, b;
+                pair16(x, a, b);
+                x = a + b;
+            }
         }
         return x;
     };
@@ -120,60 +130,138 @@ __global__ __launch_bounds__(256) void hola_scan_kernel(HolaArgs A) {
     const float* be = A.beta + (int64_t)bh * n;
     float* oo = reinterpret_cast<float*>(A.ws + A.L.o) + (int64_t)bh * n * D;
     float* ee = reinterpret_cast<float*>(A.ws + A.L.e) + (int64_t)bh * n * D;
+
+    // next block's operands in registers; a token past n reads as zero
+    float4 rk[KV4], rq[KV4];
+    float rv[VV], ra = 0.f, rb = 0.f;
+    auto fetch = [&](int t0) {
+#pragma unroll
+        for (int i = 0; i < KV4; ++i) {
+            const int f = tid + i * NT, tk = f / (D / 4);
+            const bool in = t0 + tk < n;
+            const int64_t off = (int64_t)(in ? t0 + tk : n - 1) * D + 4 * (f % (D / 4));   // always a valid row
+            const float4 k4 = *reinterpret_cast<const float4*>(kh + off);
+            const float4 q4 = *reinterpret_cast<const float4*>(qh + off);
+            rk[i] = in ? k4 : make_float4(0.f, 0.f, 0.f, 0.f);
+            rq[i] = in ? q4 : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int i = 0; i < VV; ++i) {
+            const int f = tid + i * NT, tk = f / CPW;
+            const bool in = t0 + tk < n;
+            const float x = to_f(vin[(int64_t)(in ? t0 + tk : n - 1) * D + cb + f % CPW]);
+            rv[i] = in ? x : 0.f;
+        }
+        if (tid < TB && t0 + tid < n) { ra = al[t0 + tid]; rb = be[t0 + tid]; }
+    };
+    auto stash = [&]() {
+#pragma unroll
+        for (int i = 0; i < KV4; ++i) {
+            const int f = tid + i * NT;
+            *reinterpret_cast<float4*>(&sK[0][0] + 4 * f) = rk[i];
+            *reinterpret_cast<float4*>(&sQ[0][0] + 4 * f) = rq[i];
+        }
+#pragma unroll
+        for (int i = 0; i < VV; ++i) (&sV[0][0])[tid + i * NT] = rv[i];
+        if (tid < TB) { sAl[tid] = ra; sBe[tid] = rb; }
+    };
+    auto flush = [&](int t0) {                                          // block t0's outputs, whole rows
+#pragma unroll
+        for (int i = 0; i < OV; ++i) {
+            const int f = tid + i * NT, tk = f / CPW;
+            if (t0 + tk < n) {
+                const int64_t off = (int64_t)(t0 + tk) * D + cb + f % CPW;
+                oo[off] = (&sO[0][0])[f];
+                ee[off] = (&sE[0][0])[f];
+            }
+        }
+    };
+
     float P[RP];                                                        // P[r] = S(row0 + r, col) / scl
 #pragma unroll
     for (int r = 0; r < RP; ++r) P[r] = 0.f;
     float scl = 1.f;
-    for (int t0 = 0; t0 < n; t0 += TB) {
-        const int nb = min(TB, n - t0);
-        __syncthreads();                                                // the previous block is used up
-        for (int i = tid; i < nb * D; i += NT) {
-            sK[i / D][i % D] = kh[(int64_t)t0 * D + i];
-            sQ[i / D][i % D] = qh[(int64_t)t0 * D + i];
-        }
-        for (int i = tid; i < nb * CPW; i += NT) sV[i / CPW][i % CPW] = to_f(vin[(int64_t)(t0 + i / CPW) * D + cb + i % CPW]);
-        if (tid < nb) { sAl[tid] = al[t0 + tid]; sBe[tid] = be[t0 + tid]; }
-        __syncthreads();
-        // the next token's operands are read from LDS while the current one is computed
+    // one token: returns the column's read-out o and residual e.  FOLD: check whether scl must be folded
+    // into P first (a block whose scales all stay above the threshold skips the check, which keeps its
+    // tokens in one basic block)
+    auto token = [&](int j, float& o, float& e, auto fold_tag) {
+        constexpr bool FOLD = decltype(fold_tag)::value;
         float kc[RP], qc[RP];
 #pragma unroll
-        for (int r = 0; r < RP; ++r) { kc[r] = sK[0][row0 + r]; qc[r] = sQ[0][row0 + r]; }
-        float vc = sV[0][cl], ac = sAl[0], bc = sBe[0];
-        for (int j = 0; j < nb; ++j) {
-            const int jn = j + 1 < nb ? j + 1 : j;
-            float kn[RP], qn[RP];
+        for (int r = 0; r < RP; r += 2) {
+            const float2 k2 = *reinterpret_cast<const float2*>(&sK[j][row0 + r]);
+            const float2 q2 = *reinterpret_cast<const float2*>(&sQ[j][row0 + r]);
+            kc[r] = k2.x; kc[r + 1] = k2.y;
+            qc[r] = q2.x; qc[r + 1] = q2.y;
+        }
+        const float vc = sV[j][cl], ac = sAl[j], bc = sBe[j];
+        float u2[2] = {0.f, 0.f};
 #pragma unroll
-            for (int r = 0; r < RP; ++r) { kn[r] = sK[jn][row0 + r]; qn[r] = sQ[jn][row0 + r]; }
-            const float vn = sV[jn][cl], an = sAl[jn], bnx = sBe[jn];
-            float u2[2] = {0.f, 0.f};
-#pragma unroll
-            for (int r = 0; r < RP; ++r) u2[r & 1] = fmaf(P[r], kc[r], u2[r & 1]);
-            const float stk = scl * col_sum(u2[0] + u2[1]);             // (S^T k)_col
-            if (ac * scl < 1e-20f) {                                    // fold the scale into P (S unchanged)
+        for (int r = 0; r < RP; ++r) u2[r & 1] = fmaf(P[r], kc[r], u2[r & 1]);
+        const float sp = ac * scl;                                      // alpha S^T k = sp * (P^T k)
+        if constexpr (FOLD) {
+            if (sp < 1e-20f) {                                          // fold the scale into P (S unchanged)
 #pragma unroll
                 for (int r = 0; r < RP; ++r) P[r] *= scl;
                 scl = 1.f;
             }
-            const float sd = ac * scl;                                  // scale of the decayed state
-            const float e = vc - ac * stk;                              // residual of the decayed prediction
-            const float wr = bc * e / sd;                               // the write in P's scale
-            float o2[2] = {0.f, 0.f};
+        }
+        const float sd = ac * scl;                                      // scale of the decayed state
+        const float rs = bc * __builtin_amdgcn_rcpf(sd);                // off the chain: beta / scale
+        e = fmaf(-sp, col_sum(u2[0] + u2[1]), vc);                      // v - alpha S^T k
+        const float wr = rs * e;                                        // the write in P's scale
+        float o2[2] = {0.f, 0.f};
 #pragma unroll
-            for (int r = 0; r < RP; ++r) {
-                P[r] = fmaf(wr, kc[r], P[r]);
-                o2[r & 1] = fmaf(P[r], qc[r], o2[r & 1]);
-            }
-            const float o = sd * col_sum(o2[0] + o2[1]);
-            scl = sd;
-            if (part == 0) {
-                oo[(int64_t)(t0 + j) * D + col] = o;
-                ee[(int64_t)(t0 + j) * D + col] = e;
+        for (int r = 0; r < RP; ++r) {
+            P[r] = fmaf(wr, kc[r], P[r]);
+            o2[r & 1] = fmaf(P[r], qc[r], o2[r & 1]);
+        }
+        o = sd * col_sum(o2[0] + o2[1]);
+        scl = sd;
+    };
+
+    fetch(0);
+    for (int t0 = 0; t0 < n; t0 += TB) {
+        const int nb = min(TB, n - t0);
+        __syncthreads();                                                // the previous block is used up
+        if (t0 > 0) flush(t0 - TB);
+        stash();
+        __syncthreads();
+        if (t0 + TB < n) fetch(t0 + TB);
+        // the scales this block reaches if nothing folds: the last is the smallest
+        float s = scl;
+        for (int j = 0; j < nb; ++j) s = sAl[j] * s;
+        if (nb == TB && s >= 1e-20f) {
+            // lane `part` of a column keeps the outputs of tokens part, part + LPC, ... in registers, so
+            // the block's loop writes no LDS and the next tokens' reads can run ahead
+            float mo[TB / LPC], me[TB / LPC];
+#pragma unroll
+            for (int u = 0; u < TB / LPC; ++u) mo[u] = me[u] = 0.f;
+#pragma unroll
+            for (int j = 0; j < TB; ++j) {
+                float o, e;
+                token(j, o, e, std::false_type{});
+                mo[j / LPC] = part == j % LPC ? o : mo[j / LPC];
+                me[j / LPC] = part == j % LPC ? e : me[j / LPC];
             }
 #pragma unroll
-            for (int r = 0; r < RP; ++r) { kc[r] = kn[r]; qc[r] = qn[r]; }
-            vc = vn; ac = an; bc = bnx;
+            for (int u = 0; u < TB / LPC; ++u) {
+                sO[part + LPC * u][cl] = mo[u];
+                sE[part + LPC * u][cl] = me[u];
+            }
+        } else {
+            for (int j = 0; j < nb; ++j) {
+                float o, e;
+                token(j, o, e, std::true_type{});
+                float* po = part == 0 ? &sO[j][cl] : &sJunk[0][tid];    // one lane per column keeps it
+                float* pe = part == 0 ? &sE[j][cl] : &sJunk[1][tid];
+                *po = o;
+                *pe = e;
+            }
         }
     }
+    __syncthreads();
+    flush((n - 1) / TB * TB);
     if (A.S_out) {
         float* so = A.S_out + (int64_t)bh * D * D;
 #pragma unroll
@@ -383,7 +471,15 @@ hipError_t launch_hola_t(const HolaArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((hola_prep_kernel<T, D>), dim3(rgrid), dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((hola_scan_kernel<T, D>), dim3(a.BH * (D / (256 / kHolaScanLanes))), dim3(256), 0, stream, a);
+    // lanes per column of S: the fewest (least reduction work per token) whose grid still covers the
+    // compute units; each workgroup takes 256 / lanes columns
+    const int ncu = device_cus();
+    if ((int64_t)a.BH * (D / 32) >= ncu)
+        hipLaunchKernelGGL((hola_scan_kernel<T, D, 8>), dim3(a.BH * (D / 32)), dim3(256), 0, stream, a);
+    else if ((int64_t)a.BH * (D / 16) >= ncu)
+        hipLaunchKernelGGL((hola_scan_kernel<T, D, 16>), dim3(a.BH * (D / 16)), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((hola_scan_kernel<T, D, 32>), dim3(a.BH * (D / 8)), dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((hola_mag_kernel<D>), dim3(rgrid), dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;

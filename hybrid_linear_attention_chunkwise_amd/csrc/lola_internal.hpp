@@ -139,6 +139,7 @@ struct HolaArgs {
     char* ws;
     HolaLayout L;
 };
+int device_cus();   // compute units of the current device (256 if the query fails)
 hipError_t launch_hola(const HolaArgs& a, int dtype, int d, hipStream_t stream);
 
 struct InitArgs {

@@ -562,7 +562,7 @@ static int split_chunks(int nchunks, int per_chunk, int ncu, int* bounds, int ma
     return k;
 }
 
-static int device_cus() {
+int device_cus() {
     static int ncu = 0;
     if (ncu == 0) {
         int dev = 0, v = 0;

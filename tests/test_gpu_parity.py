@@ -589,7 +589,7 @@ def test_score_rule_multi_token_decode():
 # HOLA variant (hola_prefill): gated delta rule + write-magnitude cache against oracle/hola_oracle.py.
 # ------------------------------------------------------------------------------------------------
 
-def _hola_inputs(seed, B, h, n, d, dtype):
+def _hola_inputs(seed, B, h, n, d, dtype, alpha_range=(0.9, 1.0)):
     """Seeded synthetic inputs; in bf16 mode the oracle gets the same bf16-rounded q, k, v."""
     rng = np.random.default_rng(seed)
     q = rng.standard_normal((B, h, n, d)).astype(np.float32)
@@ -597,7 +597,7 @@ def _hola_inputs(seed, B, h, n, d, dtype):
     v = rng.standard_normal((B, h, n, d)).astype(np.float32)
     if dtype == "bf16":
         q, k, v = (torch.from_numpy(x).to(torch.bfloat16).float().numpy() for x in (q, k, v))
-    alpha = rng.uniform(0.9, 1.0, (B, h, n)).astype(np.float32)
+    alpha = rng.uniform(*alpha_range, (B, h, n)).astype(np.float32)
     beta = rng.uniform(0.0, 1.0, (B, h, n)).astype(np.float32)
     gq = rng.uniform(0.5, 1.5, (h, d)).astype(np.float32)
     gk = rng.uniform(0.5, 1.5, (h, d)).astype(np.float32)
@@ -651,3 +651,50 @@ def test_hola_prefill(seed, kw, dtype):
         assert np.abs(S_out[0, hh] - S_o).max() <= 1e-4 * scale
     print(f"[hola] max output err {worst:.3e}", flush=True)
     assert worst <= tol
+
+
+# The scan kernel gives each column of S 8, 16 or 32 lanes: the fewest whose grid (sequences x heads x
+# d / (256 / lanes) workgroups) still covers the 256 compute units.  These head counts reach each
+# layout at both d; the strong decay (alpha in [0.05, 0.3]) folds the state's scale into its
+# registers inside most 32-token blocks, the slow path of the scan.
+HOLA_LANE_CASES = [
+    (96, dict(d=128, B=2, h=32, n=97, C=32, w=8)),    # 8 lanes per column
+    (97, dict(d=128, B=1, h=32, n=97, C=32, w=8)),    # 16
+    (98, dict(d=128, B=1, h=3, n=97, C=32, w=8)),     # 32
+    (99, dict(d=64, B=4, h=32, n=65, C=16, w=4)),     # 8
+    (100, dict(d=64, B=2, h=32, n=65, C=16, w=4)),    # 16
+]
+
+
+@pytest.mark.parametrize("decay", ["mild", "strong"])
+@pytest.mark.parametrize("seed,kw", HOLA_LANE_CASES, ids=[f"s{s}" for s, _ in HOLA_LANE_CASES])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_hola_scan_lane_layouts(seed, kw, dtype, decay):
+    """Final state of every head against the oracle's delta rule; outputs and caches of sampled heads
+    against the whole oracle."""
+    import hybrid_linear_attention_chunkwise_amd as lola
+    from oracle import hola_oracle as HO
+    B, h, n, C, w, d = kw["B"], kw["h"], kw["n"], kw["C"], kw["w"], kw["d"]
+    arange = (0.9, 1.0) if decay == "mild" else (0.05, 0.3)
+    q, k, v, alpha, beta, gq, gk, sink, gate = _hola_inputs(seed, B, h, n, d, dtype, arange)
+    dev = torch.device("cuda:0")
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    T = lambda x, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(dt)
+    S_out = torch.empty(B, h, d, d, device=dev)
+    cpos = torch.full((B, h, w), -7, dtype=torch.int32, device=dev)
+    print(f"[hola lanes] B={B} h={h} n={n} d={d} {dtype} {decay}", flush=True)
+    y = lola.hola_prefill(T(q, tdt), T(k, tdt), T(v, tdt), T(alpha), T(beta), T(gq), T(gk), T(sink), T(gate),
+                          C, w, S_out=S_out, cache_pos=cpos)
+    torch.cuda.synchronize()
+    y, S_out, cpos = y.float().cpu().numpy(), S_out.cpu().numpy(), cpos.cpu().numpy()
+    for b in range(B):
+        for hh in range(h):
+            _, _, S_o = HO.delta_rule(q[b, hh], k[b, hh], v[b, hh], alpha[b, hh], beta[b, hh])
+            scale = max(1.0, float(np.abs(S_o).max()))
+            assert np.abs(S_out[b, hh] - S_o).max() <= 1e-4 * scale, f"state of ({b}, {hh})"
+    tol = TL.FP32_TOL if dtype == "f32" else TL.BF16_TOL
+    for b, hh in {(0, 0), (B - 1, h - 1), (B // 2, h // 2)}:
+        y_o, _, cache_o, _, _ = HO.hola_prefill(q[b, hh], k[b, hh], v[b, hh], alpha[b, hh], beta[b, hh], gq[hh],
+                                                gk[hh], float(sink[hh]), float(gate[hh]), C, w)
+        assert [int(p) for p in cpos[b, hh] if p >= 0] == cache_o, f"cache of ({b}, {hh})"
+        assert TL.row_rel_err(y[b, hh], y_o) <= tol, f"outputs of ({b}, {hh})"
