@@ -108,18 +108,19 @@ lola_status check_prefill_config(const lola_state* st, int64_t n, int32_t C) {
 
 }  // namespace
 
-static lola::HolaLayout hola_layout(int64_t BH, int64_t d, int64_t esz, int64_t n, int64_t nchunks) {
+static lola::HolaLayout hola_layout(int64_t BH, int64_t d, int64_t esz, int64_t n, int64_t C, int64_t nchunks) {
     lola::HolaLayout L;
     int64_t p = 0;
     const int64_t rows = BH * n;
-    L.qhat = p; p = rup(p + rows * d * 4, 256);
-    L.khat = p; p = rup(p + rows * d * 4, 256);
+    L.qinv = p; p = rup(p + rows * 4, 256);
+    L.kinv = p; p = rup(p + rows * 4, 256);
     L.qtil = p; p = rup(p + rows * d * esz, 256);
     L.ktil = p; p = rup(p + rows * d * esz, 256);
     L.o = p;    p = rup(p + rows * d * 4, 256);
     L.e = p;    p = rup(p + rows * d * 4, 256);
     L.m = p;    p = rup(p + rows * 4, 256);
     L.clist = p; p = rup(p + BH * nchunks * lola::kHolaMaxW * 4, 256);
+    L.tlist = p; p = rup(p + BH * nchunks * (C < lola::kHolaMaxW ? C : lola::kHolaMaxW) * 8, 256);
     L.total = p;
     return L;
 }
@@ -298,7 +299,7 @@ size_t hola_workspace_bytes(int32_t B, int32_t n_heads, int32_t d, int32_t dtype
     if (hola_check(B, n_heads, d, dtype, n, C) != LOLA_OK) return 0;
     if (n == 0) return 256;
     const int64_t nchunks = (n + C - 1) / C;
-    return (size_t)hola_layout((int64_t)B * n_heads, d, dtype == LOLA_BF16 ? 2 : 4, n, nchunks).total;
+    return (size_t)hola_layout((int64_t)B * n_heads, d, dtype == LOLA_BF16 ? 2 : 4, n, C, nchunks).total;
 }
 
 lola_status hola_prefill(int32_t B, int32_t n_heads, int32_t d, int32_t dtype, int64_t n, int32_t C, int32_t w,
@@ -317,7 +318,7 @@ lola_status hola_prefill(int32_t B, int32_t n_heads, int32_t d, int32_t dtype, i
     const int64_t BH = (int64_t)B * n_heads;
     const int nqt = (C + 63) / 64;
     if (BH * nchunks * nqt > (int64_t)INT_MAX || (BH * n + 7) / 8 > (int64_t)INT_MAX) return LOLA_EUNSUPPORTED;
-    const lola::HolaLayout L = hola_layout(BH, d, dtype == LOLA_BF16 ? 2 : 4, n, nchunks);
+    const lola::HolaLayout L = hola_layout(BH, d, dtype == LOLA_BF16 ? 2 : 4, n, C, nchunks);
     if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes < (size_t)L.total) return LOLA_EINVAL;
     lola::HolaArgs a;
     a.BH = (int)BH;

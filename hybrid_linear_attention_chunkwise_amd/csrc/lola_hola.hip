@@ -10,18 +10,20 @@
 //   3.2 Eq. (3)       y_t = o_t + sigmoid(gate) * cache read-out.
 //
 // Kernels, in launch order:
-//   prep   one pass over the tokens: unit-norm q, k for the state (fp32) and the cache path's
-//          normalised q, k (storage type), 32 lanes per row;
+//   prep   one pass over the tokens: the inverse L2 norms of q and k (the state path normalises with
+//          them while it stages rows) and the cache path's normalised q, k (storage type), 32 lanes per row;
 //   scan   the delta rule, serial in t but separable in the value dimension: one workgroup per
-//          (sequence, head, 16 columns of S), a 16-lane row per column (d/16 of its rows per lane, in
-//          registers), so S^T k and S^T q close with DPP rotations.  Keys, queries, values and gates
-//          are staged in LDS 32 tokens at a time;
+//          (sequence, head, 256 / L columns of S), L = 8, 16 or 32 lanes per column (d / L of its rows
+//          per lane, in registers), so S^T k and S^T q close with a few DPP steps.  Keys, queries, values
+//          and gates are staged in LDS 32 tokens at a time, the next block loaded while one is scanned;
 //   mag    m_t = beta_t ||e_t||, 32 lanes per row;
-//   cache  the persistent cache at every chunk start, serial in the chunks: one workgroup per (sequence,
-//          head) keeps the current cache and merges each chunk into it by exact rank (ties: older);
+//   top    each chunk's own w largest magnitudes, all chunks in parallel;
+//   cache  the persistent cache at every chunk start, serial in the chunks: one wave per (sequence,
+//          head) merges each chunk's list into the current cache by rank (ties: older);
 //   read   one workgroup per (sequence, head, chunk, 64 queries): softmax over the chunk's persistent
 //          cache and the chunk's tokens up to each query, with the sink as the initial state of the
-//          running softmax; QK^T and PV^T on MFMA with key blocks staged in LDS; adds the state read-out.
+//          running softmax; QK^T and PV^T on MFMA with key blocks staged in LDS one block ahead; adds
+//          the state read-out.
 #include "lola_common.hpp"
 #include "lola_internal.hpp"
 
@@ -60,14 +62,11 @@ __global__ __launch_bounds__(256) void hola_prep_kernel(HolaArgs A) {
         for (int sh = 1; sh < 32; sh <<= 1) ss += __shfl_xor(ss, sh, 32);
         const float inv_l2 = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;        // a zero row stays zero
         const float inv_rms = 1.0f / sqrtf(ss / (float)D + kHolaRmsEps);
-        float* hat = reinterpret_cast<float*>(wsb + (which ? A.L.khat : A.L.qhat)) + row * D + lane * PER;
         T* til = reinterpret_cast<T*>(wsb + (which ? A.L.ktil : A.L.qtil)) + row * D + lane * PER;
         const float* gam = (which ? A.gamma_k : A.gamma_q) + (int64_t)head * D + lane * PER;
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            hat[i] = x[i] * inv_l2;
-            til[i] = from_f<T>(gam[i] * x[i] * inv_rms);
-        }
+        for (int i = 0; i < PER; ++i) til[i] = from_f<T>(gam[i] * x[i] * inv_rms);
+        if (lane == 0) reinterpret_cast<float*>(wsb + (which ? A.L.kinv : A.L.qinv))[row] = inv_l2;
     }
 }
 
@@ -87,11 +86,12 @@ __global__ __launch_bounds__(256) void hola_scan_kernel(HolaArgs A) {
     constexpr int NT = 256;
     constexpr int CPW = NT / LPC;                                       // columns per workgroup
     constexpr int RP = D / LPC;                                         // rows per lane
-    constexpr int KV4 = TB * D / 4 / NT;                                // float4 of k (and of q) per thread
+    constexpr int EPV = 16 / (int)sizeof(T), PC = D / EPV;              // elements per 16-byte piece, per row
+    constexpr int KVP = TB * PC / NT;                                   // pieces of k (and of q) per thread
     constexpr int VV = TB * CPW / NT;                                   // values per thread
     constexpr int OV = TB * CPW / NT;                                   // outputs per thread and array
     static_assert(LPC == 8 || LPC == 16 || LPC == 32, "lanes per column");
-    static_assert(RP % 2 == 0 && KV4 >= 1 && VV >= 1 && D % CPW == 0, "scan tiling");
+    static_assert(RP % 2 == 0 && KVP >= 1 && VV >= 1 && D % CPW == 0, "scan tiling");
     __shared__ __align__(16) float sK[TB][D];
     __shared__ __align__(16) float sQ[TB][D];
     __shared__ float sV[TB][CPW];
@@ -123,27 +123,32 @@ __global__ __launch_bounds__(256) void hola_scan_kernel(HolaArgs A) {
         return x;
     };
     const int n = A.n;
-    const float* kh = reinterpret_cast<const float*>(A.ws + A.L.khat) + (int64_t)bh * n * D;
-    const float* qh = reinterpret_cast<const float*>(A.ws + A.L.qhat) + (int64_t)bh * n * D;
+    const T* kin = reinterpret_cast<const T*>(A.k) + (int64_t)bh * n * D;
+    const T* qin = reinterpret_cast<const T*>(A.q) + (int64_t)bh * n * D;
+    const float* kinv = reinterpret_cast<const float*>(A.ws + A.L.kinv) + (int64_t)bh * n;
+    const float* qinv = reinterpret_cast<const float*>(A.ws + A.L.qinv) + (int64_t)bh * n;
     const T* vin = reinterpret_cast<const T*>(A.v) + (int64_t)bh * n * D;
     const float* al = A.alpha + (int64_t)bh * n;
     const float* be = A.beta + (int64_t)bh * n;
     float* oo = reinterpret_cast<float*>(A.ws + A.L.o) + (int64_t)bh * n * D;
     float* ee = reinterpret_cast<float*>(A.ws + A.L.e) + (int64_t)bh * n * D;
 
-    // next block's operands in registers; a token past n reads as zero
-    float4 rk[KV4], rq[KV4];
+    // next block's operands in registers (raw k and q rows in 16-byte pieces with their tokens' inverse
+    // norms); a token past n reads as zero
+    uint4 rk[KVP], rq[KVP];
+    float rkn[KVP], rqn[KVP];
     float rv[VV], ra = 0.f, rb = 0.f;
     auto fetch = [&](int t0) {
 #pragma unroll
-        for (int i = 0; i < KV4; ++i) {
-            const int f = tid + i * NT, tk = f / (D / 4);
+        for (int i = 0; i < KVP; ++i) {
+            const int f = tid + i * NT, tk = f / PC;
             const bool in = t0 + tk < n;
-            const int64_t off = (int64_t)(in ? t0 + tk : n - 1) * D + 4 * (f % (D / 4));   // always a valid row
-            const float4 k4 = *reinterpret_cast<const float4*>(kh + off);
-            const float4 q4 = *reinterpret_cast<const float4*>(qh + off);
-            rk[i] = in ? k4 : make_float4(0.f, 0.f, 0.f, 0.f);
-            rq[i] = in ? q4 : make_float4(0.f, 0.f, 0.f, 0.f);
+            const int tt = in ? t0 + tk : n - 1;                        // always a valid row
+            const int64_t off = (int64_t)tt * D + (f % PC) * EPV;
+            rk[i] = *reinterpret_cast<const uint4*>(kin + off);
+            rq[i] = *reinterpret_cast<const uint4*>(qin + off);
+            rkn[i] = in ? kinv[tt] : 0.f;
+            rqn[i] = in ? qinv[tt] : 0.f;
         }
 #pragma unroll
         for (int i = 0; i < VV; ++i) {
@@ -156,10 +161,19 @@ __global__ __launch_bounds__(256) void hola_scan_kernel(HolaArgs A) {
     };
     auto stash = [&]() {
 #pragma unroll
-        for (int i = 0; i < KV4; ++i) {
+        for (int i = 0; i < KVP; ++i) {
             const int f = tid + i * NT;
-            *reinterpret_cast<float4*>(&sK[0][0] + 4 * f) = rk[i];
-            *reinterpret_cast<float4*>(&sQ[0][0] + 4 * f) = rq[i];
+            const T* kp = reinterpret_cast<const T*>(&rk[i]);
+            const T* qp = reinterpret_cast<const T*>(&rq[i]);
+#pragma unroll
+            for (int e4 = 0; e4 < EPV; e4 += 4) {                        // unit-norm rows: x / ||x||
+                *reinterpret_cast<float4*>(&sK[0][0] + f * EPV + e4) =
+                    make_float4(to_f(kp[e4]) * rkn[i], to_f(kp[e4 + 1]) * rkn[i], to_f(kp[e4 + 2]) * rkn[i],
+                                to_f(kp[e4 + 3]) * rkn[i]);
+                *reinterpret_cast<float4*>(&sQ[0][0] + f * EPV + e4) =
+                    make_float4(to_f(qp[e4]) * rqn[i], to_f(qp[e4 + 1]) * rqn[i], to_f(qp[e4 + 2]) * rqn[i],
+                                to_f(qp[e4 + 3]) * rqn[i]);
+            }
         }
 #pragma unroll
         for (int i = 0; i < VV; ++i) (&sV[0][0])[tid + i * NT] = rv[i];
@@ -286,60 +300,113 @@ __global__ __launch_bounds__(256) void hola_mag_kernel(HolaArgs A) {
 }
 
 // ---------------- persistent cache per chunk ----------------
-// Ranking key: larger = kept first; equal magnitudes rank the older position higher.
+// Ranking key: larger = kept first; equal magnitudes rank the older position higher.  The magnitude's
+// bits are mapped so that unsigned order is float order (with -0 taken as +0).
+__device__ __forceinline__ unsigned ordered_bits(float m) {
+    const unsigned u = __float_as_uint(m);
+    return m == 0.f ? 0x80000000u : (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_mag(unsigned long long key) {
+    const unsigned u = (unsigned)(key >> 32);
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
 __device__ __forceinline__ unsigned long long hola_key(float m, int pos) {
-    return ((unsigned long long)__float_as_uint(m) << 32) | (unsigned long long)(0xFFFFFFFFu - (unsigned)pos);
+    return ((unsigned long long)ordered_bits(m) << 32) | (unsigned long long)(0xFFFFFFFFu - (unsigned)pos);
+}
+__device__ __forceinline__ int key_pos(unsigned long long key) { return (int)(0xFFFFFFFFu - (unsigned)key); }
+
+// Each chunk's own ranking, all chunks in parallel: the w largest keys of the chunk's tokens, largest
+// first.  The persistent cache at any chunk start is the top w of the union of these lists over the
+// earlier chunks, since a token outside its own chunk's top w has w larger keys before it anyway.
+__global__ __launch_bounds__(256) void hola_chunk_top_kernel(HolaArgs A) {
+    __shared__ unsigned long long sKey[kHolaMaxC];
+    const int bh = blockIdx.x / A.nchunks, ch = blockIdx.x % A.nchunks, tid = threadIdx.x;
+    const int n = A.n, C = A.C, a = ch * C, nx = min(C, n - a), keep = min(A.w, nx);
+    const int ls = min(kHolaMaxW, C);                                   // list stride
+    const float* m = reinterpret_cast<const float*>(A.ws + A.L.m) + (int64_t)bh * n;
+    unsigned long long* out = reinterpret_cast<unsigned long long*>(A.ws + A.L.tlist) + ((int64_t)bh * A.nchunks + ch) * ls;
+    for (int i = tid; i < nx; i += 256) sKey[i] = hola_key(m[a + i], a + i);
+    __syncthreads();
+    for (int i = tid; i < nx; i += 256) {
+        const unsigned long long ki = sKey[i];
+        int above = 0;
+#pragma unroll 16
+        for (int j = 0; j < nx; ++j) above += sKey[j] > ki;
+        if (above < keep) out[above] = ki;
+    }
 }
 
-__global__ __launch_bounds__(256) void hola_cache_kernel(HolaArgs A) {
-    __shared__ int sCur[kHolaMaxW];
-    __shared__ int sCand[kHolaMaxW + kHolaMaxC];
-    __shared__ unsigned long long sKey[kHolaMaxW + kHolaMaxC];
-    __shared__ int sCount;
-    const int bh = blockIdx.x, tid = threadIdx.x;
-    const int n = A.n, C = A.C, w = A.w, nchunks = A.nchunks;
-    const float* m = reinterpret_cast<const float*>(A.ws + A.L.m) + (int64_t)bh * n;
+// Number of entries of a list sorted largest first that exceed x (x is in neither list twice).
+__device__ __forceinline__ int count_above(const unsigned long long* L, int len, unsigned long long x) {
+    int lo = 0, hi = len;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (L[mid] > x) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// The persistent cache at every chunk start, serial in the chunks: one wave per (sequence, head) keeps
+// the current cache as a key list sorted largest first and merges each chunk's own list into it by
+// rank (an entry's new index is its index plus the number of entries of the other list above it);
+// the chunk lists are loaded eight chunks at a time, one batch ahead.
+__global__ __launch_bounds__(64) void hola_cache_kernel(HolaArgs A) {
+    constexpr int NB = 8;
+    __shared__ unsigned long long sCur[2][kHolaMaxW];
+    __shared__ unsigned long long sL[NB][kHolaMaxW];
+    const int bh = blockIdx.x, lane = threadIdx.x;
+    const int n = A.n, C = A.C, w = A.w, nchunks = A.nchunks, ls = min(kHolaMaxW, C);
+    const unsigned long long* tl = reinterpret_cast<const unsigned long long*>(A.ws + A.L.tlist) + (int64_t)bh * nchunks * ls;
     int* clist = reinterpret_cast<int*>(A.ws + A.L.clist) + (int64_t)bh * nchunks * kHolaMaxW;
-    int ncur = 0;
-    for (int ch = 0; ch <= nchunks; ++ch) {
-        // the cache at the start of chunk ch (after the last chunk: the final cache)
-        if (ch < nchunks)
-            for (int j = tid; j < kHolaMaxW; j += 256) clist[(int64_t)ch * kHolaMaxW + j] = j < ncur ? sCur[j] : -1;
-        else {
-            // final cache, sorted by position, with its magnitudes
-            for (int i = tid; i < ncur; i += 256) {
-                const int p = sCur[i];
-                int before = 0;
-                for (int j = 0; j < ncur; ++j) before += sCur[j] < p;
-                if (A.cache_pos_out) A.cache_pos_out[(int64_t)bh * w + before] = p;
-                if (A.cache_score_out) A.cache_score_out[(int64_t)bh * w + before] = m[p];
-            }
-            for (int i = ncur + tid; i < w; i += 256) {
-                if (A.cache_pos_out) A.cache_pos_out[(int64_t)bh * w + i] = -1;
-                if (A.cache_score_out) A.cache_score_out[(int64_t)bh * w + i] = 0.f;
-            }
-            break;
+    auto count_of = [&](int ch) { return min(w, min(C, n - ch * C)); };
+    unsigned long long rb[NB];
+    auto fetch = [&](int c0) {
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            const int ch = c0 + u;
+            rb[u] = ch < nchunks && lane < count_of(ch) ? tl[(int64_t)ch * ls + lane] : 0ull;
         }
-        // candidates: the current cache and this chunk's tokens; keep the w largest
-        const int a = ch * C, nx = min(C, n - a);
-        const int nc = ncur + nx;
-        for (int i = tid; i < nc; i += 256) {
-            const int p = i < ncur ? sCur[i] : a + (i - ncur);
-            sCand[i] = p;
-            sKey[i] = hola_key(m[p], p);
-        }
-        if (tid == 0) sCount = 0;
+    };
+    int ncur = 0, cb = 0;
+    fetch(0);
+    for (int c0 = 0; c0 < nchunks; c0 += NB) {
+        __syncthreads();                                                // the previous batch is used up
+#pragma unroll
+        for (int u = 0; u < NB; ++u) sL[u][lane] = rb[u];
         __syncthreads();
-        const int keep = min(w, nc);
-        for (int i = tid; i < nc; i += 256) {
-            const unsigned long long ki = sKey[i];
-            int above = 0;
-#pragma unroll 16
-            for (int j = 0; j < nc; ++j) above += sKey[j] > ki;    // unrolled: the LDS reads overlap
-            if (above < keep) sCur[atomicAdd(&sCount, 1)] = sCand[i];
+        if (c0 + NB < nchunks) fetch(c0 + NB);
+        for (int u = 0; u < NB && c0 + u < nchunks; ++u) {
+            const int ch = c0 + u, nl = count_of(ch);
+            clist[(int64_t)ch * kHolaMaxW + lane] = lane < ncur ? key_pos(sCur[cb][lane]) : -1;   // the cache now
+            const unsigned long long* L = sL[u];
+            if (lane < ncur) {
+                const unsigned long long x = sCur[cb][lane];
+                const int r = lane + count_above(L, nl, x);
+                if (r < w) sCur[cb ^ 1][r] = x;
+            }
+            if (lane < nl) {
+                const unsigned long long y = L[lane];
+                const int r = lane + count_above(sCur[cb], ncur, y);
+                if (r < w) sCur[cb ^ 1][r] = y;
+            }
+            __syncthreads();
+            cb ^= 1;
+            ncur = min(w, ncur + nl);
         }
-        __syncthreads();
-        ncur = keep;
+    }
+    // the final cache, sorted by position, with its magnitudes
+    if (lane < ncur) {
+        const unsigned long long x = sCur[cb][lane];
+        const int p = key_pos(x);
+        int before = 0;
+        for (int j = 0; j < ncur; ++j) before += key_pos(sCur[cb][j]) < p;
+        if (A.cache_pos_out) A.cache_pos_out[(int64_t)bh * w + before] = p;
+        if (A.cache_score_out) A.cache_score_out[(int64_t)bh * w + before] = key_mag(x);
+    }
+    for (int i = ncur + lane; i < w; i += 64) {
+        if (A.cache_pos_out) A.cache_pos_out[(int64_t)bh * w + i] = -1;
+        if (A.cache_score_out) A.cache_score_out[(int64_t)bh * w + i] = 0.f;
     }
 }
 
@@ -387,22 +454,67 @@ __global__ __launch_bounds__(256) void hola_read_kernel(HolaArgs A) {
 #pragma unroll
     for (int J = 0; J < JT; ++J) O[J] = zero4();
 
-    for (int kb = 0; kb * KB < NK; ++kb) {
-        __syncthreads();                                                // the previous block is used up
-        for (int i = tid; i < KB * (D / EPV); i += 256) {              // keys, 16-byte pieces
-            const int j = i / (D / EPV), p = i % (D / EPV);
-            const int kk = kb * KB + j;
-            uint4 x = make_uint4(0, 0, 0, 0);
-            if (kk < NK) x = *reinterpret_cast<const uint4*>(ktil + (int64_t)key_pos(kk) * D + p * EPV);
-            *reinterpret_cast<uint4*>(sK + j * K_LD + p * EPV) = x;
+    // key blocks are staged through registers one block ahead: keys row-major in 16-byte pieces;
+    // values transposed (dimension-major, the A operand of PV^T), each thread loading KPW = 4 / sizeof(T)
+    // keys' pieces of the same dimensions so that their elements pair into 32-bit LDS words
+    constexpr int KPW = 4 / (int)sizeof(T), PC = D / EPV;              // keys per word, pieces per row
+    constexpr int KPT = KB * PC / 256;                                  // key pieces per thread
+    constexpr int VPT = KB / KPW * PC / 256;                            // (key word, piece) items per thread
+    static_assert(KPT >= 1 && VPT >= 1, "read staging");
+    uint4 rk[KPT], rv[VPT][KPW];
+    auto clamp_pos = [&](int kk) { return key_pos(kk < NK ? kk : NK - 1); };   // NK >= 1
+    auto fetch = [&](int kb) {
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) {
+            const int i = tid + 256 * u, kk = kb * KB + i / PC;
+            const uint4 x = *reinterpret_cast<const uint4*>(ktil + (int64_t)clamp_pos(kk) * D + (i % PC) * EPV);
+            rk[u] = kk < NK ? x : make_uint4(0, 0, 0, 0);
         }
-        for (int i = tid; i < KB * D; i += 256) {                      // values, transposed
-            const int j = i % KB, d = i / KB;
-            const int kk = kb * KB + j;
-            sVT[d * VT_LD + j] = kk < NK ? vin[(int64_t)key_pos(kk) * D + d] : from_f<T>(0.f);
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+            const int i = tid + 256 * u, jw = i % (KB / KPW), p = i / (KB / KPW);
+#pragma unroll
+            for (int h = 0; h < KPW; ++h) {
+                const int kk = kb * KB + KPW * jw + h;
+                const uint4 x = *reinterpret_cast<const uint4*>(vin + (int64_t)clamp_pos(kk) * D + p * EPV);
+                rv[u][h] = kk < NK ? x : make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+    auto stash = [&](int kb) {
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) {
+            const int i = tid + 256 * u;
+            *reinterpret_cast<uint4*>(sK + (i / PC) * K_LD + (i % PC) * EPV) = rk[u];
+        }
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+            const int i = tid + 256 * u, jw = i % (KB / KPW), p = i / (KB / KPW);
+            const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&rv[u][0]);
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) {
+                uint32_t word;
+                if constexpr (KPW == 2) {
+                    const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&rv[u][1]);
+                    const uint32_t lo = (w0[e / 2] >> (16 * (e % 2))) & 0xFFFFu;   // key 2 jw, dimension p EPV + e
+                    const uint32_t hi = (w1[e / 2] >> (16 * (e % 2))) & 0xFFFFu;   // key 2 jw + 1
+                    word = lo | (hi << 16);
+                } else {
+                    word = w0[e];
+                }
+                *reinterpret_cast<uint32_t*>(sVT + (p * EPV + e) * VT_LD + KPW * jw) = word;
+            }
         }
         for (int j = tid; j < KB; j += 256) sPos[j] = kb * KB + j < NK ? key_pos(kb * KB + j) : -1;
+    };
+
+    const int nkb = (NK + KB - 1) / KB;
+    fetch(0);
+    for (int kb = 0; kb < nkb; ++kb) {
+        __syncthreads();                                                // the previous block is used up
+        stash(kb);
         __syncthreads();
+        if (kb + 1 < nkb) fetch(kb + 1);
         if (q0 + 16 * w < b) {
             f4 st[KB / 16];
 #pragma unroll
@@ -483,7 +595,11 @@ hipError_t launch_hola_t(const HolaArgs& a, hipStream_t stream) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((hola_mag_kernel<D>), dim3(rgrid), dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(hola_cache_kernel, dim3(a.BH), dim3(256), 0, stream, a);
+    if (a.w > 0) {
+        hipLaunchKernelGGL(hola_chunk_top_kernel, dim3((unsigned)((int64_t)a.BH * a.nchunks)), dim3(256), 0, stream, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(hola_cache_kernel, dim3(a.BH), dim3(64), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((hola_read_kernel<T, D>), dim3((unsigned)((int64_t)a.BH * a.nchunks * a.nqt)), dim3(256), 0,
                        stream, a);

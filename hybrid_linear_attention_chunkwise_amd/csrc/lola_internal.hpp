@@ -114,11 +114,13 @@ constexpr int kCollideRows = 2;           // map rows per workgroup (their H^T s
 constexpr int kHolaMaxW = 64;     // largest persistent cache
 constexpr int kHolaMaxC = 1024;   // largest chunk
 struct HolaLayout {               // byte offsets of whole arrays in the workspace
-    int64_t qhat, khat;           // [BH][n][d] fp32: unit-norm queries and keys of the state path
+    int64_t qinv, kinv;           // [BH][n] fp32: 1 / ||x||_2 of queries and keys (0 for a zero row)
     int64_t qtil, ktil;           // [BH][n][d] T   : RMS-normalised, gamma-scaled queries and keys
     int64_t o, e;                 // [BH][n][d] fp32: state read-out S_t^T q_t, residual e_t
     int64_t m;                    // [BH][n]    fp32: write magnitude beta_t ||e_t||
     int64_t clist;                // [BH][nchunks][kHolaMaxW] int32: persistent cache at each chunk start
+    int64_t tlist;                // [BH][nchunks][min(kHolaMaxW, C)] u64: each chunk's own top-w ranking
+                                  //   keys, largest first
     int64_t total;
 };
 struct HolaArgs {
