@@ -120,6 +120,8 @@ static lola::HolaLayout hola_layout(int64_t BH, int64_t d, int64_t esz, int64_t 
     L.e = p;    p = rup(p + rows * d * 4, 256);
     L.m = p;    p = rup(p + rows * 4, 256);
     L.clist = p; p = rup(p + BH * nchunks * lola::kHolaMaxW * 4, 256);
+    L.blk = p;  p = rup(p + BH * ((n + lola::kHolaBT - 1) / lola::kHolaBT) * (int64_t)sizeof(lola::HolaBlock), 256);
+    L.sink = p; p = rup(p + 2 * 64 * 4, 256);
     L.tlist = p; p = rup(p + BH * nchunks * (C < lola::kHolaMaxW ? C : lola::kHolaMaxW) * 8, 256);
     L.total = p;
     return L;
@@ -328,6 +330,7 @@ lola_status hola_prefill(int32_t B, int32_t n_heads, int32_t d, int32_t dtype, i
     a.w = w;
     a.nchunks = (int)nchunks;
     a.nqt = nqt;
+    a.nblk = (int)((n + lola::kHolaBT - 1) / lola::kHolaBT);
     a.q = q; a.k = k; a.v = v;
     a.alpha = alpha; a.beta = beta;
     a.gamma_q = gamma_q; a.gamma_k = gamma_k;

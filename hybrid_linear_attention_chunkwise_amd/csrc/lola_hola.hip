@@ -27,7 +27,6 @@
 #include "lola_common.hpp"
 #include "lola_internal.hpp"
 
-#include <type_traits>
 
 namespace lola {
 
@@ -70,216 +69,255 @@ __global__ __launch_bounds__(256) void hola_prep_kernel(HolaArgs A) {
     }
 }
 
-// ---------------- scan ----------------
+// ---------------- blocked delta rule ----------------
+// 16x16x4 fp32 MFMA: acc += A (16 x 4) B (4 x 16); lane (g, r) gives A[r][g], lane (g, c) gives B[g][c],
+// and lane (g, c) of the accumulator holds rows 4g .. 4g + 3 of column c.  A product over 16 (or more)
+// k indices runs as steps s = 0..3 with k = 4g + s, so an accumulator's element s is directly the B
+// operand of step s.
+__device__ __forceinline__ void mfma4(f4& acc, float a, float b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+}
 
-// The delta rule is serial in t but separable in the value dimension: column c of S only needs k, q,
-// alpha, beta and v_c.  One workgroup of four waves takes 256 / LPC columns of one (sequence, head); a
-// column belongs to LPC lanes of one wave, each lane holding d / LPC of its rows in registers, so S^T k
-// and S^T q close with a few DPP steps and the per-token chain stays short.  S = scl * P: the decay
-// multiplies the scalar scl, so the write costs one FMA per element (P += (beta e / scl) k); P is
-// rescaled into S before scl gets small.  Tokens are staged in LDS TB at a time; the next block's
-// operands are loaded into registers while the current block is scanned, and the outputs of a block
-// leave through LDS as whole rows.
-template <typename T, int D, int LPC>
-__global__ __launch_bounds__(256) void hola_scan_kernel(HolaArgs A) {
-    constexpr int TB = 32;                                              // tokens staged at a time
-    constexpr int NT = 256;
-    constexpr int CPW = NT / LPC;                                       // columns per workgroup
-    constexpr int RP = D / LPC;                                         // rows per lane
-    constexpr int EPV = 16 / (int)sizeof(T), PC = D / EPV;              // elements per 16-byte piece, per row
-    constexpr int KVP = TB * PC / NT;                                   // pieces of k (and of q) per thread
-    constexpr int VV = TB * CPW / NT;                                   // values per thread
-    constexpr int OV = TB * CPW / NT;                                   // outputs per thread and array
-    static_assert(LPC == 8 || LPC == 16 || LPC == 32, "lanes per column");
-    static_assert(RP % 2 == 0 && KVP >= 1 && VV >= 1 && D % CPW == 0, "scan tiling");
-    __shared__ __align__(16) float sK[TB][D];
-    __shared__ __align__(16) float sQ[TB][D];
-    __shared__ float sV[TB][CPW];
-    __shared__ float sO[TB][CPW], sE[TB][CPW];
-    __shared__ float sJunk[2][NT];                                      // the stores of the other lanes
-    __shared__ float sAl[TB], sBe[TB];
-    const int bh = blockIdx.x / (D / CPW), cb = CPW * (blockIdx.x % (D / CPW));   // first column of the part
-    const int tid = threadIdx.x;
-    const int cl = tid / LPC;                                           // column within the part
-    const int part = tid % LPC;
-    const int col = cb + cl, row0 = part * RP;
-    // a column's lanes: half a DPP row, one row, or two rows paired by a lane swap; every lane gets the sum
-    auto col_sum = [](float x) {
-        if constexpr (LPC == 8) {
-            x += dpp_mov<0xB1>(x);    // quad_perm [1,0,3,2]
-            x += dpp_mov<0x4E>(x);    // quad_perm [2,3,0,1]
-            x += dpp_mov<0x141>(x);   // row_half_mirror: the other quad of the eight lanes
-        } else {
-            x += dpp_mov<0x128>(x);   // row_ror:8
-            x += dpp_mov<0x124>(x);   // row_ror:4
-            x += dpp_mov<0x122>(x);   // row_ror:2
-            x += dpp_mov<0x121>(x);   // row_ror:1
-            if constexpr (LPC == 32) {
-                float a, b;
-                pair16(x, a, b);
-                x = a + b;
-            }
-        }
-        return x;
-    };
-    const int n = A.n;
+// Per-block matrices, all blocks in parallel: one wave per block of 16 tokens.  Gram products K K^T and
+// Q K^T on MFMA (the 16 x 4 pieces of a row serve as both operands), decay products taken directly
+// (no ratio of prefix products, which could underflow), T by forward substitution, one column per lane.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void hola_block_kernel(HolaArgs A) {
+    constexpr int BT = kHolaBT;
+    __shared__ float sM[4][2][BT][BT + 1];                              // per wave: A, then T; Mq
+    __shared__ float sAB[4][2][BT];                                      // alpha, beta
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 4, c = l & 15;
+    const int64_t gb = (int64_t)blockIdx.x * 4 + w;                     // (sequence-head, block)
+    if (gb >= (int64_t)A.BH * A.nblk) return;                           // whole wave; no workgroup barrier below
+    const int bh = (int)(gb / A.nblk), ib = (int)(gb % A.nblk);
+    const int n = A.n, t0 = ib * BT;
     const T* kin = reinterpret_cast<const T*>(A.k) + (int64_t)bh * n * D;
     const T* qin = reinterpret_cast<const T*>(A.q) + (int64_t)bh * n * D;
     const float* kinv = reinterpret_cast<const float*>(A.ws + A.L.kinv) + (int64_t)bh * n;
     const float* qinv = reinterpret_cast<const float*>(A.ws + A.L.qinv) + (int64_t)bh * n;
-    const T* vin = reinterpret_cast<const T*>(A.v) + (int64_t)bh * n * D;
-    const float* al = A.alpha + (int64_t)bh * n;
-    const float* be = A.beta + (int64_t)bh * n;
-    float* oo = reinterpret_cast<float*>(A.ws + A.L.o) + (int64_t)bh * n * D;
-    float* ee = reinterpret_cast<float*>(A.ws + A.L.e) + (int64_t)bh * n * D;
-
-    // next block's operands in registers (raw k and q rows in 16-byte pieces with their tokens' inverse
-    // norms); a token past n reads as zero
-    uint4 rk[KVP], rq[KVP];
-    float rkn[KVP], rqn[KVP];
-    float rv[VV], ra = 0.f, rb = 0.f;
-    auto fetch = [&](int t0) {
+    // token c of the block: unit key and query, pieces 16 kk + 4g .. + 3
+    const int tc = t0 + c;
+    const bool in = tc < n;
+    const int tv = in ? tc : n - 1;
+    const float kn = in ? kinv[tv] : 0.f, qn = in ? qinv[tv] : 0.f;
+    f4 G = zero4(), QK = zero4();
 #pragma unroll
-        for (int i = 0; i < KVP; ++i) {
-            const int f = tid + i * NT, tk = f / PC;
-            const bool in = t0 + tk < n;
-            const int tt = in ? t0 + tk : n - 1;                        // always a valid row
-            const int64_t off = (int64_t)tt * D + (f % PC) * EPV;
-            rk[i] = *reinterpret_cast<const uint4*>(kin + off);
-            rq[i] = *reinterpret_cast<const uint4*>(qin + off);
-            rkn[i] = in ? kinv[tt] : 0.f;
-            rqn[i] = in ? qinv[tt] : 0.f;
+    for (int kk = 0; kk < D / 16; ++kk) {
+        float kx[4], qx[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            kx[s] = to_f(kin[(int64_t)tv * D + 16 * kk + 4 * g + s]) * kn;
+            qx[s] = to_f(qin[(int64_t)tv * D + 16 * kk + 4 * g + s]) * qn;
         }
 #pragma unroll
-        for (int i = 0; i < VV; ++i) {
-            const int f = tid + i * NT, tk = f / CPW;
-            const bool in = t0 + tk < n;
-            const float x = to_f(vin[(int64_t)(in ? t0 + tk : n - 1) * D + cb + f % CPW]);
-            rv[i] = in ? x : 0.f;
-        }
-        if (tid < TB && t0 + tid < n) { ra = al[t0 + tid]; rb = be[t0 + tid]; }
-    };
-    auto stash = [&]() {
-#pragma unroll
-        for (int i = 0; i < KVP; ++i) {
-            const int f = tid + i * NT;
-            const T* kp = reinterpret_cast<const T*>(&rk[i]);
-            const T* qp = reinterpret_cast<const T*>(&rq[i]);
-#pragma unroll
-            for (int e4 = 0; e4 < EPV; e4 += 4) {                        // unit-norm rows: x / ||x||
-                *reinterpret_cast<float4*>(&sK[0][0] + f * EPV + e4) =
-                    make_float4(to_f(kp[e4]) * rkn[i], to_f(kp[e4 + 1]) * rkn[i], to_f(kp[e4 + 2]) * rkn[i],
-                                to_f(kp[e4 + 3]) * rkn[i]);
-                *reinterpret_cast<float4*>(&sQ[0][0] + f * EPV + e4) =
-                    make_float4(to_f(qp[e4]) * rqn[i], to_f(qp[e4 + 1]) * rqn[i], to_f(qp[e4 + 2]) * rqn[i],
-                                to_f(qp[e4 + 3]) * rqn[i]);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < VV; ++i) (&sV[0][0])[tid + i * NT] = rv[i];
-        if (tid < TB) { sAl[tid] = ra; sBe[tid] = rb; }
-    };
-    auto flush = [&](int t0) {                                          // block t0's outputs, whole rows
-#pragma unroll
-        for (int i = 0; i < OV; ++i) {
-            const int f = tid + i * NT, tk = f / CPW;
-            if (t0 + tk < n) {
-                const int64_t off = (int64_t)(t0 + tk) * D + cb + f % CPW;
-                oo[off] = (&sO[0][0])[f];
-                ee[off] = (&sE[0][0])[f];
-            }
-        }
-    };
-
-    float P[RP];                                                        // P[r] = S(row0 + r, col) / scl
-#pragma unroll
-    for (int r = 0; r < RP; ++r) P[r] = 0.f;
-    float scl = 1.f;
-    // one token: returns the column's read-out o and residual e.  FOLD: check whether scl must be folded
-    // into P first (a block whose scales all stay above the threshold skips the check, which keeps its
-    // tokens in one basic block)
-    auto token = [&](int j, float& o, float& e, auto fold_tag) {
-        constexpr bool FOLD = decltype(fold_tag)::value;
-        float kc[RP], qc[RP];
-#pragma unroll
-        for (int r = 0; r < RP; r += 2) {
-            const float2 k2 = *reinterpret_cast<const float2*>(&sK[j][row0 + r]);
-            const float2 q2 = *reinterpret_cast<const float2*>(&sQ[j][row0 + r]);
-            kc[r] = k2.x; kc[r + 1] = k2.y;
-            qc[r] = q2.x; qc[r + 1] = q2.y;
-        }
-        const float vc = sV[j][cl], ac = sAl[j], bc = sBe[j];
-        float u2[2] = {0.f, 0.f};
-#pragma unroll
-        for (int r = 0; r < RP; ++r) u2[r & 1] = fmaf(P[r], kc[r], u2[r & 1]);
-        const float sp = ac * scl;                                      // alpha S^T k = sp * (P^T k)
-        if constexpr (FOLD) {
-            if (sp < 1e-20f) {                                          // fold the scale into P (S unchanged)
-#pragma unroll
-                for (int r = 0; r < RP; ++r) P[r] *= scl;
-                scl = 1.f;
-            }
-        }
-        const float sd = ac * scl;                                      // scale of the decayed state
-        const float rs = bc * __builtin_amdgcn_rcpf(sd);                // off the chain: beta / scale
-        e = fmaf(-sp, col_sum(u2[0] + u2[1]), vc);                      // v - alpha S^T k
-        const float wr = rs * e;                                        // the write in P's scale
-        float o2[2] = {0.f, 0.f};
-#pragma unroll
-        for (int r = 0; r < RP; ++r) {
-            P[r] = fmaf(wr, kc[r], P[r]);
-            o2[r & 1] = fmaf(P[r], qc[r], o2[r & 1]);
-        }
-        o = sd * col_sum(o2[0] + o2[1]);
-        scl = sd;
-    };
-
-    fetch(0);
-    for (int t0 = 0; t0 < n; t0 += TB) {
-        const int nb = min(TB, n - t0);
-        __syncthreads();                                                // the previous block is used up
-        if (t0 > 0) flush(t0 - TB);
-        stash();
-        __syncthreads();
-        if (t0 + TB < n) fetch(t0 + TB);
-        // the scales this block reaches if nothing folds: the last is the smallest
-        float s = scl;
-        for (int j = 0; j < nb; ++j) s = sAl[j] * s;
-        if (nb == TB && s >= 1e-20f) {
-            // lane `part` of a column keeps the outputs of tokens part, part + LPC, ... in registers, so
-            // the block's loop writes no LDS and the next tokens' reads can run ahead
-            float mo[TB / LPC], me[TB / LPC];
-#pragma unroll
-            for (int u = 0; u < TB / LPC; ++u) mo[u] = me[u] = 0.f;
-#pragma unroll
-            for (int j = 0; j < TB; ++j) {
-                float o, e;
-                token(j, o, e, std::false_type{});
-                mo[j / LPC] = part == j % LPC ? o : mo[j / LPC];
-                me[j / LPC] = part == j % LPC ? e : me[j / LPC];
-            }
-#pragma unroll
-            for (int u = 0; u < TB / LPC; ++u) {
-                sO[part + LPC * u][cl] = mo[u];
-                sE[part + LPC * u][cl] = me[u];
-            }
-        } else {
-            for (int j = 0; j < nb; ++j) {
-                float o, e;
-                token(j, o, e, std::true_type{});
-                float* po = part == 0 ? &sO[j][cl] : &sJunk[0][tid];    // one lane per column keeps it
-                float* pe = part == 0 ? &sE[j][cl] : &sJunk[1][tid];
-                *po = o;
-                *pe = e;
-            }
+        for (int s = 0; s < 4; ++s) {
+            mfma4(G, kx[s], kx[s]);                                     // G[i][j] = k_i . k_j
+            mfma4(QK, qx[s], kx[s]);                                    // QK[i][j] = q_i . k_j
         }
     }
-    __syncthreads();
-    flush((n - 1) / TB * TB);
+    if (l < BT) {
+        sAB[w][0][l] = t0 + l < n ? A.alpha[(int64_t)bh * n + t0 + l] : 1.f;   // past n: no decay, no write
+        sAB[w][1][l] = t0 + l < n ? A.beta[(int64_t)bh * n + t0 + l] : 0.f;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    // ratio(i, j) = prod_{j < l <= i} alpha_l;  lane (g, c) holds rows i = 4g + e, column j = c
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int i = 4 * g + e, j = c;
+        float r = 1.f;
+        for (int m = j + 1; m <= i; ++m) r *= sAB[w][0][m];
+        const float bj = sAB[w][1][j];
+        sM[w][0][i][j] = j < i ? r * bj * G[e] : 0.f;                  // A (strictly lower)
+        sM[w][1][i][j] = j <= i ? r * bj * QK[e] : 0.f;                // Mq (lower, with the diagonal)
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    HolaBlock* out = reinterpret_cast<HolaBlock*>(A.ws + A.L.blk) + gb;
+    // T = (I + A)^{-1}: lane c < 16 solves column c by forward substitution
+    float tcol[BT];
+    if (l < BT) {
+#pragma unroll
+        for (int i = 0; i < BT; ++i) {
+            float x = i == l ? 1.f : 0.f;
+#pragma unroll
+            for (int j = 0; j < i; ++j) x = fmaf(-sM[w][0][i][j], tcol[j], x);
+            tcol[i] = x;
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    if (l < BT) {
+#pragma unroll
+        for (int i = 0; i < BT; ++i) sM[w][0][i][l] = tcol[i];         // T overwrites A
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    // operand layout: lane (g, r) holds row r, columns 4g .. 4g + 3
+    *reinterpret_cast<float4*>(out->Tp[l]) =
+        make_float4(sM[w][0][c][4 * g], sM[w][0][c][4 * g + 1], sM[w][0][c][4 * g + 2], sM[w][0][c][4 * g + 3]);
+    *reinterpret_cast<float4*>(out->Mp[l]) =
+        make_float4(sM[w][1][c][4 * g], sM[w][1][c][4 * g + 1], sM[w][1][c][4 * g + 2], sM[w][1][c][4 * g + 3]);
+    if (l < BT) {
+        float gm = 1.f, wt = sAB[w][1][l];
+        for (int m = 0; m <= l; ++m) gm *= sAB[w][0][m];
+        for (int m = l + 1; m < BT; ++m) wt *= sAB[w][0][m];
+        out->gam[l] = gm;
+        out->wgt[l] = wt;
+        if (l == BT - 1) out->glast = gm;
+    }
+}
+
+// The serial part, block by block: one workgroup of four waves per (sequence, head, 16 value columns),
+// S[:, columns] in MFMA accumulators, each wave holding d / 64 tiles of 16 rows.  Per block, each wave
+// forms its rows' share of K S and Q S; the shares meet in LDS (the one barrier of the block); then
+// every wave forms E and O (the same arithmetic in each, so all hold identical values) and updates
+// its own rows of S.  A block's operands are loaded into registers while the previous block runs.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void hola_scan_kernel(HolaArgs A) {
+    constexpr int BT = kHolaBT, TPW = D / 64;                          // row tiles per wave
+    __shared__ f4 sX[2][4][2][64];                                      // [parity][wave][K S | Q S][lane]
+    __shared__ float sKT[4][BT][TPW * 16 + 4];                          // each wave's unit keys, its rows
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 4, c = l & 15;
+    const int bh = blockIdx.x / (D / 16), cb = 16 * (blockIdx.x % (D / 16));
+    const int n = A.n, nblk = A.nblk;
+    const T* kin = reinterpret_cast<const T*>(A.k) + (int64_t)bh * n * D;
+    const T* qin = reinterpret_cast<const T*>(A.q) + (int64_t)bh * n * D;
+    const T* vin = reinterpret_cast<const T*>(A.v) + (int64_t)bh * n * D;
+    const float* kinv = reinterpret_cast<const float*>(A.ws + A.L.kinv) + (int64_t)bh * n;
+    const float* qinv = reinterpret_cast<const float*>(A.ws + A.L.qinv) + (int64_t)bh * n;
+    const HolaBlock* blk = reinterpret_cast<const HolaBlock*>(A.ws + A.L.blk) + (int64_t)bh * nblk;
+    float* oo = reinterpret_cast<float*>(A.ws + A.L.o) + (int64_t)bh * n * D;
+    float* ee = reinterpret_cast<float*>(A.ws + A.L.e) + (int64_t)bh * n * D;
+    float* sink = reinterpret_cast<float*>(A.ws + A.L.sink);
+
+    // a block's operands as loaded (raw storage type; converted where they are used, so that the loads
+    // of the next block stay in flight while a block runs)
+    // four elements of a row as 32-bit words: 2 (bf16) or 4 (fp32)
+    constexpr int NWD = 4 * (int)sizeof(T) / 4;
+    struct alignas(4 * sizeof(T)) Raw4 { uint32_t u[NWD]; };
+    auto elem = [](const Raw4& r, int s) {
+        if constexpr (sizeof(T) == 2) return __uint_as_float(s & 1 ? r.u[s >> 1] & 0xFFFF0000u : r.u[s >> 1] << 16);
+        else return __uint_as_float(r.u[s]);
+    };
+    struct Ops {
+        Raw4 ka[TPW], qa[TPW];                                          // token c: k, q at rows 16 rt + 4g ..
+        float kn, qn;                                                   // its inverse norms
+        T v[4];                                                         // V[4g + e][column c]
+        float4 tp, mp, gam, wgt;
+        float glast;
+    };
+    auto fetch = [&](int ib, Ops& o) {
+        const int t0 = ib * BT, tc = t0 + c;
+        const int tv = tc < n ? tc : n - 1;                             // always a valid row
+        o.kn = kinv[tv];
+        o.qn = qinv[tv];
+#pragma unroll
+        for (int tp = 0; tp < TPW; ++tp) {
+            const int r0 = 16 * (w * TPW + tp) + 4 * g;
+            o.ka[tp] = *reinterpret_cast<const Raw4*>(kin + (int64_t)tv * D + r0);
+            o.qa[tp] = *reinterpret_cast<const Raw4*>(qin + (int64_t)tv * D + r0);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int t = t0 + 4 * g + e;
+            o.v[e] = vin[(int64_t)(t < n ? t : n - 1) * D + cb + c];
+        }
+        const HolaBlock* b = blk + ib;
+        o.tp = *reinterpret_cast<const float4*>(b->Tp[l]);
+        o.mp = *reinterpret_cast<const float4*>(b->Mp[l]);
+        o.gam = *reinterpret_cast<const float4*>(&b->gam[4 * g]);
+        o.wgt = *reinterpret_cast<const float4*>(&b->wgt[4 * g]);
+        o.glast = b->glast;
+    };
+
+    f4 S[TPW];
+#pragma unroll
+    for (int tp = 0; tp < TPW; ++tp) S[tp] = zero4();
+    auto step = [&](int ib, const Ops& cur) {
+        // this wave's rows of K S and Q S; its unit keys go to LDS for K^T below
+        const bool cin = ib * BT + c < n;                               // token c exists
+        const float kn = cin ? cur.kn : 0.f, qn = cin ? cur.qn : 0.f;
+        f4 R = zero4(), QS = zero4();
+#pragma unroll
+        for (int tp = 0; tp < TPW; ++tp) {
+            float ka[4], qa[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                ka[s] = elem(cur.ka[tp], s) * kn;                       // unit key and query
+                qa[s] = elem(cur.qa[tp], s) * qn;
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                mfma4(R, ka[s], S[tp][s]);
+                mfma4(QS, qa[s], S[tp][s]);
+            }
+            *reinterpret_cast<float4*>(&sKT[w][c][16 * tp + 4 * g]) = make_float4(ka[0], ka[1], ka[2], ka[3]);
+        }
+        sX[ib & 1][w][0][l] = R;
+        sX[ib & 1][w][1][l] = QS;
+        __syncthreads();
+        f4 Rt = zero4(), Qt = zero4();
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) {
+            Rt += sX[ib & 1][ww][0][l];
+            Qt += sX[ib & 1][ww][1][l];
+        }
+        const float gm[4] = {cur.gam.x, cur.gam.y, cur.gam.z, cur.gam.w};
+        const float wg[4] = {cur.wgt.x, cur.wgt.y, cur.wgt.z, cur.wgt.w};
+        const float tpv[4] = {cur.tp.x, cur.tp.y, cur.tp.z, cur.tp.w};
+        const float mpv[4] = {cur.mp.x, cur.mp.y, cur.mp.z, cur.mp.w};
+        // E = T (V - diag(gam) K S);  O = diag(gam) Q S + M E
+        f4 E = zero4(), O;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const float vv = ib * BT + 4 * g + s < n ? to_f(cur.v[s]) : 0.f;
+            mfma4(E, tpv[s], fmaf(-gm[s], Rt[s], vv));
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) O[e] = gm[e] * Qt[e];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) mfma4(O, mpv[s], E[s]);
+        // S = glast S + K^T diag(wgt) E on this wave's rows
+#pragma unroll
+        for (int tp = 0; tp < TPW; ++tp) {
+            S[tp] *= cur.glast;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) mfma4(S[tp], sKT[w][4 * g + s][16 * tp + c], wg[s] * E[s]);
+        }
+        // every wave holds the same E and O: wave w stores rows 4g + w, without a branch (a token past n
+        // writes to the sink), so the waits for the next block's loads stay exact
+        float ov = O[0], ev = E[0];
+#pragma unroll
+        for (int e = 1; e < 4; ++e) {
+            ov = w == e ? O[e] : ov;
+            ev = w == e ? E[e] : ev;
+        }
+        const int t = ib * BT + 4 * g + w;
+        float* po = t < n ? oo + (int64_t)t * D + cb + c : sink + l;
+        float* pe = t < n ? ee + (int64_t)t * D + cb + c : sink + 64 + l;
+        *po = ov;
+        *pe = ev;
+    };
+    // two operand sets in turn: a block's loads were issued one block earlier, with no copies between.
+    // The loads are unconditional (past the last block they repeat it), so the waits for them stay exact.
+    Ops o0, o1;
+    fetch(0, o0);
+    for (int ib = 0; ib < nblk; ib += 2) {
+        fetch(min(ib + 1, nblk - 1), o1);
+        __builtin_amdgcn_sched_barrier(0);                              // issue the loads before the step
+        step(ib, o0);
+        if (ib + 1 >= nblk) break;
+        fetch(min(ib + 2, nblk - 1), o0);
+        __builtin_amdgcn_sched_barrier(0);
+        step(ib + 1, o1);
+    }
     if (A.S_out) {
         float* so = A.S_out + (int64_t)bh * D * D;
 #pragma unroll
-        for (int r = 0; r < RP; ++r) so[(int64_t)(row0 + r) * D + col] = P[r] * scl;
+        for (int tp = 0; tp < TPW; ++tp)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) so[(int64_t)(16 * (w * TPW + tp) + 4 * g + e) * D + cb + c] = S[tp][e];
     }
 }
 
@@ -583,15 +621,10 @@ hipError_t launch_hola_t(const HolaArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((hola_prep_kernel<T, D>), dim3(rgrid), dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // lanes per column of S: the fewest (least reduction work per token) whose grid still covers the
-    // compute units; each workgroup takes 256 / lanes columns
-    const int ncu = device_cus();
-    if ((int64_t)a.BH * (D / 32) >= ncu)
-        hipLaunchKernelGGL((hola_scan_kernel<T, D, 8>), dim3(a.BH * (D / 32)), dim3(256), 0, stream, a);
-    else if ((int64_t)a.BH * (D / 16) >= ncu)
-        hipLaunchKernelGGL((hola_scan_kernel<T, D, 16>), dim3(a.BH * (D / 16)), dim3(256), 0, stream, a);
-    else
-        hipLaunchKernelGGL((hola_scan_kernel<T, D, 32>), dim3(a.BH * (D / 8)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((hola_block_kernel<T, D>), dim3((unsigned)(((int64_t)a.BH * a.nblk + 3) / 4)), dim3(256), 0,
+                       stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((hola_scan_kernel<T, D>), dim3(a.BH * (D / 16)), dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((hola_mag_kernel<D>), dim3(rgrid), dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -119,12 +119,29 @@ struct HolaLayout {               // byte offsets of whole arrays in the workspa
     int64_t o, e;                 // [BH][n][d] fp32: state read-out S_t^T q_t, residual e_t
     int64_t m;                    // [BH][n]    fp32: write magnitude beta_t ||e_t||
     int64_t clist;                // [BH][nchunks][kHolaMaxW] int32: persistent cache at each chunk start
+    int64_t blk;                  // [BH][ceil(n / 16)] HolaBlock: the delta rule's per-block matrices
+    int64_t sink;                 // [2][64] fp32: where the scan's stores for tokens past n go
     int64_t tlist;                // [BH][nchunks][min(kHolaMaxW, C)] u64: each chunk's own top-w ranking
                                   //   keys, largest first
     int64_t total;
 };
+// The delta rule over a block of 16 tokens (state S before the block, gates alpha, beta, unit keys and
+// queries K, Q, values V):  E = T (V - diag(gam) K S),  O = diag(gam) Q S + M E,
+// S' = glast S + K^T diag(wgt) E,  with gam_i = prod_{l <= i} alpha_l, T = (I + A)^{-1},
+// A_ij = (prod_{j < l <= i} alpha_l) beta_j k_i.k_j (j < i), M_ij = (prod_{j < l <= i} alpha_l) beta_j q_i.k_j
+// (j <= i), wgt_j = (prod_{l > j} alpha_l) beta_j, glast = gam_15.  T and M are stored as the A operand
+// of a 16x16x4 MFMA: lane (g, r) holds row r, columns 4g .. 4g + 3.
+constexpr int kHolaBT = 16;
+struct HolaBlock {
+    float Tp[64][4];
+    float Mp[64][4];
+    float gam[16];
+    float wgt[16];
+    float glast;
+    float pad[3];
+};
 struct HolaArgs {
-    int BH, heads, n, C, w, nchunks, nqt;
+    int BH, heads, n, C, w, nchunks, nqt, nblk;
     const void* q;
     const void* k;
     const void* v;

@@ -653,23 +653,22 @@ def test_hola_prefill(seed, kw, dtype):
     assert worst <= tol
 
 
-# The scan kernel gives each column of S 8, 16 or 32 lanes: the fewest whose grid (sequences x heads x
-# d / (256 / lanes) workgroups) still covers the 256 compute units.  These head counts reach each
-# layout at both d; the strong decay (alpha in [0.05, 0.3]) folds the state's scale into its
-# registers inside most 32-token blocks, the slow path of the scan.
+# The delta rule runs in blocks of 16 tokens: per-block matrices from all blocks in parallel, then one
+# workgroup per (sequence, head, 16 value columns) walks the blocks.  These cases cover many heads at
+# both d, ragged last blocks, and (alpha in [0.05, 0.3]) decay products that underflow within a block.
 HOLA_LANE_CASES = [
-    (96, dict(d=128, B=2, h=32, n=97, C=32, w=8)),    # 8 lanes per column
-    (97, dict(d=128, B=1, h=32, n=97, C=32, w=8)),    # 16
-    (98, dict(d=128, B=1, h=3, n=97, C=32, w=8)),     # 32
-    (99, dict(d=64, B=4, h=32, n=65, C=16, w=4)),     # 8
-    (100, dict(d=64, B=2, h=32, n=65, C=16, w=4)),    # 16
+    (96, dict(d=128, B=2, h=32, n=97, C=32, w=8)),
+    (97, dict(d=128, B=1, h=32, n=96, C=32, w=8)),    # whole blocks only
+    (98, dict(d=128, B=1, h=3, n=97, C=32, w=8)),
+    (99, dict(d=64, B=4, h=32, n=65, C=16, w=4)),
+    (100, dict(d=64, B=2, h=32, n=7, C=16, w=4)),     # one partial block
 ]
 
 
 @pytest.mark.parametrize("decay", ["mild", "strong"])
 @pytest.mark.parametrize("seed,kw", HOLA_LANE_CASES, ids=[f"s{s}" for s, _ in HOLA_LANE_CASES])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_hola_scan_lane_layouts(seed, kw, dtype, decay):
+def test_hola_blocked_delta_rule(seed, kw, dtype, decay):
     """Final state of every head against the oracle's delta rule; outputs and caches of sampled heads
     against the whole oracle."""
     import hybrid_linear_attention_chunkwise_amd as lola
