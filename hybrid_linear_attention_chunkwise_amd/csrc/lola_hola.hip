@@ -173,11 +173,12 @@ __global__ __launch_bounds__(256) void hola_block_kernel(HolaArgs A) {
 // forms its rows' share of K S and Q S; the shares meet in LDS (the one barrier of the block); then
 // every wave forms E and O (the same arithmetic in each, so all hold identical values) and updates
 // its own rows of S.  A block's operands are loaded into registers while the previous block runs.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void hola_scan_kernel(HolaArgs A) {
-    constexpr int BT = kHolaBT, TPW = D / 64;                          // row tiles per wave
-    __shared__ f4 sX[2][4][2][64];                                      // [parity][wave][K S | Q S][lane]
-    __shared__ float sKT[4][BT][TPW * 16 + 4];                          // each wave's unit keys, its rows
+template <typename T, int D, int NW>
+__global__ __launch_bounds__(64 * NW) void hola_scan_kernel(HolaArgs A) {
+    constexpr int BT = kHolaBT, TPW = D / 16 / NW;                     // row tiles per wave
+    static_assert(TPW >= 1 && TPW * NW * 16 == D, "scan waves");
+    __shared__ f4 sX[2][NW][2][64];                                     // [parity][wave][K S | Q S][lane]
+    __shared__ float sKT[NW][BT][TPW * 16 + 4];                         // each wave's unit keys, its rows
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 4, c = l & 15;
     const int bh = blockIdx.x / (D / 16), cb = 16 * (blockIdx.x % (D / 16));
     const int n = A.n, nblk = A.nblk;
@@ -259,7 +260,7 @@ __global__ __launch_bounds__(256) void hola_scan_kernel(HolaArgs A) {
         __syncthreads();
         f4 Rt = zero4(), Qt = zero4();
 #pragma unroll
-        for (int ww = 0; ww < 4; ++ww) {
+        for (int ww = 0; ww < NW; ++ww) {
             Rt += sX[ib & 1][ww][0][l];
             Qt += sX[ib & 1][ww][1][l];
         }
@@ -290,10 +291,10 @@ __global__ __launch_bounds__(256) void hola_scan_kernel(HolaArgs A) {
         float ov = O[0], ev = E[0];
 #pragma unroll
         for (int e = 1; e < 4; ++e) {
-            ov = w == e ? O[e] : ov;
-            ev = w == e ? E[e] : ev;
+            ov = (w & 3) == e ? O[e] : ov;
+            ev = (w & 3) == e ? E[e] : ev;
         }
-        const int t = ib * BT + 4 * g + w;
+        const int t = ib * BT + 4 * g + (w & 3);                        // waves w and w + 4 store alike
         float* po = t < n ? oo + (int64_t)t * D + cb + c : sink + l;
         float* pe = t < n ? ee + (int64_t)t * D + cb + c : sink + 64 + l;
         *po = ov;
@@ -624,7 +625,8 @@ hipError_t launch_hola_t(const HolaArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((hola_block_kernel<T, D>), dim3((unsigned)(((int64_t)a.BH * a.nblk + 3) / 4)), dim3(256), 0,
                        stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((hola_scan_kernel<T, D>), dim3(a.BH * (D / 16)), dim3(256), 0, stream, a);
+    // four waves (one per SIMD); eight, with one row tile each, measured 22% slower at d = 128
+    hipLaunchKernelGGL((hola_scan_kernel<T, D, 4>), dim3(a.BH * (D / 16)), dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((hola_mag_kernel<D>), dim3(rgrid), dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
