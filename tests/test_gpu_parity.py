@@ -697,3 +697,43 @@ def test_hola_blocked_delta_rule(seed, kw, dtype, decay):
                                                 gk[hh], float(sink[hh]), float(gate[hh]), C, w)
         assert [int(p) for p in cpos[b, hh] if p >= 0] == cache_o, f"cache of ({b}, {hh})"
         assert TL.row_rel_err(y[b, hh], y_o) <= tol, f"outputs of ({b}, {hh})"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_hola_degenerate_gates(dtype):
+    """Gates and rows at the edges of their ranges: decays of 1e-30 (the state all but resets inside a
+    block) mixed with 1.0, write strengths of exactly 0 (magnitude 0: many tied scores, ranked by the
+    older position), and all-zero query and key rows (their unit vectors are zero)."""
+    import hybrid_linear_attention_chunkwise_amd as lola
+    from oracle import hola_oracle as HO
+    B, h, n, d, C, w = 1, 4, 150, 64, 32, 16
+    q, k, v, alpha, beta, gq, gk, sink, gate = _hola_inputs(101, B, h, n, d, dtype)
+    rng = np.random.default_rng(102)
+    alpha = np.where(rng.random(alpha.shape) < 0.2, np.float32(1e-30), alpha).astype(np.float32)
+    alpha = np.where(rng.random(alpha.shape) < 0.2, np.float32(1.0), alpha).astype(np.float32)
+    beta = np.where(rng.random(beta.shape) < 0.5, np.float32(0.0), beta).astype(np.float32)
+    zero_q = rng.random((B, h, n)) < 0.1
+    zero_k = rng.random((B, h, n)) < 0.1
+    q = np.where(zero_q[..., None], 0.0, q).astype(np.float32)
+    k = np.where(zero_k[..., None], 0.0, k).astype(np.float32)
+    dev = torch.device("cuda:0")
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    T = lambda x, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(dt)
+    S_out = torch.empty(B, h, d, d, device=dev)
+    cpos = torch.full((B, h, w), -7, dtype=torch.int32, device=dev)
+    cscore = torch.empty(B, h, w, device=dev)
+    print(f"[hola degenerate] {dtype}", flush=True)
+    y = lola.hola_prefill(T(q, tdt), T(k, tdt), T(v, tdt), T(alpha), T(beta), T(gq), T(gk), T(sink), T(gate),
+                          C, w, S_out=S_out, cache_pos=cpos, cache_score=cscore)
+    torch.cuda.synchronize()
+    y, S_out, cpos, cscore = y.float().cpu().numpy(), S_out.cpu().numpy(), cpos.cpu().numpy(), cscore.cpu().numpy()
+    tol = TL.FP32_TOL if dtype == "f32" else TL.BF16_TOL
+    for hh in range(h):
+        y_o, S_o, cache_o, m_o, _ = HO.hola_prefill(q[0, hh], k[0, hh], v[0, hh], alpha[0, hh], beta[0, hh], gq[hh],
+                                                     gk[hh], float(sink[hh]), float(gate[hh]), C, w)
+        assert (m_o == 0).sum() > w, "the case must hold more zero magnitudes than cache slots"
+        assert [int(p) for p in cpos[0, hh]] == cache_o, f"head {hh}: final cache differs"
+        np.testing.assert_allclose(cscore[0, hh], m_o[cache_o], rtol=1e-4 if dtype == "f32" else 2e-2, atol=1e-6)
+        scale = max(1.0, float(np.abs(S_o).max()))
+        assert np.abs(S_out[0, hh] - S_o).max() <= 1e-4 * scale
+        assert TL.row_rel_err(y[0, hh], y_o) <= tol
