@@ -26,18 +26,29 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 matrix (and fp32 vector)
 PEAK_HBM_GBS = 8000.0
 MULTI_TOKEN_C = 16          # tokens per call in the multi-token decode measurement
-KERNEL_SOURCES = ("lola_common.hpp", "lola_phi.hip", "lola_chain.hip", "lola_readout.hip", "lola_decode.hip",
-                  "lola_decode_fast.hip", "lola_collide.hip",
-                  "lola_qscore.hip", "lola_hola.hip")
+# The sources each measured kernel is built from (shared headers included): a counter figure stays
+# valid until one of them changes.
+_SHARED_SOURCES = ("lola_common.hpp", "lola_internal.hpp")
+KERNEL_SOURCES = {
+    "phi": ("lola_phi.hip",),
+    "chain": ("lola_chain.hip",),
+    "readout": ("lola_readout.hip",),
+    "commit": ("lola_readout.hip",),
+    "decode": ("lola_decode_fast.hip", "lola_decode.hip"),
+    "collide": ("lola_collide.hip",),
+    "qscore": ("lola_qscore.hip",),
+    "hola": ("lola_hola.hip",),
+}
 
 
-def log(msg: str) -> None:
-    print(msg, file=sys.stderr, flush=True)
-
-
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel: str = None) -> str:
+    """Hash of the sources one kernel is built from (all kernel sources if none is named)."""
+    if kernel is None:
+        files = sorted({f for fs in KERNEL_SOURCES.values() for f in fs})
+    else:
+        files = list(KERNEL_SOURCES[kernel])
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in _SHARED_SOURCES + tuple(files):
         with open(os.path.join(ROOT, "hybrid_linear_attention_chunkwise_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -66,13 +77,14 @@ def decode_bytes_per_seq_head(wl) -> int:
     return H + s + window + cache + writes + io
 
 
-def load_traffic(kernel: str, src_hash: str):
+def load_traffic(kernel: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it matches the source.
 
     The summary's table has one row per kernel: name, workload, grid, launches, FETCH_SIZE KiB,
-    WRITE_SIZE KiB, calibrated bytes per launch, kernel source hash.  A row taken from other kernel
-    sources than these is stale and ignored.
+    WRITE_SIZE KiB, calibrated bytes per launch, and the hash of that kernel's sources.  A row taken
+    from other sources than the current ones is stale and ignored.
     """
+    src_hash = kernel_source_hash(kernel)
     path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
     if not os.path.exists(path):
         return None
@@ -170,7 +182,7 @@ def bench_collisions(args, lola, torch, wl):
             "entries_in_state": entries, "entries_total": wl.B * wl.h * R * wl.n,
             "roofline": {"bound": "mfma", "achieved": round(ach, 3), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 5),
-                         "traffic": load_traffic("collide", kernel_source_hash()),
+                         "traffic": load_traffic("collide"),
                          "algorithmic_flop_per_launch": flop}}
 
 
@@ -407,7 +419,7 @@ def main() -> int:
     fl = prefill_flops(wl)
     dominant = max(("chain", "readout"), key=lambda k_: kern[k_])
     ach = fl[dominant] / (kern[dominant] * 1e-3) / 1e12
-    traffic = load_traffic(dominant, src_hash)
+    traffic = load_traffic(dominant)
     roofline = {"bound": "mfma", "kernel": f"lola_{dominant}", "achieved": round(ach, 3),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 5),
                 "traffic": traffic, "kernel_ms": round(kern[dominant], 4),
@@ -433,7 +445,7 @@ def main() -> int:
                          "workload": dwl.name, "ms_per_step": round(per_step * 1e3, 4),
                          "roofline": {"bound": "hbm", "kernel": "lola_decode", "achieved": round(ach_d, 1),
                                       "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach_d / PEAK_HBM_GBS, 4),
-                                      "traffic": load_traffic("decode", src_hash),
+                                      "traffic": load_traffic("decode"),
                                       "kernel_ms": round(kern_ms, 4), "algorithmic_bytes_per_launch": byts},
                          "multi_token": multi}
     if not args.no_collisions:
