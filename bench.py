@@ -41,6 +41,10 @@ KERNEL_SOURCES = {
 }
 
 
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
 def kernel_source_hash(kernel: str = None) -> str:
     """Hash of the sources one kernel is built from (all kernel sources if none is named)."""
     if kernel is None:

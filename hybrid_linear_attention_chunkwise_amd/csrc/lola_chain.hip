@@ -174,7 +174,9 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
     int* tmp = reinterpret_cast<int*>(smem + lo.tmp);
 
     const int bh = blockIdx.x;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c = l & 15;
+    // l and c are re-derived at the top of every chunk through an empty asm (see the chunk loop)
+    int tid = threadIdx.x, l = tid & 63, g = l >> 4, c = l & 15;
+    const int w = tid >> 6;
     const int64_t t0 = A.t0;
     const int nrp = cand_rows(lam, C);
     const int xb = x_base(lam);                           // first leaving-token row of the table
@@ -372,6 +374,11 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
 
     // ---------------- chunk loop ----------------
     for (int ch = A.c_begin; ch < A.c_end; ++ch) {
+        // Opaque to the optimiser: the lane-dependent LDS offsets and row pointers derived from l and c
+        // are recomputed in the loop (a few integer operations) instead of being hoisted and kept live
+        // across it, which overflowed the 256 registers a wave has here and put about twenty values in
+        // scratch memory, reloaded on the chunk's critical path.
+        asm volatile("" : "+v"(l), "+v"(c));
         int64_t xlo;
         const int nX = chunk_x(ch, xlo);
         const int NR = xb + nX;
