@@ -379,6 +379,8 @@ __global__ __launch_bounds__(256) void readout_kernel(PrefillArgs A) {
 // Rows move as 16-byte pieces; each thread has UN loads in flight.
 constexpr int kCommitThreads = 1024;
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));   // 16 bytes, a native vector
+
 template <typename T, int DK>
 __global__ __launch_bounds__(kCommitThreads) void commit_kernel(PrefillArgs A) {
     constexpr int DV = DK, EPV = 16 / (int)sizeof(T), CPR = DK / EPV, UN = 4, NTH = kCommitThreads;
@@ -397,26 +399,29 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kernel(PrefillArgs A) {
         T* cV = reinterpret_cast<T*>(A.cache_v) + (int64_t)bh * lam * DV;
         int32_t* cpos = A.cache_pos + (int64_t)bh * lam;
         const int items = lam * 2 * CPR;                 // (slot, K or V, piece)
+        // UN items per thread in flight, without branches around the loads (an item that copies nothing
+        // reads row 0 of the call's keys instead), so the values stay in registers
         for (int i0 = tid; i0 < items; i0 += NTH * UN) {
-            uint4 val[UN];
+            u32x4 val[UN];
             T* dst[UN];
+            bool ok[UN];
 #pragma unroll
             for (int u = 0; u < UN; ++u) {
                 const int it = i0 + NTH * u;
-                dst[u] = nullptr;
-                if (it >= items) continue;
-                const int j = it / (2 * CPR), rem = it % (2 * CPR), isv = rem / CPR, pc = rem % CPR;
+                const bool in = it < items;
+                const int itc = in ? it : 0;
+                const int j = itc / (2 * CPR), rem = itc % (2 * CPR), isv = rem / CPR, pc = rem % CPR;
                 const int src = fs[j];
-                if (src < 0 || src == n + j) continue;    // empty, or a member that kept its slot
-                const T* row;
-                if (src < n) row = (isv ? vin : kin) + (int64_t)src * DK;
-                else row = (isv ? ringV : ringK) + (int64_t)(src - n - lam) * DK;
-                val[u] = *reinterpret_cast<const uint4*>(row + pc * EPV);
+                ok[u] = in && src >= 0 && src != n + j;   // not empty, and not a member that kept its slot
+                const T* row = kin;
+                if (src >= 0 && src < n) row = (isv ? vin : kin) + (int64_t)src * DK;
+                else if (src >= n + lam) row = (isv ? ringV : ringK) + (int64_t)(src - n - lam) * DK;
+                val[u] = *reinterpret_cast<const u32x4*>((ok[u] ? row : kin) + (ok[u] ? pc * EPV : 0));
                 dst[u] = (isv ? cV : cK) + (int64_t)j * DK + pc * EPV;
             }
 #pragma unroll
             for (int u = 0; u < UN; ++u)
-                if (dst[u]) *reinterpret_cast<uint4*>(dst[u]) = val[u];
+                if (ok[u]) *reinterpret_cast<u32x4*>(dst[u]) = val[u];
         }
         for (int j = tid; j < lam; j += NTH) cpos[j] = fp[j];
     }
@@ -427,22 +432,23 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kernel(PrefillArgs A) {
         const int slot0 = (int)(plo % eta);             // ring slot of plo; later ones follow (x < eta)
         const int items = cnt * 2 * CPR;
         for (int i0 = tid; i0 < items; i0 += NTH * UN) {
-            uint4 val[UN];
+            u32x4 val[UN];
             T* dst[UN];
+            bool ok[UN];
 #pragma unroll
             for (int u = 0; u < UN; ++u) {
                 const int it = i0 + NTH * u;
-                dst[u] = nullptr;
-                if (it >= items) continue;
-                const int x = it / (2 * CPR), rem = it % (2 * CPR), isv = rem / CPR, pc = rem % CPR;
+                ok[u] = it < items;
+                const int itc = ok[u] ? it : 0;
+                const int x = itc / (2 * CPR), rem = itc % (2 * CPR), isv = rem / CPR, pc = rem % CPR;
                 const int64_t pos = plo + x;
                 const int slot = slot0 + x >= eta ? slot0 + x - eta : slot0 + x;
-                val[u] = *reinterpret_cast<const uint4*>((isv ? vin : kin) + (pos - t0) * DK + pc * EPV);
+                val[u] = *reinterpret_cast<const u32x4*>((isv ? vin : kin) + (pos - t0) * DK + pc * EPV);
                 dst[u] = (isv ? ringV : ringK) + (int64_t)slot * DK + pc * EPV;
             }
 #pragma unroll
             for (int u = 0; u < UN; ++u)
-                if (dst[u]) *reinterpret_cast<uint4*>(dst[u]) = val[u];
+                if (ok[u]) *reinterpret_cast<u32x4*>(dst[u]) = val[u];
         }
     }
     if (A.score_rule != kScoreSre) {
