@@ -476,7 +476,8 @@ __global__ __launch_bounds__(256) void hola_read_kernel(HolaArgs A) {
     for (int j = tid; j < kHolaMaxW; j += 256) sList[j] = clist[j];
     __syncthreads();
     int nA = 0;
-    while (nA < kHolaMaxW && sList[nA] >= 0) ++nA;
+    static_assert(kHolaMaxW == 64, "one list entry per lane");
+    nA = __popcll(__ballot(sList[l] >= 0));                             // valid entries come first
     const int hi = min(q0 + 63, b - 1);                                 // last chunk key any query here needs
     const int NK = nA + (hi - a + 1);
     auto key_pos = [&](int kk) { return kk < nA ? sList[kk] : a + (kk - nA); };
@@ -575,7 +576,7 @@ __global__ __launch_bounds__(256) void hola_read_kernel(HolaArgs A) {
                 }
             bmax = max_groups(bmax);
             const float m_new = fmaxf(m_run, bmax);
-            const float alpha = expf(m_run - m_new);
+            const float alpha = fast_exp(m_run - m_new);
 #pragma unroll
             for (int J = 0; J < JT; ++J)
 #pragma unroll
@@ -585,7 +586,7 @@ __global__ __launch_bounds__(256) void hola_read_kernel(HolaArgs A) {
             for (int kt = 0; kt < KB / 16; ++kt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float p = st[kt][r] != -INFINITY ? expf(st[kt][r] - m_new) : 0.f;
+                    const float p = st[kt][r] != -INFINITY ? fast_exp(st[kt][r] - m_new) : 0.f;
                     st[kt][r] = p;
                     l_part += p;
                 }
