@@ -12,10 +12,13 @@
 // Kernels, in launch order:
 //   prep   one pass over the tokens: the inverse L2 norms of q and k (the state path normalises with
 //          them while it stages rows) and the cache path's normalised q, k (storage type), 32 lanes per row;
-//   scan   the delta rule, serial in t but separable in the value dimension: one workgroup per
-//          (sequence, head, 256 / L columns of S), L = 8, 16 or 32 lanes per column (d / L of its rows
-//          per lane, in registers), so S^T k and S^T q close with a few DPP steps.  Keys, queries, values
-//          and gates are staged in LDS 32 tokens at a time, the next block loaded while one is scanned;
+//   block  the delta rule over blocks of 16 tokens is linear in the state at the block start: per
+//          block, in parallel, the matrices that do not depend on the state (T = (I + A)^{-1}, the
+//          masked query-key products, the decay vectors), one wave per block;
+//   scan   serial in the blocks, separable in the value dimension: one workgroup per (sequence, head,
+//          16 columns of S) holds S in MFMA accumulators and applies a whole block with fp32 MFMAs
+//          (E = T (V - diag(gam) K S), O = diag(gam) Q S + M E, S = glast S + K^T diag(wgt) E),
+//          the next block's operands loaded while one is applied;
 //   mag    m_t = beta_t ||e_t||, 32 lanes per row;
 //   top    each chunk's own w largest magnitudes, all chunks in parallel;
 //   cache  the persistent cache at every chunk start, serial in the chunks: one wave per (sequence,
@@ -26,7 +29,6 @@
 //          the state read-out.
 #include "lola_common.hpp"
 #include "lola_internal.hpp"
-
 
 namespace lola {
 
