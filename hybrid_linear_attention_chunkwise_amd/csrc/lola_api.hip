@@ -117,8 +117,7 @@ static lola::HolaLayout hola_layout(int64_t BH, int64_t d, int64_t esz, int64_t 
     L.qtil = p; p = rup(p + rows * d * esz, 256);
     L.ktil = p; p = rup(p + rows * d * esz, 256);
     L.o = p;    p = rup(p + rows * d * 4, 256);
-    L.e = p;    p = rup(p + rows * d * 4, 256);
-    L.m = p;    p = rup(p + rows * 4, 256);
+    L.esq = p;  p = rup(p + rows * (d / 16) * 4, 256);
     L.clist = p; p = rup(p + BH * nchunks * lola::kHolaMaxW * 4, 256);
     L.blk = p;  p = rup(p + BH * ((n + lola::kHolaBT - 1) / lola::kHolaBT) * (int64_t)sizeof(lola::HolaBlock), 256);
     L.sink = p; p = rup(p + 2 * 64 * 4, 256);

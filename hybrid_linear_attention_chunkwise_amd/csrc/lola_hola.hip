@@ -11,7 +11,8 @@
 //
 // Kernels, in launch order:
 //   prep   one pass over the tokens: the inverse L2 norms of q and k (the state path normalises with
-//          them while it stages rows) and the cache path's normalised q, k (storage type), 32 lanes per row;
+//          them while it stages rows) and the cache path's normalised q, k (storage type), one 16-byte
+//          piece per lane;
 //   block  the delta rule over blocks of 16 tokens is linear in the state at the block start: per
 //          block, in parallel, the matrices that do not depend on the state (T = (I + A)^{-1}, the
 //          masked query-key products, the decay vectors), one wave per block;
@@ -19,8 +20,8 @@
 //          16 columns of S) holds S in MFMA accumulators and applies a whole block with fp32 MFMAs
 //          (E = T (V - diag(gam) K S), O = diag(gam) Q S + M E, S = glast S + K^T diag(wgt) E),
 //          the next block's operands loaded while one is applied;
-//   mag    m_t = beta_t ||e_t||, 32 lanes per row;
-//   top    each chunk's own w largest magnitudes, all chunks in parallel;
+//   top    m_t = beta_t ||e_t|| (the scan leaves each token's e^2 summed over every 16 columns) and
+//          each chunk's own w largest magnitudes, all chunks in parallel;
 //   cache  the persistent cache at every chunk start, serial in the chunks: one wave per (sequence,
 //          head) merges each chunk's list into the current cache by rank (ties: older);
 //   read   one workgroup per (sequence, head, chunk, 64 queries): softmax over the chunk's persistent
@@ -36,37 +37,37 @@ namespace {
 
 constexpr float kHolaRmsEps = 1e-6f;
 
-template <typename T, int PER>
-__device__ __forceinline__ void load_row_piece(const T* p, float (&x)[PER]) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) x[i] = to_f(p[i]);
-}
-
 // ---------------- prep ----------------
+// One row per D / (16 / sizeof(T)) lanes, each lane one 16-byte piece of q and of k.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void hola_prep_kernel(HolaArgs A) {
-    constexpr int PER = D / 32;
-    const int64_t row = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);   // over B*h*n rows
-    const int lane = threadIdx.x & 31;
+    constexpr int EPV = 16 / (int)sizeof(T), LPR = D / EPV, RPB = 256 / LPR;
+    const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;   // over B*h*n rows
+    const int lane = threadIdx.x % LPR;
     if (row >= (int64_t)A.BH * A.n) return;                             // no barrier in this kernel
     const int head = (int)((row / A.n) % A.heads);
     char* wsb = A.ws;
 #pragma unroll
     for (int which = 0; which < 2; ++which) {                           // 0: queries, 1: keys
-        const T* src = reinterpret_cast<const T*>(which ? A.k : A.q) + row * D + lane * PER;
-        float x[PER];
-        load_row_piece<T, PER>(src, x);
+        const uint4 raw = *reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(which ? A.k : A.q) + row * D + lane * EPV);
+        const T* xp = reinterpret_cast<const T*>(&raw);
+        float x[EPV];
         float ss = 0.f;
 #pragma unroll
-        for (int i = 0; i < PER; ++i) ss += x[i] * x[i];
+        for (int i = 0; i < EPV; ++i) {
+            x[i] = to_f(xp[i]);
+            ss += x[i] * x[i];
+        }
 #pragma unroll
-        for (int sh = 1; sh < 32; sh <<= 1) ss += __shfl_xor(ss, sh, 32);
+        for (int sh = 1; sh < LPR; sh <<= 1) ss += __shfl_xor(ss, sh, LPR);
         const float inv_l2 = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;        // a zero row stays zero
         const float inv_rms = 1.0f / sqrtf(ss / (float)D + kHolaRmsEps);
-        T* til = reinterpret_cast<T*>(wsb + (which ? A.L.ktil : A.L.qtil)) + row * D + lane * PER;
-        const float* gam = (which ? A.gamma_k : A.gamma_q) + (int64_t)head * D + lane * PER;
+        const float* gam = (which ? A.gamma_k : A.gamma_q) + (int64_t)head * D + lane * EPV;
+        uint4 til;
+        T* tp = reinterpret_cast<T*>(&til);
 #pragma unroll
-        for (int i = 0; i < PER; ++i) til[i] = from_f<T>(gam[i] * x[i] * inv_rms);
+        for (int i = 0; i < EPV; ++i) tp[i] = from_f<T>(gam[i] * x[i] * inv_rms);
+        *reinterpret_cast<uint4*>(reinterpret_cast<T*>(wsb + (which ? A.L.ktil : A.L.qtil)) + row * D + lane * EPV) = til;
         if (lane == 0) reinterpret_cast<float*>(wsb + (which ? A.L.kinv : A.L.qinv))[row] = inv_l2;
     }
 }
@@ -191,7 +192,7 @@ __global__ __launch_bounds__(64 * NW) void hola_scan_kernel(HolaArgs A) {
     const float* qinv = reinterpret_cast<const float*>(A.ws + A.L.qinv) + (int64_t)bh * n;
     const HolaBlock* blk = reinterpret_cast<const HolaBlock*>(A.ws + A.L.blk) + (int64_t)bh * nblk;
     float* oo = reinterpret_cast<float*>(A.ws + A.L.o) + (int64_t)bh * n * D;
-    float* ee = reinterpret_cast<float*>(A.ws + A.L.e) + (int64_t)bh * n * D;
+    float* esq = reinterpret_cast<float*>(A.ws + A.L.esq) + (int64_t)bh * n * (D / 16);
     float* sink = reinterpret_cast<float*>(A.ws + A.L.sink);
 
     // a block's operands as loaded (raw storage type; converted where they are used, so that the loads
@@ -297,10 +298,17 @@ __global__ __launch_bounds__(64 * NW) void hola_scan_kernel(HolaArgs A) {
             ev = (w & 3) == e ? E[e] : ev;
         }
         const int t = ib * BT + 4 * g + (w & 3);                        // waves w and w + 4 store alike
+        // the write magnitude's share from these 16 columns: e^2 summed over the 16 lanes of the row
+        // (a DPP row is exactly the lanes of one g), stored by the lane of column 0
+        float q2 = ev * ev;
+        q2 += dpp_mov<0x128>(q2);                                       // row_ror:8
+        q2 += dpp_mov<0x124>(q2);                                       // row_ror:4
+        q2 += dpp_mov<0x122>(q2);                                       // row_ror:2
+        q2 += dpp_mov<0x121>(q2);                                       // row_ror:1
         float* po = t < n ? oo + (int64_t)t * D + cb + c : sink + l;
-        float* pe = t < n ? ee + (int64_t)t * D + cb + c : sink + 64 + l;
+        float* pe = t < n && c == 0 ? esq + (int64_t)t * (D / 16) + cb / 16 : sink + 64 + l;
         *po = ov;
-        *pe = ev;
+        *pe = q2;
     };
     // two operand sets in turn: a block's loads were issued one block earlier, with no copies between.
     // The loads are unconditional (past the last block they repeat it), so the waits for them stay exact.
@@ -324,22 +332,6 @@ __global__ __launch_bounds__(64 * NW) void hola_scan_kernel(HolaArgs A) {
     }
 }
 
-// ---------------- write magnitude ----------------
-template <int D>
-__global__ __launch_bounds__(256) void hola_mag_kernel(HolaArgs A) {
-    constexpr int PER = D / 32;
-    const int64_t row = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
-    const int lane = threadIdx.x & 31;
-    if (row >= (int64_t)A.BH * A.n) return;                             // no barrier in this kernel
-    const float* e = reinterpret_cast<const float*>(A.ws + A.L.e) + row * D + lane * PER;
-    float ss = 0.f;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) ss += e[i] * e[i];
-#pragma unroll
-    for (int sh = 1; sh < 32; sh <<= 1) ss += __shfl_xor(ss, sh, 32);
-    if (lane == 0) reinterpret_cast<float*>(A.ws + A.L.m)[row] = A.beta[row] * sqrtf(ss);
-}
-
 // ---------------- persistent cache per chunk ----------------
 // Ranking key: larger = kept first; equal magnitudes rank the older position higher.  The magnitude's
 // bits are mapped so that unsigned order is float order (with -0 taken as +0).
@@ -359,14 +351,24 @@ __device__ __forceinline__ int key_pos(unsigned long long key) { return (int)(0x
 // Each chunk's own ranking, all chunks in parallel: the w largest keys of the chunk's tokens, largest
 // first.  The persistent cache at any chunk start is the top w of the union of these lists over the
 // earlier chunks, since a token outside its own chunk's top w has w larger keys before it anyway.
+// The magnitudes m_t = beta_t ||e_t|| are formed here from the scan's per-16-column sums of e^2, added
+// in column order.
+template <int D>
 __global__ __launch_bounds__(256) void hola_chunk_top_kernel(HolaArgs A) {
+    constexpr int NG = D / 16;
     __shared__ unsigned long long sKey[kHolaMaxC];
     const int bh = blockIdx.x / A.nchunks, ch = blockIdx.x % A.nchunks, tid = threadIdx.x;
     const int n = A.n, C = A.C, a = ch * C, nx = min(C, n - a), keep = min(A.w, nx);
     const int ls = min(kHolaMaxW, C);                                   // list stride
-    const float* m = reinterpret_cast<const float*>(A.ws + A.L.m) + (int64_t)bh * n;
+    const float* esq = reinterpret_cast<const float*>(A.ws + A.L.esq) + (int64_t)bh * n * NG;
+    const float* beta = A.beta + (int64_t)bh * n;
     unsigned long long* out = reinterpret_cast<unsigned long long*>(A.ws + A.L.tlist) + ((int64_t)bh * A.nchunks + ch) * ls;
-    for (int i = tid; i < nx; i += 256) sKey[i] = hola_key(m[a + i], a + i);
+    for (int i = tid; i < nx; i += 256) {
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < NG; ++j) ss += esq[(int64_t)(a + i) * NG + j];
+        sKey[i] = hola_key(beta[a + i] * sqrtf(ss), a + i);
+    }
     __syncthreads();
     for (int i = tid; i < nx; i += 256) {
         const unsigned long long ki = sKey[i];
@@ -621,7 +623,8 @@ __global__ __launch_bounds__(256) void hola_read_kernel(HolaArgs A) {
 template <typename T, int D>
 hipError_t launch_hola_t(const HolaArgs& a, hipStream_t stream) {
     const int64_t rows = (int64_t)a.BH * a.n;
-    const unsigned rgrid = (unsigned)((rows + 7) / 8);
+    constexpr int prep_rows = 256 / (D / (16 / (int)sizeof(T)));         // rows per prep workgroup
+    const unsigned rgrid = (unsigned)((rows + prep_rows - 1) / prep_rows);
     hipLaunchKernelGGL((hola_prep_kernel<T, D>), dim3(rgrid), dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -631,10 +634,9 @@ hipError_t launch_hola_t(const HolaArgs& a, hipStream_t stream) {
     // four waves (one per SIMD); eight, with one row tile each, measured 22% slower at d = 128
     hipLaunchKernelGGL((hola_scan_kernel<T, D, 4>), dim3(a.BH * (D / 16)), dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((hola_mag_kernel<D>), dim3(rgrid), dim3(256), 0, stream, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     if (a.w > 0) {
-        hipLaunchKernelGGL(hola_chunk_top_kernel, dim3((unsigned)((int64_t)a.BH * a.nchunks)), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((hola_chunk_top_kernel<D>), dim3((unsigned)((int64_t)a.BH * a.nchunks)), dim3(256), 0, stream,
+                           a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     hipLaunchKernelGGL(hola_cache_kernel, dim3(a.BH), dim3(64), 0, stream, a);

@@ -116,8 +116,8 @@ constexpr int kHolaMaxC = 1024;   // largest chunk
 struct HolaLayout {               // byte offsets of whole arrays in the workspace
     int64_t qinv, kinv;           // [BH][n] fp32: 1 / ||x||_2 of queries and keys (0 for a zero row)
     int64_t qtil, ktil;           // [BH][n][d] T   : RMS-normalised, gamma-scaled queries and keys
-    int64_t o, e;                 // [BH][n][d] fp32: state read-out S_t^T q_t, residual e_t
-    int64_t m;                    // [BH][n]    fp32: write magnitude beta_t ||e_t||
+    int64_t o;                    // [BH][n][d] fp32: state read-out S_t^T q_t
+    int64_t esq;                  // [BH][n][d / 16] fp32: sum of e_t^2 over each group of 16 value columns
     int64_t clist;                // [BH][nchunks][kHolaMaxW] int32: persistent cache at each chunk start
     int64_t blk;                  // [BH][ceil(n / 16)] HolaBlock: the delta rule's per-block matrices
     int64_t sink;                 // [2][64] fp32: where the scan's stores for tokens past n go
