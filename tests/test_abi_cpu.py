@@ -102,3 +102,51 @@ def test_options_validation_without_gpu(lib, mask, rule, reserved):
                                  None)
     assert rc == B.LOLA_EINVAL
     assert st.t == 0
+
+
+HOLA_BAD = [
+    # (B, heads, d, dtype, n, C, w, expected): rejected before any device work
+    (0, 2, 128, B.LOLA_BF16, 64, 16, 4, B.LOLA_EINVAL),          # no sequences
+    (1, 2, 96, B.LOLA_BF16, 64, 16, 4, B.LOLA_EUNSUPPORTED),     # d outside {64, 128}
+    (1, 2, 128, 7, 64, 16, 4, B.LOLA_EINVAL),                    # unknown storage type
+    (1, 2, 128, B.LOLA_BF16, 64, 0, 4, B.LOLA_EINVAL),           # chunk of 0
+    (1, 2, 128, B.LOLA_BF16, 64, 2048, 4, B.LOLA_EUNSUPPORTED),  # chunk above the largest
+    (1, 2, 128, B.LOLA_BF16, -1, 16, 4, B.LOLA_EINVAL),          # negative length
+    (1, 2, 128, B.LOLA_BF16, 64, 16, -1, B.LOLA_EINVAL),         # negative cache
+    (1, 2, 128, B.LOLA_BF16, 64, 16, 65, B.LOLA_EUNSUPPORTED),   # cache above the largest
+]
+
+
+@pytest.mark.parametrize("Bn,h,d,dt,n,C,w,want", HOLA_BAD)
+def test_hola_validation_without_gpu(lib, Bn, h, d, dt, n, C, w, want):
+    """hola_prefill checks its shape arguments before touching memory; hola_workspace_bytes returns 0
+    for a shape hola_prefill would reject."""
+    p = 0x300000
+    rc = lib.hola_prefill(Bn, h, d, dt, n, C, w, p, p, p, p, p, p, p, p, p, p, None, None, None, 0x400000, 1 << 40,
+                          None)
+    assert rc == want
+    if w >= 0 and w <= 64:
+        assert lib.hola_workspace_bytes(Bn, h, d, dt, n, C) == 0
+
+
+def test_hola_pointer_validation_without_gpu(lib):
+    """Null or misaligned tensors, and a workspace that is missing, misaligned or too small."""
+    p = 0x300000
+    good = dict(q=p, k=p, v=p, alpha=p, beta=p, gq=p, gk=p, sink=p, gate=p, y=p)
+    need = lib.hola_workspace_bytes(1, 2, 128, B.LOLA_BF16, 64, 16)
+    assert need > 0
+
+    def call(ws=0x400000, nbytes=1 << 40, **over):
+        a = dict(good, **over)
+        return lib.hola_prefill(1, 2, 128, B.LOLA_BF16, 64, 16, 4, a["q"], a["k"], a["v"], a["alpha"], a["beta"],
+                                a["gq"], a["gk"], a["sink"], a["gate"], a["y"], None, None, None, ws, nbytes, None)
+    for name in good:
+        assert call(**{name: None}) == B.LOLA_EINVAL, name
+    for name in ("q", "k", "v", "y"):
+        assert call(**{name: p + 2}) == B.LOLA_EINVAL, name
+    assert call(ws=None) == B.LOLA_EINVAL
+    assert call(ws=0x400010) == B.LOLA_EINVAL                       # workspace not 256-byte aligned
+    assert call(nbytes=need - 1) == B.LOLA_EINVAL
+    # an empty call is a no-op that needs no buffers at all
+    assert lib.hola_prefill(1, 2, 128, B.LOLA_BF16, 0, 16, 4, None, None, None, None, None, None, None, None,
+                            None, None, None, None, None, None, 0, None) == B.LOLA_OK
