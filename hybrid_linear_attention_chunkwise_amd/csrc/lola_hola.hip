@@ -125,14 +125,24 @@ __global__ __launch_bounds__(256) void hola_block_kernel(HolaArgs A) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     // ratio(i, j) = prod_{j < l <= i} alpha_l;  lane (g, c) holds rows i = 4g + e, column j = c
+    // one running product over the block: run = prod_{c < l <= m} alpha_l (1 for m <= c), captured at
+    // the lane's rows m = 4g .. 4g + 3
+    float rr[4] = {1.f, 1.f, 1.f, 1.f};
+    {
+        float run = 1.f;
+#pragma unroll
+        for (int m = 0; m < BT; ++m) {
+            run = m > c ? run * sAB[w][0][m] : 1.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rr[e] = m == 4 * g + e ? run : rr[e];
+        }
+    }
+    const float bj = sAB[w][1][c];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int i = 4 * g + e, j = c;
-        float r = 1.f;
-        for (int m = j + 1; m <= i; ++m) r *= sAB[w][0][m];
-        const float bj = sAB[w][1][j];
-        sM[w][0][i][j] = j < i ? r * bj * G[e] : 0.f;                  // A (strictly lower)
-        sM[w][1][i][j] = j <= i ? r * bj * QK[e] : 0.f;                // Mq (lower, with the diagonal)
+        sM[w][0][i][j] = j < i ? rr[e] * bj * G[e] : 0.f;              // A (strictly lower)
+        sM[w][1][i][j] = j <= i ? rr[e] * bj * QK[e] : 0.f;            // Mq (lower, with the diagonal)
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
