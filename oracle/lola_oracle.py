@@ -57,7 +57,7 @@ textbook special cases, hand-derived schedules, invariants and an independent pe
 from __future__ import annotations
 
 import dataclasses
-from typing import Callable, List, Optional
+from typing import Callable, List, Optional, Sequence
 
 import numpy as np
 
@@ -244,13 +244,17 @@ def exact_attention_read(q_t, phi_q, H, s, keys, vals, d_k, use_state: bool = Tr
 
 def prefill(st: SeqState, phi, q, k, v, C: int, fold_at_in: Optional[np.ndarray] = None,
             tol: float = 0.0, on_chunk_end: Optional[Callable[[int, SeqState], None]] = None,
-            read_mask: int = READ_ALL, score_rule: str = "sre"):
+            read_mask: int = READ_ALL, score_rule: str = "sre",
+            fold_sets_in: Optional[Sequence[Sequence[int]]] = None):
     """Chunked prefill of n tokens for one sequence and head (section 2.6), read out token by token.
 
     q, k: [n][d_k]; v: [n][d_v].  Mutates ``st``.  Returns (y [n][d_v], Schedule).
     ``fold_at_in`` replays an external schedule (call-local chunk id per input token, -1 = not
     folded): its decisions replace the top-lambda, and each is checked against the fp64 SRE order
     with relative tolerance ``tol`` (problems are recorded in the returned Schedule).
+    ``fold_sets_in`` replays an external schedule given as the folded positions of each chunk (any
+    position, so it can also name tokens of earlier calls, as a decode step does); it is validated in
+    the same way.  At most one of ``fold_at_in`` and ``fold_sets_in`` may be given.
     ``on_chunk_end(c, st)`` is called once per chunk, after the chunk's folds and commit.
     ``read_mask`` (READ_*) selects the memories the queries read (reading R18); ``score_rule`` one of
     SCORE_RULES ranks the candidates (SRE against the state, or reading R19's accumulated scores)."""
@@ -267,6 +271,8 @@ def prefill(st: SeqState, phi, q, k, v, C: int, fold_at_in: Optional[np.ndarray]
         raise ValueError("reading R18: a read mask holds the window and nothing but the three memories")
     if score_rule not in SCORE_RULES:
         raise ValueError(f"unknown score rule {score_rule!r}")
+    if fold_at_in is not None and fold_sets_in is not None:
+        raise ValueError("give fold_at_in or fold_sets_in, not both")
     t0 = st.t
     st.ensure(t0 + n)
     st.K[t0:t0 + n] = k
@@ -286,7 +292,7 @@ def prefill(st: SeqState, phi, q, k, v, C: int, fold_at_in: Optional[np.ndarray]
             else:   # reading R19: what queries before the chunk start have added
                 scores = {i: float(st.score[i]) for i in E}
         gap = None
-        if fold_at_in is None:
+        if fold_at_in is None and fold_sets_in is None:
             if len(E) <= lam:
                 kept, S = E, []
             elif lam == 0:
@@ -297,7 +303,13 @@ def prefill(st: SeqState, phi, q, k, v, C: int, fold_at_in: Optional[np.ndarray]
                 hi = scores[order[lam - 1]]
                 gap = (hi - scores[order[lam]]) / hi if hi > 0 else 0.0
         else:
-            S = sorted(i for i in E if i >= t0 and fold_at_in[i - t0] == c)
+            if fold_at_in is not None:
+                S = sorted(i for i in E if i >= t0 and fold_at_in[i - t0] == c)
+            else:
+                given = sorted(int(i) for i in fold_sets_in[c])
+                S = [i for i in given if i in set(E)]
+                if len(S) != len(given):
+                    sched.problems.append((c, "not a candidate", sorted(set(given) - set(E))))
             kept = sorted(set(E) - set(S))
             if len(kept) != min(lam, len(E)):
                 sched.problems.append((c, "size", len(kept), min(lam, len(E))))
@@ -349,14 +361,20 @@ def prefill(st: SeqState, phi, q, k, v, C: int, fold_at_in: Optional[np.ndarray]
     return y, sched
 
 
-def decode_step(st: SeqState, phi, q, k, v, read_mask: int = READ_ALL, score_rule: str = "sre"):
+def decode_step(st: SeqState, phi, q, k, v, read_mask: int = READ_ALL, score_rule: str = "sre",
+                fold: Optional[int] = None, tol: float = 0.0, want_schedule: bool = False):
     """One decode token (section 2.4 single-token update, then Eq. (14)): prefill with C = 1.
 
-    Returns (y [d_v], folded position or -1)."""
+    ``fold`` (a position, or -1 for none) replays an external decision in place of the top-lambda and
+    validates it with relative tolerance ``tol`` (see ``replay``).  Returns (y [d_v], folded position
+    or -1), plus the step's Schedule when ``want_schedule``."""
+    sets = None if fold is None else [[] if fold < 0 else [int(fold)]]
     y, sched = prefill(st, phi, np.asarray(q)[None, :], np.asarray(k)[None, :],
-                       np.asarray(v)[None, :], C=1, read_mask=read_mask, score_rule=score_rule)
+                       np.asarray(v)[None, :], C=1, read_mask=read_mask, score_rule=score_rule,
+                       tol=tol, fold_sets_in=sets)
     S = sched.folded[0]
-    return y[0], (S[0] if S else -1)
+    out = (y[0], (S[0] if S else -1))
+    return out + (sched,) if want_schedule else out
 
 
 def replay(st: SeqState, phi, q, k, v, C: int, fold_at: np.ndarray, tol: float):

@@ -120,6 +120,41 @@ def grade_prefill(res: dict, y_gpu: np.ndarray, fold_gpu: np.ndarray, dtype: str
     return rep
 
 
+def grade_decode_steps(so, phi_o, dq, dk, dv, ys, folds, dtype: str, read_mask: int = 7) -> dict:
+    """Grades single-token decode steps of one (sequence, head) against the oracle state ``so``
+    (mutated: it follows the GPU).
+
+    dq, dk, dv [steps][d]; ys [steps][d_v] GPU outputs; folds [steps] GPU folded positions (-1: none).
+    Each step is decided by the oracle on a copy of the state.  Where the GPU folded another candidate:
+    in fp32 the oracle's boundary gap must lie within the tie band; in both modes the GPU's choice is
+    replayed (validated in fp64: the folded SRE may exceed the smallest kept SRE by at most the
+    dtype's tolerance) and the oracle continues from there, so every step is graded."""
+    from oracle import lola_oracle as O
+    tol = TIE_BAND if dtype == "f32" else BF16_TOL
+    out_tol = FP32_TOL if dtype == "f32" else BF16_TOL
+    worst, mism = 0.0, 0
+    for s in range(len(ys)):
+        trial = so.copy()
+        y_o, f_o, sch = O.decode_step(trial, phi_o, dq[s], dk[s], dv[s], read_mask=read_mask, want_schedule=True)
+        f_g = int(folds[s])
+        if f_o == f_g:
+            so.__dict__.update(trial.__dict__)
+        else:
+            mism += 1
+            if dtype == "f32":
+                gap = sch.gap[0]
+                assert gap is not None and gap <= TIE_BAND, (
+                    f"fp32 decode fold differs at step {s}: oracle {f_o}, GPU {f_g}, gap {gap}")
+            y_o, f_r, sch_r = O.decode_step(so, phi_o, dq[s], dk[s], dv[s], read_mask=read_mask,
+                                            fold=f_g, tol=tol, want_schedule=True)
+            assert not sch_r.problems, f"invalid GPU fold at step {s}: {sch_r.problems}"
+            assert f_r == f_g
+        err = row_rel_err(np.asarray(ys[s])[None], y_o[None])
+        assert err <= out_tol, f"decode output error {err:.3e} > {out_tol} at step {s}"
+        worst = max(worst, err)
+    return {"max_row_rel_err": worst, "fold_mismatches": mism, "steps": len(ys)}
+
+
 def gpu_run_prefill(q, k, v, W, phi_kind: str, eta: int, lam: int, C: int, dtype: str, D: int = 128,
                     chunks: Optional[Sequence[int]] = None, state=None):
     """Runs lola_prefill on cuda:0 for numpy q, k, v [B][h][n][d]; returns host arrays.

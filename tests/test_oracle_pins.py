@@ -134,19 +134,85 @@ def test_hand_schedule():
 
 
 def test_exact_tie_keeps_older_position():
-    """Reading R6: identical (k, v) give identical SRE; the older one stays exact."""
-    rng = np.random.default_rng(3)
-    n, eta, lam = 12, 2, 3
-    phi, q, k, v = _rand_problem(3, n)
-    k[5], v[5] = k[2], v[2]             # token 5 duplicates token 2
-    st = O.new_state(8, 6, 8, eta, lam)
-    y, sched = O.prefill(st, phi, q, k, v, C=1)
-    for c, (S, kept) in enumerate(zip(sched.folded, sched.kept)):
-        if 2 in kept + S and 5 in kept + S:
-            # they tie exactly; if exactly one of them is kept it must be the older one
-            if (2 in S) != (5 in S):
-                assert 5 in S
-    del rng
+    """Reading R6 (2.4, exactly lambda kept): an exact duplicate competes with its original for the
+    one slot, so both have the same SRE against the same state; the older copy stays, the newer is
+    folded.  Worked by hand with eta = lambda = C = 1 over four tokens:
+      t = 1: token 0 leaves the window, the cache is empty, so it is kept (no scoring);
+      t = 2: token 1 leaves; candidates {0, 1} score against the empty state, SRE = ||v|| (reading R5):
+             1 for token 0, 3 for token 1, so token 0 is folded and token 1 kept;
+      t = 3: token 2 (a copy of token 1) leaves; candidates {1, 2} tie exactly; token 1 is kept."""
+    k = np.array([[0.3, -0.2], [1.1, 0.4], [1.1, 0.4], [-0.5, 0.9]])
+    v = np.array([[1.0, 0.0], [0.0, 3.0], [0.0, 3.0], [5.0, 5.0]])
+    q = np.array([[0.1, 0.2], [0.3, -0.1], [-0.4, 0.5], [0.2, 0.2]])
+    phi = O.make_phi("softmax_pm", np.array([[0.5, -0.3], [0.2, 0.8]]))
+    st = O.new_state(2, 2, 4, 1, 1)
+    _, sched = O.prefill(st, phi, q, k, v, C=1)
+    assert sched.fold_at.tolist() == [2, -1, 3, -1]
+    assert st.cache == [1]
+    assert sched.gap[3] == 0.0        # the last allocation was decided by the tie rule alone
+    assert sched.folded[3] == [2] and sched.kept[3] == [1]
+
+
+def _chunked_tie_case():
+    """A duplicate pair inside one leaving block (C = 4): tokens 4 and 5 carry the same key and the
+    same large value, so in chunk 2 (positions 8..11, leaving block 4..7) they have the two largest
+    SREs and tie for the single cache slot."""
+    phi, q, k, v = _rand_problem(31, 16, d_k=6, d_v=6)
+    k[5] = k[4]
+    v[4] = 100.0 * v[4]
+    v[5] = v[4]
+    st = O.new_state(6, 6, 8, 4, 1)
+    _, sched = O.prefill(st, phi, q, k, v, C=4)
+    return sched
+
+
+def test_exact_tie_in_a_chunk_keeps_older_position():
+    """Reading R6 in a chunked allocation (2.6): |E| = 5 > lambda = 1 and the boundary falls inside
+    an exact tie; the older token 4 is kept, token 5 is folded in chunk 2."""
+    sched = _chunked_tie_case()
+    assert sched.chunk_start[2] == 8 and 4 in sched.kept[2] + sched.folded[2]
+    assert len(sched.kept[2]) + len(sched.folded[2]) == 5
+    assert sched.gap[2] == 0.0
+    assert sched.kept[2] == [4]
+    assert sched.fold_at[5] == 2
+
+
+def test_tie_pins_catch_a_reversed_tie_rule(monkeypatch):
+    """Negative control: plant 'equal SRE keeps the newer position' in the oracle's ranking; both tie
+    pins must fail."""
+    import builtins
+
+    def newer_first(it, key=None, reverse=False):
+        if key is None:
+            return builtins.sorted(it, reverse=reverse)
+        return builtins.sorted(it, key=lambda i: (key(i)[0], -key(i)[1]), reverse=reverse)
+    monkeypatch.setattr(O, "sorted", newer_first, raising=False)
+    with pytest.raises(AssertionError):
+        test_exact_tie_keeps_older_position()
+    with pytest.raises(AssertionError):
+        test_exact_tie_in_a_chunk_keeps_older_position()
+
+
+def test_decode_replay_validates_the_fold():
+    """A decode step replayed under an external fold (2.4, one fold per overflowing step): the
+    oracle's own choice replays to the same output with no problem; folding the candidate with the
+    largest SRE instead is reported as an order problem, and a position that is no candidate as such."""
+    phi, q, k, v = _rand_problem(32, 40)
+    st = O.new_state(8, 6, 8, 5, 4)
+    O.prefill(st, phi, q[:30], k[:30], v[:30], C=5)
+    base = st.copy()
+    y_o, f_o, sch = O.decode_step(base.copy(), phi, q[30], k[30], v[30], want_schedule=True)
+    assert f_o >= 0 and not sch.problems
+    y_r, f_r, sch_r = O.decode_step(base.copy(), phi, q[30], k[30], v[30], fold=f_o, want_schedule=True)
+    assert f_r == f_o and not sch_r.problems
+    np.testing.assert_array_equal(y_r, y_o)
+    E = sorted(set(base.cache) | {30 - 5})
+    scores = O.sre(phi(base.K[E]), base.V[E], base.H, base.s)
+    worst = E[int(np.argmax(scores))]
+    _, _, sch_w = O.decode_step(base.copy(), phi, q[30], k[30], v[30], fold=worst, tol=2e-2, want_schedule=True)
+    assert [p[1] for p in sch_w.problems] == ["order"]
+    _, _, sch_n = O.decode_step(base.copy(), phi, q[30], k[30], v[30], fold=29, want_schedule=True)
+    assert "not a candidate" in [p[1] for p in sch_n.problems]
 
 
 # ------------------------------------------------------------------------------------------------
