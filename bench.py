@@ -1,10 +1,13 @@
 #!/usr/bin/env python3
 """Throughput of the LoLA hot path on one MI355X; prints one JSON line.
 
-Headline step: one chunked prefill of the n = 4096, 32-head, d = 128 bf16 workload (softmax-pair
-feature map, C = 64, eta = lambda = 256, 2% outlier keys) from a freshly initialised state.
-Also measured: 256 decode steps of 64 sequences x 32 heads after an 8192-token prior context, and the
-fp64 CPU oracle on a bounded sample of the headline workload.
+Headline step: one chunked prefill of the largest single-GPU prefill workload, 4 sequences x 32 heads
+x 16384 tokens, d = 128, bf16 (softmax-pair feature map, C = 64, eta = lambda = 256), from a freshly
+initialised state, with the read-out overlapped on a second stream.  Also measured: the 32-head
+n = 4096 workload with 2% outlier keys, the 8-head n = 131072 workload with planted pairs (C = 128,
+eta = lambda = 512), 256 decode steps of 64 sequences x 32 heads after an 8192-token prior context, the
+device's attainable bf16 matrix rate and copy bandwidth, and the fp64 CPU oracle on a bounded sample
+of the headline workload.
 
 Inputs are seeded synthetic data resident in device memory before timing starts.
 """
@@ -59,14 +62,21 @@ def kernel_source_hash(kernel: str = None) -> str:
 
 
 def prefill_flops(wl) -> dict:
-    """Algorithmic FLOPs per launch of each prefill kernel (per token and head, times B*h*n)."""
+    """Algorithmic FLOPs per launch of each prefill kernel (per token and head, times B*h*n).
+
+    Per token and head: features of the key (feature kernel) and of the query (read-out), 2 d_k D_W
+    each; the exact branch 2 (d_k + d_v)(eta + lambda) (an upper bound: a query reads at most eta + lambda
+    exact keys); the linear read 2 D (d_v + 1); the intra-chunk fold term (D + d_v + 1)(C + 1); SRE
+    scoring of the C + lambda candidates of a chunk, 2 D (d_v + 1)(C + lambda) / C; the fold 2 D (d_v + 1).
+    The chain kernel does the scoring and the fold, the read-out the rest but the key features."""
     dw = wl.D if wl.phi == "elu1" else wl.D // 2
     phi = 2 * wl.d_k * dw
-    chain = 2 * wl.D * (wl.d_v + 1) * (wl.C + wl.lam) / wl.C + 2 * wl.D * (wl.d_v + 1) + phi
+    chain = 2 * wl.D * (wl.d_v + 1) * (wl.C + wl.lam) / wl.C + 2 * wl.D * (wl.d_v + 1)
     readout = (phi + 2 * (wl.d_k + wl.d_v) * (wl.eta + wl.lam) + 2 * wl.D * (wl.d_v + 1)
                + (wl.D + wl.d_v + 1) * (wl.C + 1))
     units = wl.B * wl.h * wl.n
-    return {"chain": chain * units, "readout": readout * units, "per_token_head": chain + readout}
+    return {"phi": phi * units, "chain": chain * units, "readout": readout * units,
+            "per_token_head": phi + chain + readout, "total": (phi + chain + readout) * units}
 
 
 def decode_bytes_per_seq_head(wl) -> int:
@@ -100,8 +110,18 @@ def load_traffic(kernel: str):
     return None
 
 
-def bench_prefill(args, lola, torch, wl):
+def bench_prefill(args, lola, torch, wl, steps=None, warmup=None, kernel_steps=20):
+    """Whole-prefill timing of one workload, then per-kernel timing.
+
+    Timed region: `steps` back-to-back steps, each a state reset (lola_state_init) and one overlapped
+    prefill call, bracketed by synchronisations (wall clock).  HIP events on the caller's stream around
+    each prefill call alone (the reset excluded) give the per-call median and minimum.  A second pass
+    runs the sequential schedule with events between its kernels (lola_prefill_profiled) for the
+    per-kernel durations; every kernel there is launched on the caller's stream."""
+    import statistics
     from workloads import make_qkv, make_weights
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
     dev = torch.device("cuda:0")
     tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     W = make_weights(wl)
@@ -109,42 +129,70 @@ def bench_prefill(args, lola, torch, wl):
     qt = torch.from_numpy(q).to(dev).to(tdt)
     kt = torch.from_numpy(k).to(dev).to(tdt)
     vt = torch.from_numpy(v).to(dev).to(tdt)
+    del q, k, v
     st = lola.LolaState(wl.B, wl.h, wl.d_k, wl.d_v, wl.D, wl.eta, wl.lam, tdt, device=dev)
     phi = lola.LolaPhi(wl.phi, torch.from_numpy(W).to(dev), wl.D)
     y = torch.empty_like(vt)
     ws = torch.empty(lola.lola_workspace_bytes(st, wl.n, wl.C), dtype=torch.uint8, device=dev)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
-    for e in ev:
-        e.record()
+    ov = lola.LolaOverlap(dev)
+    log(f"prefill {wl.name}: inputs resident, {warmup} warm-up + {steps} timed steps")
 
-    def step(events=None):
+    def step(e0=None, e1=None):
         lola.lola_state_init(st)
-        lola.lola_prefill(st, phi, qt, kt, vt, wl.C, y=y, workspace=ws, events=events)
+        if e0 is not None:
+            e0.record()
+        lola.lola_prefill(st, phi, qt, kt, vt, wl.C, y=y, workspace=ws, overlap=ov)
+        if e1 is not None:
+            e1.record()
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
-    torch.cuda.synchronize()
-    kern = {"phi": 0.0, "chain": 0.0, "readout": 0.0, "commit": 0.0}
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(ev)
-        # per-kernel durations from the boundary events of this step (same stream as the kernels)
-        ev[4].synchronize()
-        for i, name in enumerate(("phi", "chain", "readout", "commit")):
-            kern[name] += ev[i].elapsed_time(ev[i + 1])
-    torch.cuda.synchronize()
-    t_evented = time.perf_counter() - t0
-    # the timed region proper: K back-to-back steps, no host waits inside
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for i in range(steps):
+        step(*evs[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    kern = {k_: v_ / args.steps for k_, v_ in kern.items()}   # ms per launch
-    log(f"prefill: {elapsed / args.steps * 1e3:.3f} ms/step (evented pass {t_evented / args.steps * 1e3:.3f}); "
-        f"kernels ms: {kern}")
-    return elapsed, kern
+    call_ms = [a.elapsed_time(b) for a, b in evs]
+    # per-kernel durations: sequential schedule with events between the kernels (same stream)
+    kev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    for e in kev:
+        e.record()                      # creates the HIP events the library records into
+    kern = {"phi": 0.0, "chain": 0.0, "readout": 0.0, "commit": 0.0}
+    for _ in range(kernel_steps):
+        lola.lola_state_init(st)
+        lola.lola_prefill(st, phi, qt, kt, vt, wl.C, y=y, workspace=ws, events=kev)
+        kev[4].synchronize()
+        for i, name in enumerate(("phi", "chain", "readout", "commit")):
+            kern[name] += kev[i].elapsed_time(kev[i + 1])
+    kern = {k_: v_ / kernel_steps for k_, v_ in kern.items()}   # ms per launch
+    med, mn = statistics.median(call_ms), min(call_ms)
+    log(f"prefill {wl.name}: {elapsed / steps * 1e3:.3f} ms/step wall, prefill call median {med:.3f} ms, "
+        f"min {mn:.3f} ms; kernels ms (sequential): {kern}")
+    del qt, kt, vt, y, ws
+    return {"elapsed": elapsed, "steps": steps, "call_ms_median": med, "call_ms_min": mn, "kernels_ms": kern}
+
+
+def prefill_report(wl, r) -> dict:
+    """Throughput and roofline figures of one prefill workload from bench_prefill's timings."""
+    fl = prefill_flops(wl)
+    kern = r["kernels_ms"]
+    tokens = wl.B * wl.n
+    out = {"workload": wl.name, "tokens_per_s": round(tokens * r["steps"] / r["elapsed"], 1),
+           "ms_per_step": round(r["elapsed"] / r["steps"] * 1e3, 4),
+           "prefill_call_ms": {"median": round(r["call_ms_median"], 4), "min": round(r["call_ms_min"], 4),
+                               "runs": r["steps"]},
+           "kernels_ms_sequential": {k_: round(v_, 4) for k_, v_ in kern.items()}}
+    fr = {}
+    for name in ("chain", "readout"):
+        ach = fl[name] / (kern[name] * 1e-3) / 1e12
+        fr[name] = {"achieved_tflops": round(ach, 3), "frac": round(ach / PEAK_BF16_TFLOPS, 5),
+                    "algorithmic_flop_per_launch": fl[name], "kernel_ms": round(kern[name], 4)}
+    out["kernel_fractions"] = fr
+    out["mfma_frac_whole_step"] = round(fl["total"] / (r["call_ms_median"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 5)
+    out["algorithmic_flop_per_step"] = fl["total"]
+    return out
 
 
 def bench_collisions(args, lola, torch, wl):
@@ -204,13 +252,15 @@ def bench_options(args, lola, torch, wl):
     phi = lola.LolaPhi(wl.phi, torch.from_numpy(W).to(dev), wl.D)
     y = torch.empty_like(vt)
     ws = torch.empty(lola.lola_workspace_bytes(st, wl.n, wl.C), dtype=torch.uint8, device=dev)
+    ov = lola.LolaOverlap(dev)
     out = {}
     cases = [(r, lola.LOLA_READ_ALL) for r in ("kernel_sq", "kernel_abs", "ratio", "attn")]
     cases += [("sre", lola.LOLA_READ_WINDOW), ("sre", lola.LOLA_READ_WINDOW | lola.LOLA_READ_SPARSE)]
     for rule, mask in cases:
         def step():
             lola.lola_state_init(st)
-            lola.lola_prefill(st, phi, qt, kt, vt, wl.C, y=y, workspace=ws, read_mask=mask, score_rule=rule)
+            lola.lola_prefill(st, phi, qt, kt, vt, wl.C, y=y, workspace=ws, read_mask=mask, score_rule=rule,
+                              overlap=ov)
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
@@ -272,6 +322,11 @@ def bench_hola(args, lola, torch, wl):
 
 
 def bench_decode(args, lola, torch, wl):
+    """256 single-token decode steps of every (sequence, head) after the untimed prior context; each run
+    restores the same post-prefill snapshot (untimed) and times the steps with HIP events on the caller's
+    stream, one event per step boundary (per-step kernel time) and the wall clock around the run.  Then
+    the same tokens in prefill calls of MULTI_TOKEN_C tokens (allocation once per call)."""
+    import statistics
     from workloads import make_decode_tokens_device, make_qkv_device, make_weights
     dev = torch.device("cuda:0")
     tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
@@ -293,8 +348,7 @@ def bench_decode(args, lola, torch, wl):
     y = torch.empty(wl.B, wl.h, wl.d_v, dtype=tdt, device=dev)
     steps = wl.decode_steps
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    best = None
-    kern_ms = None
+    walls, kerns = [], []
     for run in range(args.decode_runs + 1):      # first run is warm-up
         st.restore(snap)
         torch.cuda.synchronize()
@@ -305,10 +359,13 @@ def bench_decode(args, lola, torch, wl):
         evs[steps].record()
         torch.cuda.synchronize()
         el = time.perf_counter() - t0
-        if run > 0 and (best is None or el < best):
-            best = el
-            kern_ms = sum(evs[s].elapsed_time(evs[s + 1]) for s in range(steps)) / steps
-    log(f"decode: {best / steps * 1e3:.3f} ms/step wall, kernel {kern_ms:.3f} ms/step")
+        if run > 0:
+            walls.append(el)
+            kerns.append(sum(evs[s].elapsed_time(evs[s + 1]) for s in range(steps)) / steps)
+    wall = statistics.median(walls)
+    kern_ms = statistics.median(kerns)
+    log(f"decode: {wall / steps * 1e3:.3f} ms/step wall (median of {len(walls)} runs), kernel {kern_ms:.4f} ms/step "
+        f"(min {min(kerns):.4f})")
     # multi-token decode: the same tokens in calls of C_DEC tokens (allocation once per call)
     c_dec = MULTI_TOKEN_C
     calls = steps // c_dec
@@ -316,7 +373,7 @@ def bench_decode(args, lola, torch, wl):
                    for x in (dq, dk, dv)) for c in range(calls)]
     ws_m = torch.empty(lola.lola_workspace_bytes(st, c_dec, c_dec), dtype=torch.uint8, device=dev)
     ym = torch.empty(wl.B, wl.h, c_dec, wl.d_v, dtype=tdt, device=dev)
-    best_m = None
+    walls_m = []
     for run in range(args.decode_runs + 1):
         st.restore(snap)
         torch.cuda.synchronize()
@@ -324,13 +381,55 @@ def bench_decode(args, lola, torch, wl):
         for mq, mk, mv in parts:
             lola.lola_prefill(st, phi, mq, mk, mv, c_dec, y=ym, workspace=ws_m)
         torch.cuda.synchronize()
-        el = time.perf_counter() - t0
-        if run > 0 and (best_m is None or el < best_m):
-            best_m = el
+        if run > 0:
+            walls_m.append(time.perf_counter() - t0)
+    best_m = statistics.median(walls_m)
     log(f"multi-token decode ({c_dec} tokens per call): {best_m / calls * 1e3:.3f} ms/call")
     multi = {"value": round(wl.B * calls * c_dec / best_m, 1), "unit": "decode tokens/s", "tokens_per_call": c_dec,
              "ms_per_call": round(best_m / calls * 1e3, 4)}
-    return best, kern_ms, multi
+    return {"wall": wall, "kern_ms": kern_ms, "kern_ms_min": min(kerns), "runs": len(walls), "multi": multi}
+
+
+def bench_peaks(lola, torch):
+    """The device's attainable dense bf16 matrix rate (an MFMA loop from registers) and streaming copy
+    bandwidth (a 4 GiB device-to-device copy), each the best of several event-timed launches."""
+    import ctypes
+    lib = lola._b.load()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    wgs, iters = 8 * torch.cuda.get_device_properties(dev).multi_processor_count, 2048
+    out = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+    flop = wgs * 4 * 4 * iters * 32768.0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = None
+    for i in range(6):
+        e0.record()
+        lola._b.check("lola_peak_mfma_bf16", lib.lola_peak_mfma_bf16(wgs, iters, ctypes.c_void_p(out.data_ptr()), stream))
+        e1.record()
+        e1.synchronize()
+        if i > 0:
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+    mfma = flop / (best * 1e-3) / 1e12
+    nbytes = 4 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    bestc = None
+    for i in range(6):
+        e0.record()
+        lola._b.check("lola_peak_copy", lib.lola_peak_copy(src.data_ptr(), dst.data_ptr(), nbytes, stream))
+        e1.record()
+        e1.synchronize()
+        if i > 0:
+            ms = e0.elapsed_time(e1)
+            bestc = ms if bestc is None else min(bestc, ms)
+    copy = 2.0 * nbytes / (bestc * 1e-3) / 1e9
+    del src, dst
+    log(f"peaks: bf16 MFMA loop {mfma:.1f} TFLOP/s ({best:.3f} ms), copy {copy:.1f} GB/s ({bestc:.3f} ms)")
+    return {"mfma_bf16_tflops": round(mfma, 1), "copy_gbs": round(copy, 1),
+            "mfma_loop": f"{wgs} workgroups x 4 waves x {4 * iters} v_mfma_f32_32x32x16_bf16 per wave, best of 5",
+            "copy": f"{nbytes} bytes read + written, 16-byte pieces, best of 5",
+            "vendor": {"mfma_bf16_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS}}
 
 
 def _oracle_head(job):
@@ -344,46 +443,67 @@ def _oracle_head(job):
 
 
 def cpu_baseline(wl, heads: int):
-    """The fp64 oracle, as it stands, on `heads` full heads of the headline workload."""
+    """The fp64 oracle, as it stands, on `heads` full (sequence, head) pairs of the headline workload,
+    one pair per worker process with BLAS pinned to one thread in each."""
     import concurrent.futures
     import multiprocessing
     from workloads import make_qkv, make_weights
-    W = make_weights(wl)
-    q, k, v = make_qkv(wl)
     heads = min(heads, wl.B * wl.h)
+    W = make_weights(wl)
+    bsel = max(1, min(wl.B, (heads + wl.h - 1) // wl.h))
+    q, k, v = make_qkv(wl, B=bsel)
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count() or 1
     workers = max(1, min(16, cores, heads))
-    jobs = [dict(phi=wl.phi, W=W, q=q[0, h], k=k[0, h], v=v[0, h], C=wl.C, eta=wl.eta, lam=wl.lam, D=wl.D)
-            for h in range(heads)]
-    ctx = multiprocessing.get_context("spawn")
-    with concurrent.futures.ProcessPoolExecutor(max_workers=workers, mp_context=ctx) as ex:
-        list(ex.map(_oracle_head, jobs[:1]))          # start the workers before timing
-        t0 = time.perf_counter()
-        list(ex.map(_oracle_head, jobs))
-        wall = time.perf_counter() - t0
-    layer_tokens = wl.n * heads / (wl.B * wl.h)        # tokens of the whole layer this sample equals
-    return {"value": layer_tokens / wall, "unit": "prefill tokens/s", "cores": workers, "kind": "oracle",
-            "sample": f"{heads} of {wl.B * wl.h} (sequence, head) pairs of the headline workload, full "
-                      f"n = {wl.n} each, fp64 numpy, {workers} worker processes; value = "
-                      f"{wl.n} * {heads}/{wl.B * wl.h} layer tokens / {wall:.2f} s wall"}
+    pairs = [(b, h) for b in range(bsel) for h in range(wl.h)][:heads]
+    jobs = [dict(phi=wl.phi, W=W, q=q[b, h], k=k[b, h], v=v[b, h], C=wl.C, eta=wl.eta, lam=wl.lam, D=wl.D)
+            for (b, h) in pairs]
+    # spawned workers inherit these before they import numpy: one BLAS thread per worker
+    pinned = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS")
+    saved = {key: os.environ.get(key) for key in pinned}
+    for key in pinned:
+        os.environ[key] = "1"
+    try:
+        ctx = multiprocessing.get_context("spawn")
+        with concurrent.futures.ProcessPoolExecutor(max_workers=workers, mp_context=ctx) as ex:
+            list(ex.map(_oracle_head, [dict(jobs[0], q=jobs[0]["q"][:8], k=jobs[0]["k"][:8], v=jobs[0]["v"][:8])] * workers))
+            t0 = time.perf_counter()
+            list(ex.map(_oracle_head, jobs))
+            wall = time.perf_counter() - t0
+    finally:
+        for key, val in saved.items():
+            if val is None:
+                os.environ.pop(key, None)
+            else:
+                os.environ[key] = val
+    layer_tokens = wl.B * wl.n * heads / (wl.B * wl.h)        # tokens of the whole layer this sample equals
+    return {"value": round(layer_tokens / wall, 2), "unit": "prefill tokens/s", "cores": workers, "kind": "oracle",
+            "host_cores": cores, "workers": workers, "blas_threads_per_worker": 1,
+            "wall_s": round(wall, 2), "core_seconds": round(wall * workers, 1),
+            "sample": f"{heads} of {wl.B * wl.h} (sequence, head) pairs of {wl.name}, full n = {wl.n} each, "
+                      f"fp64 numpy, {workers} worker processes with one BLAS thread each on {cores} host cores; "
+                      f"value = {wl.B * wl.n} * {heads}/{wl.B * wl.h} layer tokens / {wall:.2f} s wall"}
 
 
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--decode-runs", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=100, help="timed steps of the headline prefill")
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--leg-steps", type=int, default=20, help="timed steps of the other prefill legs")
+    ap.add_argument("--decode-runs", type=int, default=10)
+    ap.add_argument("--headline", type=int, default=3, choices=(2, 3, 5), help="workload of the headline line")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=16)
+    ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-legs", action="store_true", help="skip the other prefill workloads")
     ap.add_argument("--no-collisions", action="store_true")
     ap.add_argument("--no-options", action="store_true")
     ap.add_argument("--no-hola", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -405,59 +525,76 @@ def main() -> int:
         src = torch.ones(n, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        lola._b.check("lola_peak_copy", lola._b.load().lola_peak_copy(src.data_ptr(), dst.data_ptr(), n * 4,
+                                                                     torch.cuda.current_stream().cuda_stream))
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n * 4}))
         return 0
-    wl = CONFIGS[2]
     src_hash = kernel_source_hash()
     if args.no_prefill:        # profiling mode: the decode workload only
         dwl = CONFIGS[4]
-        best, kern_ms, _ = bench_decode(args, lola, torch, dwl)
-        print(json.dumps({"decode_ms_per_step": best / dwl.decode_steps * 1e3, "decode_kernel_ms": kern_ms}))
+        r = bench_decode(args, lola, torch, dwl)
+        print(json.dumps({"decode_ms_per_step": r["wall"] / dwl.decode_steps * 1e3, "decode_kernel_ms": r["kern_ms"]}))
         return 0
-    elapsed, kern = bench_prefill(args, lola, torch, wl)
-    ms_per_step = elapsed / args.steps * 1e3
-    tokens = wl.B * wl.n
-    value = tokens * args.steps / elapsed
-    fl = prefill_flops(wl)
+    wl = CONFIGS[args.headline]
+    head = prefill_report(wl, bench_prefill(args, lola, torch, wl))
+    kern = head["kernels_ms_sequential"]
     dominant = max(("chain", "readout"), key=lambda k_: kern[k_])
-    ach = fl[dominant] / (kern[dominant] * 1e-3) / 1e12
-    traffic = load_traffic(dominant)
-    roofline = {"bound": "mfma", "kernel": f"lola_{dominant}", "achieved": round(ach, 3),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 5),
-                "traffic": traffic, "kernel_ms": round(kern[dominant], 4),
-                "algorithmic_flop_per_launch": fl[dominant]}
-    out = {"metric": METRIC, "value": round(value, 1), "unit": "prefill tokens/s", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+    fr = head["kernel_fractions"][dominant]
+    roofline = {"bound": "mfma", "kernel": f"lola_{dominant}", "achieved": fr["achieved_tflops"],
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": fr["frac"],
+                "traffic": load_traffic(dominant), "kernel_ms": fr["kernel_ms"],
+                "algorithmic_flop_per_launch": fr["algorithmic_flop_per_launch"]}
+    out = {"metric": METRIC, "value": head["tokens_per_s"], "unit": "prefill tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-           "data": "synthetic (seeded N(0,1) q/k/v, 2% keys x4)",
+           "data": "synthetic: seeded N(0,1) q/k/v rounded to bf16, seeded N(0, 1/d_k) feature weights",
            "config": {"workload": wl.name, "B": wl.B, "heads": wl.h, "n": wl.n, "d_k": wl.d_k,
                       "d_v": wl.d_v, "D": wl.D, "phi": wl.phi, "C": wl.C, "eta": wl.eta, "lambda": wl.lam},
            "roofline": roofline,
-           "kernels_ms": {k_: round(v_, 4) for k_, v_ in kern.items()},
+           "prefill_call_ms": head["prefill_call_ms"],
+           "kernels_ms": kern,
+           "kernel_fractions": head["kernel_fractions"],
+           "prefill_mfma_frac_whole_step": head["mfma_frac_whole_step"],
+           "algorithmic_flop_per_step": head["algorithmic_flop_per_step"],
            "kernel_source_hash": src_hash}
-    all_fl = fl["chain"] + fl["readout"]
-    out["prefill_mfma_frac_whole_step"] = round(all_fl / (elapsed / args.steps) / 1e12 / PEAK_BF16_TFLOPS, 5)
+    if not args.no_peaks:
+        pk = bench_peaks(lola, torch)
+        pk["roofline_frac_vs_measured"] = round(roofline["achieved"] / pk["mfma_bf16_tflops"], 5)
+        out["peaks_measured"] = pk
+    if not args.no_legs:
+        legs = {}
+        for cid in (2, 3, 5):
+            if cid == args.headline:
+                continue
+            lw = CONFIGS[cid]
+            legs[lw.name] = prefill_report(lw, bench_prefill(args, lola, torch, lw, steps=args.leg_steps,
+                                                             warmup=max(2, args.warmup // 2), kernel_steps=5))
+        out["prefill_legs"] = legs
     if not args.no_decode:
         dwl = CONFIGS[4]
-        best, kern_ms, multi = bench_decode(args, lola, torch, dwl)
-        per_step = best / dwl.decode_steps
+        r = bench_decode(args, lola, torch, dwl)
+        per_step = r["wall"] / dwl.decode_steps
         byts = decode_bytes_per_seq_head(dwl) * dwl.B * dwl.h
-        ach_d = byts / (kern_ms * 1e-3) / 1e9
-        out["decode"] = {"value": round(dwl.B * dwl.decode_steps / best, 1), "unit": "decode tokens/s",
-                         "workload": dwl.name, "ms_per_step": round(per_step * 1e3, 4),
+        ach_d = byts / (r["kern_ms"] * 1e-3) / 1e9
+        out["decode"] = {"value": round(dwl.B * dwl.decode_steps / r["wall"], 1), "unit": "decode tokens/s",
+                         "workload": dwl.name, "ms_per_step": round(per_step * 1e3, 4), "runs": r["runs"],
                          "roofline": {"bound": "hbm", "kernel": "lola_decode", "achieved": round(ach_d, 1),
                                       "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach_d / PEAK_HBM_GBS, 4),
-                                      "traffic": load_traffic("decode"),
-                                      "kernel_ms": round(kern_ms, 4), "algorithmic_bytes_per_launch": byts},
-                         "multi_token": multi}
+                                      "traffic": load_traffic("decode"), "kernel_ms": round(r["kern_ms"], 4),
+                                      "kernel_ms_min": round(r["kern_ms_min"], 4),
+                                      "algorithmic_bytes_per_launch": byts},
+                         "multi_token": r["multi"]}
+        if "peaks_measured" in out:
+            out["decode"]["roofline"]["frac_vs_measured_copy"] = round(ach_d / out["peaks_measured"]["copy_gbs"], 4)
+    import argparse as _ap
+    leg_args = _ap.Namespace(**{**vars(args), "steps": args.leg_steps, "warmup": max(2, args.warmup // 2)})
     if not args.no_collisions:
-        out["collision_map"] = bench_collisions(args, lola, torch, wl)
+        out["collision_map"] = bench_collisions(leg_args, lola, torch, CONFIGS[2])
     if not args.no_options:
-        out["options"] = bench_options(args, lola, torch, wl)
+        out["options"] = bench_options(leg_args, lola, torch, CONFIGS[2])
     if not args.no_hola:
-        out["hola"] = bench_hola(args, lola, torch, wl)
+        out["hola"] = bench_hola(leg_args, lola, torch, CONFIGS[2])
     if not args.no_cpu_baseline:
         log("cpu baseline: running the oracle ...")
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_heads)

@@ -16,7 +16,7 @@ from ._binding import (LOLA_BF16, LOLA_EDEVICE, LOLA_EINVAL, LOLA_EUNSUPPORTED, 
                        LOLA_PHI_ELU1, LOLA_PHI_SOFTMAX_PM, LOLA_READ_ALL, LOLA_READ_SPARSE,
                        LOLA_READ_STATE, LOLA_READ_WINDOW, SCORE_RULES, LolaError)
 
-__all__ = ["LolaState", "LolaPhi", "lola_state_init", "lola_workspace_bytes", "lola_prefill",
+__all__ = ["LolaState", "LolaPhi", "LolaOverlap", "lola_state_init", "lola_workspace_bytes", "lola_prefill",
            "lola_decode_step", "lola_sre_collisions", "LolaError", "LOLA_OK", "LOLA_EINVAL", "LOLA_EUNSUPPORTED",
            "LOLA_EDEVICE", "library_path", "PHI_KINDS", "LOLA_READ_STATE", "LOLA_READ_SPARSE",
            "LOLA_READ_WINDOW", "LOLA_READ_ALL", "SCORE_RULES", "hola_workspace_bytes", "hola_prefill"]
@@ -93,6 +93,20 @@ class LolaState:
         self.c.t = snap["t"]
 
 
+class LolaOverlap:
+    """A second stream and its events (lola_overlap) for the overlapped prefill schedule, owned here by
+    torch.  One object serves any number of calls issued one after another from one thread."""
+
+    def __init__(self, device="cuda"):
+        self.stream = torch.cuda.Stream(device=device)      # default priority
+        self.events = [torch.cuda.Event() for _ in range(_b.LOLA_OVERLAP_EVENTS)]
+        with torch.cuda.stream(self.stream):
+            for e in self.events:
+                e.record()                                    # creates the HIP event behind it
+        self.c = _b.LolaOverlap(self.stream.cuda_stream,
+                                (ctypes.c_void_p * _b.LOLA_OVERLAP_EVENTS)(*[e.cuda_event for e in self.events]))
+
+
 def lola_workspace_bytes(state: LolaState, n_max: int, C: int) -> int:
     return int(_b.load().lola_workspace_bytes(ctypes.byref(state.c), n_max, C))
 
@@ -101,22 +115,26 @@ def lola_state_init(state: LolaState, stream=None) -> None:
     _b.check("lola_state_init", _b.load().lola_state_init(ctypes.byref(state.c), _stream(stream)))
 
 
-def _options(read_mask: int, score_rule: str):
+def _options(read_mask: int, score_rule: str, overlap: Optional[LolaOverlap] = None):
     """ctypes options, or None for the defaults."""
-    if read_mask == LOLA_READ_ALL and score_rule == "sre":
+    if read_mask == LOLA_READ_ALL and score_rule == "sre" and overlap is None:
         return None
-    return _b.LolaOptions(read_mask, SCORE_RULES[score_rule], (ctypes.c_int32 * 2)(0, 0))
+    ov = ctypes.pointer(overlap.c) if overlap is not None else None
+    return _b.LolaOptions(read_mask, SCORE_RULES[score_rule], (ctypes.c_int32 * 2)(0, 0), ov)
 
 
 def lola_prefill(state: LolaState, phi: LolaPhi, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                  C: int, y: Optional[torch.Tensor] = None, fold_at: Optional[torch.Tensor] = None,
                  workspace: Optional[torch.Tensor] = None, stream=None, events=None,
-                 read_mask: int = LOLA_READ_ALL, score_rule: str = "sre"):
+                 read_mask: int = LOLA_READ_ALL, score_rule: str = "sre",
+                 overlap: Optional[LolaOverlap] = None):
     """Chunked prefill of q, k, v [B][h][n][d]; returns (y, fold_at).  Asynchronous on `stream`.
 
     ``events``: optional 5 torch.cuda.Event (created with enable_timing=True) recorded at the kernel
     boundaries: before the feature kernel, then after the feature, chain, read-out and commit kernels.
-    ``read_mask`` / ``score_rule``: see lola_options (lola_prefill_ex); not combinable with events."""
+    ``read_mask`` / ``score_rule``: see lola_options (lola_prefill_ex); not combinable with events.
+    ``overlap``: a LolaOverlap whose stream runs the read-out beside the allocation chain (the
+    results are the same bits as without it)."""
     n = q.shape[2]
     if y is None:
         y = torch.empty(q.shape[0], q.shape[1], n, v.shape[3], dtype=v.dtype, device=v.device)
@@ -126,7 +144,7 @@ def lola_prefill(state: LolaState, phi: LolaPhi, q: torch.Tensor, k: torch.Tenso
     lib = _b.load()
     args = (ctypes.byref(state.c), ctypes.byref(phi.c), _ptr(q), _ptr(k), _ptr(v), n, C, _ptr(y),
             _ptr(fold_at), _ptr(workspace), workspace.numel(), _stream(stream))
-    opts = _options(read_mask, score_rule)
+    opts = _options(read_mask, score_rule, overlap)
     if opts is not None:
         if events is not None:
             raise ValueError("events are recorded by the default-options entry point only")

@@ -23,7 +23,8 @@ LOLA_PHI_SOFTMAX_PM = 1
 
 EXPORTED = ("lola_workspace_bytes", "lola_state_init", "lola_prefill", "lola_prefill_ex",
             "lola_prefill_profiled", "lola_decode_step", "lola_decode_step_ex", "lola_sre_collisions",
-            "lola_status_string", "hola_workspace_bytes", "hola_prefill")
+            "lola_status_string", "hola_workspace_bytes", "hola_prefill", "lola_peak_mfma_bf16",
+            "lola_peak_copy")
 LOLA_READ_STATE = 1
 LOLA_READ_SPARSE = 2
 LOLA_READ_WINDOW = 4
@@ -46,9 +47,16 @@ class LolaState(ctypes.Structure):
                 ("cache_score", ctypes.c_void_p)]
 
 
+LOLA_OVERLAP_EVENTS = 9
+
+
+class LolaOverlap(ctypes.Structure):
+    _fields_ = [("stream", ctypes.c_void_p), ("events", ctypes.c_void_p * LOLA_OVERLAP_EVENTS)]
+
+
 class LolaOptions(ctypes.Structure):
     _fields_ = [("read_mask", ctypes.c_int32), ("score_rule", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 2)]
+                ("reserved", ctypes.c_int32 * 2), ("overlap", ctypes.POINTER(LolaOverlap))]
 
 
 class LolaError(RuntimeError):
@@ -94,6 +102,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hola_prefill.argtypes = [i32, i32, i32, i32, i64, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                  vp, vp, vp, vp, sz, vp]
     lib.hola_prefill.restype = i32
+    lib.lola_peak_mfma_bf16.argtypes = [i32, i32, vp, vp]
+    lib.lola_peak_mfma_bf16.restype = i32
+    lib.lola_peak_copy.argtypes = [vp, vp, sz, vp]
+    lib.lola_peak_copy.restype = i32
     lib.lola_status_string.argtypes = [i32]
     lib.lola_status_string.restype = ctypes.c_char_p
     _lib = lib

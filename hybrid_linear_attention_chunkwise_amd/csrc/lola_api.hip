@@ -49,6 +49,11 @@ lola_status check_options(const lola_state* st, const lola_options* opt) {
     if ((opt->read_mask & ~LOLA_READ_ALL) != 0 || !(opt->read_mask & LOLA_READ_WINDOW)) return LOLA_EINVAL;
     if (opt->score_rule < LOLA_SCORE_SRE || opt->score_rule > LOLA_SCORE_ATTN) return LOLA_EINVAL;
     if (opt->reserved[0] != 0 || opt->reserved[1] != 0) return LOLA_EINVAL;
+    if (opt->overlap) {
+        if (!opt->overlap->stream) return LOLA_EINVAL;
+        for (int i = 0; i < LOLA_OVERLAP_EVENTS; ++i)
+            if (!opt->overlap->events[i]) return LOLA_EINVAL;
+    }
     if (opt->score_rule != LOLA_SCORE_SRE) {
         if (st->eta > 0 && (!st->win_score || !aligned16(st->win_score))) return LOLA_EINVAL;
         if (st->lambda > 0 && (!st->cache_score || !aligned16(st->cache_score))) return LOLA_EINVAL;
@@ -188,6 +193,7 @@ static lola_status prefill_impl(lola_state* st, const lola_phi* phi, const void*
     if (rc != LOLA_OK) return rc;
     rc = check_prefill_config(st, n, C);
     if (rc != LOLA_OK) return rc;
+    if (opt && opt->overlap && opt->overlap->stream == stream) return LOLA_EINVAL;
     if (n == 0) return LOLA_OK;
     if (!q || !k || !v || !y || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y)) return LOLA_EINVAL;
     if (fold_at && !aligned16(fold_at)) return LOLA_EINVAL;
@@ -217,8 +223,15 @@ static lola_status prefill_impl(lola_state* st, const lola_phi* phi, const void*
     a.ws = reinterpret_cast<char*>(workspace);
     a.L = L;
     if ((int64_t)a.BH * a.nchunks * a.nqt > (int64_t)INT_MAX) return LOLA_EUNSUPPORTED;
+    lola::Overlap ov;
+    const bool use_ov = opt && opt->overlap;
+    if (use_ov) {
+        static_assert(LOLA_OVERLAP_EVENTS == lola::kOverlapEvents, "overlap event count");
+        ov.stream = (hipStream_t)opt->overlap->stream;
+        for (int i = 0; i < lola::kOverlapEvents; ++i) ov.ev[i] = (hipEvent_t)opt->overlap->events[i];
+    }
     const hipError_t e = lola::launch_prefill(a, st->dtype, st->d_k, phi->kind, (hipStream_t)stream,
-                                              reinterpret_cast<hipEvent_t const*>(events));
+                                              reinterpret_cast<hipEvent_t const*>(events), use_ov ? &ov : nullptr);
     if (e != hipSuccess) return LOLA_EDEVICE;
     if (getenv("LOLA_DEBUG_SYNC") && hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return LOLA_EDEVICE;
     st->t += n;

@@ -158,7 +158,7 @@ struct HolaArgs {
     char* ws;
     HolaLayout L;
 };
-int device_cus();   // compute units of the current device (256 if the query fails)
+int device_cus();   // compute units of the current device, queried per call (256 if the query fails)
 hipError_t launch_hola(const HolaArgs& a, int dtype, int d, hipStream_t stream);
 
 struct InitArgs {
@@ -177,8 +177,14 @@ hipError_t launch_init(const InitArgs& a, hipStream_t stream);
 // Query-accumulated scores of the call's keys (after the feature kernel, before the chain).
 template <typename T, int DK>
 hipError_t launch_qscore_t(const PrefillArgs& a, hipStream_t stream);
+// The caller's second stream and events for the overlapped schedule (nullptr: sequential).
+constexpr int kOverlapEvents = 9;
+struct Overlap {
+    hipStream_t stream;
+    hipEvent_t ev[kOverlapEvents];
+};
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int d, int phi_kind, hipStream_t stream,
-                          hipEvent_t const* events = nullptr);
+                          hipEvent_t const* events = nullptr, const Overlap* overlap = nullptr);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int d, int phi_kind, hipStream_t stream);
 // Register-resident decode for bf16 storage, when the cache and window fit its tiles.
 bool decode_fast_fits(int d, int lam, int eta);

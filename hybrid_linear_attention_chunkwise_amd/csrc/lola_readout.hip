@@ -16,7 +16,6 @@
 #include "lola_common.hpp"
 #include "lola_internal.hpp"
 
-#include <mutex>
 #include <type_traits>
 
 namespace lola {
@@ -485,38 +484,10 @@ static hipError_t launch_commit(const PrefillArgs& a, hipStream_t stream) {
 template <typename T, int DK, int PHI>
 hipError_t launch_chain_t(const PrefillArgs& a, hipStream_t stream);
 
-// A second stream per device for the read-out, with the events that order it against the caller's
-// stream.  Created on first use with default priority and kept for the life of the process; the
-// mutex serialises enqueueing (the events are reused by every call).
-constexpr int kMaxSegments = 8;
+// The overlapped schedule walks the chain in at most kMaxSegments chunk ranges; it takes one event per
+// range boundary plus one to join the second stream back (kOverlapEvents in all), all the caller's.
+constexpr int kMaxSegments = kOverlapEvents - 1;
 constexpr int kOverlapMinChunks = 8;
-struct SideStream {
-    hipStream_t stream = nullptr;
-    hipEvent_t seg[kMaxSegments] = {};
-    hipEvent_t join = nullptr;
-    std::mutex mu;
-};
-
-static SideStream* side_stream() {
-    static std::mutex init_mu;
-    static SideStream* per_dev[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-    std::lock_guard<std::mutex> guard(init_mu);
-    if (per_dev[dev]) return per_dev[dev];
-    SideStream* s = new SideStream();
-    bool ok = hipStreamCreateWithFlags(&s->stream, hipStreamNonBlocking) == hipSuccess;
-    for (int i = 0; ok && i < kMaxSegments; ++i)
-        ok = hipEventCreateWithFlags(&s->seg[i], hipEventDisableTiming) == hipSuccess;
-    ok = ok && hipEventCreateWithFlags(&s->join, hipEventDisableTiming) == hipSuccess;
-    if (!ok) {
-        (void)hipGetLastError();
-        delete s;                       // handles created so far are left to the process end
-        return nullptr;
-    }
-    per_dev[dev] = s;
-    return s;
-}
 
 static hipError_t record(hipEvent_t const* ev, int i, hipStream_t stream) {
     if (!ev || !ev[i]) return hipSuccess;
@@ -569,23 +540,19 @@ static int split_chunks(int nchunks, int per_chunk, int ncu, int* bounds, int ma
 }
 
 int device_cus() {
-    static int ncu = 0;
-    if (ncu == 0) {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-            ncu = v;
-        else
-            ncu = 256;
-    }
-    return ncu;
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+        return v;
+    (void)hipGetLastError();
+    return 256;
 }
 
 template <typename T, int DK, int PHI>
-hipError_t launch_prefill_t(const PrefillArgs& a0, hipStream_t stream, hipEvent_t const* ev) {
+hipError_t launch_prefill_t(const PrefillArgs& a0, hipStream_t stream, hipEvent_t const* ev, const Overlap* ov) {
     PrefillArgs a = a0;
     hipError_t e;
-    SideStream* side = (ev == nullptr && a.nchunks >= kOverlapMinChunks) ? side_stream() : nullptr;
+    const Overlap* side = (ev == nullptr && a.nchunks >= kOverlapMinChunks) ? ov : nullptr;
     if (side == nullptr) {
         // one chain launch, then the read-out: used when timing the kernels one by one
         if ((e = record(ev, 0, stream)) != hipSuccess) return e;
@@ -602,10 +569,9 @@ hipError_t launch_prefill_t(const PrefillArgs& a0, hipStream_t stream, hipEvent_
         return record(ev, 4, stream);
     }
     // Overlapped: the chain walks the chunk ranges on the caller's stream; the read-out of a range
-    // runs on the side stream as soon as the chain has finished it, beside the next range's chain.
-    // The side stream forks from and joins back into the caller's stream, so the call stays ordered
-    // (and capturable) as one unit.
-    std::lock_guard<std::mutex> guard(side->mu);
+    // runs on the caller's second stream as soon as the chain has finished it, beside the next range's
+    // chain.  The second stream forks from and joins back into the call's stream through the caller's
+    // events (one per range boundary, one for the join), so the call stays ordered as one unit.
     int bounds[kMaxSegments + 1];
     const int nseg = split_chunks(a.nchunks, a.BH * a.nqt, device_cus(), bounds, kMaxSegments);
     if ((e = launch_phi_t<T, DK, PHI>(a, stream)) != hipSuccess) return e;
@@ -614,9 +580,9 @@ hipError_t launch_prefill_t(const PrefillArgs& a0, hipStream_t stream, hipEvent_
     // cross-stream hop; the earlier ranges' read-outs run on the side stream.
     for (int i = 0; i < nseg; ++i) {
         if ((e = launch_chain_range<T, DK, PHI>(a, bounds[i], bounds[i + 1], stream)) != hipSuccess) return e;
-        if ((e = hipEventRecord(side->seg[i], stream)) != hipSuccess) return e;
+        if ((e = hipEventRecord(side->ev[i], stream)) != hipSuccess) return e;
         if (i == nseg - 1) break;
-        if ((e = hipStreamWaitEvent(side->stream, side->seg[i], 0)) != hipSuccess) return e;
+        if ((e = hipStreamWaitEvent(side->stream, side->ev[i], 0)) != hipSuccess) return e;
         if ((e = launch_readout<T, DK, PHI>(a, bounds[i], bounds[i + 1], side->stream, false)) != hipSuccess) return e;
     }
     if ((e = launch_readout<T, DK, PHI>(a, bounds[nseg - 1], bounds[nseg], stream, nseg > 1)) != hipSuccess) return e;
@@ -629,23 +595,23 @@ hipError_t launch_prefill_t(const PrefillArgs& a0, hipStream_t stream, hipEvent_
     a.c_end = a.nchunks;
     const bool fresh = a.t0 == 0;
     if (fresh) {
-        if ((e = hipStreamWaitEvent(side->stream, side->seg[nseg - 1], 0)) != hipSuccess) return e;
+        if ((e = hipStreamWaitEvent(side->stream, side->ev[nseg - 1], 0)) != hipSuccess) return e;
         if ((e = launch_commit<T, DK>(a, side->stream)) != hipSuccess) return e;
     }
-    if ((e = hipEventRecord(side->join, side->stream)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(stream, side->join, 0)) != hipSuccess) return e;
+    if ((e = hipEventRecord(side->ev[kOverlapEvents - 1], side->stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(stream, side->ev[kOverlapEvents - 1], 0)) != hipSuccess) return e;
     if (!fresh) return launch_commit<T, DK>(a, stream);
     return hipSuccess;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int d, int phi_kind, hipStream_t stream,
-                          hipEvent_t const* ev) {
+                          hipEvent_t const* ev, const Overlap* ov) {
     if (dtype == 0) {
-        if (d == 64) return phi_kind ? launch_prefill_t<float, 64, 1>(a, stream, ev) : launch_prefill_t<float, 64, 0>(a, stream, ev);
-        return phi_kind ? launch_prefill_t<float, 128, 1>(a, stream, ev) : launch_prefill_t<float, 128, 0>(a, stream, ev);
+        if (d == 64) return phi_kind ? launch_prefill_t<float, 64, 1>(a, stream, ev, ov) : launch_prefill_t<float, 64, 0>(a, stream, ev, ov);
+        return phi_kind ? launch_prefill_t<float, 128, 1>(a, stream, ev, ov) : launch_prefill_t<float, 128, 0>(a, stream, ev, ov);
     }
-    if (d == 64) return phi_kind ? launch_prefill_t<bf16, 64, 1>(a, stream, ev) : launch_prefill_t<bf16, 64, 0>(a, stream, ev);
-    return phi_kind ? launch_prefill_t<bf16, 128, 1>(a, stream, ev) : launch_prefill_t<bf16, 128, 0>(a, stream, ev);
+    if (d == 64) return phi_kind ? launch_prefill_t<bf16, 64, 1>(a, stream, ev, ov) : launch_prefill_t<bf16, 64, 0>(a, stream, ev, ov);
+    return phi_kind ? launch_prefill_t<bf16, 128, 1>(a, stream, ev, ov) : launch_prefill_t<bf16, 128, 0>(a, stream, ev, ov);
 }
 
 }  // namespace lola

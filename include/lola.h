@@ -24,12 +24,14 @@
  *
  * Conventions for every entry point:
  *   - All array pointers are DEVICE pointers owned by the caller.  The library never allocates,
- *     frees or synchronises; all work is enqueued on `stream` (a hipStream_t; NULL = default stream)
- *     and the call returns before it completes.
+ *     frees or synchronises; all work is enqueued on `stream` (a hipStream_t; NULL = default stream),
+ *     or on a second stream the caller hands to lola_prefill_ex (lola_overlap), and the call returns
+ *     before it completes.
  *   - Arguments are validated on the host before anything is enqueued.  A failed validation returns
  *     LOLA_EINVAL or LOLA_EUNSUPPORTED and leaves the state (device arrays and `t`) untouched.
  *     A launch failure returns LOLA_EDEVICE (the state may then be partially updated).
- *   - No global state: distinct states may be driven from different threads and streams.
+ *   - No global state: the library keeps no stream, event, lock or cached device property between
+ *     calls, so distinct states may be driven from different threads and streams.
  *   - Supported shapes (v1): d_k == d_v in {64, 128}, D == 128, 0 <= lambda <= 1024, 1 <= C <= 128,
  *     eta >= 0, positions below 2^31.
  *   - Device arrays must be 16-byte aligned.
@@ -119,10 +121,28 @@ typedef struct lola_state {
 #define LOLA_SCORE_RATIO 3
 #define LOLA_SCORE_ATTN 4
 
+/* Resources for the overlapped prefill schedule, created and owned by the caller.  With them, the
+ * read-out of chunk ranges the allocation chain has finished runs on `stream` below, beside the chain's
+ * next range, which keeps running on the call's stream.  The second stream forks from the call's stream
+ * and joins back into it through `events`, so the whole call still completes in the call's stream order
+ * (later work on that stream sees all of it).  The library creates, keeps and destroys nothing.
+ *   stream  hipStream_t, not NULL and not the call's stream.  Keep it at the default priority.
+ *   events  LOLA_OVERLAP_EVENTS hipEvent_t handles, none NULL (hipEventDisableTiming is enough).
+ * A block may serve any number of calls one after another, also calls whose device work is still
+ * running.  Two calls enqueued at the same time from different host threads must not share a block
+ * (the events are re-recorded by every call). */
+#define LOLA_OVERLAP_EVENTS 9
+typedef struct lola_overlap {
+    void *stream;
+    void *events[LOLA_OVERLAP_EVENTS];
+} lola_overlap;
+
 typedef struct lola_options {
     int32_t read_mask;    /* LOLA_READ_* bits, containing LOLA_READ_WINDOW */
     int32_t score_rule;   /* LOLA_SCORE_* */
     int32_t reserved[2];  /* must be 0 */
+    /* nullable: without it every kernel of the call runs on the call's stream, one after another */
+    const lola_overlap *overlap;
 } lola_options;
 
 /* Bytes of device scratch lola_prefill needs for calls of up to n_max tokens with chunk C, for the
@@ -133,7 +153,8 @@ size_t lola_workspace_bytes(const lola_state *st, int64_t n_max, int32_t C);
  * Window and cache K/V contents are left as they are (they are dead until written). */
 lola_status lola_state_init(lola_state *st, void *stream);
 
-/* Chunked prefill (section 2.6, Eq. (15)) of n new tokens for every sequence and head.
+/* Chunked prefill (section 2.6, Eq. (15)) of n new tokens for every sequence and head, every kernel on
+ * `stream` in turn (lola_prefill_ex with an overlap block runs the read-out beside the chain).
  *   q, k: [B][n_heads][n][d_k], v: [B][n_heads][n][d_v], y (output): [B][n_heads][n][d_v], all in
  *   the state's dtype, contiguous.  Chunk boundaries are t, t+C, t+2C, ... (relative to the call's
  *   starting t).  fold_at (nullable) [B][n_heads][n] int32 receives, for each input token, the
@@ -155,10 +176,12 @@ lola_status lola_prefill_profiled(lola_state *st, const lola_phi *phi, const voi
                                   void *workspace, size_t workspace_bytes, void *stream,
                                   void *const events[5]);
 
-/* lola_prefill with options (NULL = LOLA_READ_ALL and LOLA_SCORE_SRE, which is lola_prefill).
- * A rule other than LOLA_SCORE_SRE needs the state's win_score and cache_score (16-byte aligned).
- * LOLA_EINVAL for a mask without the window or with other bits, an unknown rule, non-zero reserved
- * fields or missing score arrays. */
+/* lola_prefill with options (NULL = LOLA_READ_ALL, LOLA_SCORE_SRE and no overlap, which is
+ * lola_prefill).  A rule other than LOLA_SCORE_SRE needs the state's win_score and cache_score (16-byte
+ * aligned).  LOLA_EINVAL for a mask without the window or with other bits, an unknown rule, non-zero
+ * reserved fields, missing score arrays, or an overlap block with a NULL handle or whose stream is the
+ * call's own.  The overlap changes where the kernels run, never what they compute: results are
+ * bit-identical with and without it. */
 lola_status lola_prefill_ex(lola_state *st, const lola_phi *phi, const void *q, const void *k, const void *v,
                             int64_t n, int32_t C, const lola_options *opt, void *y, int32_t *fold_at,
                             void *workspace, size_t workspace_bytes, void *stream);
@@ -228,6 +251,21 @@ lola_status hola_prefill(int32_t B, int32_t n_heads, int32_t d, int32_t dtype, i
                          const float *gamma_q, const float *gamma_k, const float *sink, const float *gate,
                          void *y, float *S_out, int32_t *cache_pos_out, float *cache_score_out,
                          void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Measurement probes (not part of the method): the device's attainable rates, measured beside the
+ * vendor's peaks so that roofline fractions can be stated against both.
+ * --------------------------------------------------------------------------------------------- */
+
+/* A dense bf16 matrix loop: `workgroups` workgroups of 4 waves; each wave issues 4 * iters
+ * v_mfma_f32_32x32x16_bf16 (32768 FLOP each) from register operands, so one launch performs
+ * workgroups * 4 * 4 * iters * 32768 FLOP.  out: device, workgroups * 256 floats, 16-byte aligned
+ * (one sum per lane, written so the work is kept).  LOLA_EINVAL for non-positive sizes or a bad out. */
+lola_status lola_peak_mfma_bf16(int32_t workgroups, int32_t iters, float *out, void *stream);
+
+/* A streaming device-to-device copy of `bytes` (a multiple of 16; src and dst 16-byte aligned and not
+ * overlapping): each byte is read once and written once.  LOLA_EINVAL for bad pointers or sizes. */
+lola_status lola_peak_copy(const void *src, void *dst, size_t bytes, void *stream);
 
 /* Static, human-readable text for a status code. */
 const char *lola_status_string(lola_status status);

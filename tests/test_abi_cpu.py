@@ -15,7 +15,7 @@ HEADER = os.path.join(ROOT, "include", "lola.h")
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b((?:lola|hola)_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:lola|hola)_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -150,3 +150,40 @@ def test_hola_pointer_validation_without_gpu(lib):
     # an empty call is a no-op that needs no buffers at all
     assert lib.hola_prefill(1, 2, 128, B.LOLA_BF16, 0, 16, 4, None, None, None, None, None, None, None, None,
                             None, None, None, None, None, None, 0, None) == B.LOLA_OK
+
+
+def test_overlap_validation_without_gpu(lib):
+    """An overlap block needs a stream that is not the call's and all of its events; a bad block is
+    rejected before anything is queued (the library owns no stream of its own to fall back on)."""
+    phi = B.LolaPhi(B.LOLA_PHI_SOFTMAX_PM, 128, 128, 0, 0x200000)
+    p = 0x300000
+    good_events = [0x500000 + 0x100 * i for i in range(B.LOLA_OVERLAP_EVENTS)]
+    cases = []
+    for bad in range(B.LOLA_OVERLAP_EVENTS):
+        ev = list(good_events)
+        ev[bad] = 0
+        cases.append((0x600000, ev, None))
+    cases.append((0, good_events, None))              # no second stream
+    cases.append((0x600000, good_events, 0x600000))   # the call's own stream
+    for ov_stream, ev, call_stream in cases:
+        st = _fake_ptrs(_state())
+        ov = B.LolaOverlap(ov_stream, (ctypes.c_void_p * B.LOLA_OVERLAP_EVENTS)(*ev))
+        opt = B.LolaOptions(B.LOLA_READ_ALL, 0, (ctypes.c_int32 * 2)(0, 0), ctypes.pointer(ov))
+        rc = lib.lola_prefill_ex(ctypes.byref(st), ctypes.byref(phi), p, p, p, 16, 16, ctypes.byref(opt), p,
+                                 None, 0x400000, 1 << 40, call_stream)
+        assert rc == B.LOLA_EINVAL
+        assert st.t == 0
+
+
+def test_no_process_wide_handles_in_the_sources():
+    """The library keeps no stream, event, lock or cached device property between calls: no kernel
+    source creates a stream or an event, holds a mutex, or caches a value in a function-local static."""
+    csrc = os.path.join(ROOT, "hybrid_linear_attention_chunkwise_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        text = open(os.path.join(csrc, name)).read()
+        for banned in ("hipStreamCreate", "hipEventCreate", "std::mutex", "<mutex>"):
+            assert banned not in text, (name, banned)
+        for line in text.splitlines():
+            code = line.split("//")[0].strip()
+            if code.startswith("static ") and "=" in code and "constexpr" not in code and "(" not in code.split("=")[0]:
+                raise AssertionError(f"{name}: static data: {line.strip()}")

@@ -47,3 +47,18 @@ def test_multi_gpu_request_is_refused():
                        text=True, timeout=120)
     assert r.returncode != 0
     assert "gpus 1" in r.stderr
+
+
+def test_flop_model_matches_the_scope_table():
+    """The algorithmic work per token and head at the 128-dimensional workloads (C = 64,
+    eta = lambda = 256): features 2 x 2 d D/2, exact branch 2 (d_k + d_v)(eta + lambda), linear read
+    2 D (d_v + 1), intra-chunk term (D + d_v + 1)(C + 1), scoring 2 D (d_v + 1)(C + lambda) / C and fold
+    2 D (d_v + 1) add up to 542,785 FLOP; the chain kernel's share is the scoring and the fold."""
+    import bench
+    from workloads import CONFIGS
+    for cid in (2, 3):
+        fl = bench.prefill_flops(CONFIGS[cid])
+        assert fl["per_token_head"] == 542785
+        units = CONFIGS[cid].B * CONFIGS[cid].h * CONFIGS[cid].n
+        assert fl["chain"] == (165120 + 33024) * units
+        assert abs(fl["phi"] + fl["chain"] + fl["readout"] - fl["total"]) < 1

@@ -22,7 +22,7 @@ def _need_gpu():
     lola._b.load()
 
 
-def _run_config(cfg_id, dtype, heads):
+def _run_config(cfg_id, dtype, heads, replay_only=False):
     wl = CONFIGS[cfg_id]
     W = make_weights(wl)
     q, k, v = make_qkv(wl)
@@ -33,7 +33,9 @@ def _run_config(cfg_id, dtype, heads):
     tol = TL.TIE_BAND if dtype == "f32" else TL.BF16_TOL
     jobs = [dict(phi=wl.phi, W=W, q=q[b, h].astype(np.float64), k=k[b, h].astype(np.float64),
                  v=v[b, h].astype(np.float64), C=wl.C, eta=wl.eta, lam=wl.lam, D=wl.D,
-                 fold_at_gpu=fold[b, h].astype(np.int64), tol=tol) for (b, h) in heads]
+                 fold_at_gpu=fold[b, h].astype(np.int64), tol=tol, replay_only=replay_only,
+                 progress_every=max(1, (wl.n // wl.C) // 8), tag=f"cfg{cfg_id} {dtype} ({b},{h})")
+            for (b, h) in heads]
     print(f"[config {cfg_id}] oracle on {len(heads)} sampled heads ...", flush=True)
     results = TL.run_oracle_heads(jobs)
     reps = []
@@ -62,22 +64,29 @@ def test_config3_sampled(dtype):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_config5_sampled(dtype):
-    _run_config(5, dtype, [(0, 5)])
+    # bf16 membership is graded under the fp64 replay of the GPU schedule (the oracle's own schedule
+    # would only be reported), so the bf16 case runs the replay alone
+    _run_config(5, dtype, [(0, 2), (0, 5)], replay_only=dtype == "bf16")
 
 
-def test_config4_decode_sampled():
-    """64 sequences x 32 heads, 8192-token prior context (prefill), then 256 decode steps."""
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_config4_decode_sampled(dtype):
+    """64 sequences x 32 heads, 8192-token prior context (prefill), then 256 decode steps, all in the
+    benchmark's launch configuration.  fp32 reuses the bf16-representable fixture upcast.  Sampled
+    heads: the prior-context prefill is graded against the oracle, then every decode step against the
+    oracle continuing from the GPU's post-prefill state (every fold validated, see grade_decode_steps)."""
     import hybrid_linear_attention_chunkwise_amd as lola
     from oracle import lola_oracle as O
     wl = CONFIGS[4]
     dev = torch.device("cuda:0")
-    tdt = torch.bfloat16
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     W = make_weights(wl)
     st = lola.LolaState(wl.B, wl.h, wl.d_k, wl.d_v, wl.D, wl.eta, wl.lam, tdt, device=dev)
     phi = lola.LolaPhi(wl.phi, torch.from_numpy(W).to(dev), wl.D)
     lola.lola_state_init(st)
-    qp, kp, vp = make_qkv_device(wl, dev, tdt)
+    qp, kp, vp = (x.to(tdt) for x in make_qkv_device(wl, dev, torch.bfloat16))
     heads = [(0, 0), (17, 5), (63, 31)]
+    print(f"[config 4 {dtype}] prior-context prefill of B={wl.B} h={wl.h} n={wl.n}", flush=True)
     fold = torch.full((wl.B, wl.h, wl.n), -7, dtype=torch.int32, device=dev)
     y, _ = lola.lola_prefill(st, phi, qp, kp, vp, wl.C, fold_at=fold)
     y_pref = torch.stack([y[b, h] for (b, h) in heads]).float().cpu().numpy()
@@ -87,7 +96,8 @@ def test_config4_decode_sampled():
                vp[bh].float().cpu().numpy().astype(np.float64)) for bh in heads}
     del qp, kp, vp
     snap = TL.state_to_host(st)
-    dq, dk, dv = make_decode_tokens_device(wl, dev, tdt)
+    dq, dk, dv = (x.to(tdt) for x in make_decode_tokens_device(wl, dev, torch.bfloat16))
+    print(f"[config 4 {dtype}] {wl.decode_steps} decode steps", flush=True)
     ys, folds = [], []
     for s in range(wl.decode_steps):
         fp = torch.full((wl.B, wl.h), -7, dtype=torch.int32, device=dev)
@@ -98,27 +108,23 @@ def test_config4_decode_sampled():
     ys = torch.stack(ys).cpu().numpy()
     folds = torch.stack(folds).cpu().numpy()
     dqh, dkh, dvh = dq.float().cpu().numpy(), dk.float().cpu().numpy(), dv.float().cpu().numpy()
-    # (1) the prior-context prefill of the sampled heads: oracle replaying the GPU schedule (bf16)
+    # (1) the prior-context prefill of two sampled heads
+    tol = TL.TIE_BAND if dtype == "f32" else TL.BF16_TOL
     jobs = [dict(phi=wl.phi, W=W, q=hq[bh][0], k=hq[bh][1], v=hq[bh][2], C=wl.C, eta=wl.eta, lam=wl.lam,
-                 D=wl.D, fold_at_gpu=fold_h[bh], tol=TL.BF16_TOL) for bh in heads[:2]]
+                 D=wl.D, fold_at_gpu=fold_h[bh], tol=tol) for bh in heads[:2]]
     phi_o = O.make_phi(wl.phi, W)
     for i, (bh, res) in enumerate(zip(heads[:2], TL.run_oracle_heads(jobs))):
-        rep = TL.grade_prefill(res, y_pref[i], fold_h[bh], "bf16")
-        print(f"[config 4] prior-context prefill head {bh}: {rep}", flush=True)
-    # (2) decode: the oracle continues from the GPU's post-prefill state
-    worst, mism = 0.0, 0
+        rep = TL.grade_prefill(res, y_pref[i], fold_h[bh], dtype)
+        print(f"[config 4 {dtype}] prior-context prefill head {bh}: {rep}", flush=True)
+    # (2) decode: the oracle continues from the GPU's post-prefill state, step by step
     for (b, h) in heads:
         so = O.state_from_arrays(snap["t"], wl.eta, wl.lam, snap["H"][b, h].T, snap["s"][b, h],
                                  snap["win_k"][b, h], snap["win_v"][b, h], snap["cache_k"][b, h],
                                  snap["cache_v"][b, h], snap["cache_pos"][b, h])
-        for s in range(wl.decode_steps):
-            y_o, f_o = O.decode_step(so, phi_o, dqh[s, b, h], dkh[s, b, h], dvh[s, b, h])
-            worst = max(worst, TL.row_rel_err(ys[s, b, h][None], y_o[None]))
-            if f_o != folds[s, b, h]:
-                mism += 1
-                break       # a bf16 near-tie: the two states part ways from here
-    print(f"[config 4] decode: max err {worst:.3e}, heads that diverged at a near-tie: {mism}", flush=True)
-    assert worst <= TL.BF16_TOL
+        rep = TL.grade_decode_steps(so, phi_o, dqh[:, b, h], dkh[:, b, h], dvh[:, b, h], ys[:, b, h],
+                                    folds[:, b, h], dtype)
+        print(f"[config 4 {dtype}] decode head {(b, h)}: {rep}", flush=True)
+        assert rep["fold_mismatches"] <= wl.decode_steps // 8
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
