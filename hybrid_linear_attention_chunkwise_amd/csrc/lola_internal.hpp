@@ -193,6 +193,11 @@ hipError_t launch_decode_fast(const DecodeArgs& a, int d, int phi_kind, hipStrea
 
 hipError_t launch_collide(const CollideArgs& a, int dtype, int d, hipStream_t stream);
 
+// Read-out for bf16 storage with C = 64 or 128 (128 queries per workgroup): whether a call takes it,
+// and its launcher over the chunk range [c0, c1) (c0 a multiple of 128 / C).
+bool readout_fast_fits(const PrefillArgs& a, int dtype);
+hipError_t launch_readout_fast(const PrefillArgs& a, int d, int phi_kind, int c0, int c1, hipStream_t stream);
+
 // LDS bytes the chain kernel uses (sized for kMaxLambda / kMaxChunk) at element size esz.
 size_t chain_lds_bytes(int d, int phi_kind, int esz);
 size_t decode_lds_bytes(int d, int phi_kind, int esz, int lam);

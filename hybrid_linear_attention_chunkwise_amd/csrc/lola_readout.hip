@@ -498,6 +498,7 @@ template <typename T, int DK, int PHI>
 static hipError_t launch_readout(PrefillArgs a, int c0, int c1, hipStream_t stream, bool last_range = false) {
     a.c_begin = c0;
     a.c_end = c1;
+    if (std::is_same<T, bf16>::value && readout_fast_fits(a, 1)) return launch_readout_fast(a, DK, PHI, c0, c1, stream);
     const int64_t blocks = (int64_t)a.BH * (c1 - c0) * a.nqt;
     if (last_range)
         hipLaunchKernelGGL((readout_kernel<T, DK, PHI, 2>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
@@ -573,7 +574,13 @@ hipError_t launch_prefill_t(const PrefillArgs& a0, hipStream_t stream, hipEvent_
     // chain.  The second stream forks from and joins back into the call's stream through the caller's
     // events (one per range boundary, one for the join), so the call stays ordered as one unit.
     int bounds[kMaxSegments + 1];
-    const int nseg = split_chunks(a.nchunks, a.BH * a.nqt, device_cus(), bounds, kMaxSegments);
+    // The read-out's unit of work: chunks it takes in one workgroup (the bf16 kernel for C = 64 covers
+    // two chunks per tile, so ranges are cut between tiles) and workgroups per unit.
+    const bool fastro = std::is_same<T, bf16>::value && readout_fast_fits(a, 1);
+    const int cpu = fastro ? (a.C == 64 ? 2 : 1) : 1;
+    const int nunits = (a.nchunks + cpu - 1) / cpu;
+    const int nseg = split_chunks(nunits, fastro ? a.BH : a.BH * a.nqt, device_cus(), bounds, kMaxSegments);
+    for (int i = 0; i <= nseg; ++i) bounds[i] = bounds[i] * cpu < a.nchunks ? bounds[i] * cpu : a.nchunks;
     if ((e = launch_phi_t<T, DK, PHI>(a, stream)) != hipSuccess) return e;
     if (a.score_rule != kScoreSre && (e = launch_qscore_t<T, DK>(a, stream)) != hipSuccess) return e;
     // The last range's read-out follows the chain on the caller's stream, so it starts without a

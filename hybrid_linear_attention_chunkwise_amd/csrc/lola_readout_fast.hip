@@ -1,0 +1,676 @@
+// Prefill read-out for bf16 storage with chunks of 64 or 128 tokens: one workgroup per (sequence/head,
+// 128 consecutive queries); four waves of 32 queries (two 16-query MFMA tiles each).
+//
+// Eq. (14) of the LoLA notes (2.5) with the chunk schedule the chain kernel recorded:
+//   linear part  L(t) = H_c^T phi(q_t) + sum_{i in S_c, tau_i <= t} (phi(q_t).phi(k_i)) v_i   (den: phi(q_t).s_c + ...)
+//   exact part   E(t) = sum_{i in window(t) U cache_c, i not linear} exp(q_t.k_i / sqrt(d_k)) v_i
+//   y_t = (L + E) / (L_den + E_den), one shared denominator.
+// The linear part is formed first and seeds the running softmax state as if it were one more term of
+// weight L_den: max m = log L_den, accumulator L / L_den, sum 1.  The key loop then only rescales and
+// adds, and the output is accumulator / sum; no second accumulator stays live through the loop.
+//
+// Keys.  The 128 queries share one stream of 64-key blocks staged in LDS (keys row-major, values
+// transposed): the window band [q0 - eta + 1, q0 + 127], then the cache list of the first chunk of the
+// tile, then (chunks of 64) the slots whose member changed at the second chunk.  Every key carries, per
+// query group (the chunk of waves 0-1 and of waves 2-3), the range of queries that read it exactly:
+//   band key p: [p, p + eta - 1]; cache member p: [p + eta, inf) (a member still inside a query's window
+//   is read through the window); a slot replaced at the second chunk: nothing for its second group;
+//   the replacement: nothing for the first group.
+// A wave classifies each block against its 32 queries: no key read (skipped), every key read by every
+// query (no mask), or mixed (mask from the ranges: one subtraction and one unsigned comparison).
+//
+// Softmax in base 2 with the scale folded into one FMA; the running max is raised only when a block's
+// max exceeds it by more than 8 (wave-uniform), so most blocks skip the accumulator rescale.  Probabilities
+// are at most 2^8 and the result is the same up to rounding.
+//
+// Workgroups are ordered so that each XCD (workgroup id mod 8) takes a contiguous run of tiles of the
+// same heads: neighbouring chunks share most window and cache keys in that XCD's L2.
+#include "lola_common.hpp"
+#include "lola_internal.hpp"
+
+namespace lola {
+
+namespace {
+
+constexpr int kRfQ = 128;          // queries per workgroup
+constexpr int kRfKB = 64;          // keys per staged block
+constexpr int kRfThreads = 256;
+constexpr unsigned kNoKey = 0x7FFFFFFFu;
+
+// Whole-wave min / max of unsigned values below 2^31 (DPP inside rows of 16, lane swaps across rows).
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+    return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, true);
+}
+__device__ __forceinline__ void wave_minmax_i(int& mn, int& mx) {
+    mn = min(mn, dpp_i<0xB1>(mn)); mx = max(mx, dpp_i<0xB1>(mx));     // quad_perm [1,0,3,2]
+    mn = min(mn, dpp_i<0x4E>(mn)); mx = max(mx, dpp_i<0x4E>(mx));     // quad_perm [2,3,0,1]
+    mn = min(mn, dpp_i<0x124>(mn)); mx = max(mx, dpp_i<0x124>(mx));   // row_ror:4
+    mn = min(mn, dpp_i<0x128>(mn)); mx = max(mx, dpp_i<0x128>(mx));   // row_ror:8
+    {
+        const auto a = __builtin_amdgcn_permlane16_swap((unsigned)mn, (unsigned)mn, false, false);
+        mn = min((int)a[0], (int)a[1]);
+        const auto b = __builtin_amdgcn_permlane16_swap((unsigned)mx, (unsigned)mx, false, false);
+        mx = max((int)b[0], (int)b[1]);
+    }
+    {
+        const auto a = __builtin_amdgcn_permlane32_swap((unsigned)mn, (unsigned)mn, false, false);
+        mn = min((int)a[0], (int)a[1]);
+        const auto b = __builtin_amdgcn_permlane32_swap((unsigned)mx, (unsigned)mx, false, false);
+        mx = max((int)b[0], (int)b[1]);
+    }
+}
+
+// phi of two 16-query tiles (section 2.2), each W^T fragment from LDS serving both: the features as
+// MFMA B operands pf[qq][ss] (reduction order over D) and phi(q).s in lden[qq] (this lane's part).
+template <int DK, int PHI>
+__device__ __forceinline__ void phi_pair(const bf16* wt, int wt_ld, const Frag8<bf16> (&qf)[2][DK / 32],
+                                         const float* s, Frag8<bf16> (&pf)[2][kFeat / 32], float (&lden)[2]) {
+    constexpr int D = kFeat, DW = (PHI == kPhiSoftmaxPM) ? D / 2 : D;
+    const int l = lane_id(), g = l >> 4, c = l & 15;
+    f4 pre[DW / 16][2];
+#pragma unroll
+    for (int ft = 0; ft < DW / 16; ++ft) {
+        pre[ft][0] = zero4();
+        pre[ft][1] = zero4();
+#pragma unroll
+        for (int ss = 0; ss < DK / 32; ++ss) {
+            const Frag8<bf16> a = load_frag(wt + (16 * ft + c) * wt_ld, ss, g);
+            mma32(pre[ft][0], a, qf[0][ss]);
+            mma32(pre[ft][1], a, qf[1][ss]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+        float ph[D / 16][4];
+        if constexpr (PHI == kPhiSoftmaxPM) {
+            float mx = -INFINITY, mn = INFINITY;
+#pragma unroll
+            for (int ft = 0; ft < DW / 16; ++ft)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) { mx = fmaxf(mx, pre[ft][qq][r]); mn = fminf(mn, pre[ft][qq][r]); }
+            mx = max_groups(mx);
+            mn = min_groups(mn);
+            float sp = 0.f, sm = 0.f;
+#pragma unroll
+            for (int ft = 0; ft < DW / 16; ++ft)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float ep = fast_exp(pre[ft][qq][r] - mx);
+                    const float em = fast_exp(mn - pre[ft][qq][r]);
+                    ph[ft][r] = ep;
+                    ph[ft + DW / 16][r] = em;
+                    sp += ep;
+                    sm += em;
+                }
+            const float ip = fast_rcp(sum_groups(sp)), im = fast_rcp(sum_groups(sm));
+#pragma unroll
+            for (int ft = 0; ft < DW / 16; ++ft)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) { ph[ft][r] *= ip; ph[ft + DW / 16][r] *= im; }
+        } else {
+#pragma unroll
+            for (int ft = 0; ft < DW / 16; ++ft)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float z = pre[ft][qq][r];
+                    ph[ft][r] = z > 0.f ? z + 1.f : fast_exp(z);
+                }
+        }
+        float ld = 0.f;
+#pragma unroll
+        for (int ft = 0; ft < D / 16; ++ft) {
+            const f4 sv = *reinterpret_cast<const f4*>(s + 16 * ft + 4 * g);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ld += ph[ft][r] * sv[r];
+        }
+        asm volatile("" : "+v"(ld));      // formed here: the features are not kept live until it is used
+        lden[qq] = ld;
+#pragma unroll
+        for (int ss = 0; ss < D / 32; ++ss)
+            pf[qq][ss] = frag_from_acc<bf16>(f4{ph[2 * ss][0], ph[2 * ss][1], ph[2 * ss][2], ph[2 * ss][3]},
+                                             f4{ph[2 * ss + 1][0], ph[2 * ss + 1][1], ph[2 * ss + 1][2], ph[2 * ss + 1][3]});
+    }
+}
+
+template <int DK, int PHI>
+struct RfCfg {
+    static constexpr int D = kFeat, DV = DK, JT = DV / 16;
+    static constexpr int DW = (PHI == kPhiSoftmaxPM) ? D / 2 : D;
+    static constexpr int WT_LD = DK + 4;
+    static constexpr int CPK = DK / 8;             // 16-byte chunks per key (and value) row
+    static constexpr int RPB = 256 / (2 * DK);     // rows per 256 bytes (the 64 LDS banks): 1 or 2
+    static constexpr int SEG = DV / 16;            // 32-byte segments per value row
+    static constexpr int PPT = kRfKB * CPK / kRfThreads;   // chunks per thread and block (one row)
+};
+
+// Staged rows are unpadded and swizzled so that fragment reads hit 64 distinct banks:
+//   key row r, 16-byte chunk q  -> chunk q ^ ((r / RPB) mod CPK)
+//     (a fragment read takes one chunk of 16 consecutive rows, or two halves of it);
+//   value row r, 32-byte segment s -> segment s ^ ((r / RPB) mod SEG), chunk halves kept
+//     (a transposed read takes one segment of 8 consecutive rows per half-wave).
+template <int DK>
+__device__ __forceinline__ int kswz(int row, int q) {
+    constexpr int RPB = 256 / (2 * DK), CPK = DK / 8;
+    return q ^ ((row / RPB) % CPK);
+}
+template <int DK>
+__device__ __forceinline__ int vswz(int row, int q) {
+    constexpr int RPB = 256 / (2 * DK), SEG = DK / 16;
+    return (((q >> 1) ^ ((row / RPB) % SEG)) << 1) | (q & 1);
+}
+
+// Four bf16 of a transposed LDS read (gfx950): in each group of 16 lanes, lanes 4r .. 4r + 3 give
+// the addresses of row r (four elements each, sixteen in all) and lane i receives element i of rows
+// 0 .. 3.
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (v4s __attribute__((address_space(3)))*)((__attribute__((address_space(3))) char*)p));
+    bf16x4 out;
+    __builtin_memcpy(&out, &r, sizeof(out));
+    return out;
+}
+
+struct RfLds {
+    size_t k, vt, wt, tlo, span, cpos, csrc, g1ok, dpos, dsrc, fpos, fsrc, misc, total;
+};
+__host__ __device__ constexpr size_t rf_al(size_t x) { return (x + 15) & ~size_t(15); }
+
+template <int DK, int PHI>
+__host__ __device__ constexpr RfLds rf_lds() {
+    using Cfg = RfCfg<DK, PHI>;
+    RfLds o{};
+    size_t p = 0;
+    o.k = p;     p = rf_al(p + 2 * kRfKB * DK);
+    o.vt = p;    p = rf_al(p + 2 * kRfKB * Cfg::DV);
+    o.wt = p;    p = rf_al(p + 2 * Cfg::DW * Cfg::WT_LD);
+    o.tlo = p;   p = rf_al(p + 4 * 2 * kRfKB);
+    o.span = p;  p = rf_al(p + 4 * 2 * kRfKB);
+    o.cpos = p;  p = rf_al(p + 4 * kMaxLambda);
+    o.csrc = p;  p = rf_al(p + 4 * kMaxLambda);
+    o.g1ok = p;  p = rf_al(p + 4 * kMaxLambda);
+    o.dpos = p;  p = rf_al(p + 4 * kRfKB);
+    o.dsrc = p;  p = rf_al(p + 4 * kRfKB);
+    o.fpos = p;  p = rf_al(p + 4 * 2 * kMaxChunk);
+    o.fsrc = p;  p = rf_al(p + 4 * 2 * kMaxChunk);
+    o.misc = p;  p = rf_al(p + 4 * 16);
+    o.total = p;
+    return o;
+}
+
+template <int DK, int PHI>
+__global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs A, int tiles_per_bh, int u_begin,
+                                                                    int ntiles) {
+    using T = bf16;
+    using Cfg = RfCfg<DK, PHI>;
+    constexpr int D = Cfg::D, DV = Cfg::DV, JT = Cfg::JT, DW = Cfg::DW, WT_LD = Cfg::WT_LD, PPT = Cfg::PPT,
+                  KB = kRfKB;
+    extern __shared__ __align__(16) char smem[];
+    constexpr RfLds lo = rf_lds<DK, PHI>();
+    T* sK = reinterpret_cast<T*>(smem + lo.k);
+    T* sV = reinterpret_cast<T*>(smem + lo.vt);             // [KB][DV], swizzled
+    T* wt = reinterpret_cast<T*>(smem + lo.wt);
+    int* sTlo = reinterpret_cast<int*>(smem + lo.tlo);      // [2][KB]
+    int* sSpan = reinterpret_cast<int*>(smem + lo.span);    // [2][KB]
+    int* cPos = reinterpret_cast<int*>(smem + lo.cpos);     // cache list of the tile's first chunk
+    int* cSrc = reinterpret_cast<int*>(smem + lo.csrc);
+    int* g1ok = reinterpret_cast<int*>(smem + lo.g1ok);     // slot unchanged at the second chunk
+    int* dPos = reinterpret_cast<int*>(smem + lo.dpos);     // slots replaced at the second chunk
+    int* dSrc = reinterpret_cast<int*>(smem + lo.dsrc);
+    int* fPos = reinterpret_cast<int*>(smem + lo.fpos);     // [2][kMaxChunk] fold lists per group
+    int* fSrc = reinterpret_cast<int*>(smem + lo.fsrc);
+    int* misc = reinterpret_cast<int*>(smem + lo.misc);
+
+    // XCD-aware order: workgroup id mod 8 picks a contiguous eighth of the tiles.
+    const int G = gridDim.x;
+    const int per = G / 8;                          // G is a multiple of 8 (host pads)
+    const int tile = (blockIdx.x % 8) * per + blockIdx.x / 8;
+    if (tile >= ntiles) return;
+    const int bh = tile / tiles_per_bh;
+    const int u = u_begin + tile % tiles_per_bh;
+    const int n = A.n, C = A.C, eta = A.eta, lam = A.lam;
+    const int64_t t0 = A.t0;
+    const int64_t q0 = t0 + (int64_t)kRfQ * u;
+    const int64_t tend = t0 + n;                    // first position past the call
+    const int cpt = kRfQ / C;                       // chunks per tile: 2 (C = 64) or 1 (C = 128)
+    const int ch0 = u * cpt;                        // first chunk of the tile
+    const bool two = cpt == 2 && ch0 + 1 < A.nchunks && q0 + 64 < tend;   // a second chunk with queries
+    const bool sparse = (A.read_mask & kReadSparse) && lam > 0;
+
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c = l & 15;
+    const int grp = cpt == 2 ? (w >> 1) : 0;        // query group (chunk) of this wave
+    const int chw = ch0 + grp;
+    const int64_t tw0 = q0 + 32 * w;                // first query of this wave
+    const bool wave_active = tw0 < tend;
+
+    const char* wsb = A.ws + (int64_t)bh * A.L.per_bh;
+    const char* rec0 = wsb + A.L.chunk0 + (int64_t)ch0 * A.L.per_chunk;
+    const char* rec1 = two ? rec0 + A.L.per_chunk : rec0;
+    const T* phiStore = reinterpret_cast<const T*>(wsb + A.L.phi_store);
+    const T* qin = reinterpret_cast<const T*>(A.q) + (int64_t)bh * n * DK;
+    const T* kin = reinterpret_cast<const T*>(A.k) + (int64_t)bh * n * DK;
+    const T* vin = reinterpret_cast<const T*>(A.v) + (int64_t)bh * n * DV;
+    const T* ringK = eta > 0 ? reinterpret_cast<const T*>(A.win_k) + (int64_t)bh * eta * DK : nullptr;
+    const T* ringV = eta > 0 ? reinterpret_cast<const T*>(A.win_v) + (int64_t)bh * eta * DV : nullptr;
+    const T* cK = lam > 0 ? reinterpret_cast<const T*>(A.cache_k) + (int64_t)bh * lam * DK : nullptr;
+    const T* cV = lam > 0 ? reinterpret_cast<const T*>(A.cache_v) + (int64_t)bh * lam * DV : nullptr;
+    T* yout = reinterpret_cast<T*>(A.y) + (int64_t)bh * n * DV;
+
+    // ---- key stream of the tile ----
+    const int64_t blo = q0 - eta + 1 > 0 ? q0 - eta + 1 : 0;
+    const int64_t bhi = (q0 + kRfQ - 1 < tend - 1) ? q0 + kRfQ - 1 : tend - 1;
+    const int nb = (eta > 0 && bhi >= blo) ? (int)(bhi - blo + 1) : 0;
+    const int ring0 = eta > 0 ? (int)(blo % eta) : 0;       // ring slot of the first band key
+    const int nbb = (nb + KB - 1) / KB;
+    const int ncb = sparse ? (lam + KB - 1) / KB : 0;
+
+    // cache list of the first chunk, the second chunk's changes, and both chunks' fold lists
+    if (sparse) {
+        const int* p0 = reinterpret_cast<const int*>(rec0 + A.L.c_cache_pos);
+        const int* s0 = reinterpret_cast<const int*>(rec0 + A.L.c_cache_src);
+        const int* p1 = reinterpret_cast<const int*>(rec1 + A.L.c_cache_pos);
+        const int* s1 = reinterpret_cast<const int*>(rec1 + A.L.c_cache_src);
+        for (int j = tid; j < lam; j += kRfThreads) {
+            const int a0 = p0[j], a1 = p1[j];
+            cPos[j] = a0;
+            cSrc[j] = s0[j];
+            g1ok[j] = a0 == a1;
+        }
+        // replaced slots: ballot over 64-slot groups, one wave
+        if (w == 0) {
+            int base = 0;
+            const unsigned long long lt = l ? (~0ull >> (64 - l)) : 0ull;
+            for (int j0 = 0; j0 < lam; j0 += 64) {
+                const int j = j0 + l;
+                int a0 = -1, a1 = -1, sr = -1;
+                if (j < lam) { a0 = p0[j]; a1 = p1[j]; sr = s1[j]; }
+                const bool rep = j < lam && a1 >= 0 && a1 != a0;
+                const unsigned long long m = __ballot(rep);
+                const int k = base + __popcll(m & lt);
+                if (rep && k < KB) { dPos[k] = a1; dSrc[k] = sr; }
+                base += __popcll(m);
+            }
+            if (l == 0) misc[0] = base < KB ? base : KB;
+        }
+    } else if (tid == 0) {
+        misc[0] = 0;
+    }
+    {
+        const int nf0 = *reinterpret_cast<const int*>(rec0 + A.L.c_fold_n);
+        const int nf1 = two ? *reinterpret_cast<const int*>(rec1 + A.L.c_fold_n) : 0;
+        const int* fp0 = reinterpret_cast<const int*>(rec0 + A.L.c_fold_pos);
+        const int* fs0 = reinterpret_cast<const int*>(rec0 + A.L.c_fold_src);
+        const int* fp1 = reinterpret_cast<const int*>(rec1 + A.L.c_fold_pos);
+        const int* fs1 = reinterpret_cast<const int*>(rec1 + A.L.c_fold_src);
+        for (int i = tid; i < nf0; i += kRfThreads) { fPos[i] = fp0[i]; fSrc[i] = fs0[i]; }
+        for (int i = tid; i < nf1; i += kRfThreads) { fPos[kMaxChunk + i] = fp1[i]; fSrc[kMaxChunk + i] = fs1[i]; }
+        if (tid == 0) { misc[1] = nf0; misc[2] = nf1; }
+    }
+    // W^T in LDS for the query features
+    if (A.read_mask & kReadState) stage_wt<T, DK, DW, kRfThreads>(wt, WT_LD, A.W);
+    __syncthreads();
+    const int nd = misc[0];
+    const int ndb = (sparse && two && nd > 0) ? 1 : 0;
+    const int nblk = nbb + ncb + ndb;
+
+    // key kk of block kb -> position, rows, and the query ranges of both groups
+    auto key_of = [&](int kb, int j, int& pos, const T*& rk, const T*& rv, unsigned& tl0, unsigned& sp0,
+                      unsigned& tl1, unsigned& sp1) {
+        pos = -1; rk = kin; rv = vin;
+        tl0 = tl1 = kNoKey; sp0 = sp1 = 0u;
+        if (kb < nbb) {
+            const int kk = kb * KB + j;
+            if (kk < nb) {
+                const int64_t p = blo + kk;
+                pos = (int)p;
+                if (p >= t0) { rk = kin + (p - t0) * DK; rv = vin + (p - t0) * DV; }
+                else {
+                    int sl = ring0 + kk;
+                    sl = sl >= eta ? sl - eta : sl;      // kk < eta here (p < t0 <= q0)
+                    rk = ringK + (int64_t)sl * DK;
+                    rv = ringV + (int64_t)sl * DV;
+                }
+                tl0 = tl1 = (unsigned)p;
+                sp0 = sp1 = (unsigned)(eta - 1);
+            }
+            return;
+        }
+        int p = -1, src = -1, ok0 = 0, ok1 = 0;
+        if (kb < nbb + ncb) {
+            const int jj = (kb - nbb) * KB + j;
+            if (jj < lam) { p = cPos[jj]; src = cSrc[jj]; ok0 = 1; ok1 = g1ok[jj]; }
+        } else if (j < nd) {
+            p = dPos[j]; src = dSrc[j]; ok0 = 0; ok1 = 1;
+        }
+        if (p < 0) return;
+        pos = p;
+        if (src < n) { rk = kin + (int64_t)src * DK; rv = vin + (int64_t)src * DV; }
+        else if (src < n + lam) { rk = cK + (int64_t)(src - n) * DK; rv = cV + (int64_t)(src - n) * DV; }
+        else { rk = ringK + (int64_t)(src - n - lam) * DK; rv = ringV + (int64_t)(src - n - lam) * DV; }
+        const unsigned lo_ = (unsigned)(p + eta);
+        if (ok0) { tl0 = lo_; sp0 = kNoKey - lo_; }
+        if (ok1) { tl1 = lo_; sp1 = kNoKey - lo_; }
+    };
+
+    // A block in flight: thread t stages key t / 4 of the block, chunks (t mod 4) * PPT .. + PPT - 1 of
+    // its key row and of its value row, and (t mod 4 == 0) the key's query ranges.
+    struct Buf {
+        uint4 k[PPT];
+        uint4 v[PPT];
+        unsigned tl0, sp0, tl1, sp1;
+    };
+    Buf buf;
+    const int sj = tid >> 2, sq0 = (tid & 3) * PPT;
+    auto prefetch = [&](int kb) {
+        int pos;
+        const T* rk;
+        const T* rv;
+        key_of(kb, sj, pos, rk, rv, buf.tl0, buf.sp0, buf.tl1, buf.sp1);
+#pragma unroll
+        for (int x = 0; x < PPT; ++x) {
+            buf.k[x] = pos >= 0 ? *reinterpret_cast<const uint4*>(rk + (sq0 + x) * 8) : make_uint4(0, 0, 0, 0);
+            buf.v[x] = pos >= 0 ? *reinterpret_cast<const uint4*>(rv + (sq0 + x) * 8) : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto stage = [&]() {
+#pragma unroll
+        for (int x = 0; x < PPT; ++x) {
+            *reinterpret_cast<uint4*>(sK + sj * DK + kswz<DK>(sj, sq0 + x) * 8) = buf.k[x];
+            *reinterpret_cast<uint4*>(sV + sj * DV + vswz<DK>(sj, sq0 + x) * 8) = buf.v[x];
+        }
+        if ((tid & 3) == 0) {
+            sTlo[sj] = (int)buf.tl0;
+            sSpan[sj] = (int)buf.sp0;
+            sTlo[KB + sj] = (int)buf.tl1;
+            sSpan[KB + sj] = (int)buf.sp1;
+        }
+    };
+    // this wave's view of the staged block, from the keys' query ranges (lane l reads key l): none of
+    // its queries reads a key, or every query reads every key, or a mask is needed
+    const unsigned ta = (unsigned)tw0;
+    const unsigned tb = (unsigned)(tw0 + 31 < tend - 1 ? tw0 + 31 : tend - 1);
+    auto classify = [&](bool& none, bool& full) {
+        const unsigned tl = (unsigned)sTlo[grp * KB + l], sp = (unsigned)sSpan[grp * KB + l];
+        const unsigned hi = tl == kNoKey ? 0u : tl + sp;
+        int lo_mn = (int)tl, lo_mx = (int)tl, hi_mn = (int)hi, hi_mx = (int)hi;
+        wave_minmax_i(lo_mn, lo_mx);
+        wave_minmax_i(hi_mn, hi_mx);
+        none = (unsigned)lo_mn > tb || (unsigned)hi_mx < ta;
+        full = !none && (unsigned)lo_mx <= ta && (unsigned)hi_mn >= tb;
+    };
+    if (nblk > 0) {
+        prefetch(0);
+        stage();
+    }
+
+    // ---- queries, and the linear part seeding the softmax state ----
+    // The query fragments are loaded for the features, dropped through the linear part (which needs
+    // every register it can get) and loaded again from L2 for the key loop.
+    Frag8<T> qf[2][DK / 32];
+    auto load_q = [&]() {
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+            const int64_t tq = tw0 + 16 * qq + c;
+#pragma unroll
+            for (int ss = 0; ss < DK / 32; ++ss)
+                qf[qq][ss] = tq < tend ? load_frag(qin + (tq - t0) * DK, ss, g) : frag_zero<T>();
+        }
+    };
+    constexpr float kLog2e = 1.4426950408889634f;
+    const float sl2 = kLog2e / sqrtf((float)DK);       // score -> base-2 logit
+    f4 O[JT][2];
+    float m_run[2], l_run[2];
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+        m_run[qq] = -INFINITY;
+        l_run[qq] = 0.f;
+#pragma unroll
+        for (int J = 0; J < JT; ++J) O[J][qq] = zero4();
+    }
+    if ((A.read_mask & kReadState) && wave_active) {
+        const char* recw = grp ? rec1 : rec0;
+        const T* snapH = reinterpret_cast<const T*>(recw + A.L.c_snap_h);
+        const float* snapS = reinterpret_cast<const float*>(recw + A.L.c_snap_s);
+        const T* foldVT = reinterpret_cast<const T*>(recw + A.L.c_fold_vt);
+        const int cpv = A.L.c_pad64;
+        const int nf = misc[1 + grp];
+        const int* fp = fPos + grp * kMaxChunk;
+        const int* fs = fSrc + grp * kMaxChunk;
+        const int64_t a = t0 + (int64_t)chw * C;       // the wave's chunk start
+        Frag8<T> pf[2][D / 32];
+        float lden[2];
+        load_q();
+        phi_pair<DK, PHI>(wt, WT_LD, qf, snapS, pf, lden);
+        // H_c^T phi(Q)^T from the fragment-order snapshot (each fragment serves both query tiles)
+#pragma unroll
+        for (int ss = 0; ss < D / 32; ++ss)
+#pragma unroll
+            for (int J = 0; J < JT; ++J) {
+                const Frag8<T> hf = *reinterpret_cast<const Frag8<T>*>(snapH + ((int64_t)(J * (D / 32) + ss) * 64 + l) * 8);
+                mma32(O[J][0], hf, pf[0][ss]);
+                mma32(O[J][1], hf, pf[1][ss]);
+                if (J % 4 == 3) __builtin_amdgcn_sched_barrier(0);   // bound the snapshot fragments in flight
+            }
+        // tokens folded by this chunk become linear at tau = max(exit time, chunk start)
+        float lf[2] = {0.f, 0.f};
+        for (int fb = 0; fb * 32 < nf; ++fb) {
+            // the kernel values phi(q_t).phi(k_i) of 32 folded tokens (two halves of 16) and both query
+            // tiles, masked by tau_i <= t, then their values
+            f4 sp[2][2];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int i = 32 * fb + 16 * h2 + c;
+                const T* prow = phiStore + (int64_t)(i < nf ? fs[i] : 0) * D;
+                Frag8<T> af[D / 32];
+#pragma unroll
+                for (int ss = 0; ss < D / 32; ++ss) af[ss] = i < nf ? load_frag(prow, ss, g) : frag_zero<T>();
+#pragma unroll
+                for (int qq = 0; qq < 2; ++qq) {
+                    sp[h2][qq] = zero4();
+#pragma unroll
+                    for (int ss = 0; ss < D / 32; ++ss) mma32(sp[h2][qq], af[ss], pf[qq][ss]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            Frag8<T> bw[2];
+#pragma unroll
+            for (int qq = 0; qq < 2; ++qq) {
+                const int64_t tq = tw0 + 16 * qq + c;
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int ii = 32 * fb + 16 * h2 + 4 * g + r;
+                        bool ok = false;
+                        if (ii < nf) {
+                            const int64_t tau = max((int64_t)fp[ii] + eta, a);
+                            ok = tau <= tq;
+                        }
+                        sp[h2][qq][r] = ok ? sp[h2][qq][r] : 0.f;
+                        lf[qq] += sp[h2][qq][r];
+                    }
+                bw[qq] = frag_from_acc<T>(sp[0][qq], sp[1][qq]);
+            }
+#pragma unroll
+            for (int J = 0; J < JT; ++J) {
+                const Frag8<T> vf = load_frag(foldVT + (int64_t)(16 * J + c) * cpv, fb, g);
+                mma32(O[J][0], vf, bw[0]);
+                mma32(O[J][1], vf, bw[1]);
+                if (J % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+            const float den = sum_groups(lden[qq]) + sum_groups(lf[qq]);
+            if (den > 0.f) {
+                const float inv = 1.f / den;
+                m_run[qq] = __builtin_amdgcn_logf(den);            // log2 of the linear weight
+                l_run[qq] = g == 0 ? 1.f : 0.f;                   // counted once in the group sum
+#pragma unroll
+                for (int J = 0; J < JT; ++J)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) O[J][qq][r] *= inv;
+            } else {
+#pragma unroll
+                for (int J = 0; J < JT; ++J) O[J][qq] = zero4();
+            }
+        }
+    }
+
+    // ---- exact part: the key blocks ----
+    asm volatile("" ::: "memory");                  // a second load, not the first one kept live
+    load_q();
+    const int* tloG = sTlo + grp * KB;
+    const int* spanG = sSpan + grp * KB;
+    __syncthreads();                                // block 0 staged
+    for (int kb = 0; kb < nblk; ++kb) {
+        bool none, full;
+        classify(none, full);
+        if (kb + 1 < nblk) prefetch(kb + 1);
+        if (wave_active && !none) {
+            f4 S[KB / 16][2];
+#pragma unroll
+            for (int kt = 0; kt < KB / 16; ++kt) {
+                S[kt][0] = zero4();
+                S[kt][1] = zero4();
+#pragma unroll
+                for (int ss = 0; ss < DK / 32; ++ss) {
+                    const int row = 16 * kt + c;
+                    const T* kr = sK + row * DK + 4 * (g & 1);
+                    Frag8<T> kf;
+                    kf.v = __builtin_shufflevector(*reinterpret_cast<const bf16x4*>(kr + kswz<DK>(row, 4 * ss + (g >> 1)) * 8),
+                                                   *reinterpret_cast<const bf16x4*>(kr + kswz<DK>(row, 4 * ss + 2 + (g >> 1)) * 8),
+                                                   0, 1, 2, 3, 4, 5, 6, 7);
+                    mma32(S[kt][0], kf, qf[0][ss]);
+                    mma32(S[kt][1], kf, qf[1][ss]);
+                }
+                __builtin_amdgcn_sched_barrier(0);            // bound the key fragments in flight
+            }
+            if (!full) {
+#pragma unroll
+                for (int kt = 0; kt < KB / 16; ++kt) {
+                    const int4 tv = *reinterpret_cast<const int4*>(tloG + 16 * kt + 4 * g);
+                    const int4 sv = *reinterpret_cast<const int4*>(spanG + 16 * kt + 4 * g);
+                    const unsigned tlr[4] = {(unsigned)tv.x, (unsigned)tv.y, (unsigned)tv.z, (unsigned)tv.w};
+                    const unsigned spr[4] = {(unsigned)sv.x, (unsigned)sv.y, (unsigned)sv.z, (unsigned)sv.w};
+#pragma unroll
+                    for (int qq = 0; qq < 2; ++qq) {
+                        const unsigned tq = (unsigned)(tw0 + 16 * qq + c);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            S[kt][qq][r] = (tq - tlr[r]) <= spr[r] ? S[kt][qq][r] : -INFINITY;
+                    }
+                }
+            }
+#pragma unroll
+            for (int qq = 0; qq < 2; ++qq) {
+                float bm = -INFINITY;
+#pragma unroll
+                for (int kt = 0; kt < KB / 16; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) bm = fmaxf(bm, S[kt][qq][r]);
+                bm = max_groups(bm) * sl2;
+                // raise the running max only when the block's exceeds it by more than 8 (base 2)
+                if (__ballot(bm > m_run[qq] + 8.f)) {
+                    const float mn_ = fmaxf(m_run[qq], bm);
+                    const float alpha = m_run[qq] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[qq] - mn_);
+                    l_run[qq] *= alpha;
+#pragma unroll
+                    for (int J = 0; J < JT; ++J)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) O[J][qq][r] *= alpha;
+                    m_run[qq] = mn_;
+                }
+                const float mref = m_run[qq] == -INFINITY ? 0.f : m_run[qq];
+                float ls = 0.f;
+#pragma unroll
+                for (int kt = 0; kt < KB / 16; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kt][qq][r], sl2, -mref));
+                        S[kt][qq][r] = p;
+                        ls += p;
+                    }
+                l_run[qq] += ls;
+            }
+#pragma unroll
+            for (int k2 = 0; k2 < KB / 32; ++k2) {
+                const Frag8<T> p0 = frag_from_acc<T>(S[2 * k2][0], S[2 * k2 + 1][0]);
+                const Frag8<T> p1 = frag_from_acc<T>(S[2 * k2][1], S[2 * k2 + 1][1]);
+#pragma unroll
+                for (int J = 0; J < JT; ++J) {
+                    // value rows 16J + c, keys 32k2 + 4g .. + 3 and 32k2 + 16 + 4g .. + 3, by transposed reads of
+                    // the row-major block: lane (g, c) names key 4g + c / 4, values 16J + 4(c mod 4) .. + 3
+                    const int ka = 32 * k2 + 4 * g + (c >> 2), kb2 = ka + 16;
+                    const int q = 2 * J + ((c >> 1) & 1), off = 4 * (c & 1);
+                    Frag8<T> vf;
+                    vf.v = __builtin_shufflevector(lds_read_tr(sV + ka * DV + vswz<DK>(ka, q) * 8 + off),
+                                                   lds_read_tr(sV + kb2 * DV + vswz<DK>(kb2, q) * 8 + off),
+                                                   0, 1, 2, 3, 4, 5, 6, 7);
+                    mma32(O[J][0], vf, p0);
+                    mma32(O[J][1], vf, p1);
+                    if (J % 4 == 3) __builtin_amdgcn_sched_barrier(0);   // bound the value fragments in flight
+                }
+            }
+        }
+        __syncthreads();
+        if (kb + 1 < nblk) {
+            stage();
+            __syncthreads();
+        }
+    }
+
+    // ---- output: accumulator / sum ----
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+        const int64_t tq = tw0 + 16 * qq + c;
+        // l_run holds each lane's partial sum over its key rows (and the linear seed on lane group 0)
+        const float tot = sum_groups(l_run[qq]);
+        if (wave_active && tq < tend) {
+            const float inv = 1.f / tot;
+            T* yrow = yout + (tq - t0) * DV;
+#pragma unroll
+            for (int J = 0; J < JT; ++J) {
+                bf16x4 v4;
+                v4[0] = (bf16)(O[J][qq][0] * inv);
+                v4[1] = (bf16)(O[J][qq][1] * inv);
+                v4[2] = (bf16)(O[J][qq][2] * inv);
+                v4[3] = (bf16)(O[J][qq][3] * inv);
+                *reinterpret_cast<bf16x4*>(yrow + 16 * J + 4 * g) = v4;
+            }
+        }
+    }
+}
+
+}  // namespace
+
+bool readout_fast_fits(const PrefillArgs& a, int dtype) {
+    return dtype == 1 && (a.C == 64 || a.C == 128);
+}
+
+template <int DK, int PHI>
+hipError_t launch_readout_fast_t(const PrefillArgs& a, int c0, int c1, hipStream_t stream) {
+    constexpr size_t lds = rf_lds<DK, PHI>().total;
+    const int cpt = kRfQ / a.C;
+    const int u0 = c0 / cpt;
+    const int u1 = (c1 + cpt - 1) / cpt;
+    if (u1 <= u0) return hipSuccess;
+    const int tiles_per_bh = u1 - u0;
+    const int64_t ntiles = (int64_t)a.BH * tiles_per_bh;
+    const int64_t grid = (ntiles + 7) / 8 * 8;
+    auto kern = readout_fast_kernel<DK, PHI>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kRfThreads), lds, stream, a, tiles_per_bh, u0, (int)ntiles);
+    return hipGetLastError();
+}
+
+hipError_t launch_readout_fast(const PrefillArgs& a, int d, int phi_kind, int c0, int c1, hipStream_t stream) {
+    if (d == 64) return phi_kind ? launch_readout_fast_t<64, 1>(a, c0, c1, stream) : launch_readout_fast_t<64, 0>(a, c0, c1, stream);
+    return phi_kind ? launch_readout_fast_t<128, 1>(a, c0, c1, stream) : launch_readout_fast_t<128, 0>(a, c0, c1, stream);
+}
+
+}  // namespace lola
