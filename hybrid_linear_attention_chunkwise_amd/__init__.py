@@ -19,7 +19,8 @@ from ._binding import (LOLA_BF16, LOLA_EDEVICE, LOLA_EINVAL, LOLA_EUNSUPPORTED, 
 __all__ = ["LolaState", "LolaPhi", "LolaOverlap", "lola_state_init", "lola_workspace_bytes", "lola_prefill",
            "lola_decode_step", "lola_sre_collisions", "LolaError", "LOLA_OK", "LOLA_EINVAL", "LOLA_EUNSUPPORTED",
            "LOLA_EDEVICE", "library_path", "PHI_KINDS", "LOLA_READ_STATE", "LOLA_READ_SPARSE",
-           "LOLA_READ_WINDOW", "LOLA_READ_ALL", "SCORE_RULES", "hola_workspace_bytes", "hola_prefill"]
+           "LOLA_READ_WINDOW", "LOLA_READ_ALL", "SCORE_RULES", "hola_workspace_bytes", "hola_prefill",
+           "lola_prefill_noalloc"]
 
 PHI_KINDS = {"elu1": LOLA_PHI_ELU1, "softmax_pm": LOLA_PHI_SOFTMAX_PM}
 _DTYPES = {torch.float32: LOLA_F32, torch.bfloat16: LOLA_BF16}
@@ -155,6 +156,20 @@ def lola_prefill(state: LolaState, phi: LolaPhi, q: torch.Tensor, k: torch.Tenso
         handles = (ctypes.c_void_p * 5)(*[None if e is None else e.cuda_event for e in events])
         code = lib.lola_prefill_profiled(*args, handles)
     _b.check("lola_prefill", code)
+    return y, fold_at
+
+
+def lola_prefill_noalloc(state: LolaState, phi: LolaPhi, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                         C: int, y: torch.Tensor, fold_at: Optional[torch.Tensor] = None, stream=None,
+                         read_mask: int = LOLA_READ_ALL, score_rule: str = "sre",
+                         overlap: Optional[LolaOverlap] = None):
+    """lola_prefill with the library's own per-device scratch (no workspace; nothing is allocated here
+    either: y is the caller's).  Asynchronous on `stream`; returns (y, fold_at)."""
+    opts = _options(read_mask, score_rule, overlap)
+    code = _b.load().lola_prefill_noalloc(ctypes.byref(state.c), ctypes.byref(phi.c), _ptr(q), _ptr(k), _ptr(v),
+                                          q.shape[2], C, None if opts is None else ctypes.byref(opts), _ptr(y),
+                                          _ptr(fold_at), _stream(stream))
+    _b.check("lola_prefill_noalloc", code)
     return y, fold_at
 
 

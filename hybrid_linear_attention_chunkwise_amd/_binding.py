@@ -24,7 +24,8 @@ LOLA_PHI_SOFTMAX_PM = 1
 EXPORTED = ("lola_workspace_bytes", "lola_state_init", "lola_prefill", "lola_prefill_ex",
             "lola_prefill_profiled", "lola_decode_step", "lola_decode_step_ex", "lola_sre_collisions",
             "lola_status_string", "hola_workspace_bytes", "hola_prefill", "lola_peak_mfma_bf16",
-            "lola_peak_copy")
+            "lola_peak_copy", "lola_prefill_noalloc")
+LOLA_NOALLOC_SCRATCH_BYTES = 64 << 20
 LOLA_READ_STATE = 1
 LOLA_READ_SPARSE = 2
 LOLA_READ_WINDOW = 4
@@ -93,6 +94,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     op = ctypes.POINTER(LolaOptions)
     lib.lola_prefill_ex.argtypes = [sp, pp, vp, vp, vp, i64, i32, op, vp, vp, vp, sz, vp]
     lib.lola_prefill_ex.restype = i32
+    lib.lola_prefill_noalloc.argtypes = [sp, pp, vp, vp, vp, i64, i32, op, vp, vp, vp]
+    lib.lola_prefill_noalloc.restype = i32
     lib.lola_decode_step_ex.argtypes = [sp, pp, vp, vp, vp, op, vp, vp, vp]
     lib.lola_decode_step_ex.restype = i32
     lib.lola_sre_collisions.argtypes = [sp, vp, vp, i64, i32, vp, sz, i32, vp, vp]

@@ -139,6 +139,29 @@ static lola_status hola_check(int32_t B, int32_t n_heads, int32_t d, int32_t dty
     return LOLA_OK;
 }
 
+namespace lola {
+// Every check of a prefill call but the workspace's (shared with the allocation-free entry point).
+lola_status prefill_checks(const lola_state* st, const lola_phi* phi, const void* q, const void* k, const void* v,
+                           int64_t n, int32_t C, const lola_options* opt, const void* y, const int32_t* fold_at,
+                           void* stream) {
+    lola_status rc = check_shape(st);
+    if (rc != LOLA_OK) return rc;
+    rc = check_state_ptrs(st);
+    if (rc != LOLA_OK) return rc;
+    rc = check_phi(st, phi);
+    if (rc != LOLA_OK) return rc;
+    rc = check_options(st, opt);
+    if (rc != LOLA_OK) return rc;
+    rc = check_prefill_config(st, n, C);
+    if (rc != LOLA_OK) return rc;
+    if (opt && opt->overlap && opt->overlap->stream == stream) return LOLA_EINVAL;
+    if (n == 0) return LOLA_OK;
+    if (!q || !k || !v || !y || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y)) return LOLA_EINVAL;
+    if (fold_at && !aligned16(fold_at)) return LOLA_EINVAL;
+    return LOLA_OK;
+}
+}  // namespace lola
+
 extern "C" {
 
 const char* lola_status_string(lola_status status) {
@@ -179,24 +202,13 @@ lola_status lola_state_init(lola_state* st, void* stream) {
     return LOLA_OK;
 }
 
+
 static lola_status prefill_impl(lola_state* st, const lola_phi* phi, const void* q, const void* k,
                                 const void* v, int64_t n, int32_t C, const lola_options* opt, void* y,
                                 int32_t* fold_at, void* workspace, size_t workspace_bytes, void* stream,
                                 void* const* events) {
-    lola_status rc = check_shape(st);
-    if (rc != LOLA_OK) return rc;
-    rc = check_state_ptrs(st);
-    if (rc != LOLA_OK) return rc;
-    rc = check_phi(st, phi);
-    if (rc != LOLA_OK) return rc;
-    rc = check_options(st, opt);
-    if (rc != LOLA_OK) return rc;
-    rc = check_prefill_config(st, n, C);
-    if (rc != LOLA_OK) return rc;
-    if (opt && opt->overlap && opt->overlap->stream == stream) return LOLA_EINVAL;
-    if (n == 0) return LOLA_OK;
-    if (!q || !k || !v || !y || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y)) return LOLA_EINVAL;
-    if (fold_at && !aligned16(fold_at)) return LOLA_EINVAL;
+    const lola_status rc = lola::prefill_checks(st, phi, q, k, v, n, C, opt, y, fold_at, stream);
+    if (rc != LOLA_OK || n == 0) return rc;
     const WsLayout L = make_layout(st, n, C);
     const size_t need = (size_t)L.per_bh * (size_t)st->B * (size_t)st->n_heads;
     if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes < need) return LOLA_EINVAL;

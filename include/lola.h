@@ -31,7 +31,8 @@
  *     LOLA_EINVAL or LOLA_EUNSUPPORTED and leaves the state (device arrays and `t`) untouched.
  *     A launch failure returns LOLA_EDEVICE (the state may then be partially updated).
  *   - No global state: the library keeps no stream, event, lock or cached device property between
- *     calls, so distinct states may be driven from different threads and streams.
+ *     calls, so distinct states may be driven from different threads and streams.  (The one exception
+ *     is lola_prefill_noalloc's scratch array and its per-device address, below.)
  *   - Supported shapes (v1): d_k == d_v in {64, 128}, D == 128, 0 <= lambda <= 1024, 1 <= C <= 128,
  *     eta >= 0, positions below 2^31.
  *   - Device arrays must be 16-byte aligned.
@@ -185,6 +186,18 @@ lola_status lola_prefill_profiled(lola_state *st, const lola_phi *phi, const voi
 lola_status lola_prefill_ex(lola_state *st, const lola_phi *phi, const void *q, const void *k, const void *v,
                             int64_t n, int32_t C, const lola_options *opt, void *y, int32_t *fold_at,
                             void *workspace, size_t workspace_bytes, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): lola_prefill_ex without a workspace argument.  The scratch is a
+ * device array of LOLA_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until the process
+ * ends; its address is looked up once per device.  A call needs lola_workspace_bytes(st, n, C) <=
+ * LOLA_NOALLOC_SCRATCH_BYTES, else LOLA_EUNSUPPORTED before anything is queued.  Calls on one GPU share
+ * its array: calls whose device work overlaps on one GPU race (order them on one stream, or wait).
+ * Results equal lola_prefill_ex's.  Allocates and frees nothing. */
+#define LOLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+lola_status lola_prefill_noalloc(lola_state *st, const lola_phi *phi, const void *q, const void *k,
+                                 const void *v, int64_t n, int32_t C, const lola_options *opt, void *y,
+                                 int32_t *fold_at, void *stream);
 
 /* One decode token for every sequence and head (section 2.4 single-token update, then Eq. (14)):
  * the token leaving the window (if any) joins the candidates, one candidate is folded when the cache

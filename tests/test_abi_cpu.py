@@ -177,9 +177,13 @@ def test_overlap_validation_without_gpu(lib):
 
 def test_no_process_wide_handles_in_the_sources():
     """The library keeps no stream, event, lock or cached device property between calls: no kernel
-    source creates a stream or an event, holds a mutex, or caches a value in a function-local static."""
+    source creates a stream or an event, holds a mutex, or caches a value in a static.  The one
+    exception is the allocation-free entry point's scratch array and its per-device address
+    (lola_noalloc.hip), which the header states."""
     csrc = os.path.join(ROOT, "hybrid_linear_attention_chunkwise_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
+        if name == "lola_noalloc.hip":
+            continue
         text = open(os.path.join(csrc, name)).read()
         for banned in ("hipStreamCreate", "hipEventCreate", "std::mutex", "<mutex>"):
             assert banned not in text, (name, banned)
@@ -187,3 +191,22 @@ def test_no_process_wide_handles_in_the_sources():
             code = line.split("//")[0].strip()
             if code.startswith("static ") and "=" in code and "constexpr" not in code and "(" not in code.split("=")[0]:
                 raise AssertionError(f"{name}: static data: {line.strip()}")
+
+
+def test_noalloc_rejects_before_any_work(lib):
+    """lola_prefill_noalloc validates like lola_prefill_ex and refuses calls whose scratch exceeds its
+    array (LOLA_NOALLOC_SCRATCH_BYTES) before touching the device."""
+    phi = B.LolaPhi(B.LOLA_PHI_SOFTMAX_PM, 128, 128, 0, 0x200000)
+    p = 0x300000
+    st = _fake_ptrs(_state(d_k=96, d_v=96))
+    assert lib.lola_prefill_noalloc(ctypes.byref(st), ctypes.byref(phi), p, p, p, 16, 16, None, p, None,
+                                    None) == B.LOLA_EUNSUPPORTED
+    st = _state()                                          # null state arrays
+    assert lib.lola_prefill_noalloc(ctypes.byref(st), ctypes.byref(phi), p, p, p, 16, 16, None, p, None,
+                                    None) == B.LOLA_EINVAL
+    big = _fake_ptrs(_state(B=8, n_heads=32))
+    n = 4096
+    assert lib.lola_workspace_bytes(ctypes.byref(big), n, 64) > B.LOLA_NOALLOC_SCRATCH_BYTES
+    assert lib.lola_prefill_noalloc(ctypes.byref(big), ctypes.byref(phi), p, p, p, n, 64, None, p, None,
+                                    None) == B.LOLA_EUNSUPPORTED
+    assert big.t == 0
