@@ -387,7 +387,29 @@ def bench_decode(args, lola, torch, wl):
     log(f"multi-token decode ({c_dec} tokens per call): {best_m / calls * 1e3:.3f} ms/call")
     multi = {"value": round(wl.B * calls * c_dec / best_m, 1), "unit": "decode tokens/s", "tokens_per_call": c_dec,
              "ms_per_call": round(best_m / calls * 1e3, 4)}
-    return {"wall": wall, "kern_ms": kern_ms, "kern_ms_min": min(kerns), "runs": len(walls), "multi": multi}
+    # chunked decode: the same single-token steps with the allocation once per group of C_DEC steps
+    walls_c, kerns_c = [], []
+    for run in range(args.decode_runs + 1):
+        st.restore(snap)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(steps):
+            evs[s].record()
+            lola.lola_decode_step(st, phi, dq[s], dk[s], dv[s], y=y, decode_chunk=c_dec)
+        evs[steps].record()
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        if run > 0:
+            walls_c.append(el)
+            kerns_c.append(sum(evs[s].elapsed_time(evs[s + 1]) for s in range(steps)) / steps)
+    wall_c, kern_c = statistics.median(walls_c), statistics.median(kerns_c)
+    log(f"chunked decode (groups of {c_dec} steps): {wall_c / steps * 1e3:.3f} ms/step wall, kernel "
+        f"{kern_c:.4f} ms/step")
+    chunked = {"value": round(wl.B * steps / wall_c, 1), "unit": "decode tokens/s", "decode_chunk": c_dec,
+               "kernel_ms_per_step": round(kern_c, 5), "kernel_ms_per_step_min": round(min(kerns_c), 5),
+               "ms_per_step_wall": round(wall_c / steps * 1e3, 4)}
+    return {"wall": wall, "kern_ms": kern_ms, "kern_ms_min": min(kerns), "runs": len(walls), "multi": multi,
+            "chunked": chunked}
 
 
 def bench_peaks(lola, torch):
@@ -584,7 +606,7 @@ def main() -> int:
                                       "traffic": load_traffic("decode"), "kernel_ms": round(r["kern_ms"], 4),
                                       "kernel_ms_min": round(r["kern_ms_min"], 4),
                                       "algorithmic_bytes_per_launch": byts},
-                         "multi_token": r["multi"]}
+                         "multi_token": r["multi"], "chunked": r["chunked"]}
         if "peaks_measured" in out:
             out["decode"]["roofline"]["frac_vs_measured_copy"] = round(ach_d / out["peaks_measured"]["copy_gbs"], 4)
     import argparse as _ap

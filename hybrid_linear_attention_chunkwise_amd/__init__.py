@@ -67,11 +67,12 @@ class LolaState:
         self.cache_pos = torch.full((B, n_heads, max(lam, 1)), -1, dtype=torch.int32, **kw)
         self.win_score = torch.zeros(B, n_heads, max(eta, 1), dtype=torch.float32, **kw)
         self.cache_score = torch.zeros(B, n_heads, max(lam, 1), dtype=torch.float32, **kw)
+        self.dec_fold = torch.zeros(B, n_heads, dtype=torch.int64, **kw)
         self.c = _b.LolaState(B, n_heads, d_k, d_v, D, eta, lam, _DTYPES[dtype], 0,
                               self.H.data_ptr(), self.s.data_ptr(), self.win_k.data_ptr(),
                               self.win_v.data_ptr(), self.cache_k.data_ptr(), self.cache_v.data_ptr(),
                               self.cache_pos.data_ptr(), self.win_score.data_ptr(),
-                              self.cache_score.data_ptr())
+                              self.cache_score.data_ptr(), self.dec_fold.data_ptr(), 0, 0)
 
     @property
     def t(self) -> int:
@@ -84,14 +85,16 @@ class LolaState:
 
     def snapshot(self) -> dict:
         """Device copies of every state array plus t (for restore / checkpoint)."""
-        return {k: getattr(self, k).clone() for k in self._ARRAYS} | {"t": self.t}
+        return {k: getattr(self, k).clone() for k in self._ARRAYS} | {"t": self.t, "dec_chunk": int(self.c.dec_chunk)}
 
-    _ARRAYS = ("H", "s", "win_k", "win_v", "cache_k", "cache_v", "cache_pos", "win_score", "cache_score")
+    _ARRAYS = ("H", "s", "win_k", "win_v", "cache_k", "cache_v", "cache_pos", "win_score", "cache_score",
+               "dec_fold")
 
     def restore(self, snap: dict) -> None:
         for k in self._ARRAYS:
             getattr(self, k).copy_(snap[k])
         self.c.t = snap["t"]
+        self.c.dec_chunk = snap.get("dec_chunk", 0)
 
 
 class LolaOverlap:
@@ -116,12 +119,12 @@ def lola_state_init(state: LolaState, stream=None) -> None:
     _b.check("lola_state_init", _b.load().lola_state_init(ctypes.byref(state.c), _stream(stream)))
 
 
-def _options(read_mask: int, score_rule: str, overlap: Optional[LolaOverlap] = None):
+def _options(read_mask: int, score_rule: str, overlap: Optional[LolaOverlap] = None, decode_chunk: int = 0):
     """ctypes options, or None for the defaults."""
-    if read_mask == LOLA_READ_ALL and score_rule == "sre" and overlap is None:
+    if read_mask == LOLA_READ_ALL and score_rule == "sre" and overlap is None and decode_chunk <= 1:
         return None
     ov = ctypes.pointer(overlap.c) if overlap is not None else None
-    return _b.LolaOptions(read_mask, SCORE_RULES[score_rule], (ctypes.c_int32 * 2)(0, 0), ov)
+    return _b.LolaOptions(read_mask, SCORE_RULES[score_rule], decode_chunk, 0, ov)
 
 
 def lola_prefill(state: LolaState, phi: LolaPhi, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
@@ -175,12 +178,15 @@ def lola_prefill_noalloc(state: LolaState, phi: LolaPhi, q: torch.Tensor, k: tor
 
 def lola_decode_step(state: LolaState, phi: LolaPhi, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                      y: Optional[torch.Tensor] = None, folded_pos: Optional[torch.Tensor] = None,
-                     stream=None, read_mask: int = LOLA_READ_ALL, score_rule: str = "sre"):
-    """One decode token, q, k, v [B][h][d]; returns (y, folded_pos).  Asynchronous on `stream`."""
+                     stream=None, read_mask: int = LOLA_READ_ALL, score_rule: str = "sre",
+                     decode_chunk: int = 0):
+    """One decode token, q, k, v [B][h][d]; returns (y, folded_pos).  Asynchronous on `stream`.
+    decode_chunk > 1: chunked decode (allocation once per group of that many steps; folded_pos must
+    be None)."""
     if y is None:
         y = torch.empty(v.shape, dtype=v.dtype, device=v.device)
     lib = _b.load()
-    opts = _options(read_mask, score_rule)
+    opts = _options(read_mask, score_rule, None, decode_chunk)
     if opts is None:
         code = lib.lola_decode_step(ctypes.byref(state.c), ctypes.byref(phi.c), _ptr(q), _ptr(k),
                                     _ptr(v), _ptr(y), _ptr(folded_pos), _stream(stream))

@@ -45,7 +45,8 @@ class LolaState(ctypes.Structure):
                 ("H", ctypes.c_void_p), ("s", ctypes.c_void_p), ("win_k", ctypes.c_void_p),
                 ("win_v", ctypes.c_void_p), ("cache_k", ctypes.c_void_p), ("cache_v", ctypes.c_void_p),
                 ("cache_pos", ctypes.c_void_p), ("win_score", ctypes.c_void_p),
-                ("cache_score", ctypes.c_void_p)]
+                ("cache_score", ctypes.c_void_p), ("dec_fold", ctypes.c_void_p), ("dec_chunk", ctypes.c_int32),
+                ("reserved_state", ctypes.c_int32)]
 
 
 LOLA_OVERLAP_EVENTS = 9
@@ -57,7 +58,8 @@ class LolaOverlap(ctypes.Structure):
 
 class LolaOptions(ctypes.Structure):
     _fields_ = [("read_mask", ctypes.c_int32), ("score_rule", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 2), ("overlap", ctypes.POINTER(LolaOverlap))]
+                ("decode_chunk", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("overlap", ctypes.POINTER(LolaOverlap))]
 
 
 class LolaError(RuntimeError):

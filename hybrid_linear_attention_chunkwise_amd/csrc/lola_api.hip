@@ -48,7 +48,7 @@ lola_status check_options(const lola_state* st, const lola_options* opt) {
     if (!opt) return LOLA_OK;
     if ((opt->read_mask & ~LOLA_READ_ALL) != 0 || !(opt->read_mask & LOLA_READ_WINDOW)) return LOLA_EINVAL;
     if (opt->score_rule < LOLA_SCORE_SRE || opt->score_rule > LOLA_SCORE_ATTN) return LOLA_EINVAL;
-    if (opt->reserved[0] != 0 || opt->reserved[1] != 0) return LOLA_EINVAL;
+    if (opt->reserved != 0 || opt->decode_chunk < 0 || opt->decode_chunk > 64) return LOLA_EINVAL;
     if (opt->overlap) {
         if (!opt->overlap->stream) return LOLA_EINVAL;
         for (int i = 0; i < LOLA_OVERLAP_EVENTS; ++i)
@@ -154,6 +154,7 @@ lola_status prefill_checks(const lola_state* st, const lola_phi* phi, const void
     if (rc != LOLA_OK) return rc;
     rc = check_prefill_config(st, n, C);
     if (rc != LOLA_OK) return rc;
+    if (st->dec_chunk != 0 || (opt && opt->decode_chunk > 1)) return LOLA_EINVAL;   // a decode group is open
     if (opt && opt->overlap && opt->overlap->stream == stream) return LOLA_EINVAL;
     if (n == 0) return LOLA_OK;
     if (!q || !k || !v || !y || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y)) return LOLA_EINVAL;
@@ -199,6 +200,7 @@ lola_status lola_state_init(lola_state* st, void* stream) {
     a.cache_score = st->lambda > 0 ? st->cache_score : nullptr;
     if (lola::launch_init(a, (hipStream_t)stream) != hipSuccess) return LOLA_EDEVICE;
     st->t = 0;
+    st->dec_chunk = 0;
     return LOLA_OK;
 }
 
@@ -280,12 +282,22 @@ static lola_status decode_impl(lola_state* st, const lola_phi* phi, const void* 
     rc = check_options(st, opt);
     if (rc != LOLA_OK) return rc;
     if (opt && opt->score_rule != LOLA_SCORE_SRE) return LOLA_EUNSUPPORTED;
+    if (opt && opt->overlap) return LOLA_EINVAL;                         // decode runs one kernel per step
+    const int cd = (opt && opt->decode_chunk > 1) ? opt->decode_chunk : 0;
+    if (st->dec_chunk != 0 && st->dec_chunk != cd) return LOLA_EINVAL;  // another group is open
     if (!q || !k || !v || !y || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y)) return LOLA_EINVAL;
     if (folded_pos && !aligned16(folded_pos)) return LOLA_EINVAL;
     if (st->t + 1 + st->eta >= (int64_t)INT_MAX) return LOLA_EUNSUPPORTED;
     const int esz = st->dtype == LOLA_BF16 ? 2 : 4;
-    const size_t lds = lola::decode_lds_bytes(st->d_k, phi->kind, esz, st->lambda) + 4 * (size_t)(st->eta + 16);
-    if (lds > kLdsLimit) return LOLA_EUNSUPPORTED;
+    if (cd > 0) {
+        if (folded_pos || !st->dec_fold || ((uintptr_t)st->dec_fold & 7u) != 0) return LOLA_EINVAL;
+        if (st->lambda > 0 && st->eta < cd - 1) return LOLA_EINVAL;     // causality of the group's allocation
+        if (lola::decode_group_lds_bytes(st->d_k, phi->kind, esz, st->lambda, st->eta, cd) > kLdsLimit)
+            return LOLA_EUNSUPPORTED;
+    } else {
+        const size_t lds = lola::decode_lds_bytes(st->d_k, phi->kind, esz, st->lambda) + 4 * (size_t)(st->eta + 16);
+        if (lds > kLdsLimit) return LOLA_EUNSUPPORTED;
+    }
 
     lola::DecodeArgs a;
     a.BH = st->B * st->n_heads;
@@ -299,15 +311,24 @@ static lola_status decode_impl(lola_state* st, const lola_phi* phi, const void* 
     a.win_k = st->win_k; a.win_v = st->win_v;
     a.cache_k = st->cache_k; a.cache_v = st->cache_v; a.cache_pos = st->cache_pos;
     a.folded_pos = folded_pos;
-    // bf16 states whose cache and window fit the register-resident kernel take it
-    const bool fast = st->dtype == LOLA_BF16 && lola::decode_fast_fits(st->d_k, st->lambda, st->eta) &&
-                      lola::decode_fast_lds_bytes(st->d_k, phi->kind) <= kLdsLimit &&
-                      !getenv("LOLA_DECODE_GENERAL");
-    const hipError_t e = fast ? lola::launch_decode_fast(a, st->d_k, phi->kind, (hipStream_t)stream)
-                              : lola::launch_decode(a, st->dtype, st->d_k, phi->kind, (hipStream_t)stream);
+    a.dec_chunk = cd;
+    a.group_start = (cd > 0 && st->dec_chunk == 0) ? 1 : 0;
+    a.dec_fold = reinterpret_cast<unsigned long long*>(st->dec_fold);
+    hipError_t e;
+    if (cd > 0) {
+        e = lola::launch_decode_group(a, st->dtype, st->d_k, phi->kind, (hipStream_t)stream);
+    } else {
+        // bf16 states whose cache and window fit the register-resident kernel take it
+        const bool fast = st->dtype == LOLA_BF16 && lola::decode_fast_fits(st->d_k, st->lambda, st->eta) &&
+                          lola::decode_fast_lds_bytes(st->d_k, phi->kind) <= kLdsLimit &&
+                          !getenv("LOLA_DECODE_GENERAL");
+        e = fast ? lola::launch_decode_fast(a, st->d_k, phi->kind, (hipStream_t)stream)
+                 : lola::launch_decode(a, st->dtype, st->d_k, phi->kind, (hipStream_t)stream);
+    }
     if (e != hipSuccess) return LOLA_EDEVICE;
     if (getenv("LOLA_DEBUG_SYNC") && hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return LOLA_EDEVICE;
     st->t += 1;
+    if (cd > 0) st->dec_chunk = (st->t % cd == 0) ? 0 : cd;              // the group's last step closes it
     return LOLA_OK;
 }
 
@@ -377,6 +398,7 @@ lola_status lola_sre_collisions(const lola_state* st, const void* v, const int32
     if (rc != LOLA_OK) return rc;
     if (!st->H || !st->s || !aligned16(st->H) || !aligned16(st->s)) return LOLA_EINVAL;
     if (n < 0 || C < 1 || (relative != 0 && relative != 1)) return LOLA_EINVAL;
+    if (st->dec_chunk != 0) return LOLA_EINVAL;
     if (C > kMaxChunk || n > INT_MAX / 2) return LOLA_EUNSUPPORTED;
     if (n == 0) return LOLA_OK;
     if (!v || !fold_at || !out || !aligned16(v) || !aligned16(fold_at) || !aligned16(out)) return LOLA_EINVAL;

@@ -92,6 +92,11 @@ struct DecodeArgs {
     void* cache_v;
     int32_t* cache_pos;
     int32_t* folded_pos;  // nullable
+    // chunked decode (dec_chunk > 1): the group's fold mask per (sequence, head), and whether this step
+    // opens a group (allocation for the group's leaving tokens)
+    int dec_chunk;
+    int group_start;
+    unsigned long long* dec_fold;
 };
 
 // SRE collision map of one prefill call, read from that call's workspace and the state it left.
@@ -186,6 +191,9 @@ struct Overlap {
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int d, int phi_kind, hipStream_t stream,
                           hipEvent_t const* events = nullptr, const Overlap* overlap = nullptr);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int d, int phi_kind, hipStream_t stream);
+// Chunked decode step (DecodeArgs::dec_chunk > 1), and its LDS bytes.
+hipError_t launch_decode_group(const DecodeArgs& a, int dtype, int d, int phi_kind, hipStream_t stream);
+size_t decode_group_lds_bytes(int d, int phi_kind, int esz, int lam, int eta, int cd);
 // Register-resident decode for bf16 storage, when the cache and window fit its tiles.
 bool decode_fast_fits(int d, int lam, int eta);
 size_t decode_fast_lds_bytes(int d, int phi_kind);

@@ -99,6 +99,15 @@ typedef struct lola_state {
      * A state keeps one scoring rule for its whole life; lola_state_init zeroes both. */
     float *win_score;
     float *cache_score;
+    /* Chunked decode (lola_decode_step_ex with decode_chunk > 1; may be NULL otherwise):
+     *   dec_fold  [B][n_heads] uint64, device: which of the open group's leaving tokens are folded at
+     *             their exit (bit = exit time mod decode_chunk)
+     *   dec_chunk host: the decode_chunk of the group still open (0: none).  lola_state_init sets 0.
+     *             While a group is open only lola_decode_step_ex with the same decode_chunk accepts the
+     *             state; every other entry point returns LOLA_EINVAL. */
+    uint64_t *dec_fold;
+    int32_t dec_chunk;
+    int32_t reserved_state;
 } lola_state;
 
 /* Read-branch masks (section 4.8, Table 12): the memories a query reads in Eq. (14).  Storage and
@@ -141,7 +150,8 @@ typedef struct lola_overlap {
 typedef struct lola_options {
     int32_t read_mask;    /* LOLA_READ_* bits, containing LOLA_READ_WINDOW */
     int32_t score_rule;   /* LOLA_SCORE_* */
-    int32_t reserved[2];  /* must be 0 */
+    int32_t decode_chunk; /* lola_decode_step_ex only: 0 or 1 = allocate every step; 2..64 = chunked decode */
+    int32_t reserved;     /* must be 0 */
     /* nullable: without it every kernel of the call runs on the call's stream, one after another */
     const lola_overlap *overlap;
 } lola_options;
@@ -210,7 +220,19 @@ lola_status lola_decode_step(lola_state *st, const lola_phi *phi, const void *q,
 /* lola_decode_step with options (NULL = defaults, which is lola_decode_step).  The read mask applies as
  * in lola_prefill_ex.  A scoring rule other than LOLA_SCORE_SRE returns LOLA_EUNSUPPORTED here: such
  * states decode through lola_prefill_ex with n = C = 1 (or several tokens per call), which is the same
- * single-token update and needs the workspace this entry point does not take. */
+ * single-token update and needs the workspace this entry point does not take.
+ *
+ * Chunked decode (section 2.6, Eq. (15), Fig. 2, for one token at a time): with decode_chunk = Cd in
+ * 2..64 the allocation runs once per group of steps, groups covering the exit times [a, b) with b the
+ * next multiple of Cd after a (from a state with t a multiple of Cd every group is Cd steps).  At a
+ * group's first step the cache and the tokens that leave the window during the group are scored against
+ * the state (as one prefill chunk: same candidates, same top-lambda, ties to the older position); the
+ * losing cache members are folded at once, the losing leaving tokens at their own exit step, and the
+ * kept leaving tokens take the freed slots.  Each step reads out over the window, the cache members
+ * that have left the window and the state, so Cd steps give what lola_prefill with C = Cd gives on
+ * the same tokens.  Needs st->dec_fold (8-byte aligned), folded_pos == NULL (a group step may fold
+ * several tokens) and lambda == 0 or eta >= Cd - 1; LOLA_EINVAL otherwise.  The group's last step closes
+ * it (st->dec_chunk back to 0). */
 lola_status lola_decode_step_ex(lola_state *st, const lola_phi *phi, const void *q, const void *k, const void *v,
                                 const lola_options *opt, void *y, int32_t *folded_pos, void *stream);
 

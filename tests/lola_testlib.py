@@ -178,6 +178,48 @@ def grade_decode_steps(so, phi_o, dq, dk, dv, ys, folds, dtype: str, read_mask: 
     return {"max_row_rel_err": worst, "fold_mismatches": mism, "steps": len(ys)}
 
 
+def grade_chunked_decode(so, phi_o, q, k, v, ys, caches, t0: int, cd: int, dtype: str) -> dict:
+    """Grades chunked decode steps of one (sequence, head) against the oracle state ``so`` (mutated:
+    it follows the GPU).  Each group of steps [a, b) (b the next multiple of cd after a) is one chunk
+    of the oracle's prefill (LoLA notes 2.6).
+
+    q, k, v [steps][d]; ys [steps][d_v] GPU outputs; caches [steps + 1] GPU cache positions (sorted
+    lists) before the first step and after every step.  The GPU's folds of a group are the group's
+    candidates (the cache at its start and the tokens leaving during it) minus its cache at the end.
+    Where they differ from the oracle's own: fp32 needs the oracle's boundary gap within the tie band;
+    both modes replay the GPU's choice (validated in fp64) and continue from it."""
+    from oracle import lola_oracle as O
+    tol = TIE_BAND if dtype == "f32" else BF16_TOL
+    out_tol = FP32_TOL if dtype == "f32" else BF16_TOL
+    worst, mism, s, steps = 0.0, 0, 0, len(ys)
+    while s < steps:
+        a = t0 + s
+        b = min((a // cd + 1) * cd, t0 + steps)
+        n = b - a
+        X = [p for p in range(a - so.eta, b - so.eta) if p >= 0]
+        cand = set(caches[s]) | set(X)
+        s_gpu = sorted(cand - set(caches[s + n - 1 + 1]))
+        trial = so.copy()
+        y_o, sch = O.prefill(trial, phi_o, q[s:s + n], k[s:s + n], v[s:s + n], C=n)
+        if sorted(sch.folded[0]) == s_gpu:
+            so.__dict__.update(trial.__dict__)
+        else:
+            mism += 1
+            if dtype == "f32":
+                gap = sch.gap[0]
+                assert gap is not None and gap <= TIE_BAND, (
+                    f"fp32 group at {a}: oracle folds {sch.folded[0]}, GPU {s_gpu}, gap {gap}")
+            y_o, sch_r = O.prefill(so, phi_o, q[s:s + n], k[s:s + n], v[s:s + n], C=n, fold_sets_in=[s_gpu],
+                                   tol=tol)
+            assert not sch_r.problems, f"invalid GPU group fold at {a}: {sch_r.problems}"
+        assert sorted(so.cache) == sorted(caches[s + n]), f"cache after the group at {a} differs"
+        err = row_rel_err(np.asarray(ys[s:s + n]), y_o)
+        assert err <= out_tol, f"chunked decode output error {err:.3e} > {out_tol} in the group at {a}"
+        worst = max(worst, err)
+        s += n
+    return {"max_row_rel_err": worst, "group_mismatches": mism, "steps": steps}
+
+
 def gpu_run_prefill(q, k, v, W, phi_kind: str, eta: int, lam: int, C: int, dtype: str, D: int = 128,
                     chunks: Optional[Sequence[int]] = None, state=None):
     """Runs lola_prefill on cuda:0 for numpy q, k, v [B][h][n][d]; returns host arrays.

@@ -93,7 +93,7 @@ def test_options_validation_without_gpu(lib, mask, rule, reserved):
     query-accumulated rule on a state without score arrays are all rejected up front."""
     phi = B.LolaPhi(B.LOLA_PHI_SOFTMAX_PM, 128, 128, 0, 0x200000)
     st = _fake_ptrs(_state())
-    opt = B.LolaOptions(mask, rule, (ctypes.c_int32 * 2)(reserved, 0))
+    opt = B.LolaOptions(mask, rule, 0, reserved)
     p = 0x300000
     rc = lib.lola_prefill_ex(ctypes.byref(st), ctypes.byref(phi), p, p, p, 16, 16, ctypes.byref(opt), p,
                              None, 0x400000, 1 << 40, None)
@@ -168,7 +168,7 @@ def test_overlap_validation_without_gpu(lib):
     for ov_stream, ev, call_stream in cases:
         st = _fake_ptrs(_state())
         ov = B.LolaOverlap(ov_stream, (ctypes.c_void_p * B.LOLA_OVERLAP_EVENTS)(*ev))
-        opt = B.LolaOptions(B.LOLA_READ_ALL, 0, (ctypes.c_int32 * 2)(0, 0), ctypes.pointer(ov))
+        opt = B.LolaOptions(B.LOLA_READ_ALL, 0, 0, 0, ctypes.pointer(ov))
         rc = lib.lola_prefill_ex(ctypes.byref(st), ctypes.byref(phi), p, p, p, 16, 16, ctypes.byref(opt), p,
                                  None, 0x400000, 1 << 40, call_stream)
         assert rc == B.LOLA_EINVAL
@@ -210,3 +210,25 @@ def test_noalloc_rejects_before_any_work(lib):
     assert lib.lola_prefill_noalloc(ctypes.byref(big), ctypes.byref(phi), p, p, p, n, 64, None, p, None,
                                     None) == B.LOLA_EUNSUPPORTED
     assert big.t == 0
+
+
+def test_chunked_decode_validation_without_gpu(lib):
+    """decode_chunk above 64, a chunked step with folded_pos, without the fold mask array, or with
+    lambda > 0 and eta < decode_chunk - 1 are rejected before anything is queued."""
+    phi = B.LolaPhi(B.LOLA_PHI_SOFTMAX_PM, 128, 128, 0, 0x200000)
+    p = 0x300000
+    cases = [(65, dict(), None), (8, dict(), 0x500000), (8, dict(dec_fold=0), None),
+             (32, dict(eta=16), None)]
+    for cd, over, folded in cases:
+        st = _fake_ptrs(_state(eta=over.get("eta", 256)))
+        st.dec_fold = over.get("dec_fold", 0x700000)
+        opt = B.LolaOptions(B.LOLA_READ_ALL, 0, cd, 0, None)
+        rc = lib.lola_decode_step_ex(ctypes.byref(st), ctypes.byref(phi), p, p, p, ctypes.byref(opt), p, folded,
+                                     None)
+        assert rc == B.LOLA_EINVAL, (cd, over)
+        assert st.t == 0 and st.dec_chunk == 0
+    st = _fake_ptrs(_state())
+    st.dec_chunk = 8                      # a group is open: prefill is refused
+    rc = lib.lola_prefill_ex(ctypes.byref(st), ctypes.byref(phi), p, p, p, 16, 16, None, p, None, 0x400000,
+                             1 << 40, None)
+    assert rc == B.LOLA_EINVAL

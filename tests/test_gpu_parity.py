@@ -782,3 +782,92 @@ def test_hola_degenerate_gates(dtype):
         scale = max(1.0, float(np.abs(S_o).max()))
         assert np.abs(S_out[0, hh] - S_o).max() <= 1e-4 * scale
         assert TL.row_rel_err(y[0, hh], y_o) <= tol
+
+
+# ------------------------------------------------------------------------------------------------
+# Chunked single-token decode (allocation once per group of decode_chunk steps).
+# ------------------------------------------------------------------------------------------------
+
+def chunked_decode_check(wl, n0, steps, cd, heads):
+    """Prefill n0 tokens, then `steps` single-token decode steps with decode_chunk = cd.  Each group
+    of steps is graded against the oracle's prefill of the same tokens as one chunk, continuing from
+    the GPU's post-prefill state (grade_chunked_decode)."""
+    import hybrid_linear_attention_chunkwise_amd as lola
+    from oracle import lola_oracle as O
+    W = make_weights(wl)
+    q, k, v = make_qkv(wl, n=n0)
+    tdt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+    C0 = 16 if wl.lam == 0 else min(16, wl.eta + 1)
+    _, _, st, phi = TL.gpu_run_prefill(q, k, v, W, wl.phi, wl.eta, wl.lam, C0, wl.dtype, D=wl.D)
+    snap = TL.state_to_host(st)
+    dq, dk, dv = make_decode_tokens(wl, steps=steps)
+    ys, caches = [], [st.cache_pos.cpu().numpy().copy()]
+    for s in range(steps):
+        y, _ = lola.lola_decode_step(st, phi, torch.from_numpy(dq[s]).cuda().to(tdt),
+                                     torch.from_numpy(dk[s]).cuda().to(tdt),
+                                     torch.from_numpy(dv[s]).cuda().to(tdt), decode_chunk=cd)
+        ys.append(y.float())
+        caches.append(st.cache_pos.cpu().numpy().copy())
+    torch.cuda.synchronize()
+    assert st.c.dec_chunk == (0 if (n0 + steps) % cd == 0 else cd)
+    ys = torch.stack(ys).cpu().numpy()
+    phi_o = O.make_phi(wl.phi, W)
+    worst, mism = 0.0, 0
+    for (b, h) in heads:
+        so = O.state_from_arrays(snap["t"], wl.eta, wl.lam, snap["H"][b, h].T, snap["s"][b, h],
+                                 snap["win_k"][b, h], snap["win_v"][b, h], snap["cache_k"][b, h],
+                                 snap["cache_v"][b, h], snap["cache_pos"][b, h])
+        cl = [TL.cache_members(c_[b, h]) for c_ in caches]
+        rep = TL.grade_chunked_decode(so, phi_o, dq[:, b, h].astype(np.float64), dk[:, b, h].astype(np.float64),
+                                      dv[:, b, h].astype(np.float64), ys[:, b, h], cl, n0, cd, wl.dtype)
+        worst = max(worst, rep["max_row_rel_err"])
+        mism += rep["group_mismatches"]
+    print(f"[chunked decode] {wl.name} cd={cd}: max err {worst:.3e}, group mismatches {mism}", flush=True)
+    return worst
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("cd", [4, 16])
+def test_chunked_decode_small(dtype, cd):
+    wl = small_workload(140 + cd, B=2, h=2, n=0, C=1, eta=20, lam=16, d_k=64, d_v=64, dtype=dtype)
+    chunked_decode_check(wl, n0=64, steps=48, cd=cd, heads=[(0, 0), (1, 1)])
+
+
+def test_chunked_decode_d128_unaligned_start():
+    """d = 128; the decode starts at t = 70 (not a multiple of 16), so the first group is 10 steps."""
+    wl = small_workload(150, B=1, h=2, n=0, C=1, eta=40, lam=36, d_k=128, d_v=128, dtype="bf16")
+    chunked_decode_check(wl, n0=70, steps=58, cd=16, heads=[(0, 0), (0, 1)])
+
+
+def test_chunked_decode_edge_cases():
+    """lambda = 0 (every leaving token folds at its exit), a cache that is not yet full (no scoring),
+    and eta = Cd - 1 (the group's last leaving token is the current token)."""
+    for kw in (dict(eta=12, lam=0, n0=40), dict(eta=24, lam=300, n0=40), dict(eta=7, lam=10, n0=64)):
+        n0 = kw.pop("n0")
+        wl = small_workload(151, B=1, h=2, n=0, C=1, d_k=64, d_v=64, dtype="f32", **kw)
+        chunked_decode_check(wl, n0=n0, steps=32, cd=8, heads=[(0, 0), (0, 1)])
+
+
+def test_chunked_decode_open_group_is_exclusive():
+    """While a group is open, prefill, per-token decode and another decode_chunk are refused (state
+    untouched); the group's own steps continue."""
+    import hybrid_linear_attention_chunkwise_amd as lola
+    wl = small_workload(152, B=1, h=2, n=0, C=1, eta=20, lam=16, d_k=64, d_v=64, dtype="f32")
+    W = make_weights(wl)
+    q, k, v = make_qkv(wl, n=32)
+    _, _, st, phi = TL.gpu_run_prefill(q, k, v, W, wl.phi, wl.eta, wl.lam, 16, "f32", D=wl.D)
+    dq = torch.randn(wl.B, wl.h, wl.d_k, device="cuda")
+    lola.lola_decode_step(st, phi, dq, dq, dq, decode_chunk=8)
+    assert st.c.dec_chunk == 8 and st.t == 33
+    for call in (lambda: lola.lola_decode_step(st, phi, dq, dq, dq),
+                 lambda: lola.lola_decode_step(st, phi, dq, dq, dq, decode_chunk=4),
+                 lambda: lola.lola_prefill(st, phi, dq[:, :, None].contiguous(), dq[:, :, None].contiguous(),
+                                           dq[:, :, None].contiguous(), 1)):
+        with pytest.raises(lola.LolaError):
+            call()
+        assert st.t == 33
+    for _ in range(7):
+        lola.lola_decode_step(st, phi, dq, dq, dq, decode_chunk=8)
+    assert st.c.dec_chunk == 0 and st.t == 40
+    lola.lola_decode_step(st, phi, dq, dq, dq)
+    torch.cuda.synchronize()
