@@ -208,6 +208,10 @@ hipError_t launch_readout_fast(const PrefillArgs& a, int d, int phi_kind, int c0
 
 // LDS bytes the chain kernel uses (sized for kMaxLambda / kMaxChunk) at element size esz.
 size_t chain_lds_bytes(int d, int phi_kind, int esz);
+// Register-resident chain for bf16, d = 128, lambda <= 256, C <= 64 and SRE scoring (the same
+// decisions and records as the general chain); LOLA_CHAIN_GENERAL in the environment turns it off.
+bool chain_fast_fits(const PrefillArgs& a, int esz, int d);
+hipError_t launch_chain_fast(const PrefillArgs& a, hipStream_t stream);
 size_t decode_lds_bytes(int d, int phi_kind, int esz, int lam);
 
 }  // namespace lola

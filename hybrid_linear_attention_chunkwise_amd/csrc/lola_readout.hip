@@ -511,6 +511,7 @@ template <typename T, int DK, int PHI>
 static hipError_t launch_chain_range(PrefillArgs a, int c0, int c1, hipStream_t stream) {
     a.c_begin = c0;
     a.c_end = c1;
+    if (chain_fast_fits(a, (int)sizeof(T), DK)) return launch_chain_fast(a, stream);
     return launch_chain_t<T, DK, PHI>(a, stream);
 }
 
