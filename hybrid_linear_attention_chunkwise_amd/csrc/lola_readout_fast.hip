@@ -27,112 +27,17 @@
 // same heads: neighbouring chunks share most window and cache keys in that XCD's L2.
 #include "lola_common.hpp"
 #include "lola_internal.hpp"
+#include "lola_readout_common.hpp"
 
 namespace lola {
 
 namespace {
 
+using namespace rd;
+
 constexpr int kRfQ = 128;          // queries per workgroup
 constexpr int kRfKB = 64;          // keys per staged block
 constexpr int kRfThreads = 256;
-constexpr unsigned kNoKey = 0x7FFFFFFFu;
-
-// Whole-wave min / max of unsigned values below 2^31 (DPP inside rows of 16, lane swaps across rows).
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int x) {
-    return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, true);
-}
-__device__ __forceinline__ void wave_minmax_i(int& mn, int& mx) {
-    mn = min(mn, dpp_i<0xB1>(mn)); mx = max(mx, dpp_i<0xB1>(mx));     // quad_perm [1,0,3,2]
-    mn = min(mn, dpp_i<0x4E>(mn)); mx = max(mx, dpp_i<0x4E>(mx));     // quad_perm [2,3,0,1]
-    mn = min(mn, dpp_i<0x124>(mn)); mx = max(mx, dpp_i<0x124>(mx));   // row_ror:4
-    mn = min(mn, dpp_i<0x128>(mn)); mx = max(mx, dpp_i<0x128>(mx));   // row_ror:8
-    {
-        const auto a = __builtin_amdgcn_permlane16_swap((unsigned)mn, (unsigned)mn, false, false);
-        mn = min((int)a[0], (int)a[1]);
-        const auto b = __builtin_amdgcn_permlane16_swap((unsigned)mx, (unsigned)mx, false, false);
-        mx = max((int)b[0], (int)b[1]);
-    }
-    {
-        const auto a = __builtin_amdgcn_permlane32_swap((unsigned)mn, (unsigned)mn, false, false);
-        mn = min((int)a[0], (int)a[1]);
-        const auto b = __builtin_amdgcn_permlane32_swap((unsigned)mx, (unsigned)mx, false, false);
-        mx = max((int)b[0], (int)b[1]);
-    }
-}
-
-// phi of two 16-query tiles (section 2.2), each W^T fragment from LDS serving both: the features as
-// MFMA B operands pf[qq][ss] (reduction order over D) and phi(q).s in lden[qq] (this lane's part).
-template <int DK, int PHI>
-__device__ __forceinline__ void phi_pair(const bf16* wt, int wt_ld, const Frag8<bf16> (&qf)[2][DK / 32],
-                                         const float* s, Frag8<bf16> (&pf)[2][kFeat / 32], float (&lden)[2]) {
-    constexpr int D = kFeat, DW = (PHI == kPhiSoftmaxPM) ? D / 2 : D;
-    const int l = lane_id(), g = l >> 4, c = l & 15;
-    f4 pre[DW / 16][2];
-#pragma unroll
-    for (int ft = 0; ft < DW / 16; ++ft) {
-        pre[ft][0] = zero4();
-        pre[ft][1] = zero4();
-#pragma unroll
-        for (int ss = 0; ss < DK / 32; ++ss) {
-            const Frag8<bf16> a = load_frag(wt + (16 * ft + c) * wt_ld, ss, g);
-            mma32(pre[ft][0], a, qf[0][ss]);
-            mma32(pre[ft][1], a, qf[1][ss]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-        float ph[D / 16][4];
-        if constexpr (PHI == kPhiSoftmaxPM) {
-            float mx = -INFINITY, mn = INFINITY;
-#pragma unroll
-            for (int ft = 0; ft < DW / 16; ++ft)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) { mx = fmaxf(mx, pre[ft][qq][r]); mn = fminf(mn, pre[ft][qq][r]); }
-            mx = max_groups(mx);
-            mn = min_groups(mn);
-            float sp = 0.f, sm = 0.f;
-#pragma unroll
-            for (int ft = 0; ft < DW / 16; ++ft)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float ep = fast_exp(pre[ft][qq][r] - mx);
-                    const float em = fast_exp(mn - pre[ft][qq][r]);
-                    ph[ft][r] = ep;
-                    ph[ft + DW / 16][r] = em;
-                    sp += ep;
-                    sm += em;
-                }
-            const float ip = fast_rcp(sum_groups(sp)), im = fast_rcp(sum_groups(sm));
-#pragma unroll
-            for (int ft = 0; ft < DW / 16; ++ft)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) { ph[ft][r] *= ip; ph[ft + DW / 16][r] *= im; }
-        } else {
-#pragma unroll
-            for (int ft = 0; ft < DW / 16; ++ft)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float z = pre[ft][qq][r];
-                    ph[ft][r] = z > 0.f ? z + 1.f : fast_exp(z);
-                }
-        }
-        float ld = 0.f;
-#pragma unroll
-        for (int ft = 0; ft < D / 16; ++ft) {
-            const f4 sv = *reinterpret_cast<const f4*>(s + 16 * ft + 4 * g);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) ld += ph[ft][r] * sv[r];
-        }
-        asm volatile("" : "+v"(ld));      // formed here: the features are not kept live until it is used
-        lden[qq] = ld;
-#pragma unroll
-        for (int ss = 0; ss < D / 32; ++ss)
-            pf[qq][ss] = frag_from_acc<bf16>(f4{ph[2 * ss][0], ph[2 * ss][1], ph[2 * ss][2], ph[2 * ss][3]},
-                                             f4{ph[2 * ss + 1][0], ph[2 * ss + 1][1], ph[2 * ss + 1][2], ph[2 * ss + 1][3]});
-    }
-}
 
 template <int DK, int PHI>
 struct RfCfg {
@@ -145,36 +50,8 @@ struct RfCfg {
     static constexpr int PPT = kRfKB * CPK / kRfThreads;   // chunks per thread and block (one row)
 };
 
-// Staged rows are unpadded and swizzled so that fragment reads hit 64 distinct banks:
-//   key row r, 16-byte chunk q  -> chunk q ^ ((r / RPB) mod CPK)
-//     (a fragment read takes one chunk of 16 consecutive rows, or two halves of it);
-//   value row r, 32-byte segment s -> segment s ^ ((r / RPB) mod SEG), chunk halves kept
-//     (a transposed read takes one segment of 8 consecutive rows per half-wave).
-template <int DK>
-__device__ __forceinline__ int kswz(int row, int q) {
-    constexpr int RPB = 256 / (2 * DK), CPK = DK / 8;
-    return q ^ ((row / RPB) % CPK);
-}
-template <int DK>
-__device__ __forceinline__ int vswz(int row, int q) {
-    constexpr int RPB = 256 / (2 * DK), SEG = DK / 16;
-    return (((q >> 1) ^ ((row / RPB) % SEG)) << 1) | (q & 1);
-}
-
-// Four bf16 of a transposed LDS read (gfx950): in each group of 16 lanes, lanes 4r .. 4r + 3 give
-// the addresses of row r (four elements each, sixteen in all) and lane i receives element i of rows
-// 0 .. 3.
-__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
-    typedef short v4s __attribute__((ext_vector_type(4)));
-    const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (v4s __attribute__((address_space(3)))*)((__attribute__((address_space(3))) char*)p));
-    bf16x4 out;
-    __builtin_memcpy(&out, &r, sizeof(out));
-    return out;
-}
-
 struct RfLds {
-    size_t k, vt, wt, tlo, span, cpos, csrc, g1ok, dpos, dsrc, fpos, fsrc, misc, total;
+    size_t k, vt, wt, tlo, span, cpos, csrc, g1ok, cpos1, csrc1, dpos, dsrc, fpos, fsrc, misc, total;
 };
 __host__ __device__ constexpr size_t rf_al(size_t x) { return (x + 15) & ~size_t(15); }
 
@@ -191,6 +68,8 @@ __host__ __device__ constexpr RfLds rf_lds() {
     o.cpos = p;  p = rf_al(p + 4 * kMaxLambda);
     o.csrc = p;  p = rf_al(p + 4 * kMaxLambda);
     o.g1ok = p;  p = rf_al(p + 4 * kMaxLambda);
+    o.cpos1 = p; p = rf_al(p + 4 * kMaxLambda);
+    o.csrc1 = p; p = rf_al(p + 4 * kMaxLambda);
     o.dpos = p;  p = rf_al(p + 4 * kRfKB);
     o.dsrc = p;  p = rf_al(p + 4 * kRfKB);
     o.fpos = p;  p = rf_al(p + 4 * 2 * kMaxChunk);
@@ -217,6 +96,8 @@ __global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs
     int* cPos = reinterpret_cast<int*>(smem + lo.cpos);     // cache list of the tile's first chunk
     int* cSrc = reinterpret_cast<int*>(smem + lo.csrc);
     int* g1ok = reinterpret_cast<int*>(smem + lo.g1ok);     // slot unchanged at the second chunk
+    int* cPos1 = reinterpret_cast<int*>(smem + lo.cpos1);   // the second chunk's slot table
+    int* cSrc1 = reinterpret_cast<int*>(smem + lo.csrc1);
     int* dPos = reinterpret_cast<int*>(smem + lo.dpos);     // slots replaced at the second chunk
     int* dSrc = reinterpret_cast<int*>(smem + lo.dsrc);
     int* fPos = reinterpret_cast<int*>(smem + lo.fpos);     // [2][kMaxChunk] fold lists per group
@@ -266,33 +147,33 @@ __global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs
     const int nbb = (nb + KB - 1) / KB;
     const int ncb = sparse ? (lam + KB - 1) / KB : 0;
 
-    // cache list of the first chunk, the second chunk's changes, and both chunks' fold lists
+    // The prologue issues its independent loads together: the query fragments (for the features),
+    // both chunks' slot tables and fold lists, W^T, then (after the barrier) the first key block; the
+    // replaced-slot pass reads the slot tables from LDS.
+    Frag8<T> qf[2][DK / 32];
+    auto load_q = [&]() {
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+            const int64_t tq = tw0 + 16 * qq + c;
+#pragma unroll
+            for (int ss = 0; ss < DK / 32; ++ss)
+                qf[qq][ss] = tq < tend ? load_frag(qin + (tq - t0) * DK, ss, g) : frag_zero<T>();
+        }
+    };
+    const bool lin = (A.read_mask & kReadState) && wave_active;
+    if (lin) load_q();
     if (sparse) {
         const int* p0 = reinterpret_cast<const int*>(rec0 + A.L.c_cache_pos);
         const int* s0 = reinterpret_cast<const int*>(rec0 + A.L.c_cache_src);
         const int* p1 = reinterpret_cast<const int*>(rec1 + A.L.c_cache_pos);
         const int* s1 = reinterpret_cast<const int*>(rec1 + A.L.c_cache_src);
         for (int j = tid; j < lam; j += kRfThreads) {
-            const int a0 = p0[j], a1 = p1[j];
+            const int a0 = p0[j], b0 = s0[j], a1 = p1[j], b1 = s1[j];
             cPos[j] = a0;
-            cSrc[j] = s0[j];
+            cSrc[j] = b0;
+            cPos1[j] = a1;
+            cSrc1[j] = b1;
             g1ok[j] = a0 == a1;
-        }
-        // replaced slots: ballot over 64-slot groups, one wave
-        if (w == 0) {
-            int base = 0;
-            const unsigned long long lt = l ? (~0ull >> (64 - l)) : 0ull;
-            for (int j0 = 0; j0 < lam; j0 += 64) {
-                const int j = j0 + l;
-                int a0 = -1, a1 = -1, sr = -1;
-                if (j < lam) { a0 = p0[j]; a1 = p1[j]; sr = s1[j]; }
-                const bool rep = j < lam && a1 >= 0 && a1 != a0;
-                const unsigned long long m = __ballot(rep);
-                const int k = base + __popcll(m & lt);
-                if (rep && k < KB) { dPos[k] = a1; dSrc[k] = sr; }
-                base += __popcll(m);
-            }
-            if (l == 0) misc[0] = base < KB ? base : KB;
         }
     } else if (tid == 0) {
         misc[0] = 0;
@@ -311,9 +192,23 @@ __global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs
     // W^T in LDS for the query features
     if (A.read_mask & kReadState) stage_wt<T, DK, DW, kRfThreads>(wt, WT_LD, A.W);
     __syncthreads();
-    const int nd = misc[0];
-    const int ndb = (sparse && two && nd > 0) ? 1 : 0;
-    const int nblk = nbb + ncb + ndb;
+    // slots replaced at the second chunk: ballot over 64-slot groups, one wave, from LDS
+    if (sparse && w == 0) {
+        int base = 0;
+        const unsigned long long lt = l ? (~0ull >> (64 - l)) : 0ull;
+        for (int j0 = 0; j0 < lam; j0 += 64) {
+            const int j = j0 + l;
+            const int a0 = j < lam ? cPos[j] : -1, a1 = j < lam ? cPos1[j] : -1;
+            const bool rep = j < lam && a1 >= 0 && a1 != a0;
+            const unsigned long long m = __ballot(rep);
+            const int k = base + __popcll(m & lt);
+            if (rep && k < KB) { dPos[k] = a1; dSrc[k] = cSrc1[j]; }
+            base += __popcll(m);
+        }
+        if (l == 0) misc[0] = base < KB ? base : KB;
+    }
+    const int nblk0 = nbb + ncb;                    // blocks known before the replaced-slot pass
+    int nd = 0;                                     // replaced slots (known after the next barrier)
 
     // key kk of block kb -> position, rows, and the query ranges of both groups
     auto key_of = [&](int kb, int j, int& pos, const T*& rk, const T*& rv, unsigned& tl0, unsigned& sp0,
@@ -400,24 +295,11 @@ __global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs
         none = (unsigned)lo_mn > tb || (unsigned)hi_mx < ta;
         full = !none && (unsigned)lo_mx <= ta && (unsigned)hi_mn >= tb;
     };
-    if (nblk > 0) {
-        prefetch(0);
-        stage();
-    }
+    if (nblk0 > 0) prefetch(0);                    // in flight through the linear part
 
-    // ---- queries, and the linear part seeding the softmax state ----
-    // The query fragments are loaded for the features, dropped through the linear part (which needs
-    // every register it can get) and loaded again from L2 for the key loop.
-    Frag8<T> qf[2][DK / 32];
-    auto load_q = [&]() {
-#pragma unroll
-        for (int qq = 0; qq < 2; ++qq) {
-            const int64_t tq = tw0 + 16 * qq + c;
-#pragma unroll
-            for (int ss = 0; ss < DK / 32; ++ss)
-                qf[qq][ss] = tq < tend ? load_frag(qin + (tq - t0) * DK, ss, g) : frag_zero<T>();
-        }
-    };
+    // ---- the linear part seeding the softmax state ----
+    // The query fragments serve the features, are dropped through the linear part and are loaded
+    // again from L2 for the key loop.
     constexpr float kLog2e = 1.4426950408889634f;
     const float sl2 = kLog2e / sqrtf((float)DK);       // score -> base-2 logit
     f4 O[JT][2];
@@ -429,7 +311,7 @@ __global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs
 #pragma unroll
         for (int J = 0; J < JT; ++J) O[J][qq] = zero4();
     }
-    if ((A.read_mask & kReadState) && wave_active) {
+    if (lin) {
         const char* recw = grp ? rec1 : rec0;
         const T* snapH = reinterpret_cast<const T*>(recw + A.L.c_snap_h);
         const float* snapS = reinterpret_cast<const float*>(recw + A.L.c_snap_s);
@@ -441,23 +323,38 @@ __global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs
         const int64_t a = t0 + (int64_t)chw * C;       // the wave's chunk start
         Frag8<T> pf[2][D / 32];
         float lden[2];
-        load_q();
+        // H_c^T phi(Q)^T from the fragment-order snapshot (each fragment serves both query tiles), in
+        // batches of four fragments: the next batch is requested before the current one is used.  The
+        // first batch is requested before the features are formed.
+        constexpr int HB = 4, NHB = JT * (D / 32) / HB;
+        Frag8<T> hb[2][HB];
+        auto load_hb = [&](int b, Frag8<T> (&dst)[HB]) {
+            const int ss = b / (JT / HB), J0 = (b % (JT / HB)) * HB;
+#pragma unroll
+            for (int jj = 0; jj < HB; ++jj)
+                dst[jj] = *reinterpret_cast<const Frag8<T>*>(snapH + ((int64_t)((J0 + jj) * (D / 32) + ss) * 64 + l) * 8);
+        };
+        load_hb(0, hb[0]);
         phi_pair<DK, PHI>(wt, WT_LD, qf, snapS, pf, lden);
-        // H_c^T phi(Q)^T from the fragment-order snapshot (each fragment serves both query tiles)
 #pragma unroll
-        for (int ss = 0; ss < D / 32; ++ss)
+        for (int b = 0; b < NHB; ++b) {
+            if (b + 1 < NHB) load_hb(b + 1, hb[(b + 1) & 1]);
+            const int ss = b / (JT / HB), J0 = (b % (JT / HB)) * HB;
 #pragma unroll
-            for (int J = 0; J < JT; ++J) {
-                const Frag8<T> hf = *reinterpret_cast<const Frag8<T>*>(snapH + ((int64_t)(J * (D / 32) + ss) * 64 + l) * 8);
-                mma32(O[J][0], hf, pf[0][ss]);
-                mma32(O[J][1], hf, pf[1][ss]);
-                if (J % 4 == 3) __builtin_amdgcn_sched_barrier(0);   // bound the snapshot fragments in flight
+            for (int jj = 0; jj < HB; ++jj) {
+                mma32(O[J0 + jj][0], hb[b & 1][jj], pf[0][ss]);
+                mma32(O[J0 + jj][1], hb[b & 1][jj], pf[1][ss]);
             }
+            __builtin_amdgcn_sched_barrier(0);        // bound the snapshot fragments in flight
+        }
         // tokens folded by this chunk become linear at tau = max(exit time, chunk start)
         float lf[2] = {0.f, 0.f};
         for (int fb = 0; fb * 32 < nf; ++fb) {
             // the kernel values phi(q_t).phi(k_i) of 32 folded tokens (two halves of 16) and both query
-            // tiles, masked by tau_i <= t, then their values
+            // tiles, masked by tau_i <= t, then their values (requested first)
+            Frag8<T> vfs[JT];
+#pragma unroll
+            for (int J = 0; J < JT; ++J) vfs[J] = load_frag(foldVT + (int64_t)(16 * J + c) * cpv, fb, g);
             f4 sp[2][2];
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
@@ -495,7 +392,7 @@ __global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs
             }
 #pragma unroll
             for (int J = 0; J < JT; ++J) {
-                const Frag8<T> vf = load_frag(foldVT + (int64_t)(16 * J + c) * cpv, fb, g);
+                const Frag8<T> vf = vfs[J];
                 mma32(O[J][0], vf, bw[0]);
                 mma32(O[J][1], vf, bw[1]);
                 if (J % 4 == 3) __builtin_amdgcn_sched_barrier(0);
@@ -522,9 +419,13 @@ __global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs
     // ---- exact part: the key blocks ----
     asm volatile("" ::: "memory");                  // a second load, not the first one kept live
     load_q();
+    if (nblk0 > 0) stage();
     const int* tloG = sTlo + grp * KB;
     const int* spanG = sSpan + grp * KB;
-    __syncthreads();                                // block 0 staged
+    __syncthreads();                                // block 0 staged, the replaced slots listed
+    nd = misc[0];
+    const int ndb = (sparse && two && nd > 0) ? 1 : 0;
+    const int nblk = nbb + ncb + ndb;
     for (int kb = 0; kb < nblk; ++kb) {
         bool none, full;
         classify(none, full);
