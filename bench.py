@@ -34,10 +34,11 @@ MULTI_TOKEN_C = 16          # tokens per call in the multi-token decode measurem
 _SHARED_SOURCES = ("lola_common.hpp", "lola_internal.hpp")
 KERNEL_SOURCES = {
     "phi": ("lola_phi.hip",),
-    "chain": ("lola_chain.hip",),
-    "readout": ("lola_readout.hip",),
+    "chain": ("lola_chain_fast.hip", "lola_chain.hip"),
+    "readout": ("lola_readout.hip", "lola_readout_fast.hip", "lola_readout_common.hpp"),
     "commit": ("lola_readout.hip",),
     "decode": ("lola_decode_fast.hip", "lola_decode.hip"),
+    "decode_group": ("lola_decode_group.hip",),
     "collide": ("lola_collide.hip",),
     "qscore": ("lola_qscore.hip",),
     "hola": ("lola_hola.hip",),
