@@ -17,7 +17,7 @@
 //   1. H^T to LDS, the chunk-start snapshot to the chunk record;                               barrier
 //   2. every wave scores its tiles (at most two cache tiles and one leaving-token tile), reading
 //      each A fragment of H^T once for all of them;                                            barrier
-//   3. wave 0 selects the nF smallest keys (64-bin histograms of SRE, then an exact rank of the
+//   3. wave 0 selects the nF smallest keys (a 256-bin histogram of SRE, then an exact rank of the
 //      boundary bin), ranks folds, freed slots and entrants with ballots and writes the fold list;
 //                                                                                              barrier
 //   4. slot owners stage their folded members' rows and take entrants from the leaving buffer;
