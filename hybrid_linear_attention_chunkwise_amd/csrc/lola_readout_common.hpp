@@ -1,6 +1,6 @@
 // Building blocks of the bf16 read-out kernel (lola_readout_fast.hip):
-// whole-wave min / max, the query features of two 16-query tiles, the swizzles of staged key and value
-// rows, and the transposing LDS read.
+// the query features of two 16-query tiles, the swizzles of staged key and value rows, and the
+// transposing LDS read.
 #pragma once
 
 #include "lola_common.hpp"
@@ -10,32 +10,9 @@ namespace rd {
 
 constexpr unsigned kNoKey = 0x7FFFFFFFu;   // query-range start of a key that no query reads
 
-// Whole-wave min / max of unsigned values below 2^31 (DPP inside rows of 16, lane swaps across rows).
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int x) {
-    return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, true);
-}
-__device__ __forceinline__ void wave_minmax_i(int& mn, int& mx) {
-    mn = min(mn, dpp_i<0xB1>(mn)); mx = max(mx, dpp_i<0xB1>(mx));     // quad_perm [1,0,3,2]
-    mn = min(mn, dpp_i<0x4E>(mn)); mx = max(mx, dpp_i<0x4E>(mx));     // quad_perm [2,3,0,1]
-    mn = min(mn, dpp_i<0x124>(mn)); mx = max(mx, dpp_i<0x124>(mx));   // row_ror:4
-    mn = min(mn, dpp_i<0x128>(mn)); mx = max(mx, dpp_i<0x128>(mx));   // row_ror:8
-    {
-        const auto a = __builtin_amdgcn_permlane16_swap((unsigned)mn, (unsigned)mn, false, false);
-        mn = min((int)a[0], (int)a[1]);
-        const auto b = __builtin_amdgcn_permlane16_swap((unsigned)mx, (unsigned)mx, false, false);
-        mx = max((int)b[0], (int)b[1]);
-    }
-    {
-        const auto a = __builtin_amdgcn_permlane32_swap((unsigned)mn, (unsigned)mn, false, false);
-        mn = min((int)a[0], (int)a[1]);
-        const auto b = __builtin_amdgcn_permlane32_swap((unsigned)mx, (unsigned)mx, false, false);
-        mx = max((int)b[0], (int)b[1]);
-    }
-}
-
 // phi of two 16-query tiles (section 2.2), each W^T fragment from LDS serving both: the features as
 // MFMA B operands pf[qq][ss] (reduction order over D) and phi(q).s in lden[qq] (this lane's part).
+// The query fragments qf and the rows of W^T (16-byte aligned) are in the contiguous order over d_k.
 template <int DK, int PHI>
 __device__ __forceinline__ void phi_pair(const bf16* wt, int wt_ld, const Frag8<bf16> (&qf)[2][DK / 32],
                                          const float* s, Frag8<bf16> (&pf)[2][kFeat / 32], float (&lden)[2]) {
@@ -48,7 +25,7 @@ __device__ __forceinline__ void phi_pair(const bf16* wt, int wt_ld, const Frag8<
         pre[ft][1] = zero4();
 #pragma unroll
         for (int ss = 0; ss < DK / 32; ++ss) {
-            const Frag8<bf16> a = load_frag(wt + (16 * ft + c) * wt_ld, ss, g);
+            const Frag8<bf16> a = load_frag_contig(wt + (16 * ft + c) * wt_ld, ss, g);
             mma32(pre[ft][0], a, qf[0][ss]);
             mma32(pre[ft][1], a, qf[1][ss]);
         }

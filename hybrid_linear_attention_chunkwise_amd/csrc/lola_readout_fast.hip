@@ -43,7 +43,7 @@ template <int DK, int PHI>
 struct RfCfg {
     static constexpr int D = kFeat, DV = DK, JT = DV / 16;
     static constexpr int DW = (PHI == kPhiSoftmaxPM) ? D / 2 : D;
-    static constexpr int WT_LD = DK + 4;
+    static constexpr int WT_LD = DK + 8;           // 16-byte aligned rows for whole-fragment reads
     static constexpr int CPK = DK / 8;             // 16-byte chunks per key (and value) row
     static constexpr int RPB = 256 / (2 * DK);     // rows per 256 bytes (the 64 LDS banks): 1 or 2
     static constexpr int SEG = DV / 16;            // 32-byte segments per value row
@@ -154,10 +154,12 @@ __global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs
     auto load_q = [&]() {
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq) {
+            // a query past the call's end reads the call's first row instead: its lanes' results are
+            // never stored, and every row is finite
             const int64_t tq = tw0 + 16 * qq + c;
+            const T* qrow = qin + (tq < tend ? tq - t0 : 0) * DK;
 #pragma unroll
-            for (int ss = 0; ss < DK / 32; ++ss)
-                qf[qq][ss] = tq < tend ? load_frag(qin + (tq - t0) * DK, ss, g) : frag_zero<T>();
+            for (int ss = 0; ss < DK / 32; ++ss) qf[qq][ss] = load_frag_contig(qrow, ss, g);
         }
     };
     const bool lin = (A.read_mask & kReadState) && wave_active;
@@ -251,35 +253,31 @@ __global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs
 
     // A block in flight: thread t stages key t / 4 of the block, chunks (t mod 4) * PPT .. + PPT - 1 of
     // its key row and of its value row, and (t mod 4 == 0) the key's query ranges.
-    struct Buf {
-        uint4 k[PPT];
-        uint4 v[PPT];
-        unsigned tl0, sp0, tl1, sp1;
-    };
-    Buf buf;
+    uint4 bufk[PPT], bufv[PPT];
+    unsigned btl0, bsp0, btl1, bsp1;
     const int sj = tid >> 2, sq0 = (tid & 3) * PPT;
     auto prefetch = [&](int kb) {
         int pos;
         const T* rk;
         const T* rv;
-        key_of(kb, sj, pos, rk, rv, buf.tl0, buf.sp0, buf.tl1, buf.sp1);
+        key_of(kb, sj, pos, rk, rv, btl0, bsp0, btl1, bsp1);
 #pragma unroll
         for (int x = 0; x < PPT; ++x) {
-            buf.k[x] = pos >= 0 ? *reinterpret_cast<const uint4*>(rk + (sq0 + x) * 8) : make_uint4(0, 0, 0, 0);
-            buf.v[x] = pos >= 0 ? *reinterpret_cast<const uint4*>(rv + (sq0 + x) * 8) : make_uint4(0, 0, 0, 0);
+            bufk[x] = pos >= 0 ? *reinterpret_cast<const uint4*>(rk + (sq0 + x) * 8) : make_uint4(0, 0, 0, 0);
+            bufv[x] = pos >= 0 ? *reinterpret_cast<const uint4*>(rv + (sq0 + x) * 8) : make_uint4(0, 0, 0, 0);
         }
     };
     auto stage = [&]() {
 #pragma unroll
         for (int x = 0; x < PPT; ++x) {
-            *reinterpret_cast<uint4*>(sK + sj * DK + kswz<DK>(sj, sq0 + x) * 8) = buf.k[x];
-            *reinterpret_cast<uint4*>(sV + sj * DV + vswz<DK>(sj, sq0 + x) * 8) = buf.v[x];
+            *reinterpret_cast<uint4*>(sK + sj * DK + kswz<DK>(sj, sq0 + x) * 8) = bufk[x];
+            *reinterpret_cast<uint4*>(sV + sj * DV + vswz<DK>(sj, sq0 + x) * 8) = bufv[x];
         }
         if ((tid & 3) == 0) {
-            sTlo[sj] = (int)buf.tl0;
-            sSpan[sj] = (int)buf.sp0;
-            sTlo[KB + sj] = (int)buf.tl1;
-            sSpan[KB + sj] = (int)buf.sp1;
+            sTlo[sj] = (int)btl0;
+            sSpan[sj] = (int)bsp0;
+            sTlo[KB + sj] = (int)btl1;
+            sSpan[KB + sj] = (int)bsp1;
         }
     };
     // this wave's view of the staged block, from the keys' query ranges (lane l reads key l): none of
@@ -289,11 +287,10 @@ __global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs
     auto classify = [&](bool& none, bool& full) {
         const unsigned tl = (unsigned)sTlo[grp * KB + l], sp = (unsigned)sSpan[grp * KB + l];
         const unsigned hi = tl == kNoKey ? 0u : tl + sp;
-        int lo_mn = (int)tl, lo_mx = (int)tl, hi_mn = (int)hi, hi_mx = (int)hi;
-        wave_minmax_i(lo_mn, lo_mx);
-        wave_minmax_i(hi_mn, hi_mx);
-        none = (unsigned)lo_mn > tb || (unsigned)hi_mx < ta;
-        full = !none && (unsigned)lo_mx <= ta && (unsigned)hi_mn >= tb;
+        const bool read_by_none = tl > tb || hi < ta;      // no query of the wave reads key l
+        const bool read_by_all = tl <= ta && hi >= tb;     // every query of the wave reads key l
+        none = __ballot(!read_by_none) == 0ull;
+        full = !none && __ballot(!read_by_all) == 0ull;
     };
     if (nblk0 > 0) prefetch(0);                    // in flight through the linear part
 
@@ -431,21 +428,27 @@ __global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs
         classify(none, full);
         if (kb + 1 < nblk) prefetch(kb + 1);
         if (wave_active && !none) {
+            // K Q^T by reduction step: the eight accumulators of a step are independent, so the matrix
+            // cores do not wait on one accumulator's previous product
             f4 S[KB / 16][2];
 #pragma unroll
             for (int kt = 0; kt < KB / 16; ++kt) {
                 S[kt][0] = zero4();
                 S[kt][1] = zero4();
+            }
 #pragma unroll
-                for (int ss = 0; ss < DK / 32; ++ss) {
+            for (int ss = 0; ss < DK / 32; ++ss) {
+                Frag8<T> kf[KB / 16];
+#pragma unroll
+                for (int kt = 0; kt < KB / 16; ++kt) {
+                    // the contiguous reduction order (the query fragments use it too): one 16-byte chunk
                     const int row = 16 * kt + c;
-                    const T* kr = sK + row * DK + 4 * (g & 1);
-                    Frag8<T> kf;
-                    kf.v = __builtin_shufflevector(*reinterpret_cast<const bf16x4*>(kr + kswz<DK>(row, 4 * ss + (g >> 1)) * 8),
-                                                   *reinterpret_cast<const bf16x4*>(kr + kswz<DK>(row, 4 * ss + 2 + (g >> 1)) * 8),
-                                                   0, 1, 2, 3, 4, 5, 6, 7);
-                    mma32(S[kt][0], kf, qf[0][ss]);
-                    mma32(S[kt][1], kf, qf[1][ss]);
+                    kf[kt].v = *reinterpret_cast<const bf16x8*>(sK + row * DK + kswz<DK>(row, 4 * ss + g) * 8);
+                }
+#pragma unroll
+                for (int kt = 0; kt < KB / 16; ++kt) {
+                    mma32(S[kt][0], kf[kt], qf[0][ss]);
+                    mma32(S[kt][1], kf[kt], qf[1][ss]);
                 }
                 __builtin_amdgcn_sched_barrier(0);            // bound the key fragments in flight
             }
