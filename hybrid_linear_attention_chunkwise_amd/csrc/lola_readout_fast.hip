@@ -50,32 +50,35 @@ struct RfCfg {
     static constexpr int PPT = kRfKB * CPK / kRfThreads;   // chunks per thread and block (one row)
 };
 
+// LDS: two key-block buffers (keys row-major, values transposed; W^T shares the second one, which the
+// key loop first fills after the features are formed), the blocks' query ranges, the replaced slots,
+// the fold lists, then the five slot tables of lambda entries each (rounded up to 4), whose size is
+// set at launch.
 struct RfLds {
-    size_t k, vt, wt, tlo, span, cpos, csrc, g1ok, cpos1, csrc1, dpos, dsrc, fpos, fsrc, misc, total;
+    size_t k, vt, wt, tlo, span, dpos, dsrc, fpos, fsrc, misc, tables;
 };
+constexpr size_t kRfBufBytes = 2 * 2 * (size_t)kRfKB * 128;   // one buffer: keys + values at d = 128
 __host__ __device__ constexpr size_t rf_al(size_t x) { return (x + 15) & ~size_t(15); }
 
 template <int DK, int PHI>
 __host__ __device__ constexpr RfLds rf_lds() {
     using Cfg = RfCfg<DK, PHI>;
+    static_assert(2 * kRfKB * (DK + Cfg::DV) <= (int)kRfBufBytes, "one key block per buffer");
     RfLds o{};
     size_t p = 0;
-    o.k = p;     p = rf_al(p + 2 * kRfKB * DK);
-    o.vt = p;    p = rf_al(p + 2 * kRfKB * Cfg::DV);
-    o.wt = p;    p = rf_al(p + 2 * Cfg::DW * Cfg::WT_LD);
-    o.tlo = p;   p = rf_al(p + 4 * 2 * kRfKB);
-    o.span = p;  p = rf_al(p + 4 * 2 * kRfKB);
-    o.cpos = p;  p = rf_al(p + 4 * kMaxLambda);
-    o.csrc = p;  p = rf_al(p + 4 * kMaxLambda);
-    o.g1ok = p;  p = rf_al(p + 4 * kMaxLambda);
-    o.cpos1 = p; p = rf_al(p + 4 * kMaxLambda);
-    o.csrc1 = p; p = rf_al(p + 4 * kMaxLambda);
+    o.k = p;     p = rf_al(p + 2 * kRfKB * DK);          // buffer b: keys at k + b * kRfBufBytes
+    o.vt = p;    p = rf_al(p + 2 * kRfKB * Cfg::DV);      //           values at vt + b * kRfBufBytes
+    o.wt = kRfBufBytes;                                   // from buffer 1 on (elu at d = 128: past it)
+    p = 2 * kRfBufBytes;
+    p = p > kRfBufBytes + rf_al(2 * Cfg::DW * Cfg::WT_LD) ? p : kRfBufBytes + rf_al(2 * Cfg::DW * Cfg::WT_LD);
+    o.tlo = p;   p = rf_al(p + 4 * 2 * 2 * kRfKB);        // [buffer][group][key]
+    o.span = p;  p = rf_al(p + 4 * 2 * 2 * kRfKB);
     o.dpos = p;  p = rf_al(p + 4 * kRfKB);
     o.dsrc = p;  p = rf_al(p + 4 * kRfKB);
     o.fpos = p;  p = rf_al(p + 4 * 2 * kMaxChunk);
     o.fsrc = p;  p = rf_al(p + 4 * 2 * kMaxChunk);
     o.misc = p;  p = rf_al(p + 4 * 16);
-    o.total = p;
+    o.tables = p;
     return o;
 }
 
@@ -88,16 +91,18 @@ __global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs
                   KB = kRfKB;
     extern __shared__ __align__(16) char smem[];
     constexpr RfLds lo = rf_lds<DK, PHI>();
-    T* sK = reinterpret_cast<T*>(smem + lo.k);
-    T* sV = reinterpret_cast<T*>(smem + lo.vt);             // [KB][DV], swizzled
-    T* wt = reinterpret_cast<T*>(smem + lo.wt);
-    int* sTlo = reinterpret_cast<int*>(smem + lo.tlo);      // [2][KB]
-    int* sSpan = reinterpret_cast<int*>(smem + lo.span);    // [2][KB]
-    int* cPos = reinterpret_cast<int*>(smem + lo.cpos);     // cache list of the tile's first chunk
-    int* cSrc = reinterpret_cast<int*>(smem + lo.csrc);
-    int* g1ok = reinterpret_cast<int*>(smem + lo.g1ok);     // slot unchanged at the second chunk
-    int* cPos1 = reinterpret_cast<int*>(smem + lo.cpos1);   // the second chunk's slot table
-    int* cSrc1 = reinterpret_cast<int*>(smem + lo.csrc1);
+    constexpr int BUFE = (int)(kRfBufBytes / sizeof(T));   // buffer stride in elements
+    T* sK = reinterpret_cast<T*>(smem + lo.k);              // [2 buffers] [KB][DK], swizzled
+    T* sV = reinterpret_cast<T*>(smem + lo.vt);             // [2 buffers] [KB][DV], swizzled
+    T* wt = reinterpret_cast<T*>(smem + lo.wt);             // shares buffer 1 until the key loop
+    int* sTlo = reinterpret_cast<int*>(smem + lo.tlo);      // [2 buffers][2 groups][KB]
+    int* sSpan = reinterpret_cast<int*>(smem + lo.span);    // [2 buffers][2 groups][KB]
+    const int lam4 = (A.lam + 3) & ~3;
+    int* cPos = reinterpret_cast<int*>(smem + lo.tables);   // cache list of the tile's first chunk
+    int* cSrc = cPos + lam4;
+    int* g1ok = cSrc + lam4;                                // slot unchanged at the second chunk
+    int* cPos1 = g1ok + lam4;                               // the second chunk's slot table
+    int* cSrc1 = cPos1 + lam4;
     int* dPos = reinterpret_cast<int*>(smem + lo.dpos);     // slots replaced at the second chunk
     int* dSrc = reinterpret_cast<int*>(smem + lo.dsrc);
     int* fPos = reinterpret_cast<int*>(smem + lo.fpos);     // [2][kMaxChunk] fold lists per group
@@ -267,25 +272,29 @@ __global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs
             bufv[x] = pos >= 0 ? *reinterpret_cast<const uint4*>(rv + (sq0 + x) * 8) : make_uint4(0, 0, 0, 0);
         }
     };
-    auto stage = [&]() {
+    auto stage = [&](int b) {
+        T* bk = sK + b * BUFE;
+        T* bv = sV + b * BUFE;
 #pragma unroll
         for (int x = 0; x < PPT; ++x) {
-            *reinterpret_cast<uint4*>(sK + sj * DK + kswz<DK>(sj, sq0 + x) * 8) = bufk[x];
-            *reinterpret_cast<uint4*>(sV + sj * DV + vswz<DK>(sj, sq0 + x) * 8) = bufv[x];
+            *reinterpret_cast<uint4*>(bk + sj * DK + kswz<DK>(sj, sq0 + x) * 8) = bufk[x];
+            *reinterpret_cast<uint4*>(bv + sj * DV + vswz<DK>(sj, sq0 + x) * 8) = bufv[x];
         }
         if ((tid & 3) == 0) {
-            sTlo[sj] = (int)btl0;
-            sSpan[sj] = (int)bsp0;
-            sTlo[KB + sj] = (int)btl1;
-            sSpan[KB + sj] = (int)bsp1;
+            int* tl = sTlo + b * 2 * KB;
+            int* sp = sSpan + b * 2 * KB;
+            tl[sj] = (int)btl0;
+            sp[sj] = (int)bsp0;
+            tl[KB + sj] = (int)btl1;
+            sp[KB + sj] = (int)bsp1;
         }
     };
     // this wave's view of the staged block, from the keys' query ranges (lane l reads key l): none of
     // its queries reads a key, or every query reads every key, or a mask is needed
     const unsigned ta = (unsigned)tw0;
     const unsigned tb = (unsigned)(tw0 + 31 < tend - 1 ? tw0 + 31 : tend - 1);
-    auto classify = [&](bool& none, bool& full) {
-        const unsigned tl = (unsigned)sTlo[grp * KB + l], sp = (unsigned)sSpan[grp * KB + l];
+    auto classify = [&](int b, bool& none, bool& full) {
+        const unsigned tl = (unsigned)sTlo[(2 * b + grp) * KB + l], sp = (unsigned)sSpan[(2 * b + grp) * KB + l];
         const unsigned hi = tl == kNoKey ? 0u : tl + sp;
         const bool read_by_none = tl > tb || hi < ta;      // no query of the wave reads key l
         const bool read_by_all = tl <= ta && hi >= tb;     // every query of the wave reads key l
@@ -416,16 +425,21 @@ __global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs
     // ---- exact part: the key blocks ----
     asm volatile("" ::: "memory");                  // a second load, not the first one kept live
     load_q();
-    if (nblk0 > 0) stage();
-    const int* tloG = sTlo + grp * KB;
-    const int* spanG = sSpan + grp * KB;
+    if (nblk0 > 0) stage(0);
     __syncthreads();                                // block 0 staged, the replaced slots listed
     nd = misc[0];
     const int ndb = (sparse && two && nd > 0) ? 1 : 0;
     const int nblk = nbb + ncb + ndb;
+    // Two buffers: block kb + 1 is staged into the other buffer while block kb is read, so one
+    // barrier per block orders both (the buffer staged at kb was last read at kb - 1).
     for (int kb = 0; kb < nblk; ++kb) {
+        const int cb = kb & 1;
+        const T* bK = sK + cb * BUFE;
+        const T* bV = sV + cb * BUFE;
+        const int* tloG = sTlo + (2 * cb + grp) * KB;
+        const int* spanG = sSpan + (2 * cb + grp) * KB;
         bool none, full;
-        classify(none, full);
+        classify(cb, none, full);
         if (kb + 1 < nblk) prefetch(kb + 1);
         if (wave_active && !none) {
             // K Q^T by reduction step: the eight accumulators of a step are independent, so the matrix
@@ -443,7 +457,7 @@ __global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs
                 for (int kt = 0; kt < KB / 16; ++kt) {
                     // the contiguous reduction order (the query fragments use it too): one 16-byte chunk
                     const int row = 16 * kt + c;
-                    kf[kt].v = *reinterpret_cast<const bf16x8*>(sK + row * DK + kswz<DK>(row, 4 * ss + g) * 8);
+                    kf[kt].v = *reinterpret_cast<const bf16x8*>(bK + row * DK + kswz<DK>(row, 4 * ss + g) * 8);
                 }
 #pragma unroll
                 for (int kt = 0; kt < KB / 16; ++kt) {
@@ -510,8 +524,8 @@ __global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs
                     const int ka = 32 * k2 + 4 * g + (c >> 2), kb2 = ka + 16;
                     const int q = 2 * J + ((c >> 1) & 1), off = 4 * (c & 1);
                     Frag8<T> vf;
-                    vf.v = __builtin_shufflevector(lds_read_tr(sV + ka * DV + vswz<DK>(ka, q) * 8 + off),
-                                                   lds_read_tr(sV + kb2 * DV + vswz<DK>(kb2, q) * 8 + off),
+                    vf.v = __builtin_shufflevector(lds_read_tr(bV + ka * DV + vswz<DK>(ka, q) * 8 + off),
+                                                   lds_read_tr(bV + kb2 * DV + vswz<DK>(kb2, q) * 8 + off),
                                                    0, 1, 2, 3, 4, 5, 6, 7);
                     mma32(O[J][0], vf, p0);
                     mma32(O[J][1], vf, p1);
@@ -519,11 +533,8 @@ __global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs
                 }
             }
         }
+        if (kb + 1 < nblk) stage(cb ^ 1);
         __syncthreads();
-        if (kb + 1 < nblk) {
-            stage();
-            __syncthreads();
-        }
     }
 
     // ---- output: accumulator / sum ----
@@ -556,7 +567,7 @@ bool readout_fast_fits(const PrefillArgs& a, int dtype) {
 
 template <int DK, int PHI>
 hipError_t launch_readout_fast_t(const PrefillArgs& a, int c0, int c1, hipStream_t stream) {
-    constexpr size_t lds = rf_lds<DK, PHI>().total;
+    const size_t lds = rf_lds<DK, PHI>().tables + (size_t)5 * 4 * ((a.lam + 3) & ~3);
     const int cpt = kRfQ / a.C;
     const int u0 = c0 / cpt;
     const int u1 = (c1 + cpt - 1) / cpt;
