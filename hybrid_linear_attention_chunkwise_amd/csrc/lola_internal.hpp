@@ -204,6 +204,7 @@ hipError_t launch_collide(const CollideArgs& a, int dtype, int d, hipStream_t st
 // Read-out for bf16 storage with C = 64 or 128 (128 queries per workgroup): whether a call takes it,
 // and its launcher over the chunk range [c0, c1) (c0 a multiple of 128 / C).
 bool readout_fast_fits(const PrefillArgs& a, int dtype);
+int readout_fast_groups_per_cu();             // workgroups of it one compute unit holds
 hipError_t launch_readout_fast(const PrefillArgs& a, int d, int phi_kind, int c0, int c1, hipStream_t stream);
 
 // LDS bytes the chain kernel uses (sized for kMaxLambda / kMaxChunk) at element size esz.

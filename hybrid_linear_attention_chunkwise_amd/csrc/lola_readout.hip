@@ -16,6 +16,7 @@
 #include "lola_common.hpp"
 #include "lola_internal.hpp"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace lola {
@@ -541,6 +542,30 @@ static int split_chunks(int nchunks, int per_chunk, int ncu, int* bounds, int ma
     return k;
 }
 
+// Ranges when the read-outs beside the chain are cut into launches that fit the free compute units:
+// those read-outs run behind the chain, so the first range is short (they start early), the ranges then
+// double, and the last range, whose read-out runs on the whole device after the chain, takes
+// last_pct percent of the units.
+static int split_capped(int units, int last_pct, int* bounds, int max_seg) {
+    constexpr int first = 2;
+    int last = (units * last_pct + 50) / 100;
+    last = last < 1 ? 1 : last;
+    if (units < 2 || max_seg < 2) { bounds[0] = 0; bounds[1] = units; return 1; }
+    if (last > units - 1) last = units - 1;
+    const int rest = units - last;
+    int k = 0, sum = 0, sz = first;
+    bounds[0] = 0;
+    while (sum < rest && k < max_seg - 2) {
+        const int take = sz < rest - sum ? sz : rest - sum;
+        sum += take;
+        bounds[++k] = sum;
+        sz *= 2;
+    }
+    if (sum < rest) bounds[++k] = rest;
+    bounds[++k] = units;
+    return k;
+}
+
 int device_cus() {
     int dev = 0, v = 0;
     if (hipGetDevice(&dev) == hipSuccess &&
@@ -580,7 +605,15 @@ hipError_t launch_prefill_t(const PrefillArgs& a0, hipStream_t stream, hipEvent_
     const bool fastro = std::is_same<T, bf16>::value && readout_fast_fits(a, 1);
     const int cpu = fastro ? (a.C == 64 ? 2 : 1) : 1;
     const int nunits = (a.nchunks + cpu - 1) / cpu;
-    const int nseg = split_chunks(nunits, fastro ? a.BH : a.BH * a.nqt, device_cus(), bounds, kMaxSegments);
+    const int ncu = device_cus();
+    // When the chain holds a quarter of the compute units or more, its read-outs take about as long as
+    // the chain itself, and a read-out launch whose workgroups wait for free units holds up the dispatch
+    // of the chain's next range behind it.  The read-outs beside the chain are then cut into launches of
+    // at most cap units, whose workgroups fit the units the chain leaves free at once.
+    const int cap = (fastro && 4 * a.BH >= ncu && a.BH < ncu)
+                        ? std::max(1, readout_fast_groups_per_cu() * (ncu - a.BH) / a.BH) : 0;
+    const int nseg = cap > 0 ? split_capped(nunits, 45, bounds, kMaxSegments)
+                             : split_chunks(nunits, fastro ? a.BH : a.BH * a.nqt, ncu, bounds, kMaxSegments);
     for (int i = 0; i <= nseg; ++i) bounds[i] = bounds[i] * cpu < a.nchunks ? bounds[i] * cpu : a.nchunks;
     if ((e = launch_phi_t<T, DK, PHI>(a, stream)) != hipSuccess) return e;
     if (a.score_rule != kScoreSre && (e = launch_qscore_t<T, DK>(a, stream)) != hipSuccess) return e;
@@ -591,7 +624,11 @@ hipError_t launch_prefill_t(const PrefillArgs& a0, hipStream_t stream, hipEvent_
         if ((e = hipEventRecord(side->ev[i], stream)) != hipSuccess) return e;
         if (i == nseg - 1) break;
         if ((e = hipStreamWaitEvent(side->stream, side->ev[i], 0)) != hipSuccess) return e;
-        if ((e = launch_readout<T, DK, PHI>(a, bounds[i], bounds[i + 1], side->stream, false)) != hipSuccess) return e;
+        const int step = cap > 0 ? cap * cpu : bounds[i + 1] - bounds[i];
+        for (int c0 = bounds[i]; c0 < bounds[i + 1]; c0 += step) {
+            const int c1 = c0 + step < bounds[i + 1] ? c0 + step : bounds[i + 1];
+            if ((e = launch_readout<T, DK, PHI>(a, c0, c1, side->stream, false)) != hipSuccess) return e;
+        }
     }
     if ((e = launch_readout<T, DK, PHI>(a, bounds[nseg - 1], bounds[nseg], stream, nseg > 1)) != hipSuccess) return e;
     // The commit overwrites the state's cache and window rows.  A call that starts from an empty

@@ -561,6 +561,8 @@ __global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs
 
 }  // namespace
 
+int readout_fast_groups_per_cu() { return 2; }
+
 bool readout_fast_fits(const PrefillArgs& a, int dtype) {
     return dtype == 1 && (a.C == 64 || a.C == 128);
 }

@@ -139,12 +139,13 @@ def test_fast_readout_read_masks(mask):
     assert worst <= TL.BF16_TOL
 
 
-@pytest.mark.parametrize("C", [64, 128])
-def test_fast_readout_overlapped_equals_sequential(C):
+@pytest.mark.parametrize("C,h", [(64, 2), (128, 2), (64, 48)])
+def test_fast_readout_overlapped_equals_sequential(C, h):
     """Chunk ranges of the overlapped schedule are cut between 128-query tiles: the same bits as the
-    sequential schedule."""
+    sequential schedule.  With 96 (sequence, head) pairs the chain holds over a quarter of the compute
+    units, so the read-outs beside it run in launches of a few 128-query units each."""
     import hybrid_linear_attention_chunkwise_amd as lola
-    wl = small_workload(130 + C, B=2, h=2, n=1500, C=C, eta=96 if C == 64 else 160, lam=80, d_k=128, d_v=128,
+    wl = small_workload(130 + C + h, B=2, h=h, n=1500, C=C, eta=96 if C == 64 else 160, lam=80, d_k=128, d_v=128,
                         dtype="bf16")
     W = make_weights(wl)
     q, k, v = make_qkv(wl)
