@@ -195,6 +195,25 @@ __global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs
         for (int i = tid; i < nf0; i += kRfThreads) { fPos[i] = fp0[i]; fSrc[i] = fs0[i]; }
         for (int i = tid; i < nf1; i += kRfThreads) { fPos[kMaxChunk + i] = fp1[i]; fSrc[kMaxChunk + i] = fs1[i]; }
         if (tid == 0) { misc[1] = nf0; misc[2] = nf1; }
+        // The folded tokens' features, gathered into key buffer 0 (free until block 0 is staged after the
+        // linear part): 128 rows, those of the second chunk from row 64 (C = 64), half a row a thread.
+        // Their loads overlap the ones above; the fold term then reads its operands from LDS.
+        if (A.read_mask & kReadState) {
+            static_assert(kRfThreads == 256, "two threads a fold row");
+            const int row = tid & 127, half = tid >> 7;
+            const int gi = cpt == 2 ? row >> 6 : 0, i = cpt == 2 ? row & 63 : row;
+            const int64_t goff = gi ? (int64_t)(rec1 - rec0) : 0;     // an offset, not a pointer select
+            const int* fsg = reinterpret_cast<const int*>(rec0 + goff + A.L.c_fold_src);
+            const int src = i < (gi ? nf1 : nf0) ? fsg[i] : 0;
+            const T* prow = phiStore + (int64_t)src * D + 64 * half;
+            typedef unsigned u32x4 __attribute__((ext_vector_type(4)));   // a vector value, kept in registers
+            u32x4 fr[8];
+#pragma unroll
+            for (int x = 0; x < 8; ++x) fr[x] = *reinterpret_cast<const u32x4*>(prow + 8 * x);
+#pragma unroll
+            for (int x = 0; x < 8; ++x)
+                *reinterpret_cast<u32x4*>(sK + row * D + kswz<D>(row, 8 * half + x) * 8) = fr[x];
+        }
     }
     // W^T in LDS for the query features
     if (A.read_mask & kReadState) stage_wt<T, DK, DW, kRfThreads>(wt, WT_LD, A.W);
@@ -365,10 +384,16 @@ __global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
                 const int i = 32 * fb + 16 * h2 + c;
-                const T* prow = phiStore + (int64_t)(i < nf ? fs[i] : 0) * D;
+                const int row = (cpt == 2 ? 64 * grp : 0) + (i < nf ? i : 0);   // the gathered rows in LDS
+                const T* fr = sK + row * D + 4 * (g & 1);
                 Frag8<T> af[D / 32];
 #pragma unroll
-                for (int ss = 0; ss < D / 32; ++ss) af[ss] = i < nf ? load_frag(prow, ss, g) : frag_zero<T>();
+                for (int ss = 0; ss < D / 32; ++ss) {
+                    af[ss].v = __builtin_shufflevector(*reinterpret_cast<const bf16x4*>(fr + kswz<D>(row, 4 * ss + (g >> 1)) * 8),
+                                                       *reinterpret_cast<const bf16x4*>(fr + kswz<D>(row, 4 * ss + 2 + (g >> 1)) * 8),
+                                                       0, 1, 2, 3, 4, 5, 6, 7);
+                    if (i >= nf) af[ss] = frag_zero<T>();
+                }
 #pragma unroll
                 for (int qq = 0; qq < 2; ++qq) {
                     sp[h2][qq] = zero4();
@@ -425,6 +450,7 @@ __global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs
     // ---- exact part: the key blocks ----
     asm volatile("" ::: "memory");                  // a second load, not the first one kept live
     load_q();
+    __syncthreads();                                // every wave is past the fold term: buffer 0 is free
     if (nblk0 > 0) stage(0);
     __syncthreads();                                // block 0 staged, the replaced slots listed
     nd = misc[0];
