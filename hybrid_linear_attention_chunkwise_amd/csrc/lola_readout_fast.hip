@@ -277,7 +277,8 @@ __global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs
 
     // A block in flight: thread t stages key t / 4 of the block, chunks (t mod 4) * PPT .. + PPT - 1 of
     // its key row and of its value row, and (t mod 4 == 0) the key's query ranges.
-    uint4 bufk[PPT], bufv[PPT];
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));   // vector values, kept in registers
+    u32x4 bufk[PPT], bufv[PPT];
     unsigned btl0, bsp0, btl1, bsp1;
     const int sj = tid >> 2, sq0 = (tid & 3) * PPT;
     auto prefetch = [&](int kb) {
@@ -285,10 +286,13 @@ __global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs
         const T* rk;
         const T* rv;
         key_of(kb, sj, pos, rk, rv, btl0, bsp0, btl1, bsp1);
+        // a key slot without a key (pos < 0) loads the call's first row: finite values that every
+        // query masks out (its query range is empty), so no branch around the loads
+        (void)pos;
 #pragma unroll
         for (int x = 0; x < PPT; ++x) {
-            bufk[x] = pos >= 0 ? *reinterpret_cast<const uint4*>(rk + (sq0 + x) * 8) : make_uint4(0, 0, 0, 0);
-            bufv[x] = pos >= 0 ? *reinterpret_cast<const uint4*>(rv + (sq0 + x) * 8) : make_uint4(0, 0, 0, 0);
+            bufk[x] = *reinterpret_cast<const u32x4*>(rk + (sq0 + x) * 8);
+            bufv[x] = *reinterpret_cast<const u32x4*>(rv + (sq0 + x) * 8);
         }
     };
     auto stage = [&](int b) {
@@ -296,8 +300,8 @@ __global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs
         T* bv = sV + b * BUFE;
 #pragma unroll
         for (int x = 0; x < PPT; ++x) {
-            *reinterpret_cast<uint4*>(bk + sj * DK + kswz<DK>(sj, sq0 + x) * 8) = bufk[x];
-            *reinterpret_cast<uint4*>(bv + sj * DV + vswz<DK>(sj, sq0 + x) * 8) = bufv[x];
+            *reinterpret_cast<u32x4*>(bk + sj * DK + kswz<DK>(sj, sq0 + x) * 8) = bufk[x];
+            *reinterpret_cast<u32x4*>(bv + sj * DV + vswz<DK>(sj, sq0 + x) * 8) = bufv[x];
         }
         if ((tid & 3) == 0) {
             int* tl = sTlo + b * 2 * KB;
