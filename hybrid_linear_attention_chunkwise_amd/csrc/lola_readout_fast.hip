@@ -55,7 +55,7 @@ struct RfCfg {
 // the fold lists, then the five slot tables of lambda entries each (rounded up to 4), whose size is
 // set at launch.
 struct RfLds {
-    size_t k, vt, wt, tlo, span, dpos, dsrc, fpos, fsrc, misc, tables;
+    size_t k, vt, wt, tlo, span, dpos, dsrc, fpos, fsrc, snaps, repm, misc, tables;
 };
 constexpr size_t kRfBufBytes = 2 * 2 * (size_t)kRfKB * 128;   // one buffer: keys + values at d = 128
 __host__ __device__ constexpr size_t rf_al(size_t x) { return (x + 15) & ~size_t(15); }
@@ -77,6 +77,8 @@ __host__ __device__ constexpr RfLds rf_lds() {
     o.dsrc = p;  p = rf_al(p + 4 * kRfKB);
     o.fpos = p;  p = rf_al(p + 4 * 2 * kMaxChunk);
     o.fsrc = p;  p = rf_al(p + 4 * 2 * kMaxChunk);
+    o.snaps = p; p = rf_al(p + 4 * 2 * kFeat);          // s of both chunks' snapshots
+    o.repm = p;  p = rf_al(p + 8 * (kMaxLambda / 64));  // replaced-slot masks, one word per 64 slots
     o.misc = p;  p = rf_al(p + 4 * 16);
     o.tables = p;
     return o;
@@ -108,6 +110,8 @@ __global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs
     int* fPos = reinterpret_cast<int*>(smem + lo.fpos);     // [2][kMaxChunk] fold lists per group
     int* fSrc = reinterpret_cast<int*>(smem + lo.fsrc);
     int* misc = reinterpret_cast<int*>(smem + lo.misc);
+    float* snapsL = reinterpret_cast<float*>(smem + lo.snaps);
+    unsigned long long* repm = reinterpret_cast<unsigned long long*>(smem + lo.repm);
 
     // XCD-aware order: workgroup id mod 8 picks a contiguous eighth of the tiles.
     const int G = gridDim.x;
@@ -199,6 +203,12 @@ __global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs
         // linear part): 128 rows, those of the second chunk from row 64 (C = 64), half a row a thread.
         // Their loads overlap the ones above; the fold term then reads its operands from LDS.
         if (A.read_mask & kReadState) {
+            for (int i = tid; i < 2 * D; i += kRfThreads) {
+                const int64_t soff = i >= D ? (int64_t)(rec1 - rec0) : 0;
+                snapsL[i] = reinterpret_cast<const float*>(rec0 + soff + A.L.c_snap_s)[i % D];
+            }
+        }
+        if (A.read_mask & kReadState) {
             static_assert(kRfThreads == 256, "two threads a fold row");
             const int row = tid & 127, half = tid >> 7;
             const int gi = cpt == 2 ? row >> 6 : 0, i = cpt == 2 ? row & 63 : row;
@@ -218,21 +228,19 @@ __global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs
     // W^T in LDS for the query features
     if (A.read_mask & kReadState) stage_wt<T, DK, DW, kRfThreads>(wt, WT_LD, A.W);
     __syncthreads();
-    // slots replaced at the second chunk: ballot over 64-slot groups, one wave, from LDS
-    if (sparse && w == 0) {
-        int base = 0;
-        const unsigned long long lt = l ? (~0ull >> (64 - l)) : 0ull;
-        for (int j0 = 0; j0 < lam; j0 += 64) {
-            const int j = j0 + l;
-            const int a0 = j < lam ? cPos[j] : -1, a1 = j < lam ? cPos1[j] : -1;
-            const bool rep = j < lam && a1 >= 0 && a1 != a0;
-            const unsigned long long m = __ballot(rep);
-            const int k = base + __popcll(m & lt);
-            if (rep && k < KB) { dPos[k] = a1; dSrc[k] = cSrc1[j]; }
-            base += __popcll(m);
+    // slots replaced at the second chunk, first step: one ballot mask per 64 slots, the waves taking
+    // the groups in turn (the ranks follow after the next barrier, before block 0 is staged)
+    const unsigned long long lt = l ? (~0ull >> (64 - l)) : 0ull;
+    const int nrg = (lam + 63) >> 6;
+    auto replaced = [&](int j) {
+        const int a0 = j < lam ? cPos[j] : -1, a1 = j < lam ? cPos1[j] : -1;
+        return j < lam && a1 >= 0 && a1 != a0;
+    };
+    if (sparse)
+        for (int gi = w; gi < nrg; gi += kRfThreads / 64) {
+            const unsigned long long m = __ballot(replaced(64 * gi + l));
+            if (l == 0) repm[gi] = m;
         }
-        if (l == 0) misc[0] = base < KB ? base : KB;
-    }
     const int nblk0 = nbb + ncb;                    // blocks known before the replaced-slot pass
     int nd = 0;                                     // replaced slots (known after the next barrier)
 
@@ -343,7 +351,7 @@ __global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs
     if (lin) {
         const char* recw = grp ? rec1 : rec0;
         const T* snapH = reinterpret_cast<const T*>(recw + A.L.c_snap_h);
-        const float* snapS = reinterpret_cast<const float*>(recw + A.L.c_snap_s);
+        const float* snapS = snapsL + grp * D;           // staged in LDS with the prologue's loads
         const T* foldVT = reinterpret_cast<const T*>(recw + A.L.c_fold_vt);
         const int cpv = A.L.c_pad64;
         const int nf = misc[1 + grp];
@@ -455,6 +463,22 @@ __global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs
     asm volatile("" ::: "memory");                  // a second load, not the first one kept live
     load_q();
     __syncthreads();                                // every wave is past the fold term: buffer 0 is free
+    // replaced slots, second step: each group's entries at its rank among all groups
+    if (sparse) {
+        for (int gi = w; gi < nrg; gi += kRfThreads / 64) {
+            int base = 0;
+            for (int g2 = 0; g2 < gi; ++g2) base += __popcll(repm[g2]);
+            const unsigned long long m = repm[gi];
+            const int j = 64 * gi + l;
+            const int k = base + __popcll(m & lt);
+            if (((m >> l) & 1ull) && k < KB) { dPos[k] = cPos1[j]; dSrc[k] = cSrc1[j]; }
+        }
+        if (tid == 0) {
+            int tot = 0;
+            for (int g2 = 0; g2 < nrg; ++g2) tot += __popcll(repm[g2]);
+            misc[0] = tot < KB ? tot : KB;
+        }
+    }
     if (nblk0 > 0) stage(0);
     __syncthreads();                                // block 0 staged, the replaced slots listed
     nd = misc[0];
