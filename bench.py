@@ -280,16 +280,15 @@ def bench_options(args, lola, torch, wl):
 HOLA_W, HOLA_C = 64, 256     # the HOLA page's persistent cache and chunk
 
 
-def bench_hola(args, lola, torch, wl):
-    """The HOLA variant (hola_prefill) on the headline shape (32 heads, n = 4096, d = 128, bf16) with the
-    page's w = 64 and C = 256: K back-to-back layer calls on resident seeded inputs.  The delta rule's
+def bench_hola(args, lola, torch, B, h, n, d):
+    """The HOLA variant (hola_prefill) with the page's w = 64 and C = 256 on B x h heads of n tokens and
+    head dimension d, bf16: K back-to-back layer calls on resident seeded inputs.  The delta rule's
     algorithmic work is three d x d matrix-vector products per token and head (prediction S^T k, the
     write k e^T, the read-out S^T q): 6 d^2 fp32 FLOP.  It runs on fp32 MFMA in blocks of 16 tokens, so
     it is priced against the fp32 matrix peak."""
     import numpy as np
     dev = torch.device("cuda:0")
     rng = np.random.default_rng(20)
-    B, h, n, d = wl.B, wl.h, wl.n, wl.d_k
     q, k, v = (torch.from_numpy(rng.standard_normal((B, h, n, d)).astype(np.float32)).to(dev).to(torch.bfloat16)
                for _ in range(3))
     alpha = torch.from_numpy(rng.uniform(0.9, 1.0, (B, h, n)).astype(np.float32)).to(dev)
@@ -617,7 +616,10 @@ def main() -> int:
     if not args.no_options:
         out["options"] = bench_options(leg_args, lola, torch, CONFIGS[2])
     if not args.no_hola:
-        out["hola"] = bench_hola(leg_args, lola, torch, CONFIGS[2])
+        hw = CONFIGS[2]
+        out["hola"] = bench_hola(leg_args, lola, torch, hw.B, hw.h, hw.n, hw.d_k)
+        # the HOLA page's own setup: 4 heads of dimension 256
+        out["hola"]["d256"] = bench_hola(leg_args, lola, torch, 1, 4, hw.n, 256)
     if not args.no_cpu_baseline:
         log("cpu baseline: running the oracle ...")
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_heads)

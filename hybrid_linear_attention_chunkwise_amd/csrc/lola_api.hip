@@ -134,7 +134,7 @@ static lola::HolaLayout hola_layout(int64_t BH, int64_t d, int64_t esz, int64_t 
 static lola_status hola_check(int32_t B, int32_t n_heads, int32_t d, int32_t dtype, int64_t n, int32_t C) {
     if (B <= 0 || n_heads <= 0 || n < 0 || C < 1) return LOLA_EINVAL;
     if (dtype != LOLA_F32 && dtype != LOLA_BF16) return LOLA_EINVAL;
-    if (d != 64 && d != 128) return LOLA_EUNSUPPORTED;
+    if (d != 64 && d != 128 && d != 256) return LOLA_EUNSUPPORTED;
     if (C > lola::kHolaMaxC || n > INT_MAX / 2 || (int64_t)B * n_heads > INT_MAX / 2) return LOLA_EUNSUPPORTED;
     return LOLA_OK;
 }

@@ -659,8 +659,11 @@ hipError_t launch_hola_t(const HolaArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_hola(const HolaArgs& a, int dtype, int d, hipStream_t stream) {
-    if (dtype == 0) return d == 64 ? launch_hola_t<float, 64>(a, stream) : launch_hola_t<float, 128>(a, stream);
-    return d == 64 ? launch_hola_t<bf16, 64>(a, stream) : launch_hola_t<bf16, 128>(a, stream);
+    if (dtype == 0)
+        return d == 64 ? launch_hola_t<float, 64>(a, stream)
+                       : d == 128 ? launch_hola_t<float, 128>(a, stream) : launch_hola_t<float, 256>(a, stream);
+    return d == 64 ? launch_hola_t<bf16, 64>(a, stream)
+                   : d == 128 ? launch_hola_t<bf16, 128>(a, stream) : launch_hola_t<bf16, 256>(a, stream);
 }
 
 }  // namespace lola

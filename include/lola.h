@@ -273,7 +273,7 @@ lola_status lola_sre_collisions(const lola_state *st, const void *v, const int32
 size_t hola_workspace_bytes(int32_t B, int32_t n_heads, int32_t d, int32_t dtype, int64_t n, int32_t C);
 
 /* One HOLA layer call over n tokens of B sequences x n_heads heads (all device pointers):
- *   q, k, v, y [B][n_heads][n][d] in dtype (LOLA_F32 or LOLA_BF16), 16-byte aligned, d in {64, 128};
+ *   q, k, v, y [B][n_heads][n][d] in dtype (LOLA_F32 or LOLA_BF16), 16-byte aligned, d in {64, 128, 256};
  *   alpha, beta [B][n_heads][n] fp32 gates (alpha in (0, 1], beta in [0, 1]);
  *   gamma_q, gamma_k [n_heads][d] fp32 cache-path scales; sink, gate [n_heads] fp32;
  *   S_out (nullable) [B][n_heads][d][d] fp32 final state, row = key dimension;

@@ -107,7 +107,7 @@ def test_options_validation_without_gpu(lib, mask, rule, reserved):
 HOLA_BAD = [
     # (B, heads, d, dtype, n, C, w, expected): rejected before any device work
     (0, 2, 128, B.LOLA_BF16, 64, 16, 4, B.LOLA_EINVAL),          # no sequences
-    (1, 2, 96, B.LOLA_BF16, 64, 16, 4, B.LOLA_EUNSUPPORTED),     # d outside {64, 128}
+    (1, 2, 96, B.LOLA_BF16, 64, 16, 4, B.LOLA_EUNSUPPORTED),     # d outside {64, 128, 256}
     (1, 2, 128, 7, 64, 16, 4, B.LOLA_EINVAL),                    # unknown storage type
     (1, 2, 128, B.LOLA_BF16, 64, 0, 4, B.LOLA_EINVAL),           # chunk of 0
     (1, 2, 128, B.LOLA_BF16, 64, 2048, 4, B.LOLA_EUNSUPPORTED),  # chunk above the largest

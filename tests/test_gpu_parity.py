@@ -657,6 +657,8 @@ HOLA_CASES = [
     (92, dict(n=100, C=1, w=8, d=64)),          # one-token chunks
     (93, dict(n=70, C=256, w=64, d=128)),       # n < C: no persistent cache is ever read
     (94, dict(n=200, C=32, w=0, d=64)),         # w = 0: chunk tokens and the sink only
+    (95, dict(n=530, C=256, w=64, d=256)),      # the page's head dimension, w and C
+    (96, dict(n=300, C=64, w=16, d=256)),       # d = 256, several chunks, ragged tail
 ]
 
 
