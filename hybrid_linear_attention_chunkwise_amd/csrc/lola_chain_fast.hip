@@ -44,8 +44,10 @@ constexpr int kFcStageRow = 128;          // rows 0..63 and 64..127: leaving buf
 constexpr int kFcZeroRow = 192;
 constexpr int kFcRows = 193;
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
 struct FcLds {
-    size_t rows, hcopy, key, spos, ssrc, s, bits, frow, hist, list, misc, total;
+    size_t rows, hcopy, list, spos, ssrc, s, mm, tw, em, frow, hist, misc, total;
 };
 
 __host__ __device__ constexpr FcLds fc_lds() {
@@ -53,14 +55,15 @@ __host__ __device__ constexpr FcLds fc_lds() {
     size_t p = 0;
     o.rows = p;   p += (size_t)kFcRows * kFcRowB;
     o.hcopy = p;  p += (size_t)kFcNW * (kFcD / 32) * 64 * 16;
-    o.key = p;    p += 8 * kFcMaxCand;
+    o.list = p;   p += 8 * kFcMaxCand;
     o.spos = p;   p += 4 * 2 * kFcMaxLam;
     o.ssrc = p;   p += 4 * 2 * kFcMaxLam;
     o.s = p;      p += 4 * kFcD;
-    o.bits = p;   p += 8 * 16;
+    o.mm = p;     p += 4 * 2 * kFcNW;
+    o.tw = p;     p += 4 * 32;
+    o.em = p;     p += 16;
     o.frow = p;   p += 4 * kFcMaxC;
     o.hist = p;   p += 4 * 256;
-    o.list = p;   p += 8 * 64;
     o.misc = p;   p += 64;
     o.total = p;
     return o;
@@ -89,14 +92,15 @@ __global__ __launch_bounds__(kFcNT) void chain_fast_kernel(PrefillArgs A) {
     extern __shared__ __align__(16) char smem[];
     char* rows = smem + lo.rows;
     bf16* hcopy = reinterpret_cast<bf16*>(smem + lo.hcopy);
-    unsigned long long* key = reinterpret_cast<unsigned long long*>(smem + lo.key);
+    unsigned long long* list = reinterpret_cast<unsigned long long*>(smem + lo.list);  // boundary-bin keys
     int* sPos = reinterpret_cast<int*>(smem + lo.spos);       // [2][kFcMaxLam], by chunk parity
     int* sSrc = reinterpret_cast<int*>(smem + lo.ssrc);
     float* sS = reinterpret_cast<float*>(smem + lo.s);
-    unsigned long long* bits = reinterpret_cast<unsigned long long*>(smem + lo.bits);   // [3][5] candidate bit sets
+    unsigned* mm = reinterpret_cast<unsigned*>(smem + lo.mm);  // per wave: min and max SRE bits
+    int* tw = reinterpret_cast<int*>(smem + lo.tw);           // per tile: folds | freed slots << 16
+    unsigned short* em = reinterpret_cast<unsigned short*>(smem + lo.em);   // entrants by leaving tile
     int* frow = reinterpret_cast<int*>(smem + lo.frow);       // fold rank -> LDS row
     int* hist = reinterpret_cast<int*>(smem + lo.hist);
-    unsigned long long* list = reinterpret_cast<unsigned long long*>(smem + lo.list);
     int* misc = reinterpret_cast<int*>(smem + lo.misc);
 
     const int lam = A.lam, eta = A.eta, n = A.n, C = A.C;
@@ -164,6 +168,22 @@ __global__ __launch_bounds__(kFcNT) void chain_fast_kernel(PrefillArgs A) {
         int64_t xl;
         const int nx = chunk_x(ch_, xl);
         const int rel = (int)(xl - t0);                       // >= -eta: leaving token 0 relative to the call
+        if (rel >= 0) {
+            // every leaving token is an input token: lanes with l mod 32 < 16 read features, the others
+            // values, of consecutive input rows
+            const uintptr_t fb = reinterpret_cast<uintptr_t>(phiS + (int64_t)rel * D);
+            const uintptr_t vb = reinterpret_cast<uintptr_t>(vin + (int64_t)rel * D);
+            const uintptr_t base = (l & 16) ? vb : fb;
+            for (int pr = w; 2 * pr < nx; pr += kFcNW) {
+                const int x = 2 * pr + (l >> 5);
+                const int off = min(x, nx - 1) * (D * 2) + (((l & 15) ^ (x & 15)) << 4);
+                __builtin_amdgcn_global_load_lds(
+                    reinterpret_cast<const void*>(base + off),
+                    (void __attribute__((address_space(3)))*)((__attribute__((address_space(3))) char*)(rows + (64 * buf + 2 * pr) * kFcRowB)),
+                    16, 0, 0);
+            }
+            return;
+        }
         for (int pr = w; 2 * pr < nx; pr += kFcNW) {
             const int x = 2 * pr + (l >> 5);
             const int p = (l & 31) ^ ((64 * buf + x) & 15);
@@ -280,8 +300,16 @@ __global__ __launch_bounds__(kFcNT) void chain_fast_kernel(PrefillArgs A) {
             for (int d = tid; d < D; d += kFcNT) snapS[d] = sS[d];
         }
 
-        // (2) scoring: SRE of every candidate against the chunk-start state
+        // (2) scoring: SRE of every candidate against the chunk-start state.  From here on lane (g, c),
+        // g < 3, stands for candidate c of tile w + 8g: a cache slot (tiles below nct) or a leaving
+        // token; its key stays in its registers.
         const bool scoring = lam > 0 && nG + nX > lam;
+        const int Tg = w + 8 * g;
+        const bool lane_c = g < 2 && 16 * Tg + c < lam;
+        const int xg = 16 * (Tg - nct) + c;
+        const bool lane_x = Tg >= nct && Tg < nct + nlt && xg < nX;
+        const int posg = g == 0 ? posR[0] : posR[1];
+        bool fold = false;
         if (scoring) {
             const bool h0 = w < nct, h1 = w + 8 < nct;
             int L = -1;
@@ -367,209 +395,106 @@ __global__ __launch_bounds__(kFcNT) void chain_fast_kernel(PrefillArgs A) {
             };
             if (hx) recall(std::true_type{});
             else recall(std::false_type{});
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int j = 16 * (w + 8 * u) + c;
-                const float sre = __builtin_amdgcn_sqrtf(sum_groups(sq[u]));
-                if ((u == 0 ? h0 : h1) && g == 0) key[j] = (j < lam && posR[u] >= 0) ? fc_key(sre, posR[u]) : 0ull;
-            }
+            unsigned long long myk = 0ull;
             {
-                const float sre = __builtin_amdgcn_sqrtf(sum_groups(sq[2]));
-                if (hx && g == 0) key[lamp + xr] = xr < nX ? fc_key(sre, (int)(xlo + xr)) : 0ull;
+                const float sre0 = __builtin_amdgcn_sqrtf(sum_groups(sq[0]));
+                const float sre1 = __builtin_amdgcn_sqrtf(sum_groups(sq[1]));
+                const float sre2 = __builtin_amdgcn_sqrtf(sum_groups(sq[2]));
+                if (lane_c && posg >= 0) myk = fc_key(g == 0 ? sre0 : sre1, posg);
+                else if (lane_x) myk = fc_key(sre2, (int)(xlo + xg));
+            }
+            // (3) selection by all waves: the nF = nG + nX - lambda smallest keys fold.  A 256-bin
+            // histogram over the SRE's bit pattern between the smallest and largest SRE (SRE >= 0, so
+            // the bits order like the value: a logarithmic scale on which a bin is monotone in the key)
+            // finds the boundary bin; its members are ranked exactly against each other.
+            {
+                const float kf = __uint_as_float((unsigned)(myk >> 32));
+                const float lo_ = wave_min(myk ? kf : INFINITY), hi_ = wave_max(myk ? kf : 0.f);
+                if (l == 0) {
+                    mm[2 * w] = __float_as_uint(lo_);
+                    mm[2 * w + 1] = __float_as_uint(hi_);
+                }
+                if (l < 32) hist[32 * w + l] = 0;
+                if (tid == 0) misc[2] = 0;                    // boundary list length
             }
             __syncthreads();
+            unsigned bmn = 0xFFFFFFFFu, bmx = 0u;
+#pragma unroll
+            for (int k2 = 0; k2 < kFcNW / 2; ++k2) {
+                const u32x4 m4 = *reinterpret_cast<const u32x4*>(mm + 4 * k2);
+                bmn = min(bmn, min(m4.x, m4.z));
+                bmx = max(bmx, max(m4.y, m4.w));
+            }
+            const float scale = bmx > bmn ? 256.f / ((float)(bmx - bmn) + 1.f) : 0.f;
+            const unsigned kb = (unsigned)(myk >> 32);
+            const int bin = kb <= bmn ? 0 : min(255, (int)((float)(kb - bmn) * scale));
+            if (myk) atomicAdd(&hist[bin], 1);
+            __syncthreads();
+            const int need = nG + nX - lam;
+            const int4 h4 = *reinterpret_cast<const int4*>(hist + 4 * l);
+            const int s4 = h4.x + h4.y + h4.z + h4.w;
+            const int cum = wave_inclusive_sum(s4);
+            const int lb = __builtin_amdgcn_readfirstlane(__ffsll((long long)__ballot(cum >= need)) - 1);
+            int run = cum - s4, bl = 0, bef = 0, hb = 0;
+            {
+                const int hv[4] = {h4.x, h4.y, h4.z, h4.w};
+                bool found = false;
+#pragma unroll
+                for (int k2 = 0; k2 < 4; ++k2) {
+                    if (!found && need <= run + hv[k2]) { bl = 4 * l + k2; bef = run; hb = hv[k2]; found = true; }
+                    run += hv[k2];
+                }
+            }
+            const int bstar = __builtin_amdgcn_readlane(bl, lb);
+            const int needp = need - __builtin_amdgcn_readlane(bef, lb);   // folds inside the boundary bin
+            const int mb = __builtin_amdgcn_readlane(hb, lb);              // its members
+            fold = myk != 0ull && bin < bstar;
+            const bool member = myk != 0ull && bin == bstar;
+            if (mb > needp) {
+                if (member) list[atomicAdd(&misc[2], 1)] = myk;
+                __syncthreads();
+                if (__ballot(member) != 0ull) {
+                    int below = 0;
+#pragma unroll 4
+                    for (int t = 0; t < mb; t += 2) {
+                        typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
+                        const u64x2 pk = *reinterpret_cast<const u64x2*>(list + t);
+                        below += (pk.x < myk ? 1 : 0) + (t + 1 < mb && pk.y < myk ? 1 : 0);
+                    }
+                    fold = fold || (member && below < needp);
+                }
+            } else {
+                fold = fold || member;
+            }
+        } else if (lam == 0) {
+            fold = lane_x;
         }
 
-        // (3) wave 0: which candidates fold.  A lane holds candidates l + 64i, i < 5; the result is three
-        // candidate bit sets in LDS (folds, freed cache slots, entrants), 64 candidates a word.
-        if (w == 0) {
-            const int nc = lamp + nX;
-            const unsigned long long lt = l ? (~0ull >> (64 - l)) : 0ull;
-            unsigned long long kv[kFcKPL];
-            unsigned fo = 0u, und = 0u;                        // per-candidate flags: bit i
-#pragma unroll
-            for (int i = 0; i < kFcKPL; ++i) {
-                const int cand = l + 64 * i;
-                kv[i] = (scoring && cand < nc) ? key[cand] : 0ull;
-                und |= (kv[i] != 0ull ? 1u : 0u) << i;
-            }
-            auto count = [&](unsigned bset) {
-                int m_ = 0;
-#pragma unroll
-                for (int i = 0; i < kFcKPL; ++i) m_ += __popcll(__ballot((bset >> i) & 1u));
-                return m_;
-            };
-            if (scoring) {
-                int need = __builtin_amdgcn_readfirstlane(nG + nX - lam);   // folds among the undecided
-                // one 256-bin histogram over the SRE's bit pattern (SRE >= 0, so the bits order like the
-                // value: a logarithmic scale on which a bin is monotone in the key), four bins a lane
-                float fmn = INFINITY, fmx = 0.f;
-#pragma unroll
-                for (int i = 0; i < kFcKPL; ++i)
-                    if ((und >> i) & 1u) {
-                        const float v = __uint_as_float((unsigned)(kv[i] >> 32));
-                        fmn = fminf(fmn, v);
-                        fmx = fmaxf(fmx, v);
-                    }
-                const unsigned bmn = __builtin_amdgcn_readfirstlane(__float_as_uint(wave_min(fmn)));
-                const unsigned bmx = __builtin_amdgcn_readfirstlane(__float_as_uint(wave_max(fmx)));
-                if (bmx > bmn) {
-                    const float scale = 256.f / ((float)(bmx - bmn) + 1.f);
-                    int bin[kFcKPL];
-#pragma unroll
-                    for (int i = 0; i < kFcKPL; ++i) {
-                        const unsigned b = (unsigned)(kv[i] >> 32);
-                        bin[i] = b <= bmn ? 0 : min(255, (int)((float)(b - bmn) * scale));
-                    }
-                    *reinterpret_cast<int4*>(hist + 4 * l) = make_int4(0, 0, 0, 0);
-#pragma unroll
-                    for (int i = 0; i < kFcKPL; ++i)
-                        if ((und >> i) & 1u) atomicAdd(&hist[bin[i]], 1);
-                    const int4 h4 = *reinterpret_cast<const int4*>(hist + 4 * l);
-                    const int s4 = h4.x + h4.y + h4.z + h4.w;
-                    const int cum = wave_inclusive_sum(s4);
-                    const int lb = __builtin_amdgcn_readfirstlane(__ffsll((long long)__ballot(cum >= need)) - 1);
-                    int run = cum - s4, bl = 0, bef = 0;
-                    const int hv[4] = {h4.x, h4.y, h4.z, h4.w};
-                    bool found = false;
-#pragma unroll
-                    for (int k2 = 0; k2 < 4; ++k2) {
-                        if (!found && need <= run + hv[k2]) { bl = 4 * l + k2; bef = run; found = true; }
-                        run += hv[k2];
-                    }
-                    const int bstar = __builtin_amdgcn_readlane(bl, lb);
-                    need -= __builtin_amdgcn_readlane(bef, lb);
-#pragma unroll
-                    for (int i = 0; i < kFcKPL; ++i)
-                        if ((und >> i) & 1u) {
-                            if (bin[i] < bstar) fo |= 1u << i;
-                            if (bin[i] != bstar) und &= ~(1u << i);
-                        }
-                }
-                // exact rank of the undecided: the `need` smallest keys fold
-                const int m = __builtin_amdgcn_readfirstlane(count(und));
-                if (m > 0 && need >= m) {
-                    fo |= und;
-                } else if (m > 0 && need > 0 && m <= 64) {
-                    // one member a lane: list[idx] = the idx-th undecided key, padded with keys that rank
-                    // above every candidate
-                    int idx[kFcKPL];
-                    int pre = 0;
-                    if (l >= m) list[l] = ~0ull;
-#pragma unroll
-                    for (int i = 0; i < kFcKPL; ++i) {
-                        const bool u_ = (und >> i) & 1u;
-                        const unsigned long long mk = __ballot(u_);
-                        idx[i] = pre + __popcll(mk & lt);
-                        if (u_) list[idx[i]] = kv[i];
-                        pre += __popcll(mk);
-                    }
-                    const unsigned long long my = list[l];
-                    int below = 0;
-                    for (int jj = 0; jj < m; jj += 4) {
-                        typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
-                        const u64x2 xa = *reinterpret_cast<const u64x2*>(list + jj);
-                        const u64x2 xb = *reinterpret_cast<const u64x2*>(list + jj + 2);
-                        below += (xa.x < my ? 1 : 0) + (xa.y < my ? 1 : 0) + (xb.x < my ? 1 : 0) + (xb.y < my ? 1 : 0);
-                    }
-                    const unsigned long long fm = __ballot(l < m && below < need);
-#pragma unroll
-                    for (int i = 0; i < kFcKPL; ++i)
-                        if (((und >> i) & 1u) && ((fm >> idx[i]) & 1ull)) fo |= 1u << i;
-                } else if (m > 0 && need > 0) {
-                    // many keys share the boundary bin: every undecided key against all of them, 64 at a time
-                    int below[kFcKPL];
-#pragma unroll
-                    for (int i = 0; i < kFcKPL; ++i) below[i] = 0;
-                    for (int r0 = 0; r0 < m; r0 += 64) {
-                        int pre = 0;
-                        const int cnt = min(64, m - r0);
-                        if (l >= cnt) list[l] = ~0ull;
-#pragma unroll
-                        for (int i = 0; i < kFcKPL; ++i) {
-                            const bool u_ = (und >> i) & 1u;
-                            const unsigned long long mk = __ballot(u_);
-                            const int id = pre + __popcll(mk & lt);
-                            if (u_ && id >= r0 && id < r0 + 64) list[id - r0] = kv[i];
-                            pre += __popcll(mk);
-                        }
-                        for (int jj = 0; jj < cnt; ++jj) {
-                            const unsigned long long x = list[jj];
-#pragma unroll
-                            for (int i = 0; i < kFcKPL; ++i) below[i] += (x < kv[i]) ? 1 : 0;
-                        }
-                    }
-#pragma unroll
-                    for (int i = 0; i < kFcKPL; ++i)
-                        if (((und >> i) & 1u) && below[i] < need) fo |= 1u << i;
-                }
-            } else if (lam == 0) {
-#pragma unroll
-                for (int i = 0; i < kFcKPL; ++i) {
-                    const int cand = l + 64 * i;
-                    if (cand >= lamp && cand - lamp < nX) fo |= 1u << i;
-                }
-            }
-            // the bit sets: folds, freed cache slots (empty, or holding a fold), entrants (kept leaving tokens)
-            int nS = 0, nE = 0;
-#pragma unroll
-            for (int i = 0; i < kFcKPL; ++i) {
-                const int cand = l + 64 * i;
-                const bool isC = cand < lam;
-                const bool isX = cand >= lamp && cand - lamp < nX;
-                const bool f_ = ((fo >> i) & 1u) && (isC || isX);
-                const bool r_ = isC && (sPos[cb * kFcMaxLam + cand] < 0 || f_);
-                const bool e_ = isX && !f_;
-                const unsigned long long m1 = __ballot(f_), m2 = __ballot(r_), m3 = __ballot(e_);
-                if (l == 0) {
-                    bits[i] = m1;
-                    bits[kFcKPL + i] = m2;
-                    bits[2 * kFcKPL + i] = m3;
-                }
-                nS += __popcll(m1);
-                nE += __popcll(m3);
-            }
-            if (l >= nS) frow[l] = kFcZeroRow;
-            if (l == 0) {
-                misc[0] = nS;
-                misc[1] = nE;
-                *reinterpret_cast<int*>(rec + A.L.c_fold_n) = nS;
-            }
+        // (4) the three candidate sets, in candidate order: folds, freed cache slots (empty, or holding
+        // a fold) and entrants (kept leaving tokens).  A member's rank in its set is its fold rank or its
+        // freed-slot rank; the freed slot of rank k takes the entrant of rank k.  Each wave publishes its
+        // tiles' counts and the leaving tiles' entrant masks; after one exchange every slot owner ranks
+        // its own slots, moves their rows and writes the fold list and the slot table.
+        const unsigned long long bf = __ballot(fold), br = __ballot(lane_c && (posg < 0 || fold)),
+                                 be = __ballot(lane_x && !fold);
+        if (c == 0 && g < 3) {
+            const unsigned fm = (unsigned)(bf >> (16 * g)) & 0xFFFFu, rm = (unsigned)(br >> (16 * g)) & 0xFFFFu;
+            tw[Tg] = __popc(fm) | (__popc(rm) << 16);
+            if (Tg >= nct && Tg < nct + nlt) em[Tg - nct] = (unsigned short)((be >> (16 * g)) & 0xFFFFull);
         }
         __syncthreads();
-        const int nS = misc[0], nE = misc[1];
-
-        // (4) every owner from the bit sets: its fold rank (staged row, fold list, records), its freed-slot
-        // rank (the entrant of the same rank moves in), the new slot table
+        int nS;
         {
-            auto rank_in = [&](int set, int cand) {           // members of bit set `set` before cand
-                const int i = cand >> 6;
-                int r = __popcll(bits[set * kFcKPL + i] & ((1ull << (cand & 63)) - 1ull));
+            const int twl = l < 3 * kFcNW ? tw[l] : 0;
+            unsigned long long E = *reinterpret_cast<const unsigned long long*>(em);
+            E &= nX >= 64 ? ~0ull : ((1ull << nX) - 1ull);
+            const int incl = wave_inclusive_sum(twl);
+            const int excl = incl - twl;
+            nS = __builtin_amdgcn_readlane(incl, 3 * kFcNW - 1) & 0xFFFF;
+            const int nE = __popcll(E);
+            int P[3];
 #pragma unroll
-                for (int k2 = 0; k2 < kFcKPL; ++k2)
-                    if (k2 < i) r += __popcll(bits[set * kFcKPL + k2]);
-                return r;
-            };
-            auto has = [&](int set, int cand) { return ((bits[set * kFcKPL + (cand >> 6)] >> (cand & 63)) & 1ull) != 0; };
-            auto kth_entrant = [&](int k) {                   // candidate index of the k-th entrant
-                int i = 0;
-                unsigned long long mk = bits[2 * kFcKPL];
-#pragma unroll
-                for (int k2 = 0; k2 < kFcKPL - 1; ++k2) {
-                    const int pc = __popcll(mk);
-                    if (k < pc) break;
-                    k -= pc;
-                    ++i;
-                    mk = bits[2 * kFcKPL + i];
-                }
-                int pos = 0;
-#pragma unroll
-                for (int wdt = 32; wdt >= 1; wdt >>= 1) {
-                    const int cnt = __popcll(mk & ((1ull << wdt) - 1ull));
-                    if (k >= cnt) { k -= cnt; pos += wdt; mk >>= wdt; }
-                }
-                return 64 * i + pos;
-            };
+            for (int u = 0; u < 3; ++u) P[u] = __builtin_amdgcn_readlane(excl, w + 8 * u);
             int* recFoldPos = reinterpret_cast<int*>(rec + A.L.c_fold_pos);
             int* recFoldSrc = reinterpret_cast<int*>(rec + A.L.c_fold_src);
             int* rp = reinterpret_cast<int*>(rec + A.L.c_cache_pos);
@@ -578,9 +503,10 @@ __global__ __launch_bounds__(kFcNT) void chain_fast_kernel(PrefillArgs A) {
             for (int u = 0; u < 2; ++u) {
                 const int j = 16 * (w + 8 * u) + c;
                 if (j < lam) {
+                    const unsigned long long lowc = ((1ull << c) - 1ull) << (16 * u);
                     int np = posR[u], ns = sSrc[cb * kFcMaxLam + j];
-                    if (has(0, j)) {
-                        const int fr = rank_in(0, j);
+                    if ((bf >> (16 * u + c)) & 1ull) {
+                        const int fr = (P[u] & 0xFFFF) + __popcll(bf & lowc);
                         row_store(kFcStageRow + fr, CF[u], CV[u]);
                         if (g == 0) {
                             frow[fr] = kFcStageRow + fr;
@@ -589,10 +515,17 @@ __global__ __launch_bounds__(kFcNT) void chain_fast_kernel(PrefillArgs A) {
                             if (foldAt && np >= t0) foldAt[np - t0] = ch;
                         }
                     }
-                    if (has(1, j)) {
-                        const int fk = rank_in(1, j);
-                        if (fk < nE) {
-                            const int x = kth_entrant(fk) - lamp;
+                    if ((br >> (16 * u + c)) & 1ull) {
+                        int rk = (P[u] >> 16) + __popcll(br & lowc);
+                        if (rk < nE) {
+                            // the rk-th set bit of E: the entrant's leaving-token index
+                            unsigned long long mk = E;
+                            int x = 0;
+#pragma unroll
+                            for (int wdt = 32; wdt >= 1; wdt >>= 1) {
+                                const int cnt = __popcll(mk & ((1ull << wdt) - 1ull));
+                                if (rk >= cnt) { rk -= cnt; x += wdt; mk >>= wdt; }
+                            }
                             row_load(64 * cb + x, CF[u], CV[u]);
                             np = (int)(xlo + x);
                             ns = source_of(xlo + x);
@@ -610,14 +543,14 @@ __global__ __launch_bounds__(kFcNT) void chain_fast_kernel(PrefillArgs A) {
                     }
                 }
             }
-            // leaving tokens that fold: fold list entries and records (the tile's owner)
+            // the folds among the wave's leaving tokens
 #pragma unroll
             for (int u = 0; u < 3; ++u) {
                 const int T = w + 8 * u;
-                if (T >= nct && T < nct + nlt && g == 0) {
+                if (T >= nct && T < nct + nlt) {
                     const int x = 16 * (T - nct) + c;
-                    if (x < nX && has(0, lamp + x)) {
-                        const int fr = rank_in(0, lamp + x);
+                    if (g == 0 && x < nX && ((bf >> (16 * u + c)) & 1ull)) {
+                        const int fr = (P[u] & 0xFFFF) + __popcll(bf & (((1ull << c) - 1ull) << (16 * u)));
                         const int64_t pos = xlo + x;
                         frow[fr] = 64 * cb + x;
                         recFoldPos[fr] = (int)pos;
@@ -626,6 +559,8 @@ __global__ __launch_bounds__(kFcNT) void chain_fast_kernel(PrefillArgs A) {
                     }
                 }
             }
+            if (w == 0 && l >= nS) frow[l] = kFcZeroRow;
+            if (tid == 0) *reinterpret_cast<int*>(rec + A.L.c_fold_n) = nS;
         }
         nG = scoring ? lam : (lam == 0 ? 0 : nG + nX);
         __syncthreads();
