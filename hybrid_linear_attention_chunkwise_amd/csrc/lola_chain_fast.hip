@@ -43,6 +43,8 @@ constexpr int kFcRowB = 512;              // one token row
 constexpr int kFcStageRow = 128;          // rows 0..63 and 64..127: leaving buffers; 128..191: folds
 constexpr int kFcZeroRow = 192;
 constexpr int kFcRows = 193;
+constexpr int kFcBucket = 16;             // keys a histogram bin keeps for the exact rank
+static_assert(256 * kFcBucket * 8 <= 64 * kFcRowB, "buckets fit the staging rows");
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
@@ -67,6 +69,15 @@ __host__ __device__ constexpr FcLds fc_lds() {
     o.misc = p;   p += 64;
     o.total = p;
     return o;
+}
+
+// A workgroup barrier that orders LDS only: the chain's global stores (chunk records, the fold list)
+// are read by later kernels, never by another wave of the same chain, so they stay in flight across it.
+// Each wave waits for its own leaving-token loads at the top of a chunk, before the first barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 __device__ __forceinline__ unsigned long long fc_key(float sre, int pos) {
@@ -293,7 +304,7 @@ __global__ __launch_bounds__(kFcNT) void chain_fast_kernel(PrefillArgs A) {
                 *reinterpret_cast<Frag8<bf16>*>(hcopy + ((w * 4 + ss) * 64 + l) * 8) = f;
             }
         }
-        __syncthreads();
+        lds_barrier();
         if (ch + 1 < A.c_end) prefetch(ch + 1, nb);
         {
             float* snapS = reinterpret_cast<float*>(rec + A.L.c_snap_s);
@@ -417,7 +428,7 @@ __global__ __launch_bounds__(kFcNT) void chain_fast_kernel(PrefillArgs A) {
                 if (l < 32) hist[32 * w + l] = 0;
                 if (tid == 0) misc[2] = 0;                    // boundary list length
             }
-            __syncthreads();
+            lds_barrier();
             unsigned bmn = 0xFFFFFFFFu, bmx = 0u;
 #pragma unroll
             for (int k2 = 0; k2 < kFcNW / 2; ++k2) {
@@ -428,8 +439,15 @@ __global__ __launch_bounds__(kFcNT) void chain_fast_kernel(PrefillArgs A) {
             const float scale = bmx > bmn ? 256.f / ((float)(bmx - bmn) + 1.f) : 0.f;
             const unsigned kb = (unsigned)(myk >> 32);
             const int bin = kb <= bmn ? 0 : min(255, (int)((float)(kb - bmn) * scale));
-            if (myk) atomicAdd(&hist[bin], 1);
-            __syncthreads();
+            // Each key also goes to its bin's bucket (16 keys a bin, in the staging rows, which hold
+            // nothing until the slot owners fill them), so a small boundary bin is ranked without a
+            // further exchange.
+            unsigned long long* bucket = reinterpret_cast<unsigned long long*>(rows + kFcStageRow * kFcRowB);
+            if (myk) {
+                const int id = atomicAdd(&hist[bin], 1);
+                if (id < kFcBucket) bucket[kFcBucket * bin + id] = myk;
+            }
+            lds_barrier();
             const int need = nG + nX - lam;
             const int4 h4 = *reinterpret_cast<const int4*>(hist + 4 * l);
             const int s4 = h4.x + h4.y + h4.z + h4.w;
@@ -451,14 +469,19 @@ __global__ __launch_bounds__(kFcNT) void chain_fast_kernel(PrefillArgs A) {
             fold = myk != 0ull && bin < bstar;
             const bool member = myk != 0ull && bin == bstar;
             if (mb > needp) {
-                if (member) list[atomicAdd(&misc[2], 1)] = myk;
-                __syncthreads();
+                // the members' keys: the bin's bucket, or (more than a bucket holds) a list built now
+                const unsigned long long* keys = bucket + kFcBucket * bstar;
+                if (mb > kFcBucket) {
+                    if (member) list[atomicAdd(&misc[2], 1)] = myk;
+                    lds_barrier();
+                    keys = list;
+                }
                 if (__ballot(member) != 0ull) {
                     int below = 0;
 #pragma unroll 4
                     for (int t = 0; t < mb; t += 2) {
                         typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
-                        const u64x2 pk = *reinterpret_cast<const u64x2*>(list + t);
+                        const u64x2 pk = *reinterpret_cast<const u64x2*>(keys + t);
                         below += (pk.x < myk ? 1 : 0) + (t + 1 < mb && pk.y < myk ? 1 : 0);
                     }
                     fold = fold || (member && below < needp);
@@ -482,7 +505,7 @@ __global__ __launch_bounds__(kFcNT) void chain_fast_kernel(PrefillArgs A) {
             tw[Tg] = __popc(fm) | (__popc(rm) << 16);
             if (Tg >= nct && Tg < nct + nlt) em[Tg - nct] = (unsigned short)((be >> (16 * g)) & 0xFFFFull);
         }
-        __syncthreads();
+        lds_barrier();
         int nS;
         {
             const int twl = l < 3 * kFcNW ? tw[l] : 0;
@@ -563,7 +586,7 @@ __global__ __launch_bounds__(kFcNT) void chain_fast_kernel(PrefillArgs A) {
             if (tid == 0) *reinterpret_cast<int*>(rec + A.L.c_fold_n) = nS;
         }
         nG = scoring ? lam : (lam == 0 ? 0 : nG + nX);
-        __syncthreads();
+        lds_barrier();
 
         // (5) fold: H += Phi_S^T V_S (32 tokens a step), s += column sums; the values, transposed, go
         // to the chunk record for the read-out kernel

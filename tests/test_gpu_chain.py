@@ -7,8 +7,9 @@ now run through this kernel.
 
 Cases: several chunks with a ragged end, lambda that is not a multiple of 16, lambda = 0, a cache
 that never fills, C = 16 and 32, eta = C - 1, n < C, outlier keys, planted duplicate pairs (exact SRE
-ties), continuation calls from a live state, and the overlapped schedule (several chain launches
-per call, the slot table carried through the workspace).
+ties), inputs of a few repeated tokens (ties in groups of tens to hundreds, so the selection's boundary
+bin overflows its bucket), continuation calls from a live state, and the overlapped schedule (several
+chain launches per call, the slot table carried through the workspace).
 """
 import os
 
@@ -29,11 +30,14 @@ def _need_gpu():
     lola._b.load()
 
 
-def _run(wl, split, general: bool, overlap: bool = False):
+def _run(wl, split, general: bool, overlap: bool = False, repeat: int = 0):
     import hybrid_linear_attention_chunkwise_amd as lola
     dev = torch.device("cuda:0")
     W = make_weights(wl)
     q, k, v = make_qkv(wl)
+    if repeat:   # only `repeat` distinct tokens: SREs collide in large groups of exact ties
+        idx = np.arange(wl.n) % repeat
+        q, k, v = q[:, :, idx].copy(), k[:, :, idx].copy(), v[:, :, idx].copy()
     phi = lola.LolaPhi(wl.phi, torch.from_numpy(W).to(dev), wl.D)
     st = lola.LolaState(wl.B, wl.h, wl.d_k, wl.d_v, wl.D, wl.eta, wl.lam, torch.bfloat16, device=dev)
     lola.lola_state_init(st)
@@ -79,14 +83,18 @@ CASES = [
     (210, dict(n=757, C=64, eta=96, lam=80), [300, 1, 456], False),      # continuation calls
     (211, dict(n=2100, C=64, eta=256, lam=256), [2100], True),           # several chain launches
     (212, dict(n=1300, C=32, eta=64, lam=144), [700, 600], True),
+    (213, dict(n=900, C=64, eta=64, lam=256, repeat=3), [900], False),    # boundary bins of ~100 tied keys
+    (214, dict(n=700, C=64, eta=80, lam=100, repeat=40), [700], False),
 ]
 
 
 @pytest.mark.parametrize("seed,kw,split,overlap", CASES, ids=[f"s{c[0]}" for c in CASES])
 def test_register_chain_equals_general_chain(seed, kw, split, overlap):
+    kw = dict(kw)
+    repeat = kw.pop("repeat", 0)
     wl = small_workload(seed, B=2, h=2, d_k=128, d_v=128, dtype="bf16", **kw)
-    fast = _run(wl, split, general=False, overlap=overlap)
-    gen = _run(wl, split, general=True, overlap=overlap)
+    fast = _run(wl, split, general=False, overlap=overlap, repeat=repeat)
+    gen = _run(wl, split, general=True, overlap=overlap, repeat=repeat)
     nfold = int((gen["fold"] >= 0).sum())
     print(f"[chain] {wl.name} split={split} overlap={overlap}: {nfold} tokens folded", flush=True)
     for name in gen:
