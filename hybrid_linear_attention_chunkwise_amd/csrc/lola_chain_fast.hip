@@ -216,6 +216,21 @@ __global__ __launch_bounds__(kFcNT) void chain_fast_kernel(PrefillArgs A) {
         }
     };
 
+    // One step of the contiguous case (every leaving token an input token, rows from the input row of
+    // the first on): the pair of rows w + 8 it.  The chunk loop spreads the four steps over the first
+    // scoring steps, so these loads are not issued in one burst behind the snapshot's stores.
+    auto prefetch_step = [&](int nx, uintptr_t base, int buf, int it) {
+        const int pr = w + kFcNW * it;
+        if (2 * pr < nx) {
+            const int x = 2 * pr + (l >> 5);
+            const int off = min(x, nx - 1) * (D * 2) + (((l & 15) ^ (x & 15)) << 4);
+            __builtin_amdgcn_global_load_lds(
+                reinterpret_cast<const void*>(base + off),
+                (void __attribute__((address_space(3)))*)((__attribute__((address_space(3))) char*)(rows + (64 * buf + 2 * pr) * kFcRowB)),
+                16, 0, 0);
+        }
+    };
+
     // ---------------- set-up ----------------
     const int cb0 = A.c_begin & 1;
     const bool first = A.c_begin == 0;
@@ -305,7 +320,22 @@ __global__ __launch_bounds__(kFcNT) void chain_fast_kernel(PrefillArgs A) {
             }
         }
         lds_barrier();
-        if (ch + 1 < A.c_end) prefetch(ch + 1, nb);
+        // the next chunk's leaving tokens: the contiguous case in four steps (during scoring, or here
+        // when the chunk does not score), any other at once
+        int pnx = 0;
+        uintptr_t pbase = 0;
+        bool pf_steps = false;
+        if (ch + 1 < A.c_end) {
+            int64_t pxl;
+            pnx = chunk_x(ch + 1, pxl);
+            const int prel = (int)(pxl - t0);
+            if (prel >= 0) {
+                pf_steps = true;
+                pbase = reinterpret_cast<uintptr_t>(((l & 16) ? vin : phiS) + (int64_t)prel * D);
+            } else {
+                prefetch(ch + 1, nb);
+            }
+        }
         {
             float* snapS = reinterpret_cast<float*>(rec + A.L.c_snap_s);
             for (int d = tid; d < D; d += kFcNT) snapS[d] = sS[d];
@@ -321,6 +351,10 @@ __global__ __launch_bounds__(kFcNT) void chain_fast_kernel(PrefillArgs A) {
         const bool lane_x = Tg >= nct && Tg < nct + nlt && xg < nX;
         const int posg = g == 0 ? posR[0] : posR[1];
         bool fold = false;
+        if (!scoring && pf_steps) {
+#pragma unroll
+            for (int it = 0; it < 4; ++it) prefetch_step(pnx, pbase, nb, it);
+        }
         if (scoring) {
             const bool h0 = w < nct, h1 = w + 8 < nct;
             int L = -1;
@@ -368,21 +402,26 @@ __global__ __launch_bounds__(kFcNT) void chain_fast_kernel(PrefillArgs A) {
             }
             auto recall = [&](auto with_x) {
                 constexpr bool WX = decltype(with_x)::value;
+                // A fragments and the leaving tile's values of step J + 1 are requested before step J
+                // is computed (the values first, so a wait for step J never waits for step J + 1)
                 Frag8<bf16> a[2][4];
+                bf16x4 xvb[2];
+                if (WX) xvb[0] = *reinterpret_cast<const bf16x4*>(rows + fc_off(xrow, 16 + (g >> 1), g & 1));
 #pragma unroll
                 for (int ss = 0; ss < 4; ++ss)
                     a[0][ss] = *reinterpret_cast<const Frag8<bf16>*>(hcopy + (ss * 64 + l) * 8);
 #pragma unroll
                 for (int J = 0; J < 8; ++J) {
                     const int cur = J & 1;
+                    if (J < 4 && pf_steps) prefetch_step(pnx, pbase, nb, J);
                     if (J + 1 < 8) {
+                        if (WX) xvb[cur ^ 1] = *reinterpret_cast<const bf16x4*>(rows + fc_off(xrow, 16 + 2 * (J + 1) + (g >> 1), g & 1));
 #pragma unroll
                         for (int ss = 0; ss < 4; ++ss)
                             a[cur ^ 1][ss] = *reinterpret_cast<const Frag8<bf16>*>(hcopy + (((J + 1) * 4 + ss) * 64 + l) * 8);
                     }
                     bf16x4 xv = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
-                    if (WX) xv = *reinterpret_cast<const bf16x4*>(rows + fc_off(xrow, 16 + 2 * J + (g >> 1), g & 1));
-                    if (WX && !xok) xv = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+                    if (WX && xok) xv = xvb[cur];
                     f4 r0 = zero4(), r1 = zero4(), r2 = zero4();
 #pragma unroll
                     for (int ss = 0; ss < 4; ++ss) {
