@@ -29,16 +29,23 @@ Readings where the notes leave a step open (listed in the design notes of the re
      sqrt(mean(x^2) + 1e-6); the null sink is one more logit (a per-head value) with a zero value.
   H4 output y_t = o_t + sigmoid(g) * (cache read-out), g a per-head gate value.
   H5 unit-norm state keys and queries: x / ||x||_2 (a zero vector stays zero).
+  H6 decode, one token at a time after a prefill, keeps the prefill's chunk grid (chunks of C
+     positions from position 0).  The memory between tokens is what 3.5 sizes for one head: the state
+     S plus at most w + C exact key-value rows, here the persistent cache at the start of the open
+     chunk (positions, raw keys and values, magnitudes) and the open chunk's tokens so far.  When a
+     token closes its chunk, the cache becomes the top w of the cache and the chunk's tokens (ties:
+     older), as in H2.
 
 Parity status: every function here is pinned by tests/test_oracle_hola.py (closed forms of the delta
-rule, brute-force top-w, causal softmax through torch's attention, invariants).
+rule, brute-force top-w, causal softmax through torch's attention, invariants; the decode step by
+equality with a prefill over the longer sequence).
 """
 from __future__ import annotations
 
 import numpy as np
 
 __all__ = ["unit", "rms_norm", "delta_rule", "write_magnitude", "persistent_cache", "cache_read",
-           "hola_prefill", "RMS_EPS"]
+           "hola_prefill", "HolaState", "hola_state_after_prefill", "hola_decode_step", "RMS_EPS"]
 
 RMS_EPS = 1e-6
 
@@ -121,3 +128,64 @@ def hola_prefill(q, k, v, alpha, beta, gamma_q, gamma_k, sink: float, gate: floa
             vis = A + list(range(a, t + 1))
             y[t] = o[t] + g * cache_read(q[t], k[vis], v[vis], sink, gamma_q, gamma_k)
     return y, S, persistent_cache(m, n, w), m, caches
+
+
+class HolaState:
+    """Reading H6: the memory of one sequence and head between decode steps.
+
+    t tokens seen; S [d_k][d_v]; cache: the persistent cache at the start of the open chunk, a list of
+    (position, raw key, raw value, magnitude) sorted by position; open_: the open chunk's tokens so far,
+    the same tuples in position order."""
+
+    def __init__(self, t, S, cache, open_):
+        self.t = int(t)
+        self.S = np.array(S, dtype=np.float64)
+        self.cache = list(cache)
+        self.open_ = list(open_)
+
+
+def _top_w(entries, w):
+    """Reading H2 on explicit entries: the w largest magnitudes (ties: older), sorted by position."""
+    kept = sorted(entries, key=lambda e: (-e[3], e[0]))[:w]
+    return sorted(kept, key=lambda e: e[0])
+
+
+def hola_state_after_prefill(q, k, v, alpha, beta, C: int, w: int) -> HolaState:
+    """The memory hola_prefill leaves after n tokens from an empty memory (reading H6)."""
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n = k.shape[0]
+    _, e, S = delta_rule(q, k, v, alpha, beta)
+    m = write_magnitude(e, beta)
+    a = (n // C) * C                                          # start of the open chunk
+    cache = [(i, k[i].copy(), v[i].copy(), float(m[i])) for i in persistent_cache(m, a, w)]
+    open_ = [(i, k[i].copy(), v[i].copy(), float(m[i])) for i in range(a, n)]
+    return HolaState(n, S, cache, open_)
+
+
+def hola_decode_step(st: HolaState, q_t, k_t, v_t, alpha_t: float, beta_t: float, gamma_q, gamma_k,
+                     sink: float, gate: float, C: int, w: int) -> np.ndarray:
+    """One token through the memory (readings H1-H6); mutates ``st`` and returns y_t.
+
+    The delta rule writes the token, the cache path reads the cache, the open chunk's earlier tokens and
+    the token itself, plus the sink; then the token joins the open chunk, and a full chunk is merged
+    into the cache."""
+    q_t = np.asarray(q_t, dtype=np.float64)
+    k_t = np.asarray(k_t, dtype=np.float64)
+    v_t = np.asarray(v_t, dtype=np.float64)
+    qh, kh = unit(q_t[None, :])[0], unit(k_t[None, :])[0]
+    e = v_t - alpha_t * (st.S.T @ kh)
+    st.S = alpha_t * st.S + beta_t * np.outer(kh, e)
+    o = st.S.T @ qh
+    m = float(beta_t * np.sqrt((e * e).sum()))
+    vis = st.cache + st.open_ + [(st.t, k_t, v_t, m)]
+    keys = np.array([x[1] for x in vis])
+    vals = np.array([x[2] for x in vis])
+    g = 1.0 / (1.0 + np.exp(-gate))
+    y = o + g * cache_read(q_t, keys, vals, sink, gamma_q, gamma_k)
+    st.open_.append((st.t, k_t.copy(), v_t.copy(), m))
+    st.t += 1
+    if st.t % C == 0:
+        st.cache = _top_w(st.cache + st.open_, w)
+        st.open_ = []
+    return y

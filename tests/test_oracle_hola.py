@@ -144,3 +144,71 @@ def test_gate_closed_is_the_state_alone():
     y, _, _, _, _ = H.hola_prefill(q, k, v, alpha, beta, np.ones(8), np.ones(8), 0.0, -80.0, 4, 3)
     o, _, _ = H.delta_rule(q, k, v, alpha, beta)
     np.testing.assert_allclose(y, o, atol=1e-30)
+
+
+# ---- decode (reading H6): the step is pinned to the prefill, itself pinned above ----
+
+def _gates(seed, d):
+    rng = np.random.default_rng(seed + 1000)
+    return rng.uniform(0.5, 1.5, d), rng.uniform(0.5, 1.5, d), float(rng.normal()), float(rng.normal())
+
+
+@pytest.mark.parametrize("n0,steps,C,w", [(8, 9, 4, 3), (10, 7, 4, 3), (0, 13, 5, 2), (12, 12, 3, 6),
+                                          (7, 10, 16, 4), (9, 6, 1, 2), (6, 8, 4, 0)])
+def test_decode_steps_continue_the_prefill(n0, steps, C, w):
+    """Prefill of n0 tokens then decode steps over the next ones gives the prefill of n0 + steps tokens:
+    the outputs, the final state and the persistent cache (chunk closes inside the decode included)."""
+    n = n0 + steps
+    q, k, v, alpha, beta = _problem(30 + n0 + 7 * C, n, d=8, dv=8)
+    gq, gk, sink, gate = _gates(n0 + C, 8)
+    y_ref, S_ref, cache_ref, m_ref, _ = H.hola_prefill(q, k, v, alpha, beta, gq, gk, sink, gate, C, w)
+    st = H.hola_state_after_prefill(q[:n0], k[:n0], v[:n0], alpha[:n0], beta[:n0], C, w)
+    assert st.t == n0
+    for t in range(n0, n):
+        y_t = H.hola_decode_step(st, q[t], k[t], v[t], alpha[t], beta[t], gq, gk, sink, gate, C, w)
+        np.testing.assert_allclose(y_t, y_ref[t], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(st.S, S_ref, rtol=1e-12, atol=1e-12)
+    # the memory after n tokens: cache at the start of the open chunk, then the open tokens
+    a = (n // C) * C
+    assert [e[0] for e in st.cache] == H.persistent_cache(m_ref, a, w)
+    assert [e[0] for e in st.open_] == list(range(a, n))
+    if n % C == 0:
+        assert [e[0] for e in st.cache] == list(cache_ref)
+    for e in st.cache + st.open_:
+        np.testing.assert_array_equal(e[1], k[e[0]])
+        np.testing.assert_allclose(e[3], m_ref[e[0]], rtol=1e-12)
+
+
+def test_decode_memory_is_bounded_and_sees_the_token():
+    """3.5: at most w + C exact rows at any time; with C = 1 and w = 0 and no sink weight the cache path
+    of a step reads only the token itself (its own value, whatever the logit)."""
+    q, k, v, alpha, beta = _problem(5, 30, d=8, dv=8)
+    gq, gk, _, _ = _gates(5, 8)
+    st = H.hola_state_after_prefill(q[:1], k[:1], v[:1], alpha[:1], beta[:1], 4, 3)
+    for t in range(1, 30):
+        H.hola_decode_step(st, q[t], k[t], v[t], alpha[t], beta[t], gq, gk, 0.0, 0.0, 4, 3)
+        assert len(st.cache) <= 3 and len(st.open_) < 4 and len(st.open_) == st.t % 4
+    st = H.hola_state_after_prefill(q[:3], k[:3], v[:3], alpha[:3], beta[:3], 1, 0)
+    o_prev = st.S.copy()
+    y = H.hola_decode_step(st, q[3], k[3], v[3], alpha[3], beta[3], gq, gk, -80.0, 80.0, 1, 0)
+    kh = k[3] / np.linalg.norm(k[3])
+    e = v[3] - alpha[3] * (o_prev.T @ kh)
+    S = alpha[3] * o_prev + beta[3] * np.outer(kh, e)
+    np.testing.assert_allclose(y, S.T @ (q[3] / np.linalg.norm(q[3])) + v[3], rtol=1e-12, atol=1e-12)
+
+
+def test_decode_negative_control_wrong_merge(monkeypatch):
+    """Control: a chunk close that kept the smallest magnitudes instead of the largest makes the decode
+    differ from the prefill, so the continuation pin above does see the merge rule."""
+    q, k, v, alpha, beta = _problem(77, 20, d=8, dv=8)
+    gq, gk, sink, gate = _gates(77, 8)
+    C, w = 3, 2
+    y_ref, *_ = H.hola_prefill(q, k, v, alpha, beta, gq, gk, sink, gate, C, w)
+    monkeypatch.setattr(H, "_top_w", lambda entries, w_: sorted(sorted(entries, key=lambda e: (e[3], e[0]))[:w_],
+                                                                   key=lambda e: e[0]))
+    st = H.hola_state_after_prefill(q[:4], k[:4], v[:4], alpha[:4], beta[:4], C, w)
+    worst = 0.0
+    for t in range(4, 20):
+        y_t = H.hola_decode_step(st, q[t], k[t], v[t], alpha[t], beta[t], gq, gk, sink, gate, C, w)
+        worst = max(worst, float(np.abs(y_t - y_ref[t]).max()))
+    assert worst > 1e-6
