@@ -20,7 +20,7 @@ __all__ = ["LolaState", "LolaPhi", "LolaOverlap", "lola_state_init", "lola_works
            "lola_decode_step", "lola_sre_collisions", "LolaError", "LOLA_OK", "LOLA_EINVAL", "LOLA_EUNSUPPORTED",
            "LOLA_EDEVICE", "library_path", "PHI_KINDS", "LOLA_READ_STATE", "LOLA_READ_SPARSE",
            "LOLA_READ_WINDOW", "LOLA_READ_ALL", "SCORE_RULES", "hola_workspace_bytes", "hola_prefill",
-           "lola_prefill_noalloc"]
+           "lola_prefill_noalloc", "HolaState", "hola_state_init", "hola_prefill_state", "hola_decode_step"]
 
 PHI_KINDS = {"elu1": LOLA_PHI_ELU1, "softmax_pm": LOLA_PHI_SOFTMAX_PM}
 _DTYPES = {torch.float32: LOLA_F32, torch.bfloat16: LOLA_BF16}
@@ -235,4 +235,62 @@ def hola_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch
                                   _ptr(S_out), _ptr(cache_pos), _ptr(cache_score), _ptr(workspace),
                                   workspace.numel(), _stream(stream))
     _b.check("hola_prefill", code)
+    return y
+
+
+class HolaState:
+    """HOLA decode memory of B sequences x n_heads heads on `device` (see hola_state): the state S, the
+    persistent cache at the start of the open chunk and the open chunk's tokens."""
+
+    def __init__(self, B: int, n_heads: int, d: int, C: int, w: int, dtype: torch.dtype, device="cuda"):
+        kw = dict(device=device)
+        self.dtype = dtype
+        self.S = torch.zeros(B, n_heads, d, d, dtype=torch.float32, **kw)
+        self.cache_pos = torch.full((B, n_heads, max(w, 1)), -1, dtype=torch.int32, **kw)
+        self.cache_score = torch.zeros(B, n_heads, max(w, 1), dtype=torch.float32, **kw)
+        self.cache_k = torch.zeros(B, n_heads, max(w, 1), d, dtype=dtype, **kw)
+        self.cache_v = torch.zeros(B, n_heads, max(w, 1), d, dtype=dtype, **kw)
+        self.open_k = torch.zeros(B, n_heads, C, d, dtype=dtype, **kw)
+        self.open_v = torch.zeros(B, n_heads, C, d, dtype=dtype, **kw)
+        self.open_score = torch.zeros(B, n_heads, C, dtype=torch.float32, **kw)
+        self.c = _b.HolaState(B, n_heads, d, _DTYPES[dtype], C, w, 0, self.S.data_ptr(), self.cache_pos.data_ptr(),
+                              self.cache_score.data_ptr(), self.cache_k.data_ptr(), self.cache_v.data_ptr(),
+                              self.open_k.data_ptr(), self.open_v.data_ptr(), self.open_score.data_ptr())
+
+    @property
+    def t(self) -> int:
+        return int(self.c.t)
+
+
+def hola_state_init(state: HolaState, stream=None) -> None:
+    _b.check("hola_state_init", _b.load().hola_state_init(ctypes.byref(state.c), _stream(stream)))
+
+
+def hola_prefill_state(state: HolaState, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
+                       beta: torch.Tensor, gamma_q: torch.Tensor, gamma_k: torch.Tensor, sink: torch.Tensor,
+                       gate: torch.Tensor, y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                       stream=None) -> torch.Tensor:
+    """hola_prefill from the empty memory `state`, leaving the decode memory in it; returns y."""
+    B, h, n, d = q.shape
+    if y is None:
+        y = torch.empty_like(v)
+    need = hola_workspace_bytes(B, h, d, q.dtype, n, state.c.C)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    code = _b.load().hola_prefill_state(ctypes.byref(state.c), n, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                        _ptr(gamma_q), _ptr(gamma_k), _ptr(sink), _ptr(gate), _ptr(y),
+                                        _ptr(workspace), workspace.numel(), _stream(stream))
+    _b.check("hola_prefill_state", code)
+    return y
+
+
+def hola_decode_step(state: HolaState, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
+                     beta: torch.Tensor, gamma_q: torch.Tensor, gamma_k: torch.Tensor, sink: torch.Tensor,
+                     gate: torch.Tensor, y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One token through the HOLA memory: q, k, v [B][h][d], alpha, beta [B][h]; returns y [B][h][d]."""
+    if y is None:
+        y = torch.empty_like(v)
+    code = _b.load().hola_decode_step(ctypes.byref(state.c), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                      _ptr(gamma_q), _ptr(gamma_k), _ptr(sink), _ptr(gate), _ptr(y), _stream(stream))
+    _b.check("hola_decode_step", code)
     return y

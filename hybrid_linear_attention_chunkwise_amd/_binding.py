@@ -23,8 +23,9 @@ LOLA_PHI_SOFTMAX_PM = 1
 
 EXPORTED = ("lola_workspace_bytes", "lola_state_init", "lola_prefill", "lola_prefill_ex",
             "lola_prefill_profiled", "lola_decode_step", "lola_decode_step_ex", "lola_sre_collisions",
-            "lola_status_string", "hola_workspace_bytes", "hola_prefill", "lola_peak_mfma_bf16",
-            "lola_peak_copy", "lola_prefill_noalloc")
+            "lola_status_string", "hola_workspace_bytes", "hola_prefill", "hola_state_init",
+            "hola_prefill_state", "hola_decode_step", "lola_peak_mfma_bf16", "lola_peak_copy",
+            "lola_prefill_noalloc")
 LOLA_NOALLOC_SCRATCH_BYTES = 64 << 20
 LOLA_READ_STATE = 1
 LOLA_READ_SPARSE = 2
@@ -50,6 +51,14 @@ class LolaState(ctypes.Structure):
 
 
 LOLA_OVERLAP_EVENTS = 9
+
+
+class HolaState(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("C", ctypes.c_int32), ("w", ctypes.c_int32), ("t", ctypes.c_int64),
+                ("S", ctypes.c_void_p), ("cache_pos", ctypes.c_void_p), ("cache_score", ctypes.c_void_p),
+                ("cache_k", ctypes.c_void_p), ("cache_v", ctypes.c_void_p), ("open_k", ctypes.c_void_p),
+                ("open_v", ctypes.c_void_p), ("open_score", ctypes.c_void_p)]
 
 
 class LolaOverlap(ctypes.Structure):
@@ -107,6 +116,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hola_prefill.argtypes = [i32, i32, i32, i32, i64, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                  vp, vp, vp, vp, sz, vp]
     lib.hola_prefill.restype = i32
+    hp = ctypes.POINTER(HolaState)
+    lib.hola_state_init.argtypes = [hp, vp]
+    lib.hola_state_init.restype = i32
+    lib.hola_prefill_state.argtypes = [hp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hola_prefill_state.restype = i32
+    lib.hola_decode_step.argtypes = [hp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.hola_decode_step.restype = i32
     lib.lola_peak_mfma_bf16.argtypes = [i32, i32, vp, vp]
     lib.lola_peak_mfma_bf16.restype = i32
     lib.lola_peak_copy.argtypes = [vp, vp, sz, vp]

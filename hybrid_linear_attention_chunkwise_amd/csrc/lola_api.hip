@@ -123,7 +123,7 @@ static lola::HolaLayout hola_layout(int64_t BH, int64_t d, int64_t esz, int64_t 
     L.ktil = p; p = rup(p + rows * d * esz, 256);
     L.o = p;    p = rup(p + rows * d * 4, 256);
     L.esq = p;  p = rup(p + rows * (d / 16) * 4, 256);
-    L.clist = p; p = rup(p + BH * nchunks * lola::kHolaMaxW * 4, 256);
+    L.clist = p; p = rup(p + BH * (nchunks + 1) * lola::kHolaMaxW * 4, 256);
     L.blk = p;  p = rup(p + BH * ((n + lola::kHolaBT - 1) / lola::kHolaBT) * (int64_t)sizeof(lola::HolaBlock), 256);
     L.sink = p; p = rup(p + 2 * 64 * 4, 256);
     L.tlist = p; p = rup(p + BH * nchunks * (C < lola::kHolaMaxW ? C : lola::kHolaMaxW) * 8, 256);
@@ -386,8 +386,127 @@ lola_status hola_prefill(int32_t B, int32_t n_heads, int32_t d, int32_t dtype, i
     a.cache_score_out = w > 0 ? cache_score_out : nullptr;
     a.ws = reinterpret_cast<char*>(workspace);
     a.L = L;
+    a.st_cache_pos = nullptr;
+    a.st_cache_score = nullptr;
+    a.st_cache_k = a.st_cache_v = a.st_open_k = a.st_open_v = nullptr;
+    a.st_open_score = nullptr;
     if (lola::launch_hola(a, dtype, d, (hipStream_t)stream) != hipSuccess) return LOLA_EDEVICE;
     if (getenv("LOLA_DEBUG_SYNC") && hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return LOLA_EDEVICE;
+    return LOLA_OK;
+}
+
+static lola_status hola_state_check(const hola_state* st) {
+    if (!st) return LOLA_EINVAL;
+    lola_status rc = hola_check(st->B, st->n_heads, st->d, st->dtype, 0, st->C);
+    if (rc != LOLA_OK) return rc;
+    if (st->w < 0 || st->t < 0) return LOLA_EINVAL;
+    if (st->w > lola::kHolaMaxW) return LOLA_EUNSUPPORTED;
+    if (!st->S || !aligned16(st->S) || !st->open_k || !st->open_v || !st->open_score || !aligned16(st->open_k) ||
+        !aligned16(st->open_v))
+        return LOLA_EINVAL;
+    if (st->w > 0 && (!st->cache_pos || !st->cache_score || !st->cache_k || !st->cache_v || !aligned16(st->cache_k) ||
+                      !aligned16(st->cache_v)))
+        return LOLA_EINVAL;
+    return LOLA_OK;
+}
+
+lola_status hola_state_init(hola_state* st, void* stream) {
+    lola_status rc = hola_state_check(st);
+    if (rc != LOLA_OK) return rc;
+    lola::HolaInitArgs a;
+    a.BH = st->B * st->n_heads;
+    a.d = st->d;
+    a.w = st->w;
+    a.S = st->S;
+    a.cache_pos = st->cache_pos;
+    a.cache_score = st->cache_score;
+    if (lola::launch_hola_init(a, (hipStream_t)stream) != hipSuccess) return LOLA_EDEVICE;
+    st->t = 0;
+    return LOLA_OK;
+}
+
+lola_status hola_prefill_state(hola_state* st, int64_t n, const void* q, const void* k, const void* v,
+                               const float* alpha, const float* beta, const float* gamma_q, const float* gamma_k,
+                               const float* sink, const float* gate, void* y, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    lola_status rc = hola_state_check(st);
+    if (rc != LOLA_OK) return rc;
+    if (n < 0) return LOLA_EINVAL;
+    if (st->t != 0) return LOLA_EUNSUPPORTED;
+    if (n == 0) return LOLA_OK;
+    rc = hola_check(st->B, st->n_heads, st->d, st->dtype, n, st->C);
+    if (rc != LOLA_OK) return rc;
+    if (!q || !k || !v || !y || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y)) return LOLA_EINVAL;
+    if (!alpha || !beta || !gamma_q || !gamma_k || !sink || !gate) return LOLA_EINVAL;
+    const int32_t C = st->C, d = st->d, dtype = st->dtype;
+    const int64_t nchunks = (n + C - 1) / C;
+    const int64_t BH = (int64_t)st->B * st->n_heads;
+    const int nqt = (C + 63) / 64;
+    if (BH * nchunks * nqt > (int64_t)INT_MAX || (BH * n + 7) / 8 > (int64_t)INT_MAX) return LOLA_EUNSUPPORTED;
+    const lola::HolaLayout L = hola_layout(BH, d, dtype == LOLA_BF16 ? 2 : 4, n, C, nchunks);
+    if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes < (size_t)L.total) return LOLA_EINVAL;
+    lola::HolaArgs a;
+    a.BH = (int)BH;
+    a.heads = st->n_heads;
+    a.n = (int)n;
+    a.C = C;
+    a.w = st->w;
+    a.nchunks = (int)nchunks;
+    a.nqt = nqt;
+    a.nblk = (int)((n + lola::kHolaBT - 1) / lola::kHolaBT);
+    a.q = q; a.k = k; a.v = v;
+    a.alpha = alpha; a.beta = beta;
+    a.gamma_q = gamma_q; a.gamma_k = gamma_k;
+    a.sink = sink; a.gate = gate;
+    a.y = y;
+    a.S_out = st->S;
+    a.cache_pos_out = nullptr;
+    a.cache_score_out = nullptr;
+    a.ws = reinterpret_cast<char*>(workspace);
+    a.L = L;
+    a.st_cache_pos = st->cache_pos;
+    a.st_cache_score = st->cache_score;
+    a.st_cache_k = st->cache_k;
+    a.st_cache_v = st->cache_v;
+    a.st_open_k = st->open_k;
+    a.st_open_v = st->open_v;
+    a.st_open_score = st->open_score;
+    if (lola::launch_hola(a, dtype, d, (hipStream_t)stream) != hipSuccess) return LOLA_EDEVICE;
+    if (getenv("LOLA_DEBUG_SYNC") && hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return LOLA_EDEVICE;
+    st->t = n;
+    return LOLA_OK;
+}
+
+lola_status hola_decode_step(hola_state* st, const void* q, const void* k, const void* v, const float* alpha,
+                             const float* beta, const float* gamma_q, const float* gamma_k, const float* sink,
+                             const float* gate, void* y, void* stream) {
+    lola_status rc = hola_state_check(st);
+    if (rc != LOLA_OK) return rc;
+    if (!q || !k || !v || !y || !alpha || !beta || !gamma_q || !gamma_k || !sink || !gate) return LOLA_EINVAL;
+    if (st->t >= (int64_t)INT_MAX) return LOLA_EUNSUPPORTED;   // positions are int32
+    lola::HolaDecodeArgs a;
+    a.BH = st->B * st->n_heads;
+    a.heads = st->n_heads;
+    a.C = st->C;
+    a.w = st->w;
+    a.nopen = (int)(st->t % st->C);
+    a.t = st->t;
+    a.q = q; a.k = k; a.v = v;
+    a.alpha = alpha; a.beta = beta;
+    a.gamma_q = gamma_q; a.gamma_k = gamma_k;
+    a.sink = sink; a.gate = gate;
+    a.y = y;
+    a.S = st->S;
+    a.cache_pos = st->cache_pos;
+    a.cache_score = st->cache_score;
+    a.cache_k = st->cache_k;
+    a.cache_v = st->cache_v;
+    a.open_k = st->open_k;
+    a.open_v = st->open_v;
+    a.open_score = st->open_score;
+    if (lola::launch_hola_decode(a, st->dtype, st->d, (hipStream_t)stream) != hipSuccess) return LOLA_EDEVICE;
+    if (getenv("LOLA_DEBUG_SYNC") && hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return LOLA_EDEVICE;
+    st->t += 1;
     return LOLA_OK;
 }
 

@@ -28,6 +28,8 @@
 //          cache and the chunk's tokens up to each query, with the sink as the initial state of the
 //          running softmax; QK^T and PV^T on MFMA with key blocks staged in LDS one block ahead; adds
 //          the state read-out.
+#include <algorithm>
+
 #include "lola_common.hpp"
 #include "lola_internal.hpp"
 
@@ -411,7 +413,7 @@ __global__ __launch_bounds__(64) void hola_cache_kernel(HolaArgs A) {
     const int bh = blockIdx.x, lane = threadIdx.x;
     const int n = A.n, C = A.C, w = A.w, nchunks = A.nchunks, ls = min(kHolaMaxW, C);
     const unsigned long long* tl = reinterpret_cast<const unsigned long long*>(A.ws + A.L.tlist) + (int64_t)bh * nchunks * ls;
-    int* clist = reinterpret_cast<int*>(A.ws + A.L.clist) + (int64_t)bh * nchunks * kHolaMaxW;
+    int* clist = reinterpret_cast<int*>(A.ws + A.L.clist) + (int64_t)bh * (nchunks + 1) * kHolaMaxW;
     auto count_of = [&](int ch) { return min(w, min(C, n - ch * C)); };
     unsigned long long rb[NB];
     auto fetch = [&](int c0) {
@@ -448,7 +450,8 @@ __global__ __launch_bounds__(64) void hola_cache_kernel(HolaArgs A) {
             ncur = min(w, ncur + nl);
         }
     }
-    // the final cache, sorted by position, with its magnitudes
+    // the final cache: in rank order after the chunk lists, and sorted by position with its magnitudes
+    clist[(int64_t)nchunks * kHolaMaxW + lane] = lane < ncur ? key_pos(sCur[cb][lane]) : -1;
     if (lane < ncur) {
         const unsigned long long x = sCur[cb][lane];
         const int p = key_pos(x);
@@ -486,7 +489,7 @@ __global__ __launch_bounds__(256) void hola_read_kernel(HolaArgs A) {
     const T* qtil = reinterpret_cast<const T*>(A.ws + A.L.qtil) + (int64_t)bh * n * D;
     const T* vin = reinterpret_cast<const T*>(A.v) + (int64_t)bh * n * D;
     const float* ost = reinterpret_cast<const float*>(A.ws + A.L.o) + (int64_t)bh * n * D;
-    const int* clist = reinterpret_cast<const int*>(A.ws + A.L.clist) + ((int64_t)bh * A.nchunks + ch) * kHolaMaxW;
+    const int* clist = reinterpret_cast<const int*>(A.ws + A.L.clist) + ((int64_t)bh * (A.nchunks + 1) + ch) * kHolaMaxW;
     for (int j = tid; j < kHolaMaxW; j += 256) sList[j] = clist[j];
     __syncthreads();
     int nA = 0;
@@ -630,6 +633,311 @@ __global__ __launch_bounds__(256) void hola_read_kernel(HolaArgs A) {
     }
 }
 
+// ---------------- decode memory after a prefill ----------------
+// The memory a decode step continues from: the persistent cache at the start of the open chunk (the
+// last chunk's list, or the final cache when the call ends on a chunk boundary), sorted by position,
+// with magnitudes formed as the ranking formed them, and the open chunk's tokens.  Keys and values are
+// copied raw (the cache path normalises them when it reads).  One workgroup per (sequence, head).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void hola_state_kernel(HolaArgs A) {
+    constexpr int NG = D / 16, EPV = 16 / (int)sizeof(T), PPR = D / EPV;
+    __shared__ int sPos[kHolaMaxW];
+    __shared__ int sIdx[kHolaMaxW];
+    const int bh = blockIdx.x, tid = threadIdx.x;
+    const int n = A.n, C = A.C, w = A.w, nchunks = A.nchunks;
+    const int nopen = n % C, cs = n - nopen;
+    const int* clist = reinterpret_cast<const int*>(A.ws + A.L.clist) +
+                       ((int64_t)bh * (nchunks + 1) + (nopen > 0 ? nchunks - 1 : nchunks)) * kHolaMaxW;
+    const float* esq = reinterpret_cast<const float*>(A.ws + A.L.esq) + (int64_t)bh * n * NG;
+    const float* beta = A.beta + (int64_t)bh * n;
+    auto mag = [&](int p) {                       // as the chunk ranking forms it
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < NG; ++j) ss += esq[(int64_t)p * NG + j];
+        return beta[p] * sqrtf(ss);
+    };
+    if (tid < kHolaMaxW) sPos[tid] = tid < w ? clist[tid] : -1;
+    __syncthreads();
+    if (tid < w) {                                // valid entries come first in rank order
+        const int p = sPos[tid];
+        int idx = tid;
+        if (p >= 0) {
+            idx = 0;
+            for (int j = 0; j < w; ++j) idx += (sPos[j] >= 0 && sPos[j] < p) ? 1 : 0;
+        }
+        sIdx[tid] = idx;
+        A.st_cache_pos[(int64_t)bh * w + idx] = p;
+        A.st_cache_score[(int64_t)bh * w + idx] = p >= 0 ? mag(p) : 0.f;
+    }
+    __syncthreads();
+    const T* kin = reinterpret_cast<const T*>(A.k) + (int64_t)bh * n * D;
+    const T* vin = reinterpret_cast<const T*>(A.v) + (int64_t)bh * n * D;
+    T* ck = reinterpret_cast<T*>(A.st_cache_k) + (int64_t)bh * w * D;
+    T* cv = reinterpret_cast<T*>(A.st_cache_v) + (int64_t)bh * w * D;
+    for (int it = tid; it < w * PPR; it += 256) {
+        const int e = it / PPR, pc = it % PPR, p = sPos[e];
+        if (p >= 0) {
+            const int idx = sIdx[e];
+            *reinterpret_cast<uint4*>(ck + (int64_t)idx * D + pc * EPV) = *reinterpret_cast<const uint4*>(kin + (int64_t)p * D + pc * EPV);
+            *reinterpret_cast<uint4*>(cv + (int64_t)idx * D + pc * EPV) = *reinterpret_cast<const uint4*>(vin + (int64_t)p * D + pc * EPV);
+        }
+    }
+    T* ok = reinterpret_cast<T*>(A.st_open_k) + (int64_t)bh * C * D;
+    T* ov = reinterpret_cast<T*>(A.st_open_v) + (int64_t)bh * C * D;
+    for (int it = tid; it < nopen * PPR; it += 256) {
+        const int i = it / PPR, pc = it % PPR;
+        *reinterpret_cast<uint4*>(ok + (int64_t)i * D + pc * EPV) = *reinterpret_cast<const uint4*>(kin + (int64_t)(cs + i) * D + pc * EPV);
+        *reinterpret_cast<uint4*>(ov + (int64_t)i * D + pc * EPV) = *reinterpret_cast<const uint4*>(vin + (int64_t)(cs + i) * D + pc * EPV);
+    }
+    for (int i = tid; i < nopen; i += 256) A.st_open_score[(int64_t)bh * C + i] = mag(cs + i);
+}
+
+// ---------------- decode ----------------
+// Sum over a workgroup of NT threads (every thread gets it); red holds NT / 64 floats.
+template <int NT>
+__device__ __forceinline__ float block_sum(float x, float* red) {
+    x = wave_sum(x);
+    __syncthreads();                              // red is free (its previous use is complete)
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+    __syncthreads();
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) t += red[i];
+    return t;
+}
+template <int NT>
+__device__ __forceinline__ float block_max(float x, float* red) {
+    x = wave_max(x);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+    __syncthreads();
+    float t = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) t = fmaxf(t, red[i]);
+    return t;
+}
+
+// One token for every (sequence, head): one workgroup of 4D threads, thread (row group rg, column j)
+// holding rows rg D/4 .. + D/4 - 1 of column j of S in registers.
+//   1. unit-norm q, k for the state, the RMS-normalised, gamma-scaled query of the cache path;
+//   2. S^T k and S^T q in one pass over S; e = v - alpha S^T k, m = beta |e|,
+//      S <- alpha S + beta k e^T (written back), o = S_new^T q = alpha S^T q + beta (k.q) e;
+//   3. the cache path over the persistent cache, the open chunk's earlier tokens and the token, with
+//      the sink: logits by 16-lane groups, one row each, then the weighted sum of the value rows;
+//   4. y = o + sigmoid(gate) * read-out; the token joins the open chunk; a token that closes its chunk
+//      merges the chunk into the cache (top w by magnitude, ties to the older, sorted by position).
+template <typename T, int D>
+__global__ __launch_bounds__(4 * D) void hola_decode_kernel(HolaDecodeArgs A) {
+    constexpr int NT = 4 * D, R = D / 4, NG16 = NT / 16, EPL = D / 16;
+    constexpr int EPV = 16 / (int)sizeof(T), PPR = D / EPV;
+    constexpr int MAXE = kHolaMaxW + kHolaMaxC;
+    __shared__ float sQ[D], sK[D], sKr[D], sV[D], sU[D], sE[D];
+    __shared__ float sPart[2][4][D];
+    __shared__ float sRed[NT / 64];
+    __shared__ float sLg[MAXE];
+    __shared__ unsigned long long sKey[MAXE];
+    __shared__ int sKeep[kHolaMaxW];              // kept candidates in position order
+    const int bh = blockIdx.x, tid = threadIdx.x, head = bh % A.heads;
+    const int w = A.w, C = A.C, nopen = A.nopen;
+    const int j = tid % D, rg = tid / D;
+    const float alpha = A.alpha[bh], beta = A.beta[bh];
+
+    // 1. the token
+    float qx = 0.f, kx = 0.f;
+    if (tid < D) {
+        qx = to_f(reinterpret_cast<const T*>(A.q)[(int64_t)bh * D + tid]);
+        kx = to_f(reinterpret_cast<const T*>(A.k)[(int64_t)bh * D + tid]);
+        sV[tid] = to_f(reinterpret_cast<const T*>(A.v)[(int64_t)bh * D + tid]);
+        sKr[tid] = kx;
+    }
+    const float qq = block_sum<NT>(qx * qx, sRed);
+    const float kk = block_sum<NT>(kx * kx, sRed);
+    const float kq = block_sum<NT>(kx * qx, sRed);
+    const float iq = qq > 0.f ? 1.0f / sqrtf(qq) : 0.f, ik = kk > 0.f ? 1.0f / sqrtf(kk) : 0.f;
+    if (tid < D) {
+        sQ[tid] = qx * iq;
+        sK[tid] = kx * ik;
+        const float qt = A.gamma_q[(int64_t)head * D + tid] * qx * (1.0f / sqrtf(qq / (float)D + kHolaRmsEps));
+        sU[tid] = A.gamma_k[(int64_t)head * D + tid] * qt * (1.0f / sqrtf((float)D));
+    }
+    __syncthreads();
+
+    // 2. the state (held in registers up to d = 128; read again for the update at d = 256)
+    constexpr bool KEEP = R <= 32;
+    float* Sg = A.S + (int64_t)bh * D * D;
+    float sr[KEEP ? R : 1];
+    float pk = 0.f, pq = 0.f;
+#pragma unroll 16
+    for (int r = 0; r < R; ++r) {
+        const int i = rg * R + r;
+        const float sv = Sg[(int64_t)i * D + j];
+        if (KEEP) sr[r] = sv;
+        pk += sv * sK[i];
+        pq += sv * sQ[i];
+    }
+    sPart[0][rg][j] = pk;
+    sPart[1][rg][j] = pq;
+    __syncthreads();
+    float e = 0.f, o = 0.f;
+    if (tid < D) {
+        const float stk = (sPart[0][0][j] + sPart[0][1][j]) + (sPart[0][2][j] + sPart[0][3][j]);
+        const float stq = (sPart[1][0][j] + sPart[1][1][j]) + (sPart[1][2][j] + sPart[1][3][j]);
+        e = sV[j] - alpha * stk;
+        o = alpha * stq + beta * (kq * iq * ik) * e;
+        sE[j] = e;
+    }
+    const float m = beta * sqrtf(block_sum<NT>(e * e, sRed));   // its barriers also publish sE
+#pragma unroll 16
+    for (int r = 0; r < R; ++r) {
+        const int i = rg * R + r;
+        const float sv = KEEP ? sr[KEEP ? r : 0] : Sg[(int64_t)i * D + j];
+        Sg[(int64_t)i * D + j] = alpha * sv + beta * sK[i] * sE[j];
+    }
+
+    // 3. the cache path: entries = cache (valid slots first), open tokens, the token
+    const int* cpos = A.cache_pos + (int64_t)bh * w;
+    int nv = 0;
+    for (int i = 0; i < w; ++i) nv += cpos[i] >= 0 ? 1 : 0;
+    const int NE = nv + nopen + 1;
+    const T* ck = reinterpret_cast<const T*>(A.cache_k) + (int64_t)bh * w * D;
+    const T* cvv = reinterpret_cast<const T*>(A.cache_v) + (int64_t)bh * w * D;
+    T* okp = reinterpret_cast<T*>(A.open_k) + (int64_t)bh * C * D;
+    T* ovp = reinterpret_cast<T*>(A.open_v) + (int64_t)bh * C * D;
+    {
+        const int grp = tid >> 4, gl = tid & 15;
+        for (int en = grp; en < NE; en += NG16) {
+            float dot = 0.f, ss = 0.f;
+            if (en < nv + nopen) {
+                const T* kr = en < nv ? ck + (int64_t)en * D : okp + (int64_t)(en - nv) * D;
+#pragma unroll
+                for (int x = 0; x < EPL; ++x) {
+                    const float kv = to_f(kr[gl * EPL + x]);
+                    dot += kv * sU[gl * EPL + x];
+                    ss += kv * kv;
+                }
+            } else {
+#pragma unroll
+                for (int x = 0; x < EPL; ++x) {
+                    const float kv = sKr[gl * EPL + x];
+                    dot += kv * sU[gl * EPL + x];
+                    ss += kv * kv;
+                }
+            }
+#pragma unroll
+            for (int sh = 8; sh >= 1; sh >>= 1) {
+                dot += __shfl_xor(dot, sh, 16);
+                ss += __shfl_xor(ss, sh, 16);
+            }
+            if (gl == 0) sLg[en] = dot / sqrtf(ss / (float)D + kHolaRmsEps);
+        }
+    }
+    __syncthreads();
+    const float sink = A.sink[head];
+    float lmax = -INFINITY;
+    for (int en = tid; en < NE; en += NT) lmax = fmaxf(lmax, sLg[en]);
+    const float mx = fmaxf(block_max<NT>(lmax, sRed), sink);
+    float psum = 0.f;
+    for (int en = tid; en < NE; en += NT) {
+        const float p = expf(sLg[en] - mx);
+        sLg[en] = p;
+        psum += p;
+    }
+    const float den = block_sum<NT>(psum, sRed) + expf(sink - mx);   // its barriers also publish sLg
+    float acc = 0.f;
+    for (int en = rg; en < NE; en += 4) {
+        float vv;
+        if (en < nv) vv = to_f(cvv[(int64_t)en * D + j]);
+        else if (en < nv + nopen) vv = to_f(ovp[(int64_t)(en - nv) * D + j]);
+        else vv = sV[j];
+        acc += sLg[en] * vv;
+    }
+    __syncthreads();                              // sPart is free
+    sPart[0][rg][j] = acc;
+    __syncthreads();
+
+    // 4. output, the open chunk, the chunk close
+    if (tid < D) {
+        const float rd = ((sPart[0][0][j] + sPart[0][1][j]) + (sPart[0][2][j] + sPart[0][3][j])) / den;
+        const float gsig = 1.0f / (1.0f + expf(-A.gate[head]));
+        reinterpret_cast<T*>(A.y)[(int64_t)bh * D + j] = from_f<T>(o + gsig * rd);
+        okp[(int64_t)nopen * D + j] = from_f<T>(sKr[j]);
+        ovp[(int64_t)nopen * D + j] = from_f<T>(sV[j]);
+    }
+    if (tid == 0) A.open_score[(int64_t)bh * C + nopen] = m;
+    if (nopen + 1 < C || w == 0) return;           // uniform: the chunk stays open, or nothing is kept
+
+    __syncthreads();                              // the token's row and magnitude are written
+    const int N = nv + nopen + 1;
+    const int64_t cs = A.t - nopen;               // first position of the closing chunk
+    float* cscore = A.cache_score + (int64_t)bh * w;
+    const float* oscore = A.open_score + (int64_t)bh * C;
+    for (int c = tid; c < N; c += NT)
+        sKey[c] = c < nv ? hola_key(cscore[c], cpos[c]) : hola_key(oscore[c - nv], (int)(cs + (c - nv)));
+    __syncthreads();
+    const int keep = min(w, N);
+    for (int c = tid; c < N; c += NT) {
+        const unsigned long long kc = sKey[c];
+        int above = 0;
+        for (int c2 = 0; c2 < N; ++c2) above += sKey[c2] > kc ? 1 : 0;
+        sLg[c] = above < keep ? 1.f : 0.f;        // kept flag
+    }
+    __syncthreads();
+    // kept candidates in position order: cache entries come before open ones and are sorted already
+    for (int c = tid; c < N; c += NT)
+        if (sLg[c] != 0.f) {
+            int idx = 0;
+            for (int c2 = 0; c2 < c; ++c2) idx += sLg[c2] != 0.f ? 1 : 0;
+            sKeep[idx] = c;
+        }
+    __syncthreads();
+    // rows: every source piece is read before any slot is written (a kept cache entry moves down)
+    constexpr int NP = (kHolaMaxW * PPR * 2 + NT - 1) / NT;
+    uint4 buf[NP];
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+        const int it = tid + u * NT;              // over [keep][k, v][PPR]
+        buf[u] = make_uint4(0u, 0u, 0u, 0u);
+        if (it < keep * 2 * PPR) {
+            const int slot = it / (2 * PPR), which = (it / PPR) & 1, pc = it % PPR;
+            const int c = sKeep[slot];
+            const T* src = c < nv ? (which ? cvv : ck) + (int64_t)c * D : (which ? ovp : okp) + (int64_t)(c - nv) * D;
+            buf[u] = *reinterpret_cast<const uint4*>(src + pc * EPV);
+        }
+    }
+    int newpos = -1;
+    float newscore = 0.f;
+    if (tid < keep) {
+        const int c = sKeep[tid];
+        newpos = c < nv ? cpos[c] : (int)(cs + (c - nv));
+        newscore = c < nv ? cscore[c] : oscore[c - nv];
+    }
+    __syncthreads();
+    T* ckw = reinterpret_cast<T*>(A.cache_k) + (int64_t)bh * w * D;
+    T* cvw = reinterpret_cast<T*>(A.cache_v) + (int64_t)bh * w * D;
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+        const int it = tid + u * NT;
+        if (it < keep * 2 * PPR) {
+            const int slot = it / (2 * PPR), which = (it / PPR) & 1, pc = it % PPR;
+            *reinterpret_cast<uint4*>((which ? cvw : ckw) + (int64_t)slot * D + pc * EPV) = buf[u];
+        }
+    }
+    if (tid < w) {
+        A.cache_pos[(int64_t)bh * w + tid] = tid < keep ? newpos : -1;
+        cscore[tid] = tid < keep ? newscore : 0.f;
+    }
+}
+
+// An empty memory: S = 0, every cache slot empty.
+__global__ __launch_bounds__(256) void hola_init_kernel(HolaInitArgs A) {
+    const int64_t nS = (int64_t)A.BH * A.d * A.d, nc = (int64_t)A.BH * A.w;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nS; i += (int64_t)gridDim.x * 256) A.S[i] = 0.f;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nc; i += (int64_t)gridDim.x * 256) {
+        A.cache_pos[i] = -1;
+        A.cache_score[i] = 0.f;
+    }
+}
+
 template <typename T, int D>
 hipError_t launch_hola_t(const HolaArgs& a, hipStream_t stream) {
     const int64_t rows = (int64_t)a.BH * a.n;
@@ -653,10 +961,36 @@ hipError_t launch_hola_t(const HolaArgs& a, hipStream_t stream) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((hola_read_kernel<T, D>), dim3((unsigned)((int64_t)a.BH * a.nchunks * a.nqt)), dim3(256), 0,
                        stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (a.st_open_k) {
+        hipLaunchKernelGGL((hola_state_kernel<T, D>), dim3(a.BH), dim3(256), 0, stream, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+template <typename T, int D>
+hipError_t launch_hola_decode_t(const HolaDecodeArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL((hola_decode_kernel<T, D>), dim3(a.BH), dim3(4 * D), 0, stream, a);
     return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t launch_hola_decode(const HolaDecodeArgs& a, int dtype, int d, hipStream_t stream) {
+    if (dtype == 0)
+        return d == 64 ? launch_hola_decode_t<float, 64>(a, stream)
+                       : d == 128 ? launch_hola_decode_t<float, 128>(a, stream) : launch_hola_decode_t<float, 256>(a, stream);
+    return d == 64 ? launch_hola_decode_t<bf16, 64>(a, stream)
+                   : d == 128 ? launch_hola_decode_t<bf16, 128>(a, stream) : launch_hola_decode_t<bf16, 256>(a, stream);
+}
+
+hipError_t launch_hola_init(const HolaInitArgs& a, hipStream_t stream) {
+    const int64_t tot = (int64_t)a.BH * a.d * a.d;
+    const unsigned grid = (unsigned)std::min<int64_t>(2048, (tot + 255) / 256);
+    hipLaunchKernelGGL(hola_init_kernel, dim3(grid > 0 ? grid : 1), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_hola(const HolaArgs& a, int dtype, int d, hipStream_t stream) {
     if (dtype == 0)

@@ -123,7 +123,8 @@ struct HolaLayout {               // byte offsets of whole arrays in the workspa
     int64_t qtil, ktil;           // [BH][n][d] T   : RMS-normalised, gamma-scaled queries and keys
     int64_t o;                    // [BH][n][d] fp32: state read-out S_t^T q_t
     int64_t esq;                  // [BH][n][d / 16] fp32: sum of e_t^2 over each group of 16 value columns
-    int64_t clist;                // [BH][nchunks][kHolaMaxW] int32: persistent cache at each chunk start
+    int64_t clist;                // [BH][nchunks + 1][kHolaMaxW] int32: persistent cache at each chunk start,
+                                  // then after the last chunk (rank order)
     int64_t blk;                  // [BH][ceil(n / 16)] HolaBlock: the delta rule's per-block matrices
     int64_t sink;                 // [2][64] fp32: where the scan's stores for tokens past n go
     int64_t tlist;                // [BH][nchunks][min(kHolaMaxW, C)] u64: each chunk's own top-w ranking
@@ -162,7 +163,47 @@ struct HolaArgs {
     float* cache_score_out;       // nullable [BH][w]
     char* ws;
     HolaLayout L;
+    // nullable: the decode memory after the call (the persistent cache at the start of the open chunk,
+    // sorted by position, and the open chunk's tokens; the state itself goes to S_out)
+    int32_t* st_cache_pos;        // [BH][w]
+    float* st_cache_score;        // [BH][w]
+    void* st_cache_k;             // [BH][w][d]
+    void* st_cache_v;
+    void* st_open_k;              // [BH][C][d]
+    void* st_open_v;
+    float* st_open_score;         // [BH][C]
 };
+// One decode step of the HOLA memory for every (sequence, head).
+struct HolaDecodeArgs {
+    int BH, heads, C, w, nopen;   // nopen = t mod C: the open chunk's tokens before this one
+    int64_t t;
+    const void* q;                // [BH][d]
+    const void* k;
+    const void* v;
+    const float* alpha;           // [BH]
+    const float* beta;
+    const float* gamma_q;         // [heads][d]
+    const float* gamma_k;
+    const float* sink;            // [heads]
+    const float* gate;
+    void* y;                      // [BH][d]
+    float* S;                     // [BH][d][d]
+    int32_t* cache_pos;           // [BH][w]
+    float* cache_score;
+    void* cache_k;                // [BH][w][d]
+    void* cache_v;
+    void* open_k;                 // [BH][C][d]
+    void* open_v;
+    float* open_score;            // [BH][C]
+};
+hipError_t launch_hola_decode(const HolaDecodeArgs& a, int dtype, int d, hipStream_t stream);
+struct HolaInitArgs {
+    int BH, d, w;
+    float* S;
+    int32_t* cache_pos;
+    float* cache_score;
+};
+hipError_t launch_hola_init(const HolaInitArgs& a, hipStream_t stream);
 int device_cus();   // compute units of the current device, queried per call (256 if the query fails)
 hipError_t launch_hola(const HolaArgs& a, int dtype, int d, hipStream_t stream);
 

@@ -287,6 +287,53 @@ lola_status hola_prefill(int32_t B, int32_t n_heads, int32_t d, int32_t dtype, i
                          void *y, float *S_out, int32_t *cache_pos_out, float *cache_score_out,
                          void *workspace, size_t workspace_bytes, void *stream);
 
+/* HOLA decode (the same notes, part 2: 3.5 sizes one head's runtime memory as the state plus at most
+ * w + C exact key-value rows).  Decode keeps the prefill's chunk grid (chunks of C positions from
+ * position 0).  Between tokens the memory of a (sequence, head) is the state S, the persistent cache
+ * at the start of the open chunk and the open chunk's tokens so far; a token that closes its chunk
+ * merges the chunk into the cache (the w largest magnitudes, ties: the older; sorted by position).
+ * Buffers are device memory owned by the caller, rows 16-byte aligned:
+ *   S            [B][n_heads][d][d]  fp32   row = key dimension
+ *   cache_pos    [B][n_heads][w]     int32  positions, ascending, then -1 for empty slots
+ *   cache_score  [B][n_heads][w]     fp32   their write magnitudes (0 for empty slots)
+ *   cache_k, cache_v [B][n_heads][w][d] dtype  raw keys and values of the cached tokens
+ *   open_k, open_v   [B][n_heads][C][d] dtype  the open chunk's tokens (t mod C of them)
+ *   open_score   [B][n_heads][C]     fp32   their magnitudes
+ * The cache_* pointers may be NULL when w == 0.  t (host) counts the tokens seen; C and w are fixed
+ * for the state's life. */
+typedef struct hola_state {
+    int32_t B, n_heads, d, dtype, C, w;
+    int64_t t;
+    float *S;
+    int32_t *cache_pos;
+    float *cache_score;
+    void *cache_k, *cache_v;
+    void *open_k, *open_v;
+    float *open_score;
+} hola_state;
+
+/* An empty memory: t = 0, S = 0, every cache slot empty (enqueued on stream).  LOLA_EINVAL for a
+ * malformed state, LOLA_EUNSUPPORTED for sizes hola_prefill does not take. */
+lola_status hola_state_init(hola_state *st, void *stream);
+
+/* hola_prefill over n tokens from the empty memory st (st->t must be 0: LOLA_EUNSUPPORTED otherwise),
+ * with B, n_heads, d, dtype, C, w taken from st; also leaves the decode memory in st (S, the cache at
+ * the start of the open chunk, the open chunk's tokens) and sets st->t = n.  Other arguments and the
+ * workspace (hola_workspace_bytes with st's sizes) as for hola_prefill. */
+lola_status hola_prefill_state(hola_state *st, int64_t n, const void *q, const void *k, const void *v,
+                               const float *alpha, const float *beta, const float *gamma_q, const float *gamma_k,
+                               const float *sink, const float *gate, void *y, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/* One decode token for every (sequence, head) of st: q, k, v, y [B][n_heads][d] in st->dtype; alpha,
+ * beta [B][n_heads] fp32; gamma_q, gamma_k [n_heads][d], sink, gate [n_heads] fp32 (all device).
+ * The token is written into the state, read out by y_t = S_t^T q^_t + sigmoid(gate) * (softmax over
+ * the cache, the open chunk's earlier tokens, the token itself and the sink), joins the open chunk,
+ * and st->t advances by one.  No workspace; one kernel on stream. */
+lola_status hola_decode_step(hola_state *st, const void *q, const void *k, const void *v, const float *alpha,
+                             const float *beta, const float *gamma_q, const float *gamma_k, const float *sink,
+                             const float *gate, void *y, void *stream);
+
 /* ---------------------------------------------------------------------------------------------
  * Measurement probes (not part of the method): the device's attainable rates, measured beside the
  * vendor's peaks so that roofline fractions can be stated against both.

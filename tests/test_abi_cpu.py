@@ -152,6 +152,44 @@ def test_hola_pointer_validation_without_gpu(lib):
                             None, None, None, None, None, None, 0, None) == B.LOLA_OK
 
 
+def _hola_state(**over):
+    p = 0x300000
+    f = dict(B=1, n_heads=2, d=128, dtype=B.LOLA_BF16, C=16, w=4, t=0, S=p, cache_pos=p, cache_score=p, cache_k=p,
+             cache_v=p, open_k=p, open_v=p, open_score=p)
+    f.update(over)
+    return B.HolaState(*(f[name] for name, _ in B.HolaState._fields_))
+
+
+def test_hola_state_validation_without_gpu(lib):
+    """hola_state_init / hola_prefill_state / hola_decode_step reject a malformed state, a prefill from a
+    non-empty memory and missing token arrays before anything is queued."""
+    bad = [dict(d=96), dict(C=0), dict(C=2048), dict(w=-1), dict(w=65), dict(S=None), dict(open_k=None),
+           dict(open_score=None), dict(open_v=0x300002), dict(cache_k=None), dict(cache_pos=None), dict(B=0)]
+    want = [B.LOLA_EUNSUPPORTED, B.LOLA_EINVAL, B.LOLA_EUNSUPPORTED, B.LOLA_EINVAL, B.LOLA_EUNSUPPORTED,
+            B.LOLA_EINVAL, B.LOLA_EINVAL, B.LOLA_EINVAL, B.LOLA_EINVAL, B.LOLA_EINVAL, B.LOLA_EINVAL, B.LOLA_EINVAL]
+    for over, w_ in zip(bad, want):
+        st = _hola_state(**over)
+        assert lib.hola_state_init(ctypes.byref(st), None) == w_, over
+    # w == 0 needs no cache arrays; a prefill needs an empty memory
+    p = 0x300000
+    st = _hola_state(w=0, cache_pos=None, cache_score=None, cache_k=None, cache_v=None, t=5)
+    assert lib.hola_prefill_state(ctypes.byref(st), 64, p, p, p, p, p, p, p, p, p, p, 0x400000, 1 << 40,
+                                  None) == B.LOLA_EUNSUPPORTED
+    st = _hola_state()
+    assert lib.hola_prefill_state(ctypes.byref(st), -1, p, p, p, p, p, p, p, p, p, p, 0x400000, 1 << 40,
+                                  None) == B.LOLA_EINVAL
+    assert lib.hola_prefill_state(ctypes.byref(st), 64, p, p, p, p, p, p, p, p, p, p, 0x400010, 1 << 40,
+                                  None) == B.LOLA_EINVAL
+    assert lib.hola_prefill_state(ctypes.byref(st), 0, None, None, None, None, None, None, None, None, None,
+                                  None, None, 0, None) == B.LOLA_OK and st.t == 0
+    args = [p] * 10
+    for i in range(10):
+        a = list(args)
+        a[i] = None
+        assert lib.hola_decode_step(ctypes.byref(st), *a, None) == B.LOLA_EINVAL, i
+    assert st.t == 0
+
+
 def test_overlap_validation_without_gpu(lib):
     """An overlap block needs a stream that is not the call's and all of its events; a bad block is
     rejected before anything is queued (the library owns no stream of its own to fall back on)."""

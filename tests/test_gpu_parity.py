@@ -700,6 +700,75 @@ def test_hola_prefill(seed, kw, dtype):
     assert worst <= tol
 
 
+# HOLA decode (hola_prefill_state then hola_decode_step): every output of the prefill part and of each
+# decode step against the oracle's prefill over the whole sequence, then the memory after the last step.
+HOLA_DECODE_CASES = [
+    (110, dict(n0=300, steps=40, C=64, w=16, d=64)),    # a chunk closes during the decode
+    (111, dict(n0=256, steps=20, C=256, w=64, d=128)),  # the prefill ends on a chunk boundary
+    (112, dict(n0=50, steps=34, C=16, w=8, d=128)),     # several closes
+    (113, dict(n0=0, steps=40, C=8, w=4, d=64)),        # decode from the empty memory
+    (114, dict(n0=100, steps=12, C=1, w=8, d=64)),      # every token closes its chunk
+    (115, dict(n0=60, steps=10, C=32, w=0, d=64)),      # no persistent cache
+    (116, dict(n0=300, steps=20, C=64, w=16, d=256)),   # the page's head dimension
+]
+
+
+@pytest.mark.parametrize("seed,kw", HOLA_DECODE_CASES, ids=[f"s{s}" for s, _ in HOLA_DECODE_CASES])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_hola_prefill_then_decode(seed, kw, dtype):
+    import hybrid_linear_attention_chunkwise_amd as lola
+    from oracle import hola_oracle as HO
+    B, h = 1, 2
+    n0, steps, C, w, d = kw["n0"], kw["steps"], kw["C"], kw["w"], kw["d"]
+    n = n0 + steps
+    q, k, v, alpha, beta, gq, gk, sink, gate = _hola_inputs(seed, B, h, n, d, dtype)
+    dev = torch.device("cuda:0")
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    T = lambda x, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(dt)
+    st = lola.HolaState(B, h, d, C, w, tdt, device=dev)
+    lola.hola_state_init(st)
+    print(f"[hola decode] n0={n0} steps={steps} C={C} w={w} d={d} {dtype}", flush=True)
+    ys = []
+    if n0 > 0:
+        ys.append(lola.hola_prefill_state(st, T(q[:, :, :n0], tdt), T(k[:, :, :n0], tdt), T(v[:, :, :n0], tdt),
+                                          T(alpha[:, :, :n0]), T(beta[:, :, :n0]), T(gq), T(gk), T(sink), T(gate)))
+    assert st.t == n0
+    G = (T(gq), T(gk), T(sink), T(gate))
+    for t in range(n0, n):
+        yt = lola.hola_decode_step(st, T(q[:, :, t], tdt), T(k[:, :, t], tdt), T(v[:, :, t], tdt), T(alpha[:, :, t]),
+                                   T(beta[:, :, t]), *G)
+        ys.append(yt.unsqueeze(2))
+    torch.cuda.synchronize()
+    assert st.t == n
+    y = torch.cat(ys, dim=2).float().cpu().numpy()
+    S = st.S.cpu().numpy()
+    cpos = st.cache_pos.cpu().numpy()
+    ocnt = n % C
+    tol = TL.FP32_TOL if dtype == "f32" else TL.BF16_TOL
+    worst = 0.0
+    for hh in range(h):
+        y_o, S_o, cache_o, m_o, _ = HO.hola_prefill(q[0, hh], k[0, hh], v[0, hh], alpha[0, hh], beta[0, hh],
+                                                     gq[hh], gk[hh], float(sink[hh]), float(gate[hh]), C, w)
+        worst = max(worst, TL.row_rel_err(y[0, hh], y_o))
+        scale = max(1.0, float(np.abs(S_o).max()))
+        assert np.abs(S[0, hh] - S_o).max() <= 1e-4 * scale, f"head {hh}: state differs"
+        want = HO.persistent_cache(m_o, n - ocnt, w)
+        got = [int(p) for p in cpos[0, hh][:w] if p >= 0]
+        assert got == want, f"head {hh}: cache at the open chunk's start differs"
+        if w > 0:
+            assert all(p < 0 for p in cpos[0, hh][len(want):w])
+            np.testing.assert_allclose(st.cache_score[0, hh][:len(want)].cpu().numpy(), m_o[want],
+                                       rtol=1e-4 if dtype == "f32" else 2e-2)
+            kc = st.cache_k[0, hh][:len(want)].float().cpu().numpy()
+            np.testing.assert_array_equal(kc, k[0, hh][want])
+        if ocnt:
+            np.testing.assert_array_equal(st.open_v[0, hh][:ocnt].float().cpu().numpy(), v[0, hh][n - ocnt:n])
+            np.testing.assert_allclose(st.open_score[0, hh][:ocnt].cpu().numpy(), m_o[n - ocnt:n],
+                                       rtol=1e-4 if dtype == "f32" else 2e-2, atol=1e-6)
+    print(f"[hola decode] max output err {worst:.3e}", flush=True)
+    assert worst <= tol
+
+
 # The delta rule runs in blocks of 16 tokens: per-block matrices from all blocks in parallel, then one
 # workgroup per (sequence, head, 16 value columns) walks the blocks.  These cases cover many heads at
 # both d, ragged last blocks, and (alpha in [0.05, 0.3]) decay products that underflow within a block.
