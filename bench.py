@@ -321,6 +321,63 @@ def bench_hola(args, lola, torch, B, h, n, d):
                          "frac": round(ach / PEAK_FP32_MFMA_TFLOPS, 5), "algorithmic_flop_per_call": flop}}
 
 
+def bench_hola_decode(args, lola, torch, B, h, n0, d, steps=64, runs=3):
+    """HOLA decode (hola_decode_step) after an untimed hola_prefill_state of n0 tokens, with the page's
+    w = 64 and C = 256, bf16: each run restores the post-prefill memory (untimed) and times `steps`
+    single-token steps with HIP events on the calling stream.  HBM-bound: per (sequence, head, step) the
+    step reads and writes the fp32 state (8 d^2 bytes), reads the cached rows and the open chunk's rows
+    (keys and values) and the token, writes y and the token's open row."""
+    import numpy as np
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(21)
+    bf = torch.bfloat16
+    mk = lambda *shape: torch.from_numpy(rng.standard_normal(shape).astype(np.float32)).to(dev).to(bf)
+    q, k, v = mk(B, h, n0, d), mk(B, h, n0, d), mk(B, h, n0, d)
+    alpha = torch.from_numpy(rng.uniform(0.9, 1.0, (B, h, n0)).astype(np.float32)).to(dev)
+    beta = torch.from_numpy(rng.uniform(0.0, 1.0, (B, h, n0)).astype(np.float32)).to(dev)
+    gq = torch.from_numpy(rng.uniform(0.5, 1.5, (h, d)).astype(np.float32)).to(dev)
+    gk = torch.from_numpy(rng.uniform(0.5, 1.5, (h, d)).astype(np.float32)).to(dev)
+    sink = torch.zeros(h, device=dev)
+    gate = torch.full((h,), -4.0, device=dev)
+    tq, tk, tv = mk(steps, B, h, d), mk(steps, B, h, d), mk(steps, B, h, d)
+    ta = torch.from_numpy(rng.uniform(0.9, 1.0, (steps, B, h)).astype(np.float32)).to(dev)
+    tb = torch.from_numpy(rng.uniform(0.0, 1.0, (steps, B, h)).astype(np.float32)).to(dev)
+    st = lola.HolaState(B, h, d, HOLA_C, HOLA_W, bf, device=dev)
+    lola.hola_state_init(st)
+    lola.hola_prefill_state(st, q, k, v, alpha, beta, gq, gk, sink, gate)
+    torch.cuda.synchronize()
+    del q, k, v, alpha, beta
+    names = ("S", "cache_pos", "cache_score", "cache_k", "cache_v", "open_k", "open_v", "open_score")
+    snap = {nm: getattr(st, nm).clone() for nm in names}
+    y = torch.empty(B, h, d, dtype=bf, device=dev)
+    times = []
+    for r in range(runs + 1):
+        for nm in names:
+            getattr(st, nm).copy_(snap[nm])
+        st.c.t = n0
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            lola.hola_decode_step(st, tq[i], tk[i], tv[i], ta[i], tb[i], gq, gk, sink, gate, y=y)
+        e1.record()
+        torch.cuda.synchronize()
+        if r > 0:                                             # the first run warms up
+            times.append(e0.elapsed_time(e1) / steps)
+    ms = float(np.median(times))
+    nopen_avg = n0 % HOLA_C + (steps - 1) / 2.0
+    nv = min(HOLA_W, n0 - n0 % HOLA_C)
+    per = 8 * d * d + (nv + nopen_avg) * 2 * d * 2 + 6 * d * 2 + 8 * d + 32
+    byts = per * B * h
+    ach = byts / (ms * 1e-3) / 1e9
+    log(f"hola decode: {ms:.4f} ms/step")
+    return {"workload": f"hola_decode_b{B}_h{h}_ctx{n0}_d{d}_w{HOLA_W}_C{HOLA_C}_bf16", "ms_per_step": round(ms, 4),
+            "tokens_per_s": round(B / (ms * 1e-3), 1), "steps": steps,
+            "roofline": {"bound": "hbm", "kernel": "hola_decode", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                         "algorithmic_bytes_per_step": round(byts)}}
+
+
 def bench_decode(args, lola, torch, wl):
     """256 single-token decode steps of every (sequence, head) after the untimed prior context; each run
     restores the same post-prefill snapshot (untimed) and times the steps with HIP events on the caller's
@@ -526,6 +583,7 @@ def main() -> int:
     ap.add_argument("--no-options", action="store_true")
     ap.add_argument("--no-hola", action="store_true")
     ap.add_argument("--no-peaks", action="store_true")
+    ap.add_argument("--only-hola", action="store_true", help="only the HOLA legs (prefill, d = 256, decode)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -553,6 +611,13 @@ def main() -> int:
         print(json.dumps({"copy_calibration_bytes": n * 4}))
         return 0
     src_hash = kernel_source_hash()
+    if args.only_hola:
+        hw = CONFIGS[2]
+        r = bench_hola(args, lola, torch, hw.B, hw.h, hw.n, hw.d_k)
+        r["d256"] = bench_hola(args, lola, torch, 1, 4, hw.n, 256)
+        r["decode"] = bench_hola_decode(args, lola, torch, 32, hw.h, 4196, hw.d_k)
+        print(json.dumps({"hola": r}))
+        return 0
     if args.no_prefill:        # profiling mode: the decode workload only
         dwl = CONFIGS[4]
         r = bench_decode(args, lola, torch, dwl)
@@ -620,6 +685,8 @@ def main() -> int:
         out["hola"] = bench_hola(leg_args, lola, torch, hw.B, hw.h, hw.n, hw.d_k)
         # the HOLA page's own setup: 4 heads of dimension 256
         out["hola"]["d256"] = bench_hola(leg_args, lola, torch, 1, 4, hw.n, 256)
+        # decode after a 4196-token prefill (an open chunk of 100 tokens), 32 sequences x 32 heads
+        out["hola"]["decode"] = bench_hola_decode(leg_args, lola, torch, 32, hw.h, 4196, hw.d_k)
     if not args.no_cpu_baseline:
         log("cpu baseline: running the oracle ...")
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_heads)
