@@ -609,11 +609,11 @@ hipError_t launch_prefill_t(const PrefillArgs& a0, hipStream_t stream, hipEvent_
     // When the chain holds a quarter of the compute units or more, its read-outs take about as long as
     // the chain itself, and a read-out launch whose workgroups wait for free units holds up the dispatch
     // of the chain's next range behind it until its last workgroup is placed.  The read-outs beside the
-    // chain are then cut into launches of at most cap units: two rounds of the workgroups the free units
-    // hold, so a chain range waits at most about one read-out workgroup's time.
+    // chain are then cut into launches of at most cap units: three rounds of the workgroups the free
+    // units hold, so a chain range waits at most about one read-out workgroup's time.
     const int cap = (fastro && 4 * a.BH >= ncu && a.BH < ncu)
-                        ? std::max(1, 2 * readout_fast_groups_per_cu() * (ncu - a.BH) / a.BH) : 0;
-    const int nseg = cap > 0 ? split_capped(nunits, 35, bounds, kMaxSegments)
+                        ? std::max(1, 3 * readout_fast_groups_per_cu() * (ncu - a.BH) / a.BH) : 0;
+    const int nseg = cap > 0 ? split_capped(nunits, 40, bounds, kMaxSegments)
                              : split_chunks(nunits, fastro ? a.BH : a.BH * a.nqt, ncu, bounds, kMaxSegments);
     for (int i = 0; i <= nseg; ++i) bounds[i] = bounds[i] * cpu < a.nchunks ? bounds[i] * cpu : a.nchunks;
     if ((e = launch_phi_t<T, DK, PHI>(a, stream)) != hipSuccess) return e;
