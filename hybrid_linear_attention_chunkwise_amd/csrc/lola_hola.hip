@@ -693,6 +693,23 @@ __global__ __launch_bounds__(256) void hola_state_kernel(HolaArgs A) {
 }
 
 // ---------------- decode ----------------
+// N consecutive elements of a row, 16-byte aligned, in 16-byte pieces (8 bytes when that is all).
+template <typename T, int N>
+__device__ __forceinline__ void load_row_piece(const T* p, T (&out)[N]) {
+    constexpr int BYTES = N * (int)sizeof(T);
+    static_assert(BYTES % 8 == 0, "whole 8-byte pieces");
+    if constexpr (BYTES >= 16) {
+#pragma unroll
+        for (int u = 0; u < BYTES / 16; ++u) {
+            const uint4 x = reinterpret_cast<const uint4*>(p)[u];
+            __builtin_memcpy(reinterpret_cast<char*>(out) + 16 * u, &x, 16);
+        }
+    } else {
+        const uint2 x = *reinterpret_cast<const uint2*>(p);
+        __builtin_memcpy(out, &x, 8);
+    }
+}
+
 // Sum over a workgroup of NT threads (every thread gets it); red holds NT / 64 floats.
 template <int NT>
 __device__ __forceinline__ float block_sum(float x, float* red) {
@@ -728,18 +745,21 @@ __device__ __forceinline__ float block_max(float x, float* red) {
 //      merges the chunk into the cache (top w by magnitude, ties to the older, sorted by position).
 template <typename T, int D>
 __global__ __launch_bounds__(4 * D) void hola_decode_kernel(HolaDecodeArgs A) {
-    constexpr int NT = 4 * D, R = D / 4, NG16 = NT / 16, EPL = D / 16;
+    constexpr int NT = 4 * D, NG16 = NT / 16, EPL = D / 16;
     constexpr int EPV = 16 / (int)sizeof(T), PPR = D / EPV;
     constexpr int MAXE = kHolaMaxW + kHolaMaxC;
+    constexpr int SRG = NT / (D / 4), SR = D / SRG;      // state: row groups of float4 columns, rows each
+    constexpr int CPL = 8, VRG = NT / (D / CPL);         // value rows: 8 columns a thread, row groups
+    static_assert(SRG == 16 && VRG == 32, "the reduction buffer holds 32 row groups");
     __shared__ float sQ[D], sK[D], sKr[D], sV[D], sU[D], sE[D];
-    __shared__ float sPart[2][4][D];
+    __shared__ __align__(16) float sPart[32][D];
     __shared__ float sRed[NT / 64];
     __shared__ float sLg[MAXE];
     __shared__ unsigned long long sKey[MAXE];
     __shared__ int sKeep[kHolaMaxW];              // kept candidates in position order
     const int bh = blockIdx.x, tid = threadIdx.x, head = bh % A.heads;
     const int w = A.w, C = A.C, nopen = A.nopen;
-    const int j = tid % D, rg = tid / D;
+    const int j = tid % D;
     const float alpha = A.alpha[bh], beta = A.beta[bh];
 
     // 1. the token
@@ -762,36 +782,53 @@ __global__ __launch_bounds__(4 * D) void hola_decode_kernel(HolaDecodeArgs A) {
     }
     __syncthreads();
 
-    // 2. the state (held in registers up to d = 128; read again for the update at d = 256)
-    constexpr bool KEEP = R <= 32;
+    // 2. the state: thread (row group sg, columns 4 jc .. + 3) holds D / 16 rows of four columns (in
+    // registers up to d = 128, read again for the update at d = 256), as 16-byte pieces
+    constexpr bool KEEP = SR <= 8;
+    const int jc = tid % (D / 4), sg = tid / (D / 4);
     float* Sg = A.S + (int64_t)bh * D * D;
-    float sr[KEEP ? R : 1];
-    float pk = 0.f, pq = 0.f;
-#pragma unroll 16
-    for (int r = 0; r < R; ++r) {
-        const int i = rg * R + r;
-        const float sv = Sg[(int64_t)i * D + j];
-        if (KEEP) sr[r] = sv;
+    f4 sr[KEEP ? SR : 1];
+    f4 pk = zero4(), pq = zero4();
+#pragma unroll 8
+    for (int r = 0; r < SR; ++r) {
+        const int i = sg * SR + r;
+        const float4 v4 = *reinterpret_cast<const float4*>(Sg + (int64_t)i * D + 4 * jc);
+        const f4 sv = f4{v4.x, v4.y, v4.z, v4.w};
+        if (KEEP) sr[KEEP ? r : 0] = sv;
         pk += sv * sK[i];
         pq += sv * sQ[i];
     }
-    sPart[0][rg][j] = pk;
-    sPart[1][rg][j] = pq;
+    *reinterpret_cast<float4*>(&sPart[sg][4 * jc]) = make_float4(pk[0], pk[1], pk[2], pk[3]);
+    *reinterpret_cast<float4*>(&sPart[16 + sg][4 * jc]) = make_float4(pq[0], pq[1], pq[2], pq[3]);
     __syncthreads();
     float e = 0.f, o = 0.f;
     if (tid < D) {
-        const float stk = (sPart[0][0][j] + sPart[0][1][j]) + (sPart[0][2][j] + sPart[0][3][j]);
-        const float stq = (sPart[1][0][j] + sPart[1][1][j]) + (sPart[1][2][j] + sPart[1][3][j]);
+        float stk = 0.f, stq = 0.f;
+#pragma unroll
+        for (int g2 = 0; g2 < SRG; ++g2) {
+            stk += sPart[g2][j];
+            stq += sPart[16 + g2][j];
+        }
         e = sV[j] - alpha * stk;
         o = alpha * stq + beta * (kq * iq * ik) * e;
         sE[j] = e;
     }
     const float m = beta * sqrtf(block_sum<NT>(e * e, sRed));   // its barriers also publish sE
-#pragma unroll 16
-    for (int r = 0; r < R; ++r) {
-        const int i = rg * R + r;
-        const float sv = KEEP ? sr[KEEP ? r : 0] : Sg[(int64_t)i * D + j];
-        Sg[(int64_t)i * D + j] = alpha * sv + beta * sK[i] * sE[j];
+    {
+        const f4 e4 = f4{sE[4 * jc], sE[4 * jc + 1], sE[4 * jc + 2], sE[4 * jc + 3]};
+#pragma unroll 8
+        for (int r = 0; r < SR; ++r) {
+            const int i = sg * SR + r;
+            f4 sv;
+            if (KEEP) {
+                sv = sr[KEEP ? r : 0];
+            } else {
+                const float4 v4 = *reinterpret_cast<const float4*>(Sg + (int64_t)i * D + 4 * jc);
+                sv = f4{v4.x, v4.y, v4.z, v4.w};
+            }
+            const f4 nw = alpha * sv + (beta * sK[i]) * e4;
+            *reinterpret_cast<float4*>(Sg + (int64_t)i * D + 4 * jc) = make_float4(nw[0], nw[1], nw[2], nw[3]);
+        }
     }
 
     // 3. the cache path: entries = cache (valid slots first), open tokens, the token
@@ -808,10 +845,12 @@ __global__ __launch_bounds__(4 * D) void hola_decode_kernel(HolaDecodeArgs A) {
         for (int en = grp; en < NE; en += NG16) {
             float dot = 0.f, ss = 0.f;
             if (en < nv + nopen) {
-                const T* kr = en < nv ? ck + (int64_t)en * D : okp + (int64_t)(en - nv) * D;
+                const T* kr = (en < nv ? ck + (int64_t)en * D : okp + (int64_t)(en - nv) * D) + gl * EPL;
+                T kb[EPL];
+                load_row_piece<T, EPL>(kr, kb);
 #pragma unroll
                 for (int x = 0; x < EPL; ++x) {
-                    const float kv = to_f(kr[gl * EPL + x]);
+                    const float kv = to_f(kb[x]);
                     dot += kv * sU[gl * EPL + x];
                     ss += kv * kv;
                 }
@@ -843,21 +882,37 @@ __global__ __launch_bounds__(4 * D) void hola_decode_kernel(HolaDecodeArgs A) {
         psum += p;
     }
     const float den = block_sum<NT>(psum, sRed) + expf(sink - mx);   // its barriers also publish sLg
-    float acc = 0.f;
-    for (int en = rg; en < NE; en += 4) {
-        float vv;
-        if (en < nv) vv = to_f(cvv[(int64_t)en * D + j]);
-        else if (en < nv + nopen) vv = to_f(ovp[(int64_t)(en - nv) * D + j]);
-        else vv = sV[j];
-        acc += sLg[en] * vv;
+    // the value rows: thread (row group vg, columns 8 vc .. + 7), rows vg, vg + 32, ...
+    {
+        const int vc = tid % (D / CPL), vg = tid / (D / CPL);
+        float acc[CPL];
+#pragma unroll
+        for (int x = 0; x < CPL; ++x) acc[x] = 0.f;
+        for (int en = vg; en < NE; en += VRG) {
+            const float p = sLg[en];
+            if (en < nv + nopen) {
+                const T* vr = (en < nv ? cvv + (int64_t)en * D : ovp + (int64_t)(en - nv) * D) + CPL * vc;
+                T vb[CPL];
+                load_row_piece<T, CPL>(vr, vb);
+#pragma unroll
+                for (int x = 0; x < CPL; ++x) acc[x] += p * to_f(vb[x]);
+            } else {
+#pragma unroll
+                for (int x = 0; x < CPL; ++x) acc[x] += p * sV[CPL * vc + x];
+            }
+        }
+        __syncthreads();                          // sPart is free
+#pragma unroll
+        for (int x = 0; x < CPL; ++x) sPart[vg][CPL * vc + x] = acc[x];
     }
-    __syncthreads();                              // sPart is free
-    sPart[0][rg][j] = acc;
     __syncthreads();
 
     // 4. output, the open chunk, the chunk close
     if (tid < D) {
-        const float rd = ((sPart[0][0][j] + sPart[0][1][j]) + (sPart[0][2][j] + sPart[0][3][j])) / den;
+        float rsum = 0.f;
+#pragma unroll
+        for (int g2 = 0; g2 < VRG; ++g2) rsum += sPart[g2][j];
+        const float rd = rsum / den;
         const float gsig = 1.0f / (1.0f + expf(-A.gate[head]));
         reinterpret_cast<T*>(A.y)[(int64_t)bh * D + j] = from_f<T>(o + gsig * rd);
         okp[(int64_t)nopen * D + j] = from_f<T>(sKr[j]);
