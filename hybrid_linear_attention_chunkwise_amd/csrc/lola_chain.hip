@@ -662,7 +662,6 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
             T* stPhi = stage;                     // [D][ST_LD]
             T* stV = stage + D * ST_LD;           // [DV][ST_LD]
             for (int fb = 0; fb * FB < nS; ++fb) {
-                if (fb > 0) load_fold(fb);
 #pragma unroll
                 for (int u = 0; u < FIPT; ++u) {
                     const int q = tid + NT * u;
@@ -677,6 +676,9 @@ __global__ __launch_bounds__(4 * DK) void chain_kernel(PrefillArgs A) {
                     }
                 }
                 __syncthreads();
+                // the next batch's rows are in flight under this batch's products (the staging
+                // registers are free once their pieces are in LDS)
+                if ((fb + 1) * FB < nS) load_fold(fb + 1);
                 if (more && (fb + 1) * FB >= nS) build_table(ch + 1);
 #pragma unroll
                 for (int kk = 0; kk < FB / 32; ++kk) {
