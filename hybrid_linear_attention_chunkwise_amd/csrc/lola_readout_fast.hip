@@ -341,10 +341,18 @@ __global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs
     const float sl2 = kLog2e / sqrtf((float)DK);       // score -> base-2 logit
     f4 O[JT][2];
     float m_run[2], l_run[2];
+    // The exact terms' weights are summed by the matrix cores: an all-ones A operand against the
+    // probability fragments gives every lane the sum over a step's 32 keys for its query (the same
+    // bf16-rounded weights the value products use).  l_run keeps the linear seed only.
+    f4 lsum[2];
+    Frag8<T> ones;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ones.v[i] = (T)1.f;
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq) {
         m_run[qq] = -INFINITY;
         l_run[qq] = 0.f;
+        lsum[qq] = zero4();
 #pragma unroll
         for (int J = 0; J < JT; ++J) O[J][qq] = zero4();
     }
@@ -549,6 +557,7 @@ __global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs
                     const float mn_ = fmaxf(m_run[qq], bm);
                     const float alpha = m_run[qq] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[qq] - mn_);
                     l_run[qq] *= alpha;
+                    lsum[qq][0] *= alpha;
 #pragma unroll
                     for (int J = 0; J < JT; ++J)
 #pragma unroll
@@ -556,21 +565,18 @@ __global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs
                     m_run[qq] = mn_;
                 }
                 const float mref = m_run[qq] == -INFINITY ? 0.f : m_run[qq];
-                float ls = 0.f;
 #pragma unroll
                 for (int kt = 0; kt < KB / 16; ++kt)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kt][qq][r], sl2, -mref));
-                        S[kt][qq][r] = p;
-                        ls += p;
-                    }
-                l_run[qq] += ls;
+                    for (int r = 0; r < 4; ++r)
+                        S[kt][qq][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kt][qq][r], sl2, -mref));
             }
 #pragma unroll
             for (int k2 = 0; k2 < KB / 32; ++k2) {
                 const Frag8<T> p0 = frag_from_acc<T>(S[2 * k2][0], S[2 * k2 + 1][0]);
                 const Frag8<T> p1 = frag_from_acc<T>(S[2 * k2][1], S[2 * k2 + 1][1]);
+                mma32(lsum[0], ones, p0);
+                mma32(lsum[1], ones, p1);
 #pragma unroll
                 for (int J = 0; J < JT; ++J) {
                     // value rows 16J + c, keys 32k2 + 4g .. + 3 and 32k2 + 16 + 4g .. + 3, by transposed reads of
@@ -595,8 +601,8 @@ __global__ __launch_bounds__(kRfThreads, 2) void readout_fast_kernel(PrefillArgs
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq) {
         const int64_t tq = tw0 + 16 * qq + c;
-        // l_run holds each lane's partial sum over its key rows (and the linear seed on lane group 0)
-        const float tot = sum_groups(l_run[qq]);
+        // the linear seed (on lane group 0, hence the group sum) and the exact weights (every lane)
+        const float tot = sum_groups(l_run[qq]) + lsum[qq][0];
         if (wave_active && tq < tend) {
             const float inv = 1.f / tot;
             T* yrow = yout + (tq - t0) * DV;
