@@ -17,11 +17,14 @@
 //   1. H^T to LDS, the chunk-start snapshot to the chunk record;                               barrier
 //   2. every wave scores its tiles (at most two cache tiles and one leaving-token tile), reading
 //      each A fragment of H^T once for all of them;                                            barrier
-//   3. wave 0 selects the nF smallest keys (a 256-bin histogram of SRE, then an exact rank of the
-//      boundary bin), ranks folds, freed slots and entrants with ballots and writes the fold list;
-//                                                                                              barrier
-//   4. slot owners stage their folded members' rows and take entrants from the leaving buffer;
-//                                                                                              barrier
+//   3. all eight waves select the nF smallest keys together: a shared 256-bin histogram of the SRE
+//      bits between their extremes, a scan that every wave repeats to find the boundary bin, and an
+//      exact rank of that bin's members (its 16-key bucket, or a list when it holds more);
+//                                                                                      two barriers
+//   4. each wave publishes its tiles' fold and freed-slot counts and entrant masks; after one
+//      exchange every slot owner ranks its own slots, writes the fold list and the slot table,
+//      stages its folded members' rows and takes its entrants from the leaving buffer;
+//                                                                                      two barriers
 //   5. fold: H += Phi_S^T V_S, both operands read with transposing LDS reads of the token rows.
 #include <stdlib.h>
 
