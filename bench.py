@@ -594,7 +594,7 @@ def main() -> int:
 
     import torch
     import hybrid_linear_attention_chunkwise_amd as lola
-    from workloads import CONFIGS
+    from workloads import WORKLOADS
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -612,18 +612,18 @@ def main() -> int:
         return 0
     src_hash = kernel_source_hash()
     if args.only_hola:
-        hw = CONFIGS[2]
+        hw = WORKLOADS[2]
         r = bench_hola(args, lola, torch, hw.B, hw.h, hw.n, hw.d_k)
         r["d256"] = bench_hola(args, lola, torch, 1, 4, hw.n, 256)
         r["decode"] = bench_hola_decode(args, lola, torch, 32, hw.h, 4196, hw.d_k)
         print(json.dumps({"hola": r}))
         return 0
     if args.no_prefill:        # profiling mode: the decode workload only
-        dwl = CONFIGS[4]
+        dwl = WORKLOADS[4]
         r = bench_decode(args, lola, torch, dwl)
         print(json.dumps({"decode_ms_per_step": r["wall"] / dwl.decode_steps * 1e3, "decode_kernel_ms": r["kern_ms"]}))
         return 0
-    wl = CONFIGS[args.headline]
+    wl = WORKLOADS[args.headline]
     head = prefill_report(wl, bench_prefill(args, lola, torch, wl))
     kern = head["kernels_ms_sequential"]
     dominant = max(("chain", "readout"), key=lambda k_: kern[k_])
@@ -654,12 +654,12 @@ def main() -> int:
         for cid in (2, 3, 5):
             if cid == args.headline:
                 continue
-            lw = CONFIGS[cid]
+            lw = WORKLOADS[cid]
             legs[lw.name] = prefill_report(lw, bench_prefill(args, lola, torch, lw, steps=args.leg_steps,
                                                              warmup=max(2, args.warmup // 2), kernel_steps=5))
         out["prefill_legs"] = legs
     if not args.no_decode:
-        dwl = CONFIGS[4]
+        dwl = WORKLOADS[4]
         r = bench_decode(args, lola, torch, dwl)
         per_step = r["wall"] / dwl.decode_steps
         byts = decode_bytes_per_seq_head(dwl) * dwl.B * dwl.h
@@ -677,11 +677,11 @@ def main() -> int:
     import argparse as _ap
     leg_args = _ap.Namespace(**{**vars(args), "steps": args.leg_steps, "warmup": max(2, args.warmup // 2)})
     if not args.no_collisions:
-        out["collision_map"] = bench_collisions(leg_args, lola, torch, CONFIGS[2])
+        out["collision_map"] = bench_collisions(leg_args, lola, torch, WORKLOADS[2])
     if not args.no_options:
-        out["options"] = bench_options(leg_args, lola, torch, CONFIGS[2])
+        out["options"] = bench_options(leg_args, lola, torch, WORKLOADS[2])
     if not args.no_hola:
-        hw = CONFIGS[2]
+        hw = WORKLOADS[2]
         out["hola"] = bench_hola(leg_args, lola, torch, hw.B, hw.h, hw.n, hw.d_k)
         # the HOLA page's own setup: 4 heads of dimension 256
         out["hola"]["d256"] = bench_hola(leg_args, lola, torch, 1, 4, hw.n, 256)

@@ -55,10 +55,10 @@ def test_flop_model_matches_the_scope_table():
     2 D (d_v + 1), intra-chunk term (D + d_v + 1)(C + 1), scoring 2 D (d_v + 1)(C + lambda) / C and fold
     2 D (d_v + 1) add up to 542,785 FLOP; the chain kernel's share is the scoring and the fold."""
     import bench
-    from workloads import CONFIGS
+    from workloads import WORKLOADS
     for cid in (2, 3):
-        fl = bench.prefill_flops(CONFIGS[cid])
+        fl = bench.prefill_flops(WORKLOADS[cid])
         assert fl["per_token_head"] == 542785
-        units = CONFIGS[cid].B * CONFIGS[cid].h * CONFIGS[cid].n
+        units = WORKLOADS[cid].B * WORKLOADS[cid].h * WORKLOADS[cid].n
         assert fl["chain"] == (165120 + 33024) * units
         assert abs(fl["phi"] + fl["chain"] + fl["readout"] - fl["total"]) < 1

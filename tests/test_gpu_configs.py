@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import lola_testlib as TL
-from workloads import CONFIGS, make_decode_tokens_device, make_qkv, make_qkv_device, make_weights
+from workloads import WORKLOADS, make_decode_tokens_device, make_qkv, make_qkv_device, make_weights
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -23,7 +23,7 @@ def _need_gpu():
 
 
 def _run_config(cfg_id, dtype, heads, replay_only=False):
-    wl = CONFIGS[cfg_id]
+    wl = WORKLOADS[cfg_id]
     W = make_weights(wl)
     q, k, v = make_qkv(wl)
     print(f"[config {cfg_id}] {wl.name} as {dtype}: GPU prefill of B={wl.B} h={wl.h} n={wl.n}", flush=True)
@@ -77,7 +77,7 @@ def test_config4_decode_sampled(dtype):
     oracle continuing from the GPU's post-prefill state (every fold validated, see grade_decode_steps)."""
     import hybrid_linear_attention_chunkwise_amd as lola
     from oracle import lola_oracle as O
-    wl = CONFIGS[4]
+    wl = WORKLOADS[4]
     dev = torch.device("cuda:0")
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     W = make_weights(wl)
@@ -133,7 +133,7 @@ def test_config2_collision_map_sampled(dtype):
     heads recomputed in full by the oracle."""
     import dataclasses
     from test_gpu_parity import collision_check
-    wl = dataclasses.replace(CONFIGS[2], dtype=dtype)
+    wl = dataclasses.replace(WORKLOADS[2], dtype=dtype)
     collision_check(wl, [(0, 3), (0, 30)])
 
 

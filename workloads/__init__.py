@@ -15,7 +15,7 @@ from typing import Dict, Optional
 
 import numpy as np
 
-__all__ = ["Workload", "CONFIGS", "round_to_bf16", "make_weights", "make_qkv", "make_inputs",
+__all__ = ["Workload", "WORKLOADS", "round_to_bf16", "make_weights", "make_qkv", "make_inputs",
            "make_decode_tokens", "small_workload", "make_qkv_device", "make_decode_tokens_device"]
 
 
@@ -48,7 +48,7 @@ class Workload:
 
 
 # The five workloads of the hot path (one attention layer, all heads).
-CONFIGS: Dict[int, Workload] = {
+WORKLOADS: Dict[int, Workload] = {
     1: Workload("n512_h1_d64_elu1_f32", B=1, h=1, n=512, d_k=64, d_v=64, phi="elu1", D=128, C=64,
                 eta=64, lam=64, dtype="f32", seed=1),
     2: Workload("n4096_h32_d128_pm_outliers_bf16", B=1, h=32, n=4096, d_k=128, d_v=128,
@@ -151,7 +151,7 @@ def make_decode_tokens(wl: Workload, B: Optional[int] = None, h: Optional[int] =
 
 def make_inputs(cfg_id: int, **overrides):
     """(workload, W, q, k, v) for one of the five configurations; keyword overrides shrink B/h/n."""
-    wl = CONFIGS[cfg_id]
+    wl = WORKLOADS[cfg_id]
     q, k, v = make_qkv(wl, n=overrides.get("n"), B=overrides.get("B"), h=overrides.get("h"))
     return wl, make_weights(wl), q, k, v
 
