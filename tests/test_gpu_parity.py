@@ -113,6 +113,21 @@ def test_outlier_keys_and_planted_pairs_small():
     _check_workload(wl)
 
 
+LARGEST_CASES = [
+    # the largest cache (lambda = 1024) and chunk (C = 128) the library accepts; the cache fills after
+    # eta + lambda tokens, so the last chunks each select among lambda + C candidates
+    (90, dict(n=1700, C=128, eta=128, lam=1024, d_k=128, d_v=128)),   # d = 128, ragged last chunk
+    (91, dict(n=1500, C=128, eta=127, lam=1024, d_k=64, d_v=64)),     # d = 64, eta = C - 1
+]
+
+
+@pytest.mark.parametrize("seed,kw", LARGEST_CASES, ids=[f"s{s}" for s, _ in LARGEST_CASES])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_at_the_largest_cache_and_chunk(seed, kw, dtype):
+    wl = small_workload(seed, B=1, h=2, dtype=dtype, **kw)
+    _check_workload(wl)
+
+
 @pytest.mark.parametrize("split", [[64, 136], [32, 32, 96, 40], [192, 8]])
 def test_continuation_calls_equal_one_call(split):
     wl = small_workload(30, B=1, h=2, n=200, C=16, eta=24, lam=20, dtype="f32")
@@ -247,6 +262,14 @@ def test_decode_bf16_cache_beyond_register_path():
     general kernel automatically."""
     wl = small_workload(54, B=1, h=2, n=0, C=1, eta=32, lam=400, d_k=128, d_v=128, dtype="bf16")
     _decode_check(wl, n0=480, steps=24, heads=[(0, 0), (0, 1)], C0=32)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_at_the_largest_cache(dtype):
+    """Decode with the largest cache the library accepts (lambda = 1024, d = 128): every step scores
+    lambda + 1 candidates through the general decode kernel."""
+    wl = small_workload(92, B=1, h=2, n=0, C=1, eta=128, lam=1024, d_k=128, d_v=128, dtype=dtype)
+    _decode_check(wl, n0=1300, steps=16, heads=[(0, 0), (0, 1)], C0=128)
 
 
 def test_overlapped_prefill_equals_sequential():
