@@ -192,9 +192,12 @@ def grade_chunked_decode(so, phi_o, q, k, v, ys, caches, t0: int, cd: int, dtype
     tol = TIE_BAND if dtype == "f32" else BF16_TOL
     out_tol = FP32_TOL if dtype == "f32" else BF16_TOL
     worst, mism, s, steps = 0.0, 0, 0, len(ys)
+    # A group's allocation covers every token that leaves during the whole group, so a group the
+    # steps stop inside cannot be compared with a prefill chunk of the steps taken: whole groups only.
+    assert (t0 + steps) % cd == 0, "chunked decode grading needs the steps to end on a group boundary"
     while s < steps:
         a = t0 + s
-        b = min((a // cd + 1) * cd, t0 + steps)
+        b = (a // cd + 1) * cd
         n = b - a
         X = [p for p in range(a - so.eta, b - so.eta) if p >= 0]
         cand = set(caches[s]) | set(X)

@@ -682,6 +682,11 @@ HOLA_CASES = [
     (94, dict(n=200, C=32, w=0, d=64)),         # w = 0: chunk tokens and the sink only
     (95, dict(n=530, C=256, w=64, d=256)),      # the page's head dimension, w and C
     (96, dict(n=300, C=64, w=16, d=256)),       # d = 256, several chunks, ragged tail
+    # the largest chunk and cache: two full chunks and a ragged one.  The bound is relative to each
+    # output row's norm; the seed is one whose rows are all at least a quarter of the median row norm
+    # (with seed 97 the state and cache terms of row 0 cancel to 3% of it, and that row's bf16
+    # rounding, no larger than any other row's, exceeds the relative bound)
+    (98, dict(n=2500, C=1024, w=64, d=128)),
 ]
 
 
@@ -733,6 +738,7 @@ HOLA_DECODE_CASES = [
     (114, dict(n0=100, steps=12, C=1, w=8, d=64)),      # every token closes its chunk
     (115, dict(n0=60, steps=10, C=32, w=0, d=64)),      # no persistent cache
     (116, dict(n0=300, steps=20, C=64, w=16, d=256)),   # the page's head dimension
+    (118, dict(n0=1000, steps=40, C=1024, w=64, d=128)),  # the largest chunk closes during the decode
 ]
 
 
@@ -925,6 +931,13 @@ def chunked_decode_check(wl, n0, steps, cd, heads):
 def test_chunked_decode_small(dtype, cd):
     wl = small_workload(140 + cd, B=2, h=2, n=0, C=1, eta=20, lam=16, d_k=64, d_v=64, dtype=dtype)
     chunked_decode_check(wl, n0=64, steps=48, cd=cd, heads=[(0, 0), (1, 1)])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunked_decode_largest_group(dtype):
+    """decode_chunk = 64, the largest group: the fold mask uses all 64 bits of its word."""
+    wl = small_workload(153, B=1, h=2, n=0, C=1, eta=64, lam=48, d_k=64, d_v=64, dtype=dtype)
+    chunked_decode_check(wl, n0=200, steps=184, cd=64, heads=[(0, 0), (0, 1)])
 
 
 def test_chunked_decode_d128_unaligned_start():
