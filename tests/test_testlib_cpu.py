@@ -49,3 +49,10 @@ def test_decode_grader_rejects_a_wrong_fold(dtype):
     assert bad[s] != folds[s]
     with pytest.raises(AssertionError):
         TL.grade_decode_steps(st, phi, q, k, v, ys, bad, dtype)
+
+
+def test_chunked_decode_grader_needs_whole_groups():
+    """A run that stops inside a group is refused before any grading: the group's allocation covers
+    tokens whose steps were never taken."""
+    with pytest.raises(AssertionError, match="group boundary"):
+        TL.grade_chunked_decode(None, None, None, None, None, [None] * 5, None, t0=2, cd=4, dtype="f32")
