@@ -21,7 +21,9 @@
 //
 // Softmax in base 2 with the scale folded into one FMA; the running max is raised only when a block's
 // max exceeds it by more than 8 (wave-uniform), so most blocks skip the accumulator rescale.  Probabilities
-// are at most 2^8 and the result is the same up to rounding.
+// are at most 2^8 and the result is the same up to rounding.  The exact weights of the denominator are
+// summed on the matrix cores (an all-ones operand against each bf16 probability fragment), so numerator
+// and denominator use the same rounded weights.
 //
 // Workgroups are ordered so that each XCD (workgroup id mod 8) takes a contiguous run of tiles of the
 // same heads: neighbouring chunks share most window and cache keys in that XCD's L2.
